@@ -1,0 +1,453 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle (``oracle/mxq_oracle.c``) is checked against things other than
+itself: the values the pages state (``tests/golden/pages_facts.json``), closed
+forms derived by hand from the E4M3 / bf16 bit layouts, library routines
+(torch's float8 and bfloat16 casts), invariants the pages claim (decode of the
+direct conversions reproduces the projection), and an exact-rational brute
+force (``tests/frac_ref.py``) on exhaustive small inputs.  The mutation tests
+plant plausible mistakes in the brute force and show the pins catch them.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import frac_ref as F
+
+BF16, FP32 = oracle.BF16, oracle.FP32
+
+
+def bf16_bits(v: float) -> int:
+    return int(W.bf16_bits_of(v))
+
+
+# ---------------------------------------------------------------- decoding and rounding
+
+def test_unpack_matches_numpy_and_torch():
+    """Bit decoding against numpy's fp32 view (bf16) and torch's float8 dtypes."""
+    for b in range(0, 65536, 7):
+        neg, M, k, cls = oracle.unpack(b, oracle.FMT_BF16)
+        ref = np.array([b << 16], dtype=np.uint32).view(np.float32)[0]
+        if np.isnan(ref):
+            assert cls == 2
+        elif np.isinf(ref):
+            assert cls == 1
+        else:
+            assert cls == 0 and (-1) ** neg * Fraction(M) * Fraction(2) ** k == Fraction(float(ref))
+    for fmt, tdt in ((oracle.FMT_E4M3, torch.float8_e4m3fn), (oracle.FMT_E5M2, torch.float8_e5m2)):
+        vals = torch.arange(256, dtype=torch.uint8).view(tdt).to(torch.float64).numpy()
+        for b in range(256):
+            neg, M, k, cls = oracle.unpack(b, fmt)
+            if np.isnan(vals[b]):
+                assert cls == 2
+            elif np.isinf(vals[b]):
+                assert cls == 1
+            else:
+                assert cls == 0 and (-1) ** neg * Fraction(M) * Fraction(2) ** k == Fraction(float(vals[b]))
+
+
+def _fp32_samples(n, seed):
+    g = np.random.default_rng(seed)
+    bits = g.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+    return bits[np.isfinite(bits.view(np.float32))]
+
+
+def test_round_to_bf16_matches_torch_cast():
+    """Nearest-even rounding into bf16 equals torch's fp32 -> bf16 cast
+    (a library routine), including subnormals and overflow to Inf."""
+    bits = np.concatenate([_fp32_samples(20000, 1),
+                           np.arange(0, 1 << 20, 97, dtype=np.uint32),            # fp32 subnormals
+                           np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x007F8000, 0x00008000], dtype=np.uint32)])
+    ref = torch.from_numpy(bits.view(np.float32).copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for b, r in zip(bits, ref):
+        neg, M, k, cls = oracle.unpack(int(b), oracle.FMT_FP32)
+        got, _, _ = oracle.round_to_format(neg, M, k, oracle.FMT_BF16)
+        assert got == r, hex(b)
+
+
+def test_round_to_e4m3_matches_torch_cast():
+    """Nearest-even rounding into E4M3 (subnormals included) equals torch's
+    fp32 -> float8_e4m3fn cast on every value inside E4M3's range."""
+    g = np.random.default_rng(2)
+    mags = np.concatenate([np.ldexp(g.random(30000), g.integers(-14, 9, 30000)),
+                           np.arange(0, 2 ** -5, 2 ** -13), np.array([448.0, 447.0, 2 ** -10, 3 * 2 ** -11])])
+    mags = mags[mags <= 448].astype(np.float32)
+    vals = np.concatenate([mags, -mags])
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v, r in zip(vals.view(np.uint32), ref):
+        neg, M, k, cls = oracle.unpack(int(v), oracle.FMT_FP32)
+        got, _, ovf = oracle.round_to_format(neg, M, k, oracle.FMT_E4M3)
+        assert not ovf and got == r, hex(v)
+
+
+# ---------------------------------------------------------------- the scale exponent
+
+def test_scale_exponent_exhaustive_bf16_vs_brute_force(facts):
+    lo, hi = facts["scale_exponent_clamp"]["value"]
+    seen = set()
+    for b in range(0x7F80):
+        e = oracle.scale_exponent_bits(b, BF16)
+        assert e == F.scale_exponent(F.bf16_value(b)), hex(b)
+        seen.add(e)
+    assert min(seen) == lo and max(seen) == hi
+
+
+def test_scale_exponent_fp32_fuzz_vs_brute_force():
+    for b in _fp32_samples(20000, 3):
+        b = int(b) & 0x7FFFFFFF
+        assert oracle.scale_exponent_bits(b, FP32) == F.scale_exponent(F.fp32_value(b)), hex(b)
+
+
+@pytest.mark.parametrize("k", [-124, -60, -3, -1, 0, 1, 2, 60, 126])
+def test_one_point_five_times_two_to_k_triples(k):
+    """amax = 1.5*2^k gives amax/6 = 2^(k-2) exactly: e = k-2 there and one ulp
+    below, and e flips to k-1 one ulp above (clamped at 125)."""
+    b = bf16_bits(np.ldexp(1.5, k))
+    assert oracle.scale_exponent_bits(b, BF16) == max(-126, min(125, k - 2))
+    assert oracle.scale_exponent_bits(b - 1, BF16) == max(-126, min(125, k - 2))
+    assert oracle.scale_exponent_bits(b + 1, BF16) == max(-126, min(125, k - 1))
+    f = int(np.array(np.ldexp(1.5, k), dtype=np.float32).view(np.uint32))
+    assert oracle.scale_exponent_bits(f + 1, FP32) == max(-126, min(125, k - 1))
+    assert oracle.scale_exponent_bits(f, FP32) == max(-126, min(125, k - 2))
+
+
+# ---------------------------------------------------------------- E2M1 rounding
+
+GRID = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+# ties go to the neighbour with the even 3-bit code
+TIE_RESULT = {0.25: 0, 0.75: 1, 1.25: 1, 1.75: 2, 2.5: 2, 3.5: 4, 5: 4}
+
+
+@pytest.mark.parametrize("e", [-126, -122, -121, 0, 125])
+def test_e2m1_grid_points_and_midpoints(e, facts):
+    assert facts["e2m1_grid"]["value"] == GRID
+    for c, p in enumerate(GRID):
+        if p:
+            assert oracle.e2m1_code_bits(bf16_bits(np.ldexp(p, e)), e) == c
+    for mid, want in TIE_RESULT.items():
+        b = bf16_bits(np.ldexp(mid, e))
+        assert GRID[oracle.e2m1_code_bits(b, e)] == want
+        below, above = max(x for x in GRID if x < mid), min(x for x in GRID if x > mid)
+        assert GRID[oracle.e2m1_code_bits(b - 1, e)] == below
+        assert GRID[oracle.e2m1_code_bits(b + 1, e)] == above
+
+
+def test_e2m1_codes_exhaustive_vs_brute_force():
+    for e in (-126, -125, -124, -3, 0, 7, 125):
+        for b in range(0, 0x7F80, 3):
+            t = F.bf16_value(b) / Fraction(2) ** e
+            assert oracle.e2m1_code_bits(b, e) == F.e2m1_code(t), (hex(b), e)
+
+
+# ---------------------------------------------------------------- projection edge cases
+
+def test_subnormal_ladder():
+    """In a block whose scale is 2^-126: 2^-127 stays, 2^-128 is the tie and goes
+    to +0, 2^-129 .. 2^-133 go to 0."""
+    ladder = [bf16_bits(np.ldexp(1.0, -127 - i)) for i in range(7)]
+    x = np.array([ladder + [0] * 25], dtype=np.uint16)
+    y = oracle.fake_quantize_mxfp4(x)[0]
+    assert y[0] == 0x0040 and all(v == 0 for v in y[1:7])
+    x = np.array([[bf16_bits(2.0 ** -128)] * 32], dtype=np.uint16)
+    assert oracle.fake_quantize_mxfp4(x)[0].tolist() == [0] * 32
+
+
+def test_saturation_at_the_cap(facts):
+    assert facts["saturation_cap"]["value"] == "6*2^125"
+    cap = bf16_bits(6 * 2.0 ** 125)
+    assert cap == 0x7F40
+    x = np.array([list(range(0x7F41, 0x7F61))], dtype=np.uint16)
+    assert set(oracle.fake_quantize_mxfp4(x)[0].tolist()) == {0x7F40}
+    x = np.array([list(range(0xFF60, 0xFF80))], dtype=np.uint16)
+    assert set(oracle.fake_quantize_mxfp4(x)[0].tolist()) == {0xFF40}
+    data, scale = oracle.mxfp4_to_mxfp8_row(x)
+    assert scale[0, 0] == 125 + 121 and set(data[0].tolist()) == {0xFC}
+
+
+@pytest.mark.parametrize("bad", [0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0xFFFF])
+def test_non_finite_block_poisoning(bad):
+    x = np.array([[0x3F80] * 31 + [bad] + [0x3F80] * 32], dtype=np.uint16)
+    y = oracle.fake_quantize_mxfp4(x)[0]
+    assert set(y[:32].tolist()) == {0x7FC0} and set(y[32:].tolist()) == {0x3F80}
+    data, scale = oracle.mxfp4_to_mxfp8_row(x)
+    assert scale[0].tolist() == [255, -2 + 121]          # a block of ones has e = -2
+    assert set(data[0, :32].tolist()) == {0x7F}
+    out = oracle.dequantize(data, scale)
+    assert set(out[0, :32].tolist()) == {0x7FC0} and set(out[0, 32:].tolist()) == {0x3F80}
+
+
+def test_negative_zero_kept():
+    x = np.array([[0x8000, 0x0000, bf16_bits(-2.0 ** -10), bf16_bits(6.0)] + [0] * 28], dtype=np.uint16)
+    y = oracle.fake_quantize_mxfp4(x)[0]
+    assert y[0] == 0x8000 and y[1] == 0 and y[2] == 0x8000
+    data, _ = oracle.mxfp4_to_mxfp8_row(x)
+    assert data[0, 0] == 0x80 and data[0, 2] == 0x80
+
+
+# ---------------------------------------------------------------- direct row lift
+
+ROW_TABLE = {0: 0x00, 0.5: 0x60, 1: 0x68, 1.5: 0x6C, 2: 0x70, 3: 0x74, 4: 0x78, 6: 0x7C}
+
+
+def test_row_payload_closed_table(facts):
+    """p * 2^6 in E4M3 (bias 7, 3 mantissa bits) written out by hand; below
+    e = -121 the scale sits at code 0 and the payload absorbs the shift, which
+    lowers its exponent field by 6 - shift, i.e. the byte by 8*(6 - shift)."""
+    assert facts["row_fixed_shift"]["value"] == 6
+    for e in range(-126, 126):
+        shift = min(6, e + 127)
+        for p, byte in ROW_TABLE.items():
+            for sign in (1, -1):
+                vals = [6.0, sign * float(p)] + [0.0] * 30
+                x = np.array([W.bf16_bits_of(np.ldexp(np.array(vals), e))], dtype=np.uint16)
+                data, scale = oracle.mxfp4_to_mxfp8_row(x)
+                assert scale[0, 0] == max(e + 121, 0)
+                want = 0 if p == 0 else byte - 8 * (6 - shift)
+                if sign < 0:
+                    want |= 0x80
+                assert data[0, 1] == want, (e, p, sign)
+                assert data[0, 0] == ROW_TABLE[6] - 8 * (6 - shift)
+
+
+def test_code_zero_and_255_decode(facts):
+    assert facts["e8m0_code0"]["value"] == "2^-127" and facts["e8m0_code255"]["value"] == "NaN"
+    data = np.array([[0x38, 0xB8, 0x01, 0x7E]], dtype=np.uint8)       # 1.0, -1.0, 2^-9, 448
+    scale = np.array([[0]], dtype=np.uint8)
+    f32 = oracle.dequantize(data, scale, out_dtype=FP32)[0]
+    assert f32[0] == 0x00400000 and f32[1] == 0x80400000            # 2^-127 exactly
+    assert f32[2] == 1 << (149 - 136)                                # 2^-136, an fp32 subnormal
+    assert oracle.dequantize(data, scale, out_dtype=BF16)[0][:3].tolist() == [0x0040, 0x8040, 0x0000]
+    nan = oracle.dequantize(data, np.array([[255]], dtype=np.uint8), out_dtype=BF16)[0]
+    assert set(nan.tolist()) == {0x7FC0}
+    # a block of 2^-127: e = -126, E8M0 code 0, payload 1.0 (0x38), decoding to 2^-127
+    x = np.array([[0x0040] * 32], dtype=np.uint16)
+    d, s = oracle.mxfp4_to_mxfp8_row(x)
+    assert s[0, 0] == 0 and set(d[0].tolist()) == {0x38}
+    assert set(oracle.dequantize(d, s)[0].tolist()) == {0x0040}
+
+
+def _same_bits_nan_canonical(a, b):
+    return np.array_equal(a, b)
+
+
+CORPORA = {
+    "c1": lambda: W.c1_small(),
+    "c2_shuffled": lambda: W.c2_exhaustive(),
+    "c2_natural": lambda: W.c2_exhaustive(natural=True),
+    "c2_planted": lambda: W.c2_planted(),
+}
+
+
+@pytest.mark.parametrize("name", list(CORPORA))
+def test_decode_of_row_lift_is_the_projection(name):
+    """The pages: rowwise MXFP8 bytes decode back to the projected weight
+    exactly, including 2^-127 at code 0; poisoned blocks decode to NaN."""
+    x = CORPORA[name]()
+    y = oracle.fake_quantize_mxfp4(x)
+    data, scale = oracle.mxfp4_to_mxfp8_row(x)
+    assert np.array_equal(oracle.dequantize(data, scale), y)
+    assert np.array_equal(oracle.dequantize(data, scale, out_dtype=FP32), (y.astype(np.uint32) << 16))
+
+
+def test_decode_of_row_lift_is_the_projection_fp32():
+    x = W.fp32_fuzz(1 << 15)
+    y = oracle.fake_quantize_mxfp4(x)
+    data, scale = oracle.mxfp4_to_mxfp8_row(x)
+    assert np.array_equal(oracle.dequantize(data, scale, out_dtype=FP32), y)
+
+
+def test_exhaustive_corpus_block_count(facts):
+    """Natural order: 2036 of 2048 blocks are finite and below saturation."""
+    fact = facts["exhaustive_finite_below_saturation_blocks"]
+    x = W.c2_exhaustive(natural=True)
+    data, scale = oracle.mxfp4_to_mxfp8_row(x)
+    finite = scale[:, 0] != 255
+    mags = (x & 0x7FFF).astype(np.int64)
+    below_cap = (mags <= 0x7F40).all(axis=1)
+    assert x.shape[0] == fact["of"]
+    assert int((finite & below_cap).sum()) == fact["value"]
+
+
+# ---------------------------------------------------------------- 128x128 folding
+
+def spread_row(d: int, base: int, sign_flip: bool = False) -> np.ndarray:
+    """One 128-wide tile row: block 0 at exponent base holds 6 and every +-grid
+    point and midpoint, block 1 sets the tile maximum base+d, blocks 2-3 are the
+    low block negated / shifted."""
+    low = [6.0] + [s * p for p in GRID for s in (1, -1)] + [s * m for m in TIE_RESULT for s in (1, -1)] + [-6.0]
+    low = np.ldexp(np.array(low), base)
+    high = np.ldexp(np.array([6.0] + [0.5] * 31), base + d)
+    row = np.concatenate([low, high, -low, np.ldexp(np.array(GRID * 4), base)])
+    return row
+
+
+def _fp32_bits_of(v):
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, dtype=np.float64))
+    return f.view(np.uint32)
+
+
+def test_block128_exactness_boundary(facts):
+    """decode(blockwise bytes) equals the projection for every tile whose block
+    exponents spread by at most 2^14; at 2^15 the first values are lost."""
+    exact_through = facts["block128_exact_through_log2_spread"]["value"]
+    first_loss = facts["block128_first_loss_log2_spread"]["value"]
+    for base in (-126, -120, -60, 0, 90):
+        row = np.concatenate([spread_row(d, base) for d in range(17)])
+        x = _fp32_bits_of(row)[None, :]
+        y = oracle.fake_quantize_mxfp4(x)
+        data, codes = oracle.mxfp4_to_fp8_block128(x)
+        dec = oracle.dequantize(data, codes, layout=oracle.TILE_128X128, out_dtype=FP32)
+        for d in range(17):
+            sl = slice(128 * d, 128 * d + 128)
+            same = np.array_equal(dec[0, sl], y[0, sl])
+            if d <= exact_through:
+                assert same, (base, d)
+            elif base + d - 6 > -127 and d >= first_loss:
+                assert not same, (base, d)
+            if base + d - 6 <= -127:      # tile clamp at code 0 keeps every value exact
+                assert same, (base, d)
+
+
+def test_block128_closed_form_first_losses():
+    """At spread d the low block's p*2^(6-d) lands on E4M3's subnormal step
+    2^-9: d = 15 sends 0.5 to 0 (tie) and 1.5 to 2^-8 (tie up to even); d = 16
+    sends 0.5, 1 to 0, 1.5 to 2^-9 and 3 to 2^-8; 2, 4, 6 stay exact."""
+    base = 0
+    for d, want in ((15, {0.5: 0, 1.5: 2.0 ** -8, 1: 2.0 ** -9, 3: 3 * 2.0 ** -9}),
+                    (16, {0.5: 0, 1: 0, 1.5: 2.0 ** -9, 3: 2.0 ** -8, 2: 2.0 ** -9, 4: 2.0 ** -8, 6: 3 * 2.0 ** -9})):
+        x = _fp32_bits_of(spread_row(d, base))[None, :]
+        data, codes = oracle.mxfp4_to_fp8_block128(x)
+        assert codes[0, 0] == base + d - 6 + 127
+        vals = torch.from_numpy(data[0, :32].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        lowvals = [6.0] + [s * p for p in GRID for s in (1, -1)]
+        for i, v in enumerate(lowvals):
+            p = abs(v)
+            if p in want:
+                assert abs(vals[i]) == want[p], (d, p, vals[i])
+
+
+def test_block128_tile_clamp():
+    """M < -121 puts the tile scale at code 0 and the payload takes e + 127."""
+    row = np.concatenate([spread_row(d, -126) for d in range(5)])
+    x = _fp32_bits_of(row)[None, :]
+    data, codes = oracle.mxfp4_to_fp8_block128(x)
+    assert codes[0].tolist() == [0] * 5
+
+
+def test_block128_poisoned_and_zero_tiles():
+    x = np.zeros((128, 256), dtype=np.uint16)
+    x[5, 3] = 0x7FC0                        # tile 0: one poisoned block, rest zero
+    x[:, 128:] = 0x3F80                     # tile 1: all ones
+    x[0, 200] = 0x7F80                      # ... with one poisoned block
+    data, codes = oracle.mxfp4_to_fp8_block128(x)
+    assert codes[0, 0] == 0                               # no finite nonzero block: M = -126
+    assert set(data[5, 0:32].tolist()) == {0x7F}
+    assert codes[0, 1] == (-2 - 6 + 127)                   # e of a block of ones is -2
+    assert set(data[0, 192:224].tolist()) == {0x7F}
+
+
+# ---------------------------------------------------------------- export
+
+def test_export_shapes(facts):
+    assert facts["export_scale_shape_100x48"]["value"] == [100, 2]
+    x = W.c1_small()
+    data, scale = oracle.mxfp4_to_mxfp8_row(x, scale_ld=4, fill=0xAB)
+    out = oracle.export_mxfp8(scale, 48)
+    assert list(out.shape) == [100, 2] and np.array_equal(out, scale[:, :2])
+    assert (scale[:, 2:] == 0xAB).all()                   # padding never written
+    x16 = W.c1_small()[:, :16].copy()
+    d16, s16 = oracle.mxfp4_to_mxfp8_row(x16, scale_ld=4)
+    assert oracle.export_mxfp8(s16, 16).shape == (100, facts["export_scale_cols_K16"]["value"])
+
+
+def test_export_floor_mutation_fails_partial_block_cases(facts):
+    """The pages' mutation check: scale columns K // 32 break exactly the
+    partial-block cases (K = 48 and K = 16); full-block shapes are unaffected."""
+    failing = 0
+    for rows, K in ((100, 48), (100, 16), (7, 48), (7, 16), (3, 80), (2, 112), (100, 64), (4, 32)):
+        x = W.c1_small()[:rows, :min(K, 48)]
+        if K > 48:
+            x = np.tile(x, (1, 3))[:, :K]
+        x = np.ascontiguousarray(x)
+        _, scale = oracle.mxfp4_to_mxfp8_row(x, scale_ld=((K + 31) // 32 + 3) // 4 * 4)
+        good = oracle.export_mxfp8(scale, K)
+        bad = F.export(scale, K, mutation="floor_cols")
+        if good.shape != bad.shape:
+            failing += 1
+        assert np.array_equal(good, F.export(scale, K))
+    assert failing == facts["export_partial_block_cases_failing_with_floor"]["value"]
+
+
+# ---------------------------------------------------------------- oracle vs brute force
+
+@pytest.mark.parametrize("name", ["c1", "c2_shuffled", "c2_natural", "c2_planted"])
+def test_oracle_matches_brute_force_bf16(name):
+    x = CORPORA[name]()
+    assert np.array_equal(oracle.fake_quantize_mxfp4(x), F.fake_quantize(x, "bf16"))
+    d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+    d1, s1 = F.row_lift(x, "bf16")
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+
+
+def test_oracle_matches_brute_force_fp32():
+    x = W.fp32_fuzz(1 << 13)
+    assert np.array_equal(oracle.fake_quantize_mxfp4(x), F.fake_quantize(x, "fp32"))
+    d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+    d1, s1 = F.row_lift(x, "fp32")
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+
+
+def test_oracle_matches_brute_force_block128():
+    row = np.concatenate([spread_row(d, b) for d in range(17) for b in (-126, -121, 3)])
+    x = np.stack([_fp32_bits_of(row), _fp32_bits_of(-row[::-1])])
+    d0, c0 = oracle.mxfp4_to_fp8_block128(x)
+    d1, c1 = F.block128(x, "fp32")
+    assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
+    xb = W.c2_planted()[:, :32]
+    xb = np.ascontiguousarray(np.tile(xb, (3, 5)))       # 192 x 160: partial tiles both ways
+    d0, c0 = oracle.mxfp4_to_fp8_block128(xb)
+    d1, c1 = F.block128(xb, "bf16")
+    assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
+
+
+@pytest.mark.parametrize("fp8", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_oracle_decode_matches_brute_force_every_byte_and_code(fp8, out):
+    data = np.tile(np.arange(256, dtype=np.uint8), (256, 1))          # row r holds every byte
+    scale = np.arange(256, dtype=np.uint8).reshape(256, 1).repeat(8, axis=1)   # row r uses code r
+    got = oracle.dequantize(data, scale, fp8=oracle.E4M3 if fp8 == "e4m3" else oracle.E5M2,
+                            out_dtype=BF16 if out == "bf16" else FP32)
+    want = F.dequantize(data, scale, "row", out, fp8)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- mutation sensitivity
+
+@pytest.mark.parametrize("mutation,where", [
+    ("clamp_low_127", "proj"),
+    ("ties_away", "proj"),
+    ("no_absorption", "row"),
+    ("tile_clamp_126", "block128"),
+])
+def test_pins_catch_planted_mistakes(mutation, where):
+    """Each planted mistake changes some output the pins compare, so the same
+    mistake in the oracle could not pass them."""
+    if where == "proj":
+        x = W.c2_planted()
+        assert not np.array_equal(F.fake_quantize(x, "bf16", mutation), oracle.fake_quantize_mxfp4(x))
+    elif where == "row":
+        x = W.c2_planted()
+        d1, s1 = F.row_lift(x, "bf16", mutation=mutation)
+        d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+        assert not (np.array_equal(d0, d1) and np.array_equal(s0, s1))
+    else:
+        row = np.concatenate([spread_row(d, -126) for d in range(6)])
+        x = _fp32_bits_of(row)[None, :]
+        d1, c1 = F.block128(x, "fp32", mutation=mutation)
+        d0, c0 = oracle.mxfp4_to_fp8_block128(x)
+        assert not (np.array_equal(d0, d1) and np.array_equal(c0, c1))
