@@ -1,0 +1,222 @@
+"""Throughput of the block-scaled weight-quantization path on one MI355X.
+
+One step = one pass of the whole path over the 8192 x 8192 bf16 weight
+(N(0, 0.02), seed 1):
+  proj      MXFP4 projection, bf16 -> bf16
+  row       direct MXFP8 rowwise lift (E4M3 payload + E8M0 codes, scale storage
+            padded to 260 columns so the export has to copy)
+  export    unpadded [8192, 256] scale export
+  block128  direct 128x128 blockwise FP8 (E4M3 payload + tile codes)
+  dec_row   decode of the rowwise payload -> bf16
+  dec_tile  decode of the blockwise payload -> bf16
+Inputs are resident in HBM before timing starts.  Six buffer sets rotate so that
+a buffer is read again only after more than 1 GB of other traffic (the
+Infinity Cache cannot serve repeated reads).  The K timed passes run
+kernel-major (each kernel K times back to back, then the next), which is the
+same work as K step-major passes; `value` is the steps' algorithmic bytes over
+their wall time, and per-kernel times come from HIP events recorded around each
+kernel's burst on the stream the kernels are launched on.
+
+python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--calibrate]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+ROWS = COLS = 8192
+SCALE_LD = 260                   # padded scale storage: ceil(K/32) = 256 plus 4 columns
+NSETS = 6
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_bf16.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "microscaling_weight_quantization_amd", "csrc", "mxq.hip")
+
+
+def algorithmic_bytes(rows: int, K: int) -> dict:
+    """Bytes each kernel must move (read + write) for a [rows, K] bf16 weight."""
+    n = rows * K
+    nb = rows * ((K + 31) // 32)
+    tiles = ((rows + 127) // 128) * ((K + 127) // 128)
+    return {
+        "proj": 2 * n + 2 * n,
+        "row": 2 * n + n + nb,
+        "export": nb + nb,
+        "block128": 2 * n + n + tiles,
+        "dec_row": n + nb + 2 * n,
+        "dec_tile": n + tiles + 2 * n,
+    }
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernels changed since."""
+    try:
+        lines = open(COUNTERS_FILE).read().splitlines()
+    except OSError:
+        return None
+    meta = dict(l.split("=", 1) for l in lines if "=" in l and not l.startswith("#"))
+    if meta.get("source_sha256_16") != kernel_source_hash():
+        return None
+    v = meta.get(f"traffic_bytes.{kernel}")
+    return int(float(v)) if v else None
+
+
+def cpu_baseline(bits, threads: int) -> dict:
+    """The CPU oracle over the same workload (one pass of every step), as is."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.fake_quantize_mxfp4(bits, threads=threads)
+    d, s = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=SCALE_LD, threads=threads)
+    c = oracle.export_mxfp8(s, bits.shape[1])
+    bd, tc = oracle.mxfp4_to_fp8_block128(bits, threads=threads)
+    oracle.dequantize(d, c, threads=threads)
+    oracle.dequantize(bd, tc, layout=oracle.TILE_128X128, threads=threads)
+    dt = time.perf_counter() - t0
+    total = sum(algorithmic_bytes(*bits.shape).values())
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} bf16 weight, one pass of all six steps "
+                      f"({dt:.1f} s wall on {threads} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+              "(rows shard with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import microscaling_weight_quantization_amd as mxq
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    mxq.load()
+    bits = W.c4_headline()
+    rows, K = bits.shape
+    nb = (K + 31) // 32
+    x0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    sets = []
+    for i in range(NSETS):
+        s = {
+            "x": x0.clone(),
+            "y": torch.empty_like(x0),
+            "data": torch.empty((rows, K), dtype=torch.uint8, device=dev),
+            "scale": torch.zeros((rows, SCALE_LD), dtype=torch.uint8, device=dev),
+            "scale_c": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
+            "bdata": torch.empty((rows, K), dtype=torch.uint8, device=dev),
+            "tc": torch.empty(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev),
+            "dec_r": torch.empty_like(x0),
+            "dec_t": torch.empty_like(x0),
+        }
+        mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
+        mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
+        mxq.mxq_mxfp4_to_fp8_block128(s["x"], s["bdata"], s["tc"])
+        sets.append(s)
+    del x0
+    torch.cuda.synchronize()
+
+    names = ["proj", "row", "export", "block128", "dec_row", "dec_tile"]
+    launches = {
+        "proj": lambda s: mxq.mxq_fake_quantize_mxfp4(s["x"], s["y"]),
+        "row": lambda s: mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"]),
+        "export": lambda s: mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"]),
+        "block128": lambda s: mxq.mxq_mxfp4_to_fp8_block128(s["x"], s["bdata"], s["tc"]),
+        "dec_row": lambda s: mxq.mxq_dequantize(s["data"], s["scale_c"], out=s["dec_r"]),
+        "dec_tile": lambda s: mxq.mxq_dequantize(s["bdata"], s["tc"], layout=mxq.MXQ_SCALE_TILE_128X128,
+                                                 out=s["dec_t"]),
+    }
+    # kernel -> buffer-set offset inside a step, so each x is re-read only two steps later
+    offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5}
+
+    # The timed region runs K whole passes kernel-major: each kernel is launched K
+    # times back to back (rotating buffer sets) between two HIP events on the
+    # launch stream, so an event pair brackets K launches and its average is the
+    # kernel's own duration plus the small gap between dispatches.
+    stream = torch.cuda.current_stream(dev)
+    bursts = {}
+
+    def run(i0: int, k: int, timed: bool):
+        for n in names:
+            if timed:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            for i in range(i0, i0 + k):
+                launches[n](sets[(i + offset[n]) % NSETS])
+            if timed:
+                b.record(stream)
+                bursts[n] = (a, b)
+
+    run(0, args.warmup, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.warmup, args.steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.calibrate:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nbytes = algorithmic_bytes(rows, K)
+    ms_per_step = wall * 1e3 / args.steps
+    total = sum(nbytes.values())
+    kernels = {}
+    for n in names:
+        a, b = bursts[n]
+        us = 1e3 * a.elapsed_time(b) / args.steps
+        gbs = nbytes[n] / (us * 1e-6) / 1e9
+        kernels[n] = {"us": round(us, 2), "bytes": nbytes[n], "GB/s": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dominant = max(names, key=lambda n: kernels[n]["us"])
+    rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
+          "unit": "GB/s", "frac": kernels[dominant]["frac"], "traffic": read_traffic(dominant)}
+    out = {
+        "metric": "GB/s and % HBM peak, MXFP4 proj + MXFP8-row/128x128 at 8192^2 bf16",
+        "value": round(total / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int16",
+        "data": "synthetic",
+        "config": {"workload": "8192x8192 bf16 weight, N(0,0.02) seed 1: proj + row (scale_ld 260) + export "
+                               "+ block128 + decode(row) + decode(tile)",
+                   "bytes_per_step": total, "buffer_sets": NSETS},
+        "roofline": rl,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(bits, threads=min(16, os.cpu_count() or 1))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) block-scaled weight-quantization library.
+ *
+ * Five entry points make up the path:
+ *   mxq_fake_quantize_mxfp4     per-1x32 MXFP4 projection, output in the input dtype
+ *   mxq_mxfp4_to_mxfp8_row      direct MXFP8 rowwise lift (E4M3 payload + E8M0 codes)
+ *   mxq_mxfp4_to_fp8_block128   direct 128x128 blockwise FP8 (E4M3 payload + tile codes)
+ *   mxq_export_mxfp8            unpadded (*shape[:-1], ceil(K/32)) E8M0 scale export
+ *   mxq_dequantize              FP8 payload + E8M0 codes -> bf16 / fp32
+ *
+ * Sources, by page title and section:
+ *   [QAT] "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8 block-scaling recipes"
+ *         (TransformerEngine pull request 3264): Description, Test results (B200),
+ *         Known limitations.
+ *   [EXP] "MXFP8TensorStorage.export_components()" (TransformerEngine pull request
+ *         3790): Description.
+ *
+ * Conventions for every entry point:
+ *   - A matrix is [rows, K]: leading dimensions are flattened into rows and the
+ *     last dimension K is contiguous.  Every ld / scale_ld / tile_ld is a row
+ *     stride counted in elements of that buffer.
+ *   - All pointers are device pointers.  The caller owns every buffer; the
+ *     library never allocates, frees or keeps a pointer, holds no state and is
+ *     safe to call from several host threads.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is asynchronous.
+ *     Argument errors are detected on the host and returned before anything is
+ *     enqueued; no kernel asserts on the device.
+ *   - rows == 0 or K == 0 returns MXQ_OK and enqueues nothing.
+ *   - Results are bit-exact and do not depend on the build's floating-point
+ *     flags: every step is integer arithmetic.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of a high-precision buffer.  fp16 exists only to be rejected:
+ * the MXFP4 grid exceeds its range ([QAT] Description, STE paragraph, and
+ * Known limitations). */
+typedef enum { MXQ_BF16 = 0, MXQ_FP32 = 1, MXQ_FP16 = 2 } mxq_dtype;
+
+/* FP8 payload format: OCP E4M3 "FN" (bias 7, max 448, NaN = S.1111.111, no Inf)
+ * or E5M2 (bias 15, IEEE Inf/NaN) -- the torch.float8_e4m3fn / float8_e5m2 views
+ * of [EXP] Description. */
+typedef enum { MXQ_E4M3 = 0, MXQ_E5M2 = 1 } mxq_fp8;
+
+/* Where a payload element's E8M0 code lives: one per 1x32 block of a row
+ * (scale[r*scale_ld + c/32]) or one per 128x128 tile anchored at (0,0)
+ * (scale[(r/128)*scale_ld + c/128]). */
+typedef enum { MXQ_SCALE_ROW_1X32 = 0, MXQ_SCALE_TILE_128X128 = 1 } mxq_scale_layout;
+
+/* Status codes. */
+enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = 1,             /* a required pointer is NULL (non-empty shape) */
+  MXQ_ERR_SHAPE = 2,            /* negative dims, ld < K, scale_ld / tile_ld too small, or too large */
+  MXQ_ERR_DTYPE = 3,            /* fp16 or an unknown dtype / format / layout */
+  MXQ_ERR_NO_ROWWISE_DATA = 4,  /* export without payload or scale storage ([EXP]: ValueError) */
+  MXQ_ERR_ALIAS = 5,            /* an output overlaps an input (other than the allowed exact in-place) */
+  MXQ_ERR_HIP = 6               /* the HIP runtime refused a launch */
+};
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* mxq_status_string(int status);
+
+/*
+ * MXFP4 projection ("fake quantization"), [QAT] Description, conversion mode 1.
+ * For each 1x32 block of a row (the last block of a row may be shorter and
+ * keeps its own scale, [EXP] Description): amax = max |x|; scale exponent
+ * e = clamp(ceil(log2(amax/6)), -126, 125), taken from amax's bit pattern;
+ * y = RTNE_E2M1(x / 2^e) * 2^e, i.e. x rounded to the nearest of
+ * {0, .5, 1, 1.5, 2, 3, 4, 6} * 2^e with ties to the even E2M1 code, sign kept
+ * (including -0), saturating at 6 * 2^e ([QAT] Known limitations: amax above
+ * 6*2^125 saturates at the cap).  A block holding any Inf or NaN becomes all
+ * canonical quiet NaN (0x7FC0 / 0x7FC00000) ([QAT] Test results: non-finite
+ * block poisoning).  amax = 0 uses e = -126.
+ *   x    [rows, K] bf16 or fp32, row stride ld_x >= K
+ *   y    [rows, K] same dtype, row stride ld_y >= K.  y == x with ld_y == ld_x
+ *        (in place) is allowed; any other overlap is MXQ_ERR_ALIAS.
+ *   dt   MXQ_BF16 or MXQ_FP32 (MXQ_FP16 -> MXQ_ERR_DTYPE)
+ */
+int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y,
+                            int64_t rows, int64_t K, mxq_dtype dt, hipStream_t stream);
+
+/*
+ * Direct MXFP8 rowwise lift, [QAT] Description, conversion mode 2 ("fixed-shift-6
+ * lift ... scale clamps at UE8M0 code 0 with exact payload absorption").
+ * From each block's MXFP4 decomposition x ~ p * 2^e of the master weight (the
+ * same e and p as mxq_fake_quantize_mxfp4): scale code = max(e + 121, 0), i.e.
+ * scale 2^(e-6) clamped at 2^-127, and payload = E4M3(p * 2^min(6, e+127)),
+ * which is always exact.  Decoding payload * 2^(code-127) gives back the
+ * projection bit for bit.  A poisoned block gets code 255 and payload 0x7F.
+ *   x         [rows, K] bf16 or fp32, row stride ld_x >= K
+ *   data      [rows, K] uint8 E4M3 payload, contiguous (row stride K)
+ *   scale     [rows, scale_ld] uint8 E8M0 codes, scale_ld >= ceil(K/32); columns
+ *             j >= ceil(K/32) (padding) are not written
+ *   data and scale must not overlap x or each other (MXQ_ERR_ALIAS).
+ */
+int mxq_mxfp4_to_mxfp8_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                           uint8_t* data, uint8_t* scale, int64_t scale_ld, hipStream_t stream);
+
+/*
+ * Direct 128x128 blockwise FP8, [QAT] Description, conversion mode 2 ("per-tile
+ * exponent folding: tile scale 2^(max fp4 exp - 6) clamped at 2^-127, RTNE onto
+ * E4M3 incl. subnormals").  Tiles are anchored at (0,0) and truncated at the
+ * edges.  Per tile: M = max e over its finite 1x32 blocks (-126 if none);
+ * S = max(M - 6, -127); tile code = S + 127; payload = RTNE_E4M3(p * 2^(e - S))
+ * with E4M3 subnormals and ties to even.  Exact while the tile's exponent
+ * spread M - e is at most 14 ([QAT] Test results).  Poisoned blocks are left out
+ * of M and get payload 0x7F.
+ *   x          [rows, K] bf16 or fp32, row stride ld_x >= K
+ *   data       [rows, K] uint8 E4M3 payload, contiguous (row stride K)
+ *   tile_code  [ceil(rows/128), tile_ld] uint8 E8M0 codes, tile_ld >= ceil(K/128)
+ *   data and tile_code must not overlap x or each other (MXQ_ERR_ALIAS).
+ */
+int mxq_mxfp4_to_fp8_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                              uint8_t* data, uint8_t* tile_code, int64_t tile_ld, hipStream_t stream);
+
+/*
+ * Unpadded export of MXFP8 rowwise scales, [EXP] Description: scale_inv holds
+ * E8M0 codes with shape (*shape[:-1], ceil(K/32)), without padding; a partial
+ * last block keeps its own scale.  Copies the first ceil(K/32) columns of each
+ * row of the padded storage into a compact [rows, ceil(K/32)] array.  The
+ * payload needs no copy: it is `data` viewed with the tensor's shape.
+ *   data           the payload (only checked for presence)
+ *   scale_storage  [rows, scale_ld] uint8, scale_ld >= ceil(K/32)
+ *   scale_out      [rows, ceil(K/32)] uint8, contiguous
+ * data == NULL or scale_storage == NULL -> MXQ_ERR_NO_ROWWISE_DATA ([EXP]: a
+ * tensor without row-scaled data raises ValueError).  scale_out == scale_storage
+ * with scale_ld == ceil(K/32) is the view case and returns MXQ_OK without work;
+ * any other overlap is MXQ_ERR_ALIAS.
+ */
+int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t rows, int64_t K,
+                     int64_t scale_ld, uint8_t* scale_out, hipStream_t stream);
+
+/*
+ * Decode FP8 payload with E8M0 codes: out = RNE_out(FP8(q) * 2^(code - 127)).
+ * Code 0 is 2^-127 and code 255 is NaN ([QAT] Description: decode UE8M0 code 0
+ * as 2^-127 and code 255 as NaN; Test results: planted extreme codes).  A NaN
+ * payload or code 255 gives canonical quiet NaN; an E5M2 infinity stays
+ * infinite; values beyond the output range round to Inf.
+ *   data     [rows, K] uint8 payload, contiguous (row stride K)
+ *   scale    E8M0 codes: [rows, scale_ld] for MXQ_SCALE_ROW_1X32 (scale_ld >=
+ *            ceil(K/32)) or [ceil(rows/128), scale_ld] for MXQ_SCALE_TILE_128X128
+ *            (scale_ld >= ceil(K/128))
+ *   out      [rows, K] bf16 or fp32, row stride ld_out >= K; must not overlap
+ *            data or scale
+ */
+int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                   mxq_fp8 fmt, mxq_scale_layout layout, void* out, int64_t ld_out, mxq_dtype out_dt,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

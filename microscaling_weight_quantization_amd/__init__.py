@@ -1,0 +1,223 @@
+"""Python binding of the gfx950 block-scaled weight-quantization library (libmxq.so).
+
+The ``mxq_*`` functions carry the names of the C entry points in
+``include/mxq.h`` and only marshal arguments: tensors become device pointers,
+row strides and sizes, and the call is enqueued on torch's current stream.
+Every step of the computation runs in the HIP kernels of ``csrc/mxq.hip``;
+there is no fallback of any kind, and a missing library raises.
+
+PyTorch is used for device memory and streams only.  A [rows, K] operand is a
+tensor whose last dimension is contiguous; leading dimensions of a contiguous
+tensor are flattened into rows.
+
+Sources (page title, section): "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8
+block-scaling recipes" -- Description, Test results, Known limitations; and
+"MXFP8TensorStorage.export_components()" -- Description.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import build as _build
+
+MXQ_BF16, MXQ_FP32, MXQ_FP16 = 0, 1, 2
+MXQ_E4M3, MXQ_E5M2 = 0, 1
+MXQ_SCALE_ROW_1X32, MXQ_SCALE_TILE_128X128 = 0, 1
+MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_DTYPE, MXQ_ERR_NO_ROWWISE_DATA, MXQ_ERR_ALIAS, MXQ_ERR_HIP = range(7)
+
+ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mxfp8_row",
+                "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize")
+
+_libs = {}
+_lock = threading.Lock()
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"mxq status {status}: {text}")
+        self.status = status
+
+
+def load(name: str = "libmxq.so") -> ctypes.CDLL:
+    """Load a built variant of the library (build it first: ``__graft_entry__.build()``)."""
+    with _lock:
+        if name in _libs:
+            return _libs[name]
+        path = _build.library_path(name)
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build() "
+                                    "(python -m microscaling_weight_quantization_amd.build)")
+        L = ctypes.CDLL(path)
+        i64, vp, i32, u8p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+        L.mxq_status_string.argtypes = [i32]
+        L.mxq_status_string.restype = ctypes.c_char_p
+        L.mxq_fake_quantize_mxfp4.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp]
+        L.mxq_mxfp4_to_mxfp8_row.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
+        L.mxq_mxfp4_to_fp8_block128.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
+        L.mxq_export_mxfp8.argtypes = [u8p, u8p, i64, i64, i64, u8p, vp]
+        L.mxq_dequantize.argtypes = [u8p, u8p, i64, i64, i64, i32, i32, vp, i64, i32, vp]
+        for n in ENTRY_POINTS[1:]:
+            getattr(L, n).restype = i32
+        _libs[name] = L
+        return L
+
+
+def _check(L, rc: int):
+    if rc != MXQ_OK:
+        raise MxqError(rc, L.mxq_status_string(rc).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MXQ_BF16
+    if t.dtype == torch.float32:
+        return MXQ_FP32
+    if t.dtype == torch.float16:
+        return MXQ_FP16
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32 expected")
+
+
+def _matrix(t: torch.Tensor):
+    """(pointer, rows, K, row stride in elements) of a tensor with a contiguous last dim."""
+    if t.dim() == 0:
+        raise ValueError("a matrix needs at least one dimension")
+    if t.dim() == 1:
+        t = t.view(1, -1)
+    if t.dim() > 2:
+        if not t.is_contiguous():
+            raise ValueError("leading dimensions can only be flattened for a contiguous tensor")
+        t = t.view(-1, t.shape[-1])
+    rows, K = t.shape
+    if K > 1 and t.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    ld = t.stride(0) if rows > 1 else K
+    return t.data_ptr(), rows, K, ld
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+# ---- the C entry points, one to one ---------------------------------------------------
+
+def mxq_fake_quantize_mxfp4(x: torch.Tensor, y: Optional[torch.Tensor] = None, lib: str = "libmxq.so") -> torch.Tensor:
+    """MXFP4 projection of x (bf16 / fp32) into y (same dtype; y may be x)."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have x's dtype and shape")
+    px, rows, K, ldx = _matrix(x)
+    py, _, _, ldy = _matrix(y)
+    _check(L, L.mxq_fake_quantize_mxfp4(px, ldx, py, ldy, rows, K, dt, _stream(x)))
+    return y
+
+
+def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                           scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+    """Direct MXFP8 rowwise lift -> (payload uint8 [rows, K], E8M0 codes uint8 [rows, scale_ld])."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    px, rows, K, ldx = _matrix(x)
+    nb = (K + 31) // 32
+    if scale is None:
+        scale = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=x.device)
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    pd, _, _, ldd = _matrix(data)
+    ps, _, sld, ld_s = _matrix(scale)
+    if rows * K and (ldd != K or data.numel() != rows * K):
+        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    _check(L, L.mxq_mxfp4_to_mxfp8_row(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    return data, scale
+
+
+def mxq_mxfp4_to_fp8_block128(x: torch.Tensor, data: Optional[torch.Tensor] = None,
+                              tile_code: Optional[torch.Tensor] = None, lib: str = "libmxq.so"):
+    """Direct 128x128 blockwise FP8 -> (payload uint8 [rows, K], tile codes uint8 [ceil(rows/128), tile_ld])."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    px, rows, K, ldx = _matrix(x)
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if tile_code is None:
+        tile_code = torch.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=x.device)
+    pd, _, _, ldd = _matrix(data)
+    pt, trows, tcols, ldt = _matrix(tile_code)
+    if rows * K and (ldd != K or data.numel() != rows * K):
+        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    _check(L, L.mxq_mxfp4_to_fp8_block128(px, ldx, rows, K, dt, pd, pt, ldt, _stream(x)))
+    return data, tile_code
+
+
+def mxq_export_mxfp8(data: Optional[torch.Tensor], scale_storage: Optional[torch.Tensor], K: int,
+                     scale_out: Optional[torch.Tensor] = None, lib: str = "libmxq.so") -> torch.Tensor:
+    """Compact [rows, ceil(K/32)] copy of padded E8M0 scale storage (rows, scale_ld)."""
+    L = load(lib)
+    if data is None or scale_storage is None:
+        rc = L.mxq_export_mxfp8(None, None, 0, K, 0, None, None)
+        _check(L, rc)
+    ps, rows, sld, ld_s = _matrix(scale_storage)
+    nb = (K + 31) // 32
+    if scale_out is None:
+        scale_out = torch.empty((rows, nb), dtype=torch.uint8, device=scale_storage.device)
+    po, _, _, _ = _matrix(scale_out)
+    _check(L, L.mxq_export_mxfp8(data.data_ptr(), ps, rows, K, ld_s, po, _stream(scale_storage)))
+    return scale_out
+
+
+def mxq_dequantize(data: torch.Tensor, scale: torch.Tensor, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3,
+                   out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                   lib: str = "libmxq.so") -> torch.Tensor:
+    """Decode FP8 payload bytes with E8M0 codes into bf16 / fp32."""
+    L = load(lib)
+    pd, rows, K, ldd = _matrix(data)
+    if rows * K and ldd != K:
+        raise ValueError("payload must be contiguous")
+    ps, srows, scols, lds = _matrix(scale)
+    if out is None:
+        out = torch.empty((rows, K), dtype=out_dtype, device=data.device)
+    po, _, _, ldo = _matrix(out)
+    _check(L, L.mxq_dequantize(pd, ps, lds, rows, K, fmt, layout, po, ldo,
+                               _dtype_code(out), _stream(data)))
+    return out
+
+
+# ---- convenience layer ------------------------------------------------------------------
+
+class MXFP8Components(NamedTuple):
+    """FP8 values and unpadded E8M0 scales of an MXFP8 rowwise tensor."""
+    data: torch.Tensor        # payload viewed as float8 with the tensor's shape
+    scale_inv: torch.Tensor   # uint8 E8M0 codes, shape (*shape[:-1], ceil(K/32))
+
+
+def export_components(data: Optional[torch.Tensor], scale_storage: Optional[torch.Tensor], shape,
+                      fp8_dtype: torch.dtype = torch.float8_e4m3fn, lib: str = "libmxq.so") -> MXFP8Components:
+    """Export values and scales in a storage-independent layout.  The values are
+    always a view of `data`; the scales are a view when the storage has exactly
+    ceil(K/32) columns and a copy (made by the library's kernel) when it is
+    padded.  Missing row-scaled data raises ValueError."""
+    if data is None or scale_storage is None:
+        raise ValueError("tensor has no row-scaled data to export")
+    shape = tuple(shape)
+    K = shape[-1]
+    nb = (K + 31) // 32
+    values = data.view(fp8_dtype).view(shape)
+    scale2d = scale_storage.view(-1, scale_storage.shape[-1]) if scale_storage.dim() != 2 else scale_storage
+    if scale2d.shape[1] == nb:
+        scale_inv = scale2d
+    else:
+        scale_inv = mxq_export_mxfp8(data, scale2d, K, lib=lib)
+    return MXFP8Components(values, scale_inv.view(*shape[:-1], nb))
+
+
+def fake_quantize_mxfp4(t: torch.Tensor, lib: str = "libmxq.so") -> torch.Tensor:
+    if t.dtype == torch.float16:
+        raise TypeError("fp16 is not supported: the MXFP4 grid exceeds fp16's range")
+    return mxq_fake_quantize_mxfp4(t, lib=lib)

@@ -1,0 +1,93 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry point
+include/mxq.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import microscaling_weight_quantization_amd as mxq
+from microscaling_weight_quantization_amd import build as B
+
+HEADER = os.path.join(B.ROOT, "include", "mxq.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(mxq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if B.stale():
+        B.build(["libmxq.so"])
+    return mxq.load()
+
+
+def test_header_declares_the_five_entry_points():
+    assert declared() == sorted(["mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mxfp8_row",
+                                 "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(mxq_\w+)$", out, flags=re.M))
+    assert set(declared()) <= exported
+    for name in declared():
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = f'#include "mxq.h"\nint main(void) {{ return (int)(mxq_status_string != 0) - 1; }}\n'
+    r = subprocess.run(["gcc", "-fsyntax-only", "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER),
+                        "-I", "/opt/rocm/include", "-x", "c", "-"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.mxq_status_string(code)
+    assert b"fp16" in lib.mxq_status_string(mxq.MXQ_ERR_DTYPE)
+    assert lib.mxq_status_string(99) == b"unknown status"
+
+
+def test_host_validation_without_a_gpu(lib):
+    """Every one of these returns before anything is enqueued."""
+    P = ctypes.c_void_p
+    fake = P(0x100000)
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, fake, 64, 4, 64, mxq.MXQ_FP16, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, fake, 64, 4, 64, 7, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_fake_quantize_mxfp4(None, 64, fake, 64, 4, 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_fake_quantize_mxfp4(fake, 32, P(0x200000), 64, 4, 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, fake, 64, -1, 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_fake_quantize_mxfp4(None, 0, None, 0, 0, 64, mxq.MXQ_BF16, None) == mxq.MXQ_OK   # empty
+    assert lib.mxq_fake_quantize_mxfp4(None, 0, None, 0, 4, 0, mxq.MXQ_FP32, None) == mxq.MXQ_OK
+    # partial overlap between x and y
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, P(0x100002), 64, 4, 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_ALIAS
+    # in place with a different stride is an overlap, not in-place
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, fake, 128, 4, 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_ALIAS
+    # row lift: scale storage too narrow, outputs overlapping
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, mxq.MXQ_BF16, P(0x200000), P(0x300000), 1, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, mxq.MXQ_BF16, P(0x200000), P(0x200010), 2, None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, mxq.MXQ_BF16, P(0x100040), P(0x300000), 2, None) == mxq.MXQ_ERR_ALIAS
+    # block128: tile_ld too small
+    assert lib.mxq_mxfp4_to_fp8_block128(fake, 256, 4, 256, mxq.MXQ_FP32, P(0x200000), P(0x300000), 1, None) == mxq.MXQ_ERR_SHAPE
+    # export: no row-scaled data, the view case, bad stride
+    assert lib.mxq_export_mxfp8(None, fake, 4, 64, 2, P(0x200000), None) == mxq.MXQ_ERR_NO_ROWWISE_DATA
+    assert lib.mxq_export_mxfp8(fake, None, 4, 64, 2, P(0x200000), None) == mxq.MXQ_ERR_NO_ROWWISE_DATA
+    assert lib.mxq_export_mxfp8(P(0x500000), fake, 4, 64, 2, fake, None) == mxq.MXQ_OK
+    assert lib.mxq_export_mxfp8(P(0x500000), fake, 4, 64, 1, P(0x200000), None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_export_mxfp8(P(0x500000), fake, 4, 64, 4, P(0x100001), None) == mxq.MXQ_ERR_ALIAS
+    # dequantize: bad format / layout / dtype, narrow scale
+    assert lib.mxq_dequantize(fake, P(0x200000), 2, 4, 64, 5, 0, P(0x300000), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_dequantize(fake, P(0x200000), 2, 4, 64, 0, 9, P(0x300000), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_dequantize(fake, P(0x200000), 2, 4, 64, 0, 0, P(0x300000), 64, mxq.MXQ_FP16, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_dequantize(fake, P(0x200000), 1, 4, 64, 0, 0, P(0x300000), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_dequantize(fake, P(0x200000), 1, 4, 64, 0, 1, P(0x100010), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_ALIAS
+
+
+def test_binding_raises_without_the_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(B, "library_path", lambda name="libmxq.so": str(tmp_path / name))
+    with pytest.raises(FileNotFoundError):
+        mxq.load("libmxq_missing.so")

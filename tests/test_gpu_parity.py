@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for bit.
+
+Tolerance is 0: every payload byte, scale code and output bit must match,
+NaNs included (both sides write the canonical quiet NaN).  Inputs are the
+seeded workloads of ``workloads`` -- the same host bits feed the oracle and the
+device copy.  Sizes: the small and exhaustive corpora, the 4096 x 4096 spread
+sweep and the 8192 x 8192 headline weight in full; the 28672 x 8192 /
+8192 x 28672 MLP weights are launched in full and compared on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_weight_quantization_amd as mxq
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+THREADS = 16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mxq.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(bits: np.ndarray, device) -> torch.Tensor:
+    if bits.dtype == np.uint16:
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    if bits.dtype == np.uint32:
+        return torch.from_numpy(bits.view(np.int32)).to(device).view(torch.float32)
+    return torch.from_numpy(bits).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    t = t.contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def assert_bits(got: np.ndarray, want: np.ndarray, what: str):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches; first at {i}: got {got[i]:#x} want {want[i]:#x}")
+
+
+def out_dtype_of(bits):
+    return (torch.bfloat16, oracle.BF16) if bits.dtype == np.uint16 else (torch.float32, oracle.FP32)
+
+
+def check_all(bits: np.ndarray, dev, scale_ld=None, tile=True, lib="libmxq.so"):
+    """Projection, row lift (+ padded scale storage), export, decode and the
+    128x128 fold of one weight, each against the oracle."""
+    x = to_dev(bits, dev)
+    rows, K = bits.shape
+    nb = (K + 31) // 32
+    scale_ld = scale_ld or nb
+    tdt, odt = out_dtype_of(bits)
+    assert_bits(to_host(mxq.mxq_fake_quantize_mxfp4(x, lib=lib)), oracle.fake_quantize_mxfp4(bits, threads=THREADS),
+                "projection")
+    scale = torch.full((rows, scale_ld), 0xA5, dtype=torch.uint8, device=dev)
+    data, scale = mxq.mxq_mxfp4_to_mxfp8_row(x, scale=scale, lib=lib)
+    wd, ws = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=scale_ld, threads=THREADS, fill=0xA5)
+    assert_bits(to_host(data), wd, "row payload")
+    assert_bits(to_host(scale), ws, "row scale codes (padding untouched)")
+    comp = mxq.export_components(data, scale, (rows, K), lib=lib)
+    assert_bits(to_host(comp.scale_inv), oracle.export_mxfp8(ws, K), "exported scales")
+    assert comp.data.dtype == torch.float8_e4m3fn and comp.data.data_ptr() == data.data_ptr()
+    dec = mxq.mxq_dequantize(data, comp.scale_inv, out_dtype=tdt, lib=lib)
+    assert_bits(to_host(dec), oracle.dequantize(wd, ws[:, :nb], out_dtype=odt, threads=THREADS), "row decode")
+    if tile:
+        bd, tc = mxq.mxq_mxfp4_to_fp8_block128(x, lib=lib)
+        wbd, wtc = oracle.mxfp4_to_fp8_block128(bits, threads=THREADS)
+        assert_bits(to_host(bd), wbd, "128x128 payload")
+        assert_bits(to_host(tc), wtc, "tile codes")
+        dec = mxq.mxq_dequantize(bd, tc, layout=mxq.MXQ_SCALE_TILE_128X128, out_dtype=tdt, lib=lib)
+        assert_bits(to_host(dec), oracle.dequantize(wbd, wtc, layout=oracle.TILE_128X128, out_dtype=odt,
+                                                    threads=THREADS), "tile decode")
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_c1_small(dev):
+    check_all(W.c1_small(), dev, scale_ld=4)
+
+
+@pytest.mark.parametrize("natural", [False, True])
+def test_c2_exhaustive(dev, natural):
+    check_all(W.c2_exhaustive(natural=natural), dev, scale_ld=4)
+
+
+def test_c2_planted(dev):
+    check_all(W.c2_planted(), dev)
+
+
+def test_fp32_fuzz(dev):
+    check_all(W.fp32_fuzz(1 << 18).reshape(-1, 256), dev)
+
+
+def test_c3_spread_sweep(dev):
+    check_all(W.c3_spread(), dev)
+
+
+def test_c4_headline(dev):
+    check_all(W.c4_headline(), dev)
+
+
+def _sampled_rows(rows, n, seed):
+    g = np.random.default_rng(seed)
+    pick = np.unique(np.concatenate([[0, 1, rows - 1], g.choice(rows, n, replace=False)]))
+    return pick
+
+
+@pytest.mark.parametrize("which", ["up", "down", "up_master"])
+def test_c5_mlp_sampled(dev, which):
+    """Full-size launches; outputs compared on sampled rows (and whole 128-row
+    tile bands for the blockwise fold).  Scale storage padded by 4 columns so
+    the export takes the copy path."""
+    bits = W.c5_mlp(which)
+    rows, K = bits.shape
+    nb = (K + 31) // 32
+    x = to_dev(bits, dev)
+    tdt, odt = out_dtype_of(bits)
+    y = to_host(mxq.mxq_fake_quantize_mxfp4(x))
+    data, scale = mxq.mxq_mxfp4_to_mxfp8_row(x, scale_ld=nb + 4)
+    out = to_host(mxq.mxq_export_mxfp8(data, scale, K))
+    dec = to_host(mxq.mxq_dequantize(data, torch.from_numpy(out).to(dev), out_dtype=tdt))
+    data, scale = to_host(data), to_host(scale)
+    pick = _sampled_rows(rows, 384, 7)
+    sub = np.ascontiguousarray(bits[pick])
+    assert_bits(y[pick], oracle.fake_quantize_mxfp4(sub, threads=THREADS), "projection (sampled rows)")
+    wd, ws = oracle.mxfp4_to_mxfp8_row(sub, scale_ld=nb + 4, threads=THREADS)
+    assert_bits(data[pick], wd, "row payload (sampled rows)")
+    assert_bits(scale[pick][:, :nb], ws[:, :nb], "row codes (sampled rows)")
+    assert_bits(out[pick], ws[:, :nb], "export (sampled rows)")
+    assert_bits(dec, y, "decode of the row lift == projection (all rows)")
+    if which != "up_master":
+        bd, tc = mxq.mxq_mxfp4_to_fp8_block128(x)
+        bd, tc = to_host(bd), to_host(tc)
+        for band in (0, rows // 128 // 2, rows // 128 - 1):
+            sl = slice(band * 128, band * 128 + 128)
+            wbd, wtc = oracle.mxfp4_to_fp8_block128(np.ascontiguousarray(bits[sl]), threads=THREADS)
+            assert_bits(bd[sl], wbd, f"128x128 payload (band {band})")
+            assert_bits(tc[band:band + 1], wtc, f"tile codes (band {band})")
+
+
+# ------------------------------------------------------------------ invariants on the device
+
+def test_decode_of_row_is_projection_c4(dev):
+    """The pages' invariant, checked on the device at the headline size."""
+    x = to_dev(W.c4_headline(), dev)
+    y = mxq.mxq_fake_quantize_mxfp4(x)
+    data, scale = mxq.mxq_mxfp4_to_mxfp8_row(x)
+    dec = mxq.mxq_dequantize(data, scale)
+    assert torch.equal(dec.view(torch.int16), y.view(torch.int16))
+
+
+# ------------------------------------------------------------------ edges
+
+@pytest.mark.parametrize("K", [1, 7, 8, 16, 31, 33, 48, 100, 130, 257, 2049])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_ragged_shapes(dev, K, dtype):
+    g = np.random.default_rng(K)
+    rows = 131
+    if dtype == "bf16":
+        flat = np.tile(W.c2_exhaustive().reshape(-1), (rows * K) // 65536 + 1)
+    else:
+        flat = W.fp32_fuzz(((rows * K + 31) // 32) * 32).reshape(-1)
+    bits = np.ascontiguousarray(flat[: rows * K].reshape(rows, K))
+    check_all(bits, dev, scale_ld=(K + 31) // 32 + int(g.integers(0, 3)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_strided_and_misaligned_views(dev, dtype):
+    """ld > K and base pointers one element off the 16-byte grid."""
+    base = W.c2_planted() if dtype == "bf16" else W.fp32_fuzz(64 * 200).reshape(64, 200)
+    big = to_dev(np.ascontiguousarray(np.tile(base, (1, 4))), dev)    # wider than K + 3
+    K = 96
+    for off in (0, 1, 3):
+        view = big[:, off:off + K]                                     # row stride 3 * width
+        bits = to_host(view)
+        assert view.stride(0) > K
+        assert_bits(to_host(mxq.mxq_fake_quantize_mxfp4(view)), oracle.fake_quantize_mxfp4(bits), f"proj off={off}")
+        d, s = mxq.mxq_mxfp4_to_mxfp8_row(view)
+        wd, ws = oracle.mxfp4_to_mxfp8_row(bits)
+        assert_bits(to_host(d), wd, f"row off={off}")
+        assert_bits(to_host(s), ws, f"codes off={off}")
+        bd, tc = mxq.mxq_mxfp4_to_fp8_block128(view)
+        wbd, wtc = oracle.mxfp4_to_fp8_block128(bits)
+        assert_bits(to_host(bd), wbd, f"block128 off={off}")
+        assert_bits(to_host(tc), wtc, f"tile codes off={off}")
+        y = torch.empty((64, 2 * K), dtype=view.dtype, device=dev)[:, 1:K + 1]   # misaligned strided output
+        mxq.mxq_fake_quantize_mxfp4(view, y)
+        assert_bits(to_host(y), oracle.fake_quantize_mxfp4(bits), f"proj into strided y off={off}")
+
+
+def test_in_place_projection(dev):
+    bits = W.c1_small()
+    x = to_dev(bits, dev)
+    mxq.mxq_fake_quantize_mxfp4(x, x)
+    assert_bits(to_host(x), oracle.fake_quantize_mxfp4(bits), "in-place projection")
+
+
+def test_empty_shapes(dev):
+    for shape in ((0, 32), (5, 0), (0, 0)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        assert mxq.mxq_fake_quantize_mxfp4(x).shape == shape
+        d, s = mxq.mxq_mxfp4_to_mxfp8_row(x)
+        assert d.shape == shape
+        bd, tc = mxq.mxq_mxfp4_to_fp8_block128(x)
+        assert bd.shape == shape
+
+
+def test_errors(dev):
+    x = torch.zeros((4, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(mxq.MxqError) as e:
+        mxq.mxq_fake_quantize_mxfp4(x)
+    assert e.value.status == mxq.MXQ_ERR_DTYPE
+    with pytest.raises(TypeError):
+        mxq.fake_quantize_mxfp4(x)
+    xb = torch.zeros((4, 64), dtype=torch.bfloat16, device=dev)
+    buf = torch.zeros((4, 96), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(mxq.MxqError) as e:      # partial overlap of x and y
+        mxq.mxq_fake_quantize_mxfp4(buf[:, :64], buf[:, 1:65])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
+    with pytest.raises(mxq.MxqError) as e:      # scale storage narrower than ceil(K/32)
+        mxq.mxq_mxfp4_to_mxfp8_row(xb, scale=torch.zeros((4, 1), dtype=torch.uint8, device=dev))
+    assert e.value.status == mxq.MXQ_ERR_SHAPE
+    with pytest.raises(ValueError):
+        mxq.export_components(None, None, (4, 64))
+
+
+def test_decode_every_byte_and_code(dev):
+    """Planted payloads and codes: every (code, byte) pair, both FP8 formats,
+    both output dtypes, both scale layouts."""
+    data = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    codes_row = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 8, axis=1)
+    dd, dr = to_dev(data, dev), to_dev(codes_row, dev)
+    for fmt_dev, fmt_orc in ((mxq.MXQ_E4M3, oracle.E4M3), (mxq.MXQ_E5M2, oracle.E5M2)):
+        for tdt, odt in ((torch.bfloat16, oracle.BF16), (torch.float32, oracle.FP32)):
+            got = to_host(mxq.mxq_dequantize(dd, dr, fmt=fmt_dev, out_dtype=tdt))
+            assert_bits(got, oracle.dequantize(data, codes_row, fp8=fmt_orc, out_dtype=odt), f"decode {fmt_orc} {odt}")
+    # tile layout: 256 rows = 2 tile rows, 256 cols = 2 tile cols -> 4 codes
+    tcodes = np.array([[0, 255], [1, 254]], dtype=np.uint8)
+    got = to_host(mxq.mxq_dequantize(dd, to_dev(tcodes, dev), layout=mxq.MXQ_SCALE_TILE_128X128, out_dtype=torch.float32))
+    assert_bits(got, oracle.dequantize(data, tcodes, layout=oracle.TILE_128X128, out_dtype=oracle.FP32), "tile decode")
+
+
+@pytest.mark.parametrize("variant", ["libmxq_fastmath.so", "libmxq_o1.so"])
+def test_build_variants_identical_bits(dev, variant):
+    """Same source built with fast-math + flushed denormals, and at -O1: the
+    same bits (the pages rebuild with fast math and compare)."""
+    for bits in (W.c2_exhaustive(), W.c2_planted(), W.fp32_fuzz(1 << 16).reshape(-1, 128), W.c3_spread()[:256, :512]):
+        check_all(np.ascontiguousarray(bits), dev, lib=variant)
