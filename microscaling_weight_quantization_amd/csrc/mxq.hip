@@ -11,11 +11,19 @@
 // Design (CDNA4, wave64).  Every kernel streams HBM once; nothing here is a
 // contraction, so there is no MFMA.  A lane owns one 16-byte chunk of a row per
 // step (8 bf16 or 4 fp32), so a 1x32 block spans 4 (bf16) or 8 (fp32)
-// neighbouring lanes and its amax is reduced with two or three DPP moves.  All
-// arithmetic is integer: the scale exponent comes from the amax bit pattern,
-// E2M1 rounding is done on bit patterns relative to the block scale, and bf16
-// pairs are processed as packed 16-bit lanes (v_pk_* integer ops).  Results do
-// not depend on denormal or fast-math settings.
+// neighbouring lanes and its amax is reduced with two or three DPP moves.  The
+// block's scale exponent is integer arithmetic on the amax bit pattern.  The
+// rounding steps run on CDNA4's scaled conversions:
+//   v_cvt_scalef32_pk_fp4_{bf16,f32}  RTNE(x / 2^e) onto E2M1, saturating at 6
+//   v_cvt_scalef32_pk_bf16_fp4        E2M1 * 2^e back to bf16 (always exact)
+//   v_cvt_scalef32_pk_fp8_bf16        RTNE(y / 2^S) onto E4M3 with subnormals
+//   v_cvt_scalef32_{pk_bf16,f32}_{fp8,bf8}  FP8 * 2^(code-127)
+// Each was compared bit for bit with the CPU oracle over every bf16 input and
+// every scale exponent (fp32: every bf16-widened pattern plus random low
+// halves) and matches exactly when the wave keeps denormals; every kernel
+// therefore sets the MODE register's denormal field itself, which makes the
+// results independent of the build's floating-point flags.  The scale operand
+// is passed as an E8M0 code placed in the f32 exponent field (code 0 = 2^-127).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -26,12 +34,12 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 // Launch-shape tunables (compile-time).
 #ifndef MXQ_STEPS_PER_WG
-#define MXQ_STEPS_PER_WG 4        // 16-byte chunks in flight per lane in the streaming kernels
+#define MXQ_STEPS_PER_WG 2        // 16-byte chunks in flight per lane in the streaming kernels
 #endif
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
@@ -61,26 +69,40 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 }
 
 // ------------------------------------------------------------------------------------
-// Packed 16-bit integer helpers (two bf16 patterns per 32-bit register)
+// Conversions
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ u16x2 U2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
-__device__ __forceinline__ i16x2 I2(uint32_t v) { return __builtin_bit_cast(i16x2, v); }
-__device__ __forceinline__ uint32_t W(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __forceinline__ uint32_t W(i16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+// hwreg(HW_REG_MODE, offset 4, size 4): the FP_DENORM field.  0xF keeps
+// denormals (f32 and f16/f64 classes, inputs and outputs).
+constexpr int kModeFpDenorm = 1 | (4 << 6) | (3 << 11);
+__device__ __forceinline__ void keep_denormals() { __builtin_amdgcn_s_setreg(kModeFpDenorm, 0xF); }
 
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) { return W(__builtin_elementwise_max(U2(a), U2(b))); }
-__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) { return W(__builtin_elementwise_min(U2(a), U2(b))); }
-__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) { return W(__builtin_elementwise_max(I2(a), I2(b))); }
-__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint16_t m, uint32_t c) {
-  return W(U2(a) * (u16x2)(m) + U2(c));
+// Scale operand of the scaled conversions: E8M0 code in the f32 exponent field.
+__device__ __forceinline__ float e8m0(uint32_t code) { return __builtin_bit_cast(float, code << 23); }
+
+__device__ __forceinline__ bf16x2 BF(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+__device__ __forceinline__ float F(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+// E2M1 nibbles (element k of the chunk in nibble k) of RTNE(x / 2^e).
+__device__ __forceinline__ uint32_t fp4_of(u32x4 w, float s, uint16_t) {
+  uint32_t f = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, BF(w[0]), s, 0);
+  f = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(f, BF(w[1]), s, 1);
+  f = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(f, BF(w[2]), s, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(f, BF(w[3]), s, 3);
 }
-__device__ __forceinline__ uint32_t pk_add_u16(uint32_t a, uint32_t b) { return W(U2(a) + U2(b)); }
-__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b) { return W(U2(a) - U2(b)); }
-__device__ __forceinline__ uint32_t splat16(uint32_t v) { return (v & 0xFFFFu) * 0x00010001u; }
-
-// Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+__device__ __forceinline__ uint32_t fp4_of(u32x4 w, float s, uint32_t) {
+  uint32_t f = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, F(w[0]), F(w[1]), s, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(f, F(w[2]), F(w[3]), s, 1);
+}
+// Two bf16 values p * 2^e from nibble pair SEL (byte SEL of f).
+template <int SEL>
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t f, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, s, SEL));
+}
+// Four E4M3 bytes RTNE(y / 2^S) of two bf16 pairs.
+__device__ __forceinline__ uint32_t e4m3x4(uint32_t y01, uint32_t y23, float s) {
+  s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, BF(y01), s, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, BF(y23), s, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // DPP lane moves inside a row of 16 lanes.
@@ -110,17 +132,21 @@ template <>
 struct Fmt<uint16_t> {   // bf16 bit patterns
   static constexpr int kEPL = 8;   // elements per 16-byte chunk
   static constexpr int kLPB = 4;   // lanes per 1x32 block
-  static constexpr uint32_t kNaN = 0x7FC0u;
+  static constexpr uint32_t kNaN2 = 0x7FC07FC0u;          // canonical quiet NaN, twice
+  static constexpr uint32_t kMag = 0x7FFF7FFFu, kInf = 0x7F80u;
+  static constexpr int kMbits = 7;
 };
 template <>
 struct Fmt<uint32_t> {   // fp32 bit patterns
   static constexpr int kEPL = 4;
   static constexpr int kLPB = 8;
-  static constexpr uint32_t kNaN = 0x7FC00000u;
+  static constexpr uint32_t kNaN2 = 0x7FC00000u;
+  static constexpr uint32_t kMag = 0x7FFFFFFFu, kInf = 0x7F800000u;
+  static constexpr int kMbits = 23;
 };
 
 // ------------------------------------------------------------------------------------
-// The MXFP4 decomposition of one block ([QAT] Description, conversion mode 1)
+// The scale exponent of one block ([QAT] Description, conversion mode 1)
 //
 // eb = e + 127 is the biased scale exponent, 1..252.  With A the amax bit
 // pattern, 6 * 2^e >= amax first holds at e = E - 2 when the amax mantissa is
@@ -134,177 +160,89 @@ struct Block {
   bool poison;
 };
 
-__device__ __forceinline__ Block block_from_amax_bf16(uint32_t amax) {
-  int eb = (int)((amax + 0x3Fu) >> 7) - 2;
+template <typename T>
+__device__ __forceinline__ Block block_of_amax(uint32_t amax) {
+  constexpr int MB = Fmt<T>::kMbits;
+  int eb = (int)((amax + ((1u << (MB - 1)) - 1u)) >> MB) - 2;
   eb = min(max(eb, 1), 252);
-  return Block{(uint32_t)eb, amax >= 0x7F80u};
-}
-__device__ __forceinline__ Block block_from_amax_fp32(uint32_t amax) {
-  int eb = (int)((amax + 0x3FFFFFu) >> 23) - 2;
-  eb = min(max(eb, 1), 252);
-  return Block{(uint32_t)eb, amax >= 0x7F800000u};
+  return Block{(uint32_t)eb, amax >= Fmt<T>::kInf};
 }
 
-// E2M1 code c (0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6) of RTNE(|x| / 2^e), returned
-// as C = c + 2.
-//
-// Let d = |x| - 2^e measured in bit-pattern units (one binade = 2^mbits).  The
-// value t = |x| / 2^e, mapped to D = 2^(mbits+2) * (t - 1), is the rounding
-// variable: E2M1 steps of 0.5 below t = 2 are steps of 2^(mbits+1) in D, and
-// above t = 1 bit patterns are linear within each binade with two E2M1 values
-// per binade, so there D = 4d.  Below t = 1 the binades shrink: D = 2d in the
-// binade just below 2^e and D = d - 2^mbits in the next one (further down t <
-// 1/4 rounds to 0 whatever D is).  D = max(4d, 2d, d - 2^mbits) covers all of
-// that at once; when eb <= 2 the subnormal patterns continue binade 1 linearly,
-// so the pieces that assume a narrower binade are switched off.  Ties are
-// broken to the even code by the usual "add half - 1 + lsb" step.  The
-// clamp of |x| to [2^e / 16, 6 * 2^e] keeps D in range and makes values above
-// 6 * 2^e (only possible at the e = 125 cap) saturate to 6.
-struct CodeConsts16 {   // bf16, broadcast to both 16-bit halves
-  uint32_t lo, hi, k4, k2, k1;
-};
-__device__ __forceinline__ CodeConsts16 code_consts_bf16(uint32_t eb) {
-  const uint32_t A1 = eb << 7;                      // pattern of 2^e
-  CodeConsts16 k;
-  k.lo = splat16(A1 > 512u ? A1 - 512u : 0u);       // 2^(e-4)
-  k.hi = splat16(A1 + 320u);                        // 6 * 2^e
-  // D + 1024 for each piece (1024 keeps D positive and the tie parity intact)
-  k.k4 = splat16(1024u - 4u * A1);
-  k.k2 = splat16(1024u - 2u * A1 - (eb == 1 ? 4096u : 0u));
-  k.k1 = splat16(896u - A1 - (eb <= 2 ? 4096u : 0u));
-  return k;
-}
-
-// Codes of two bf16 elements (one 32-bit word of magnitudes a): two C values.
-__device__ __forceinline__ uint32_t codes_bf16(uint32_t a, const CodeConsts16& k) {
-  uint32_t ac = pk_min_u16(pk_max_u16(a, k.lo), k.hi);
-  uint32_t p4 = pk_mad_u16(ac, 4, k.k4);
-  uint32_t p2 = pk_mad_u16(ac, 2, k.k2);
-  uint32_t p1 = pk_add_u16(ac, k.k1);
-  uint32_t D = pk_max_i16(pk_max_i16(p4, p2), p1);            // 384 .. 2304 per half
-  uint32_t lsb = (D >> 8) & 0x00010001u;
-  uint32_t S = D + 0x007F007Fu + lsb;                           // no carry between halves
-  return (S >> 8) & 0x00FF00FFu;                                // C = c + 2 in 2..9
-}
-
-struct CodeConsts32 {
-  uint32_t A1, lo, hi;
-  int32_t k2, k1;
-};
-__device__ __forceinline__ CodeConsts32 code_consts_fp32(uint32_t eb) {
-  CodeConsts32 k;
-  k.A1 = eb << 23;
-  k.lo = k.A1 > (4u << 23) ? k.A1 - (4u << 23) : 0u;
-  k.hi = k.A1 + (5u << 22);
-  k.k2 = eb == 1 ? -(1 << 28) : 0;
-  k.k1 = (eb <= 2 ? -(1 << 28) : 0) - (1 << 23);
-  return k;
-}
-__device__ __forceinline__ uint32_t code_fp32(uint32_t a, const CodeConsts32& k) {
-  uint32_t ac = min(max(a, k.lo), k.hi);
-  int32_t d = (int32_t)(ac - k.A1);
-  int32_t D = max(max(4 * d, 2 * d + k.k2), d + k.k1) + (1 << 26);
-  uint32_t Du = (uint32_t)D;
-  return (Du + (1u << 23) - 1u + ((Du >> 24) & 1u)) >> 24;      // C = c + 2 in 2..9
-}
-
-// ------------------------------------------------------------------------------------
-// Output encodings from C = c + 2
-// ------------------------------------------------------------------------------------
-// Projection, bf16: p * 2^e for c >= 2 has pattern (eb-1)*128 + 64c, i.e.
-// (eb-2)*128 + 64C; c = 1 (0.5 * 2^e) is (eb-1)*128, except at eb = 1 where it
-// is the subnormal 0x0040, which the first formula already gives; c = 0 is 0.
-// min() of three affine pieces picks the right one for every C.
-struct ProjConsts16 {
-  uint32_t kq, k3, floor, smask;
-};
-__device__ __forceinline__ ProjConsts16 proj_consts_bf16(Block b) {
-  ProjConsts16 p;
-  p.kq = splat16((b.eb - 2u) << 7);
-  p.k3 = splat16(b.eb == 1 ? 0x7C00u : (b.eb - 4u) << 7);
-  p.floor = b.poison ? 0x7FC07FC0u : 0u;
-  p.smask = b.poison ? 0u : 0x80008000u;
-  return p;
-}
-__device__ __forceinline__ uint32_t proj_word_bf16(uint32_t w, uint32_t C, const ProjConsts16& p) {
-  uint32_t q = pk_mad_u16(C, 64, p.kq);
-  uint32_t q3 = pk_mad_u16(C, 128, p.k3);
-  uint32_t q5 = pk_sub_u16(0x00020002u, C);                     // 0 for c = 0, huge otherwise
-  uint32_t m = pk_max_u16(pk_min_u16(pk_min_u16(q, q3), q5), p.floor);
-  return (w & p.smask) | m;
-}
-
-__device__ __forceinline__ uint32_t proj_fp32(uint32_t w, uint32_t C, Block b) {
-  if (b.poison) return Fmt<uint32_t>::kNaN;
-  uint32_t m;
-  if (C <= 2u) m = 0u;
-  else if (C == 3u && b.eb >= 2u) m = (b.eb - 1u) << 23;
-  else m = ((b.eb - 2u) << 23) + (C << 22);
-  return (w & 0x80000000u) | m;
-}
-
-// Row lift payload: E4M3 of p * 2^s with s = min(6, e + 127) >= 1.  For c >= 1
-// the exponent field is s + 6 + E(c) and the mantissa the E2M1 mantissa bit,
-// giving bytes b, b+8, b+12, b+16, b+20, b+24, b+28 with b = (s + 6) * 8
-// (b = 0x60 at s = 6: 0x60, 0x68, 0x6C, ..., 0x7C).  Eight entries = a v_perm LUT.
-struct Lut8 {
-  uint32_t lo, hi;    // bytes for codes 0..3 and 4..7
-};
-__device__ __forceinline__ Lut8 row_lut(Block b) {
-  if (b.poison) return Lut8{0x7F7F7F7Fu, 0x7F7F7F7Fu};
-  uint32_t s = min(b.eb, 6u);
-  uint32_t base = (s + 6u) << 3;
-  return Lut8{base * 0x01010100u + 0x0C080000u, base * 0x01010101u + 0x1C181410u};
-}
-__device__ __forceinline__ uint32_t row_code(Block b) {
-  return b.poison ? 255u : (b.eb > 6u ? b.eb - 6u : 0u);         // max(e + 121, 0)
-}
-
-// 128x128 fold payload: RTNE_E4M3(p * 2^sh) for sh = e - S in [-16, 6] (anything
-// lower rounds to zero like -16).  In units of the E4M3 subnormal step 2^-9 the
-// value is N = 2p * 2^(sh + 8); below 16 steps the encoding is N itself
-// (subnormals and the first normal binade share the step), above it the grid
-// values are exact with at most two significant bits.
-constexpr int kFoldMin = -16, kFoldMax = 6, kFoldEntries = kFoldMax - kFoldMin + 1;
-
-constexpr uint32_t e4m3_grid_byte(int c, int sh) {
-  const uint32_t twice_p[8] = {0, 1, 2, 3, 4, 6, 8, 12};
-  const int s = sh + 8;
-  uint32_t N = 0;
-  if (s >= 0) {
-    N = twice_p[c] << s;
+template <typename T>
+__device__ __forceinline__ uint32_t chunk_amax(u32x4 w) {
+  const uint32_t M = Fmt<T>::kMag;
+  if constexpr (sizeof(T) == 2) {
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 m = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[0] & M), __builtin_bit_cast(u16x2, w[1] & M)),
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[2] & M), __builtin_bit_cast(u16x2, w[3] & M)));
+    return max((uint32_t)m[0], (uint32_t)m[1]);
   } else {
-    const int r = -s;
-    const uint32_t q = twice_p[c] >> r, rem = twice_p[c] & ((1u << r) - 1u), half = 1u << (r - 1);
-    N = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+    return max(max(w[0] & M, w[1] & M), max(w[2] & M, w[3] & M));
   }
-  if (N < 16u) return N;
-  int j = 0;
-  while ((N >> (j + 1)) != 0u) j++;
-  return ((uint32_t)(j - 2) << 3) | ((N >> (j - 3)) - 8u);
 }
 
-struct FoldTable {
-  uint32_t w[2 * kFoldEntries];
+template <typename T>
+__device__ __forceinline__ Block chunk_block(u32x4 w) {
+  return block_of_amax<T>(block_max<Fmt<T>::kLPB>(chunk_amax<T>(w)));
+}
+
+// Projected values p * 2^e of a chunk, as bf16 pairs: 4 words (bf16 chunk) or
+// 2 words (fp32 chunk) -- exact, since p has two significant bits and
+// p * 2^e >= 2^-127 is a bf16 subnormal at worst.
+template <typename T>
+struct Proj16 {
+  uint32_t p[sizeof(T) == 2 ? 4 : 2];
 };
-constexpr FoldTable make_fold_table() {
-  FoldTable t{};
-  for (int i = 0; i < kFoldEntries; i++) {
-    const int sh = kFoldMin + i;
-    for (int c = 0; c < 8; c++) t.w[2 * i + c / 4] |= e4m3_grid_byte(c, sh) << (8 * (c % 4));
+template <typename T>
+__device__ __forceinline__ Proj16<T> project(uint32_t f, float s) {
+  Proj16<T> y;
+  y.p[0] = bf16_pair<0>(f, s);
+  y.p[1] = bf16_pair<1>(f, s);
+  if constexpr (sizeof(T) == 2) {
+    y.p[2] = bf16_pair<2>(f, s);
+    y.p[3] = bf16_pair<3>(f, s);
   }
-  return t;
+  return y;
 }
-__constant__ FoldTable kFold = make_fold_table();
-static_assert(e4m3_grid_byte(7, 6) == 0x7C && e4m3_grid_byte(1, 6) == 0x60, "fold table");
-static_assert(e4m3_grid_byte(1, -6) == 0x04 && e4m3_grid_byte(7, -6) == 0x1C, "fold table");
-static_assert(e4m3_grid_byte(1, -9) == 0x00 && e4m3_grid_byte(3, -9) == 0x02, "fold table");
 
-// Payload bytes of four elements from their C = c + 2 values (one byte each in
-// `sel_plus2`) and their sign bytes.
-__device__ __forceinline__ uint32_t payload4(uint32_t sel_plus2, Lut8 lut, uint32_t sign_bytes, uint32_t smask8) {
-  uint32_t q = perm(lut.hi, lut.lo, sel_plus2 - 0x02020202u);
-  return q | (sign_bytes & smask8);
+// Projection output chunk in the input dtype; a poisoned block is all NaN.
+template <typename T>
+__device__ __forceinline__ u32x4 proj_chunk(const Proj16<T>& y, bool poison) {
+  u32x4 o;
+  if constexpr (sizeof(T) == 2) {
+    o = u32x4{y.p[0], y.p[1], y.p[2], y.p[3]};
+  } else {
+    o = u32x4{y.p[0] << 16, y.p[0] & 0xFFFF0000u, y.p[1] << 16, y.p[1] & 0xFFFF0000u};
+  }
+  if (poison) o = u32x4{Fmt<T>::kNaN2, Fmt<T>::kNaN2, Fmt<T>::kNaN2, Fmt<T>::kNaN2};
+  return o;
+}
+
+// E4M3 payload bytes of a chunk at scale 2^(code-127): 8 bytes (bf16 chunk) or 4
+// (fp32 chunk); a poisoned block is all 0x7F (NaN).
+template <typename T>
+struct PayloadChunk;
+template <>
+struct PayloadChunk<uint16_t> { typedef u32x2 type; };
+template <>
+struct PayloadChunk<uint32_t> { typedef uint32_t type; };
+
+template <typename T>
+__device__ __forceinline__ typename PayloadChunk<T>::type payload_chunk(const Proj16<T>& y, uint32_t code, bool poison) {
+  const float s = e8m0(code);
+  if constexpr (sizeof(T) == 2) {
+    u32x2 q{e4m3x4(y.p[0], y.p[1], s), e4m3x4(y.p[2], y.p[3], s)};
+    if (poison) q = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+    return q;
+  } else {
+    return poison ? 0x7F7F7F7Fu : e4m3x4(y.p[0], y.p[1], s);
+  }
+}
+
+// Direct-row scale code: 2^(e-6) clamped at 2^-127 = max(e + 121, 0); 255 if poisoned.
+__device__ __forceinline__ uint32_t row_code(Block b) {
+  return b.poison ? 255u : (b.eb > 6u ? b.eb - 6u : 0u);
 }
 
 // ------------------------------------------------------------------------------------
@@ -347,14 +285,6 @@ __device__ __forceinline__ void store_chunk(T* __restrict__ row, int64_t col0, i
   }
 }
 
-// Payload bytes of one chunk: 8 (bf16 chunk) or 4 (fp32 chunk).
-template <typename T>
-struct PayloadChunk;
-template <>
-struct PayloadChunk<uint16_t> { typedef u32x2 type; };
-template <>
-struct PayloadChunk<uint32_t> { typedef uint32_t type; };
-
 template <typename T, bool VEC>
 __device__ __forceinline__ void store_payload(uint8_t* __restrict__ row, int64_t col0, int64_t K,
                                               typename PayloadChunk<T>::type p) {
@@ -376,82 +306,10 @@ __device__ __forceinline__ void store_payload(uint8_t* __restrict__ row, int64_t
 }
 
 // ------------------------------------------------------------------------------------
-// Per-chunk pipelines
-// ------------------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ uint32_t chunk_amax(u32x4 w) {
-  if constexpr (sizeof(T) == 2) {
-    uint32_t m = pk_max_u16(pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
-                            pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
-    return max(m & 0xFFFFu, m >> 16);
-  } else {
-    return max(max(w[0] & 0x7FFFFFFFu, w[1] & 0x7FFFFFFFu), max(w[2] & 0x7FFFFFFFu, w[3] & 0x7FFFFFFFu));
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ Block chunk_block(u32x4 w) {
-  uint32_t amax = block_max<Fmt<T>::kLPB>(chunk_amax<T>(w));
-  if constexpr (sizeof(T) == 2) return block_from_amax_bf16(amax);
-  else return block_from_amax_fp32(amax);
-}
-
-// C = c + 2 of every element of the chunk: bf16 -> 4 words of two 16-bit
-// values; fp32 -> 4 words of one value each.
-template <typename T>
-__device__ __forceinline__ u32x4 chunk_codes(u32x4 w, Block b) {
-  u32x4 C;
-  if constexpr (sizeof(T) == 2) {
-    const CodeConsts16 k = code_consts_bf16(b.eb);
-#pragma unroll
-    for (int i = 0; i < 4; i++) C[i] = codes_bf16(w[i] & 0x7FFF7FFFu, k);
-  } else {
-    const CodeConsts32 k = code_consts_fp32(b.eb);
-#pragma unroll
-    for (int i = 0; i < 4; i++) C[i] = code_fp32(w[i] & 0x7FFFFFFFu, k);
-  }
-  return C;
-}
-
-template <typename T>
-__device__ __forceinline__ u32x4 chunk_proj(u32x4 w, Block b) {
-  const u32x4 C = chunk_codes<T>(w, b);
-  u32x4 y;
-  if constexpr (sizeof(T) == 2) {
-    const ProjConsts16 p = proj_consts_bf16(b);
-#pragma unroll
-    for (int i = 0; i < 4; i++) y[i] = proj_word_bf16(w[i], C[i], p);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; i++) y[i] = proj_fp32(w[i], C[i], b);
-  }
-  return y;
-}
-
-// E4M3 payload of the chunk through an 8-entry byte LUT indexed by code.
-template <typename T>
-__device__ __forceinline__ typename PayloadChunk<T>::type chunk_payload(u32x4 w, u32x4 C, Lut8 lut, bool poison) {
-  const uint32_t smask8 = poison ? 0u : 0x80808080u;
-  if constexpr (sizeof(T) == 2) {
-    // bytes 0 and 2 of two words = the four low bytes of four 16-bit C values
-    const uint32_t sel01 = perm(C[1], C[0], 0x06040200u), sel23 = perm(C[3], C[2], 0x06040200u);
-    const uint32_t sg01 = perm(w[1], w[0], 0x07050301u), sg23 = perm(w[3], w[2], 0x07050301u);
-    u32x2 p;
-    p[0] = payload4(sel01, lut, sg01, smask8);
-    p[1] = payload4(sel23, lut, sg23, smask8);
-    return p;
-  } else {
-    const uint32_t sel = C[0] | (C[1] << 8) | (C[2] << 16) | (C[3] << 24);
-    const uint32_t sg = perm(perm(w[3], w[2], 0x0C0C0703u), perm(w[1], w[0], 0x0C0C0703u), 0x05040100u);
-    return payload4(sel, lut, sg, smask8);
-  }
-}
-
-// ------------------------------------------------------------------------------------
 // Streaming kernels: projection and row lift.  A "step" is 256 lanes x one
 // 16-byte chunk = 2048 bf16 / 1024 fp32 elements of ONE row (64 / 32 blocks);
 // rows are padded to whole steps, so the row / segment split is per-step
-// uniform (scalar) arithmetic and no block straddles two lanes' rows.
+// uniform (scalar) arithmetic and a block never straddles two rows.
 // ------------------------------------------------------------------------------------
 template <typename T>
 struct StepGeom {
@@ -465,6 +323,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const T* __restrict__ x,
                                                         int64_t ld_y, int64_t K, uint32_t steps_per_row,
                                                         uint32_t total_steps) {
   using G = StepGeom<T>;
+  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   u32x4 w[kStepsPerWG];
@@ -483,7 +342,9 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const T* __restrict__ x,
     if (step < total_steps) {
       const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
       const Block b = chunk_block<T>(w[u]);
-      store_chunk<T, VEC>(y + (int64_t)row * ld_y, seg * G::kElemsPerStep + lane_col, K, chunk_proj<T>(w[u], b));
+      const float s = e8m0(b.eb);
+      const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
+      store_chunk<T, VEC>(y + (int64_t)row * ld_y, seg * G::kElemsPerStep + lane_col, K, proj_chunk<T>(p, b.poison));
     }
   }
 }
@@ -494,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
                                                        int64_t scale_ld, uint32_t steps_per_row,
                                                        uint32_t total_steps) {
   using G = StepGeom<T>;
+  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   u32x4 w[kStepsPerWG];
@@ -513,18 +375,20 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
       const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
       const Block b = chunk_block<T>(w[u]);
-      const u32x4 C = chunk_codes<T>(w[u], b);
-      store_payload<T, VEC>(data + (int64_t)row * K, col0, K, chunk_payload<T>(w[u], C, row_lut(b), b.poison));
-      if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)row_code(b);
+      const float s = e8m0(b.eb);
+      const uint32_t code = row_code(b);
+      const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
+      store_payload<T, VEC>(data + (int64_t)row * K, col0, K, payload_chunk<T>(p, code, b.poison));
+      if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)code;
     }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// 128x128 tile fold: one workgroup per tile, one HBM pass.  The 256 lanes hold
-// the whole tile in registers (bf16: 8 chunks per lane, fp32: 16), reduce the
-// largest finite block exponent through DPP / shuffles and LDS, then write the
-// folded payload.
+// 128x128 tile fold: one workgroup per tile, one HBM pass.  Each lane keeps the
+// E2M1 nibbles and block exponents of its chunks (bf16: 8 chunks, fp32: 16) in
+// registers, the workgroup reduces the largest finite block exponent through
+// DPP / shuffles and LDS, then every lane folds and writes its payload.
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
@@ -537,19 +401,17 @@ __global__ __launch_bounds__(kThreads) void block128_kernel(const T* __restrict_
                                                             int64_t K, uint8_t* __restrict__ data,
                                                             uint8_t* __restrict__ tile_code, int64_t tile_ld,
                                                             uint32_t tiles_per_row) {
-  constexpr int EPL = Fmt<T>::kEPL, LPB = Fmt<T>::kLPB;
-  constexpr int kChunksPerRow = 128 / EPL;             // 16 (bf16) / 32 (fp32)
+  constexpr int EPL = Fmt<T>::kEPL;
+  constexpr int kChunksPerRow = 128 / EPL;                 // 16 (bf16) / 32 (fp32)
   constexpr int kRowsPerPass = kThreads / kChunksPerRow;   // 16 / 8
   constexpr int kPasses = 128 / kRowsPerPass;              // 8 / 16
-  __shared__ uint32_t s_fold[2 * kFoldEntries];
   __shared__ uint32_t s_wave_max[kThreads / 64];
+  keep_denormals();
 
   const uint32_t tid = threadIdx.x;
   const uint32_t tr = blockIdx.x / tiles_per_row, tc = blockIdx.x - tr * tiles_per_row;
   const int64_t r0 = (int64_t)tr * 128 + tid / kChunksPerRow;
   const int64_t col0 = (int64_t)tc * 128 + (tid % kChunksPerRow) * EPL;
-
-  if (tid < 2 * kFoldEntries) s_fold[tid] = kFold.w[tid];
 
   u32x4 w[kPasses];
 #pragma unroll
@@ -557,57 +419,67 @@ __global__ __launch_bounds__(kThreads) void block128_kernel(const T* __restrict_
     const int64_t r = r0 + i * kRowsPerPass;
     w[i] = (r < rows) ? load_chunk<T, VEC>(x + r * ld_x, col0, K) : u32x4{0u, 0u, 0u, 0u};
   }
-  Block b[kPasses];
+  uint32_t f[kPasses], eb[kPasses];
+  uint32_t poisoned = 0u;                                  // bit i: chunk i's block is poisoned
   uint32_t m = 1u;
 #pragma unroll
   for (int i = 0; i < kPasses; i++) {
-    b[i] = chunk_block<T>(w[i]);
-    if (!b[i].poison) m = max(m, b[i].eb);
+    const Block b = chunk_block<T>(w[i]);
+    eb[i] = b.eb;
+    f[i] = fp4_of(w[i], e8m0(b.eb), T{});
+    poisoned |= (uint32_t)b.poison << i;
+    if (!b.poison) m = max(m, b.eb);
   }
   m = wave_max(m);
   if ((tid & 63u) == 0u) s_wave_max[tid >> 6] = m;
   __syncthreads();
   m = max(max(s_wave_max[0], s_wave_max[1]), max(s_wave_max[2], s_wave_max[3]));
-  const uint32_t code = m > 6u ? m - 6u : 0u;                    // S + 127 = max(M - 6, -127) + 127
+  const uint32_t code = m > 6u ? m - 6u : 0u;              // S + 127 = max(M - 6, -127) + 127
   if (tid == 0) tile_code[(int64_t)tr * tile_ld + tc] = (uint8_t)code;
 
 #pragma unroll
   for (int i = 0; i < kPasses; i++) {
     const int64_t r = r0 + i * kRowsPerPass;
-    const int sh = min(max((int)b[i].eb - (int)code, kFoldMin), kFoldMax);   // e - S
-    const uint32_t idx = 2u * (uint32_t)(sh - kFoldMin);
-    const Lut8 lut = b[i].poison ? Lut8{0x7F7F7F7Fu, 0x7F7F7F7Fu} : Lut8{s_fold[idx], s_fold[idx + 1]};
-    const u32x4 C = chunk_codes<T>(w[i], b[i]);
-    const auto p = chunk_payload<T>(w[i], C, lut, b[i].poison);
-    if (r < rows) store_payload<T, VEC>(data + r * K, col0, K, p);
+    const Proj16<T> p = project<T>(f[i], e8m0(eb[i]));
+    const auto q = payload_chunk<T>(p, code, (poisoned >> i) & 1u);
+    if (r < rows) store_payload<T, VEC>(data + r * K, col0, K, q);
   }
-  (void)LPB;
 }
 
 // ------------------------------------------------------------------------------------
-// Decode: FP8 payload * 2^(code - 127) -> fp32 bits, exact (or Inf above the fp32
-// range); bf16 is the nearest-even rounding of those fp32 bits.
+// Decode: FP8 payload * 2^(code - 127).  The conversions return a negative quiet
+// NaN for NaN payloads and code 255; those (rare) chunks are rewritten to the
+// canonical positive quiet NaN.
 // ------------------------------------------------------------------------------------
 template <bool kE5M2>
-__device__ __forceinline__ uint32_t decode_fp32(uint32_t q, uint32_t code) {
-  constexpr int MB = kE5M2 ? 2 : 3, BIAS = kE5M2 ? 15 : 7;
-  const uint32_t sign = (q & 0x80u) << 24, mag = q & 0x7Fu;
-  const uint32_t E = mag >> MB, m = mag & ((1u << MB) - 1u);
-  const bool nan = (code == 255u) || (kE5M2 ? (E == 31u && m != 0u) : (mag == 0x7Fu));
-  if (nan) return 0x7FC00000u;
-  if (kE5M2 && E == 31u) return sign | 0x7F800000u;
-  const uint32_t sig = E ? ((1u << MB) | m) : m;
-  if (sig == 0u) return sign;
-  const int ex = E ? (int)E : 1;
-  const int L = 31 - __clz((int)sig);
-  const int biased = ex + (int)code + L - BIAS - MB;            // fp32 biased exponent
-  if (biased >= 255) return sign | 0x7F800000u;
-  if (biased >= 1) return sign | ((uint32_t)biased << 23) | ((sig << (23 - L)) & 0x7FFFFFu);
-  return sign | (sig << (ex + (int)code + 22 - BIAS - MB));      // fp32 subnormal, exact
+__device__ __forceinline__ u32x4 decode8_bf16(u32x2 q, float s) {
+  u32x4 o;
+  if constexpr (kE5M2) {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(q[0], s, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(q[0], s, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(q[1], s, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(q[1], s, true));
+  } else {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[0], s, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[0], s, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[1], s, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[1], s, true));
+  }
+  return o;
 }
-__device__ __forceinline__ uint32_t fp32_to_bf16_rne(uint32_t f) {
-  if ((f & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  return (f + 0x7FFFu + ((f >> 16) & 1u)) >> 16;
+// One f32 from byte SEL of q.  (The packed two-result f32 forms of these
+// conversions are not used: the compiler's model of their second result is not
+// reliable.)
+template <bool kE5M2, int SEL>
+__device__ __forceinline__ uint32_t decode1_f32(uint32_t q, float s) {
+  if constexpr (kE5M2) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_f32_bf8(q, s, SEL));
+  else return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_f32_fp8(q, s, SEL));
+}
+// Any NaN payload byte among the 8 (E4M3: magnitude 0x7F; E5M2: above 0x7C).
+template <bool kE5M2>
+__device__ __forceinline__ bool has_nan_byte(u32x2 q) {
+  constexpr uint32_t add = kE5M2 ? 0x03030303u : 0x01010101u;
+  return ((((q[0] & 0x7F7F7F7Fu) + add) | ((q[1] & 0x7F7F7F7Fu) + add)) & 0x80808080u) != 0u;
 }
 
 template <typename TO, bool kE5M2, bool kTile, bool VEC>
@@ -616,6 +488,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
                                                            uint32_t steps_per_row, uint32_t total_steps) {
   // 8 payload bytes per lane per step; 64 x 1x32 blocks per step.
+  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 8;
   for (int u = 0; u < kStepsPerWG; u++) {
@@ -625,25 +498,27 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     const int64_t col0 = (int64_t)seg * 2048 + lane_col;
     if (col0 >= K) continue;
     const uint8_t* drow = data + (int64_t)row * K;
-    uint32_t q[2] = {0u, 0u};
+    u32x2 q = {0u, 0u};
     if (VEC) {
-      const u32x2 v = stream_load(reinterpret_cast<const u32x2*>(drow + col0));
-      q[0] = v[0];
-      q[1] = v[1];
+      q = stream_load(reinterpret_cast<const u32x2*>(drow + col0));
     } else {
       for (int i = 0; i < 8; i++)
         if (col0 + i < K) q[i / 4] |= (uint32_t)drow[col0 + i] << (8 * (i % 4));
     }
     const uint32_t code = kTile ? scale[(int64_t)(row / 128) * scale_ld + col0 / 128]
                                 : scale[(int64_t)row * scale_ld + col0 / 32];
-    uint32_t f[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) f[i] = decode_fp32<kE5M2>((q[i / 4] >> (8 * (i % 4))) & 0xFFu, code);
+    const float s = e8m0(code);
+    const bool fix_nan = code == 255u || has_nan_byte<kE5M2>(q);
     TO* orow = out + (int64_t)row * ld_out;
     if constexpr (sizeof(TO) == 2) {
-      u32x4 o;
+      u32x4 o = decode8_bf16<kE5M2>(q, s);
+      if (fix_nan) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) o[i] = fp32_to_bf16_rne(f[2 * i]) | (fp32_to_bf16_rne(f[2 * i + 1]) << 16);
+        for (int i = 0; i < 8; i++) {
+          const uint32_t h = (o[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+          if ((h & 0x7FFFu) > 0x7F80u) o[i / 2] = (o[i / 2] & ~(0xFFFFu << (16 * (i % 2)))) | (0x7FC0u << (16 * (i % 2)));
+        }
+      }
       if (VEC) {
         stream_store(o, reinterpret_cast<u32x4*>(orow + col0));
       } else {
@@ -651,6 +526,15 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
           if (col0 + i < K) orow[col0 + i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
       }
     } else {
+      uint32_t f[8] = {decode1_f32<kE5M2, 0>(q[0], s), decode1_f32<kE5M2, 1>(q[0], s),
+                       decode1_f32<kE5M2, 2>(q[0], s), decode1_f32<kE5M2, 3>(q[0], s),
+                       decode1_f32<kE5M2, 0>(q[1], s), decode1_f32<kE5M2, 1>(q[1], s),
+                       decode1_f32<kE5M2, 2>(q[1], s), decode1_f32<kE5M2, 3>(q[1], s)};
+      if (fix_nan) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if ((f[i] & 0x7FFFFFFFu) > 0x7F800000u) f[i] = 0x7FC00000u;
+      }
       if (VEC) {
         stream_store(u32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<u32x4*>(orow + col0));
         stream_store(u32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<u32x4*>(orow + col0 + 4));

@@ -421,6 +421,29 @@ int orc_e2m1_code_bits(uint32_t x_bits, int dtype, int e) {
   return orc_e2m1_code(a, e);
 }
 
+/* E2M1 codes of RTNE(|x| / 2^e) for n elements (sign bit in bit 3, as a 4-bit
+ * E2M1 value); 0xFF for a non-finite element. */
+void orc_e2m1_codes(const void* x, int64_t n, int dtype, int e, uint8_t* out) {
+  fmt_t f = dtype_fmt(dtype);
+  for (int64_t i = 0; i < n; i++) {
+    dyadic d = unpack(load_bits(x, dtype, (size_t)i), f);
+    out[i] = d.cls != CLS_FINITE ? 0xFF : (uint8_t)((d.neg << 3) | orc_e2m1_code(d, e));
+  }
+}
+
+/* Nearest-even FP8 encodings (fmt_id 2 E4M3, 3 E5M2) of x * 2^-S for n
+ * elements; overflow or non-finite input gives 0xFF. */
+void orc_fp8_encode_bulk(const void* x, int64_t n, int dtype, int S, int fmt_id, uint8_t* out) {
+  fmt_t f = dtype_fmt(dtype), q = fmt_id == 2 ? FMT_E4M3 : FMT_E5M2;
+  for (int64_t i = 0; i < n; i++) {
+    dyadic d = unpack(load_bits(x, dtype, (size_t)i), f);
+    int inexact, ovf;
+    if (d.cls != CLS_FINITE) { out[i] = 0xFF; continue; }
+    uint32_t b = round_to_format(d.neg, d.M, d.k - S, q, &inexact, &ovf);
+    out[i] = ovf ? 0xFF : (uint8_t)b;
+  }
+}
+
 /* Nearest-even rounding of (-1)^neg * M * 2^k to fmt_id (0 bf16, 1 fp32, 2 E4M3, 3 E5M2).
  * flags bit 0: inexact, bit 1: overflow. */
 uint32_t orc_round_to_format(int neg, uint64_t M, int k, int fmt_id, int* flags) {
