@@ -146,7 +146,7 @@ def main():
         "dec_tile": lambda s: mxq.mxq_dequantize(s["bdata"], s["tc"], layout=mxq.MXQ_SCALE_TILE_128X128,
                                                  out=s["dec_t"]),
     }
-    # kernel -> buffer-set offset inside a step, so each x is re-read only two steps later
+    # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
     offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K

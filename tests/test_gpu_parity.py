@@ -153,6 +153,14 @@ def test_c5_mlp_sampled(dev, which):
             assert_bits(tc[band:band + 1], wtc, f"tile codes (band {band})")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_every_value_at_every_block_exponent(dev, dtype):
+    """Each element value meets each scale exponent: for bf16 this is every
+    (pattern, e) pair in the domain, so the kernels' rounding (including the
+    hardware conversions they use) is checked over its whole input space."""
+    check_all(W.value_exponent_pairs(dtype), dev)
+
+
 # ------------------------------------------------------------------ invariants on the device
 
 def test_decode_of_row_is_projection_c4(dev):

@@ -184,6 +184,47 @@ def c5_mlp(which: str):
     raise ValueError(which)
 
 
+def value_exponent_pairs(dtype: str = "bf16", width: int = 256, seed: int = 7) -> np.ndarray:
+    """Every (element value, block exponent e) pair, e in [-126, 125]: for each
+    e, every finite value with |x| <= 6 * 2^e (every finite value at e = 125,
+    where larger ones saturate) is placed in 1x32 blocks whose first element is
+    6 * 2^e, so that is the block's amax and e its scale exponent.  bf16: all
+    65536 patterns; fp32: every bf16 pattern widened with two random low halves.
+    Returned as a [rows, width] bit array (zeros pad the last row)."""
+    g = np.random.default_rng(seed)
+    if dtype == "bf16":
+        pool = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        vals = pool.astype(np.uint32).view(np.uint32) << 16
+        out_t, anchor_of = np.uint16, lambda e: int(bf16_bits_of(np.ldexp(6.0, e)))
+    else:
+        hi = np.arange(65536, dtype=np.uint32) << 16
+        pool = np.concatenate([hi | g.integers(0, 65536, 65536).astype(np.uint32),
+                               hi | g.integers(0, 65536, 65536).astype(np.uint32)])
+        vals = pool
+        out_t = np.uint32
+        anchor_of = lambda e: int(np.array(np.ldexp(6.0, e), dtype=np.float32).view(np.uint32))
+    with np.errstate(invalid="ignore"):
+        mags = np.abs(vals.view(np.float32).astype(np.float64))
+    finite = np.isfinite(mags)
+    blocks = []
+    for e in range(-126, 126):
+        sel = pool[finite & ((mags <= np.ldexp(6.0, e)) | (e == 125))]
+        sel = g.permutation(sel)
+        nb = (len(sel) + 30) // 31
+        padded = np.zeros(nb * 31, dtype=out_t)
+        padded[: len(sel)] = sel
+        b = np.empty((nb, 32), dtype=out_t)
+        b[:, 0] = anchor_of(e)
+        b[:, 1:] = padded.reshape(nb, 31)
+        blocks.append(b)
+    flat = np.concatenate(blocks).reshape(-1)
+    per_row = width
+    rows = (len(flat) + per_row - 1) // per_row
+    out = np.zeros(rows * per_row, dtype=out_t)
+    out[: len(flat)] = flat
+    return out.reshape(rows, per_row)
+
+
 def fp32_fuzz(n: int = 1 << 16, seed: int = 5) -> np.ndarray:
     """Random fp32 bit patterns (all classes) reshaped to (n/32, 32), with a
     random per-row exponent window so blocks hold values of similar size."""
