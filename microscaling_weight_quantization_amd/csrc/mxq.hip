@@ -38,8 +38,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 // Launch-shape tunables (compile-time).
-#ifndef MXQ_STEPS_PER_WG
-#define MXQ_STEPS_PER_WG 2        // 16-byte chunks in flight per lane in the streaming kernels
+// 16-byte chunks in flight per lane (steps per workgroup) in the streaming kernels
+#ifndef MXQ_PROJ_STEPS
+#define MXQ_PROJ_STEPS 1
+#endif
+#ifndef MXQ_ROW_STEPS
+#define MXQ_ROW_STEPS 2
+#endif
+#ifndef MXQ_DEQUANT_STEPS
+#define MXQ_DEQUANT_STEPS 2
 #endif
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
@@ -47,9 +54,12 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_NT_STORES
 #define MXQ_NT_STORES 1           // streaming stores carry the non-temporal hint
 #endif
+#ifndef MXQ_TILE_COLUMN_MAJOR
+#define MXQ_TILE_COLUMN_MAJOR 0   // 128x128 fold: consecutive workgroups walk down a tile column
+#endif
 
 constexpr int kThreads = 256;     // 4 waves per workgroup
-constexpr int kStepsPerWG = MXQ_STEPS_PER_WG;
+constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS;
 
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
@@ -326,10 +336,10 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const T* __restrict__ x,
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
-  u32x4 w[kStepsPerWG];
+  u32x4 w[kProjSteps];
 #pragma unroll
-  for (int u = 0; u < kStepsPerWG; u++) {
-    const uint32_t step = blockIdx.x * kStepsPerWG + u;
+  for (int u = 0; u < kProjSteps; u++) {
+    const uint32_t step = blockIdx.x * kProjSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
       const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
@@ -337,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const T* __restrict__ x,
     }
   }
 #pragma unroll
-  for (int u = 0; u < kStepsPerWG; u++) {
-    const uint32_t step = blockIdx.x * kStepsPerWG + u;
+  for (int u = 0; u < kProjSteps; u++) {
+    const uint32_t step = blockIdx.x * kProjSteps + u;
     if (step < total_steps) {
       const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
       const Block b = chunk_block<T>(w[u]);
@@ -358,10 +368,10 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
-  u32x4 w[kStepsPerWG];
+  u32x4 w[kRowSteps];
 #pragma unroll
-  for (int u = 0; u < kStepsPerWG; u++) {
-    const uint32_t step = blockIdx.x * kStepsPerWG + u;
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = blockIdx.x * kRowSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
       const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
@@ -369,8 +379,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
     }
   }
 #pragma unroll
-  for (int u = 0; u < kStepsPerWG; u++) {
-    const uint32_t step = blockIdx.x * kStepsPerWG + u;
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = blockIdx.x * kRowSteps + u;
     if (step < total_steps) {
       const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
@@ -385,61 +395,97 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
 }
 
 // ------------------------------------------------------------------------------------
-// 128x128 tile fold: one workgroup per tile, one HBM pass.  Each lane keeps the
-// E2M1 nibbles and block exponents of its chunks (bf16: 8 chunks, fp32: 16) in
-// registers, the workgroup reduces the largest finite block exponent through
-// DPP / shuffles and LDS, then every lane folds and writes its payload.
+// 128x128 tile fold, one HBM pass.  A workgroup folds J tiles that sit side by
+// side in one 128-row band, so each row of the band contributes a contiguous
+// run of J * 256 bytes (bf16) per load.  Each lane keeps only the E2M1 nibbles,
+// block exponents and poison bits of its chunks (all in one tile); the largest
+// finite block exponent of every tile is reduced with DPP inside each 16-lane
+// row, shuffles across rows of the wave, and LDS across the 4 waves; then every
+// lane folds and writes its payload.
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
+#ifndef MXQ_TILES_PER_WG
+#define MXQ_TILES_PER_WG 1
+#endif
+#ifndef MXQ_FOLD_THREADS
+#define MXQ_FOLD_THREADS 1024
+#endif
+constexpr int kFoldThreads = MXQ_FOLD_THREADS;
+constexpr int kFoldWaves = kFoldThreads / 64;
+
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within each row of 16
+
+// Max over each aligned group of 16 lanes.
+__device__ __forceinline__ uint32_t max16(uint32_t v) {
+  v = max(v, dpp<kQuadXor1>(v));
+  v = max(v, dpp<kQuadXor2>(v));
+  v = max(v, dpp<kRowHalfMirror>(v));
+  return max(v, dpp<kRowMirror>(v));
 }
 
+template <typename T>
+struct FoldGeom {
+  static constexpr int kEPL = Fmt<T>::kEPL;
+  static constexpr int kJ = sizeof(T) == 2 ? MXQ_TILES_PER_WG : (MXQ_TILES_PER_WG > 2 ? 2 : MXQ_TILES_PER_WG);
+  static constexpr int kCPT = 128 / kEPL;                  // lanes across one tile row (16 / 32)
+  static constexpr int kLPR = kCPT * kJ;                   // lanes across the band row (<= 64)
+  static constexpr int kRowsPerPass = kFoldThreads / kLPR;
+  static constexpr int kPasses = 128 / kRowsPerPass;
+  static_assert(kLPR <= 64, "a band row must fit in one wave");
+};
+
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
+__global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
                                                             int64_t K, uint8_t* __restrict__ data,
                                                             uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                            uint32_t tiles_per_row) {
-  constexpr int EPL = Fmt<T>::kEPL;
-  constexpr int kChunksPerRow = 128 / EPL;                 // 16 (bf16) / 32 (fp32)
-  constexpr int kRowsPerPass = kThreads / kChunksPerRow;   // 16 / 8
-  constexpr int kPasses = 128 / kRowsPerPass;              // 8 / 16
-  __shared__ uint32_t s_wave_max[kThreads / 64];
+                                                            uint32_t tiles_per_row, uint32_t groups_per_row) {
+  using G = FoldGeom<T>;
+  constexpr int EPL = G::kEPL, J = G::kJ, CPT = G::kCPT, LPR = G::kLPR, P = G::kPasses;
+  __shared__ uint32_t s_max[kFoldWaves][J];
   keep_denormals();
 
-  const uint32_t tid = threadIdx.x;
-  const uint32_t tr = blockIdx.x / tiles_per_row, tc = blockIdx.x - tr * tiles_per_row;
-  const int64_t r0 = (int64_t)tr * 128 + tid / kChunksPerRow;
-  const int64_t col0 = (int64_t)tc * 128 + (tid % kChunksPerRow) * EPL;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+#if MXQ_TILE_COLUMN_MAJOR
+  const uint32_t band_count = gridDim.x / groups_per_row;
+  const uint32_t tg = blockIdx.x / band_count, tr = blockIdx.x - tg * band_count;
+#else
+  const uint32_t tr = blockIdx.x / groups_per_row, tg = blockIdx.x - tr * groups_per_row;
+#endif
+  const uint32_t j = (tid % LPR) / CPT;                    // this lane's tile within the group
+  const int64_t r0 = (int64_t)tr * 128 + tid / LPR;
+  const int64_t col0 = (int64_t)tg * (128 * J) + (tid % LPR) * EPL;
 
-  u32x4 w[kPasses];
+  u32x4 w[P];
 #pragma unroll
-  for (int i = 0; i < kPasses; i++) {
-    const int64_t r = r0 + i * kRowsPerPass;
+  for (int i = 0; i < P; i++) {
+    const int64_t r = r0 + i * G::kRowsPerPass;
     w[i] = (r < rows) ? load_chunk<T, VEC>(x + r * ld_x, col0, K) : u32x4{0u, 0u, 0u, 0u};
   }
-  uint32_t f[kPasses], eb[kPasses];
-  uint32_t poisoned = 0u;                                  // bit i: chunk i's block is poisoned
+  uint32_t f[P], eb[P];
+  uint64_t poisoned = 0u;                                  // bit i: chunk i's block is poisoned
   uint32_t m = 1u;
 #pragma unroll
-  for (int i = 0; i < kPasses; i++) {
+  for (int i = 0; i < P; i++) {
     const Block b = chunk_block<T>(w[i]);
     eb[i] = b.eb;
     f[i] = fp4_of(w[i], e8m0(b.eb), T{});
-    poisoned |= (uint32_t)b.poison << i;
+    poisoned |= (uint64_t)b.poison << i;
     if (!b.poison) m = max(m, b.eb);
   }
-  m = wave_max(m);
-  if ((tid & 63u) == 0u) s_wave_max[tid >> 6] = m;
+  m = max16(m);
+  if constexpr (CPT == 32) m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+#pragma unroll
+  for (int off = LPR; off < 64; off *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if (lane < (uint32_t)LPR && lane % CPT == 0) s_max[wave][j] = m;
   __syncthreads();
-  m = max(max(s_wave_max[0], s_wave_max[1]), max(s_wave_max[2], s_wave_max[3]));
+#pragma unroll
+  for (int v = 0; v < kFoldWaves; v++) m = max(m, s_max[v][j]);
   const uint32_t code = m > 6u ? m - 6u : 0u;              // S + 127 = max(M - 6, -127) + 127
-  if (tid == 0) tile_code[(int64_t)tr * tile_ld + tc] = (uint8_t)code;
+  const uint32_t tc = tg * J + j;
+  if (tid < (uint32_t)LPR && tid % CPT == 0 && tc < tiles_per_row) tile_code[(int64_t)tr * tile_ld + tc] = (uint8_t)code;
 
 #pragma unroll
-  for (int i = 0; i < kPasses; i++) {
-    const int64_t r = r0 + i * kRowsPerPass;
+  for (int i = 0; i < P; i++) {
+    const int64_t r = r0 + i * G::kRowsPerPass;
     const Proj16<T> p = project<T>(f[i], e8m0(eb[i]));
     const auto q = payload_chunk<T>(p, code, (poisoned >> i) & 1u);
     if (r < rows) store_payload<T, VEC>(data + r * K, col0, K, q);
@@ -491,8 +537,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 8;
-  for (int u = 0; u < kStepsPerWG; u++) {
-    const uint32_t step = blockIdx.x * kStepsPerWG + u;
+  for (int u = 0; u < kDequantSteps; u++) {
+    const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
     const int64_t col0 = (int64_t)seg * 2048 + lane_col;
@@ -547,14 +593,18 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------------------------
-// Export: strided copy of the first ncols columns of each row.
+// Export: strided copy of the first ncols columns of each row, in units of V
+// (16, 4 or 1 bytes, whichever the pointers, strides and width allow).
 // ------------------------------------------------------------------------------------
+template <typename V>
 __global__ __launch_bounds__(kThreads) void export_kernel(const uint8_t* __restrict__ src, int64_t src_ld,
-                                                          uint8_t* __restrict__ dst, int64_t rows, int64_t ncols) {
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < ncols; j += (int64_t)gridDim.x * kThreads)
-      dst[r * ncols + j] = src[r * src_ld + j];
-  }
+                                                          uint8_t* __restrict__ dst, uint32_t units_per_row,
+                                                          uint32_t total_units) {
+  // one V-sized unit per lane, rows flattened, so short rows still fill whole waves
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total_units) return;
+  const uint32_t r = i / units_per_row, j = i - r * units_per_row;
+  reinterpret_cast<V*>(dst)[i] = reinterpret_cast<const V*>(src + (int64_t)r * src_ld)[j];
 }
 
 // ------------------------------------------------------------------------------------
@@ -586,7 +636,7 @@ int steps_for(int64_t rows, int64_t K, int64_t elems_per_step, uint32_t* per_row
   return MXQ_OK;
 }
 
-uint32_t grid_for(uint32_t total_steps) { return (total_steps + kStepsPerWG - 1) / kStepsPerWG; }
+uint32_t grid_for(uint32_t total_steps, int per_wg) { return (total_steps + per_wg - 1) / per_wg; }
 
 int check_dtype(mxq_dtype dt) {
   return (dt == MXQ_BF16 || dt == MXQ_FP32) ? MXQ_OK : MXQ_ERR_DTYPE;
@@ -599,7 +649,7 @@ int launch_proj(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows
   if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && aligned(y, 16) && ld_x % EPL == 0 && ld_y % EPL == 0 && K % EPL == 0;
-  const dim3 grid(grid_for(total)), block(kThreads);
+  const dim3 grid(grid_for(total, kProjSteps)), block(kThreads);
   if (vec)
     hipLaunchKernelGGL((proj_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, (T*)y, ld_y, K, spr, total);
   else
@@ -614,7 +664,7 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
   if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL);
-  const dim3 grid(grid_for(total)), block(kThreads);
+  const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
   if (vec)
     hipLaunchKernelGGL((row_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, spr,
                        total);
@@ -627,17 +677,18 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
 template <typename T>
 int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* data, uint8_t* tile_code,
                     int64_t tile_ld, hipStream_t s) {
-  const int64_t tpr = (K + 127) / 128, tiles = tpr * ((rows + 127) / 128);
-  if (tiles >= kMaxSteps) return MXQ_ERR_SHAPE;
+  constexpr int J = FoldGeom<T>::kJ;
+  const int64_t tpr = (K + 127) / 128, gpr = (tpr + J - 1) / J, groups = gpr * ((rows + 127) / 128);
+  if (groups >= kMaxSteps) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL);
-  const dim3 grid((uint32_t)tiles), block(kThreads);
+  const dim3 grid((uint32_t)groups), block(kFoldThreads);
   if (vec)
     hipLaunchKernelGGL((block128_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data, tile_code,
-                       tile_ld, (uint32_t)tpr);
+                       tile_ld, (uint32_t)tpr, (uint32_t)gpr);
   else
     hipLaunchKernelGGL((block128_kernel<T, false>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data, tile_code,
-                       tile_ld, (uint32_t)tpr);
+                       tile_ld, (uint32_t)tpr, (uint32_t)gpr);
   return launch_status();
 }
 
@@ -648,7 +699,7 @@ int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld
   if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
   const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
-  const dim3 grid(grid_for(total)), block(kThreads);
+  const dim3 grid(grid_for(total, kDequantSteps)), block(kThreads);
   if (vec)
     hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kTile, true>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
@@ -741,9 +792,19 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
   if (scale_out == scale_storage && scale_ld == nb) return MXQ_OK;          // already unpadded: a view
   if (overlap(matrix_range(scale_storage, rows, nb, scale_ld, 1), matrix_range(scale_out, rows, nb, nb, 1)))
     return MXQ_ERR_ALIAS;
-  const int64_t gx = (nb + kThreads - 1) / kThreads;
-  const dim3 grid((uint32_t)(gx < 65535 ? gx : 65535), (uint32_t)(rows < 65535 ? rows : 65535)), block(kThreads);
-  hipLaunchKernelGGL(export_kernel, grid, block, 0, stream, scale_storage, scale_ld, scale_out, rows, nb);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(scale_storage) | reinterpret_cast<uintptr_t>(scale_out);
+  const int64_t width = (a % 16 == 0 && scale_ld % 16 == 0 && nb % 16 == 0) ? 16
+                        : (a % 4 == 0 && scale_ld % 4 == 0 && nb % 4 == 0) ? 4 : 1;
+  const int64_t units = rows * (nb / width);
+  if (units >= kMaxSteps * 2) return MXQ_ERR_SHAPE;
+  const dim3 grid((uint32_t)((units + kThreads - 1) / kThreads)), block(kThreads);
+  const uint32_t upr = (uint32_t)(nb / width), total = (uint32_t)units;
+  if (width == 16)
+    hipLaunchKernelGGL(export_kernel<u32x4>, grid, block, 0, stream, scale_storage, scale_ld, scale_out, upr, total);
+  else if (width == 4)
+    hipLaunchKernelGGL(export_kernel<uint32_t>, grid, block, 0, stream, scale_storage, scale_ld, scale_out, upr, total);
+  else
+    hipLaunchKernelGGL(export_kernel<uint8_t>, grid, block, 0, stream, scale_storage, scale_ld, scale_out, upr, total);
   return launch_status();
 }
 
