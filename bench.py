@@ -54,6 +54,12 @@ def algorithmic_bytes(rows: int, K: int) -> dict:
     }
 
 
+def fused_bytes(rows: int, K: int) -> int:
+    """Projection + row lift from one read: 2n in, 2n + n + n/32 out (bf16)."""
+    n = rows * K
+    return 2 * n + 2 * n + n + rows * ((K + 31) // 32)
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -85,9 +91,22 @@ def cpu_baseline(bits, threads: int) -> dict:
     oracle.dequantize(bd, tc, layout=oracle.TILE_128X128, threads=threads)
     dt = time.perf_counter() - t0
     total = sum(algorithmic_bytes(*bits.shape).values())
-    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} bf16 weight, one pass of all six steps "
-                      f"({dt:.1f} s wall on {threads} threads)"}
+    out = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} bf16 weight, one pass of all six steps "
+                     f"({dt:.1f} s wall on {threads} threads)"}
+    # the same steps on one thread, over the first 512 rows
+    sub = bits[:512]
+    t0 = time.perf_counter()
+    oracle.fake_quantize_mxfp4(sub)
+    d, s = oracle.mxfp4_to_mxfp8_row(sub, scale_ld=SCALE_LD)
+    c = oracle.export_mxfp8(s, sub.shape[1])
+    bd, tc = oracle.mxfp4_to_fp8_block128(sub)
+    oracle.dequantize(d, c)
+    oracle.dequantize(bd, tc, layout=oracle.TILE_128X128)
+    dt1 = time.perf_counter() - t0
+    out["one_thread"] = {"value": round(sum(algorithmic_bytes(*sub.shape).values()) / dt1 / 1e9, 3), "unit": "GB/s",
+                         "sample": f"rows 0..511 of the same weight, one pass of all six steps ({dt1:.1f} s)"}
+    return out
 
 
 def main():
@@ -128,6 +147,9 @@ def main():
             "tc": torch.empty(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev),
             "dec_r": torch.empty_like(x0),
             "dec_t": torch.empty_like(x0),
+            "y2": torch.empty_like(x0),
+            "data2": torch.empty((rows, K), dtype=torch.uint8, device=dev),
+            "scale2": torch.zeros((rows, SCALE_LD), dtype=torch.uint8, device=dev),
         }
         mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
         mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
@@ -146,8 +168,10 @@ def main():
         "dec_tile": lambda s: mxq.mxq_dequantize(s["bdata"], s["tc"], layout=mxq.MXQ_SCALE_TILE_128X128,
                                                  out=s["dec_t"]),
     }
+    # outside the step: projection + row lift fused into one pass (one read of x)
+    launches["fused"] = lambda s: mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(s["x"], s["y2"], s["data2"], s["scale2"])
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
-    offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5}
+    offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -156,8 +180,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     bursts = {}
 
-    def run(i0: int, k: int, timed: bool):
-        for n in names:
+    def run(i0: int, k: int, timed: bool, which=names):
+        for n in which:
             if timed:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -173,6 +197,9 @@ def main():
     run(args.warmup, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    run(0, args.warmup, False, ["fused"])
+    run(args.warmup, args.steps, True, ["fused"])
+    torch.cuda.synchronize()
 
     if args.calibrate:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -191,6 +218,12 @@ def main():
         gbs = nbytes[n] / (us * 1e-6) / 1e9
         kernels[n] = {"us": round(us, 2), "bytes": nbytes[n], "GB/s": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    a, b = bursts["fused"]
+    us = 1e3 * a.elapsed_time(b) / args.steps
+    fb = fused_bytes(rows, K)
+    extra = {"fused_proj_row": {"us": round(us, 2), "bytes": fb, "GB/s": round(fb / (us * 1e-6) / 1e9, 1),
+                                "frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "vs_separate_us": round(kernels["proj"]["us"] + kernels["row"]["us"], 2)}}
     dominant = max(names, key=lambda n: kernels[n]["us"])
     rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
           "unit": "GB/s", "frac": kernels[dominant]["frac"], "traffic": read_traffic(dominant)}
@@ -212,6 +245,7 @@ def main():
                    "bytes_per_step": total, "buffer_sets": NSETS},
         "roofline": rl,
         "kernels": kernels,
+        "outside_step": extra,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(bits, threads=min(16, os.cpu_count() or 1))

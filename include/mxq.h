@@ -7,6 +7,10 @@
  *   mxq_mxfp4_to_fp8_block128   direct 128x128 blockwise FP8 (E4M3 payload + tile codes)
  *   mxq_export_mxfp8            unpadded (*shape[:-1], ceil(K/32)) E8M0 scale export
  *   mxq_dequantize              FP8 payload + E8M0 codes -> bf16 / fp32
+ * and three variants of them:
+ *   mxq_fake_quantize_mxfp4_with_mxfp8_row    projection + row lift in one pass
+ *   mxq_mxfp4_to_mxfp8_row_guarded,
+ *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
  *
  * Sources, by page title and section:
  *   [QAT] "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8 block-scaling recipes"
@@ -27,7 +31,9 @@
  *     enqueued; no kernel asserts on the device.
  *   - rows == 0 or K == 0 returns MXQ_OK and enqueues nothing.
  *   - Results are bit-exact and do not depend on the build's floating-point
- *     flags: every step is integer arithmetic.
+ *     flags: the scale exponents are integer arithmetic on bit patterns, and the
+ *     kernels set the wave's denormal mode before using the gfx950 scaled
+ *     conversions.
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -120,6 +126,34 @@ int mxq_mxfp4_to_mxfp8_row(const void* x, int64_t ld_x, int64_t rows, int64_t K,
  */
 int mxq_mxfp4_to_fp8_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
                               uint8_t* data, uint8_t* tile_code, int64_t tile_ld, hipStream_t stream);
+
+/*
+ * Projection and direct MXFP8 row lift in one pass over the weight: writes the
+ * outputs of mxq_fake_quantize_mxfp4 (y) and of mxq_mxfp4_to_mxfp8_row (data,
+ * scale) from a single read of x.  [QAT] Known limitations names a fused
+ * projection + quantize kernel as future work; the results are bit-identical to
+ * the two separate calls.  Arguments and rules as for those two calls (y == x
+ * with ld_y == ld_x is allowed; every other overlap is MXQ_ERR_ALIAS).
+ */
+int mxq_fake_quantize_mxfp4_with_mxfp8_row(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                                           int64_t K, mxq_dtype dt, uint8_t* data, uint8_t* scale,
+                                           int64_t scale_ld, hipStream_t stream);
+
+/*
+ * mxq_mxfp4_to_mxfp8_row / mxq_mxfp4_to_fp8_block128 gated by a device-side
+ * no-op flag: when *noop != 0 at the time the work runs on the stream, every
+ * output is left untouched.  For cached-weight updates inside a captured HIP
+ * graph, where a replay must be able to keep the existing workspace ([QAT]
+ * review: the CUDA-graph skip-update flag must gate the cached update).
+ *   noop   device pointer to one int32, read by the kernels; required (NULL ->
+ *          MXQ_ERR_NULL).  Other arguments as for the ungated calls.
+ */
+int mxq_mxfp4_to_mxfp8_row_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                   uint8_t* data, uint8_t* scale, int64_t scale_ld, const int32_t* noop,
+                                   hipStream_t stream);
+int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                      uint8_t* data, uint8_t* tile_code, int64_t tile_ld, const int32_t* noop,
+                                      hipStream_t stream);
 
 /*
  * Unpadded export of MXFP8 rowwise scales, [EXP] Description: scale_inv holds

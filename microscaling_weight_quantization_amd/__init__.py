@@ -31,7 +31,9 @@ MXQ_SCALE_ROW_1X32, MXQ_SCALE_TILE_128X128 = 0, 1
 MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_DTYPE, MXQ_ERR_NO_ROWWISE_DATA, MXQ_ERR_ALIAS, MXQ_ERR_HIP = range(7)
 
 ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mxfp8_row",
-                "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize")
+                "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize",
+                "mxq_fake_quantize_mxfp4_with_mxfp8_row", "mxq_mxfp4_to_mxfp8_row_guarded",
+                "mxq_mxfp4_to_fp8_block128_guarded")
 
 _libs = {}
 _lock = threading.Lock()
@@ -61,6 +63,9 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_mxfp4_to_fp8_block128.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
         L.mxq_export_mxfp8.argtypes = [u8p, u8p, i64, i64, i64, u8p, vp]
         L.mxq_dequantize.argtypes = [u8p, u8p, i64, i64, i64, i32, i32, vp, i64, i32, vp]
+        L.mxq_fake_quantize_mxfp4_with_mxfp8_row.argtypes = [vp, i64, vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
+        L.mxq_mxfp4_to_mxfp8_row_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
+        L.mxq_mxfp4_to_fp8_block128_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -99,6 +104,12 @@ def _matrix(t: torch.Tensor):
     return t.data_ptr(), rows, K, ld
 
 
+def _flag(t: torch.Tensor) -> int:
+    if t.dtype != torch.int32 or not t.is_cuda or t.numel() < 1:
+        raise ValueError("the no-op flag is a device int32 tensor")
+    return t.data_ptr()
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -120,8 +131,10 @@ def mxq_fake_quantize_mxfp4(x: torch.Tensor, y: Optional[torch.Tensor] = None, l
 
 
 def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
-                           scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
-    """Direct MXFP8 rowwise lift -> (payload uint8 [rows, K], E8M0 codes uint8 [rows, scale_ld])."""
+                           scale_ld: Optional[int] = None, lib: str = "libmxq.so",
+                           noop: Optional[torch.Tensor] = None):
+    """Direct MXFP8 rowwise lift -> (payload uint8 [rows, K], E8M0 codes uint8 [rows, scale_ld]).
+    With `noop` (an int32 device tensor) this is mxq_mxfp4_to_mxfp8_row_guarded."""
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
@@ -134,13 +147,18 @@ def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     ps, _, sld, ld_s = _matrix(scale)
     if rows * K and (ldd != K or data.numel() != rows * K):
         raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
-    _check(L, L.mxq_mxfp4_to_mxfp8_row(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    if noop is None:
+        _check(L, L.mxq_mxfp4_to_mxfp8_row(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    else:
+        _check(L, L.mxq_mxfp4_to_mxfp8_row_guarded(px, ldx, rows, K, dt, pd, ps, ld_s, _flag(noop), _stream(x)))
     return data, scale
 
 
 def mxq_mxfp4_to_fp8_block128(x: torch.Tensor, data: Optional[torch.Tensor] = None,
-                              tile_code: Optional[torch.Tensor] = None, lib: str = "libmxq.so"):
-    """Direct 128x128 blockwise FP8 -> (payload uint8 [rows, K], tile codes uint8 [ceil(rows/128), tile_ld])."""
+                              tile_code: Optional[torch.Tensor] = None, lib: str = "libmxq.so",
+                              noop: Optional[torch.Tensor] = None):
+    """Direct 128x128 blockwise FP8 -> (payload uint8 [rows, K], tile codes uint8 [ceil(rows/128), tile_ld]).
+    With `noop` (an int32 device tensor) this is mxq_mxfp4_to_fp8_block128_guarded."""
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
@@ -152,8 +170,34 @@ def mxq_mxfp4_to_fp8_block128(x: torch.Tensor, data: Optional[torch.Tensor] = No
     pt, trows, tcols, ldt = _matrix(tile_code)
     if rows * K and (ldd != K or data.numel() != rows * K):
         raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
-    _check(L, L.mxq_mxfp4_to_fp8_block128(px, ldx, rows, K, dt, pd, pt, ldt, _stream(x)))
+    if noop is None:
+        _check(L, L.mxq_mxfp4_to_fp8_block128(px, ldx, rows, K, dt, pd, pt, ldt, _stream(x)))
+    else:
+        _check(L, L.mxq_mxfp4_to_fp8_block128_guarded(px, ldx, rows, K, dt, pd, pt, ldt, _flag(noop), _stream(x)))
     return data, tile_code
+
+
+def mxq_fake_quantize_mxfp4_with_mxfp8_row(x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                                           data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                                           scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+    """Projection and row lift from one read of x -> (y, payload, codes)."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    px, rows, K, ldx = _matrix(x)
+    nb = (K + 31) // 32
+    if y is None:
+        y = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if scale is None:
+        scale = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=x.device)
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    py, _, _, ldy = _matrix(y)
+    pd, _, _, ldd = _matrix(data)
+    ps, _, _, ld_s = _matrix(scale)
+    if rows * K and (ldd != K or data.numel() != rows * K):
+        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    _check(L, L.mxq_fake_quantize_mxfp4_with_mxfp8_row(px, ldx, py, ldy, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    return y, data, scale
 
 
 def mxq_export_mxfp8(data: Optional[torch.Tensor], scale_storage: Optional[torch.Tensor], K: int,

@@ -359,12 +359,22 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(const T* __restrict__ x,
   }
 }
 
-template <typename T, bool VEC>
+// A no-op flag (device memory, read once per workgroup): when it is non-zero the
+// launch leaves every output untouched, so a captured graph can replay a cached
+// update conditionally.
+__device__ __forceinline__ bool skipped(const int32_t* __restrict__ noop) {
+  return noop != nullptr && *reinterpret_cast<const volatile int32_t*>(noop) != 0;
+}
+
+// Row lift; with kProj it also writes the projection y (the fused one-pass form).
+template <typename T, bool VEC, bool kProj>
 __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                        uint8_t* __restrict__ data, uint8_t* __restrict__ scale,
-                                                       int64_t scale_ld, uint32_t steps_per_row,
-                                                       uint32_t total_steps) {
+                                                       int64_t scale_ld, T* __restrict__ y, int64_t ld_y,
+                                                       uint32_t steps_per_row, uint32_t total_steps,
+                                                       const int32_t* __restrict__ noop) {
   using G = StepGeom<T>;
+  if (skipped(noop)) return;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
@@ -388,6 +398,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
       const float s = e8m0(b.eb);
       const uint32_t code = row_code(b);
       const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
+      if constexpr (kProj) store_chunk<T, VEC>(y + (int64_t)row * ld_y, col0, K, proj_chunk<T>(p, b.poison));
       store_payload<T, VEC>(data + (int64_t)row * K, col0, K, payload_chunk<T>(p, code, b.poison));
       if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)code;
     }
@@ -437,10 +448,12 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
                                                             int64_t K, uint8_t* __restrict__ data,
                                                             uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                            uint32_t tiles_per_row, uint32_t groups_per_row) {
+                                                            uint32_t tiles_per_row, uint32_t groups_per_row,
+                                                            const int32_t* __restrict__ noop) {
   using G = FoldGeom<T>;
   constexpr int EPL = G::kEPL, J = G::kJ, CPT = G::kCPT, LPR = G::kLPR, P = G::kPasses;
   __shared__ uint32_t s_max[kFoldWaves][J];
+  if (skipped(noop)) return;
   keep_denormals();
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
@@ -659,24 +672,28 @@ int launch_proj(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows
 
 template <typename T>
 int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* data, uint8_t* scale,
-               int64_t scale_ld, hipStream_t s) {
+               int64_t scale_ld, void* y, int64_t ld_y, const int32_t* noop, hipStream_t s) {
   uint32_t spr, total;
   if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
-  const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL);
+  const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
+                   (y == nullptr || (aligned(y, 16) && ld_y % EPL == 0));
   const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
-  if (vec)
-    hipLaunchKernelGGL((row_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, spr,
-                       total);
-  else
-    hipLaunchKernelGGL((row_kernel<T, false>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, spr,
-                       total);
+#define MXQ_ROW_LAUNCH(V, P)                                                                                  \
+  hipLaunchKernelGGL((row_kernel<T, V, P>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \
+                     (T*)y, ld_y, spr, total, noop)
+  if (y != nullptr) {
+    if (vec) MXQ_ROW_LAUNCH(true, true); else MXQ_ROW_LAUNCH(false, true);
+  } else {
+    if (vec) MXQ_ROW_LAUNCH(true, false); else MXQ_ROW_LAUNCH(false, false);
+  }
+#undef MXQ_ROW_LAUNCH
   return launch_status();
 }
 
 template <typename T>
 int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* data, uint8_t* tile_code,
-                    int64_t tile_ld, hipStream_t s) {
+                    int64_t tile_ld, const int32_t* noop, hipStream_t s) {
   constexpr int J = FoldGeom<T>::kJ;
   const int64_t tpr = (K + 127) / 128, gpr = (tpr + J - 1) / J, groups = gpr * ((rows + 127) / 128);
   if (groups >= kMaxSteps) return MXQ_ERR_SHAPE;
@@ -685,10 +702,10 @@ int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_
   const dim3 grid((uint32_t)groups), block(kFoldThreads);
   if (vec)
     hipLaunchKernelGGL((block128_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data, tile_code,
-                       tile_ld, (uint32_t)tpr, (uint32_t)gpr);
+                       tile_ld, (uint32_t)tpr, (uint32_t)gpr, noop);
   else
     hipLaunchKernelGGL((block128_kernel<T, false>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data, tile_code,
-                       tile_ld, (uint32_t)tpr, (uint32_t)gpr);
+                       tile_ld, (uint32_t)tpr, (uint32_t)gpr, noop);
   return launch_status();
 }
 
@@ -751,34 +768,70 @@ int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y, 
                         : launch_proj<uint32_t>(x, ld_x, y, ld_y, rows, K, stream);
 }
 
-int mxq_mxfp4_to_mxfp8_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
-                           uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
+static int row_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                     uint8_t* scale, int64_t scale_ld, void* y, int64_t ld_y, bool need_y, const int32_t* noop,
+                     bool need_noop, hipStream_t stream) {
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (rows == 0 || K == 0) return MXQ_OK;
-  if (!x || !data || !scale) return MXQ_ERR_NULL;
+  if (!x || !data || !scale || (need_noop && !noop) || (need_y && !y)) return MXQ_ERR_NULL;
   const int64_t nb = (K + 31) / 32;
-  if (ld_x < K || scale_ld < nb) return MXQ_ERR_SHAPE;
-  const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), rd = matrix_range(data, rows, K, K, 1),
+  if (ld_x < K || scale_ld < nb || (y && ld_y < K)) return MXQ_ERR_SHAPE;
+  const size_t es = dtype_size(dt);
+  const Range rx = matrix_range(x, rows, K, ld_x, es), rd = matrix_range(data, rows, K, K, 1),
               rs = matrix_range(scale, rows, nb, scale_ld, 1);
   if (overlap(rx, rd) || overlap(rx, rs) || overlap(rd, rs)) return MXQ_ERR_ALIAS;
-  return dt == MXQ_BF16 ? launch_row<uint16_t>(x, ld_x, rows, K, data, scale, scale_ld, stream)
-                        : launch_row<uint32_t>(x, ld_x, rows, K, data, scale, scale_ld, stream);
+  if (y) {
+    const Range ry = matrix_range(y, rows, K, ld_y, es);
+    const bool in_place = (x == y) && (ld_x == ld_y);
+    if ((!in_place && overlap(rx, ry)) || overlap(ry, rd) || overlap(ry, rs)) return MXQ_ERR_ALIAS;
+  }
+  return dt == MXQ_BF16 ? launch_row<uint16_t>(x, ld_x, rows, K, data, scale, scale_ld, y, ld_y, noop, stream)
+                        : launch_row<uint32_t>(x, ld_x, rows, K, data, scale, scale_ld, y, ld_y, noop, stream);
 }
 
-int mxq_mxfp4_to_fp8_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
-                              uint8_t* tile_code, int64_t tile_ld, hipStream_t stream) {
+static int block128_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                          uint8_t* tile_code, int64_t tile_ld, const int32_t* noop, bool need_noop,
+                          hipStream_t stream) {
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (rows == 0 || K == 0) return MXQ_OK;
-  if (!x || !data || !tile_code) return MXQ_ERR_NULL;
+  if (!x || !data || !tile_code || (need_noop && !noop)) return MXQ_ERR_NULL;
   const int64_t ntc = (K + 127) / 128, ntr = (rows + 127) / 128;
   if (ld_x < K || tile_ld < ntc) return MXQ_ERR_SHAPE;
   const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), rd = matrix_range(data, rows, K, K, 1),
               rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
   if (overlap(rx, rd) || overlap(rx, rt) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
-  return dt == MXQ_BF16 ? launch_block128<uint16_t>(x, ld_x, rows, K, data, tile_code, tile_ld, stream)
-                        : launch_block128<uint32_t>(x, ld_x, rows, K, data, tile_code, tile_ld, stream);
+  return dt == MXQ_BF16 ? launch_block128<uint16_t>(x, ld_x, rows, K, data, tile_code, tile_ld, noop, stream)
+                        : launch_block128<uint32_t>(x, ld_x, rows, K, data, tile_code, tile_ld, noop, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                           uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
+  return row_entry(x, ld_x, rows, K, dt, data, scale, scale_ld, nullptr, 0, false, nullptr, false, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_row_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                   uint8_t* data, uint8_t* scale, int64_t scale_ld, const int32_t* noop,
+                                   hipStream_t stream) {
+  return row_entry(x, ld_x, rows, K, dt, data, scale, scale_ld, nullptr, 0, false, noop, true, stream);
+}
+
+int mxq_fake_quantize_mxfp4_with_mxfp8_row(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                                           int64_t K, mxq_dtype dt, uint8_t* data, uint8_t* scale,
+                                           int64_t scale_ld, hipStream_t stream) {
+  return row_entry(x, ld_x, rows, K, dt, data, scale, scale_ld, y, ld_y, true, nullptr, false, stream);
+}
+
+int mxq_mxfp4_to_fp8_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                              uint8_t* tile_code, int64_t tile_ld, hipStream_t stream) {
+  return block128_entry(x, ld_x, rows, K, dt, data, tile_code, tile_ld, nullptr, false, stream);
+}
+
+int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                      uint8_t* data, uint8_t* tile_code, int64_t tile_ld, const int32_t* noop,
+                                      hipStream_t stream) {
+  return block128_entry(x, ld_x, rows, K, dt, data, tile_code, tile_ld, noop, true, stream);
 }
 
 int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t rows, int64_t K, int64_t scale_ld,

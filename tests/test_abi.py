@@ -25,9 +25,8 @@ def lib():
     return mxq.load()
 
 
-def test_header_declares_the_five_entry_points():
-    assert declared() == sorted(["mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mxfp8_row",
-                                 "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize"])
+def test_header_declares_the_entry_points():
+    assert declared() == sorted(mxq.ENTRY_POINTS)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -71,6 +70,13 @@ def test_host_validation_without_a_gpu(lib):
     assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, mxq.MXQ_BF16, P(0x200000), P(0x300000), 1, None) == mxq.MXQ_ERR_SHAPE
     assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, mxq.MXQ_BF16, P(0x200000), P(0x200010), 2, None) == mxq.MXQ_ERR_ALIAS
     assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, mxq.MXQ_BF16, P(0x100040), P(0x300000), 2, None) == mxq.MXQ_ERR_ALIAS
+    # fused projection + row lift: y required, y must not overlap the payload
+    assert lib.mxq_fake_quantize_mxfp4_with_mxfp8_row(fake, 64, None, 64, 4, 64, 0, P(0x200000), P(0x300000), 2, None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_fake_quantize_mxfp4_with_mxfp8_row(fake, 64, P(0x200000), 64, 4, 64, 0, P(0x200010), P(0x300000), 2, None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_fake_quantize_mxfp4_with_mxfp8_row(fake, 64, fake, 64, 4, 64, mxq.MXQ_FP16, P(0x200000), P(0x300000), 2, None) == mxq.MXQ_ERR_DTYPE
+    # guarded variants need their flag
+    assert lib.mxq_mxfp4_to_mxfp8_row_guarded(fake, 64, 4, 64, 0, P(0x200000), P(0x300000), 2, None, None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_mxfp4_to_fp8_block128_guarded(fake, 256, 4, 256, 0, P(0x200000), P(0x300000), 2, None, None) == mxq.MXQ_ERR_NULL
     # block128: tile_ld too small
     assert lib.mxq_mxfp4_to_fp8_block128(fake, 256, 4, 256, mxq.MXQ_FP32, P(0x200000), P(0x300000), 1, None) == mxq.MXQ_ERR_SHAPE
     # export: no row-scaled data, the view case, bad stride

@@ -161,6 +161,90 @@ def test_every_value_at_every_block_exponent(dev, dtype):
     check_all(W.value_exponent_pairs(dtype), dev)
 
 
+@pytest.mark.parametrize("which", ["c1", "planted", "fuzz", "c4"])
+def test_fused_projection_and_row_lift(dev, which):
+    """One pass writes exactly what the two separate calls write (the oracle's
+    projection and row lift), including in place."""
+    bits = {"c1": W.c1_small, "planted": W.c2_planted, "fuzz": lambda: W.fp32_fuzz(1 << 16).reshape(-1, 128),
+            "c4": W.c4_headline}[which]()
+    rows, K = bits.shape
+    nb = (K + 31) // 32
+    x = to_dev(bits, dev)
+    scale = torch.full((rows, nb + 3), 0x5A, dtype=torch.uint8, device=dev)
+    y, data, scale = mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x, scale=scale)
+    wd, ws = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=nb + 3, threads=THREADS, fill=0x5A)
+    assert_bits(to_host(y), oracle.fake_quantize_mxfp4(bits, threads=THREADS), "fused projection")
+    assert_bits(to_host(data), wd, "fused payload")
+    assert_bits(to_host(scale), ws, "fused codes")
+    if which == "c1":
+        mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x, y=x)
+        assert_bits(to_host(x), oracle.fake_quantize_mxfp4(bits), "fused projection in place")
+
+
+def test_noop_flag_gates_the_direct_conversions(dev):
+    bits = W.c4_headline(shape=(512, 1024))
+    x = to_dev(bits, dev)
+    wd, ws = oracle.mxfp4_to_mxfp8_row(bits)
+    wbd, wtc = oracle.mxfp4_to_fp8_block128(bits)
+    flag = torch.ones(1, dtype=torch.int32, device=dev)
+    data = torch.full((512, 1024), 0x11, dtype=torch.uint8, device=dev)
+    scale = torch.full((512, 32), 0x22, dtype=torch.uint8, device=dev)
+    bdata = torch.full((512, 1024), 0x33, dtype=torch.uint8, device=dev)
+    tc = torch.full((4, 8), 0x44, dtype=torch.uint8, device=dev)
+    mxq.mxq_mxfp4_to_mxfp8_row(x, data, scale, noop=flag)
+    mxq.mxq_mxfp4_to_fp8_block128(x, bdata, tc, noop=flag)
+    assert (to_host(data) == 0x11).all() and (to_host(scale) == 0x22).all()
+    assert (to_host(bdata) == 0x33).all() and (to_host(tc) == 0x44).all()
+    flag.zero_()
+    mxq.mxq_mxfp4_to_mxfp8_row(x, data, scale, noop=flag)
+    mxq.mxq_mxfp4_to_fp8_block128(x, bdata, tc, noop=flag)
+    assert_bits(to_host(data), wd, "gated payload")
+    assert_bits(to_host(scale), ws, "gated codes")
+    assert_bits(to_host(bdata), wbd, "gated 128x128 payload")
+    assert_bits(to_host(tc), wtc, "gated tile codes")
+
+
+def test_noop_flag_inside_a_replayed_graph(dev):
+    """A captured update replays conditionally: with the flag set the cached
+    outputs keep their previous contents, with it clear they follow the new
+    weight.  Eager work and synchronisation between replays; every replay checked."""
+    a_bits = W.c4_headline(shape=(256, 2048))
+    b_bits = W.c1_small()[:, :32]
+    b_bits = np.ascontiguousarray(np.tile(b_bits, (3, 64))[:256, :2048])
+    x = to_dev(a_bits, dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    data = torch.empty((256, 2048), dtype=torch.uint8, device=dev)
+    scale = torch.empty((256, 64), dtype=torch.uint8, device=dev)
+    bdata = torch.empty((256, 2048), dtype=torch.uint8, device=dev)
+    tc = torch.empty((2, 16), dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm up outside the graph
+        mxq.mxq_mxfp4_to_mxfp8_row(x, data, scale, noop=flag)
+        mxq.mxq_mxfp4_to_fp8_block128(x, bdata, tc, noop=flag)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mxq.mxq_mxfp4_to_mxfp8_row(x, data, scale, noop=flag)
+        mxq.mxq_mxfp4_to_fp8_block128(x, bdata, tc, noop=flag)
+    want = {}
+    for name, bits in (("a", a_bits), ("b", b_bits)):
+        want[name] = oracle.mxfp4_to_mxfp8_row(bits) + oracle.mxfp4_to_fp8_block128(bits)
+    for step, (src, skip, expect) in enumerate([("a", 0, "a"), ("b", 1, "a"), ("b", 0, "b"), ("a", 1, "b"),
+                                                ("a", 0, "a")]):
+        x.copy_(to_dev(a_bits if src == "a" else b_bits, dev))      # eager work between replays
+        flag.fill_(skip)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        wd, ws, wbd, wtc = want[expect]
+        assert_bits(to_host(data), wd, f"replay {step} payload")
+        assert_bits(to_host(scale), ws, f"replay {step} codes")
+        assert_bits(to_host(bdata), wbd, f"replay {step} 128x128 payload")
+        assert_bits(to_host(tc), wtc, f"replay {step} tile codes")
+
+
 # ------------------------------------------------------------------ invariants on the device
 
 def test_decode_of_row_is_projection_c4(dev):
