@@ -60,6 +60,14 @@ def fused_bytes(rows: int, K: int) -> int:
     return 2 * n + 2 * n + n + rows * ((K + 31) // 32)
 
 
+def packed_bytes(rows: int, K: int) -> dict:
+    """Bytes of the packed-MXFP4 kernels for a [rows, K] bf16 weight."""
+    n, nb = rows * K, rows * ((K + 31) // 32)
+    tiles = ((rows + 127) // 128) * ((K + 127) // 128)
+    return {"quantize_mxfp4": 2 * n + n // 2 + nb, "dequantize_mxfp4": n // 2 + nb + 2 * n,
+            "packed_to_row": n // 2 + nb + n + nb, "packed_to_block128": n // 2 + nb + n + tiles}
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -148,12 +156,15 @@ def main():
             "dec_r": torch.empty_like(x0),
             "dec_t": torch.empty_like(x0),
             "y2": torch.empty_like(x0),
+            "packed": torch.empty((rows, K // 2), dtype=torch.uint8, device=dev),
+            "pscale": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
             "data2": torch.empty((rows, K), dtype=torch.uint8, device=dev),
             "scale2": torch.zeros((rows, SCALE_LD), dtype=torch.uint8, device=dev),
         }
         mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
         mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
         mxq.mxq_mxfp4_to_fp8_block128(s["x"], s["bdata"], s["tc"])
+        mxq.mxq_quantize_mxfp4(s["x"], s["packed"], s["pscale"])
         sets.append(s)
     del x0
     torch.cuda.synchronize()
@@ -170,8 +181,17 @@ def main():
     }
     # outside the step: projection + row lift fused into one pass (one read of x)
     launches["fused"] = lambda s: mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(s["x"], s["y2"], s["data2"], s["scale2"])
+    # outside the step: the packed MXFP4 deployment format
+    launches["quantize_mxfp4"] = lambda s: mxq.mxq_quantize_mxfp4(s["x"], s["packed"], s["pscale"])
+    launches["dequantize_mxfp4"] = lambda s: mxq.mxq_dequantize_mxfp4(s["packed"], s["pscale"], K, out=s["dec_r"])
+    launches["packed_to_row"] = lambda s: mxq.mxq_mxfp4_packed_to_mxfp8_row(s["packed"], s["pscale"], K, s["data2"],
+                                                                              s["scale2"][:, :nb])
+    launches["packed_to_block128"] = lambda s: mxq.mxq_mxfp4_packed_to_fp8_block128(s["packed"], s["pscale"], K,
+                                                                                    s["bdata"], s["tc"])
+    extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128"]
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
-    offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1}
+    offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1,
+              "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -197,8 +217,8 @@ def main():
     run(args.warmup, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    run(0, args.warmup, False, ["fused"])
-    run(args.warmup, args.steps, True, ["fused"])
+    run(0, args.warmup, False, extra_names)
+    run(args.warmup, args.steps, True, extra_names)
     torch.cuda.synchronize()
 
     if args.calibrate:
@@ -218,12 +238,15 @@ def main():
         gbs = nbytes[n] / (us * 1e-6) / 1e9
         kernels[n] = {"us": round(us, 2), "bytes": nbytes[n], "GB/s": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    a, b = bursts["fused"]
-    us = 1e3 * a.elapsed_time(b) / args.steps
-    fb = fused_bytes(rows, K)
-    extra = {"fused_proj_row": {"us": round(us, 2), "bytes": fb, "GB/s": round(fb / (us * 1e-6) / 1e9, 1),
-                                "frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                "vs_separate_us": round(kernels["proj"]["us"] + kernels["row"]["us"], 2)}}
+    extra = {}
+    extra_bytes = dict(packed_bytes(rows, K), fused=fused_bytes(rows, K))
+    for n in extra_names:
+        a, b = bursts[n]
+        us = 1e3 * a.elapsed_time(b) / args.steps
+        gbs = extra_bytes[n] / (us * 1e-6) / 1e9
+        extra["fused_proj_row" if n == "fused" else n] = {"us": round(us, 2), "bytes": extra_bytes[n],
+                                                          "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    extra["fused_proj_row"]["vs_separate_us"] = round(kernels["proj"]["us"] + kernels["row"]["us"], 2)
     dominant = max(names, key=lambda n: kernels[n]["us"])
     rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
           "unit": "GB/s", "frac": kernels[dominant]["frac"], "traffic": read_traffic(dominant)}

@@ -7,10 +7,13 @@
  *   mxq_mxfp4_to_fp8_block128   direct 128x128 blockwise FP8 (E4M3 payload + tile codes)
  *   mxq_export_mxfp8            unpadded (*shape[:-1], ceil(K/32)) E8M0 scale export
  *   mxq_dequantize              FP8 payload + E8M0 codes -> bf16 / fp32
- * and three variants of them:
+ * three variants of them:
  *   mxq_fake_quantize_mxfp4_with_mxfp8_row    projection + row lift in one pass
  *   mxq_mxfp4_to_mxfp8_row_guarded,
  *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
+ * and the packed MXFP4 deployment format:
+ *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
+ *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
  *
  * Sources, by page title and section:
  *   [QAT] "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8 block-scaling recipes"
@@ -188,6 +191,46 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
 int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                    mxq_fp8 fmt, mxq_scale_layout layout, void* out, int64_t ld_out, mxq_dtype out_dt,
                    hipStream_t stream);
+
+/*
+ * Packed MXFP4, the deployment format: E2M1 payloads with 1x32 power-of-two
+ * E8M0 scales ([QAT] Description: "training sees exactly the deployment
+ * weight"; the export issue's workflow 2, "quantize weights for inference").
+ * Layout: packed [rows, ceil(K/2)] uint8, contiguous, element 2i in the low
+ * nibble of byte i and 2i+1 in the high nibble (0 when K is odd); each nibble
+ * is S.EE.M (sign, then the 3-bit E2M1 code of {0, .5, 1, 1.5, 2, 3, 4, 6}).
+ * scale [rows, scale_ld] uint8 E8M0 codes, scale_ld >= ceil(K/32).
+ *
+ * mxq_quantize_mxfp4: the projection's decomposition (same blocks, same RTNE),
+ * except that above the cap the scale moves to 2^126 ([QAT] Known limitations):
+ * e = clamp(ceil(log2(amax/6)), -126, 126), code = e + 127.  Below the cap the
+ * decoded packed weight equals mxq_fake_quantize_mxfp4's output bit for bit.
+ * A block holding Inf or NaN gets code 255 and zero nibbles.
+ */
+int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* packed,
+                       uint8_t* scale, int64_t scale_ld, hipStream_t stream);
+
+/* Decode packed MXFP4: out = RNE_out(E2M1 * 2^(code-127)); code 255 -> canonical
+ * NaN; values beyond the output range (codes 253, 254) -> Inf.  out [rows, K]
+ * bf16 / fp32 with row stride ld_out >= K; must not overlap the inputs. */
+int mxq_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                         void* out, int64_t ld_out, mxq_dtype out_dt, hipStream_t stream);
+
+/* Direct MXFP8 row lift from packed MXFP4 (no bf16 re-encode): the fixed-shift-6
+ * lift of mxq_mxfp4_to_mxfp8_row with (p, e = code - 127) read from the packed
+ * weight: scale_out code max(code - 6, 0), payload E4M3(p * 2^min(6, code)),
+ * exact; code 255 -> code 255 and payload 0x7F.  data [rows, K] contiguous;
+ * scale_out [rows, scale_out_ld], padding columns untouched. */
+int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows,
+                                  int64_t K, uint8_t* data, uint8_t* scale_out, int64_t scale_out_ld,
+                                  hipStream_t stream);
+
+/* Direct 128x128 blockwise FP8 from packed MXFP4: the tile fold of
+ * mxq_mxfp4_to_fp8_block128 with each block's (p, e) read from the packed
+ * weight; blocks with code 255 are the poisoned ones. */
+int mxq_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows,
+                                     int64_t K, uint8_t* data, uint8_t* tile_code, int64_t tile_ld,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,8 @@ MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_DTYPE, MXQ_ERR_NO_ROWWISE_DATA, MXQ
 ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mxfp8_row",
                 "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize",
                 "mxq_fake_quantize_mxfp4_with_mxfp8_row", "mxq_mxfp4_to_mxfp8_row_guarded",
-                "mxq_mxfp4_to_fp8_block128_guarded")
+                "mxq_mxfp4_to_fp8_block128_guarded", "mxq_quantize_mxfp4", "mxq_dequantize_mxfp4",
+                "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128")
 
 _libs = {}
 _lock = threading.Lock()
@@ -66,6 +67,10 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_fake_quantize_mxfp4_with_mxfp8_row.argtypes = [vp, i64, vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
         L.mxq_mxfp4_to_mxfp8_row_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
         L.mxq_mxfp4_to_fp8_block128_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
+        L.mxq_quantize_mxfp4.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
+        L.mxq_dequantize_mxfp4.argtypes = [u8p, u8p, i64, i64, i64, vp, i64, i32, vp]
+        L.mxq_mxfp4_packed_to_mxfp8_row.argtypes = [u8p, u8p, i64, i64, i64, u8p, u8p, i64, vp]
+        L.mxq_mxfp4_packed_to_fp8_block128.argtypes = [u8p, u8p, i64, i64, i64, u8p, u8p, i64, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -231,6 +236,77 @@ def mxq_dequantize(data: torch.Tensor, scale: torch.Tensor, layout: int = MXQ_SC
     _check(L, L.mxq_dequantize(pd, ps, lds, rows, K, fmt, layout, po, ldo,
                                _dtype_code(out), _stream(data)))
     return out
+
+
+def mxq_quantize_mxfp4(x: torch.Tensor, packed: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                       scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+    """Packed MXFP4 (deployment format) -> (nibble pairs uint8 [rows, ceil(K/2)], E8M0 codes)."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    px, rows, K, ldx = _matrix(x)
+    nb = (K + 31) // 32
+    if packed is None:
+        packed = torch.empty((rows, (K + 1) // 2), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=x.device)
+    pp, _, pw, ldp = _matrix(packed)
+    ps, _, _, ld_s = _matrix(scale)
+    if rows * K and (ldp != (K + 1) // 2 or pw != (K + 1) // 2):
+        raise ValueError("packed must be a contiguous [rows, ceil(K/2)] uint8 tensor")
+    _check(L, L.mxq_quantize_mxfp4(px, ldx, rows, K, dt, pp, ps, ld_s, _stream(x)))
+    return packed, scale
+
+
+def _packed_args(packed: torch.Tensor, scale: torch.Tensor, K: int):
+    pp, rows, pw, ldp = _matrix(packed)
+    if rows * K and (pw != (K + 1) // 2 or ldp != pw):
+        raise ValueError("packed must be a contiguous [rows, ceil(K/2)] uint8 tensor")
+    ps, _, _, ld_s = _matrix(scale)
+    return pp, ps, ld_s, rows
+
+
+def mxq_dequantize_mxfp4(packed: torch.Tensor, scale: torch.Tensor, K: int, out: Optional[torch.Tensor] = None,
+                         out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so") -> torch.Tensor:
+    """Decode packed MXFP4 into bf16 / fp32 [rows, K]."""
+    L = load(lib)
+    pp, ps, ld_s, rows = _packed_args(packed, scale, K)
+    if out is None:
+        out = torch.empty((rows, K), dtype=out_dtype, device=packed.device)
+    po, _, _, ldo = _matrix(out)
+    _check(L, L.mxq_dequantize_mxfp4(pp, ps, ld_s, rows, K, po, ldo, _dtype_code(out), _stream(packed)))
+    return out
+
+
+def mxq_mxfp4_packed_to_mxfp8_row(packed: torch.Tensor, scale: torch.Tensor, K: int,
+                                  data: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None,
+                                  lib: str = "libmxq.so"):
+    """Direct MXFP8 row lift from packed MXFP4 -> (payload uint8 [rows, K], codes)."""
+    L = load(lib)
+    pp, ps, ld_s, rows = _packed_args(packed, scale, K)
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=packed.device)
+    if scale_out is None:
+        scale_out = torch.zeros((rows, (K + 31) // 32), dtype=torch.uint8, device=packed.device)
+    pd, _, _, _ = _matrix(data)
+    po, _, _, ldo = _matrix(scale_out)
+    _check(L, L.mxq_mxfp4_packed_to_mxfp8_row(pp, ps, ld_s, rows, K, pd, po, ldo, _stream(packed)))
+    return data, scale_out
+
+
+def mxq_mxfp4_packed_to_fp8_block128(packed: torch.Tensor, scale: torch.Tensor, K: int,
+                                     data: Optional[torch.Tensor] = None, tile_code: Optional[torch.Tensor] = None,
+                                     lib: str = "libmxq.so"):
+    """Direct 128x128 blockwise FP8 from packed MXFP4 -> (payload uint8 [rows, K], tile codes)."""
+    L = load(lib)
+    pp, ps, ld_s, rows = _packed_args(packed, scale, K)
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=packed.device)
+    if tile_code is None:
+        tile_code = torch.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=packed.device)
+    pd, _, _, _ = _matrix(data)
+    pt, _, _, ldt = _matrix(tile_code)
+    _check(L, L.mxq_mxfp4_packed_to_fp8_block128(pp, ps, ld_s, rows, K, pd, pt, ldt, _stream(packed)))
+    return data, tile_code
 
 
 # ---- convenience layer ------------------------------------------------------------------

@@ -170,11 +170,13 @@ struct Block {
   bool poison;
 };
 
-template <typename T>
+// kTop: the largest biased scale exponent, 252 (e = 125) for the projection and
+// the direct conversions, 253 (e = 126) for the packed deployment format.
+template <typename T, int kTop = 252>
 __device__ __forceinline__ Block block_of_amax(uint32_t amax) {
   constexpr int MB = Fmt<T>::kMbits;
   int eb = (int)((amax + ((1u << (MB - 1)) - 1u)) >> MB) - 2;
-  eb = min(max(eb, 1), 252);
+  eb = min(max(eb, 1), kTop);
   return Block{(uint32_t)eb, amax >= Fmt<T>::kInf};
 }
 
@@ -192,9 +194,9 @@ __device__ __forceinline__ uint32_t chunk_amax(u32x4 w) {
   }
 }
 
-template <typename T>
+template <typename T, int kTop = 252>
 __device__ __forceinline__ Block chunk_block(u32x4 w) {
-  return block_of_amax<T>(block_max<Fmt<T>::kLPB>(chunk_amax<T>(w)));
+  return block_of_amax<T, kTop>(block_max<Fmt<T>::kLPB>(chunk_amax<T>(w)));
 }
 
 // Projected values p * 2^e of a chunk, as bf16 pairs: 4 words (bf16 chunk) or
@@ -606,6 +608,244 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------------------------
+// Packed MXFP4 (the deployment format): E2M1 nibble pairs, element 2i in the low
+// nibble of byte i, rows of ceil(K/2) bytes, plus one E8M0 code per 1x32 block.
+// ([QAT] Description: the deployment weight is E2M1 payloads with 1x32
+// power-of-two UE8M0 scales; Known limitations: above 6 * 2^125 the packed form
+// takes scale 2^126 where the projection saturates.)  The packed side uses the
+// bf16 chunk geometry: 8 elements (4 packed bytes) per lane, 4 lanes per block.
+// ------------------------------------------------------------------------------------
+template <typename T>
+struct Nibbles;
+template <>
+struct Nibbles<uint16_t> { typedef uint32_t type; };   // 8 nibbles per bf16 chunk
+template <>
+struct Nibbles<uint32_t> { typedef uint16_t type; };   // 4 nibbles per fp32 chunk
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+                                                                  uint8_t* __restrict__ packed,
+                                                                  uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                                  uint32_t steps_per_row, uint32_t total_steps) {
+  using G = StepGeom<T>;
+  using N = typename Nibbles<T>::type;
+  keep_denormals();
+  const uint32_t tid = threadIdx.x;
+  const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
+  const int64_t pw = (K + 1) / 2;
+  u32x4 w[kRowSteps];
+#pragma unroll
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = blockIdx.x * kRowSteps + u;
+    w[u] = u32x4{0u, 0u, 0u, 0u};
+    if (step < total_steps) {
+      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = blockIdx.x * kRowSteps + u;
+    if (step < total_steps) {
+      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const int64_t col0 = seg * G::kElemsPerStep + lane_col;
+      const Block b = chunk_block<T, 253>(w[u]);
+      const uint32_t f = b.poison ? 0u : fp4_of(w[u], e8m0(b.eb), T{});
+      if (col0 < K) {
+        uint8_t* prow = packed + (int64_t)row * pw;
+        if constexpr (VEC) {
+          *reinterpret_cast<N*>(prow + col0 / 2) = (N)f;
+        } else {
+          for (int i = 0; i < G::kEPL; i += 2)
+            if (col0 + i < K)
+              prow[(col0 + i) / 2] = (uint8_t)((f >> (4 * i)) & (col0 + i + 1 < K ? 0xFFu : 0x0Fu));
+        }
+        if (tid % G::kLPB == 0) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)(b.poison ? 255u : b.eb);
+      }
+    }
+  }
+}
+
+// Eight packed nibbles at E8M0 code c -> four bf16 pairs of p * 2^(c-127), with
+// Inf where that exceeds bf16 (codes 253 and 254) and canonical NaN for c = 255.
+__device__ __forceinline__ u32x4 decode8_fp4(uint32_t f, uint32_t c) {
+  // Codes 253/254 are decoded two binades lower (exact) and moved back up with
+  // an exponent add that saturates to Inf.
+  const bool high = c >= 253u && c != 255u;
+  const float s = e8m0(high ? c - 2u : c);
+  u32x4 o{bf16_pair<0>(f, s), bf16_pair<1>(f, s), bf16_pair<2>(f, s), bf16_pair<3>(f, s)};
+  if (c == 255u) return u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  if (high) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const uint32_t h = (o[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+      uint32_t r = h;
+      if ((h & 0x7FFFu) != 0u) {
+        const uint32_t E = ((h >> 7) & 0xFFu) + 2u;
+        r = E >= 255u ? ((h & 0x8000u) | 0x7F80u) : h + (2u << 7);
+      }
+      o[i / 2] = (o[i / 2] & ~(0xFFFFu << (16 * (i % 2)))) | (r << (16 * (i % 2)));
+    }
+  }
+  return o;
+}
+
+template <typename TO, bool VEC>
+__global__ __launch_bounds__(kThreads) void dequantize_mxfp4_kernel(const uint8_t* __restrict__ packed,
+                                                                    const uint8_t* __restrict__ scale,
+                                                                    int64_t scale_ld, int64_t K,
+                                                                    TO* __restrict__ out, int64_t ld_out,
+                                                                    uint32_t steps_per_row, uint32_t total_steps) {
+  keep_denormals();
+  const uint32_t tid = threadIdx.x;
+  const int64_t lane_col = (int64_t)tid * 8, pw = (K + 1) / 2;
+  for (int u = 0; u < kDequantSteps; u++) {
+    const uint32_t step = blockIdx.x * kDequantSteps + u;
+    if (step >= total_steps) break;
+    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    if (col0 >= K) continue;
+    const uint8_t* prow = packed + (int64_t)row * pw;
+    uint32_t f = 0u;
+    if (VEC) {
+      f = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
+    } else {
+      for (int i = 0; i < 8; i += 2)
+        if (col0 + i < K) f |= (uint32_t)prow[(col0 + i) / 2] << (4 * i);
+    }
+    const u32x4 o = decode8_fp4(f, scale[(int64_t)row * scale_ld + col0 / 32]);
+    TO* orow = out + (int64_t)row * ld_out;
+    if constexpr (sizeof(TO) == 2) {
+      if (VEC) {
+        stream_store(o, reinterpret_cast<u32x4*>(orow + col0));
+      } else {
+        for (int i = 0; i < 8; i++)
+          if (col0 + i < K) orow[col0 + i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
+      }
+    } else {
+      uint32_t fo[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t h = (o[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        fo[i] = (h & 0x7FFFu) > 0x7F80u ? 0x7FC00000u : h << 16;      // bf16 -> fp32 is exact
+      }
+      if (VEC) {
+        stream_store(u32x4{fo[0], fo[1], fo[2], fo[3]}, reinterpret_cast<u32x4*>(orow + col0));
+        stream_store(u32x4{fo[4], fo[5], fo[6], fo[7]}, reinterpret_cast<u32x4*>(orow + col0 + 4));
+      } else {
+        for (int i = 0; i < 8; i++)
+          if (col0 + i < K) orow[col0 + i] = fo[i];
+      }
+    }
+  }
+}
+
+// RTNE_E4M3(p * 2^ds) of eight packed nibbles, ds <= 6.  p * 2^ds is made exact
+// in bf16 first (scale 2^max(ds, -126)); any remaining shift is applied by the
+// E4M3 conversion's own scale, so there is a single rounding.
+__device__ __forceinline__ u32x2 e4m3x8_of_fp4(uint32_t f, int ds) {
+  const int k = ds >= -126 ? 0 : -126 - ds;
+  const float sd = e8m0((uint32_t)(127 + ds + k)), se = e8m0((uint32_t)(127 + k));
+  return u32x2{e4m3x4(bf16_pair<0>(f, sd), bf16_pair<1>(f, sd), se), e4m3x4(bf16_pair<2>(f, sd), bf16_pair<3>(f, sd), se)};
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void packed_row_kernel(const uint8_t* __restrict__ packed,
+                                                              const uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                              int64_t K, uint8_t* __restrict__ data,
+                                                              uint8_t* __restrict__ scale_out, int64_t scale_out_ld,
+                                                              uint32_t steps_per_row, uint32_t total_steps) {
+  keep_denormals();
+  const uint32_t tid = threadIdx.x;
+  const int64_t lane_col = (int64_t)tid * 8, pw = (K + 1) / 2;
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = blockIdx.x * kRowSteps + u;
+    if (step >= total_steps) break;
+    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    if (col0 >= K) continue;
+    const uint8_t* prow = packed + (int64_t)row * pw;
+    uint32_t f = 0u;
+    if (VEC) {
+      f = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
+    } else {
+      for (int i = 0; i < 8; i += 2)
+        if (col0 + i < K) f |= (uint32_t)prow[(col0 + i) / 2] << (4 * i);
+    }
+    const uint32_t c = scale[(int64_t)row * scale_ld + col0 / 32];
+    // S = max(e - 6, -127): code max(c - 6, 0); shift e - S = min(c, 6)
+    const uint32_t code = c == 255u ? 255u : (c > 6u ? c - 6u : 0u);
+    u32x2 q = c == 255u ? u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu} : e4m3x8_of_fp4(f, (int)min(c, 6u));
+    uint8_t* drow = data + (int64_t)row * K;
+    if (VEC) {
+      stream_store(q, reinterpret_cast<u32x2*>(drow + col0));
+    } else {
+      for (int i = 0; i < 8; i++)
+        if (col0 + i < K) drow[col0 + i] = (uint8_t)(q[i / 4] >> (8 * (i % 4)));
+    }
+    if (tid % 4 == 0) scale_out[(int64_t)row * scale_out_ld + col0 / 32] = (uint8_t)code;
+  }
+}
+
+// 128x128 fold from packed MXFP4: same workgroup layout as the bf16 fold (1024
+// threads, 16 lanes across a tile row), block exponents read from the codes.
+template <bool VEC>
+__global__ __launch_bounds__(kFoldThreads) void packed_block128_kernel(const uint8_t* __restrict__ packed,
+                                                                       const uint8_t* __restrict__ scale,
+                                                                       int64_t scale_ld, int64_t rows, int64_t K,
+                                                                       uint8_t* __restrict__ data,
+                                                                       uint8_t* __restrict__ tile_code,
+                                                                       int64_t tile_ld, uint32_t tiles_per_row) {
+  constexpr int LPR = 16, RPP = kFoldThreads / LPR, P = 128 / RPP;
+  __shared__ uint32_t s_max[kFoldWaves];
+  keep_denormals();
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t tr = blockIdx.x / tiles_per_row, tc = blockIdx.x - tr * tiles_per_row;
+  const int64_t r0 = (int64_t)tr * 128 + tid / LPR, col0 = (int64_t)tc * 128 + (tid % LPR) * 8, pw = (K + 1) / 2;
+  uint32_t f[P], c[P];
+  uint32_t m = 1u;                                          // biased M; 1 (e = -126) if no finite block
+#pragma unroll
+  for (int i = 0; i < P; i++) {
+    const int64_t r = r0 + i * RPP;
+    f[i] = 0u;
+    c[i] = 1u;
+    if (r < rows && col0 < K) {
+      const uint8_t* prow = packed + r * pw;
+      if (VEC) {
+        f[i] = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
+      } else {
+        for (int k = 0; k < 8; k += 2)
+          if (col0 + k < K) f[i] |= (uint32_t)prow[(col0 + k) / 2] << (4 * k);
+      }
+      c[i] = scale[r * scale_ld + col0 / 32];
+    }
+    if (c[i] != 255u) m = max(m, c[i]);
+  }
+  m = max16(m);
+#pragma unroll
+  for (int off = LPR; off < 64; off *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if (lane == 0) s_max[wave] = m;
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kFoldWaves; v++) m = max(m, s_max[v]);
+  const uint32_t code = m > 6u ? m - 6u : 0u;
+  if (tid == 0) tile_code[(int64_t)tr * tile_ld + tc] = (uint8_t)code;
+#pragma unroll
+  for (int i = 0; i < P; i++) {
+    const int64_t r = r0 + i * RPP;
+    if (r >= rows || col0 >= K) continue;
+    const u32x2 q = c[i] == 255u ? u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu} : e4m3x8_of_fp4(f[i], (int)c[i] - (int)code);
+    uint8_t* drow = data + r * K;
+    if (VEC) {
+      stream_store(q, reinterpret_cast<u32x2*>(drow + col0));
+    } else {
+      for (int k = 0; k < 8; k++)
+        if (col0 + k < K) drow[col0 + k] = (uint8_t)(q[k / 4] >> (8 * (k % 4)));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Export: strided copy of the first ncols columns of each row, in units of V
 // (16, 4 or 1 bytes, whichever the pointers, strides and width allow).
 // ------------------------------------------------------------------------------------
@@ -734,6 +974,40 @@ int launch_dequant(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
   if (e5) return launch_dequant_t<TO, true, false>(data, scale, scale_ld, rows, K, out, ld_out, s);
   if (tile) return launch_dequant_t<TO, false, true>(data, scale, scale_ld, rows, K, out, ld_out, s);
   return launch_dequant_t<TO, false, false>(data, scale, scale_ld, rows, K, out, ld_out, s);
+}
+
+template <typename T>
+int launch_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scale,
+                          int64_t scale_ld, hipStream_t s) {
+  uint32_t spr, total;
+  if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+  constexpr int EPL = Fmt<T>::kEPL;
+  const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(packed, EPL / 2);
+  const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
+  if (vec)
+    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
+                       scale_ld, spr, total);
+  else
+    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, false>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
+                       scale_ld, spr, total);
+  return launch_status();
+}
+
+template <typename TO>
+int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                            void* out, int64_t ld_out, hipStream_t s) {
+  uint32_t spr, total;
+  if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
+  constexpr int OPC = 16 / (int)sizeof(TO);
+  const bool vec = aligned(packed, 4) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
+  const dim3 grid(grid_for(total, kDequantSteps)), block(kThreads);
+  if (vec)
+    hipLaunchKernelGGL((dequantize_mxfp4_kernel<TO, true>), grid, block, 0, s, packed, scale, scale_ld, K, (TO*)out,
+                       ld_out, spr, total);
+  else
+    hipLaunchKernelGGL((dequantize_mxfp4_kernel<TO, false>), grid, block, 0, s, packed, scale, scale_ld, K, (TO*)out,
+                       ld_out, spr, total);
+  return launch_status();
 }
 
 }  // namespace
@@ -878,6 +1152,83 @@ int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
     return MXQ_ERR_ALIAS;
   return out_dt == MXQ_BF16 ? launch_dequant<uint16_t>(data, scale, scale_ld, rows, K, fmt, layout, out, ld_out, stream)
                             : launch_dequant<uint32_t>(data, scale, scale_ld, rows, K, fmt, layout, out, ld_out, stream);
+}
+
+int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* packed,
+                       uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
+  if (check_dtype(dt)) return MXQ_ERR_DTYPE;
+  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXQ_OK;
+  if (!x || !packed || !scale) return MXQ_ERR_NULL;
+  const int64_t nb = (K + 31) / 32, pw = (K + 1) / 2;
+  if (ld_x < K || scale_ld < nb) return MXQ_ERR_SHAPE;
+  const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), rp = matrix_range(packed, rows, pw, pw, 1),
+              rs = matrix_range(scale, rows, nb, scale_ld, 1);
+  if (overlap(rx, rp) || overlap(rx, rs) || overlap(rp, rs)) return MXQ_ERR_ALIAS;
+  return dt == MXQ_BF16 ? launch_quantize_mxfp4<uint16_t>(x, ld_x, rows, K, packed, scale, scale_ld, stream)
+                        : launch_quantize_mxfp4<uint32_t>(x, ld_x, rows, K, packed, scale, scale_ld, stream);
+}
+
+int mxq_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                         void* out, int64_t ld_out, mxq_dtype out_dt, hipStream_t stream) {
+  if (check_dtype(out_dt)) return MXQ_ERR_DTYPE;
+  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXQ_OK;
+  if (!packed || !scale || !out) return MXQ_ERR_NULL;
+  const int64_t nb = (K + 31) / 32, pw = (K + 1) / 2;
+  if (ld_out < K || scale_ld < nb) return MXQ_ERR_SHAPE;
+  const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt));
+  if (overlap(ro, matrix_range(packed, rows, pw, pw, 1)) || overlap(ro, matrix_range(scale, rows, nb, scale_ld, 1)))
+    return MXQ_ERR_ALIAS;
+  return out_dt == MXQ_BF16 ? launch_dequantize_mxfp4<uint16_t>(packed, scale, scale_ld, rows, K, out, ld_out, stream)
+                            : launch_dequantize_mxfp4<uint32_t>(packed, scale, scale_ld, rows, K, out, ld_out, stream);
+}
+
+int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows,
+                                  int64_t K, uint8_t* data, uint8_t* scale_out, int64_t scale_out_ld,
+                                  hipStream_t stream) {
+  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXQ_OK;
+  if (!packed || !scale || !data || !scale_out) return MXQ_ERR_NULL;
+  const int64_t nb = (K + 31) / 32, pw = (K + 1) / 2;
+  if (scale_ld < nb || scale_out_ld < nb) return MXQ_ERR_SHAPE;
+  const Range rp = matrix_range(packed, rows, pw, pw, 1), rs = matrix_range(scale, rows, nb, scale_ld, 1),
+              rd = matrix_range(data, rows, K, K, 1), ro = matrix_range(scale_out, rows, nb, scale_out_ld, 1);
+  if (overlap(rd, rp) || overlap(rd, rs) || overlap(ro, rp) || overlap(ro, rs) || overlap(rd, ro)) return MXQ_ERR_ALIAS;
+  uint32_t spr, total;
+  if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
+  const bool vec = aligned(packed, 4) && aligned(data, 8) && K % 8 == 0;
+  const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
+  if (vec)
+    hipLaunchKernelGGL(packed_row_kernel<true>, grid, block, 0, stream, packed, scale, scale_ld, K, data, scale_out,
+                       scale_out_ld, spr, total);
+  else
+    hipLaunchKernelGGL(packed_row_kernel<false>, grid, block, 0, stream, packed, scale, scale_ld, K, data, scale_out,
+                       scale_out_ld, spr, total);
+  return launch_status();
+}
+
+int mxq_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows,
+                                     int64_t K, uint8_t* data, uint8_t* tile_code, int64_t tile_ld,
+                                     hipStream_t stream) {
+  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXQ_OK;
+  if (!packed || !scale || !data || !tile_code) return MXQ_ERR_NULL;
+  const int64_t nb = (K + 31) / 32, pw = (K + 1) / 2, ntc = (K + 127) / 128, ntr = (rows + 127) / 128;
+  if (scale_ld < nb || tile_ld < ntc) return MXQ_ERR_SHAPE;
+  const Range rp = matrix_range(packed, rows, pw, pw, 1), rs = matrix_range(scale, rows, nb, scale_ld, 1),
+              rd = matrix_range(data, rows, K, K, 1), rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
+  if (overlap(rd, rp) || overlap(rd, rs) || overlap(rt, rp) || overlap(rt, rs) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
+  if (ntc * ntr >= kMaxSteps) return MXQ_ERR_SHAPE;
+  const bool vec = aligned(packed, 4) && aligned(data, 8) && K % 8 == 0;
+  const dim3 grid((uint32_t)(ntc * ntr)), block(kFoldThreads);
+  if (vec)
+    hipLaunchKernelGGL(packed_block128_kernel<true>, grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
+                       tile_code, tile_ld, (uint32_t)ntc);
+  else
+    hipLaunchKernelGGL(packed_block128_kernel<false>, grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
+                       tile_code, tile_ld, (uint32_t)ntc);
+  return launch_status();
 }
 
 }  // extern "C"

@@ -52,6 +52,13 @@ def lib() -> ctypes.CDLL:
             L.orc_mxfp4_to_fp8_block128.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, i64, i64]
             L.orc_export_mxfp8.argtypes = [vp, i64, i64, i64, vp]
             L.orc_dequantize.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, i64, i32, i64, i64]
+            L.orc_quantize_mxfp4.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, i64, i64]
+            L.orc_dequantize_mxfp4.argtypes = [vp, vp, i64, i64, i64, vp, i64, i32, i64, i64]
+            L.orc_mxfp4_packed_to_mxfp8_row.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, i64, i64]
+            L.orc_mxfp4_packed_to_fp8_block128.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64, i64, i64]
+            for name in ("orc_quantize_mxfp4", "orc_dequantize_mxfp4", "orc_mxfp4_packed_to_mxfp8_row",
+                         "orc_mxfp4_packed_to_fp8_block128"):
+                getattr(L, name).restype = ctypes.c_int
             L.orc_scale_exponent_bits.argtypes = [ctypes.c_uint32, i32]
             L.orc_e2m1_code_bits.argtypes = [ctypes.c_uint32, i32, i32]
             L.orc_e2m1_codes.argtypes = [vp, i64, i32, i32, vp]
@@ -188,6 +195,63 @@ def dequantize(data: np.ndarray, scale: np.ndarray, layout: int = ROW_1X32, fp8:
     _run(lambda r0, r1: L.orc_dequantize(_ptr(data), _ptr(scale), scale.shape[1], rows, K, fp8, layout, _ptr(out), K,
                                          out_dtype, r0, r1), rows, threads)
     return out
+
+
+# ---- packed MXFP4 (deployment format) --------------------------------------------------
+
+def quantize_mxfp4(x: np.ndarray, scale_ld: int | None = None, threads: int = 1, fill: int = 0):
+    """Packed MXFP4: (nibble pairs uint8 [rows, ceil(K/2)], E8M0 codes uint8 [rows, scale_ld])."""
+    x = _as2d(x)
+    rows, K = x.shape
+    ld = _ld(x)
+    nb = (K + 31) // 32
+    scale_ld = nb if scale_ld is None else scale_ld
+    packed = np.empty((rows, (K + 1) // 2), dtype=np.uint8)
+    scale = np.full((rows, scale_ld), fill, dtype=np.uint8)
+    L = lib()
+    _run(lambda r0, r1: L.orc_quantize_mxfp4(_ptr(x), ld, rows, K, _dtype_of(x), _ptr(packed), _ptr(scale), scale_ld,
+                                             r0, r1), rows, threads)
+    return packed, scale
+
+
+def dequantize_mxfp4(packed: np.ndarray, scale: np.ndarray, K: int, out_dtype: int = BF16, threads: int = 1):
+    packed = _as2d(np.ascontiguousarray(packed, dtype=np.uint8))
+    scale = _as2d(np.ascontiguousarray(scale, dtype=np.uint8))
+    rows = packed.shape[0]
+    out = np.empty((rows, K), dtype=np.uint16 if out_dtype == BF16 else np.uint32)
+    L = lib()
+    _run(lambda r0, r1: L.orc_dequantize_mxfp4(_ptr(packed), _ptr(scale), scale.shape[1], rows, K, _ptr(out), K,
+                                               out_dtype, r0, r1), rows, threads)
+    return out
+
+
+def mxfp4_packed_to_mxfp8_row(packed: np.ndarray, scale: np.ndarray, K: int, scale_out_ld: int | None = None,
+                              threads: int = 1, fill: int = 0):
+    packed = _as2d(np.ascontiguousarray(packed, dtype=np.uint8))
+    scale = _as2d(np.ascontiguousarray(scale, dtype=np.uint8))
+    rows = packed.shape[0]
+    nb = (K + 31) // 32
+    scale_out_ld = nb if scale_out_ld is None else scale_out_ld
+    data = np.empty((rows, K), dtype=np.uint8)
+    scale_out = np.full((rows, scale_out_ld), fill, dtype=np.uint8)
+    L = lib()
+    _run(lambda r0, r1: L.orc_mxfp4_packed_to_mxfp8_row(_ptr(packed), _ptr(scale), scale.shape[1], rows, K,
+                                                        _ptr(data), _ptr(scale_out), scale_out_ld, r0, r1),
+         rows, threads)
+    return data, scale_out
+
+
+def mxfp4_packed_to_fp8_block128(packed: np.ndarray, scale: np.ndarray, K: int, threads: int = 1):
+    packed = _as2d(np.ascontiguousarray(packed, dtype=np.uint8))
+    scale = _as2d(np.ascontiguousarray(scale, dtype=np.uint8))
+    rows = packed.shape[0]
+    data = np.empty((rows, K), dtype=np.uint8)
+    codes = np.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=np.uint8)
+    L = lib()
+    _run(lambda r0, r1: L.orc_mxfp4_packed_to_fp8_block128(_ptr(packed), _ptr(scale), scale.shape[1], rows, K,
+                                                           _ptr(data), _ptr(codes), codes.shape[1], r0, r1),
+         rows, threads, align=128)
+    return data, codes
 
 
 # ---- element-level helpers for the pins ------------------------------------------------

@@ -140,7 +140,10 @@ static const int E2M1_X2[8] = {0, 1, 2, 3, 4, 6, 8, 12};
 /* Scale exponent of one 1x32 block: e = clamp(ceil(log2(amax/6)), -126, 125),
  * i.e. the smallest integer e with 6 * 2^e >= amax, then clamped.
  * Reading: amax = 0 has log2 = -inf and clamps to -126. */
-int orc_scale_exponent(dyadic amax) {
+static int scale_exponent_clamped(dyadic amax, int lo, int hi);
+int orc_scale_exponent(dyadic amax) { return scale_exponent_clamped(amax, -126, 125); }
+
+static int scale_exponent_clamped(dyadic amax, int lo, int hi) {
   int e;
   if (amax.M == 0) {
     e = -126;
@@ -154,8 +157,8 @@ int orc_scale_exponent(dyadic amax) {
       e++;
     }
   }
-  if (e < -126) e = -126;
-  if (e > 125) e = 125;
+  if (e < lo) e = lo;
+  if (e > hi) e = hi;
   return e;
 }
 
@@ -398,6 +401,156 @@ int orc_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
         o = round_to_format(q.neg, q.M, q.k + (int)c - 127, f, &inexact, &ovf);
       }
       store_bits(out, dtype, (size_t)(r * ld_out + col), o);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed MXFP4 (the deployment format)                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * Quantize for deployment: E2M1 payloads and 1x32 power-of-two E8M0 scales
+ * ([QAT] Description: "training sees exactly the deployment weight (E2M1
+ * payloads, 1x32 power-of-two UE8M0 scales)"; [ISS] Description, workflow 2).
+ * The MXFP4 decomposition is the projection's, except that above the cap the
+ * scale moves to 2^126 ([QAT] Known limitations: "packed deployment moves to
+ * scale 2^126"): e = clamp(ceil(log2(amax/6)), -126, 126).  Code = e + 127.
+ * Packing: element 2i in the low nibble of byte i, 2i+1 in the high nibble
+ * (0 when K is odd); rows are ceil(K/2) bytes, contiguous.
+ * Readings: the lower clamp stays at -126 (so the decoded deployment weight is
+ * exactly the projection below the cap); a poisoned block gets code 255 (NaN)
+ * and zero nibbles.
+ */
+int orc_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, int dtype,
+                       uint8_t* packed, uint8_t* scale, int64_t scale_ld, int64_t r0, int64_t r1) {
+  int64_t nb = (K + 31) / 32, pw = (K + 1) / 2;
+  if (check_common(rows, K, ld_x, dtype, r0, r1) || scale_ld < nb) return ORC_BAD_ARG;
+  fmt_t f = dtype_fmt(dtype);
+  for (int64_t r = r0; r < r1; r++) {
+    for (int64_t i = 0; i < pw; i++) packed[r * pw + i] = 0;
+    for (int64_t j = 0; j < nb; j++) {
+      int64_t c0 = j * 32;
+      int n = (int)(K - c0 < 32 ? K - c0 : 32);
+      dyadic v[32];
+      int poisoned = 0;
+      dyadic amax = {0, CLS_FINITE, 0, 0};
+      for (int i = 0; i < n; i++) {
+        v[i] = unpack(load_bits(x, dtype, (size_t)(r * ld_x + c0 + i)), f);
+        if (v[i].cls != CLS_FINITE) poisoned = 1;
+        else if (cmp_mag(v[i], amax) > 0) amax = v[i];
+      }
+      if (poisoned) { scale[r * scale_ld + j] = 255; continue; }
+      int e = scale_exponent_clamped(amax, -126, 126);
+      scale[r * scale_ld + j] = (uint8_t)(e + 127);
+      for (int i = 0; i < n; i++) {
+        uint8_t nib = (uint8_t)((v[i].neg << 3) | orc_e2m1_code(v[i], e));
+        int64_t col = c0 + i;
+        packed[r * pw + col / 2] |= (uint8_t)(nib << (4 * (col % 2)));
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* E2M1 nibble of element col of a packed row, as (neg, 2p). */
+static void packed_element(const uint8_t* packed, int64_t pw, int64_t r, int64_t col, int* neg, int* twice_p) {
+  uint8_t nib = (uint8_t)((packed[r * pw + col / 2] >> (4 * (col % 2))) & 0xF);
+  *neg = nib >> 3;
+  *twice_p = E2M1_X2[nib & 7];
+}
+
+/* Decode packed MXFP4: value = E2M1 * 2^(code - 127), nearest-even into the
+ * output dtype (Inf beyond its range); code 255 gives canonical NaN. */
+int orc_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                         void* out, int64_t ld_out, int dtype, int64_t r0, int64_t r1) {
+  int64_t pw = (K + 1) / 2, nb = (K + 31) / 32;
+  if (rows < 0 || K < 0 || ld_out < K || scale_ld < nb || (dtype != 0 && dtype != 1) || r0 < 0 || r1 > rows || r0 > r1)
+    return ORC_BAD_ARG;
+  fmt_t f = dtype_fmt(dtype);
+  for (int64_t r = r0; r < r1; r++) {
+    for (int64_t col = 0; col < K; col++) {
+      uint8_t c = scale[r * scale_ld + col / 32];
+      uint32_t o;
+      if (c == 255) {
+        o = canonical_nan(dtype);
+      } else {
+        int neg, tp, inexact, ovf;
+        packed_element(packed, pw, r, col, &neg, &tp);
+        o = round_to_format(neg, (uint64_t)tp, (int)c - 127 - 1, f, &inexact, &ovf);
+      }
+      store_bits(out, dtype, (size_t)(r * ld_out + col), o);
+    }
+  }
+  return ORC_OK;
+}
+
+/* Direct MXFP8 row lift from packed MXFP4: the same fixed-shift-6 lift as
+ * orc_mxfp4_to_mxfp8_row, with (p, e) read from the packed payload and code
+ * (e = code - 127).  Code 255 (NaN) gives code 255 and payload 0x7F. */
+int orc_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows,
+                                  int64_t K, uint8_t* data, uint8_t* scale_out, int64_t scale_out_ld,
+                                  int64_t r0, int64_t r1) {
+  int64_t pw = (K + 1) / 2, nb = (K + 31) / 32;
+  if (rows < 0 || K < 0 || scale_ld < nb || scale_out_ld < nb || r0 < 0 || r1 > rows || r0 > r1) return ORC_BAD_ARG;
+  for (int64_t r = r0; r < r1; r++) {
+    for (int64_t j = 0; j < nb; j++) {
+      int64_t c0 = j * 32, c1 = c0 + 32 < K ? c0 + 32 : K;
+      uint8_t c = scale[r * scale_ld + j];
+      if (c == 255) {
+        scale_out[r * scale_out_ld + j] = 255;
+        for (int64_t col = c0; col < c1; col++) data[r * K + col] = 0x7F;
+        continue;
+      }
+      int e = (int)c - 127, S = e - 6;
+      if (S < -127) S = -127;
+      scale_out[r * scale_out_ld + j] = (uint8_t)(S + 127);
+      for (int64_t col = c0; col < c1; col++) {
+        int neg, tp, inexact, ovf;
+        packed_element(packed, pw, r, col, &neg, &tp);
+        uint32_t q = round_to_format(neg, (uint64_t)tp, e - 1 - S, FMT_E4M3, &inexact, &ovf);
+        if (inexact || ovf) die("packed row lift is not exact");
+        data[r * K + col] = (uint8_t)q;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* Direct 128x128 blockwise FP8 from packed MXFP4: the same tile fold as
+ * orc_mxfp4_to_fp8_block128 with (p, e) read from the packed form; blocks with
+ * code 255 are the poisoned ones.  Bands starting in [r0, r1), r0 % 128 == 0. */
+int orc_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows,
+                                     int64_t K, uint8_t* data, uint8_t* tile_code, int64_t tile_ld,
+                                     int64_t r0, int64_t r1) {
+  int64_t pw = (K + 1) / 2, nb = (K + 31) / 32, ntc = (K + 127) / 128;
+  if (rows < 0 || K < 0 || scale_ld < nb || tile_ld < ntc || r0 < 0 || r1 > rows || r0 > r1 || r0 % 128) return ORC_BAD_ARG;
+  for (int64_t tr0 = r0; tr0 < r1; tr0 += 128) {
+    int64_t tr1 = tr0 + 128 < rows ? tr0 + 128 : rows;
+    for (int64_t tc = 0; tc < ntc; tc++) {
+      int64_t jb0 = tc * 4, jb1 = jb0 + 4 < nb ? jb0 + 4 : nb;
+      int M = -126;
+      for (int64_t r = tr0; r < tr1; r++)
+        for (int64_t j = jb0; j < jb1; j++) {
+          uint8_t c = scale[r * scale_ld + j];
+          if (c != 255 && (int)c - 127 > M) M = (int)c - 127;
+        }
+      int S = M - 6;
+      if (S < -127) S = -127;
+      tile_code[(tr0 / 128) * tile_ld + tc] = (uint8_t)(S + 127);
+      for (int64_t r = tr0; r < tr1; r++)
+        for (int64_t j = jb0; j < jb1; j++) {
+          uint8_t c = scale[r * scale_ld + j];
+          int64_t c0 = j * 32, c1 = c0 + 32 < K ? c0 + 32 : K;
+          for (int64_t col = c0; col < c1; col++) {
+            if (c == 255) { data[r * K + col] = 0x7F; continue; }
+            int neg, tp, inexact, ovf;
+            packed_element(packed, pw, r, col, &neg, &tp);
+            uint32_t q = round_to_format(neg, (uint64_t)tp, (int)c - 127 - 1 - S, FMT_E4M3, &inexact, &ovf);
+            if (ovf) die("packed tile fold overflowed E4M3");
+            data[r * K + col] = (uint8_t)q;
+          }
+        }
     }
   }
   return ORC_OK;

@@ -281,3 +281,93 @@ def dequantize(data: np.ndarray, scale: np.ndarray, layout: str, out: str, fp8: 
                 else:
                     res[r, col] = fp32_encode_exact(v, neg)
     return res
+
+
+# ---- packed MXFP4 (deployment format) ---------------------------------------------------
+
+def quantize_mxfp4(x: np.ndarray, dtype: str):
+    """Packed E2M1 nibbles (element 2i low, 2i+1 high) and E8M0 codes with the
+    scale exponent clamped to [-126, 126]."""
+    rows, K = x.shape
+    nb = (K + 31) // 32
+    packed = np.zeros((rows, (K + 1) // 2), dtype=np.uint8)
+    scale = np.zeros((rows, nb), dtype=np.uint8)
+    for r in range(rows):
+        for j, (c0, c1) in enumerate(_blocks(K)):
+            vals, negs = _values_and_sign(x[r, c0:c1], dtype)
+            if any(not isinstance(v, Fraction) for v in vals):
+                scale[r, j] = 255
+                continue
+            amax = max(abs(v) for v in vals)
+            e = -126 if amax == 0 else max(-126, min(126, _SIX_POW[bisect.bisect_left(_SIX_VALS, amax)][0]))
+            scale[r, j] = e + 127
+            for i, (v, neg) in enumerate(zip(vals, negs)):
+                nib = (8 if neg else 0) | e2m1_code(abs(v) / Fraction(2) ** e)
+                col = c0 + i
+                packed[r, col // 2] |= nib << (4 * (col % 2))
+    return packed, scale
+
+
+def _nibble(packed, r, col):
+    nib = (int(packed[r, col // 2]) >> (4 * (col % 2))) & 0xF
+    return bool(nib & 8), GRID[nib & 7]
+
+
+def dequantize_mxfp4(packed: np.ndarray, scale: np.ndarray, K: int, out: str):
+    rows = packed.shape[0]
+    res = np.zeros((rows, K), dtype=np.uint16 if out == "bf16" else np.uint32)
+    for r in range(rows):
+        for col in range(K):
+            c = int(scale[r, col // 32])
+            if c == 255:
+                res[r, col] = 0x7FC0 if out == "bf16" else 0x7FC00000
+                continue
+            neg, p = _nibble(packed, r, col)
+            v = p * Fraction(2) ** (c - 127)
+            res[r, col] = (table("bf16").nearest_even(v, neg, overflow_bits=0x7F80) if out == "bf16"
+                           else fp32_encode_exact(v, neg))
+    return res
+
+
+def packed_to_row(packed: np.ndarray, scale: np.ndarray, K: int):
+    rows = packed.shape[0]
+    nb = (K + 31) // 32
+    data = np.zeros((rows, K), dtype=np.uint8)
+    out = np.zeros((rows, nb), dtype=np.uint8)
+    for r in range(rows):
+        for j, (c0, c1) in enumerate(_blocks(K)):
+            c = int(scale[r, j])
+            if c == 255:
+                out[r, j] = 255
+                data[r, c0:c1] = 0x7F
+                continue
+            e = c - 127
+            S = max(e - 6, -127)
+            out[r, j] = S + 127
+            for col in range(c0, c1):
+                neg, p = _nibble(packed, r, col)
+                data[r, col] = table("e4m3").nearest_even(p * Fraction(2) ** (e - S), neg)
+    return data, out
+
+
+def packed_to_block128(packed: np.ndarray, scale: np.ndarray, K: int):
+    rows = packed.shape[0]
+    data = np.zeros((rows, K), dtype=np.uint8)
+    codes = np.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=np.uint8)
+    for tr in range(0, rows, 128):
+        for tc in range(0, K, 128):
+            blocks = [(r, j) for r in range(tr, min(tr + 128, rows)) for j in range(tc // 32, min(tc + 128, K + 31) // 32)
+                      if j * 32 < K]
+            finite = [int(scale[r, j]) - 127 for r, j in blocks if scale[r, j] != 255]
+            M = max(finite) if finite else -126
+            S = max(M - 6, -127)
+            codes[tr // 128, tc // 128] = S + 127
+            for r, j in blocks:
+                c = int(scale[r, j])
+                for col in range(j * 32, min(j * 32 + 32, K)):
+                    if c == 255:
+                        data[r, col] = 0x7F
+                    else:
+                        neg, p = _nibble(packed, r, col)
+                        data[r, col] = table("e4m3").nearest_even(p * Fraction(2) ** (c - 127 - S), neg)
+    return data, codes

@@ -245,6 +245,87 @@ def test_noop_flag_inside_a_replayed_graph(dev):
         assert_bits(to_host(tc), wtc, f"replay {step} tile codes")
 
 
+# ------------------------------------------------------------------ packed MXFP4 (deployment format)
+
+def check_packed(bits: np.ndarray, dev, scale_ld=None):
+    rows, K = bits.shape
+    nb = (K + 31) // 32
+    scale_ld = scale_ld or nb
+    x = to_dev(bits, dev)
+    tdt, odt = out_dtype_of(bits)
+    scale = torch.full((rows, scale_ld), 0xC3, dtype=torch.uint8, device=dev)
+    packed, scale = mxq.mxq_quantize_mxfp4(x, scale=scale)
+    wp, ws = oracle.quantize_mxfp4(bits, scale_ld=scale_ld, threads=THREADS, fill=0xC3)
+    assert_bits(to_host(packed), wp, "packed nibbles")
+    assert_bits(to_host(scale), ws, "packed codes (padding untouched)")
+    assert_bits(to_host(mxq.mxq_dequantize_mxfp4(packed, scale, K, out_dtype=tdt)),
+                oracle.dequantize_mxfp4(wp, ws, K, out_dtype=odt, threads=THREADS), "packed decode")
+    d, c = mxq.mxq_mxfp4_packed_to_mxfp8_row(packed, scale, K)
+    wd, wc = oracle.mxfp4_packed_to_mxfp8_row(wp, ws, K, threads=THREADS)
+    assert_bits(to_host(d), wd, "row lift from packed")
+    assert_bits(to_host(c), wc, "row codes from packed")
+    d, c = mxq.mxq_mxfp4_packed_to_fp8_block128(packed, scale, K)
+    wd, wc = oracle.mxfp4_packed_to_fp8_block128(wp, ws, K, threads=THREADS)
+    assert_bits(to_host(d), wd, "128x128 payload from packed")
+    assert_bits(to_host(c), wc, "tile codes from packed")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c2_natural", "planted", "fuzz", "c3", "c4", "pairs_bf16", "pairs_fp32"])
+def test_packed_mxfp4(dev, name):
+    bits = {"c1": W.c1_small, "c2": W.c2_exhaustive, "c2_natural": lambda: W.c2_exhaustive(natural=True),
+            "planted": W.c2_planted, "fuzz": lambda: W.fp32_fuzz(1 << 18).reshape(-1, 256), "c3": W.c3_spread,
+            "c4": W.c4_headline, "pairs_bf16": lambda: W.value_exponent_pairs("bf16"),
+            "pairs_fp32": lambda: W.value_exponent_pairs("fp32")}[name]()
+    check_packed(bits, dev, scale_ld=4 if name in ("c1", "c2", "c2_natural") else None)
+
+
+def test_packed_above_the_cap(dev):
+    """Every bf16 magnitude above 6*2^125 as a block amax (scale 2^126), with
+    every smaller pattern as the other elements."""
+    big = np.arange(0x7F41, 0x7F80, dtype=np.uint16)
+    rest = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    g = np.random.default_rng(3)
+    rows = []
+    for i in range(0, len(rest), 31):
+        chunk = rest[i:i + 31]
+        blk = np.zeros(32, dtype=np.uint16)
+        blk[0] = big[(i // 31) % len(big)] | (0x8000 if (i // 31) % 2 else 0)
+        blk[1:1 + len(chunk)] = chunk ^ (g.integers(0, 2, len(chunk)).astype(np.uint16) << 15)
+        rows.append(blk)
+    bits = np.stack(rows).reshape(-1, 256 if len(rows) % 8 == 0 else 32)
+    check_packed(np.ascontiguousarray(bits), dev)
+
+
+def test_packed_every_code_and_nibble(dev):
+    rows, K = 256, 128
+    packed = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=np.uint8), (rows, 8))
+    scale = np.arange(256, dtype=np.uint8).reshape(rows, 1).repeat(4, axis=1)
+    scale[::7, 1] = 3
+    pd, sd = to_dev(packed, dev), to_dev(scale, dev)
+    for tdt, odt in ((torch.bfloat16, oracle.BF16), (torch.float32, oracle.FP32)):
+        assert_bits(to_host(mxq.mxq_dequantize_mxfp4(pd, sd, K, out_dtype=tdt)),
+                    oracle.dequantize_mxfp4(packed, scale, K, out_dtype=odt), f"decode every code {odt}")
+    d, c = mxq.mxq_mxfp4_packed_to_mxfp8_row(pd, sd, K)
+    wd, wc = oracle.mxfp4_packed_to_mxfp8_row(packed, scale, K)
+    assert_bits(to_host(d), wd, "row lift every code")
+    assert_bits(to_host(c), wc, "row codes every code")
+    d, c = mxq.mxq_mxfp4_packed_to_fp8_block128(pd, sd, K)
+    wd, wc = oracle.mxfp4_packed_to_fp8_block128(packed, scale, K)
+    assert_bits(to_host(d), wd, "fold every code")
+    assert_bits(to_host(c), wc, "tile codes every code")
+
+
+@pytest.mark.parametrize("K", [1, 7, 9, 31, 33, 100, 130, 257])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_packed_ragged(dev, K, dtype):
+    rows = 131
+    if dtype == "bf16":
+        flat = np.tile(W.c2_exhaustive().reshape(-1), (rows * K) // 65536 + 1)
+    else:
+        flat = W.fp32_fuzz(((rows * K + 31) // 32) * 32).reshape(-1)
+    check_packed(np.ascontiguousarray(flat[: rows * K].reshape(rows, K)), dev, scale_ld=(K + 31) // 32 + 1)
+
+
 # ------------------------------------------------------------------ invariants on the device
 
 def test_decode_of_row_is_projection_c4(dev):

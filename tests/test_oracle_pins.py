@@ -451,3 +451,103 @@ def test_pins_catch_planted_mistakes(mutation, where):
         d1, c1 = F.block128(x, "fp32", mutation=mutation)
         d0, c0 = oracle.mxfp4_to_fp8_block128(x)
         assert not (np.array_equal(d0, d1) and np.array_equal(c0, c1))
+
+
+# ---------------------------------------------------------------- packed MXFP4 (deployment)
+
+def _below_cap_blocks(x):
+    """[rows, nblocks] mask of finite blocks whose amax is at most 6*2^125."""
+    rows, K = x.shape
+    nb = (K + 31) // 32
+    mask = np.ones((rows, nb), dtype=bool)
+    mag = (x & 0x7FFF).astype(np.int64) if x.dtype == np.uint16 else (x & 0x7FFFFFFF).astype(np.int64)
+    cap = 0x7F40 if x.dtype == np.uint16 else 0x7F400000
+    for j in range(nb):
+        mask[:, j] = (mag[:, 32 * j:32 * j + 32] <= cap).all(axis=1)
+    return mask
+
+
+def test_packed_nibble_order_closed_form(facts):
+    """0.5, 1, 1.5, -6 at e = 0: E2M1 codes 1, 2, 3, 7|sign; element 2i sits in
+    the low nibble of byte i."""
+    assert "UE8M0" in facts["deployment_format"]["value"]
+    x = W.bf16_bits_of(np.array([0.5, 1.0, 1.5, -6.0] + [0.0] * 28))[None, :]
+    packed, scale = oracle.quantize_mxfp4(x)
+    assert packed[0, :2].tolist() == [0x21, 0xF3] and scale[0, 0] == 127 + 0
+    x3 = W.bf16_bits_of(np.array([1.0, 2.0, 6.0]))[None, :]
+    p3, _ = oracle.quantize_mxfp4(x3)
+    assert p3.tolist() == [[0x42, 0x07]]                  # odd K: the last high nibble is 0
+
+
+def test_packed_scale_moves_to_2_126_above_the_cap(facts):
+    assert facts["packed_scale_above_cap"]["value"] == "2^126"
+    x = np.array([list(range(0x7F41, 0x7F61))], dtype=np.uint16)          # amax above 6*2^125
+    packed, scale = oracle.quantize_mxfp4(x)
+    assert scale[0, 0] == 126 + 127
+    # x / 2^126 lies in (3, 3.5]: p = 3, or 4 from the 3.5 tie on; 4 * 2^126 = 2^128 is
+    # unmaterializable in bf16/fp32, so those decode to Inf
+    nib = np.stack([packed[0] & 0xF, packed[0] >> 4], axis=1).reshape(-1)
+    assert set(nib.tolist()) == {5, 6}
+    dec = oracle.dequantize_mxfp4(packed, scale, 32, out_dtype=oracle.FP32).view(np.float32)
+    assert all((v == 3 * 2.0 ** 126) if n == 5 else np.isinf(v) for v, n in zip(dec[0], nib))
+    x = np.array([[0x7F40] * 32], dtype=np.uint16)                      # exactly the cap: scale 2^125
+    assert oracle.quantize_mxfp4(x)[1][0, 0] == 125 + 127
+
+
+@pytest.mark.parametrize("name", list(CORPORA))
+def test_decoded_deployment_weight_is_the_projection(name):
+    """[QAT] Description: training sees exactly the deployment weight -- below
+    the cap the decoded packed MXFP4 equals the projection bit for bit; the row
+    lift and the tile fold from the packed form equal those from the master."""
+    x = CORPORA[name]()
+    rows, K = x.shape
+    packed, scale = oracle.quantize_mxfp4(x)
+    ok = np.repeat(_below_cap_blocks(x), 32, axis=1)[:, :K]
+    y = oracle.fake_quantize_mxfp4(x)
+    dec = oracle.dequantize_mxfp4(packed, scale, K)
+    assert np.array_equal(dec[ok], y[ok])
+    d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+    d1, s1 = oracle.mxfp4_packed_to_mxfp8_row(packed, scale, K)
+    okb = _below_cap_blocks(x)
+    assert np.array_equal(d1[ok], d0[ok]) and np.array_equal(s1[okb], s0[okb])
+
+
+def test_tile_fold_from_packed_equals_fold_from_master():
+    row = np.concatenate([spread_row(d, b) for d in range(17) for b in (-126, -121, 3)])
+    x = np.stack([_fp32_bits_of(row), _fp32_bits_of(-row[::-1])])
+    packed, scale = oracle.quantize_mxfp4(x)
+    d0, c0 = oracle.mxfp4_to_fp8_block128(x)
+    d1, c1 = oracle.mxfp4_packed_to_fp8_block128(packed, scale, x.shape[1])
+    assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2_planted", "c2_natural"])
+def test_packed_oracle_matches_brute_force(name):
+    x = CORPORA[name]()
+    K = x.shape[1]
+    packed, scale = oracle.quantize_mxfp4(x)
+    bp, bs = F.quantize_mxfp4(x, "bf16")
+    assert np.array_equal(packed, bp) and np.array_equal(scale, bs)
+    assert np.array_equal(oracle.dequantize_mxfp4(packed, scale, K), F.dequantize_mxfp4(packed, scale, K, "bf16"))
+    d0, s0 = oracle.mxfp4_packed_to_mxfp8_row(packed, scale, K)
+    d1, s1 = F.packed_to_row(packed, scale, K)
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+
+
+def test_packed_fold_and_decode_every_code_vs_brute_force():
+    """Every E8M0 code (0..255) with every nibble, through decode (bf16, fp32),
+    the row lift and the tile fold."""
+    rows = 256
+    packed = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=np.uint8), (rows, 8))  # K = 128
+    scale = np.arange(256, dtype=np.uint8).reshape(rows, 1).repeat(4, axis=1)
+    scale[::7, 1] = 3                                   # mixed exponents inside tiles
+    K = 128
+    for out, odt in (("bf16", oracle.BF16), ("fp32", oracle.FP32)):
+        assert np.array_equal(oracle.dequantize_mxfp4(packed, scale, K, out_dtype=odt),
+                              F.dequantize_mxfp4(packed, scale, K, out))
+    d0, s0 = oracle.mxfp4_packed_to_mxfp8_row(packed, scale, K)
+    d1, s1 = F.packed_to_row(packed, scale, K)
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+    d0, c0 = oracle.mxfp4_packed_to_fp8_block128(packed, scale, K)
+    d1, c1 = F.packed_to_block128(packed, scale, K)
+    assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
