@@ -78,7 +78,7 @@ enum {
 const char* mxq_status_string(int status);
 
 /*
- * MXFP4 projection ("fake quantization"), [QAT] Description, conversion mode 1.
+ * MXFP4 projection (fake quantization), [QAT] Description, conversion mode 1.
  * For each 1x32 block of a row (the last block of a row may be shorter and
  * keeps its own scale, [EXP] Description): amax = max |x|; scale exponent
  * e = clamp(ceil(log2(amax/6)), -126, 125), taken from amax's bit pattern;

@@ -48,6 +48,9 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_DEQUANT_STEPS
 #define MXQ_DEQUANT_STEPS 2
 #endif
+#ifndef MXQ_PACKED_STEPS
+#define MXQ_PACKED_STEPS 2
+#endif
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
 #endif
@@ -59,7 +62,8 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kThreads = 256;     // 4 waves per workgroup
-constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS;
+constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
+              kPackedSteps = MXQ_PACKED_STEPS;
 
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
@@ -552,22 +556,36 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 8;
+  // All of the workgroup's loads are issued before any decode or store.
+  u32x2 qs[kDequantSteps];
+  uint32_t cs[kDequantSteps];
+#pragma unroll
+  for (int u = 0; u < kDequantSteps; u++) {
+    qs[u] = u32x2{0u, 0u};
+    cs[u] = 0u;
+    const uint32_t step = blockIdx.x * kDequantSteps + u;
+    if (step >= total_steps) continue;
+    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    if (col0 >= K) continue;
+    const uint8_t* drow = data + (int64_t)row * K;
+    if (VEC) {
+      qs[u] = stream_load(reinterpret_cast<const u32x2*>(drow + col0));
+    } else {
+      for (int i = 0; i < 8; i++)
+        if (col0 + i < K) qs[u][i / 4] |= (uint32_t)drow[col0 + i] << (8 * (i % 4));
+    }
+    cs[u] = kTile ? scale[(int64_t)(row / 128) * scale_ld + col0 / 128] : scale[(int64_t)row * scale_ld + col0 / 32];
+  }
+#pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
     const int64_t col0 = (int64_t)seg * 2048 + lane_col;
     if (col0 >= K) continue;
-    const uint8_t* drow = data + (int64_t)row * K;
-    u32x2 q = {0u, 0u};
-    if (VEC) {
-      q = stream_load(reinterpret_cast<const u32x2*>(drow + col0));
-    } else {
-      for (int i = 0; i < 8; i++)
-        if (col0 + i < K) q[i / 4] |= (uint32_t)drow[col0 + i] << (8 * (i % 4));
-    }
-    const uint32_t code = kTile ? scale[(int64_t)(row / 128) * scale_ld + col0 / 128]
-                                : scale[(int64_t)row * scale_ld + col0 / 32];
+    const u32x2 q = qs[u];
+    const uint32_t code = cs[u];
     const float s = e8m0(code);
     const bool fix_nan = code == 255u || has_nan_byte<kE5M2>(q);
     TO* orow = out + (int64_t)row * ld_out;
@@ -654,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(const T* __res
       if (col0 < K) {
         uint8_t* prow = packed + (int64_t)row * pw;
         if constexpr (VEC) {
-          *reinterpret_cast<N*>(prow + col0 / 2) = (N)f;
+          stream_store((N)f, reinterpret_cast<N*>(prow + col0 / 2));
         } else {
           for (int i = 0; i < G::kEPL; i += 2)
             if (col0 + i < K)
@@ -699,21 +717,34 @@ __global__ __launch_bounds__(kThreads) void dequantize_mxfp4_kernel(const uint8_
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 8, pw = (K + 1) / 2;
+  // All of the workgroup's loads are issued before any decode or store.
+  uint32_t fs[kDequantSteps], cs[kDequantSteps];
+#pragma unroll
+  for (int u = 0; u < kDequantSteps; u++) {
+    fs[u] = 0u;
+    cs[u] = 0u;
+    const uint32_t step = blockIdx.x * kDequantSteps + u;
+    if (step >= total_steps) continue;
+    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    if (col0 >= K) continue;
+    const uint8_t* prow = packed + (int64_t)row * pw;
+    if (VEC) {
+      fs[u] = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
+    } else {
+      for (int i = 0; i < 8; i += 2)
+        if (col0 + i < K) fs[u] |= (uint32_t)prow[(col0 + i) / 2] << (4 * i);
+    }
+    cs[u] = scale[(int64_t)row * scale_ld + col0 / 32];
+  }
+#pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
     const int64_t col0 = (int64_t)seg * 2048 + lane_col;
     if (col0 >= K) continue;
-    const uint8_t* prow = packed + (int64_t)row * pw;
-    uint32_t f = 0u;
-    if (VEC) {
-      f = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
-    } else {
-      for (int i = 0; i < 8; i += 2)
-        if (col0 + i < K) f |= (uint32_t)prow[(col0 + i) / 2] << (4 * i);
-    }
-    const u32x4 o = decode8_fp4(f, scale[(int64_t)row * scale_ld + col0 / 32]);
+    const u32x4 o = decode8_fp4(fs[u], cs[u]);
     TO* orow = out + (int64_t)row * ld_out;
     if constexpr (sizeof(TO) == 2) {
       if (VEC) {
@@ -749,98 +780,134 @@ __device__ __forceinline__ u32x2 e4m3x8_of_fp4(uint32_t f, int ds) {
   return u32x2{e4m3x4(bf16_pair<0>(f, sd), bf16_pair<1>(f, sd), se), e4m3x4(bf16_pair<2>(f, sd), bf16_pair<3>(f, sd), se)};
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void packed_row_kernel(const uint8_t* __restrict__ packed,
-                                                              const uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                              int64_t K, uint8_t* __restrict__ data,
-                                                              uint8_t* __restrict__ scale_out, int64_t scale_out_ld,
-                                                              uint32_t steps_per_row, uint32_t total_steps) {
+// Payload from packed MXFP4: each lane takes 16 elements (8 packed bytes in, 16
+// payload bytes out), so a block of 32 spans two lanes.  A step is 4096 elements
+// of one row.  With kTile the E8M0 code of the element's 128x128 tile (already
+// written by tile_codes_kernel) sets the fold; otherwise it is the fixed-shift-6
+// row lift of each block.
+template <bool VEC, bool kTile>
+__global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t* __restrict__ packed,
+                                                                  const uint8_t* __restrict__ scale,
+                                                                  int64_t scale_ld, int64_t K,
+                                                                  uint8_t* __restrict__ data,
+                                                                  uint8_t* __restrict__ code_out, int64_t code_ld,
+                                                                  uint32_t steps_per_row, uint32_t total_steps) {
   keep_denormals();
   const uint32_t tid = threadIdx.x;
-  const int64_t lane_col = (int64_t)tid * 8, pw = (K + 1) / 2;
-  for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = blockIdx.x * kRowSteps + u;
-    if (step >= total_steps) break;
+  const int64_t lane_col = (int64_t)tid * 16, pw = (K + 1) / 2;
+  // All of the workgroup's loads are issued before any conversion or store.
+  u32x2 f[kPackedSteps];
+  uint32_t c[kPackedSteps], tcode[kPackedSteps];
+#pragma unroll
+  for (int u = 0; u < kPackedSteps; u++) {
+    f[u] = u32x2{0u, 0u};
+    c[u] = 0u;
+    tcode[u] = 0u;
+    const uint32_t step = blockIdx.x * kPackedSteps + u;
+    if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    const int64_t col0 = (int64_t)seg * 4096 + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
-    uint32_t f = 0u;
     if (VEC) {
-      f = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
+      f[u] = stream_load(reinterpret_cast<const u32x2*>(prow + col0 / 2));
     } else {
-      for (int i = 0; i < 8; i += 2)
-        if (col0 + i < K) f |= (uint32_t)prow[(col0 + i) / 2] << (4 * i);
+      for (int i = 0; i < 16; i += 2)
+        if (col0 + i < K) f[u][i / 8] |= (uint32_t)prow[(col0 + i) / 2] << (4 * (i % 8));
     }
-    const uint32_t c = scale[(int64_t)row * scale_ld + col0 / 32];
-    // S = max(e - 6, -127): code max(c - 6, 0); shift e - S = min(c, 6)
-    const uint32_t code = c == 255u ? 255u : (c > 6u ? c - 6u : 0u);
-    u32x2 q = c == 255u ? u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu} : e4m3x8_of_fp4(f, (int)min(c, 6u));
+    c[u] = scale[(int64_t)row * scale_ld + col0 / 32];
+    if constexpr (kTile) tcode[u] = code_out[(int64_t)(row / 128) * code_ld + col0 / 128];
+  }
+#pragma unroll
+  for (int u = 0; u < kPackedSteps; u++) {
+    const uint32_t step = blockIdx.x * kPackedSteps + u;
+    if (step >= total_steps) break;
+    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const int64_t col0 = (int64_t)seg * 4096 + lane_col;
+    if (col0 >= K) continue;
+    u32x4 q;
+    uint32_t code = 0u;
+    if (c[u] == 255u) {
+      q = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      code = 255u;
+    } else {
+      int ds;
+      if constexpr (kTile) {
+        ds = (int)c[u] - (int)tcode[u];                        // e - S <= 6
+      } else {
+        code = c[u] > 6u ? c[u] - 6u : 0u;                     // S = max(e - 6, -127)
+        ds = (int)min(c[u], 6u);
+      }
+      const u32x2 lo = e4m3x8_of_fp4(f[u][0], ds), hi = e4m3x8_of_fp4(f[u][1], ds);
+      q = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
     uint8_t* drow = data + (int64_t)row * K;
     if (VEC) {
-      stream_store(q, reinterpret_cast<u32x2*>(drow + col0));
+      stream_store(q, reinterpret_cast<u32x4*>(drow + col0));
     } else {
-      for (int i = 0; i < 8; i++)
+      for (int i = 0; i < 16; i++)
         if (col0 + i < K) drow[col0 + i] = (uint8_t)(q[i / 4] >> (8 * (i % 4)));
     }
-    if (tid % 4 == 0) scale_out[(int64_t)row * scale_out_ld + col0 / 32] = (uint8_t)code;
+    if constexpr (!kTile) {
+      if (tid % 2 == 0) code_out[(int64_t)row * code_ld + col0 / 32] = (uint8_t)code;
+    }
   }
 }
 
-// 128x128 fold from packed MXFP4: same workgroup layout as the bf16 fold (1024
-// threads, 16 lanes across a tile row), block exponents read from the codes.
+// Tile codes from the packed weight's block codes alone.  A 256-thread
+// workgroup covers one 128-row band and 16 tile columns (64 codes of each row):
+// thread t reads the 16-code chunk t & 3 (four tile columns) of band rows t >> 2
+// and (t >> 2) + 64, so each group of four lanes reads 64 consecutive code bytes
+// of one row.  Lanes with the same chunk meet by shuffles, the four waves in LDS.
+// M = the largest finite code (1, i.e. e = -126, if none); tile code max(M - 6, 0).
 template <bool VEC>
-__global__ __launch_bounds__(kFoldThreads) void packed_block128_kernel(const uint8_t* __restrict__ packed,
-                                                                       const uint8_t* __restrict__ scale,
-                                                                       int64_t scale_ld, int64_t rows, int64_t K,
-                                                                       uint8_t* __restrict__ data,
-                                                                       uint8_t* __restrict__ tile_code,
-                                                                       int64_t tile_ld, uint32_t tiles_per_row) {
-  constexpr int LPR = 16, RPP = kFoldThreads / LPR, P = 128 / RPP;
-  __shared__ uint32_t s_max[kFoldWaves];
-  keep_denormals();
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t tr = blockIdx.x / tiles_per_row, tc = blockIdx.x - tr * tiles_per_row;
-  const int64_t r0 = (int64_t)tr * 128 + tid / LPR, col0 = (int64_t)tc * 128 + (tid % LPR) * 8, pw = (K + 1) / 2;
-  uint32_t f[P], c[P];
-  uint32_t m = 1u;                                          // biased M; 1 (e = -126) if no finite block
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                         int64_t rows, int64_t nb, uint8_t* __restrict__ tile_code,
+                                                         int64_t tile_ld, int64_t tiles_per_row) {
+  __shared__ uint32_t s_max[4][16];
+  const uint32_t tid = threadIdx.x, c = tid & 3u;
+  const int64_t j0 = ((int64_t)blockIdx.x * 4 + c) * 16, tr = blockIdx.y;
+  uint32_t m[4] = {1u, 1u, 1u, 1u};
 #pragma unroll
-  for (int i = 0; i < P; i++) {
-    const int64_t r = r0 + i * RPP;
-    f[i] = 0u;
-    c[i] = 1u;
-    if (r < rows && col0 < K) {
-      const uint8_t* prow = packed + r * pw;
-      if (VEC) {
-        f[i] = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
+  for (int h = 0; h < 2; h++) {
+    const int64_t r = tr * 128 + (tid >> 2) + 64 * h;
+    if (r < rows && j0 < nb) {
+      const uint8_t* src = scale + r * scale_ld + j0;
+      uint32_t w[4];
+      if (VEC && j0 + 16 <= nb) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
       } else {
-        for (int k = 0; k < 8; k += 2)
-          if (col0 + k < K) f[i] |= (uint32_t)prow[(col0 + k) / 2] << (4 * k);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          w[t] = 0u;
+#pragma unroll
+          for (int k = 0; k < 4; k++)
+            if (j0 + 4 * t + k < nb) w[t] |= (uint32_t)src[4 * t + k] << (8 * k);
+        }
       }
-      c[i] = scale[r * scale_ld + col0 / 32];
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const uint32_t code = (w[t] >> (8 * k)) & 0xFFu;
+          if (code != 255u) m[t] = max(m[t], code);
+        }
     }
-    if (c[i] != 255u) m = max(m, c[i]);
   }
-  m = max16(m);
 #pragma unroll
-  for (int off = LPR; off < 64; off *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if (lane == 0) s_max[wave] = m;
+  for (int t = 0; t < 4; t++)
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], off));
+  if ((tid & 63u) < 4u)
+#pragma unroll
+    for (int t = 0; t < 4; t++) s_max[tid >> 6][c * 4 + t] = m[t];
   __syncthreads();
-#pragma unroll
-  for (int v = 0; v < kFoldWaves; v++) m = max(m, s_max[v]);
-  const uint32_t code = m > 6u ? m - 6u : 0u;
-  if (tid == 0) tile_code[(int64_t)tr * tile_ld + tc] = (uint8_t)code;
-#pragma unroll
-  for (int i = 0; i < P; i++) {
-    const int64_t r = r0 + i * RPP;
-    if (r >= rows || col0 >= K) continue;
-    const u32x2 q = c[i] == 255u ? u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu} : e4m3x8_of_fp4(f[i], (int)c[i] - (int)code);
-    uint8_t* drow = data + r * K;
-    if (VEC) {
-      stream_store(q, reinterpret_cast<u32x2*>(drow + col0));
-    } else {
-      for (int k = 0; k < 8; k++)
-        if (col0 + k < K) drow[col0 + k] = (uint8_t)(q[k / 4] >> (8 * (k % 4)));
+  if (tid < 16u) {
+    const int64_t tc = (int64_t)blockIdx.x * 16 + tid;
+    if (tc < tiles_per_row) {
+      const uint32_t mm = max(max(s_max[0][tid], s_max[1][tid]), max(s_max[2][tid], s_max[3][tid]));
+      tile_code[tr * tile_ld + tc] = (uint8_t)(mm > 6u ? mm - 6u : 0u);
     }
   }
 }
@@ -1196,15 +1263,15 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
               rd = matrix_range(data, rows, K, K, 1), ro = matrix_range(scale_out, rows, nb, scale_out_ld, 1);
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(ro, rp) || overlap(ro, rs) || overlap(rd, ro)) return MXQ_ERR_ALIAS;
   uint32_t spr, total;
-  if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
-  const bool vec = aligned(packed, 4) && aligned(data, 8) && K % 8 == 0;
-  const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
+  if (steps_for(rows, K, 4096, &spr, &total)) return MXQ_ERR_SHAPE;
+  const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
+  const dim3 grid(grid_for(total, kPackedSteps)), block(kThreads);
   if (vec)
-    hipLaunchKernelGGL(packed_row_kernel<true>, grid, block, 0, stream, packed, scale, scale_ld, K, data, scale_out,
-                       scale_out_ld, spr, total);
+    hipLaunchKernelGGL((packed_convert_kernel<true, false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+                       scale_out, scale_out_ld, spr, total);
   else
-    hipLaunchKernelGGL(packed_row_kernel<false>, grid, block, 0, stream, packed, scale, scale_ld, K, data, scale_out,
-                       scale_out_ld, spr, total);
+    hipLaunchKernelGGL((packed_convert_kernel<false, false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+                       scale_out, scale_out_ld, spr, total);
   return launch_status();
 }
 
@@ -1220,14 +1287,25 @@ int mxq_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale
               rd = matrix_range(data, rows, K, K, 1), rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(rt, rp) || overlap(rt, rs) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
   if (ntc * ntr >= kMaxSteps) return MXQ_ERR_SHAPE;
-  const bool vec = aligned(packed, 4) && aligned(data, 8) && K % 8 == 0;
-  const dim3 grid((uint32_t)(ntc * ntr)), block(kFoldThreads);
-  if (vec)
-    hipLaunchKernelGGL(packed_block128_kernel<true>, grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
-                       tile_code, tile_ld, (uint32_t)ntc);
+  if (ntr > 65535) return MXQ_ERR_SHAPE;
+  const dim3 tgrid((uint32_t)((nb + 63) / 64), (uint32_t)ntr);
+  if (aligned(scale, 16) && scale_ld % 16 == 0)
+    hipLaunchKernelGGL((tile_codes_kernel<true>), tgrid, dim3(256), 0, stream, scale, scale_ld, rows, nb, tile_code,
+                       tile_ld, ntc);
   else
-    hipLaunchKernelGGL(packed_block128_kernel<false>, grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
-                       tile_code, tile_ld, (uint32_t)ntc);
+    hipLaunchKernelGGL((tile_codes_kernel<false>), tgrid, dim3(256), 0, stream, scale, scale_ld, rows, nb, tile_code,
+                       tile_ld, ntc);
+  if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
+  uint32_t spr, total;
+  if (steps_for(rows, K, 4096, &spr, &total)) return MXQ_ERR_SHAPE;
+  const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
+  const dim3 grid(grid_for(total, kPackedSteps)), block(kThreads);
+  if (vec)
+    hipLaunchKernelGGL((packed_convert_kernel<true, true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+                       tile_code, tile_ld, spr, total);
+  else
+    hipLaunchKernelGGL((packed_convert_kernel<false, true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+                       tile_code, tile_ld, spr, total);
   return launch_status();
 }
 

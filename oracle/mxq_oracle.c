@@ -163,7 +163,7 @@ static int scale_exponent_clamped(dyadic amax, int lo, int hi) {
 }
 
 /* E2M1 code of |x| / 2^e rounded to the nearest grid point, ties to the even
- * code ([QAT] Description: "RTNE onto E2M1").  Values above 6 have 6 as their
+ * code ([QAT] Description: round to nearest, ties to even, on E2M1).  Values above 6 have 6 as their
  * nearest grid point (the top scale saturates: [QAT] Known limitations). */
 int orc_e2m1_code(dyadic ax, int e) {
   if (ax.M == 0) return 0;
