@@ -25,7 +25,7 @@ _LIB = os.path.join(_HERE, "libmxq_oracle.so")
 
 BF16, FP32 = 0, 1
 E4M3, E5M2 = 0, 1
-ROW_1X32, TILE_128X128 = 0, 1
+ROW_1X32, TILE_128X128, COL_32X1 = 0, 1, 2
 
 _lock = threading.Lock()
 _lib = None
@@ -50,6 +50,7 @@ def lib() -> ctypes.CDLL:
             L.orc_fake_quantize_mxfp4.argtypes = [vp, i64, vp, i64, i64, i64, i32, i64, i64]
             L.orc_mxfp4_to_mxfp8_row.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, i64, i64]
             L.orc_mxfp4_to_fp8_block128.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, i64, i64]
+            L.orc_mxfp4_to_mxfp8_col.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, i64, i64]
             L.orc_export_mxfp8.argtypes = [vp, i64, i64, i64, vp]
             L.orc_dequantize.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, i64, i32, i64, i64]
             L.orc_quantize_mxfp4.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, i64, i64]
@@ -70,7 +71,7 @@ def lib() -> ctypes.CDLL:
             L.orc_unpack.argtypes = [ctypes.c_uint32, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_uint64),
                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]
             for name in ("orc_fake_quantize_mxfp4", "orc_mxfp4_to_mxfp8_row", "orc_mxfp4_to_fp8_block128",
-                         "orc_export_mxfp8", "orc_dequantize", "orc_scale_exponent_bits", "orc_e2m1_code_bits"):
+                         "orc_mxfp4_to_mxfp8_col", "orc_export_mxfp8", "orc_dequantize", "orc_scale_exponent_bits", "orc_e2m1_code_bits"):
                 getattr(L, name).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -171,6 +172,21 @@ def mxfp4_to_fp8_block128(x: np.ndarray, tile_ld: int | None = None, threads: in
     _run(lambda r0, r1: L.orc_mxfp4_to_fp8_block128(_ptr(x), ld, rows, K, _dtype_of(x), _ptr(data), _ptr(codes),
                                                     tile_ld, r0, r1), rows, threads, align=128)
     return data, codes
+
+
+def mxfp4_to_mxfp8_col(x: np.ndarray, scale_ld: int | None = None, threads: int = 1, fill: int = 0):
+    """MXFP8 columnwise (32x1 blocks) from the decomposition: (payload uint8 [rows, K],
+    codes uint8 [ceil(rows/32), scale_ld]).  Padding columns keep `fill`."""
+    x = _as2d(x)
+    rows, K = x.shape
+    ld = _ld(x)
+    scale_ld = K if scale_ld is None else scale_ld
+    data = np.empty((rows, K), dtype=np.uint8)
+    scale = np.full(((rows + 31) // 32, scale_ld), fill, dtype=np.uint8)
+    L = lib()
+    _run(lambda r0, r1: L.orc_mxfp4_to_mxfp8_col(_ptr(x), ld, rows, K, _dtype_of(x), _ptr(data), _ptr(scale),
+                                                 scale_ld, r0, r1), rows, threads, align=32)
+    return data, scale
 
 
 def export_mxfp8(scale_storage: np.ndarray, K: int) -> np.ndarray:

@@ -359,6 +359,81 @@ int orc_mxfp4_to_fp8_block128(const void* x, int64_t ld_x, int64_t rows, int64_t
 }
 
 /*
+ * MXFP8 columnwise from the decomposition ([QAT] Description, mode 2, and its
+ * MXFP8 weight dataflow without a backward override): a fresh MXFP8
+ * quantization, over 32x1 blocks (32 consecutive rows of one column), of the
+ * projected weight y = p * 2^e, with the host quantizer's scale rule, so that
+ * the bytes equal those the host quantizer makes from the projection (mode 1).
+ *
+ * Reading (the pages name the host amax rule but do not write it out): the OCP
+ * MX rule, scale 2^S with S = floor(log2(amax)) - 8, 8 being E4M3's largest
+ * exponent, raised to -127 where it falls below the E8M0 range; payload
+ * RTNE_E4M3(y / 2^S) with subnormals.  On projected values amax has at most
+ * two significant bits, so this S equals ceil(log2(amax / 448)) (the rule that
+ * divides by E4M3's largest value) and y / 2^S <= 384 never saturates.
+ * Readings: amax is over the block's finite values; an element of a poisoned
+ * row block (NaN in y) gets payload 0x7F and takes no part in amax; a block with
+ * no nonzero finite value gets code 0; blocks start at row 0 and the last one
+ * may be short.  The code of row block j, column c, is scale[j*scale_ld + c].
+ * Processes the row blocks that start in [r0, r1) (r0 a multiple of 32).
+ */
+int orc_mxfp4_to_mxfp8_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, int dtype,
+                           uint8_t* data, uint8_t* scale, int64_t scale_ld, int64_t r0, int64_t r1) {
+  if (check_common(rows, K, ld_x, dtype, r0, r1) || scale_ld < K || (r0 % 32) != 0) return ORC_BAD_ARG;
+  if (K == 0) return ORC_OK;
+  /* the projected values of one 32-row band: |y| = M * 2^k, nan marks poison */
+  typedef struct { int neg, nan; uint64_t M; int k; } yval;
+  yval* y = (yval*)malloc(sizeof(yval) * 32 * (size_t)K);
+  if (!y) die("out of memory");
+  dyadic v[32];
+  for (int64_t b0 = r0; b0 < r1; b0 += 32) {
+    int64_t b1 = b0 + 32 < rows ? b0 + 32 : rows;
+    /* step 1: the MXFP4 decomposition of every 1x32 row block in the band */
+    for (int64_t r = b0; r < b1; r++) {
+      for (int64_t c0 = 0; c0 < K; c0 += 32) {
+        int n = (int)(K - c0 < 32 ? K - c0 : 32);
+        read_block(x, ld_x, dtype, r, c0, n, v);
+        block_info b = analyse_block(v, n);
+        for (int i = 0; i < n; i++) {
+          yval* t = &y[(r - b0) * K + c0 + i];
+          t->neg = v[i].neg;
+          t->nan = b.poisoned;
+          t->M = (uint64_t)E2M1_X2[orc_e2m1_code(v[i], b.e)];   /* 2p */
+          t->k = b.e - 1;
+        }
+      }
+    }
+    /* step 2: per column, the block's amax, its scale and the payloads */
+    for (int64_t c = 0; c < K; c++) {
+      dyadic amax = {0, CLS_FINITE, 0, 0};
+      for (int64_t r = b0; r < b1; r++) {
+        const yval* t = &y[(r - b0) * K + c];
+        dyadic d = {t->neg, CLS_FINITE, t->M, t->k};
+        if (!t->nan && cmp_mag(d, amax) > 0) amax = d;
+      }
+      int S = -127;
+      if (amax.M != 0) {
+        int fl = bitlen(amax.M) - 1 + amax.k;                   /* floor(log2(amax)) */
+        S = fl - 8 < -127 ? -127 : fl - 8;
+      }
+      scale[(b0 / 32) * scale_ld + c] = (uint8_t)(S + 127);
+      for (int64_t r = b0; r < b1; r++) {
+        const yval* t = &y[(r - b0) * K + c];
+        uint8_t q = 0x7F;
+        if (!t->nan) {
+          int inexact, ovf;
+          q = (uint8_t)round_to_format(t->neg, t->M, t->k - S, FMT_E4M3, &inexact, &ovf);
+          if (ovf) die("columnwise payload overflowed E4M3");
+        }
+        data[r * K + c] = q;
+      }
+    }
+  }
+  free(y);
+  return ORC_OK;
+}
+
+/*
  * Unpadded export ([EXP] Description): scale_inv has shape (rows, ceil(K/32)),
  * taken from the first ceil(K/32) columns of storage whose row stride is
  * scale_ld; the payload bytes are the data itself.
@@ -377,19 +452,22 @@ int orc_export_mxfp8(const uint8_t* scale_storage, int64_t rows, int64_t K, int6
  * E8M0 decode fix; Test results: planted extreme scale codes).  A NaN payload
  * also decodes to NaN.  Reading: NaN is written as the canonical quiet NaN.
  * layout 0: one code per 1x32 block of a row (scale[r*scale_ld + col/32]);
- * layout 1: one code per 128x128 tile (scale[(r/128)*scale_ld + col/128]).
+ * layout 1: one code per 128x128 tile (scale[(r/128)*scale_ld + col/128]);
+ * layout 2: one code per 32x1 block of a column (scale[(r/32)*scale_ld + col]).
  * fp8 0: E4M3 (FN); fp8 1: E5M2 (IEEE, with Inf).
  */
 int orc_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                    int fp8, int layout, void* out, int64_t ld_out, int dtype, int64_t r0, int64_t r1) {
   if (rows < 0 || K < 0 || ld_out < K || (dtype != 0 && dtype != 1) || (fp8 != 0 && fp8 != 1) ||
-      (layout != 0 && layout != 1) || r0 < 0 || r1 > rows || r0 > r1) return ORC_BAD_ARG;
-  int64_t ncols = layout == 0 ? (K + 31) / 32 : (K + 127) / 128;
+      layout < 0 || layout > 2 || r0 < 0 || r1 > rows || r0 > r1) return ORC_BAD_ARG;
+  int64_t ncols = layout == 0 ? (K + 31) / 32 : layout == 1 ? (K + 127) / 128 : K;
   if (scale_ld < ncols) return ORC_BAD_ARG;
   fmt_t f = dtype_fmt(dtype), pf = fp8 == 0 ? FMT_E4M3 : FMT_E5M2;
   for (int64_t r = r0; r < r1; r++) {
     for (int64_t col = 0; col < K; col++) {
-      uint8_t c = layout == 0 ? scale[r * scale_ld + col / 32] : scale[(r / 128) * scale_ld + col / 128];
+      uint8_t c = layout == 0   ? scale[r * scale_ld + col / 32]
+                  : layout == 1 ? scale[(r / 128) * scale_ld + col / 128]
+                                : scale[(r / 32) * scale_ld + col];
       dyadic q = unpack(data[r * K + col], pf);
       uint32_t o;
       if (c == 255 || q.cls == CLS_NAN) {
@@ -411,11 +489,11 @@ int orc_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
 /* ------------------------------------------------------------------------ */
 /*
  * Quantize for deployment: E2M1 payloads and 1x32 power-of-two E8M0 scales
- * ([QAT] Description: "training sees exactly the deployment weight (E2M1
- * payloads, 1x32 power-of-two UE8M0 scales)"; [ISS] Description, workflow 2).
- * The MXFP4 decomposition is the projection's, except that above the cap the
- * scale moves to 2^126 ([QAT] Known limitations: "packed deployment moves to
- * scale 2^126"): e = clamp(ceil(log2(amax/6)), -126, 126).  Code = e + 127.
+ * ([QAT] Description: the weight training sees is the deployed one, E2M1
+ * payloads with one power-of-two UE8M0 scale per 1x32 block; [ISS]
+ * Description, workflow 2).  The MXFP4 decomposition is the projection's,
+ * except that above the cap the scale moves to 2^126 ([QAT] Known
+ * limitations): e = clamp(ceil(log2(amax/6)), -126, 126).  Code = e + 127.
  * Packing: element 2i in the low nibble of byte i, 2i+1 in the high nibble
  * (0 when K is odd); rows are ceil(K/2) bytes, contiguous.
  * Readings: the lower clamp stays at -126 (so the decoded deployment weight is

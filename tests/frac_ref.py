@@ -250,6 +250,56 @@ def block128(x: np.ndarray, dtype: str, mutation: str | None = None):
     return data, codes_out
 
 
+_POW2 = [(k, Fraction(2) ** k) for k in range(-400, 400)]
+_POW2_VALS = [v for _, v in _POW2]
+
+
+def col_scale(amax: Fraction, mutation: str | None = None) -> int:
+    """Shared scale exponent S of a 32x1 block: the largest k with 2^k <= amax
+    (found by search over every k in [-400, 400)), minus 8 (E4M3's largest
+    exponent), at least -127; amax 0 gives -127.
+    mutation "col_rule_448": the smallest S with amax / 2^S <= 448 instead.
+    mutation "col_emax7": floor(log2 amax) - 7."""
+    if amax == 0:
+        return -127
+    if mutation == "col_rule_448":
+        S = min(k for k, v in _POW2 if amax / v <= 448)
+    else:
+        k = _POW2[bisect.bisect_right(_POW2_VALS, amax) - 1][0]
+        S = k - (7 if mutation == "col_emax7" else 8)
+    return max(S, -127)
+
+
+def col_lift(x: np.ndarray, dtype: str, scale_ld: int | None = None, mutation: str | None = None):
+    """MXFP8 columnwise from the decomposition: the projected values p * 2^e,
+    re-quantized over 32x1 blocks of each column.  A NaN (poisoned) element gets
+    0x7F and no say in the block's amax (mutation "col_nan_poisons": any NaN
+    makes the whole block code 255 / 0x7F)."""
+    rows, K = x.shape
+    y = [[None] * K for _ in range(rows)]                # (value, neg) or NAN
+    for r in range(rows):
+        for c0, c1 in _blocks(K):
+            poisoned, e, codes, negs = block_decomposition(x[r, c0:c1], dtype)
+            for i, (c, neg) in enumerate(zip(codes, negs)):
+                y[r][c0 + i] = NAN if poisoned else (GRID[c] * Fraction(2) ** e, neg)
+    data = np.zeros((rows, K), dtype=np.uint8)
+    scale = np.zeros(((rows + 31) // 32, scale_ld or K), dtype=np.uint8)
+    for b0 in range(0, rows, 32):
+        for col in range(K):
+            cells = [(r, y[r][col]) for r in range(b0, min(b0 + 32, rows))]
+            finite = [v for _, t in cells if t != NAN for v in (t[0],)]
+            if mutation == "col_nan_poisons" and len(finite) < len(cells):
+                scale[b0 // 32, col] = 255
+                for r, _ in cells:
+                    data[r, col] = 0x7F
+                continue
+            S = col_scale(max(finite) if finite else Fraction(0), mutation)
+            scale[b0 // 32, col] = S + 127
+            for r, t in cells:
+                data[r, col] = 0x7F if t == NAN else table("e4m3").nearest_even(t[0] / Fraction(2) ** S, t[1])
+    return data, scale
+
+
 def export(scale_storage: np.ndarray, K: int, mutation: str | None = None) -> np.ndarray:
     ncols = K // 32 if mutation == "floor_cols" else (K + 31) // 32
     return scale_storage[:, :ncols].copy()
@@ -266,7 +316,8 @@ def dequantize(data: np.ndarray, scale: np.ndarray, layout: str, out: str, fp8: 
     dec = e4m3_value if fp8 == "e4m3" else e5m2_value
     for r in range(rows):
         for col in range(K):
-            c = scale[r, col // 32] if layout == "row" else scale[r // 128, col // 128]
+            c = (scale[r, col // 32] if layout == "row" else scale[r // 128, col // 128] if layout == "tile"
+                 else scale[r // 32, col])
             q = dec(int(data[r, col]))
             s = e8m0_value(int(c))
             neg = bool(data[r, col] & 0x80)

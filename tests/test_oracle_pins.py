@@ -551,3 +551,150 @@ def test_packed_fold_and_decode_every_code_vs_brute_force():
     d0, c0 = oracle.mxfp4_packed_to_fp8_block128(packed, scale, K)
     d1, c1 = F.packed_to_block128(packed, scale, K)
     assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
+
+
+# ---------------------------------------------------------------- MXFP8 columnwise (32x1)
+
+def _proj_float(x):
+    """The projection of x as float64 (NaN for poisoned blocks)."""
+    y = oracle.fake_quantize_mxfp4(x)
+    if y.dtype == np.uint16:
+        return (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return y.view(np.float32).astype(np.float64)
+
+
+def _col_corpora():
+    return {"c1": W.c1_small(), "c2_natural": W.c2_exhaustive(natural=True),
+            "c2_planted": W.c2_planted(), "fp32_fuzz": W.fp32_fuzz(1 << 12)}
+
+
+def test_col_scale_rules_agree_on_projected_magnitudes():
+    """Every magnitude the projection can produce (p * 2^e, p on the E2M1 grid,
+    e in [-126, 125]) has at most two significant bits, so the OCP rule
+    floor(log2 amax) - 8 and the rule ceil(log2(amax / 448)) give the same
+    scale, and amax / 2^S (256 or 384) never saturates E4M3.  Off that domain
+    the two rules differ (1.875 * 2^k), so the agreement is not vacuous."""
+    for e in range(-126, 126):
+        for p in F.GRID[1:]:
+            v = p * Fraction(2) ** e
+            S = F.col_scale(v)
+            assert S == F.col_scale(v, "col_rule_448")
+            assert v / Fraction(2) ** S <= 384
+    v = Fraction(15, 8) * Fraction(2) ** 3
+    assert F.col_scale(v) != F.col_scale(v, "col_rule_448")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2_natural", "c2_planted", "fp32_fuzz"])
+def test_col_payload_matches_torch_cast(name):
+    """Library pin: per 32x1 block, S from numpy's frexp of the finite amax, the
+    payload from torch's float8_e4m3fn cast of y / 2^S (exact in float64), NaN
+    elements 0x7F, and codes S + 127."""
+    x = _col_corpora()[name]
+    data, scale = oracle.mxfp4_to_mxfp8_col(x)
+    y = _proj_float(x)
+    rows, K = y.shape
+    for b0 in range(0, rows, 32):
+        blk = y[b0:b0 + 32]
+        fin = np.where(np.isnan(blk), 0.0, np.abs(blk))
+        amax = fin.max(axis=0)
+        _, ex = np.frexp(amax)                                   # amax = m * 2^ex, m in [0.5, 1)
+        S = np.where(amax > 0, np.maximum(ex - 1 - 8, -127), -127)
+        assert np.array_equal(scale[b0 // 32], (S + 127).astype(np.uint8))
+        q = np.ldexp(blk, -S[None, :])
+        want = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        want = np.where(np.isnan(blk), 0x7F, want)
+        assert np.array_equal(data[b0:b0 + 32], want)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2_natural", "c2_planted", "fp32_fuzz"])
+def test_col_of_projection_equals_col_of_master(name, facts):
+    """The pages: the direct columnwise bytes equal the host quantizer's bytes
+    for the projected weight.  The bytes depend on the projected values only,
+    so quantizing the projection (whose own decomposition may differ) gives
+    the same bytes as going from the master weight."""
+    assert facts["columnwise_from_decomposition"]["value"]["bytes_equal_projection_route"]
+    x = _col_corpora()[name]
+    d0, s0 = oracle.mxfp4_to_mxfp8_col(x)
+    d1, s1 = oracle.mxfp4_to_mxfp8_col(oracle.fake_quantize_mxfp4(x))
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2_natural", "fp32_fuzz"])
+def test_col_decode_is_exact_exactly_where_e4m3_holds_the_value(name):
+    """decode(col(x)) equals the projection at every element whose y / 2^S is
+    a multiple of 2^-9 (E4M3's smallest subnormal; it never exceeds 384), and
+    differs from it everywhere else.  NaN elements decode to NaN."""
+    x = _col_corpora()[name]
+    data, scale = oracle.mxfp4_to_mxfp8_col(x)
+    y = _proj_float(x)
+    back = oracle.dequantize(data, scale, layout=oracle.COL_32X1, out_dtype=FP32).view(np.float32).astype(np.float64)
+    S = np.repeat(scale.astype(np.int64) - 127, 32, axis=0)[:y.shape[0]]
+    q = np.ldexp(np.nan_to_num(y), -S + 9)
+    exact = q == np.round(q)
+    nan = np.isnan(y)
+    assert np.array_equal(np.isnan(back), nan)
+    assert np.array_equal(back[exact & ~nan], y[exact & ~nan])
+    assert not np.any(back[~exact & ~nan] == y[~exact & ~nan])
+
+
+def test_col_special_blocks():
+    """Zero blocks get code 0 with signed zero payloads; a column of 2^-127
+    gets code 0 and payload 1.0 (0x38); a poisoned row block's elements are
+    0x7F and leave the other rows' codes as they are; bands are 32 rows from
+    row 0 and the last may be short."""
+    tiny = bf16_bits(2.0 ** -127)
+    x = np.zeros((40, 64), dtype=np.uint16)
+    x[1, :] = 0x8000                                       # -0
+    x[:, 32:] = tiny
+    data, scale = oracle.mxfp4_to_mxfp8_col(x)
+    assert scale.shape == (2, 64) and not scale.any()
+    assert set(data[1, :32].tolist()) == {0x80} and set(data[0, :32].tolist()) == {0x00}
+    assert set(data[:, 32:].ravel().tolist()) == {0x38}
+    g = np.random.default_rng(5)
+    zf = (g.standard_normal((40, 64)) * 2.0 ** g.integers(-4, 5, (40, 1))).astype(np.float32)
+    z = torch.from_numpy(zf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    d0, s0 = oracle.mxfp4_to_mxfp8_col(z)
+    zp = z.copy()
+    zp[3, 5] = 0x7FC0                                      # poisons row 3, columns 0..31
+    zz = z.copy()
+    zz[3, :32] = 0
+    d1, s1 = oracle.mxfp4_to_mxfp8_col(zp)
+    d2, s2 = oracle.mxfp4_to_mxfp8_col(zz)
+    assert set(d1[3, :32].tolist()) == {0x7F}
+    assert np.array_equal(s1, s2)
+    mask = np.ones_like(d1, dtype=bool)
+    mask[3, :32] = False
+    assert np.array_equal(d1[mask], d2[mask])
+    assert np.array_equal(d0[32:], oracle.mxfp4_to_mxfp8_col(np.ascontiguousarray(z[32:]))[0])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2_planted", "c2_natural", "fp32_fuzz"])
+def test_col_oracle_matches_brute_force(name):
+    x = _col_corpora()[name]
+    if name == "fp32_fuzz":
+        x = np.ascontiguousarray(x[:, :512])
+    d0, s0 = oracle.mxfp4_to_mxfp8_col(x)
+    d1, s1 = F.col_lift(x, "fp32" if x.dtype == np.uint32 else "bf16")
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+
+
+def test_col_decode_layout_matches_brute_force():
+    g = np.random.default_rng(7)
+    data = g.integers(0, 256, (70, 40), dtype=np.uint8)
+    scale = g.integers(0, 256, (3, 40), dtype=np.uint8)
+    scale[0, :4] = [0, 255, 127, 254]
+    for out, od in (("bf16", BF16), ("fp32", FP32)):
+        got = oracle.dequantize(data, scale, layout=oracle.COL_32X1, out_dtype=od)
+        assert np.array_equal(got, F.dequantize(data, scale, "col", out))
+
+
+@pytest.mark.parametrize("mutation,changes", [("col_emax7", True), ("col_nan_poisons", True), ("col_rule_448", False)])
+def test_col_pins_catch_planted_mistakes(mutation, changes):
+    """A wrong shift or whole-block NaN poisoning changes the bytes the pins
+    compare; the other reading of the host rule (ceil(log2(amax/448))) gives
+    the same bytes on projected weights, so that choice is not load-bearing."""
+    x = W.c2_exhaustive(natural=True)
+    d0, s0 = oracle.mxfp4_to_mxfp8_col(x)
+    d1, s1 = F.col_lift(x, "bf16", mutation=mutation)
+    same = np.array_equal(d0, d1) and np.array_equal(s0, s1)
+    assert same != changes
