@@ -68,6 +68,12 @@ def packed_bytes(rows: int, K: int) -> dict:
             "packed_to_row": n // 2 + nb + n + nb, "packed_to_block128": n // 2 + nb + n + tiles}
 
 
+def col_bytes(rows: int, K: int) -> dict:
+    """Bytes of the columnwise (32x1) kernels for a [rows, K] bf16 weight."""
+    n, nb, nc = rows * K, rows * ((K + 31) // 32), ((rows + 31) // 32) * K
+    return {"col": 2 * n + n + nc, "row_col": 2 * n + n + nb + n + nc, "dec_col": n + nc + 2 * n}
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -164,11 +170,14 @@ def main():
             "pscale": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
             "data2": torch.empty((rows, K), dtype=torch.uint8, device=dev),
             "scale2": torch.zeros((rows, SCALE_LD), dtype=torch.uint8, device=dev),
+            "cdata": torch.empty((rows, K), dtype=torch.uint8, device=dev),
+            "cscale": torch.empty(((rows + 31) // 32, K), dtype=torch.uint8, device=dev),
         }
         mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
         mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
         mxq.mxq_mxfp4_to_fp8_block128(s["x"], s["bdata"], s["tc"])
         mxq.mxq_quantize_mxfp4(s["x"], s["packed"], s["pscale"])
+        mxq.mxq_mxfp4_to_mxfp8_col(s["x"], s["cdata"], s["cscale"])
         sets.append(s)
     del x0
     torch.cuda.synchronize()
@@ -192,10 +201,18 @@ def main():
                                                                               s["scale2"][:, :nb])
     launches["packed_to_block128"] = lambda s: mxq.mxq_mxfp4_packed_to_fp8_block128(s["packed"], s["pscale"], K,
                                                                                     s["bdata"], s["tc"])
-    extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128"]
+    # outside the step: MXFP8 columnwise (32x1), alone and with the row lift in one pass, and its decode
+    launches["col"] = lambda s: mxq.mxq_mxfp4_to_mxfp8_col(s["x"], s["cdata"], s["cscale"])
+    launches["row_col"] = lambda s: mxq.mxq_mxfp4_to_mxfp8_row_col(s["x"], s["data2"], s["scale2"], s["cdata"],
+                                                                     s["cscale"])
+    launches["dec_col"] = lambda s: mxq.mxq_dequantize(s["cdata"], s["cscale"], layout=mxq.MXQ_SCALE_COL_32X1,
+                                                       out=s["dec_t"])
+    extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128", "col",
+                   "row_col", "dec_col"]
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
     offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1,
-              "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0}
+              "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0, "col": 2,
+              "row_col": 4, "dec_col": 1}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -243,7 +260,7 @@ def main():
         kernels[n] = {"us": round(us, 2), "bytes": nbytes[n], "GB/s": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
     extra = {}
-    extra_bytes = dict(packed_bytes(rows, K), fused=fused_bytes(rows, K))
+    extra_bytes = dict(packed_bytes(rows, K), fused=fused_bytes(rows, K), **col_bytes(rows, K))
     for n in extra_names:
         a, b = bursts[n]
         us = 1e3 * a.elapsed_time(b) / args.steps
@@ -251,6 +268,7 @@ def main():
         extra["fused_proj_row" if n == "fused" else n] = {"us": round(us, 2), "bytes": extra_bytes[n],
                                                           "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     extra["fused_proj_row"]["vs_separate_us"] = round(kernels["proj"]["us"] + kernels["row"]["us"], 2)
+    extra["row_col"]["vs_separate_us"] = round(kernels["row"]["us"] + extra["col"]["us"], 2)
     dominant = max(names, key=lambda n: kernels[n]["us"])
     rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
           "unit": "GB/s", "frac": kernels[dominant]["frac"], "traffic": read_traffic(dominant)}

@@ -11,9 +11,11 @@
  *   mxq_fake_quantize_mxfp4_with_mxfp8_row    projection + row lift in one pass
  *   mxq_mxfp4_to_mxfp8_row_guarded,
  *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
- * and the packed MXFP4 deployment format:
+ * the packed MXFP4 deployment format:
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
  *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
+ * and MXFP8 columnwise (32x1) from the decomposition:
+ *   mxq_mxfp4_to_mxfp8_col, mxq_mxfp4_to_mxfp8_row_col (row and column in one pass)
  *
  * Sources, by page title and section:
  *   [QAT] "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8 block-scaling recipes"
@@ -59,9 +61,10 @@ typedef enum { MXQ_BF16 = 0, MXQ_FP32 = 1, MXQ_FP16 = 2 } mxq_dtype;
 typedef enum { MXQ_E4M3 = 0, MXQ_E5M2 = 1 } mxq_fp8;
 
 /* Where a payload element's E8M0 code lives: one per 1x32 block of a row
- * (scale[r*scale_ld + c/32]) or one per 128x128 tile anchored at (0,0)
- * (scale[(r/128)*scale_ld + c/128]). */
-typedef enum { MXQ_SCALE_ROW_1X32 = 0, MXQ_SCALE_TILE_128X128 = 1 } mxq_scale_layout;
+ * (scale[r*scale_ld + c/32]), one per 128x128 tile anchored at (0,0)
+ * (scale[(r/128)*scale_ld + c/128]), or one per 32x1 block of a column
+ * anchored at row 0 (scale[(r/32)*scale_ld + c]). */
+typedef enum { MXQ_SCALE_ROW_1X32 = 0, MXQ_SCALE_TILE_128X128 = 1, MXQ_SCALE_COL_32X1 = 2 } mxq_scale_layout;
 
 /* Status codes. */
 enum {
@@ -159,6 +162,43 @@ int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows,
                                       hipStream_t stream);
 
 /*
+ * MXFP8 columnwise from the MXFP4 decomposition ([QAT] Description, conversion
+ * mode 2, and its MXFP8 weight dataflow without a backward override, where the
+ * dgrad operand is built from the same decomposition): a fresh MXFP8
+ * quantization of the projected weight y = p * 2^e over 32x1 blocks, i.e. 32
+ * consecutive rows of one column, anchored at row 0 (the last block may be
+ * short).  The pages require these bytes to equal the host quantizer's bytes for
+ * the projected weight and name its amax rule without writing it out; the rule
+ * taken is the OCP MX one: S = floor(log2 amax) - 8 (8 = E4M3's largest
+ * exponent), raised to -127 if lower; code = S + 127; payload =
+ * RTNE_E4M3(y / 2^S) with subnormals.  On projected weights amax has at most two
+ * significant bits, so S also equals ceil(log2(amax / 448)) and nothing
+ * saturates.  amax is over the block's finite values: elements of poisoned row
+ * blocks (NaN in the projection) get payload 0x7F; a block with no nonzero
+ * finite value gets code 0.  Unlike the row lift this re-rounds: decode gives
+ * back the projection wherever y / 2^S is a multiple of 2^-9.
+ *   x      [rows, K] bf16 or fp32, row stride ld_x >= K
+ *   data   [rows, K] uint8 E4M3 payload in x's (untransposed) layout, contiguous
+ *   scale  [ceil(rows/32), scale_ld] uint8 E8M0 codes, scale_ld >= K; columns
+ *          j >= K of each scale row are left untouched
+ *   data and scale must not overlap x or each other (MXQ_ERR_ALIAS).
+ */
+int mxq_mxfp4_to_mxfp8_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                           uint8_t* scale, int64_t scale_ld, hipStream_t stream);
+
+/*
+ * The MXFP8 rowwise lift (mxq_mxfp4_to_mxfp8_row) and the columnwise conversion
+ * (mxq_mxfp4_to_mxfp8_col) from one read of x: the pair the MXFP8 weight
+ * dataflow without a backward override keeps for the forward and backward GEMMs
+ * ([QAT] Description, weight dataflows).  Outputs are bit-identical to the two
+ * separate calls; arguments as for them.  No output may overlap x or another
+ * output (MXQ_ERR_ALIAS).
+ */
+int mxq_mxfp4_to_mxfp8_row_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                               uint8_t* row_data, uint8_t* row_scale, int64_t row_scale_ld, uint8_t* col_data,
+                               uint8_t* col_scale, int64_t col_scale_ld, hipStream_t stream);
+
+/*
  * Unpadded export of MXFP8 rowwise scales, [EXP] Description: scale_inv holds
  * E8M0 codes with shape (*shape[:-1], ceil(K/32)), without padding; a partial
  * last block keeps its own scale.  Copies the first ceil(K/32) columns of each
@@ -183,8 +223,9 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
  * infinite; values beyond the output range round to Inf.
  *   data     [rows, K] uint8 payload, contiguous (row stride K)
  *   scale    E8M0 codes: [rows, scale_ld] for MXQ_SCALE_ROW_1X32 (scale_ld >=
- *            ceil(K/32)) or [ceil(rows/128), scale_ld] for MXQ_SCALE_TILE_128X128
- *            (scale_ld >= ceil(K/128))
+ *            ceil(K/32)), [ceil(rows/128), scale_ld] for MXQ_SCALE_TILE_128X128
+ *            (scale_ld >= ceil(K/128)) or [ceil(rows/32), scale_ld] for
+ *            MXQ_SCALE_COL_32X1 (scale_ld >= K)
  *   out      [rows, K] bf16 or fp32, row stride ld_out >= K; must not overlap
  *            data or scale
  */
@@ -194,8 +235,8 @@ int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
 
 /*
  * Packed MXFP4, the deployment format: E2M1 payloads with 1x32 power-of-two
- * E8M0 scales ([QAT] Description: "training sees exactly the deployment
- * weight"; the export issue's workflow 2, "quantize weights for inference").
+ * E8M0 scales ([QAT] Description: the weight seen in training is the deployed
+ * one; the export issue's workflow 2, quantizing weights for inference).
  * Layout: packed [rows, ceil(K/2)] uint8, contiguous, element 2i in the low
  * nibble of byte i and 2i+1 in the high nibble (0 when K is odd); each nibble
  * is S.EE.M (sign, then the 3-bit E2M1 code of {0, .5, 1, 1.5, 2, 3, 4, 6}).

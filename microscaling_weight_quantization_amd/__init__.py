@@ -27,14 +27,15 @@ from . import build as _build
 
 MXQ_BF16, MXQ_FP32, MXQ_FP16 = 0, 1, 2
 MXQ_E4M3, MXQ_E5M2 = 0, 1
-MXQ_SCALE_ROW_1X32, MXQ_SCALE_TILE_128X128 = 0, 1
+MXQ_SCALE_ROW_1X32, MXQ_SCALE_TILE_128X128, MXQ_SCALE_COL_32X1 = 0, 1, 2
 MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_DTYPE, MXQ_ERR_NO_ROWWISE_DATA, MXQ_ERR_ALIAS, MXQ_ERR_HIP = range(7)
 
 ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mxfp8_row",
                 "mxq_mxfp4_to_fp8_block128", "mxq_export_mxfp8", "mxq_dequantize",
                 "mxq_fake_quantize_mxfp4_with_mxfp8_row", "mxq_mxfp4_to_mxfp8_row_guarded",
                 "mxq_mxfp4_to_fp8_block128_guarded", "mxq_quantize_mxfp4", "mxq_dequantize_mxfp4",
-                "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128")
+                "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
+                "mxq_mxfp4_to_mxfp8_row_col")
 
 _libs = {}
 _lock = threading.Lock()
@@ -71,6 +72,8 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_dequantize_mxfp4.argtypes = [u8p, u8p, i64, i64, i64, vp, i64, i32, vp]
         L.mxq_mxfp4_packed_to_mxfp8_row.argtypes = [u8p, u8p, i64, i64, i64, u8p, u8p, i64, vp]
         L.mxq_mxfp4_packed_to_fp8_block128.argtypes = [u8p, u8p, i64, i64, i64, u8p, u8p, i64, vp]
+        L.mxq_mxfp4_to_mxfp8_col.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
+        L.mxq_mxfp4_to_mxfp8_row_col.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -180,6 +183,52 @@ def mxq_mxfp4_to_fp8_block128(x: torch.Tensor, data: Optional[torch.Tensor] = No
     else:
         _check(L, L.mxq_mxfp4_to_fp8_block128_guarded(px, ldx, rows, K, dt, pd, pt, ldt, _flag(noop), _stream(x)))
     return data, tile_code
+
+
+def _payload_for(x: torch.Tensor, rows: int, K: int, data: Optional[torch.Tensor]):
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    pd, _, _, ldd = _matrix(data)
+    if rows * K and (ldd != K or data.numel() != rows * K):
+        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    return data, pd
+
+
+def mxq_mxfp4_to_mxfp8_col(x: torch.Tensor, data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                           scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+    """MXFP8 columnwise (32x1 blocks) from the decomposition ->
+    (payload uint8 [rows, K], E8M0 codes uint8 [ceil(rows/32), scale_ld])."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    px, rows, K, ldx = _matrix(x)
+    if scale is None:
+        scale = torch.zeros(((rows + 31) // 32, scale_ld or K), dtype=torch.uint8, device=x.device)
+    data, pd = _payload_for(x, rows, K, data)
+    ps, _, _, ld_s = _matrix(scale)
+    _check(L, L.mxq_mxfp4_to_mxfp8_col(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    return data, scale
+
+
+def mxq_mxfp4_to_mxfp8_row_col(x: torch.Tensor, row_data: Optional[torch.Tensor] = None,
+                               row_scale: Optional[torch.Tensor] = None, col_data: Optional[torch.Tensor] = None,
+                               col_scale: Optional[torch.Tensor] = None, row_scale_ld: Optional[int] = None,
+                               col_scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+    """Row lift and columnwise conversion from one read of x ->
+    (row payload, row codes [rows, row_scale_ld], column payload, column codes [ceil(rows/32), col_scale_ld])."""
+    L = load(lib)
+    dt = _dtype_code(x)
+    px, rows, K, ldx = _matrix(x)
+    nb = (K + 31) // 32
+    if row_scale is None:
+        row_scale = torch.zeros((rows, row_scale_ld or nb), dtype=torch.uint8, device=x.device)
+    if col_scale is None:
+        col_scale = torch.zeros(((rows + 31) // 32, col_scale_ld or K), dtype=torch.uint8, device=x.device)
+    row_data, prd = _payload_for(x, rows, K, row_data)
+    col_data, pcd = _payload_for(x, rows, K, col_data)
+    prs, _, _, ld_rs = _matrix(row_scale)
+    pcs, _, _, ld_cs = _matrix(col_scale)
+    _check(L, L.mxq_mxfp4_to_mxfp8_row_col(px, ldx, rows, K, dt, prd, prs, ld_rs, pcd, pcs, ld_cs, _stream(x)))
+    return row_data, row_scale, col_data, col_scale
 
 
 def mxq_fake_quantize_mxfp4_with_mxfp8_row(x: torch.Tensor, y: Optional[torch.Tensor] = None,

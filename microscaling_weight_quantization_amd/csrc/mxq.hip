@@ -51,6 +51,9 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_PACKED_STEPS
 #define MXQ_PACKED_STEPS 2
 #endif
+#ifndef MXQ_COL_THREADS
+#define MXQ_COL_THREADS 128   // columnwise: lanes per workgroup, one 16-byte chunk of columns each
+#endif
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
 #endif
@@ -62,6 +65,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kThreads = 256;     // 4 waves per workgroup
+constexpr int kColThreads = MXQ_COL_THREADS;
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
               kPackedSteps = MXQ_PACKED_STEPS;
 
@@ -412,6 +416,129 @@ __global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, 
 }
 
 // ------------------------------------------------------------------------------------
+// MXFP8 columnwise (32x1) from the decomposition ([QAT] Description, conversion
+// mode 2): the projected weight re-quantized over blocks of 32 consecutive rows
+// of one column with the OCP MX scale rule, S = floor(log2 amax) - 8 floored at
+// -127, payload RTNE_E4M3(y / 2^S).  Projected magnitudes have at most two
+// significant bits, so amax / 2^S is 256 or 384 and never saturates, and the
+// rule equals ceil(log2(amax / 448)).  amax skips the NaNs of poisoned row
+// blocks; their payload is 0x7F.
+//
+// A workgroup takes one 32-row band and one step of columns (256 lanes x one
+// 16-byte chunk).  Each lane loads its chunk of all 32 rows before anything
+// else, projects them in registers (bf16 words, exact), keeps the finite column
+// maxima with packed 16-bit max, then writes the band's codes and payload.
+// With kRow the same pass also writes the rowwise lift of every row block.
+// ------------------------------------------------------------------------------------
+// E4M3 bytes of four bf16 values at four scales: each pair is converted at
+// both of its elements' scales and the right byte of each is kept (two byte
+// permutes; the second pair's conversion writes the high half of the first's).
+__device__ __forceinline__ uint32_t e4m3x4_each(uint32_t y01, uint32_t y23, float s0, float s1, float s2, float s3) {
+  const s16x2 a = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, BF(y01), s0, false);
+  const s16x2 b = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, BF(y01), s1, false);
+  // bytes {a0, b1}: perm picks byte k of (b:a), a being bytes 0-3
+  const uint32_t lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x0C0C0500u);
+  const s16x2 c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2, lo), BF(y23), s2, true);
+  const s16x2 d = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, BF(y23), s3, true);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, c), 0x07020100u);
+}
+
+template <typename T, bool VEC, bool kRow>
+__global__ __launch_bounds__(kColThreads) void col_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K,
+                                                       uint8_t* __restrict__ cdata, uint8_t* __restrict__ cscale,
+                                                       int64_t cscale_ld, uint8_t* __restrict__ rdata,
+                                                       uint8_t* __restrict__ rscale, int64_t rscale_ld,
+                                                       uint32_t groups) {
+  using G = StepGeom<T>;
+  constexpr int EPL = Fmt<T>::kEPL, NW = sizeof(T) == 2 ? 4 : 2;   // elements, bf16 words per chunk
+  keep_denormals();
+  const uint32_t tid = threadIdx.x, band = blockIdx.x / groups, grp = blockIdx.x - band * groups;
+  const int64_t col0 = (int64_t)grp * (kColThreads * EPL) + (int64_t)tid * EPL, r0 = (int64_t)band * 32;
+  const int nr = (int)min((int64_t)32, rows - r0);
+  const bool in = col0 < K;
+
+  // Loads.  Rows past the band's end repeat its last row: never stored, and
+  // they cannot raise a column maximum.  VEC: no branch around a load, so each
+  // row is used as soon as it lands; a lane past K reads the row's last chunk
+  // and takes no part in the block maxima.  Otherwise elements past K load as 0.
+  u32x4 w[32];
+  if constexpr (VEC) {
+    const T* px = x + r0 * ld_x + (in ? col0 : K - EPL);     // per lane
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      w[i] = stream_load(reinterpret_cast<const u32x4*>(px));
+      px += i + 1 < nr ? ld_x : 0;
+    }
+  } else {
+    const T* px = x + r0 * ld_x;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      w[i] = load_chunk<T, false>(px, col0, K);
+      px += i + 1 < nr ? ld_x : 0;
+    }
+  }
+
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 cmax[NW];
+#pragma unroll
+  for (int j = 0; j < NW; j++) cmax[j] = u16x2{0, 0};
+  uint32_t poison = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    uint32_t a = chunk_amax<T>(w[i]);
+    if constexpr (VEC) a = in ? a : 0u;
+    const Block b = block_of_amax<T>(block_max<Fmt<T>::kLPB>(a));
+    const float s = e8m0(b.eb);
+    // a poisoned block's nibbles are zeroed: its y (unused) stays out of the maxima
+    const Proj16<T> y = project<T>(b.poison ? 0u : fp4_of(w[i], s, T{}), s);
+    if constexpr (kRow) {
+      if (i < nr) {
+        const uint32_t code = row_code(b);
+        store_payload<T, VEC>(rdata + (r0 + i) * K, col0, K, payload_chunk<T>(y, code, b.poison));
+        if (tid % G::kLPB == 0 && in) rscale[(r0 + i) * rscale_ld + col0 / 32] = (uint8_t)code;
+      }
+    }
+    poison |= (uint32_t)b.poison << i;
+#pragma unroll
+    for (int j = 0; j < NW; j++) {
+      w[i][j] = y.p[j];
+      cmax[j] = __builtin_elementwise_max(cmax[j], __builtin_bit_cast(u16x2, y.p[j] & 0x7FFF7FFFu));
+    }
+  }
+
+  // code = S + 127 = max(E - 8, 0) with E the bf16 exponent field of the column amax
+  float sc[EPL];
+  uint32_t codes[EPL];
+#pragma unroll
+  for (int k = 0; k < EPL; k++) {
+    const uint32_t E = (uint32_t)cmax[k / 2][k % 2] >> 7;
+    codes[k] = E > 8u ? E - 8u : 0u;
+    sc[k] = e8m0(codes[k]);
+  }
+  uint8_t* crow = cscale + (int64_t)band * cscale_ld;
+#pragma unroll
+  for (int k = 0; k < EPL; k++)
+    if (col0 + k < K) crow[col0 + k] = (uint8_t)codes[k];
+
+  uint8_t* pd = cdata + r0 * K;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    if (i < nr) {
+      typename PayloadChunk<T>::type q;
+      if constexpr (sizeof(T) == 2) {
+        q = u32x2{e4m3x4_each(w[i][0], w[i][1], sc[0], sc[1], sc[2], sc[3]),
+                  e4m3x4_each(w[i][2], w[i][3], sc[4], sc[5], sc[6], sc[7])};
+        if ((poison >> i) & 1u) q = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      } else {
+        q = (poison >> i) & 1u ? 0x7F7F7F7Fu : e4m3x4_each(w[i][0], w[i][1], sc[0], sc[1], sc[2], sc[3]);
+      }
+      store_payload<T, VEC>(pd, col0, K, q);
+      pd += K;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // 128x128 tile fold, one HBM pass.  A workgroup folds J tiles that sit side by
 // side in one 128-row band, so each row of the band contributes a contiguous
 // run of J * 256 bytes (bf16) per load.  Each lane keeps only the E2M1 nibbles,
@@ -547,7 +674,28 @@ __device__ __forceinline__ bool has_nan_byte(u32x2 q) {
   return ((((q[0] & 0x7F7F7F7Fu) + add) | ((q[1] & 0x7F7F7F7Fu) + add)) & 0x80808080u) != 0u;
 }
 
-template <typename TO, bool kE5M2, bool kTile, bool VEC>
+// Scale layouts of the decode: one code per 1x32 row block, per 128x128 tile,
+// or per 32x1 column block (then each of a lane's 8 columns has its own code).
+enum { kLayRow = 0, kLayTile = 1, kLayCol = 2 };
+
+// 8 FP8 bytes -> 8 bf16 with one scale per element: each byte pair is decoded
+// at both elements' scales and the halves are picked.
+template <bool kE5M2, bool HI>
+__device__ __forceinline__ uint32_t bf16_pair_of_fp8(uint32_t q, float s) {
+  if constexpr (kE5M2) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(q, s, HI));
+  else return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, s, HI));
+}
+template <bool kE5M2, bool HI>
+__device__ __forceinline__ uint32_t bf16_pair_of_fp8_each(uint32_t q, float s_lo, float s_hi) {
+  return (bf16_pair_of_fp8<kE5M2, HI>(q, s_lo) & 0x0000FFFFu) | (bf16_pair_of_fp8<kE5M2, HI>(q, s_hi) & 0xFFFF0000u);
+}
+template <bool kE5M2>
+__device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8]) {
+  return u32x4{bf16_pair_of_fp8_each<kE5M2, false>(q[0], s[0], s[1]), bf16_pair_of_fp8_each<kE5M2, true>(q[0], s[2], s[3]),
+               bf16_pair_of_fp8_each<kE5M2, false>(q[1], s[4], s[5]), bf16_pair_of_fp8_each<kE5M2, true>(q[1], s[6], s[7])};
+}
+
+template <typename TO, bool kE5M2, int kLay, bool VEC>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
@@ -558,11 +706,13 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   const int64_t lane_col = (int64_t)tid * 8;
   // All of the workgroup's loads are issued before any decode or store.
   u32x2 qs[kDequantSteps];
-  uint32_t cs[kDequantSteps];
+  uint32_t cs[kDequantSteps];                               // the step's code (row, tile layouts)
+  u32x2 ccs[kLay == kLayCol ? kDequantSteps : 1];           // the 8 columns' codes (column layout)
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     qs[u] = u32x2{0u, 0u};
     cs[u] = 0u;
+    if constexpr (kLay == kLayCol) ccs[u] = u32x2{0u, 0u};
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
@@ -575,7 +725,18 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       for (int i = 0; i < 8; i++)
         if (col0 + i < K) qs[u][i / 4] |= (uint32_t)drow[col0 + i] << (8 * (i % 4));
     }
-    cs[u] = kTile ? scale[(int64_t)(row / 128) * scale_ld + col0 / 128] : scale[(int64_t)row * scale_ld + col0 / 32];
+    if constexpr (kLay == kLayCol) {
+      const uint8_t* srow = scale + (int64_t)(row / 32) * scale_ld;
+      if (VEC) {
+        ccs[u] = *reinterpret_cast<const u32x2*>(srow + col0);
+      } else {
+        for (int i = 0; i < 8; i++)
+          if (col0 + i < K) ccs[u][i / 4] |= (uint32_t)srow[col0 + i] << (8 * (i % 4));
+      }
+    } else {
+      cs[u] = kLay == kLayTile ? scale[(int64_t)(row / 128) * scale_ld + col0 / 128]
+                               : scale[(int64_t)row * scale_ld + col0 / 32];
+    }
   }
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
@@ -585,12 +746,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     const int64_t col0 = (int64_t)seg * 2048 + lane_col;
     if (col0 >= K) continue;
     const u32x2 q = qs[u];
-    const uint32_t code = cs[u];
-    const float s = e8m0(code);
-    const bool fix_nan = code == 255u || has_nan_byte<kE5M2>(q);
+    float s8[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      if constexpr (kLay == kLayCol) s8[i] = e8m0((ccs[u][i / 4] >> (8 * (i % 4))) & 0xFFu);
+      else s8[i] = e8m0(cs[u]);
+    }
+    const float s = s8[0];
+    const bool fix_nan = kLay == kLayCol || cs[u] == 255u || has_nan_byte<kE5M2>(q);
     TO* orow = out + (int64_t)row * ld_out;
     if constexpr (sizeof(TO) == 2) {
-      u32x4 o = decode8_bf16<kE5M2>(q, s);
+      u32x4 o = kLay == kLayCol ? decode8_bf16_each<kE5M2>(q, s8) : decode8_bf16<kE5M2>(q, s);
       if (fix_nan) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -605,10 +771,10 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
           if (col0 + i < K) orow[col0 + i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
       }
     } else {
-      uint32_t f[8] = {decode1_f32<kE5M2, 0>(q[0], s), decode1_f32<kE5M2, 1>(q[0], s),
-                       decode1_f32<kE5M2, 2>(q[0], s), decode1_f32<kE5M2, 3>(q[0], s),
-                       decode1_f32<kE5M2, 0>(q[1], s), decode1_f32<kE5M2, 1>(q[1], s),
-                       decode1_f32<kE5M2, 2>(q[1], s), decode1_f32<kE5M2, 3>(q[1], s)};
+      uint32_t f[8] = {decode1_f32<kE5M2, 0>(q[0], s8[0]), decode1_f32<kE5M2, 1>(q[0], s8[1]),
+                       decode1_f32<kE5M2, 2>(q[0], s8[2]), decode1_f32<kE5M2, 3>(q[0], s8[3]),
+                       decode1_f32<kE5M2, 0>(q[1], s8[4]), decode1_f32<kE5M2, 1>(q[1], s8[5]),
+                       decode1_f32<kE5M2, 2>(q[1], s8[6]), decode1_f32<kE5M2, 3>(q[1], s8[7])};
       if (fix_nan) {
 #pragma unroll
         for (int i = 0; i < 8; i++)
@@ -999,6 +1165,28 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
 }
 
 template <typename T>
+int launch_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* cdata, uint8_t* cscale,
+               int64_t cscale_ld, uint8_t* rdata, uint8_t* rscale, int64_t rscale_ld, hipStream_t s) {
+  constexpr int64_t kCols = (int64_t)kColThreads * Fmt<T>::kEPL;   // columns per workgroup
+  const int64_t groups = (K + kCols - 1) / kCols, bands = (rows + 31) / 32;
+  if (bands > kMaxSteps / groups) return MXQ_ERR_SHAPE;
+  constexpr int EPL = Fmt<T>::kEPL;
+  const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(cdata, EPL) &&
+                   (rdata == nullptr || aligned(rdata, EPL));
+  const dim3 grid((uint32_t)(bands * groups)), block(kColThreads);
+#define MXQ_COL_LAUNCH(V, R)                                                                                    \
+  hipLaunchKernelGGL((col_kernel<T, V, R>), grid, block, 0, s, (const T*)x, ld_x, rows, K, cdata, cscale, cscale_ld, \
+                     rdata, rscale, rscale_ld, (uint32_t)groups)
+  if (rdata != nullptr) {
+    if (vec) MXQ_COL_LAUNCH(true, true); else MXQ_COL_LAUNCH(false, true);
+  } else {
+    if (vec) MXQ_COL_LAUNCH(true, false); else MXQ_COL_LAUNCH(false, false);
+  }
+#undef MXQ_COL_LAUNCH
+  return launch_status();
+}
+
+template <typename T>
 int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* data, uint8_t* tile_code,
                     int64_t tile_ld, const int32_t* noop, hipStream_t s) {
   constexpr int J = FoldGeom<T>::kJ;
@@ -1016,31 +1204,39 @@ int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_
   return launch_status();
 }
 
-template <typename TO, bool kE5M2, bool kTile>
+template <typename TO, bool kE5M2, int kLay>
 int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K, void* out,
                      int64_t ld_out, hipStream_t s) {
   uint32_t spr, total;
   if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
-  const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
+  const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0 &&
+                   (kLay != kLayCol || (aligned(scale, 8) && scale_ld % 8 == 0));
   const dim3 grid(grid_for(total, kDequantSteps)), block(kThreads);
   if (vec)
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kTile, true>), grid, block, 0, s, data, scale, scale_ld, K,
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
   else
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kTile, false>), grid, block, 0, s, data, scale, scale_ld, K,
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, false>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
   return launch_status();
+}
+
+template <typename TO, bool kE5M2>
+int launch_dequant_f(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                     mxq_scale_layout lay, void* out, int64_t ld_out, hipStream_t s) {
+  if (lay == MXQ_SCALE_TILE_128X128)
+    return launch_dequant_t<TO, kE5M2, kLayTile>(data, scale, scale_ld, rows, K, out, ld_out, s);
+  if (lay == MXQ_SCALE_COL_32X1)
+    return launch_dequant_t<TO, kE5M2, kLayCol>(data, scale, scale_ld, rows, K, out, ld_out, s);
+  return launch_dequant_t<TO, kE5M2, kLayRow>(data, scale, scale_ld, rows, K, out, ld_out, s);
 }
 
 template <typename TO>
 int launch_dequant(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                    mxq_fp8 fmt, mxq_scale_layout lay, void* out, int64_t ld_out, hipStream_t s) {
-  const bool e5 = fmt == MXQ_E5M2, tile = lay == MXQ_SCALE_TILE_128X128;
-  if (e5 && tile) return launch_dequant_t<TO, true, true>(data, scale, scale_ld, rows, K, out, ld_out, s);
-  if (e5) return launch_dequant_t<TO, true, false>(data, scale, scale_ld, rows, K, out, ld_out, s);
-  if (tile) return launch_dequant_t<TO, false, true>(data, scale, scale_ld, rows, K, out, ld_out, s);
-  return launch_dequant_t<TO, false, false>(data, scale, scale_ld, rows, K, out, ld_out, s);
+  return fmt == MXQ_E5M2 ? launch_dequant_f<TO, true>(data, scale, scale_ld, rows, K, lay, out, ld_out, s)
+                         : launch_dequant_f<TO, false>(data, scale, scale_ld, rows, K, lay, out, ld_out, s);
 }
 
 template <typename T>
@@ -1175,6 +1371,44 @@ int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows,
   return block128_entry(x, ld_x, rows, K, dt, data, tile_code, tile_ld, noop, true, stream);
 }
 
+static int col_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* row_data,
+                     uint8_t* row_scale, int64_t row_scale_ld, bool with_row, uint8_t* col_data, uint8_t* col_scale,
+                     int64_t col_scale_ld, hipStream_t stream) {
+  if (check_dtype(dt)) return MXQ_ERR_DTYPE;
+  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXQ_OK;
+  if (!x || !col_data || !col_scale || (with_row && (!row_data || !row_scale))) return MXQ_ERR_NULL;
+  const int64_t nb = (K + 31) / 32, bands = (rows + 31) / 32;
+  if (ld_x < K || col_scale_ld < K || (with_row && row_scale_ld < nb)) return MXQ_ERR_SHAPE;
+  const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), cd = matrix_range(col_data, rows, K, K, 1),
+              cs = matrix_range(col_scale, bands, K, col_scale_ld, 1);
+  if (overlap(rx, cd) || overlap(rx, cs) || overlap(cd, cs)) return MXQ_ERR_ALIAS;
+  if (with_row) {
+    const Range rd = matrix_range(row_data, rows, K, K, 1), rs = matrix_range(row_scale, rows, nb, row_scale_ld, 1);
+    if (overlap(rx, rd) || overlap(rx, rs) || overlap(rd, rs) || overlap(rd, cd) || overlap(rd, cs) ||
+        overlap(rs, cd) || overlap(rs, cs))
+      return MXQ_ERR_ALIAS;
+  } else {
+    row_data = nullptr, row_scale = nullptr, row_scale_ld = 0;
+  }
+  return dt == MXQ_BF16 ? launch_col<uint16_t>(x, ld_x, rows, K, col_data, col_scale, col_scale_ld, row_data,
+                                               row_scale, row_scale_ld, stream)
+                        : launch_col<uint32_t>(x, ld_x, rows, K, col_data, col_scale, col_scale_ld, row_data,
+                                               row_scale, row_scale_ld, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                           uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
+  return col_entry(x, ld_x, rows, K, dt, nullptr, nullptr, 0, false, data, scale, scale_ld, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_row_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                               uint8_t* row_data, uint8_t* row_scale, int64_t row_scale_ld, uint8_t* col_data,
+                               uint8_t* col_scale, int64_t col_scale_ld, hipStream_t stream) {
+  return col_entry(x, ld_x, rows, K, dt, row_data, row_scale, row_scale_ld, true, col_data, col_scale, col_scale_ld,
+                   stream);
+}
+
 int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t rows, int64_t K, int64_t scale_ld,
                      uint8_t* scale_out, hipStream_t stream) {
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
@@ -1207,12 +1441,14 @@ int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
                    hipStream_t stream) {
   if (check_dtype(out_dt)) return MXQ_ERR_DTYPE;
   if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_DTYPE;
-  if (layout != MXQ_SCALE_ROW_1X32 && layout != MXQ_SCALE_TILE_128X128) return MXQ_ERR_DTYPE;
+  if (layout != MXQ_SCALE_ROW_1X32 && layout != MXQ_SCALE_TILE_128X128 && layout != MXQ_SCALE_COL_32X1)
+    return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (rows == 0 || K == 0) return MXQ_OK;
   if (!data || !scale || !out) return MXQ_ERR_NULL;
-  const bool tile = layout == MXQ_SCALE_TILE_128X128;
-  const int64_t srows = tile ? (rows + 127) / 128 : rows, scols = tile ? (K + 127) / 128 : (K + 31) / 32;
+  const bool tile = layout == MXQ_SCALE_TILE_128X128, col = layout == MXQ_SCALE_COL_32X1;
+  const int64_t srows = tile ? (rows + 127) / 128 : col ? (rows + 31) / 32 : rows,
+                scols = tile ? (K + 127) / 128 : col ? K : (K + 31) / 32;
   if (ld_out < K || scale_ld < scols) return MXQ_ERR_SHAPE;
   const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt));
   if (overlap(ro, matrix_range(data, rows, K, K, 1)) || overlap(ro, matrix_range(scale, srows, scols, scale_ld, 1)))

@@ -1,0 +1,167 @@
+"""GPU parity of MXFP8 columnwise (32x1) from the MXFP4 decomposition, and of the
+row + column pass, against the CPU oracle bit for bit (tolerance 0).
+
+Inputs are the seeded workloads of ``workloads``; the same host bits feed the
+oracle and the device copy.  The small, exhaustive, spread-sweep and headline
+weights are compared in full; the MLP weights are launched in full and compared
+on sampled 32-row bands (bands are independent, so the oracle runs on just
+those rows)."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_weight_quantization_amd as mxq
+import oracle
+import workloads as W
+from tests.test_gpu_parity import assert_bits, out_dtype_of, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+THREADS = 16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mxq.load()
+    return torch.device("cuda:0")
+
+
+def check_col(bits: np.ndarray, dev, pad: int = 0, lib: str = "libmxq.so", fused: bool = True):
+    """Columnwise payload and codes (padding columns untouched), their decode in
+    both output dtypes, and the row + column pass against row and column."""
+    x = to_dev(bits, dev)
+    rows, K = bits.shape
+    nb = (K + 31) // 32
+    bands = (rows + 31) // 32
+    tdt, odt = out_dtype_of(bits)
+    scale = torch.full((bands, K + pad), 0xA5, dtype=torch.uint8, device=dev)
+    data, scale = mxq.mxq_mxfp4_to_mxfp8_col(x, scale=scale, lib=lib)
+    wd, ws = oracle.mxfp4_to_mxfp8_col(bits, scale_ld=K + pad, threads=THREADS, fill=0xA5)
+    assert_bits(to_host(data), wd, "column payload")
+    assert_bits(to_host(scale), ws, "column codes (padding untouched)")
+    for t, o in ((tdt, odt), (torch.float32, oracle.FP32)):
+        dec = mxq.mxq_dequantize(data, scale, layout=mxq.MXQ_SCALE_COL_32X1, out_dtype=t, lib=lib)
+        want = oracle.dequantize(wd, ws, layout=oracle.COL_32X1, out_dtype=o, threads=THREADS)
+        assert_bits(to_host(dec), want, f"column decode to {t}")
+    if fused:
+        rs = torch.full((rows, nb + pad), 0x5A, dtype=torch.uint8, device=dev)
+        cs = torch.full((bands, K + pad), 0x5A, dtype=torch.uint8, device=dev)
+        rd, rs, cd, cs = mxq.mxq_mxfp4_to_mxfp8_row_col(x, row_scale=rs, col_scale=cs, lib=lib)
+        wrd, wrs = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=nb + pad, threads=THREADS, fill=0x5A)
+        assert_bits(to_host(rd), wrd, "row + column pass: row payload")
+        assert_bits(to_host(rs), wrs, "row + column pass: row codes")
+        assert_bits(to_host(cd), wd, "row + column pass: column payload")
+        ws2 = ws.copy()
+        ws2[:, K:] = 0x5A
+        assert_bits(to_host(cs), ws2, "row + column pass: column codes")
+
+
+def test_col_c1_small(dev):
+    check_col(W.c1_small(), dev, pad=4)
+
+
+@pytest.mark.parametrize("natural", [False, True])
+def test_col_c2_exhaustive(dev, natural):
+    check_col(W.c2_exhaustive(natural=natural), dev)
+
+
+def test_col_c2_planted(dev):
+    check_col(W.c2_planted(), dev, pad=3)
+
+
+def test_col_fp32_fuzz(dev):
+    check_col(W.fp32_fuzz(1 << 18).reshape(-1, 256), dev)
+
+
+def test_col_c3_spread_sweep(dev):
+    check_col(W.c3_spread(), dev)
+
+
+def test_col_c4_headline(dev):
+    check_col(W.c4_headline(), dev)
+
+
+@pytest.mark.parametrize("which", ["up", "down", "up_master"])
+def test_col_c5_mlp_sampled_bands(dev, which):
+    bits = W.c5_mlp(which)
+    rows, K = bits.shape
+    x = to_dev(bits, dev)
+    rd, rs, cd, cs = mxq.mxq_mxfp4_to_mxfp8_row_col(x)
+    rd, rs, cd, cs = to_host(rd), to_host(rs), to_host(cd), to_host(cs)
+    g = np.random.default_rng(11)
+    bands = np.unique(np.concatenate([[0, rows // 32 - 1], g.choice(rows // 32, 10, replace=False)]))
+    for b in bands:
+        sub = np.ascontiguousarray(bits[32 * b:32 * b + 32])
+        wd, ws = oracle.mxfp4_to_mxfp8_col(sub, threads=THREADS)
+        assert_bits(cd[32 * b:32 * b + 32], wd, f"column payload band {b}")
+        assert_bits(cs[b:b + 1], ws, f"column codes band {b}")
+        wrd, wrs = oracle.mxfp4_to_mxfp8_row(sub, threads=THREADS)
+        assert_bits(rd[32 * b:32 * b + 32], wrd, f"row payload band {b}")
+        assert_bits(rs[32 * b:32 * b + 32], wrs, f"row codes band {b}")
+
+
+@pytest.mark.parametrize("rows,K", [(1, 1), (31, 7), (33, 33), (65, 100), (131, 257), (40, 2049), (96, 4096)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_col_ragged_shapes(dev, rows, K, dtype):
+    if dtype == "bf16":
+        flat = np.tile(W.c2_exhaustive().reshape(-1), (rows * K) // 65536 + 1)
+    else:
+        flat = W.fp32_fuzz(((rows * K + 31) // 32) * 32).reshape(-1)
+    check_col(np.ascontiguousarray(flat[: rows * K].reshape(rows, K)), dev, pad=rows % 3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_col_strided_and_misaligned_views(dev, dtype):
+    base = W.c2_planted() if dtype == "bf16" else W.fp32_fuzz(64 * 200).reshape(64, 200)
+    big = to_dev(np.ascontiguousarray(np.tile(base, (1, 4))), dev)
+    K = 96
+    for off in (0, 1, 3):
+        view = big[:, off:off + K]
+        bits = to_host(view)
+        d, s = mxq.mxq_mxfp4_to_mxfp8_col(view)
+        wd, ws = oracle.mxfp4_to_mxfp8_col(bits)
+        assert_bits(to_host(d), wd, f"column payload off={off}")
+        assert_bits(to_host(s), ws, f"column codes off={off}")
+
+
+def test_col_decode_every_byte_and_code(dev):
+    """Column layout: 256 bands of 32 rows; band b uses code b in every column
+    and column c holds byte c, so every (code, byte) pair is decoded."""
+    data = np.tile(np.arange(256, dtype=np.uint8), (32 * 256, 1))
+    codes = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 256, axis=1)
+    codes[:, 1::2] = codes[::-1, 1::2]                  # neighbouring columns use different codes
+    dd, dc = to_dev(data, dev), to_dev(codes, dev)
+    for fmt_dev, fmt_orc in ((mxq.MXQ_E4M3, oracle.E4M3), (mxq.MXQ_E5M2, oracle.E5M2)):
+        for tdt, odt in ((torch.bfloat16, oracle.BF16), (torch.float32, oracle.FP32)):
+            got = to_host(mxq.mxq_dequantize(dd, dc, layout=mxq.MXQ_SCALE_COL_32X1, fmt=fmt_dev, out_dtype=tdt))
+            want = oracle.dequantize(data, codes, layout=oracle.COL_32X1, fp8=fmt_orc, out_dtype=odt, threads=THREADS)
+            assert_bits(got, want, f"column decode {fmt_orc} {odt}")
+
+
+def test_col_empty_and_errors(dev):
+    for shape in ((0, 32), (5, 0)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        d, s = mxq.mxq_mxfp4_to_mxfp8_col(x)
+        assert d.shape == shape
+    xb = torch.zeros((40, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(mxq.MxqError) as e:              # code rows narrower than K
+        mxq.mxq_mxfp4_to_mxfp8_col(xb, scale=torch.zeros((2, 63), dtype=torch.uint8, device=dev))
+    assert e.value.status == mxq.MXQ_ERR_SHAPE
+    with pytest.raises(mxq.MxqError) as e:
+        mxq.mxq_mxfp4_to_mxfp8_col(torch.zeros((40, 64), dtype=torch.float16, device=dev))
+    assert e.value.status == mxq.MXQ_ERR_DTYPE
+    buf = torch.zeros((40 * 64 + 64,), dtype=torch.uint8, device=dev)
+    with pytest.raises(mxq.MxqError) as e:              # column codes overlapping the column payload
+        mxq.mxq_mxfp4_to_mxfp8_col(xb, data=buf[:40 * 64].view(40, 64), scale=buf[40 * 64 - 64:].view(2, 64))
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
+    with pytest.raises(mxq.MxqError) as e:              # row payload overlapping the column payload
+        d = torch.zeros((40, 64), dtype=torch.uint8, device=dev)
+        mxq.mxq_mxfp4_to_mxfp8_row_col(xb, row_data=d, col_data=d)
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
+
+
+@pytest.mark.parametrize("variant", ["libmxq_fastmath.so", "libmxq_o1.so"])
+def test_col_build_variants_identical_bits(dev, variant):
+    for bits in (W.c2_exhaustive(natural=True), W.fp32_fuzz(1 << 16).reshape(-1, 128), W.c3_spread()[:256, :512]):
+        check_col(np.ascontiguousarray(bits), dev, lib=variant)
