@@ -91,6 +91,39 @@ def test_host_validation_without_a_gpu(lib):
     assert lib.mxq_dequantize(fake, P(0x200000), 2, 4, 64, 0, 0, P(0x300000), 64, mxq.MXQ_FP16, None) == mxq.MXQ_ERR_DTYPE
     assert lib.mxq_dequantize(fake, P(0x200000), 1, 4, 64, 0, 0, P(0x300000), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_SHAPE
     assert lib.mxq_dequantize(fake, P(0x200000), 1, 4, 64, 0, 1, P(0x100010), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_ALIAS
+    # dequantize, 32x1 column layout: code rows must span K
+    assert lib.mxq_dequantize(fake, P(0x200000), 63, 40, 64, 0, 2, P(0x300000), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_dequantize(fake, P(0x200000), 64, 40, 64, 0, 3, P(0x300000), 64, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_DTYPE
+    # columnwise: code rows narrower than K, overlaps, missing row outputs, fp16
+    assert lib.mxq_mxfp4_to_mxfp8_col(fake, 64, 40, 64, 0, P(0x200000), P(0x300000), 63, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_mxfp8_col(fake, 64, 40, 64, 0, P(0x200000), P(0x200000 + 40 * 64 - 1), 64, None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_mxfp4_to_mxfp8_col(fake, 64, 40, 64, 0, P(0x100010), P(0x300000), 64, None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_mxfp4_to_mxfp8_col(fake, 64, 40, 64, mxq.MXQ_FP16, P(0x200000), P(0x300000), 64, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_mxfp4_to_mxfp8_col(None, 64, 40, 64, 0, P(0x200000), P(0x300000), 64, None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_mxfp4_to_mxfp8_col(None, 64, 0, 64, 0, None, None, 64, None) == mxq.MXQ_OK
+    assert lib.mxq_mxfp4_to_mxfp8_row_col(fake, 64, 40, 64, 0, None, P(0x400000), 2, P(0x200000), P(0x300000), 64,
+                                          None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_mxfp4_to_mxfp8_row_col(fake, 64, 40, 64, 0, P(0x200000), P(0x400000), 2, P(0x200000),
+                                          P(0x300000), 64, None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_mxfp4_to_mxfp8_row_col(fake, 64, 40, 64, 0, P(0x500000), P(0x400000), 1, P(0x200000),
+                                          P(0x300000), 64, None) == mxq.MXQ_ERR_SHAPE
+    # packed MXFP4: narrow code storage, overlaps, odd shapes
+    assert lib.mxq_quantize_mxfp4(fake, 64, 4, 64, 0, P(0x200000), P(0x300000), 1, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_quantize_mxfp4(fake, 64, 4, 64, 0, P(0x200000), P(0x200010), 2, None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_dequantize_mxfp4(fake, P(0x200000), 1, 4, 64, P(0x300000), 64, 0, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_dequantize_mxfp4(fake, P(0x200000), 2, 4, 64, P(0x300000), 64, mxq.MXQ_FP16, None) == mxq.MXQ_ERR_DTYPE
+    assert lib.mxq_mxfp4_packed_to_mxfp8_row(fake, P(0x200000), 2, 4, 64, P(0x300000), P(0x300000), 2,
+                                             None) == mxq.MXQ_ERR_ALIAS
+    assert lib.mxq_mxfp4_packed_to_fp8_block128(fake, P(0x200000), 2, 4, 64, P(0x300000), P(0x400000), 0,
+                                                None) == mxq.MXQ_ERR_SHAPE
+    # shapes too large for the launch grid are refused, not truncated (buffers
+    # placed far apart so that no overlap is reported first)
+    huge, far = 1 << 40, lambda k: P(1 << k)
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, far(50), 64, huge, 64, 0, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, huge, 64, 0, far(50), far(52), 2, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_mxfp8_col(fake, 64, huge, 64, 0, far(50), far(52), 64, None) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_fp8_block128(fake, 1 << 10, huge, 1 << 10, 0, far(56), far(58), 8,
+                                         None) == mxq.MXQ_ERR_SHAPE
 
 
 def test_binding_raises_without_the_library(tmp_path, monkeypatch):
