@@ -52,7 +52,10 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_PACKED_STEPS 2
 #endif
 #ifndef MXQ_COL_THREADS
-#define MXQ_COL_THREADS 128   // columnwise: lanes per workgroup, one 16-byte chunk of columns each
+#define MXQ_COL_THREADS 64    // columnwise: column lanes per workgroup, one 16-byte chunk of columns each
+#endif
+#ifndef MXQ_COL_ROWS
+#define MXQ_COL_ROWS 4        // columnwise: rows of the 32-row band per lane (a divisor of 32)
 #endif
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
@@ -65,7 +68,8 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kThreads = 256;     // 4 waves per workgroup
-constexpr int kColThreads = MXQ_COL_THREADS;
+constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
+static_assert(kColRows * kColGroups == 32 && kColThreads % 64 == 0, "columnwise geometry");
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
               kPackedSteps = MXQ_PACKED_STEPS;
 
@@ -444,37 +448,35 @@ __device__ __forceinline__ uint32_t e4m3x4_each(uint32_t y01, uint32_t y23, floa
 }
 
 template <typename T, bool VEC, bool kRow>
-__global__ __launch_bounds__(kColThreads) void col_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K,
-                                                       uint8_t* __restrict__ cdata, uint8_t* __restrict__ cscale,
-                                                       int64_t cscale_ld, uint8_t* __restrict__ rdata,
-                                                       uint8_t* __restrict__ rscale, int64_t rscale_ld,
-                                                       uint32_t groups) {
+__global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
+    const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* __restrict__ cdata,
+    uint8_t* __restrict__ cscale, int64_t cscale_ld, uint8_t* __restrict__ rdata, uint8_t* __restrict__ rscale,
+    int64_t rscale_ld, uint32_t groups) {
   using G = StepGeom<T>;
   constexpr int EPL = Fmt<T>::kEPL, NW = sizeof(T) == 2 ? 4 : 2;   // elements, bf16 words per chunk
+  constexpr int R = kColRows;
+  __shared__ uint32_t s_cmax[kColGroups > 1 ? kColGroups : 1][NW][kColThreads];
   keep_denormals();
-  const uint32_t tid = threadIdx.x, band = blockIdx.x / groups, grp = blockIdx.x - band * groups;
-  const int64_t col0 = (int64_t)grp * (kColThreads * EPL) + (int64_t)tid * EPL, r0 = (int64_t)band * 32;
-  const int nr = (int)min((int64_t)32, rows - r0);
+  const uint32_t lane = threadIdx.x % kColThreads, rg = threadIdx.x / kColThreads;   // rg: uniform per wave
+  const uint32_t band = blockIdx.x / groups, grp = blockIdx.x - band * groups;
+  const int64_t col0 = (int64_t)grp * (kColThreads * EPL) + (int64_t)lane * EPL;
+  const int64_t rb = (int64_t)band * 32 + (int64_t)rg * R;   // this lane group's first row
   const bool in = col0 < K;
 
-  // Loads.  Rows past the band's end repeat its last row: never stored, and
-  // they cannot raise a column maximum.  VEC: no branch around a load, so each
+  // Loads.  Rows past the matrix's end repeat its last row (never stored, and
+  // they cannot raise a column maximum).  VEC: no branch around a load, so each
   // row is used as soon as it lands; a lane past K reads the row's last chunk
   // and takes no part in the block maxima.  Otherwise elements past K load as 0.
-  u32x4 w[32];
-  if constexpr (VEC) {
-    const T* px = x + r0 * ld_x + (in ? col0 : K - EPL);     // per lane
+  u32x4 w[R];
+  {
+    int64_t r = min(rb, rows - 1);
+    const T* px = x + r * ld_x;
+    if constexpr (VEC) px += in ? col0 : K - EPL;
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
-      w[i] = stream_load(reinterpret_cast<const u32x4*>(px));
-      px += i + 1 < nr ? ld_x : 0;
-    }
-  } else {
-    const T* px = x + r0 * ld_x;
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-      w[i] = load_chunk<T, false>(px, col0, K);
-      px += i + 1 < nr ? ld_x : 0;
+    for (int i = 0; i < R; i++) {
+      if constexpr (VEC) w[i] = stream_load(reinterpret_cast<const u32x4*>(px));
+      else w[i] = load_chunk<T, false>(px, col0, K);
+      if (r + 1 < rows) px += ld_x, r++;
     }
   }
 
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kColThreads) void col_kernel(const T* __restrict__ 
   for (int j = 0; j < NW; j++) cmax[j] = u16x2{0, 0};
   uint32_t poison = 0u;
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
+  for (int i = 0; i < R; i++) {
     uint32_t a = chunk_amax<T>(w[i]);
     if constexpr (VEC) a = in ? a : 0u;
     const Block b = block_of_amax<T>(block_max<Fmt<T>::kLPB>(a));
@@ -492,10 +494,10 @@ __global__ __launch_bounds__(kColThreads) void col_kernel(const T* __restrict__ 
     // a poisoned block's nibbles are zeroed: its y (unused) stays out of the maxima
     const Proj16<T> y = project<T>(b.poison ? 0u : fp4_of(w[i], s, T{}), s);
     if constexpr (kRow) {
-      if (i < nr) {
+      if (rb + i < rows) {
         const uint32_t code = row_code(b);
-        store_payload<T, VEC>(rdata + (r0 + i) * K, col0, K, payload_chunk<T>(y, code, b.poison));
-        if (tid % G::kLPB == 0 && in) rscale[(r0 + i) * rscale_ld + col0 / 32] = (uint8_t)code;
+        store_payload<T, VEC>(rdata + (rb + i) * K, col0, K, payload_chunk<T>(y, code, b.poison));
+        if (lane % G::kLPB == 0 && in) rscale[(rb + i) * rscale_ld + col0 / 32] = (uint8_t)code;
       }
     }
     poison |= (uint32_t)b.poison << i;
@@ -503,6 +505,18 @@ __global__ __launch_bounds__(kColThreads) void col_kernel(const T* __restrict__ 
     for (int j = 0; j < NW; j++) {
       w[i][j] = y.p[j];
       cmax[j] = __builtin_elementwise_max(cmax[j], __builtin_bit_cast(u16x2, y.p[j] & 0x7FFF7FFFu));
+    }
+  }
+  if constexpr (kColGroups > 1) {     // the band's column maxima over the lane groups
+#pragma unroll
+    for (int j = 0; j < NW; j++) s_cmax[rg][j][lane] = __builtin_bit_cast(uint32_t, cmax[j]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NW; j++) {
+      cmax[j] = u16x2{0, 0};
+#pragma unroll
+      for (int g = 0; g < kColGroups; g++)
+        cmax[j] = __builtin_elementwise_max(cmax[j], __builtin_bit_cast(u16x2, s_cmax[g][j][lane]));
     }
   }
 
@@ -515,15 +529,17 @@ __global__ __launch_bounds__(kColThreads) void col_kernel(const T* __restrict__ 
     codes[k] = E > 8u ? E - 8u : 0u;
     sc[k] = e8m0(codes[k]);
   }
-  uint8_t* crow = cscale + (int64_t)band * cscale_ld;
+  if (rg == 0) {
+    uint8_t* crow = cscale + (int64_t)band * cscale_ld;
 #pragma unroll
-  for (int k = 0; k < EPL; k++)
-    if (col0 + k < K) crow[col0 + k] = (uint8_t)codes[k];
+    for (int k = 0; k < EPL; k++)
+      if (col0 + k < K) crow[col0 + k] = (uint8_t)codes[k];
+  }
 
-  uint8_t* pd = cdata + r0 * K;
+  uint8_t* pd = cdata + rb * K;
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
-    if (i < nr) {
+  for (int i = 0; i < R; i++) {
+    if (rb + i < rows) {
       typename PayloadChunk<T>::type q;
       if constexpr (sizeof(T) == 2) {
         q = u32x2{e4m3x4_each(w[i][0], w[i][1], sc[0], sc[1], sc[2], sc[3]),
@@ -1173,7 +1189,7 @@ int launch_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* cd
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(cdata, EPL) &&
                    (rdata == nullptr || aligned(rdata, EPL));
-  const dim3 grid((uint32_t)(bands * groups)), block(kColThreads);
+  const dim3 grid((uint32_t)(bands * groups)), block(kColThreads * kColGroups);
 #define MXQ_COL_LAUNCH(V, R)                                                                                    \
   hipLaunchKernelGGL((col_kernel<T, V, R>), grid, block, 0, s, (const T*)x, ld_x, rows, K, cdata, cscale, cscale_ld, \
                      rdata, rscale, rscale_ld, (uint32_t)groups)
