@@ -138,7 +138,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
-              "(rows shard with no communication; see DESIGN.md).", file=sys.stderr)
+              "(whole rows shard with no communication, so each GPU would run this kernel on its share).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
