@@ -15,7 +15,10 @@ Infinity Cache cannot serve repeated reads).  The K timed passes run
 kernel-major (each kernel K times back to back, then the next), which is the
 same work as K step-major passes; `value` is the steps' algorithmic bytes over
 their wall time, and per-kernel times come from HIP events recorded around each
-kernel's burst on the stream the kernels are launched on.
+kernel's burst on the stream the kernels are launched on: "us" is the burst's
+mean per launch, "us_median" / "us_min" the median / minimum over its
+sub-bursts of 5 launches.  Kernels outside the step (the fused passes, packed
+MXFP4, columnwise) are timed the same way after the step's timed region.
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--calibrate]
 """
@@ -26,6 +29,7 @@ import hashlib
 import json
 import os
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +39,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROWS = COLS = 8192
 SCALE_LD = 260                   # padded scale storage: ceil(K/32) = 256 plus 4 columns
 NSETS = 6
+SUB = 5          # launches per sub-burst (median / min statistics)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_bf16.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "microscaling_weight_quantization_amd", "csrc", "mxq.hip")
 
@@ -136,6 +141,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
               "(whole rows shard with no communication, so each GPU would run this kernel on its share).",
@@ -223,15 +230,19 @@ def main():
     bursts = {}
 
     def run(i0: int, k: int, timed: bool, which=names):
+        # A timed burst also records an event after every SUB launches: the
+        # sub-burst averages give the median and minimum next to the mean.
         for n in which:
-            if timed:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-            for i in range(i0, i0 + k):
+            evs = []
+            for j, i in enumerate(range(i0, i0 + k)):
+                if timed and j % SUB == 0:
+                    evs.append(torch.cuda.Event(enable_timing=True))
+                    evs[-1].record(stream)
                 launches[n](sets[(i + offset[n]) % NSETS])
             if timed:
-                b.record(stream)
-                bursts[n] = (a, b)
+                evs.append(torch.cuda.Event(enable_timing=True))
+                evs[-1].record(stream)
+                bursts[n] = evs
 
     run(0, args.warmup, False)
     torch.cuda.synchronize()
@@ -254,19 +265,28 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     total = sum(nbytes.values())
     kernels = {}
+    def burst_stats(n):
+        """Mean over the whole burst, and median / min of the sub-burst means (us)."""
+        evs = bursts[n]
+        mean = 1e3 * evs[0].elapsed_time(evs[-1]) / args.steps
+        subs = []
+        for j in range(len(evs) - 1):
+            cnt = min(SUB, args.steps - j * SUB)
+            subs.append(1e3 * evs[j].elapsed_time(evs[j + 1]) / cnt)
+        return mean, statistics.median(subs), min(subs)
+
     for n in names:
-        a, b = bursts[n]
-        us = 1e3 * a.elapsed_time(b) / args.steps
+        us, med, lo = burst_stats(n)
         gbs = nbytes[n] / (us * 1e-6) / 1e9
-        kernels[n] = {"us": round(us, 2), "bytes": nbytes[n], "GB/s": round(gbs, 1),
-                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        kernels[n] = {"us": round(us, 2), "us_median": round(med, 2), "us_min": round(lo, 2), "bytes": nbytes[n],
+                      "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     extra = {}
     extra_bytes = dict(packed_bytes(rows, K), fused=fused_bytes(rows, K), **col_bytes(rows, K))
     for n in extra_names:
-        a, b = bursts[n]
-        us = 1e3 * a.elapsed_time(b) / args.steps
+        us, med, lo = burst_stats(n)
         gbs = extra_bytes[n] / (us * 1e-6) / 1e9
-        extra["fused_proj_row" if n == "fused" else n] = {"us": round(us, 2), "bytes": extra_bytes[n],
+        extra["fused_proj_row" if n == "fused" else n] = {"us": round(us, 2), "us_median": round(med, 2),
+                                                          "us_min": round(lo, 2), "bytes": extra_bytes[n],
                                                           "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     extra["fused_proj_row"]["vs_separate_us"] = round(kernels["proj"]["us"] + kernels["row"]["us"], 2)
     extra["row_col"]["vs_separate_us"] = round(kernels["row"]["us"] + extra["col"]["us"], 2)
