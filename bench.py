@@ -16,9 +16,10 @@ kernel-major (each kernel K times back to back, then the next), which is the
 same work as K step-major passes; `value` is the steps' algorithmic bytes over
 their wall time, and per-kernel times come from HIP events recorded around each
 kernel's burst on the stream the kernels are launched on: "us" is the burst's
-mean per launch, "us_median" / "us_min" the median / minimum over its
-sub-bursts of 5 launches.  Kernels outside the step (the fused passes, packed
-MXFP4, columnwise) are timed the same way after the step's timed region.
+mean per launch.  After the timed region a separate pass gives "us_median" /
+"us_min", the median / minimum over 5 sub-bursts of 5 launches.  Kernels
+outside the step (the fused passes, packed MXFP4, columnwise) are timed the
+same way after the step's timed region.
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--calibrate]
 """
@@ -39,7 +40,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROWS = COLS = 8192
 SCALE_LD = 260                   # padded scale storage: ceil(K/32) = 256 plus 4 columns
 NSETS = 6
-SUB = 5          # launches per sub-burst (median / min statistics)
+SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_bf16.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "microscaling_weight_quantization_amd", "csrc", "mxq.hip")
 
@@ -229,20 +230,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     bursts = {}
 
-    def run(i0: int, k: int, timed: bool, which=names):
-        # A timed burst also records an event after every SUB launches: the
-        # sub-burst averages give the median and minimum next to the mean.
+    def run(i0: int, k: int, timed: bool, which=names, sub: int = 0, store=None):
+        # timed: events around each kernel's burst; with sub > 0 also after
+        # every `sub` launches (the spread statistics, outside the timed region)
+        store = bursts if store is None else store
         for n in which:
             evs = []
             for j, i in enumerate(range(i0, i0 + k)):
-                if timed and j % SUB == 0:
+                if timed and (j == 0 or (sub and j % sub == 0)):
                     evs.append(torch.cuda.Event(enable_timing=True))
                     evs[-1].record(stream)
                 launches[n](sets[(i + offset[n]) % NSETS])
             if timed:
                 evs.append(torch.cuda.Event(enable_timing=True))
                 evs[-1].record(stream)
-                bursts[n] = evs
+                store[n] = evs
 
     run(0, args.warmup, False)
     torch.cuda.synchronize()
@@ -252,6 +254,10 @@ def main():
     wall = time.perf_counter() - t0
     run(0, args.warmup, False, extra_names)
     run(args.warmup, args.steps, True, extra_names)
+    torch.cuda.synchronize()
+    # spread of the per-launch time: SPREAD_BURSTS sub-bursts of SUB launches each
+    spread = {}
+    run(0, SUB * SPREAD_BURSTS, True, names + extra_names, sub=SUB, store=spread)
     torch.cuda.synchronize()
 
     if args.calibrate:
@@ -266,13 +272,12 @@ def main():
     total = sum(nbytes.values())
     kernels = {}
     def burst_stats(n):
-        """Mean over the whole burst, and median / min of the sub-burst means (us)."""
-        evs = bursts[n]
-        mean = 1e3 * evs[0].elapsed_time(evs[-1]) / args.steps
-        subs = []
-        for j in range(len(evs) - 1):
-            cnt = min(SUB, args.steps - j * SUB)
-            subs.append(1e3 * evs[j].elapsed_time(evs[j + 1]) / cnt)
+        """Mean per launch over the timed burst, and median / min of the
+        spread pass's sub-burst means (us)."""
+        a, b = bursts[n]
+        mean = 1e3 * a.elapsed_time(b) / args.steps
+        evs = spread[n]
+        subs = [1e3 * evs[j].elapsed_time(evs[j + 1]) / SUB for j in range(len(evs) - 1)]
         return mean, statistics.median(subs), min(subs)
 
     for n in names:
