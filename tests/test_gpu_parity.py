@@ -434,3 +434,26 @@ def test_build_variants_identical_bits(dev, variant):
     same bits (the pages rebuild with fast math and compare)."""
     for bits in (W.c2_exhaustive(), W.c2_planted(), W.fp32_fuzz(1 << 16).reshape(-1, 128), W.c3_spread()[:256, :512]):
         check_all(np.ascontiguousarray(bits), dev, lib=variant)
+
+
+def test_row_longer_than_2gb(dev):
+    """Maximum-size edge: one bf16 row of 2^30 + 48 elements (2 GB + 96 bytes,
+    beyond the 32-bit byte offsets of the vectorised projection store), so the
+    projection and the row lift take their element-wise paths.  Compared on
+    sampled blocks: the start, the blocks around the 2^30-element (2^31-byte)
+    mark, and the partial last block."""
+    K = (1 << 30) + 48
+    pat = W.c2_exhaustive().reshape(-1)
+    bits = np.resize(pat, K).reshape(1, K)
+    x = to_dev(bits, dev)
+    y = mxq.mxq_fake_quantize_mxfp4(x)
+    data, scale = mxq.mxq_mxfp4_to_mxfp8_row(x)
+    torch.cuda.synchronize()
+    for c0, c1 in ((0, 4096), ((1 << 30) - 2048, (1 << 30) + 2048), (K - 4096 - 16, K)):
+        sub = np.ascontiguousarray(bits[:, c0:c1])
+        assert_bits(to_host(y[:, c0:c1]), oracle.fake_quantize_mxfp4(sub), f"projection [{c0}, {c1})")
+        wd, ws = oracle.mxfp4_to_mxfp8_row(sub)
+        assert_bits(to_host(data[:, c0:c1]), wd, f"row payload [{c0}, {c1})")
+        assert_bits(to_host(scale[:, c0 // 32:(c1 + 31) // 32]), ws, f"row codes [{c0}, {c1})")
+    del x, y, data, scale
+    torch.cuda.empty_cache()
