@@ -51,6 +51,9 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_PACKED_STEPS
 #define MXQ_PACKED_STEPS 2
 #endif
+#ifndef MXQ_PFOLD_ROWS
+#define MXQ_PFOLD_ROWS 16     // fold from packed MXFP4: band rows per lane (16, 8 or 4)
+#endif
 #ifndef MXQ_COL_THREADS
 #define MXQ_COL_THREADS 64    // columnwise: column lanes per workgroup, one 16-byte chunk of columns each
 #endif
@@ -68,6 +71,8 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kThreads = 256;     // 4 waves per workgroup
+constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
+static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
 static_assert(kColRows * kColGroups == 32 && kColThreads % 64 == 0, "columnwise geometry");
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
@@ -984,12 +989,10 @@ __device__ __forceinline__ u32x2 e4m3x8_of_fp4(uint32_t f, int ds) {
   return u32x2{e4m3x4(bf16_pair<0>(f, sd), bf16_pair<1>(f, sd), se), e4m3x4(bf16_pair<2>(f, sd), bf16_pair<3>(f, sd), se)};
 }
 
-// Payload from packed MXFP4: each lane takes 16 elements (8 packed bytes in, 16
-// payload bytes out), so a block of 32 spans two lanes.  A step is 4096 elements
-// of one row.  With kTile the E8M0 code of the element's 128x128 tile (already
-// written by tile_codes_kernel) sets the fold; otherwise it is the fixed-shift-6
-// row lift of each block.
-template <bool VEC, bool kTile>
+// MXFP8 row lift from packed MXFP4: each lane takes 16 elements (8 packed bytes
+// in, 16 payload bytes out), so a block of 32 spans two lanes; even lanes write
+// the block's code.  A step is 4096 elements of one row.
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t* __restrict__ packed,
                                                                   const uint8_t* __restrict__ scale,
                                                                   int64_t scale_ld, int64_t K,
@@ -1001,12 +1004,11 @@ __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t*
   const int64_t lane_col = (int64_t)tid * 16, pw = (K + 1) / 2;
   // All of the workgroup's loads are issued before any conversion or store.
   u32x2 f[kPackedSteps];
-  uint32_t c[kPackedSteps], tcode[kPackedSteps];
+  uint32_t c[kPackedSteps];
 #pragma unroll
   for (int u = 0; u < kPackedSteps; u++) {
     f[u] = u32x2{0u, 0u};
     c[u] = 0u;
-    tcode[u] = 0u;
     const uint32_t step = blockIdx.x * kPackedSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
@@ -1020,7 +1022,6 @@ __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t*
         if (col0 + i < K) f[u][i / 8] |= (uint32_t)prow[(col0 + i) / 2] << (4 * (i % 8));
     }
     c[u] = scale[(int64_t)row * scale_ld + col0 / 32];
-    if constexpr (kTile) tcode[u] = code_out[(int64_t)(row / 128) * code_ld + col0 / 128];
   }
 #pragma unroll
   for (int u = 0; u < kPackedSteps; u++) {
@@ -1035,13 +1036,8 @@ __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t*
       q = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
       code = 255u;
     } else {
-      int ds;
-      if constexpr (kTile) {
-        ds = (int)c[u] - (int)tcode[u];                        // e - S <= 6
-      } else {
-        code = c[u] > 6u ? c[u] - 6u : 0u;                     // S = max(e - 6, -127)
-        ds = (int)min(c[u], 6u);
-      }
+      code = c[u] > 6u ? c[u] - 6u : 0u;                       // S = max(e - 6, -127)
+      const int ds = (int)min(c[u], 6u);
       const u32x2 lo = e4m3x8_of_fp4(f[u][0], ds), hi = e4m3x8_of_fp4(f[u][1], ds);
       q = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
@@ -1052,66 +1048,115 @@ __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t*
       for (int i = 0; i < 16; i++)
         if (col0 + i < K) drow[col0 + i] = (uint8_t)(q[i / 4] >> (8 * (i % 4)));
     }
-    if constexpr (!kTile) {
-      if (tid % 2 == 0) code_out[(int64_t)row * code_ld + col0 / 32] = (uint8_t)code;
-    }
+    if (tid % 2 == 0) code_out[(int64_t)row * code_ld + col0 / 32] = (uint8_t)code;
   }
 }
 
-// Tile codes from the packed weight's block codes alone.  A 256-thread
-// workgroup covers one 128-row band and 16 tile columns (64 codes of each row):
-// thread t reads the 16-code chunk t & 3 (four tile columns) of band rows t >> 2
-// and (t >> 2) + 64, so each group of four lanes reads 64 consecutive code bytes
-// of one row.  Lanes with the same chunk meet by shuffles, the four waves in LDS.
-// M = the largest finite code (1, i.e. e = -126, if none); tile code max(M - 6, 0).
+// 128x128 fold from packed MXFP4 in one pass.  A workgroup of 4096 / R lanes
+// (R = MXQ_PFOLD_ROWS) takes one 128-row band and four tile columns (512
+// elements of each band row):
+//  1. Lane t reads 8 block codes (two tiles' worth) of band row t / 2 into LDS
+//     and keeps each tile's largest finite code; lanes of the same parity meet
+//     by shuffles, the four waves in LDS.  M = that code (1, i.e. e = -126, if
+//     the tile has none); tile code max(M - 6, 0), i.e. S = max(M - 6, -127).
+//  2. Lane t converts 16 elements (8 packed bytes -> 16 payload bytes) of R
+//     band rows, t / 32 + (128 / R) k, at the shift e - S of its block and
+//     tile; all R loads are issued first.  Poisoned blocks (code 255) get 0x7F.
 template <bool VEC>
-__global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                         int64_t rows, int64_t nb, uint8_t* __restrict__ tile_code,
-                                                         int64_t tile_ld, int64_t tiles_per_row) {
-  __shared__ uint32_t s_max[4][16];
-  const uint32_t tid = threadIdx.x, c = tid & 3u;
-  const int64_t j0 = ((int64_t)blockIdx.x * 4 + c) * 16, tr = blockIdx.y;
-  uint32_t m[4] = {1u, 1u, 1u, 1u};
-#pragma unroll
-  for (int h = 0; h < 2; h++) {
-    const int64_t r = tr * 128 + (tid >> 2) + 64 * h;
-    if (r < rows && j0 < nb) {
-      const uint8_t* src = scale + r * scale_ld + j0;
-      uint32_t w[4];
-      if (VEC && j0 + 16 <= nb) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
+__global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_t* __restrict__ packed,
+                                                          const uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                          int64_t rows, int64_t K, uint8_t* __restrict__ data,
+                                                          uint8_t* __restrict__ tile_code, int64_t tile_ld,
+                                                          uint32_t groups, bool codes_vec) {
+  __shared__ uint32_t s_codes[128][4];   // the band rows' 16 block codes
+  __shared__ uint32_t s_max[4][4];       // wave x tile
+  keep_denormals();
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t tr = blockIdx.x / groups, tg = blockIdx.x - tr * groups;
+  const int64_t r0 = (int64_t)tr * 128, nb = (K + 31) / 32, pw = (K + 1) / 2, ntc = (K + 127) / 128;
+
+  if (tid < 256u) {  // 1. block codes and tile codes (the first four waves)
+    const uint32_t rl = tid >> 1, h = tid & 1u;
+    const int64_t r = r0 + rl, j = (int64_t)tg * 16 + 8 * h;
+    uint32_t w[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};              // 255: no finite code
+    if (r < rows) {
+      const uint8_t* src = scale + r * scale_ld + j;
+      if (codes_vec && j + 8 <= nb) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+        w[0] = v[0], w[1] = v[1];
       } else {
+        for (int k = 0; k < 8; k++)
+          if (j + k < nb) w[k / 4] = (w[k / 4] & ~(0xFFu << (8 * (k % 4)))) | ((uint32_t)src[k] << (8 * (k % 4)));
+      }
+    }
+    s_codes[rl][2 * h] = w[0];
+    s_codes[rl][2 * h + 1] = w[1];
+    uint32_t m[2] = {1u, 1u};
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-          w[t] = 0u;
+    for (int t = 0; t < 2; t++)
 #pragma unroll
-          for (int k = 0; k < 4; k++)
-            if (j0 + 4 * t + k < nb) w[t] |= (uint32_t)src[4 * t + k] << (8 * k);
-        }
+      for (int k = 0; k < 4; k++) {
+        const uint32_t c = (w[t] >> (8 * k)) & 0xFFu;
+        if (c != 255u) m[t] = max(m[t], c);
       }
 #pragma unroll
-      for (int t = 0; t < 4; t++)
+    for (int t = 0; t < 2; t++)
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-          const uint32_t code = (w[t] >> (8 * k)) & 0xFFu;
-          if (code != 255u) m[t] = max(m[t], code);
-        }
+      for (int off = 2; off < 64; off <<= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], off));
+    if (lane < 2u) s_max[wave][2 * lane] = m[0], s_max[wave][2 * lane + 1] = m[1];
+  }
+  __syncthreads();
+  uint32_t tcode[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint32_t M = max(max(s_max[0][t], s_max[1][t]), max(s_max[2][t], s_max[3][t]));
+    tcode[t] = M > 6u ? M - 6u : 0u;
+  }
+  if (tid < 4u && (int64_t)tg * 4 + tid < ntc)
+    tile_code[(int64_t)tr * tile_ld + tg * 4 + tid] =
+        (uint8_t)(tid == 0 ? tcode[0] : tid == 1 ? tcode[1] : tid == 2 ? tcode[2] : tcode[3]);
+
+  // 2. payload
+  constexpr int RG = 128 / kPFoldRows;                       // row groups
+  const uint32_t cc = tid & 31u, rg = tid >> 5;             // 16-element column chunk, row group
+  const int64_t col0 = (int64_t)tg * 512 + cc * 16;
+  const uint32_t tt = cc >> 3;                               // tile within the group
+  const uint32_t ts = tt == 0 ? tcode[0] : tt == 1 ? tcode[1] : tt == 2 ? tcode[2] : tcode[3];
+  u32x2 f[kPFoldRows];
+#pragma unroll
+  for (int k = 0; k < kPFoldRows; k++) {
+    f[k] = u32x2{0u, 0u};
+    const int64_t r = r0 + rg + RG * k;
+    if (r < rows && col0 < K) {
+      const uint8_t* prow = packed + r * pw;
+      if (VEC) {
+        f[k] = stream_load(reinterpret_cast<const u32x2*>(prow + col0 / 2));
+      } else {
+        for (int i = 0; i < 16; i += 2)
+          if (col0 + i < K) f[k][i / 8] |= (uint32_t)prow[(col0 + i) / 2] << (4 * (i % 8));
+      }
     }
   }
 #pragma unroll
-  for (int t = 0; t < 4; t++)
-#pragma unroll
-    for (int off = 4; off < 64; off <<= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], off));
-  if ((tid & 63u) < 4u)
-#pragma unroll
-    for (int t = 0; t < 4; t++) s_max[tid >> 6][c * 4 + t] = m[t];
-  __syncthreads();
-  if (tid < 16u) {
-    const int64_t tc = (int64_t)blockIdx.x * 16 + tid;
-    if (tc < tiles_per_row) {
-      const uint32_t mm = max(max(s_max[0][tid], s_max[1][tid]), max(s_max[2][tid], s_max[3][tid]));
-      tile_code[tr * tile_ld + tc] = (uint8_t)(mm > 6u ? mm - 6u : 0u);
+  for (int k = 0; k < kPFoldRows; k++) {
+    const int64_t r = r0 + rg + RG * k;
+    if (r < rows && col0 < K) {
+      const uint32_t c = (s_codes[rg + RG * k][cc >> 3] >> (8 * ((cc >> 1) & 3u))) & 0xFFu;
+      u32x4 q;
+      if (c == 255u) {
+        q = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      } else {
+        const int ds = (int)c - (int)ts;                       // e - S <= 6
+        const u32x2 lo = e4m3x8_of_fp4(f[k][0], ds), hi = e4m3x8_of_fp4(f[k][1], ds);
+        q = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+      uint8_t* drow = data + r * K;
+      if (VEC) {
+        stream_store(q, reinterpret_cast<u32x4*>(drow + col0));
+      } else {
+        for (int i = 0; i < 16; i++)
+          if (col0 + i < K) drow[col0 + i] = (uint8_t)(q[i / 4] >> (8 * (i % 4)));
+      }
     }
   }
 }
@@ -1545,10 +1590,10 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
   const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
   const dim3 grid(grid_for(total, kPackedSteps)), block(kThreads);
   if (vec)
-    hipLaunchKernelGGL((packed_convert_kernel<true, false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+    hipLaunchKernelGGL((packed_convert_kernel<true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
                        scale_out, scale_out_ld, spr, total);
   else
-    hipLaunchKernelGGL((packed_convert_kernel<false, false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+    hipLaunchKernelGGL((packed_convert_kernel<false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
                        scale_out, scale_out_ld, spr, total);
   return launch_status();
 }
@@ -1565,25 +1610,17 @@ int mxq_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale
               rd = matrix_range(data, rows, K, K, 1), rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(rt, rp) || overlap(rt, rs) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
   if (ntc * ntr >= kMaxSteps) return MXQ_ERR_SHAPE;
-  if (ntr > 65535) return MXQ_ERR_SHAPE;
-  const dim3 tgrid((uint32_t)((nb + 63) / 64), (uint32_t)ntr);
-  if (aligned(scale, 16) && scale_ld % 16 == 0)
-    hipLaunchKernelGGL((tile_codes_kernel<true>), tgrid, dim3(256), 0, stream, scale, scale_ld, rows, nb, tile_code,
-                       tile_ld, ntc);
-  else
-    hipLaunchKernelGGL((tile_codes_kernel<false>), tgrid, dim3(256), 0, stream, scale, scale_ld, rows, nb, tile_code,
-                       tile_ld, ntc);
-  if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
-  uint32_t spr, total;
-  if (steps_for(rows, K, 4096, &spr, &total)) return MXQ_ERR_SHAPE;
+  const int64_t groups = (ntc + 3) / 4;
+  if (ntr * groups >= kMaxSteps) return MXQ_ERR_SHAPE;
   const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
-  const dim3 grid(grid_for(total, kPackedSteps)), block(kThreads);
+  const bool codes_vec = aligned(scale, 8) && scale_ld % 8 == 0;
+  const dim3 grid((uint32_t)(ntr * groups)), block(kPFoldThreads);
   if (vec)
-    hipLaunchKernelGGL((packed_convert_kernel<true, true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
-                       tile_code, tile_ld, spr, total);
+    hipLaunchKernelGGL((packed_fold_kernel<true>), grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
+                       tile_code, tile_ld, (uint32_t)groups, codes_vec);
   else
-    hipLaunchKernelGGL((packed_convert_kernel<false, true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
-                       tile_code, tile_ld, spr, total);
+    hipLaunchKernelGGL((packed_fold_kernel<false>), grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
+                       tile_code, tile_ld, (uint32_t)groups, codes_vec);
   return launch_status();
 }
 
