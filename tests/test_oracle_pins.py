@@ -698,3 +698,30 @@ def test_col_pins_catch_planted_mistakes(mutation, changes):
     d1, s1 = F.col_lift(x, "bf16", mutation=mutation)
     same = np.array_equal(d0, d1) and np.array_equal(s0, s1)
     assert same != changes
+
+
+def test_oracle_matches_brute_force_at_every_block_exponent():
+    """Oracle vs the Fraction brute force with the block exponent swept over the
+    whole clamp range: for every e in [-126, 125], two blocks anchored by
+    +-6 * 2^e whose other 31 elements are random bf16 patterns of magnitude at
+    most 6 * 2^e (so e is the block's scale exponent), including the grid
+    midpoints and subnormals that fall under it."""
+    g = np.random.default_rng(11)
+    pool = np.arange(0x7F80, dtype=np.uint16)                     # finite magnitudes
+    mags = (pool.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rows = []
+    for e in range(-126, 126):
+        cap = np.ldexp(6.0, e)
+        sel = pool[mags <= cap]
+        for sign in (0, 0x8000):
+            blk = g.choice(sel, 31) | (g.integers(0, 2, 31).astype(np.uint16) << 15)
+            rows.append(np.concatenate([[W.bf16_bits_of(cap) | sign], blk]).astype(np.uint16))
+    x = np.ascontiguousarray(np.stack(rows))
+    assert np.array_equal(oracle.fake_quantize_mxfp4(x), F.fake_quantize(x, "bf16"))
+    d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+    d1, s1 = F.row_lift(x, "bf16")
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+    assert np.array_equal(oracle.dequantize(d0, s0), F.dequantize(d1, s1, "row", "bf16"))
+    dc0, sc0 = oracle.mxfp4_to_mxfp8_col(x)
+    dc1, sc1 = F.col_lift(x, "bf16")
+    assert np.array_equal(dc0, dc1) and np.array_equal(sc0, sc1)
