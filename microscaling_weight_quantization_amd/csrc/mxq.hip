@@ -71,6 +71,21 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kThreads = 256;     // 4 waves per workgroup
+#ifndef MXQ_PROJ_THREADS
+#define MXQ_PROJ_THREADS 64    // projection: lanes per workgroup (one wave)
+#endif
+constexpr int kProjThreads = MXQ_PROJ_THREADS;
+#ifndef MXQ_ROW_THREADS
+#define MXQ_ROW_THREADS 256    // row lift (and fused projection + row lift), MXFP4 encode: lanes per workgroup
+#endif
+#ifndef MXQ_DEQUANT_THREADS
+#define MXQ_DEQUANT_THREADS 64   // FP8 and MXFP4 decodes: lanes per workgroup (8 elements each)
+#endif
+#ifndef MXQ_PACKED_THREADS
+#define MXQ_PACKED_THREADS 256   // row lift from packed MXFP4: lanes per workgroup (16 elements each)
+#endif
+constexpr int kRowThreads = MXQ_ROW_THREADS, kDequantThreads = MXQ_DEQUANT_THREADS,
+              kPackedThreads = MXQ_PACKED_THREADS;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
 static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
@@ -356,23 +371,23 @@ __device__ __forceinline__ void store_payload(uint8_t* __restrict__ row, int64_t
 }
 
 // ------------------------------------------------------------------------------------
-// Streaming kernels: projection and row lift.  A "step" is 256 lanes x one
-// 16-byte chunk = 2048 bf16 / 1024 fp32 elements of ONE row (64 / 32 blocks);
-// rows are padded to whole steps, so the row / segment split is per-step
-// uniform (scalar) arithmetic and a block never straddles two rows.
+// Streaming kernels: projection and row lift.  A "step" is the workgroup's
+// lanes x one 16-byte chunk (8 bf16 / 4 fp32 elements each) of ONE row; rows
+// are padded to whole steps, so the row / segment split is per-step uniform
+// (scalar) arithmetic and a block never straddles two rows.
 // ------------------------------------------------------------------------------------
-template <typename T>
+template <typename T, int TPB = kThreads>
 struct StepGeom {
   static constexpr int kEPL = Fmt<T>::kEPL, kLPB = Fmt<T>::kLPB;
-  static constexpr int kBlocksPerStep = kThreads / kLPB;
+  static constexpr int kBlocksPerStep = TPB / kLPB;
   static constexpr int64_t kElemsPerStep = (int64_t)kBlocksPerStep * 32;
 };
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void proj_kernel(const T* __restrict__ x, int64_t ld_x, T* __restrict__ y,
-                                                        int64_t ld_y, int64_t K, uint32_t steps_per_row,
-                                                        uint32_t total_steps) {
-  using G = StepGeom<T>;
+__global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict__ x, int64_t ld_x, T* __restrict__ y,
+                                                            int64_t ld_y, int64_t K, uint32_t steps_per_row,
+                                                            uint32_t total_steps) {
+  using G = StepGeom<T, kProjThreads>;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
@@ -409,12 +424,12 @@ __device__ __forceinline__ bool skipped(const int32_t* __restrict__ noop) {
 
 // Row lift; with kProj it also writes the projection y (the fused one-pass form).
 template <typename T, bool VEC, bool kProj>
-__global__ __launch_bounds__(kThreads) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+__global__ __launch_bounds__(kRowThreads) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                        uint8_t* __restrict__ data, uint8_t* __restrict__ scale,
                                                        int64_t scale_ld, T* __restrict__ y, int64_t ld_y,
                                                        uint32_t steps_per_row, uint32_t total_steps,
                                                        const int32_t* __restrict__ noop) {
-  using G = StepGeom<T>;
+  using G = StepGeom<T, kRowThreads>;
   if (skipped(noop)) return;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
@@ -739,11 +754,11 @@ __device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8])
 }
 
 template <typename TO, bool kE5M2, int kLay, bool VEC>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ data,
+__global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
                                                            uint32_t steps_per_row, uint32_t total_steps) {
-  // 8 payload bytes per lane per step; 64 x 1x32 blocks per step.
+  // 8 payload bytes per lane per step; a step is kDequantThreads * 8 elements of one row.
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 8;
@@ -759,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* drow = data + (int64_t)row * K;
     if (VEC) {
@@ -786,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const u32x2 q = qs[u];
     float s8[8];
@@ -850,11 +865,11 @@ template <>
 struct Nibbles<uint32_t> { typedef uint16_t type; };   // 4 nibbles per fp32 chunk
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+__global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                                   uint8_t* __restrict__ packed,
                                                                   uint8_t* __restrict__ scale, int64_t scale_ld,
                                                                   uint32_t steps_per_row, uint32_t total_steps) {
-  using G = StepGeom<T>;
+  using G = StepGeom<T, kRowThreads>;
   using N = typename Nibbles<T>::type;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
@@ -918,7 +933,7 @@ __device__ __forceinline__ u32x4 decode8_fp4(uint32_t f, uint32_t c) {
 }
 
 template <typename TO, bool VEC>
-__global__ __launch_bounds__(kThreads) void dequantize_mxfp4_kernel(const uint8_t* __restrict__ packed,
+__global__ __launch_bounds__(kDequantThreads) void dequantize_mxfp4_kernel(const uint8_t* __restrict__ packed,
                                                                     const uint8_t* __restrict__ scale,
                                                                     int64_t scale_ld, int64_t K,
                                                                     TO* __restrict__ out, int64_t ld_out,
@@ -935,7 +950,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_mxfp4_kernel(const uint8_
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
     if (VEC) {
@@ -951,7 +966,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_mxfp4_kernel(const uint8_
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 2048 + lane_col;
+    const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const u32x4 o = decode8_fp4(fs[u], cs[u]);
     TO* orow = out + (int64_t)row * ld_out;
@@ -991,9 +1006,9 @@ __device__ __forceinline__ u32x2 e4m3x8_of_fp4(uint32_t f, int ds) {
 
 // MXFP8 row lift from packed MXFP4: each lane takes 16 elements (8 packed bytes
 // in, 16 payload bytes out), so a block of 32 spans two lanes; even lanes write
-// the block's code.  A step is 4096 elements of one row.
+// the block's code.  A step is kPackedThreads * 16 elements of one row.
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t* __restrict__ packed,
+__global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const uint8_t* __restrict__ packed,
                                                                   const uint8_t* __restrict__ scale,
                                                                   int64_t scale_ld, int64_t K,
                                                                   uint8_t* __restrict__ data,
@@ -1012,7 +1027,7 @@ __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t*
     const uint32_t step = blockIdx.x * kPackedSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 4096 + lane_col;
+    const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
     if (VEC) {
@@ -1028,7 +1043,7 @@ __global__ __launch_bounds__(kThreads) void packed_convert_kernel(const uint8_t*
     const uint32_t step = blockIdx.x * kPackedSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * 4096 + lane_col;
+    const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
     if (col0 >= K) continue;
     u32x4 q;
     uint32_t code = 0u;
@@ -1218,11 +1233,11 @@ size_t dtype_size(mxq_dtype dt) { return dt == MXQ_BF16 ? 2 : 4; }
 template <typename T>
 int launch_proj(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows, int64_t K, hipStream_t s) {
   uint32_t spr, total;
-  if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, StepGeom<T, kProjThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && aligned(y, 16) && ld_x % EPL == 0 && ld_y % EPL == 0 && K % EPL == 0 &&
                    fits32(K * (int64_t)sizeof(T));
-  const dim3 grid(grid_for(total, kProjSteps)), block(kThreads);
+  const dim3 grid(grid_for(total, kProjSteps)), block(kProjThreads);
   if (vec)
     hipLaunchKernelGGL((proj_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, (T*)y, ld_y, K, spr, total);
   else
@@ -1234,11 +1249,11 @@ template <typename T>
 int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* data, uint8_t* scale,
                int64_t scale_ld, void* y, int64_t ld_y, const int32_t* noop, hipStream_t s) {
   uint32_t spr, total;
-  if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
                    (y == nullptr || (aligned(y, 16) && ld_y % EPL == 0));
-  const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
+  const dim3 grid(grid_for(total, kRowSteps)), block(kRowThreads);
 #define MXQ_ROW_LAUNCH(V, P)                                                                                  \
   hipLaunchKernelGGL((row_kernel<T, V, P>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \
                      (T*)y, ld_y, spr, total, noop)
@@ -1295,11 +1310,11 @@ template <typename TO, bool kE5M2, int kLay>
 int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K, void* out,
                      int64_t ld_out, hipStream_t s) {
   uint32_t spr, total;
-  if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
   const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0 &&
                    (kLay != kLayCol || (aligned(scale, 8) && scale_ld % 8 == 0));
-  const dim3 grid(grid_for(total, kDequantSteps)), block(kThreads);
+  const dim3 grid(grid_for(total, kDequantSteps)), block(kDequantThreads);
   if (vec)
     hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
@@ -1330,10 +1345,10 @@ template <typename T>
 int launch_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scale,
                           int64_t scale_ld, hipStream_t s) {
   uint32_t spr, total;
-  if (steps_for(rows, K, StepGeom<T>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(packed, EPL / 2);
-  const dim3 grid(grid_for(total, kRowSteps)), block(kThreads);
+  const dim3 grid(grid_for(total, kRowSteps)), block(kRowThreads);
   if (vec)
     hipLaunchKernelGGL((quantize_mxfp4_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
                        scale_ld, spr, total);
@@ -1347,10 +1362,10 @@ template <typename TO>
 int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                             void* out, int64_t ld_out, hipStream_t s) {
   uint32_t spr, total;
-  if (steps_for(rows, K, 2048, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);
   const bool vec = aligned(packed, 4) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
-  const dim3 grid(grid_for(total, kDequantSteps)), block(kThreads);
+  const dim3 grid(grid_for(total, kDequantSteps)), block(kDequantThreads);
   if (vec)
     hipLaunchKernelGGL((dequantize_mxfp4_kernel<TO, true>), grid, block, 0, s, packed, scale, scale_ld, K, (TO*)out,
                        ld_out, spr, total);
@@ -1586,9 +1601,9 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
               rd = matrix_range(data, rows, K, K, 1), ro = matrix_range(scale_out, rows, nb, scale_out_ld, 1);
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(ro, rp) || overlap(ro, rs) || overlap(rd, ro)) return MXQ_ERR_ALIAS;
   uint32_t spr, total;
-  if (steps_for(rows, K, 4096, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, kPackedThreads * 16, &spr, &total)) return MXQ_ERR_SHAPE;
   const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
-  const dim3 grid(grid_for(total, kPackedSteps)), block(kThreads);
+  const dim3 grid(grid_for(total, kPackedSteps)), block(kPackedThreads);
   if (vec)
     hipLaunchKernelGGL((packed_convert_kernel<true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
                        scale_out, scale_out_ld, spr, total);
