@@ -2,10 +2,14 @@
 //
 // Block-scaled weight quantization: MXFP4 projection, the direct MXFP8 rowwise
 // lift, 128x128 tile-exponent folding into E4M3, the unpadded scale export and
-// the E8M0 decode.  Sources (page title, section):
+// the E8M0 decode; the fused projection + row lift and the no-op-flag-gated
+// direct conversions; the packed MXFP4 deployment format (encode, decode, and
+// the row lift / tile fold from it); MXFP8 columnwise (32x1) from the MXFP4
+// decomposition, alone and with the row lift in one pass.  Sources (page title,
+// section):
 //   [QAT] "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8 block-scaling recipes":
-//         Description (both conversion modes, the E8M0 decode), Test results,
-//         Known limitations.
+//         Description (both conversion modes, the weight dataflows, the E8M0
+//         decode), Test results, Known limitations.
 //   [EXP] "MXFP8TensorStorage.export_components()": Description.
 //
 // Design (CDNA4, wave64).  Every kernel streams HBM once; nothing here is a
@@ -37,8 +41,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-// Launch-shape tunables (compile-time).
-// 16-byte chunks in flight per lane (steps per workgroup) in the streaming kernels
+// ------------------------------------------------------------------------------------
+// Launch-shape tunables (compile-time).  The defaults are the best of sweeps at
+// 8192 x 8192 bf16 on one MI355X.
+// ------------------------------------------------------------------------------------
+// Lanes per workgroup of the streaming kernels.
+#ifndef MXQ_PROJ_THREADS
+#define MXQ_PROJ_THREADS 64       // projection (one wave)
+#endif
+#ifndef MXQ_ROW_THREADS
+#define MXQ_ROW_THREADS 256       // row lift, fused projection + row lift, MXFP4 encode
+#endif
+#ifndef MXQ_DEQUANT_THREADS
+#define MXQ_DEQUANT_THREADS 64    // FP8 and MXFP4 decodes (8 elements per lane)
+#endif
+#ifndef MXQ_PACKED_THREADS
+#define MXQ_PACKED_THREADS 256    // row lift from packed MXFP4 (16 elements per lane)
+#endif
+// Steps (16-byte chunks in flight per lane) per workgroup of the streaming kernels.
 #ifndef MXQ_PROJ_STEPS
 #define MXQ_PROJ_STEPS 1
 #endif
@@ -51,47 +71,39 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_PACKED_STEPS
 #define MXQ_PACKED_STEPS 2
 #endif
+// The banded kernels.
 #ifndef MXQ_PFOLD_ROWS
-#define MXQ_PFOLD_ROWS 16     // fold from packed MXFP4: band rows per lane (16, 8 or 4)
+#define MXQ_PFOLD_ROWS 16         // fold from packed MXFP4: band rows per lane (16, 8 or 4)
 #endif
 #ifndef MXQ_COL_THREADS
-#define MXQ_COL_THREADS 64    // columnwise: column lanes per workgroup, one 16-byte chunk of columns each
+#define MXQ_COL_THREADS 64        // columnwise: column lanes per workgroup, one 16-byte chunk each
 #endif
 #ifndef MXQ_COL_ROWS
-#define MXQ_COL_ROWS 4        // columnwise: rows of the 32-row band per lane (a divisor of 32)
+#define MXQ_COL_ROWS 4            // columnwise: rows of the 32-row band per lane (a divisor of 32)
 #endif
+#ifndef MXQ_TILE_COLUMN_MAJOR
+#define MXQ_TILE_COLUMN_MAJOR 0   // 128x128 fold: consecutive workgroups walk down a tile column
+#endif
+// Cache policy of the streaming accesses.
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
 #endif
 #ifndef MXQ_NT_STORES
 #define MXQ_NT_STORES 1           // streaming stores carry the non-temporal hint
 #endif
-#ifndef MXQ_TILE_COLUMN_MAJOR
-#define MXQ_TILE_COLUMN_MAJOR 0   // 128x128 fold: consecutive workgroups walk down a tile column
+#ifndef MXQ_PROJ_STORE_SC1
+#define MXQ_PROJ_STORE_SC1 1      // projection output: buffer stores with the nt and sc1 bits
 #endif
 
-constexpr int kThreads = 256;     // 4 waves per workgroup
-#ifndef MXQ_PROJ_THREADS
-#define MXQ_PROJ_THREADS 64    // projection: lanes per workgroup (one wave)
-#endif
-constexpr int kProjThreads = MXQ_PROJ_THREADS;
-#ifndef MXQ_ROW_THREADS
-#define MXQ_ROW_THREADS 256    // row lift (and fused projection + row lift), MXFP4 encode: lanes per workgroup
-#endif
-#ifndef MXQ_DEQUANT_THREADS
-#define MXQ_DEQUANT_THREADS 64   // FP8 and MXFP4 decodes: lanes per workgroup (8 elements each)
-#endif
-#ifndef MXQ_PACKED_THREADS
-#define MXQ_PACKED_THREADS 256   // row lift from packed MXFP4: lanes per workgroup (16 elements each)
-#endif
-constexpr int kRowThreads = MXQ_ROW_THREADS, kDequantThreads = MXQ_DEQUANT_THREADS,
+constexpr int kThreads = 256;     // 4 waves: workgroup size of the remaining streaming kernels
+constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS, kDequantThreads = MXQ_DEQUANT_THREADS,
               kPackedThreads = MXQ_PACKED_THREADS;
+constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
+              kPackedSteps = MXQ_PACKED_STEPS;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
 static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
 static_assert(kColRows * kColGroups == 32 && kColThreads % 64 == 0, "columnwise geometry");
-constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
-              kPackedSteps = MXQ_PACKED_STEPS;
 
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
@@ -110,9 +122,6 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 #endif
 }
 
-#ifndef MXQ_PROJ_STORE_SC1
-#define MXQ_PROJ_STORE_SC1 1  // projection output: buffer stores with the nt and sc1 cache-policy bits
-#endif
 // 16-byte streaming store at byte offset `off` of a row whose base address is
 // the same for the whole wave (nbytes: the row's length, below 2^31).  With
 // MXQ_PROJ_STORE_SC1 it is a buffer store carrying the nt and sc1 bits, which
