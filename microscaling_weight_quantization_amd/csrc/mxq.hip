@@ -479,11 +479,13 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(const T* __restrict__ 
 // rule equals ceil(log2(amax / 448)).  amax skips the NaNs of poisoned row
 // blocks; their payload is 0x7F.
 //
-// A workgroup takes one 32-row band and one step of columns (256 lanes x one
-// 16-byte chunk).  Each lane loads its chunk of all 32 rows before anything
-// else, projects them in registers (bf16 words, exact), keeps the finite column
-// maxima with packed 16-bit max, then writes the band's codes and payload.
-// With kRow the same pass also writes the rowwise lift of every row block.
+// A workgroup takes one 32-row band and kColThreads 16-byte column chunks, with
+// kColGroups lane groups of kColThreads lanes each taking kColRows of the band's
+// rows.  Each lane loads its chunk of its rows before anything else, projects
+// them in registers (bf16 words, exact) and keeps the finite column maxima with
+// packed 16-bit max; the groups' maxima meet in LDS; then every lane writes its
+// rows' payload (group 0 also the band's codes).  With kRow the same pass also
+// writes the rowwise lift of every row block.
 // ------------------------------------------------------------------------------------
 // E4M3 bytes of four bf16 values at four scales: each pair is converted at
 // both of its elements' scales and the right byte of each is kept (two byte
@@ -611,8 +613,8 @@ __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
 // run of J * 256 bytes (bf16) per load.  Each lane keeps only the E2M1 nibbles,
 // block exponents and poison bits of its chunks (all in one tile); the largest
 // finite block exponent of every tile is reduced with DPP inside each 16-lane
-// row, shuffles across rows of the wave, and LDS across the 4 waves; then every
-// lane folds and writes its payload.
+// row, shuffles across rows of the wave, and LDS across the workgroup's waves;
+// then every lane folds and writes its payload.
 // ------------------------------------------------------------------------------------
 #ifndef MXQ_TILES_PER_WG
 #define MXQ_TILES_PER_WG 1
