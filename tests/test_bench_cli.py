@@ -1,0 +1,31 @@
+"""bench.py's command-line contract, checked without a GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=120)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_step_count_must_be_positive():
+    r = _run("--steps", "0")
+    assert r.returncode != 0 and "--steps" in r.stderr
+
+
+def test_algorithmic_bytes_at_8192():
+    sys.path.insert(0, ROOT)
+    import bench
+    b = bench.algorithmic_bytes(8192, 8192)
+    assert b["proj"] == 268435456 and b["row"] == 203423744 and b["block128"] == 201330688
+    assert bench.fused_bytes(8192, 8192) == 337641472
+    assert bench.col_bytes(8192, 8192)["col"] == 203423744
