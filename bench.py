@@ -99,28 +99,43 @@ def read_traffic(kernel: str):
     return int(float(v)) if v else None
 
 
-def _oracle_pass(bits, threads: int) -> None:
+def _oracle_pass(bits, threads: int) -> dict:
+    """One pass of the six steps through the CPU oracle; returns its outputs."""
     import oracle
-    oracle.fake_quantize_mxfp4(bits, threads=threads)
+    y = oracle.fake_quantize_mxfp4(bits, threads=threads)
     d, s = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=SCALE_LD, threads=threads)
     c = oracle.export_mxfp8(s, bits.shape[1])
     bd, tc = oracle.mxfp4_to_fp8_block128(bits, threads=threads)
-    oracle.dequantize(d, c, threads=threads)
-    oracle.dequantize(bd, tc, layout=oracle.TILE_128X128, threads=threads)
+    dr = oracle.dequantize(d, c, threads=threads)
+    dt = oracle.dequantize(bd, tc, layout=oracle.TILE_128X128, threads=threads)
+    return {"proj": y, "row": d, "export": c, "block128": bd, "tile_codes": tc, "dec_row": dr, "dec_tile": dt}
 
 
-def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int = 8) -> dict:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int = 8):
     """The CPU oracle over the same workload (whole passes of every step), as is.
 
     Passes repeat until the process has spent about `cpu_seconds` of CPU time
-    (all threads together), so the figure rests on 10-30 s of CPU work."""
+    (all threads together), so the figure rests on 10-30 s of CPU work.
+    Returns the JSON object and the oracle's outputs (for the parity check)."""
     c0, t0, passes = time.process_time(), time.perf_counter(), 0
     while passes < max_passes and (passes == 0 or time.process_time() - c0 < cpu_seconds):
-        _oracle_pass(bits, threads)
+        outputs = _oracle_pass(bits, threads)
         passes += 1
     dt, cpu = time.perf_counter() - t0, time.process_time() - c0
     total = passes * sum(algorithmic_bytes(*bits.shape).values())
     out = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
            "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} bf16 weight, {passes} pass{'es' if passes > 1 else ''} of all six steps "
                      f"({dt:.1f} s wall, {cpu:.1f} s CPU on {threads} threads)"}
     # the same steps on one thread, over the first 2048 rows
@@ -130,7 +145,24 @@ def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int 
     dt1 = time.perf_counter() - t0
     out["one_thread"] = {"value": round(sum(algorithmic_bytes(*sub.shape).values()) / dt1 / 1e9, 3), "unit": "GB/s",
                          "sample": f"rows 0..2047 of the same weight, one pass of all six steps ({dt1:.1f} s)"}
-    return out
+    return out, outputs
+
+
+def parity(s, want: dict) -> dict:
+    """The step's GPU outputs in one buffer set against the oracle's, bit for bit
+    (8192 x 8192, the timed launch configuration)."""
+    import torch
+
+    def host(t):
+        t = t.contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view("uint16")
+        return t.numpy()
+
+    got = {"proj": host(s["y"]), "row": host(s["data"]), "export": host(s["scale_c"]), "block128": host(s["bdata"]),
+           "tile_codes": host(s["tc"]), "dec_row": host(s["dec_r"]), "dec_tile": host(s["dec_t"])}
+    res = {k: got[k].shape == want[k].shape and bool((got[k] == want[k]).all()) for k in want}
+    return {"bit_exact": all(res.values()), "outputs": res}
 
 
 def main():
@@ -172,8 +204,11 @@ def main():
             "scale_c": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
             "bdata": torch.empty((rows, K), dtype=torch.uint8, device=dev),
             "tc": torch.empty(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev),
+            "tc2": torch.empty(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev),
             "dec_r": torch.empty_like(x0),
             "dec_t": torch.empty_like(x0),
+            "dec_c": torch.empty_like(x0),
+            "dec_p": torch.empty_like(x0),
             "y2": torch.empty_like(x0),
             "packed": torch.empty((rows, K // 2), dtype=torch.uint8, device=dev),
             "pscale": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
@@ -205,17 +240,17 @@ def main():
     launches["fused"] = lambda s: mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(s["x"], s["y2"], s["data2"], s["scale2"])
     # outside the step: the packed MXFP4 deployment format
     launches["quantize_mxfp4"] = lambda s: mxq.mxq_quantize_mxfp4(s["x"], s["packed"], s["pscale"])
-    launches["dequantize_mxfp4"] = lambda s: mxq.mxq_dequantize_mxfp4(s["packed"], s["pscale"], K, out=s["dec_r"])
+    launches["dequantize_mxfp4"] = lambda s: mxq.mxq_dequantize_mxfp4(s["packed"], s["pscale"], K, out=s["dec_p"])
     launches["packed_to_row"] = lambda s: mxq.mxq_mxfp4_packed_to_mxfp8_row(s["packed"], s["pscale"], K, s["data2"],
                                                                               s["scale2"][:, :nb])
     launches["packed_to_block128"] = lambda s: mxq.mxq_mxfp4_packed_to_fp8_block128(s["packed"], s["pscale"], K,
-                                                                                    s["bdata"], s["tc"])
+                                                                                    s["data2"], s["tc2"])
     # outside the step: MXFP8 columnwise (32x1), alone and with the row lift in one pass, and its decode
     launches["col"] = lambda s: mxq.mxq_mxfp4_to_mxfp8_col(s["x"], s["cdata"], s["cscale"])
     launches["row_col"] = lambda s: mxq.mxq_mxfp4_to_mxfp8_row_col(s["x"], s["data2"], s["scale2"], s["cdata"],
                                                                      s["cscale"])
     launches["dec_col"] = lambda s: mxq.mxq_dequantize(s["cdata"], s["cscale"], layout=mxq.MXQ_SCALE_COL_32X1,
-                                                       out=s["dec_t"])
+                                                       out=s["dec_c"])
     extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128", "col",
                    "row_col", "dec_col"]
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
@@ -319,7 +354,9 @@ def main():
         "outside_step": extra,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(bits, threads=min(16, os.cpu_count() or 1))
+        out["cpu_baseline"], want = cpu_baseline(bits, threads=min(16, os.cpu_count() or 1))
+        # the same oracle run gives the bytes for a full-size parity check of the step
+        out["parity"] = parity(sets[0], want)
     print(json.dumps(out), flush=True)
 
 
