@@ -15,7 +15,9 @@
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
  *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
  * and MXFP8 columnwise (32x1) from the decomposition:
- *   mxq_mxfp4_to_mxfp8_col, mxq_mxfp4_to_mxfp8_row_col (row and column in one pass)
+ *   mxq_mxfp4_to_mxfp8_col, mxq_mxfp4_to_mxfp8_row_col (row and column in one pass),
+ *   and their no-op-flag-gated forms mxq_mxfp4_to_mxfp8_col_guarded,
+ *   mxq_mxfp4_to_mxfp8_row_col_guarded
  *
  * Sources, by page title and section:
  *   [QAT] "[PyTorch] MXFP4 weight QAT on MXFP8 and FP8 block-scaling recipes"
@@ -197,6 +199,23 @@ int mxq_mxfp4_to_mxfp8_col(const void* x, int64_t ld_x, int64_t rows, int64_t K,
 int mxq_mxfp4_to_mxfp8_row_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
                                uint8_t* row_data, uint8_t* row_scale, int64_t row_scale_ld, uint8_t* col_data,
                                uint8_t* col_scale, int64_t col_scale_ld, hipStream_t stream);
+
+/*
+ * mxq_mxfp4_to_mxfp8_col / mxq_mxfp4_to_mxfp8_row_col gated by a device-side
+ * no-op flag, as mxq_mxfp4_to_mxfp8_row_guarded: when *noop != 0 at the time
+ * the work runs on the stream, every output is left untouched.  [QAT]'s
+ * flowchart has the skip-update flag gate every conversion into the cached
+ * workspace, the columnwise one included.
+ *   noop   device pointer to one int32; required (NULL -> MXQ_ERR_NULL).
+ *          Other arguments as for the ungated calls.
+ */
+int mxq_mxfp4_to_mxfp8_col_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                   uint8_t* data, uint8_t* scale, int64_t scale_ld, const int32_t* noop,
+                                   hipStream_t stream);
+int mxq_mxfp4_to_mxfp8_row_col_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                       uint8_t* row_data, uint8_t* row_scale, int64_t row_scale_ld,
+                                       uint8_t* col_data, uint8_t* col_scale, int64_t col_scale_ld,
+                                       const int32_t* noop, hipStream_t stream);
 
 /*
  * Unpadded export of MXFP8 rowwise scales, [EXP] Description: scale_inv holds

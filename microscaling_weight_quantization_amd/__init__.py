@@ -35,7 +35,7 @@ ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mx
                 "mxq_fake_quantize_mxfp4_with_mxfp8_row", "mxq_mxfp4_to_mxfp8_row_guarded",
                 "mxq_mxfp4_to_fp8_block128_guarded", "mxq_quantize_mxfp4", "mxq_dequantize_mxfp4",
                 "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
-                "mxq_mxfp4_to_mxfp8_row_col")
+                "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded")
 
 _libs = {}
 _lock = threading.Lock()
@@ -74,6 +74,8 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_mxfp4_packed_to_fp8_block128.argtypes = [u8p, u8p, i64, i64, i64, u8p, u8p, i64, vp]
         L.mxq_mxfp4_to_mxfp8_col.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp]
         L.mxq_mxfp4_to_mxfp8_row_col.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp]
+        L.mxq_mxfp4_to_mxfp8_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
+        L.mxq_mxfp4_to_mxfp8_row_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -195,9 +197,11 @@ def _payload_for(x: torch.Tensor, rows: int, K: int, data: Optional[torch.Tensor
 
 
 def mxq_mxfp4_to_mxfp8_col(x: torch.Tensor, data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
-                           scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+                           scale_ld: Optional[int] = None, lib: str = "libmxq.so",
+                           noop: Optional[torch.Tensor] = None):
     """MXFP8 columnwise (32x1 blocks) from the decomposition ->
-    (payload uint8 [rows, K], E8M0 codes uint8 [ceil(rows/32), scale_ld])."""
+    (payload uint8 [rows, K], E8M0 codes uint8 [ceil(rows/32), scale_ld]).
+    With `noop` (an int32 device tensor) this is mxq_mxfp4_to_mxfp8_col_guarded."""
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
@@ -205,16 +209,21 @@ def mxq_mxfp4_to_mxfp8_col(x: torch.Tensor, data: Optional[torch.Tensor] = None,
         scale = torch.zeros(((rows + 31) // 32, scale_ld or K), dtype=torch.uint8, device=x.device)
     data, pd = _payload_for(x, rows, K, data)
     ps, _, _, ld_s = _matrix(scale)
-    _check(L, L.mxq_mxfp4_to_mxfp8_col(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    if noop is None:
+        _check(L, L.mxq_mxfp4_to_mxfp8_col(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
+    else:
+        _check(L, L.mxq_mxfp4_to_mxfp8_col_guarded(px, ldx, rows, K, dt, pd, ps, ld_s, _flag(noop), _stream(x)))
     return data, scale
 
 
 def mxq_mxfp4_to_mxfp8_row_col(x: torch.Tensor, row_data: Optional[torch.Tensor] = None,
                                row_scale: Optional[torch.Tensor] = None, col_data: Optional[torch.Tensor] = None,
                                col_scale: Optional[torch.Tensor] = None, row_scale_ld: Optional[int] = None,
-                               col_scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+                               col_scale_ld: Optional[int] = None, lib: str = "libmxq.so",
+                               noop: Optional[torch.Tensor] = None):
     """Row lift and columnwise conversion from one read of x ->
-    (row payload, row codes [rows, row_scale_ld], column payload, column codes [ceil(rows/32), col_scale_ld])."""
+    (row payload, row codes [rows, row_scale_ld], column payload, column codes [ceil(rows/32), col_scale_ld]).
+    With `noop` (an int32 device tensor) this is mxq_mxfp4_to_mxfp8_row_col_guarded."""
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
@@ -227,7 +236,11 @@ def mxq_mxfp4_to_mxfp8_row_col(x: torch.Tensor, row_data: Optional[torch.Tensor]
     col_data, pcd = _payload_for(x, rows, K, col_data)
     prs, _, _, ld_rs = _matrix(row_scale)
     pcs, _, _, ld_cs = _matrix(col_scale)
-    _check(L, L.mxq_mxfp4_to_mxfp8_row_col(px, ldx, rows, K, dt, prd, prs, ld_rs, pcd, pcs, ld_cs, _stream(x)))
+    if noop is None:
+        _check(L, L.mxq_mxfp4_to_mxfp8_row_col(px, ldx, rows, K, dt, prd, prs, ld_rs, pcd, pcs, ld_cs, _stream(x)))
+    else:
+        _check(L, L.mxq_mxfp4_to_mxfp8_row_col_guarded(px, ldx, rows, K, dt, prd, prs, ld_rs, pcd, pcs, ld_cs,
+                                                       _flag(noop), _stream(x)))
     return row_data, row_scale, col_data, col_scale
 
 

@@ -504,11 +504,12 @@ template <typename T, bool VEC, bool kRow>
 __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
     const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* __restrict__ cdata,
     uint8_t* __restrict__ cscale, int64_t cscale_ld, uint8_t* __restrict__ rdata, uint8_t* __restrict__ rscale,
-    int64_t rscale_ld, uint32_t groups) {
+    int64_t rscale_ld, uint32_t groups, const int32_t* __restrict__ noop) {
   using G = StepGeom<T>;
   constexpr int EPL = Fmt<T>::kEPL, NW = sizeof(T) == 2 ? 4 : 2;   // elements, bf16 words per chunk
   constexpr int R = kColRows;
   __shared__ uint32_t s_cmax[kColGroups > 1 ? kColGroups : 1][NW][kColThreads];
+  if (skipped(noop)) return;
   keep_denormals();
   const uint32_t lane = threadIdx.x % kColThreads, rg = threadIdx.x / kColThreads;   // rg: uniform per wave
   const uint32_t band = blockIdx.x / groups, grp = blockIdx.x - band * groups;
@@ -1279,7 +1280,8 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
 
 template <typename T>
 int launch_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* cdata, uint8_t* cscale,
-               int64_t cscale_ld, uint8_t* rdata, uint8_t* rscale, int64_t rscale_ld, hipStream_t s) {
+               int64_t cscale_ld, uint8_t* rdata, uint8_t* rscale, int64_t rscale_ld, const int32_t* noop,
+               hipStream_t s) {
   constexpr int64_t kCols = (int64_t)kColThreads * Fmt<T>::kEPL;   // columns per workgroup
   const int64_t groups = (K + kCols - 1) / kCols, bands = (rows + 31) / 32;
   if (bands > kMaxSteps / groups) return MXQ_ERR_SHAPE;
@@ -1289,7 +1291,7 @@ int launch_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* cd
   const dim3 grid((uint32_t)(bands * groups)), block(kColThreads * kColGroups);
 #define MXQ_COL_LAUNCH(V, R)                                                                                    \
   hipLaunchKernelGGL((col_kernel<T, V, R>), grid, block, 0, s, (const T*)x, ld_x, rows, K, cdata, cscale, cscale_ld, \
-                     rdata, rscale, rscale_ld, (uint32_t)groups)
+                     rdata, rscale, rscale_ld, (uint32_t)groups, noop)
   if (rdata != nullptr) {
     if (vec) MXQ_COL_LAUNCH(true, true); else MXQ_COL_LAUNCH(false, true);
   } else {
@@ -1486,11 +1488,12 @@ int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows,
 
 static int col_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* row_data,
                      uint8_t* row_scale, int64_t row_scale_ld, bool with_row, uint8_t* col_data, uint8_t* col_scale,
-                     int64_t col_scale_ld, hipStream_t stream) {
+                     int64_t col_scale_ld, const int32_t* noop, bool need_noop, hipStream_t stream) {
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (rows == 0 || K == 0) return MXQ_OK;
-  if (!x || !col_data || !col_scale || (with_row && (!row_data || !row_scale))) return MXQ_ERR_NULL;
+  if (!x || !col_data || !col_scale || (with_row && (!row_data || !row_scale)) || (need_noop && !noop))
+    return MXQ_ERR_NULL;
   const int64_t nb = (K + 31) / 32, bands = (rows + 31) / 32;
   if (ld_x < K || col_scale_ld < K || (with_row && row_scale_ld < nb)) return MXQ_ERR_SHAPE;
   const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), cd = matrix_range(col_data, rows, K, K, 1),
@@ -1505,21 +1508,35 @@ static int col_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_d
     row_data = nullptr, row_scale = nullptr, row_scale_ld = 0;
   }
   return dt == MXQ_BF16 ? launch_col<uint16_t>(x, ld_x, rows, K, col_data, col_scale, col_scale_ld, row_data,
-                                               row_scale, row_scale_ld, stream)
+                                               row_scale, row_scale_ld, noop, stream)
                         : launch_col<uint32_t>(x, ld_x, rows, K, col_data, col_scale, col_scale_ld, row_data,
-                                               row_scale, row_scale_ld, stream);
+                                               row_scale, row_scale_ld, noop, stream);
 }
 
 int mxq_mxfp4_to_mxfp8_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
                            uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
-  return col_entry(x, ld_x, rows, K, dt, nullptr, nullptr, 0, false, data, scale, scale_ld, stream);
+  return col_entry(x, ld_x, rows, K, dt, nullptr, nullptr, 0, false, data, scale, scale_ld, nullptr, false, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_col_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                   uint8_t* data, uint8_t* scale, int64_t scale_ld, const int32_t* noop,
+                                   hipStream_t stream) {
+  return col_entry(x, ld_x, rows, K, dt, nullptr, nullptr, 0, false, data, scale, scale_ld, noop, true, stream);
 }
 
 int mxq_mxfp4_to_mxfp8_row_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
                                uint8_t* row_data, uint8_t* row_scale, int64_t row_scale_ld, uint8_t* col_data,
                                uint8_t* col_scale, int64_t col_scale_ld, hipStream_t stream) {
   return col_entry(x, ld_x, rows, K, dt, row_data, row_scale, row_scale_ld, true, col_data, col_scale, col_scale_ld,
-                   stream);
+                   nullptr, false, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_row_col_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                       uint8_t* row_data, uint8_t* row_scale, int64_t row_scale_ld,
+                                       uint8_t* col_data, uint8_t* col_scale, int64_t col_scale_ld,
+                                       const int32_t* noop, hipStream_t stream) {
+  return col_entry(x, ld_x, rows, K, dt, row_data, row_scale, row_scale_ld, true, col_data, col_scale, col_scale_ld,
+                   noop, true, stream);
 }
 
 int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t rows, int64_t K, int64_t scale_ld,

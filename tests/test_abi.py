@@ -107,6 +107,11 @@ def test_host_validation_without_a_gpu(lib):
                                           P(0x300000), 64, None) == mxq.MXQ_ERR_ALIAS
     assert lib.mxq_mxfp4_to_mxfp8_row_col(fake, 64, 40, 64, 0, P(0x500000), P(0x400000), 1, P(0x200000),
                                           P(0x300000), 64, None) == mxq.MXQ_ERR_SHAPE
+    # gated columnwise forms need their flag
+    assert lib.mxq_mxfp4_to_mxfp8_col_guarded(fake, 64, 40, 64, 0, P(0x200000), P(0x300000), 64, None,
+                                              None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_mxfp4_to_mxfp8_row_col_guarded(fake, 64, 40, 64, 0, P(0x500000), P(0x400000), 2, P(0x200000),
+                                                  P(0x300000), 64, None, None) == mxq.MXQ_ERR_NULL
     # packed MXFP4: narrow code storage, overlaps, odd shapes
     assert lib.mxq_quantize_mxfp4(fake, 64, 4, 64, 0, P(0x200000), P(0x300000), 1, None) == mxq.MXQ_ERR_SHAPE
     assert lib.mxq_quantize_mxfp4(fake, 64, 4, 64, 0, P(0x200000), P(0x200010), 2, None) == mxq.MXQ_ERR_ALIAS

@@ -165,3 +165,65 @@ def test_col_empty_and_errors(dev):
 def test_col_build_variants_identical_bits(dev, variant):
     for bits in (W.c2_exhaustive(natural=True), W.fp32_fuzz(1 << 16).reshape(-1, 128), W.c3_spread()[:256, :512]):
         check_col(np.ascontiguousarray(bits), dev, lib=variant)
+
+
+def test_col_noop_flag_gates_the_columnwise_conversions(dev):
+    bits = W.c4_headline(shape=(96, 1024))
+    x = to_dev(bits, dev)
+    wd, ws = oracle.mxfp4_to_mxfp8_col(bits)
+    wrd, wrs = oracle.mxfp4_to_mxfp8_row(bits)
+    flag = torch.ones(1, dtype=torch.int32, device=dev)
+    cd = torch.full((96, 1024), 0x11, dtype=torch.uint8, device=dev)
+    cs = torch.full((3, 1024), 0x22, dtype=torch.uint8, device=dev)
+    rd = torch.full((96, 1024), 0x33, dtype=torch.uint8, device=dev)
+    rs = torch.full((96, 32), 0x44, dtype=torch.uint8, device=dev)
+    cd2 = torch.full((96, 1024), 0x55, dtype=torch.uint8, device=dev)
+    cs2 = torch.full((3, 1024), 0x66, dtype=torch.uint8, device=dev)
+    mxq.mxq_mxfp4_to_mxfp8_col(x, cd, cs, noop=flag)
+    mxq.mxq_mxfp4_to_mxfp8_row_col(x, rd, rs, cd2, cs2, noop=flag)
+    for t, v in ((cd, 0x11), (cs, 0x22), (rd, 0x33), (rs, 0x44), (cd2, 0x55), (cs2, 0x66)):
+        assert (to_host(t) == v).all()
+    flag.zero_()
+    mxq.mxq_mxfp4_to_mxfp8_col(x, cd, cs, noop=flag)
+    mxq.mxq_mxfp4_to_mxfp8_row_col(x, rd, rs, cd2, cs2, noop=flag)
+    assert_bits(to_host(cd), wd, "gated column payload")
+    assert_bits(to_host(cs), ws, "gated column codes")
+    assert_bits(to_host(cd2), wd, "gated row + column: column payload")
+    assert_bits(to_host(cs2), ws, "gated row + column: column codes")
+    assert_bits(to_host(rd), wrd, "gated row + column: row payload")
+    assert_bits(to_host(rs), wrs, "gated row + column: row codes")
+
+
+def test_col_noop_flag_inside_a_replayed_graph(dev):
+    """The row + column update captured in a graph and replayed with the flag
+    set and clear, the weight changed eagerly in between; every replay checked."""
+    a_bits = W.c4_headline(shape=(128, 2048))
+    b_bits = np.ascontiguousarray(np.tile(W.c1_small()[:, :32], (2, 64))[:128, :2048])
+    x = to_dev(a_bits, dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    rd = torch.empty((128, 2048), dtype=torch.uint8, device=dev)
+    rs = torch.empty((128, 64), dtype=torch.uint8, device=dev)
+    cd = torch.empty((128, 2048), dtype=torch.uint8, device=dev)
+    cs = torch.empty((4, 2048), dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm up outside the graph
+        mxq.mxq_mxfp4_to_mxfp8_row_col(x, rd, rs, cd, cs, noop=flag)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mxq.mxq_mxfp4_to_mxfp8_row_col(x, rd, rs, cd, cs, noop=flag)
+    want = {n: oracle.mxfp4_to_mxfp8_row(b) + oracle.mxfp4_to_mxfp8_col(b) for n, b in (("a", a_bits), ("b", b_bits))}
+    for step, (src, skip, expect) in enumerate([("a", 0, "a"), ("b", 1, "a"), ("b", 0, "b"), ("a", 1, "b"),
+                                                ("a", 0, "a")]):
+        x.copy_(to_dev(a_bits if src == "a" else b_bits, dev))
+        flag.fill_(skip)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        wrd, wrs, wcd, wcs = want[expect]
+        assert_bits(to_host(rd), wrd, f"replay {step} row payload")
+        assert_bits(to_host(rs), wrs, f"replay {step} row codes")
+        assert_bits(to_host(cd), wcd, f"replay {step} column payload")
+        assert_bits(to_host(cs), wcs, f"replay {step} column codes")
