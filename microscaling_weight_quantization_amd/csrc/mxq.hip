@@ -53,7 +53,10 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_ROW_THREADS 256       // row lift, fused projection + row lift, MXFP4 encode
 #endif
 #ifndef MXQ_DEQUANT_THREADS
-#define MXQ_DEQUANT_THREADS 64    // FP8 and MXFP4 decodes (8 elements per lane)
+#define MXQ_DEQUANT_THREADS 64    // FP8 decodes (8 elements per lane)
+#endif
+#ifndef MXQ_DQ4_THREADS
+#define MXQ_DQ4_THREADS 256       // packed MXFP4 decode (8 elements per lane)
 #endif
 #ifndef MXQ_PACKED_THREADS
 #define MXQ_PACKED_THREADS 256    // row lift from packed MXFP4 (16 elements per lane)
@@ -97,7 +100,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;     // 4 waves: workgroup size of the remaining streaming kernels
 constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS, kDequantThreads = MXQ_DEQUANT_THREADS,
-              kPackedThreads = MXQ_PACKED_THREADS;
+              kDq4Threads = MXQ_DQ4_THREADS, kPackedThreads = MXQ_PACKED_THREADS;
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
               kPackedSteps = MXQ_PACKED_STEPS;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
@@ -945,7 +948,7 @@ __device__ __forceinline__ u32x4 decode8_fp4(uint32_t f, uint32_t c) {
 }
 
 template <typename TO, bool VEC>
-__global__ __launch_bounds__(kDequantThreads) void dequantize_mxfp4_kernel(const uint8_t* __restrict__ packed,
+__global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uint8_t* __restrict__ packed,
                                                                     const uint8_t* __restrict__ scale,
                                                                     int64_t scale_ld, int64_t K,
                                                                     TO* __restrict__ out, int64_t ld_out,
@@ -962,7 +965,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequantize_mxfp4_kernel(const
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
+    const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
     if (VEC) {
@@ -978,7 +981,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequantize_mxfp4_kernel(const
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
-    const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
+    const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
     if (col0 >= K) continue;
     const u32x4 o = decode8_fp4(fs[u], cs[u]);
     TO* orow = out + (int64_t)row * ld_out;
@@ -1375,10 +1378,10 @@ template <typename TO>
 int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                             void* out, int64_t ld_out, hipStream_t s) {
   uint32_t spr, total;
-  if (steps_for(rows, K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, kDq4Threads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);
   const bool vec = aligned(packed, 4) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
-  const dim3 grid(grid_for(total, kDequantSteps)), block(kDequantThreads);
+  const dim3 grid(grid_for(total, kDequantSteps)), block(kDq4Threads);
   if (vec)
     hipLaunchKernelGGL((dequantize_mxfp4_kernel<TO, true>), grid, block, 0, s, packed, scale, scale_ld, K, (TO*)out,
                        ld_out, spr, total);
