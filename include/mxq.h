@@ -102,8 +102,9 @@ int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y,
                             int64_t rows, int64_t K, mxq_dtype dt, hipStream_t stream);
 
 /*
- * Direct MXFP8 rowwise lift, [QAT] Description, conversion mode 2 ("fixed-shift-6
- * lift ... scale clamps at UE8M0 code 0 with exact payload absorption").
+ * Direct MXFP8 rowwise lift, [QAT] Description, conversion mode 2: a lift by a
+ * fixed shift of 6 whose scale stops at UE8M0 code 0, the payload taking up the
+ * rest of the shift exactly.
  * From each block's MXFP4 decomposition x ~ p * 2^e of the master weight (the
  * same e and p as mxq_fake_quantize_mxfp4): scale code = max(e + 121, 0), i.e.
  * scale 2^(e-6) clamped at 2^-127, and payload = E4M3(p * 2^min(6, e+127)),
@@ -119,9 +120,10 @@ int mxq_mxfp4_to_mxfp8_row(const void* x, int64_t ld_x, int64_t rows, int64_t K,
                            uint8_t* data, uint8_t* scale, int64_t scale_ld, hipStream_t stream);
 
 /*
- * Direct 128x128 blockwise FP8, [QAT] Description, conversion mode 2 ("per-tile
- * exponent folding: tile scale 2^(max fp4 exp - 6) clamped at 2^-127, RTNE onto
- * E4M3 incl. subnormals").  Tiles are anchored at (0,0) and truncated at the
+ * Direct 128x128 blockwise FP8, [QAT] Description, conversion mode 2: the block
+ * exponents are folded into one scale per tile, 2^(largest FP4 exponent - 6)
+ * with 2^-127 as its floor, and the payload is rounded to nearest-even onto
+ * E4M3, subnormals included.  Tiles are anchored at (0,0) and truncated at the
  * edges.  Per tile: M = max e over its finite 1x32 blocks (-126 if none);
  * S = max(M - 6, -127); tile code = S + 127; payload = RTNE_E4M3(p * 2^(e - S))
  * with E4M3 subnormals and ties to even.  Exact while the tile's exponent
