@@ -50,7 +50,10 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_PROJ_THREADS 64       // projection (one wave)
 #endif
 #ifndef MXQ_ROW_THREADS
-#define MXQ_ROW_THREADS 256       // row lift, fused projection + row lift, MXFP4 encode
+#define MXQ_ROW_THREADS 256       // row lift, MXFP4 encode
+#endif
+#ifndef MXQ_FUSED_THREADS
+#define MXQ_FUSED_THREADS 64      // fused projection + row lift
 #endif
 #ifndef MXQ_DEQUANT_THREADS
 #define MXQ_DEQUANT_THREADS 64    // FP8 decodes (8 elements per lane)
@@ -67,6 +70,9 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 #ifndef MXQ_ROW_STEPS
 #define MXQ_ROW_STEPS 2
+#endif
+#ifndef MXQ_FUSED_STEPS
+#define MXQ_FUSED_STEPS 1
 #endif
 #ifndef MXQ_DEQUANT_STEPS
 #define MXQ_DEQUANT_STEPS 2
@@ -103,6 +109,7 @@ constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS, kD
               kDq4Threads = MXQ_DQ4_THREADS, kPackedThreads = MXQ_PACKED_THREADS;
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
               kPackedSteps = MXQ_PACKED_STEPS;
+constexpr int kFusedThreads = MXQ_FUSED_THREADS, kFusedSteps = MXQ_FUSED_STEPS;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
 static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
@@ -435,13 +442,21 @@ __device__ __forceinline__ bool skipped(const int32_t* __restrict__ noop) {
 }
 
 // Row lift; with kProj it also writes the projection y (the fused one-pass form).
+// Launch shape of the row kernel: the row lift's, or (kProj) the fused pass's.
+template <bool kProj>
+struct RowShape {
+  static constexpr int kTPB = kProj ? kFusedThreads : kRowThreads, kSteps = kProj ? kFusedSteps : kRowSteps;
+};
+
 template <typename T, bool VEC, bool kProj>
-__global__ __launch_bounds__(kRowThreads) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
-                                                       uint8_t* __restrict__ data, uint8_t* __restrict__ scale,
-                                                       int64_t scale_ld, T* __restrict__ y, int64_t ld_y,
-                                                       uint32_t steps_per_row, uint32_t total_steps,
-                                                       const int32_t* __restrict__ noop) {
-  using G = StepGeom<T, kRowThreads>;
+__global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+                                                                 uint8_t* __restrict__ data,
+                                                                 uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                                 T* __restrict__ y, int64_t ld_y,
+                                                                 uint32_t steps_per_row, uint32_t total_steps,
+                                                                 const int32_t* __restrict__ noop) {
+  using G = StepGeom<T, RowShape<kProj>::kTPB>;
+  constexpr int kRowSteps = RowShape<kProj>::kSteps;
   if (skipped(noop)) return;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
@@ -1263,16 +1278,18 @@ int launch_proj(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows
 template <typename T>
 int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* data, uint8_t* scale,
                int64_t scale_ld, void* y, int64_t ld_y, const int32_t* noop, hipStream_t s) {
+  const bool fused = y != nullptr;
+  const int tpb = fused ? kFusedThreads : kRowThreads, steps = fused ? kFusedSteps : kRowSteps;
   uint32_t spr, total;
-  if (steps_for(rows, K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, (int64_t)(tpb / Fmt<T>::kLPB) * 32, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
-                   (y == nullptr || (aligned(y, 16) && ld_y % EPL == 0));
-  const dim3 grid(grid_for(total, kRowSteps)), block(kRowThreads);
+                   (!fused || (aligned(y, 16) && ld_y % EPL == 0));
+  const dim3 grid(grid_for(total, steps)), block(tpb);
 #define MXQ_ROW_LAUNCH(V, P)                                                                                  \
   hipLaunchKernelGGL((row_kernel<T, V, P>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \
                      (T*)y, ld_y, spr, total, noop)
-  if (y != nullptr) {
+  if (fused) {
     if (vec) MXQ_ROW_LAUNCH(true, true); else MXQ_ROW_LAUNCH(false, true);
   } else {
     if (vec) MXQ_ROW_LAUNCH(true, false); else MXQ_ROW_LAUNCH(false, false);
