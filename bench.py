@@ -42,7 +42,9 @@ SCALE_LD = 260                   # padded scale storage: ceil(K/32) = 256 plus 4
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_bf16.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "microscaling_weight_quantization_amd", "csrc", "mxq.hip")
+# The device code: the kernels and the divisor header they include.
+KERNEL_SOURCES = [os.path.join(ROOT, "microscaling_weight_quantization_amd", "csrc", n)
+                  for n in ("mxq.hip", "fastdiv.h")]
 
 
 def algorithmic_bytes(rows: int, K: int) -> dict:
@@ -81,8 +83,11 @@ def col_bytes(rows: int, K: int) -> dict:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str):

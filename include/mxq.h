@@ -156,7 +156,9 @@ int mxq_fake_quantize_mxfp4_with_mxfp8_row(const void* x, int64_t ld_x, void* y,
  * graph, where a replay must be able to keep the existing workspace ([QAT]
  * review: the CUDA-graph skip-update flag must gate the cached update).
  *   noop   device pointer to one int32, read by the kernels; required (NULL ->
- *          MXQ_ERR_NULL).  Other arguments as for the ungated calls.
+ *          MXQ_ERR_NULL).  Other arguments as for the ungated calls.  The
+ *          input is read either way (the kernels issue their input loads
+ *          before they read the flag), so x must be valid in both cases.
  */
 int mxq_mxfp4_to_mxfp8_row_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
                                    uint8_t* data, uint8_t* scale, int64_t scale_ld, const int32_t* noop,

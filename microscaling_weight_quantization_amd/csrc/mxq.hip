@@ -33,6 +33,7 @@
 #include <stddef.h>
 
 #include "mxq.h"
+#include "fastdiv.h"
 
 namespace {
 
@@ -62,7 +63,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_DQ4_THREADS 256       // packed MXFP4 decode (8 elements per lane)
 #endif
 #ifndef MXQ_PACKED_THREADS
-#define MXQ_PACKED_THREADS 256    // row lift from packed MXFP4 (16 elements per lane)
+#define MXQ_PACKED_THREADS 64     // row lift from packed MXFP4 (16 elements per lane)
 #endif
 // Steps (16-byte chunks in flight per lane) per workgroup of the streaming kernels.
 #ifndef MXQ_PROJ_STEPS
@@ -78,7 +79,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_DEQUANT_STEPS 2
 #endif
 #ifndef MXQ_PACKED_STEPS
-#define MXQ_PACKED_STEPS 2
+#define MXQ_PACKED_STEPS 1
 #endif
 // The banded kernels.
 #ifndef MXQ_PFOLD_ROWS
@@ -404,7 +405,7 @@ struct StepGeom {
 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict__ x, int64_t ld_x, T* __restrict__ y,
-                                                            int64_t ld_y, int64_t K, uint32_t steps_per_row,
+                                                            int64_t ld_y, int64_t K, MxqDivisor steps_per_row,
                                                             uint32_t total_steps) {
   using G = StepGeom<T, kProjThreads>;
   keep_denormals();
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict_
     const uint32_t step = blockIdx.x * kProjSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
-      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
     }
   }
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict_
   for (int u = 0; u < kProjSteps; u++) {
     const uint32_t step = blockIdx.x * kProjSteps + u;
     if (step < total_steps) {
-      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const Block b = chunk_block<T>(w[u]);
       const float s = e8m0(b.eb);
       const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
@@ -434,9 +435,10 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict_
   }
 }
 
-// A no-op flag (device memory, read once per workgroup): when it is non-zero the
-// launch leaves every output untouched, so a captured graph can replay a cached
-// update conditionally.
+// A no-op flag (device memory): when it is non-zero the launch leaves every
+// output untouched, so a captured graph can replay a cached update
+// conditionally.  Kernels read it after issuing their input loads (those only
+// read the input), so its latency overlaps theirs.
 __device__ __forceinline__ bool skipped(const int32_t* __restrict__ noop) {
   return noop != nullptr && *reinterpret_cast<const volatile int32_t*>(noop) != 0;
 }
@@ -453,11 +455,10 @@ __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __r
                                                                  uint8_t* __restrict__ data,
                                                                  uint8_t* __restrict__ scale, int64_t scale_ld,
                                                                  T* __restrict__ y, int64_t ld_y,
-                                                                 uint32_t steps_per_row, uint32_t total_steps,
+                                                                 MxqDivisor steps_per_row, uint32_t total_steps,
                                                                  const int32_t* __restrict__ noop) {
   using G = StepGeom<T, RowShape<kProj>::kTPB>;
   constexpr int kRowSteps = RowShape<kProj>::kSteps;
-  if (skipped(noop)) return;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
@@ -467,15 +468,16 @@ __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __r
     const uint32_t step = blockIdx.x * kRowSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
-      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
     }
   }
+  if (skipped(noop)) return;   // read once the input loads are in flight
 #pragma unroll
   for (int u = 0; u < kRowSteps; u++) {
     const uint32_t step = blockIdx.x * kRowSteps + u;
     if (step < total_steps) {
-      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
       const Block b = chunk_block<T>(w[u]);
       const float s = e8m0(b.eb);
@@ -522,15 +524,14 @@ template <typename T, bool VEC, bool kRow>
 __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
     const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* __restrict__ cdata,
     uint8_t* __restrict__ cscale, int64_t cscale_ld, uint8_t* __restrict__ rdata, uint8_t* __restrict__ rscale,
-    int64_t rscale_ld, uint32_t groups, const int32_t* __restrict__ noop) {
+    int64_t rscale_ld, MxqDivisor groups, const int32_t* __restrict__ noop) {
   using G = StepGeom<T>;
   constexpr int EPL = Fmt<T>::kEPL, NW = sizeof(T) == 2 ? 4 : 2;   // elements, bf16 words per chunk
   constexpr int R = kColRows;
   __shared__ uint32_t s_cmax[kColGroups > 1 ? kColGroups : 1][NW][kColThreads];
-  if (skipped(noop)) return;
   keep_denormals();
   const uint32_t lane = threadIdx.x % kColThreads, rg = threadIdx.x / kColThreads;   // rg: uniform per wave
-  const uint32_t band = blockIdx.x / groups, grp = blockIdx.x - band * groups;
+  const uint32_t band = mxq_quot(blockIdx.x, groups), grp = blockIdx.x - band * groups.d;
   const int64_t col0 = (int64_t)grp * (kColThreads * EPL) + (int64_t)lane * EPL;
   const int64_t rb = (int64_t)band * 32 + (int64_t)rg * R;   // this lane group's first row
   const bool in = col0 < K;
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
       if (r + 1 < rows) px += ld_x, r++;
     }
   }
+  if (skipped(noop)) return;   // read once the input loads are in flight (uniform: before any barrier)
 
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
   u16x2 cmax[NW];
@@ -669,20 +671,19 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
                                                             int64_t K, uint8_t* __restrict__ data,
                                                             uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                            uint32_t tiles_per_row, uint32_t groups_per_row,
+                                                            uint32_t tiles_per_row, MxqDivisor groups_per_row,
                                                             const int32_t* __restrict__ noop) {
   using G = FoldGeom<T>;
   constexpr int EPL = G::kEPL, J = G::kJ, CPT = G::kCPT, LPR = G::kLPR, P = G::kPasses;
   __shared__ uint32_t s_max[kFoldWaves][J];
-  if (skipped(noop)) return;
   keep_denormals();
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
 #if MXQ_TILE_COLUMN_MAJOR
-  const uint32_t band_count = gridDim.x / groups_per_row;
+  const uint32_t band_count = gridDim.x / groups_per_row.d;
   const uint32_t tg = blockIdx.x / band_count, tr = blockIdx.x - tg * band_count;
 #else
-  const uint32_t tr = blockIdx.x / groups_per_row, tg = blockIdx.x - tr * groups_per_row;
+  const uint32_t tr = mxq_quot(blockIdx.x, groups_per_row), tg = blockIdx.x - tr * groups_per_row.d;
 #endif
   const uint32_t j = (tid % LPR) / CPT;                    // this lane's tile within the group
   const int64_t r0 = (int64_t)tr * 128 + tid / LPR;
@@ -694,6 +695,7 @@ __global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restr
     const int64_t r = r0 + i * G::kRowsPerPass;
     w[i] = (r < rows) ? load_chunk<T, VEC>(x + r * ld_x, col0, K) : u32x4{0u, 0u, 0u, 0u};
   }
+  if (skipped(noop)) return;   // read once the input loads are in flight (uniform: before the barrier)
   uint32_t f[P], eb[P];
   uint64_t poisoned = 0u;                                  // bit i: chunk i's block is poisoned
   uint32_t m = 1u;
@@ -787,7 +789,7 @@ template <typename TO, bool kE5M2, int kLay, bool VEC>
 __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
-                                                           uint32_t steps_per_row, uint32_t total_steps) {
+                                                           MxqDivisor steps_per_row, uint32_t total_steps) {
   // 8 payload bytes per lane per step; a step is kDequantThreads * 8 elements of one row.
   keep_denormals();
   const uint32_t tid = threadIdx.x;
@@ -803,7 +805,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
     if constexpr (kLay == kLayCol) ccs[u] = u32x2{0u, 0u};
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
-    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* drow = data + (int64_t)row * K;
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
   for (int u = 0; u < kDequantSteps; u++) {
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
-    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const u32x2 q = qs[u];
@@ -898,7 +900,7 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                                   uint8_t* __restrict__ packed,
                                                                   uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                                  uint32_t steps_per_row, uint32_t total_steps) {
+                                                                  MxqDivisor steps_per_row, uint32_t total_steps) {
   using G = StepGeom<T, kRowThreads>;
   using N = typename Nibbles<T>::type;
   keep_denormals();
@@ -911,7 +913,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __
     const uint32_t step = blockIdx.x * kRowSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
-      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
     }
   }
@@ -919,7 +921,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __
   for (int u = 0; u < kRowSteps; u++) {
     const uint32_t step = blockIdx.x * kRowSteps + u;
     if (step < total_steps) {
-      const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+      const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
       const Block b = chunk_block<T, 253>(w[u]);
       const uint32_t f = b.poison ? 0u : fp4_of(w[u], e8m0(b.eb), T{});
@@ -967,7 +969,7 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
                                                                     const uint8_t* __restrict__ scale,
                                                                     int64_t scale_ld, int64_t K,
                                                                     TO* __restrict__ out, int64_t ld_out,
-                                                                    uint32_t steps_per_row, uint32_t total_steps) {
+                                                                    MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 8, pw = (K + 1) / 2;
@@ -979,7 +981,7 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
     cs[u] = 0u;
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
-    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
@@ -995,7 +997,7 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
   for (int u = 0; u < kDequantSteps; u++) {
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) break;
-    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
     if (col0 >= K) continue;
     const u32x4 o = decode8_fp4(fs[u], cs[u]);
@@ -1043,7 +1045,7 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
                                                                   int64_t scale_ld, int64_t K,
                                                                   uint8_t* __restrict__ data,
                                                                   uint8_t* __restrict__ code_out, int64_t code_ld,
-                                                                  uint32_t steps_per_row, uint32_t total_steps) {
+                                                                  MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * 16, pw = (K + 1) / 2;
@@ -1056,7 +1058,7 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
     c[u] = 0u;
     const uint32_t step = blockIdx.x * kPackedSteps + u;
     if (step >= total_steps) continue;
-    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
@@ -1072,7 +1074,7 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
   for (int u = 0; u < kPackedSteps; u++) {
     const uint32_t step = blockIdx.x * kPackedSteps + u;
     if (step >= total_steps) break;
-    const uint32_t row = step / steps_per_row, seg = step - row * steps_per_row;
+    const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
     if (col0 >= K) continue;
     u32x4 q;
@@ -1112,12 +1114,12 @@ __global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_
                                                           const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                           int64_t rows, int64_t K, uint8_t* __restrict__ data,
                                                           uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                          uint32_t groups, bool codes_vec) {
+                                                          MxqDivisor groups, bool codes_vec) {
   __shared__ uint32_t s_codes[128][4];   // the band rows' 16 block codes
   __shared__ uint32_t s_max[4][4];       // wave x tile
   keep_denormals();
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t tr = blockIdx.x / groups, tg = blockIdx.x - tr * groups;
+  const uint32_t tr = mxq_quot(blockIdx.x, groups), tg = blockIdx.x - tr * groups.d;
   const int64_t r0 = (int64_t)tr * 128, nb = (K + 31) / 32, pw = (K + 1) / 2, ntc = (K + 127) / 128;
 
   if (tid < 256u) {  // 1. block codes and tile codes (the first four waves)
@@ -1212,12 +1214,12 @@ __global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_
 // ------------------------------------------------------------------------------------
 template <typename V>
 __global__ __launch_bounds__(kThreads) void export_kernel(const uint8_t* __restrict__ src, int64_t src_ld,
-                                                          uint8_t* __restrict__ dst, uint32_t units_per_row,
+                                                          uint8_t* __restrict__ dst, MxqDivisor units_per_row,
                                                           uint32_t total_units) {
   // one V-sized unit per lane, rows flattened, so short rows still fill whole waves
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= total_units) return;
-  const uint32_t r = i / units_per_row, j = i - r * units_per_row;
+  const uint32_t r = mxq_quot(i, units_per_row), j = i - r * units_per_row.d;
   reinterpret_cast<V*>(dst)[i] = reinterpret_cast<const V*>(src + (int64_t)r * src_ld)[j];
 }
 
@@ -1245,10 +1247,10 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
-int steps_for(int64_t rows, int64_t K, int64_t elems_per_step, uint32_t* per_row, uint32_t* total) {
+int steps_for(int64_t rows, int64_t K, int64_t elems_per_step, MxqDivisor* per_row, uint32_t* total) {
   const int64_t spr = (K + elems_per_step - 1) / elems_per_step;
   if (rows > kMaxSteps / spr) return MXQ_ERR_SHAPE;
-  *per_row = (uint32_t)spr;
+  *per_row = mxq_divisor((uint32_t)spr);
   *total = (uint32_t)(rows * spr);
   return MXQ_OK;
 }
@@ -1262,7 +1264,8 @@ size_t dtype_size(mxq_dtype dt) { return dt == MXQ_BF16 ? 2 : 4; }
 
 template <typename T>
 int launch_proj(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows, int64_t K, hipStream_t s) {
-  uint32_t spr, total;
+  MxqDivisor spr;
+  uint32_t total;
   if (steps_for(rows, K, StepGeom<T, kProjThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && aligned(y, 16) && ld_x % EPL == 0 && ld_y % EPL == 0 && K % EPL == 0 &&
@@ -1280,7 +1283,8 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
                int64_t scale_ld, void* y, int64_t ld_y, const int32_t* noop, hipStream_t s) {
   const bool fused = y != nullptr;
   const int tpb = fused ? kFusedThreads : kRowThreads, steps = fused ? kFusedSteps : kRowSteps;
-  uint32_t spr, total;
+  MxqDivisor spr;
+  uint32_t total;
   if (steps_for(rows, K, (int64_t)(tpb / Fmt<T>::kLPB) * 32, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
@@ -1311,7 +1315,7 @@ int launch_col(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* cd
   const dim3 grid((uint32_t)(bands * groups)), block(kColThreads * kColGroups);
 #define MXQ_COL_LAUNCH(V, R)                                                                                    \
   hipLaunchKernelGGL((col_kernel<T, V, R>), grid, block, 0, s, (const T*)x, ld_x, rows, K, cdata, cscale, cscale_ld, \
-                     rdata, rscale, rscale_ld, (uint32_t)groups, noop)
+                     rdata, rscale, rscale_ld, mxq_divisor((uint32_t)groups), noop)
   if (rdata != nullptr) {
     if (vec) MXQ_COL_LAUNCH(true, true); else MXQ_COL_LAUNCH(false, true);
   } else {
@@ -1332,17 +1336,18 @@ int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_
   const dim3 grid((uint32_t)groups), block(kFoldThreads);
   if (vec)
     hipLaunchKernelGGL((block128_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data, tile_code,
-                       tile_ld, (uint32_t)tpr, (uint32_t)gpr, noop);
+                       tile_ld, (uint32_t)tpr, mxq_divisor((uint32_t)gpr), noop);
   else
     hipLaunchKernelGGL((block128_kernel<T, false>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data, tile_code,
-                       tile_ld, (uint32_t)tpr, (uint32_t)gpr, noop);
+                       tile_ld, (uint32_t)tpr, mxq_divisor((uint32_t)gpr), noop);
   return launch_status();
 }
 
 template <typename TO, bool kE5M2, int kLay>
 int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K, void* out,
                      int64_t ld_out, hipStream_t s) {
-  uint32_t spr, total;
+  MxqDivisor spr;
+  uint32_t total;
   if (steps_for(rows, K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
   const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0 &&
@@ -1377,7 +1382,8 @@ int launch_dequant(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
 template <typename T>
 int launch_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scale,
                           int64_t scale_ld, hipStream_t s) {
-  uint32_t spr, total;
+  MxqDivisor spr;
+  uint32_t total;
   if (steps_for(rows, K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(packed, EPL / 2);
@@ -1394,7 +1400,8 @@ int launch_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, 
 template <typename TO>
 int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                             void* out, int64_t ld_out, hipStream_t s) {
-  uint32_t spr, total;
+  MxqDivisor spr;
+  uint32_t total;
   if (steps_for(rows, K, kDq4Threads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);
   const bool vec = aligned(packed, 4) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
@@ -1576,7 +1583,8 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
   const int64_t units = rows * (nb / width);
   if (units >= kMaxSteps * 2) return MXQ_ERR_SHAPE;
   const dim3 grid((uint32_t)((units + kThreads - 1) / kThreads)), block(kThreads);
-  const uint32_t upr = (uint32_t)(nb / width), total = (uint32_t)units;
+  const MxqDivisor upr = mxq_divisor((uint32_t)(nb / width));
+  const uint32_t total = (uint32_t)units;
   if (width == 16)
     hipLaunchKernelGGL(export_kernel<u32x4>, grid, block, 0, stream, scale_storage, scale_ld, scale_out, upr, total);
   else if (width == 4)
@@ -1648,7 +1656,8 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
   const Range rp = matrix_range(packed, rows, pw, pw, 1), rs = matrix_range(scale, rows, nb, scale_ld, 1),
               rd = matrix_range(data, rows, K, K, 1), ro = matrix_range(scale_out, rows, nb, scale_out_ld, 1);
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(ro, rp) || overlap(ro, rs) || overlap(rd, ro)) return MXQ_ERR_ALIAS;
-  uint32_t spr, total;
+  MxqDivisor spr;
+  uint32_t total;
   if (steps_for(rows, K, kPackedThreads * 16, &spr, &total)) return MXQ_ERR_SHAPE;
   const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
   const dim3 grid(grid_for(total, kPackedSteps)), block(kPackedThreads);
@@ -1680,10 +1689,10 @@ int mxq_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale
   const dim3 grid((uint32_t)(ntr * groups)), block(kPFoldThreads);
   if (vec)
     hipLaunchKernelGGL((packed_fold_kernel<true>), grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
-                       tile_code, tile_ld, (uint32_t)groups, codes_vec);
+                       tile_code, tile_ld, mxq_divisor((uint32_t)groups), codes_vec);
   else
     hipLaunchKernelGGL((packed_fold_kernel<false>), grid, block, 0, stream, packed, scale, scale_ld, rows, K, data,
-                       tile_code, tile_ld, (uint32_t)groups, codes_vec);
+                       tile_code, tile_ld, mxq_divisor((uint32_t)groups), codes_vec);
   return launch_status();
 }
 
