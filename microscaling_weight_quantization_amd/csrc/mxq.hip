@@ -1109,6 +1109,18 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
 //  2. Lane t converts 16 elements (8 packed bytes -> 16 payload bytes) of R
 //     band rows, t / 32 + (128 / R) k, at the shift e - S of its block and
 //     tile; all R loads are issued first.  Poisoned blocks (code 255) get 0x7F.
+// Workgroup order for the fold from packed.  The hardware deals workgroups
+// round-robin over the 8 XCDs (b runs on XCD b % 8), each with its own L2.
+// Neighbouring workgroups of a band read neighbouring 16-byte pieces of the
+// same 128-byte lines of block codes, so within every window of 64 workgroups
+// XCD x takes work items 8x .. 8x+7: the eight that share those lines meet in
+// one L2.  A transpose of each 8 x 8 window, so a bijection; a last partial
+// window keeps the plain order.
+__device__ __forceinline__ uint32_t xcd_window_order(uint32_t b, uint32_t n) {
+  if (b >= (n & ~63u)) return b;
+  return (b & ~63u) | ((b & 7u) << 3) | ((b >> 3) & 7u);
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scale, int64_t scale_ld,
@@ -1119,7 +1131,8 @@ __global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_
   __shared__ uint32_t s_max[4][4];       // wave x tile
   keep_denormals();
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t tr = mxq_quot(blockIdx.x, groups), tg = blockIdx.x - tr * groups.d;
+  const uint32_t wb = xcd_window_order(blockIdx.x, gridDim.x);
+  const uint32_t tr = mxq_quot(wb, groups), tg = wb - tr * groups.d;
   const int64_t r0 = (int64_t)tr * 128, nb = (K + 31) / 32, pw = (K + 1) / 2, ntc = (K + 127) / 128;
 
   if (tid < 256u) {  // 1. block codes and tile codes (the first four waves)

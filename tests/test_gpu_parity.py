@@ -326,6 +326,17 @@ def test_packed_ragged(dev, K, dtype):
     check_packed(np.ascontiguousarray(flat[: rows * K].reshape(rows, K)), dev, scale_ld=(K + 31) // 32 + 1)
 
 
+@pytest.mark.parametrize("name", ["normal", "normal_elementwise", "spread"])
+def test_packed_fold_partial_window(dev, name):
+    """The fold from packed reorders its workgroups within whole windows of 64;
+    these grids hold several whole windows and a partial last one (and ragged
+    bands), so every work item must still be done exactly once."""
+    bits = {"normal": lambda: W.c4_headline(seed=11, shape=(2951, 4608)),              # 24 bands x 9 groups = 216
+            "normal_elementwise": lambda: W.c4_headline(seed=12, shape=(2951, 4500)),  # K % 16 != 0: 24 x 9 = 216
+            "spread": lambda: W.c3_spread(seed=13, shape=(2944, 4608))}[name]()       # 23 x 9 = 207
+    check_packed(bits, dev)
+
+
 # ------------------------------------------------------------------ invariants on the device
 
 def test_decode_of_row_is_projection_c4(dev):
