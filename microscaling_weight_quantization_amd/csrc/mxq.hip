@@ -483,7 +483,8 @@ __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __r
       const float s = e8m0(b.eb);
       const uint32_t code = row_code(b);
       const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
-      if constexpr (kProj) store_chunk<T, VEC>(y + (int64_t)row * ld_y, col0, K, proj_chunk<T>(p, b.poison));
+      // the projection output goes out like the projection kernel's (nt sc1 buffer stores)
+      if constexpr (kProj) store_chunk<T, VEC, true>(y + (int64_t)row * ld_y, col0, K, proj_chunk<T>(p, b.poison));
       store_payload<T, VEC>(data + (int64_t)row * K, col0, K, payload_chunk<T>(p, code, b.poison));
       if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)code;
     }
@@ -1301,7 +1302,7 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
   if (steps_for(rows, K, (int64_t)(tpb / Fmt<T>::kLPB) * 32, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
-                   (!fused || (aligned(y, 16) && ld_y % EPL == 0));
+                   (!fused || (aligned(y, 16) && ld_y % EPL == 0 && fits32(K * (int64_t)sizeof(T))));
   const dim3 grid(grid_for(total, steps)), block(tpb);
 #define MXQ_ROW_LAUNCH(V, P)                                                                                  \
   hipLaunchKernelGGL((row_kernel<T, V, P>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \

@@ -450,7 +450,7 @@ def test_build_variants_identical_bits(dev, variant):
 def test_row_longer_than_2gb(dev):
     """Maximum-size edge: one bf16 row of 2^30 + 48 elements (2 GB + 96 bytes,
     beyond the 32-bit byte offsets of the vectorised projection store), so the
-    projection and the row lift take their element-wise paths.  Compared on
+    projection and the fused pass take their element-wise paths.  Compared on
     sampled blocks: the start, the blocks around the 2^30-element (2^31-byte)
     mark, and the partial last block."""
     K = (1 << 30) + 48
@@ -466,5 +466,16 @@ def test_row_longer_than_2gb(dev):
         wd, ws = oracle.mxfp4_to_mxfp8_row(sub)
         assert_bits(to_host(data[:, c0:c1]), wd, f"row payload [{c0}, {c1})")
         assert_bits(to_host(scale[:, c0 // 32:(c1 + 31) // 32]), ws, f"row codes [{c0}, {c1})")
+    del y, data, scale
+    torch.cuda.empty_cache()
+    # the fused pass, whose projection stores share the 32-bit offset limit
+    y, data, scale = mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x)
+    torch.cuda.synchronize()
+    for c0, c1 in ((0, 4096), ((1 << 30) - 2048, (1 << 30) + 2048), (K - 4096 - 16, K)):
+        sub = np.ascontiguousarray(bits[:, c0:c1])
+        assert_bits(to_host(y[:, c0:c1]), oracle.fake_quantize_mxfp4(sub), f"fused projection [{c0}, {c1})")
+        wd, ws = oracle.mxfp4_to_mxfp8_row(sub)
+        assert_bits(to_host(data[:, c0:c1]), wd, f"fused row payload [{c0}, {c1})")
+        assert_bits(to_host(scale[:, c0 // 32:(c1 + 31) // 32]), ws, f"fused row codes [{c0}, {c1})")
     del x, y, data, scale
     torch.cuda.empty_cache()
