@@ -19,7 +19,7 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(os.path.dirname(HERE), "microscaling_weight_quantization_amd", "csrc")
 
-DRIVER = r"""
+CHECK_PROGRAM = r"""
 #include <stdint.h>
 #include <stdio.h>
 #include "fastdiv.h"
@@ -93,7 +93,7 @@ def _build(tmp_path):
     if cxx is None:
         pytest.skip("no host C++ compiler")
     src = tmp_path / "fastdiv_check.cpp"
-    src.write_text(DRIVER)
+    src.write_text(CHECK_PROGRAM)
     exe = tmp_path / "fastdiv_check"
     subprocess.check_call([cxx, "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)])
     return str(exe)
@@ -123,7 +123,7 @@ def test_mutated_multiplier_is_caught(tmp_path):
     assert mutated != hdr
     (tmp_path / "fastdiv.h").write_text(mutated)
     src = tmp_path / "fastdiv_check.cpp"
-    src.write_text(DRIVER)
+    src.write_text(CHECK_PROGRAM)
     exe = tmp_path / "fastdiv_check"
     subprocess.check_call([cxx, "-O2", "-std=c++17", "-I", str(tmp_path), str(src), "-o", str(exe)])
     out = subprocess.run([str(exe)], capture_output=True, text=True)
