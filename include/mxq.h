@@ -72,7 +72,9 @@ typedef enum { MXQ_SCALE_ROW_1X32 = 0, MXQ_SCALE_TILE_128X128 = 1, MXQ_SCALE_COL
 enum {
   MXQ_OK = 0,
   MXQ_ERR_NULL = 1,             /* a required pointer is NULL (non-empty shape) */
-  MXQ_ERR_SHAPE = 2,            /* negative dims, ld < K, scale_ld / tile_ld too small, or too large */
+  MXQ_ERR_SHAPE = 2,            /* negative dims, ld < K, scale_ld / tile_ld too small, too many steps
+                                   for one launch, or a matrix spanning 2^56 bytes or more (or past the
+                                   end of the address space) */
   MXQ_ERR_DTYPE = 3,            /* fp16 or an unknown dtype / format / layout */
   MXQ_ERR_NO_ROWWISE_DATA = 4,  /* export without payload or scale storage ([EXP]: ValueError) */
   MXQ_ERR_ALIAS = 5,            /* an output overlaps an input (other than the allowed exact in-place) */

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <initializer_list>
 
 #include "mxq.h"
 #include "fastdiv.h"
@@ -1231,8 +1232,9 @@ __global__ __launch_bounds__(kThreads) void export_kernel(const uint8_t* __restr
                                                           uint8_t* __restrict__ dst, MxqDivisor units_per_row,
                                                           uint32_t total_units) {
   // one V-sized unit per lane, rows flattened, so short rows still fill whole waves
-  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= total_units) return;
+  const uint64_t i64 = (uint64_t)blockIdx.x * kThreads + threadIdx.x;   // the last group may pass 2^32
+  if (i64 >= total_units) return;
+  const uint32_t i = (uint32_t)i64;
   const uint32_t r = mxq_quot(i, units_per_row), j = i - r * units_per_row.d;
   reinterpret_cast<V*>(dst)[i] = reinterpret_cast<const V*>(src + (int64_t)r * src_ld)[j];
 }
@@ -1247,13 +1249,25 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // longer rows take the element-wise path.
 bool fits32(int64_t bytes) { return bytes < ((int64_t)1 << 31); }
 
-// Byte range [lo, hi) of a [rows, cols] matrix with row stride ld elements of esize.
+// Byte range [lo, hi) of a [rows, cols] matrix (rows, cols >= 1) with row
+// stride ld elements of esize bytes.  ok is false when that span cannot be a
+// real allocation -- 2^56 bytes or more, or running past the end of the address
+// space -- so that no later size arithmetic can overflow; the entry points
+// reject such shapes with MXQ_ERR_SHAPE before any other use of the range.
 struct Range {
   uintptr_t lo, hi;
+  bool ok;
 };
 Range matrix_range(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t esize) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Range{lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * (int64_t)esize)};
+  const __int128 span = ((__int128)(rows - 1) * ld + cols) * (__int128)esize;
+  const bool ok = span > 0 && span < ((__int128)1 << 56) && (unsigned __int128)lo + span <= UINTPTR_MAX;
+  return Range{lo, ok ? lo + (uintptr_t)span : lo, ok};
+}
+bool spans_ok(std::initializer_list<Range> rs) {
+  for (const Range& r : rs)
+    if (!r.ok) return false;
+  return true;
 }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
@@ -1455,8 +1469,9 @@ int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y, 
   if (ld_x < K || ld_y < K) return MXQ_ERR_SHAPE;
   const size_t es = dtype_size(dt);
   const bool in_place = (x == y) && (ld_x == ld_y);
-  if (!in_place && overlap(matrix_range(x, rows, K, ld_x, es), matrix_range(y, rows, K, ld_y, es)))
-    return MXQ_ERR_ALIAS;
+  const Range rx = matrix_range(x, rows, K, ld_x, es), ry = matrix_range(y, rows, K, ld_y, es);
+  if (!spans_ok({rx, ry})) return MXQ_ERR_SHAPE;
+  if (!in_place && overlap(rx, ry)) return MXQ_ERR_ALIAS;
   return dt == MXQ_BF16 ? launch_proj<uint16_t>(x, ld_x, y, ld_y, rows, K, stream)
                         : launch_proj<uint32_t>(x, ld_x, y, ld_y, rows, K, stream);
 }
@@ -1473,9 +1488,11 @@ static int row_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_d
   const size_t es = dtype_size(dt);
   const Range rx = matrix_range(x, rows, K, ld_x, es), rd = matrix_range(data, rows, K, K, 1),
               rs = matrix_range(scale, rows, nb, scale_ld, 1);
+  if (!spans_ok({rx, rd, rs})) return MXQ_ERR_SHAPE;
   if (overlap(rx, rd) || overlap(rx, rs) || overlap(rd, rs)) return MXQ_ERR_ALIAS;
   if (y) {
     const Range ry = matrix_range(y, rows, K, ld_y, es);
+    if (!ry.ok) return MXQ_ERR_SHAPE;
     const bool in_place = (x == y) && (ld_x == ld_y);
     if ((!in_place && overlap(rx, ry)) || overlap(ry, rd) || overlap(ry, rs)) return MXQ_ERR_ALIAS;
   }
@@ -1494,6 +1511,7 @@ static int block128_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, 
   if (ld_x < K || tile_ld < ntc) return MXQ_ERR_SHAPE;
   const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), rd = matrix_range(data, rows, K, K, 1),
               rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
+  if (!spans_ok({rx, rd, rt})) return MXQ_ERR_SHAPE;
   if (overlap(rx, rd) || overlap(rx, rt) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
   return dt == MXQ_BF16 ? launch_block128<uint16_t>(x, ld_x, rows, K, data, tile_code, tile_ld, noop, stream)
                         : launch_block128<uint32_t>(x, ld_x, rows, K, data, tile_code, tile_ld, noop, stream);
@@ -1539,9 +1557,11 @@ static int col_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_d
   if (ld_x < K || col_scale_ld < K || (with_row && row_scale_ld < nb)) return MXQ_ERR_SHAPE;
   const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), cd = matrix_range(col_data, rows, K, K, 1),
               cs = matrix_range(col_scale, bands, K, col_scale_ld, 1);
+  if (!spans_ok({rx, cd, cs})) return MXQ_ERR_SHAPE;
   if (overlap(rx, cd) || overlap(rx, cs) || overlap(cd, cs)) return MXQ_ERR_ALIAS;
   if (with_row) {
     const Range rd = matrix_range(row_data, rows, K, K, 1), rs = matrix_range(row_scale, rows, nb, row_scale_ld, 1);
+    if (!spans_ok({rd, rs})) return MXQ_ERR_SHAPE;
     if (overlap(rx, rd) || overlap(rx, rs) || overlap(rd, rs) || overlap(rd, cd) || overlap(rd, cs) ||
         overlap(rs, cd) || overlap(rs, cs))
       return MXQ_ERR_ALIAS;
@@ -1589,8 +1609,9 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
   if (scale_ld < nb) return MXQ_ERR_SHAPE;
   if (!scale_out) return MXQ_ERR_NULL;
   if (scale_out == scale_storage && scale_ld == nb) return MXQ_OK;          // already unpadded: a view
-  if (overlap(matrix_range(scale_storage, rows, nb, scale_ld, 1), matrix_range(scale_out, rows, nb, nb, 1)))
-    return MXQ_ERR_ALIAS;
+  const Range rs = matrix_range(scale_storage, rows, nb, scale_ld, 1), ro = matrix_range(scale_out, rows, nb, nb, 1);
+  if (!spans_ok({rs, ro})) return MXQ_ERR_SHAPE;
+  if (overlap(rs, ro)) return MXQ_ERR_ALIAS;
   const uintptr_t a = reinterpret_cast<uintptr_t>(scale_storage) | reinterpret_cast<uintptr_t>(scale_out);
   const int64_t width = (a % 16 == 0 && scale_ld % 16 == 0 && nb % 16 == 0) ? 16
                         : (a % 4 == 0 && scale_ld % 4 == 0 && nb % 4 == 0) ? 4 : 1;
@@ -1622,9 +1643,10 @@ int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
   const int64_t srows = tile ? (rows + 127) / 128 : col ? (rows + 31) / 32 : rows,
                 scols = tile ? (K + 127) / 128 : col ? K : (K + 31) / 32;
   if (ld_out < K || scale_ld < scols) return MXQ_ERR_SHAPE;
-  const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt));
-  if (overlap(ro, matrix_range(data, rows, K, K, 1)) || overlap(ro, matrix_range(scale, srows, scols, scale_ld, 1)))
-    return MXQ_ERR_ALIAS;
+  const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt)), rd = matrix_range(data, rows, K, K, 1),
+              rs = matrix_range(scale, srows, scols, scale_ld, 1);
+  if (!spans_ok({ro, rd, rs})) return MXQ_ERR_SHAPE;
+  if (overlap(ro, rd) || overlap(ro, rs)) return MXQ_ERR_ALIAS;
   return out_dt == MXQ_BF16 ? launch_dequant<uint16_t>(data, scale, scale_ld, rows, K, fmt, layout, out, ld_out, stream)
                             : launch_dequant<uint32_t>(data, scale, scale_ld, rows, K, fmt, layout, out, ld_out, stream);
 }
@@ -1639,6 +1661,7 @@ int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq
   if (ld_x < K || scale_ld < nb) return MXQ_ERR_SHAPE;
   const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), rp = matrix_range(packed, rows, pw, pw, 1),
               rs = matrix_range(scale, rows, nb, scale_ld, 1);
+  if (!spans_ok({rx, rp, rs})) return MXQ_ERR_SHAPE;
   if (overlap(rx, rp) || overlap(rx, rs) || overlap(rp, rs)) return MXQ_ERR_ALIAS;
   return dt == MXQ_BF16 ? launch_quantize_mxfp4<uint16_t>(x, ld_x, rows, K, packed, scale, scale_ld, stream)
                         : launch_quantize_mxfp4<uint32_t>(x, ld_x, rows, K, packed, scale, scale_ld, stream);
@@ -1652,9 +1675,10 @@ int mxq_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t sc
   if (!packed || !scale || !out) return MXQ_ERR_NULL;
   const int64_t nb = (K + 31) / 32, pw = (K + 1) / 2;
   if (ld_out < K || scale_ld < nb) return MXQ_ERR_SHAPE;
-  const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt));
-  if (overlap(ro, matrix_range(packed, rows, pw, pw, 1)) || overlap(ro, matrix_range(scale, rows, nb, scale_ld, 1)))
-    return MXQ_ERR_ALIAS;
+  const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt)), rp = matrix_range(packed, rows, pw, pw, 1),
+              rs = matrix_range(scale, rows, nb, scale_ld, 1);
+  if (!spans_ok({ro, rp, rs})) return MXQ_ERR_SHAPE;
+  if (overlap(ro, rp) || overlap(ro, rs)) return MXQ_ERR_ALIAS;
   return out_dt == MXQ_BF16 ? launch_dequantize_mxfp4<uint16_t>(packed, scale, scale_ld, rows, K, out, ld_out, stream)
                             : launch_dequantize_mxfp4<uint32_t>(packed, scale, scale_ld, rows, K, out, ld_out, stream);
 }
@@ -1669,6 +1693,7 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
   if (scale_ld < nb || scale_out_ld < nb) return MXQ_ERR_SHAPE;
   const Range rp = matrix_range(packed, rows, pw, pw, 1), rs = matrix_range(scale, rows, nb, scale_ld, 1),
               rd = matrix_range(data, rows, K, K, 1), ro = matrix_range(scale_out, rows, nb, scale_out_ld, 1);
+  if (!spans_ok({rp, rs, rd, ro})) return MXQ_ERR_SHAPE;
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(ro, rp) || overlap(ro, rs) || overlap(rd, ro)) return MXQ_ERR_ALIAS;
   MxqDivisor spr;
   uint32_t total;
@@ -1694,6 +1719,7 @@ int mxq_mxfp4_packed_to_fp8_block128(const uint8_t* packed, const uint8_t* scale
   if (scale_ld < nb || tile_ld < ntc) return MXQ_ERR_SHAPE;
   const Range rp = matrix_range(packed, rows, pw, pw, 1), rs = matrix_range(scale, rows, nb, scale_ld, 1),
               rd = matrix_range(data, rows, K, K, 1), rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
+  if (!spans_ok({rp, rs, rd, rt})) return MXQ_ERR_SHAPE;
   if (overlap(rd, rp) || overlap(rd, rs) || overlap(rt, rp) || overlap(rt, rs) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
   if (ntc * ntr >= kMaxSteps) return MXQ_ERR_SHAPE;
   const int64_t groups = (ntc + 3) / 4;

@@ -131,6 +131,38 @@ def test_host_validation_without_a_gpu(lib):
                                          None) == mxq.MXQ_ERR_SHAPE
 
 
+def test_absurd_strides_are_rejected(lib):
+    """A matrix whose byte span could not be an allocation (2^56 bytes or more,
+    or past the end of the address space) is a shape error, found before any
+    range arithmetic can overflow -- including the in-place projection, which
+    has no alias check to trip over."""
+    P = ctypes.c_void_p
+    fake, far = P(0x100000), lambda k: P(1 << k)
+    S = mxq.MXQ_ERR_SHAPE
+    big = 1 << 62
+    assert lib.mxq_fake_quantize_mxfp4(fake, big, fake, big, 4, 64, 0, None) == S           # in place
+    assert lib.mxq_fake_quantize_mxfp4(fake, 64, far(50), big, 4, 64, 0, None) == S
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, big, 4, 64, 0, far(50), far(52), 2, None) == S
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, 0, far(50), far(52), big, None) == S
+    assert lib.mxq_fake_quantize_mxfp4_with_mxfp8_row(fake, 64, far(48), big, 4, 64, 0, far(50), far(52), 2,
+                                                      None) == S
+    assert lib.mxq_mxfp4_to_fp8_block128(fake, big, 4, 256, 0, far(50), far(52), 2, None) == S
+    assert lib.mxq_mxfp4_to_mxfp8_col(fake, big, 40, 64, 0, far(50), far(52), 64, None) == S
+    assert lib.mxq_mxfp4_to_mxfp8_row_col(fake, 64, 40, 64, 0, far(50), far(52), big, far(54), far(55), 64,
+                                          None) == S
+    assert lib.mxq_export_mxfp8(far(50), fake, 4, 64, 1 << 58, far(52), None) == S
+    assert lib.mxq_dequantize(fake, far(50), 2, 4, 64, 0, 0, far(52), big, mxq.MXQ_BF16, None) == S
+    assert lib.mxq_quantize_mxfp4(fake, 64, 4, 64, 0, far(50), far(52), big, None) == S
+    assert lib.mxq_dequantize_mxfp4(fake, far(50), big, 4, 64, far(52), 64, 0, None) == S
+    assert lib.mxq_mxfp4_packed_to_mxfp8_row(fake, far(50), big, 4, 64, far(52), far(54), 2, None) == S
+    # (two tile rows, so the tile-code stride matters)
+    assert lib.mxq_mxfp4_packed_to_fp8_block128(fake, far(50), 2, 256, 64, far(52), far(54), big, None) == S
+    # a buffer running past the top of the address space
+    top = P((1 << 64) - 4096)
+    assert lib.mxq_fake_quantize_mxfp4(top, 64, top, 64, 64, 64, 0, None) == S
+    assert lib.mxq_mxfp4_to_mxfp8_row(fake, 64, 4, 64, 0, P((1 << 64) - 128), far(52), 2, None) == S   # 256 B payload
+
+
 def test_binding_raises_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "library_path", lambda name="libmxq.so": str(tmp_path / name))
     with pytest.raises(FileNotFoundError):
