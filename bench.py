@@ -349,7 +349,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int16",
+        # the path is integer work on the weight's 16-bit patterns (amax, exponent
+        # fields), with the E2M1 / E4M3 encodes done by the hardware conversions
+        "dtype": "u16",
         "data": "synthetic",
         "config": {"workload": "8192x8192 bf16 weight, N(0,0.02) seed 1: proj + row (scale_ld 260) + export "
                                "+ block128 + decode(row) + decode(tile)",
