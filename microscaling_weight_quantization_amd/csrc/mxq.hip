@@ -793,17 +793,26 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
                                                            MxqDivisor steps_per_row, uint32_t total_steps) {
   // 8 payload bytes per lane per step; a step is kDequantThreads * 8 elements of one row.
+  // Lane geometry: bf16 output takes 8 consecutive elements per lane (one 16-byte
+  // store).  fp32 output (kSplit) takes two groups of 4, half a step apart, so
+  // that each of the lane's two 16-byte stores is part of one contiguous
+  // 64 x 16-byte store of the wave: two adjacent 16-byte stores per lane cover
+  // only half lines per instruction and run far slower.
+  constexpr bool kSplit = sizeof(TO) == 4;
+  constexpr int64_t kHalf = (int64_t)kDequantThreads * 4;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
-  const int64_t lane_col = (int64_t)tid * 8;
+  const int64_t lane_col = (int64_t)tid * (kSplit ? 4 : 8);
   // All of the workgroup's loads are issued before any decode or store.
-  u32x2 qs[kDequantSteps];
+  u32x2 qs[kDequantSteps];                                  // kSplit: [0] the first group's 4 bytes, [1] the second's
   uint32_t cs[kDequantSteps];                               // the step's code (row, tile layouts)
+  uint32_t cs_b[kSplit ? kDequantSteps : 1];                // kSplit: the second group's code
   u32x2 ccs[kLay == kLayCol ? kDequantSteps : 1];           // the 8 columns' codes (column layout)
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     qs[u] = u32x2{0u, 0u};
     cs[u] = 0u;
+    if constexpr (kSplit) cs_b[u] = 0u;
     if constexpr (kLay == kLayCol) ccs[u] = u32x2{0u, 0u};
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
@@ -811,6 +820,34 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* drow = data + (int64_t)row * K;
+    if constexpr (kSplit) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int64_t c = col0 + h * kHalf;
+        if (c >= K) continue;
+        if (VEC) {
+          qs[u][h] = stream_load(reinterpret_cast<const uint32_t*>(drow + c));
+        } else {
+          for (int i = 0; i < 4; i++)
+            if (c + i < K) qs[u][h] |= (uint32_t)drow[c + i] << (8 * i);
+        }
+        if constexpr (kLay == kLayCol) {
+          const uint8_t* srow = scale + (int64_t)(row / 32) * scale_ld;
+          if (VEC) {
+            ccs[u][h] = *reinterpret_cast<const uint32_t*>(srow + c);
+          } else {
+            for (int i = 0; i < 4; i++)
+              if (c + i < K) ccs[u][h] |= (uint32_t)srow[c + i] << (8 * i);
+          }
+        } else {
+          const uint32_t code = kLay == kLayTile ? scale[(int64_t)(row / 128) * scale_ld + c / 128]
+                                                 : scale[(int64_t)row * scale_ld + c / 32];
+          if (h == 0) cs[u] = code;
+          else cs_b[u] = code;
+        }
+      }
+      continue;
+    }
     if (VEC) {
       qs[u] = stream_load(reinterpret_cast<const u32x2*>(drow + col0));
     } else {
@@ -842,10 +879,12 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       if constexpr (kLay == kLayCol) s8[i] = e8m0((ccs[u][i / 4] >> (8 * (i % 4))) & 0xFFu);
+      else if constexpr (kSplit) s8[i] = e8m0(i < 4 ? cs[u] : cs_b[u]);
       else s8[i] = e8m0(cs[u]);
     }
     const float s = s8[0];
-    const bool fix_nan = kLay == kLayCol || cs[u] == 255u || has_nan_byte<kE5M2>(q);
+    bool fix_nan = kLay == kLayCol || cs[u] == 255u || has_nan_byte<kE5M2>(q);
+    if constexpr (kSplit) fix_nan = fix_nan || cs_b[u] == 255u;
     TO* orow = out + (int64_t)row * ld_out;
     if constexpr (sizeof(TO) == 2) {
       u32x4 o = kLay == kLayCol ? decode8_bf16_each<kE5M2>(q, s8) : decode8_bf16<kE5M2>(q, s);
@@ -872,12 +911,15 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
         for (int i = 0; i < 8; i++)
           if ((f[i] & 0x7FFFFFFFu) > 0x7F800000u) f[i] = 0x7FC00000u;
       }
+      // the two groups: elements col0 .. col0+3 and col0+kHalf .. col0+kHalf+3
       if (VEC) {
         stream_store(u32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<u32x4*>(orow + col0));
-        stream_store(u32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<u32x4*>(orow + col0 + 4));
+        if (col0 + kHalf < K) stream_store(u32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<u32x4*>(orow + col0 + kHalf));
       } else {
-        for (int i = 0; i < 8; i++)
-          if (col0 + i < K) orow[col0 + i] = f[i];
+        for (int i = 0; i < 8; i++) {
+          const int64_t c = col0 + (i < 4 ? i : kHalf + i - 4);
+          if (c < K) orow[c] = f[i];
+        }
       }
     }
   }
@@ -972,21 +1014,47 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
                                                                     int64_t scale_ld, int64_t K,
                                                                     TO* __restrict__ out, int64_t ld_out,
                                                                     MxqDivisor steps_per_row, uint32_t total_steps) {
+  // Lane geometry as in the FP8 decode: bf16 output takes 8 consecutive
+  // elements (4 packed bytes) per lane; fp32 output (kSplit) takes two groups of
+  // 4 (2 packed bytes each) half a step apart, so each 16-byte store of the lane
+  // is part of one contiguous store of the wave.
+  constexpr bool kSplit = sizeof(TO) == 4;
+  constexpr int64_t kHalf = (int64_t)kDq4Threads * 4;
   keep_denormals();
   const uint32_t tid = threadIdx.x;
-  const int64_t lane_col = (int64_t)tid * 8, pw = (K + 1) / 2;
+  const int64_t lane_col = (int64_t)tid * (kSplit ? 4 : 8), pw = (K + 1) / 2;
   // All of the workgroup's loads are issued before any decode or store.
   uint32_t fs[kDequantSteps], cs[kDequantSteps];
+  uint32_t fs_b[kSplit ? kDequantSteps : 1], cs_b[kSplit ? kDequantSteps : 1];   // kSplit: the second group
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     fs[u] = 0u;
     cs[u] = 0u;
+    if constexpr (kSplit) fs_b[u] = 0u, cs_b[u] = 0u;
     const uint32_t step = blockIdx.x * kDequantSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
     if (col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
+    if constexpr (kSplit) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int64_t c = col0 + h * kHalf;
+        if (c >= K) continue;
+        uint32_t f = 0u;
+        if (VEC) {
+          f = stream_load(reinterpret_cast<const uint16_t*>(prow + c / 2));
+        } else {
+          for (int i = 0; i < 4; i += 2)
+            if (c + i < K) f |= (uint32_t)prow[(c + i) / 2] << (4 * i);
+        }
+        const uint32_t code = scale[(int64_t)row * scale_ld + c / 32];
+        if (h == 0) fs[u] = f, cs[u] = code;
+        else fs_b[u] = f, cs_b[u] = code;
+      }
+      continue;
+    }
     if (VEC) {
       fs[u] = stream_load(reinterpret_cast<const uint32_t*>(prow + col0 / 2));
     } else {
@@ -1002,8 +1070,27 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
     if (col0 >= K) continue;
-    const u32x4 o = decode8_fp4(fs[u], cs[u]);
     TO* orow = out + (int64_t)row * ld_out;
+    if constexpr (kSplit) {
+      // each group's 4 nibbles decode through the bf16 path (exact), then widen
+      const u32x4 oa = decode8_fp4(fs[u], cs[u]), ob = decode8_fp4(fs_b[u], cs_b[u]);
+      const uint32_t h4[8] = {oa[0] & 0xFFFFu, oa[0] >> 16, oa[1] & 0xFFFFu, oa[1] >> 16,
+                              ob[0] & 0xFFFFu, ob[0] >> 16, ob[1] & 0xFFFFu, ob[1] >> 16};
+      uint32_t fo[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) fo[i] = (h4[i] & 0x7FFFu) > 0x7F80u ? 0x7FC00000u : h4[i] << 16;   // exact
+      if (VEC) {
+        stream_store(u32x4{fo[0], fo[1], fo[2], fo[3]}, reinterpret_cast<u32x4*>(orow + col0));
+        if (col0 + kHalf < K) stream_store(u32x4{fo[4], fo[5], fo[6], fo[7]}, reinterpret_cast<u32x4*>(orow + col0 + kHalf));
+      } else {
+        for (int i = 0; i < 8; i++) {
+          const int64_t c = col0 + (i < 4 ? i : kHalf + i - 4);
+          if (c < K) orow[c] = fo[i];
+        }
+      }
+      continue;
+    }
+    const u32x4 o = decode8_fp4(fs[u], cs[u]);
     if constexpr (sizeof(TO) == 2) {
       if (VEC) {
         stream_store(o, reinterpret_cast<u32x4*>(orow + col0));

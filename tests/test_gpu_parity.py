@@ -315,7 +315,7 @@ def test_packed_every_code_and_nibble(dev):
     assert_bits(to_host(c), wc, "tile codes every code")
 
 
-@pytest.mark.parametrize("K", [1, 7, 9, 31, 33, 100, 130, 257])
+@pytest.mark.parametrize("K", [1, 7, 9, 31, 33, 100, 130, 257, 2500])   # 2500: both fp32-output lane groups
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_packed_ragged(dev, K, dtype):
     rows = 131
