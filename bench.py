@@ -21,7 +21,8 @@ mean per launch.  After the timed region a separate pass gives "us_median" /
 outside the step (the fused passes, packed MXFP4, columnwise) are timed the
 same way after the step's timed region.
 
-python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--calibrate]
+python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--calibrate] [--weight bf16|fp32]
+(--weight fp32 runs the same step on the fp32 master copy of the weight; bf16 is the headline)
 """
 from __future__ import annotations
 
@@ -47,39 +48,40 @@ KERNEL_SOURCES = [os.path.join(ROOT, "microscaling_weight_quantization_amd", "cs
                   for n in ("mxq.hip", "fastdiv.h")]
 
 
-def algorithmic_bytes(rows: int, K: int) -> dict:
-    """Bytes each kernel must move (read + write) for a [rows, K] bf16 weight."""
+def algorithmic_bytes(rows: int, K: int, es: int = 2) -> dict:
+    """Bytes each kernel must move (read + write) for a [rows, K] weight of
+    es-byte elements (2: bf16, 4: fp32; the decodes write the same dtype)."""
     n = rows * K
     nb = rows * ((K + 31) // 32)
     tiles = ((rows + 127) // 128) * ((K + 127) // 128)
     return {
-        "proj": 2 * n + 2 * n,
-        "row": 2 * n + n + nb,
+        "proj": es * n + es * n,
+        "row": es * n + n + nb,
         "export": nb + nb,
-        "block128": 2 * n + n + tiles,
-        "dec_row": n + nb + 2 * n,
-        "dec_tile": n + tiles + 2 * n,
+        "block128": es * n + n + tiles,
+        "dec_row": n + nb + es * n,
+        "dec_tile": n + tiles + es * n,
     }
 
 
-def fused_bytes(rows: int, K: int) -> int:
-    """Projection + row lift from one read: 2n in, 2n + n + n/32 out (bf16)."""
+def fused_bytes(rows: int, K: int, es: int = 2) -> int:
+    """Projection + row lift from one read: es*n in, es*n + n + n/32 out."""
     n = rows * K
-    return 2 * n + 2 * n + n + rows * ((K + 31) // 32)
+    return es * n + es * n + n + rows * ((K + 31) // 32)
 
 
-def packed_bytes(rows: int, K: int) -> dict:
-    """Bytes of the packed-MXFP4 kernels for a [rows, K] bf16 weight."""
+def packed_bytes(rows: int, K: int, es: int = 2) -> dict:
+    """Bytes of the packed-MXFP4 kernels for a [rows, K] weight of es-byte elements."""
     n, nb = rows * K, rows * ((K + 31) // 32)
     tiles = ((rows + 127) // 128) * ((K + 127) // 128)
-    return {"quantize_mxfp4": 2 * n + n // 2 + nb, "dequantize_mxfp4": n // 2 + nb + 2 * n,
+    return {"quantize_mxfp4": es * n + n // 2 + nb, "dequantize_mxfp4": n // 2 + nb + es * n,
             "packed_to_row": n // 2 + nb + n + nb, "packed_to_block128": n // 2 + nb + n + tiles}
 
 
-def col_bytes(rows: int, K: int) -> dict:
-    """Bytes of the columnwise (32x1) kernels for a [rows, K] bf16 weight."""
+def col_bytes(rows: int, K: int, es: int = 2) -> dict:
+    """Bytes of the columnwise (32x1) kernels for a [rows, K] weight of es-byte elements."""
     n, nb, nc = rows * K, rows * ((K + 31) // 32), ((rows + 31) // 32) * K
-    return {"col": 2 * n + n + nc, "row_col": 2 * n + n + nb + n + nc, "dec_col": n + nc + 2 * n}
+    return {"col": es * n + n + nc, "row_col": es * n + n + nb + n + nc, "dec_col": n + nc + es * n}
 
 
 def kernel_source_hash() -> str:
@@ -105,14 +107,16 @@ def read_traffic(kernel: str):
 
 
 def _oracle_pass(bits, threads: int) -> dict:
-    """One pass of the six steps through the CPU oracle; returns its outputs."""
+    """One pass of the six steps through the CPU oracle; returns its outputs
+    (the decodes in the weight's own dtype)."""
     import oracle
+    odt = oracle.FP32 if bits.dtype.itemsize == 4 else oracle.BF16
     y = oracle.fake_quantize_mxfp4(bits, threads=threads)
     d, s = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=SCALE_LD, threads=threads)
     c = oracle.export_mxfp8(s, bits.shape[1])
     bd, tc = oracle.mxfp4_to_fp8_block128(bits, threads=threads)
-    dr = oracle.dequantize(d, c, threads=threads)
-    dt = oracle.dequantize(bd, tc, layout=oracle.TILE_128X128, threads=threads)
+    dr = oracle.dequantize(d, c, out_dtype=odt, threads=threads)
+    dt = oracle.dequantize(bd, tc, layout=oracle.TILE_128X128, out_dtype=odt, threads=threads)
     return {"proj": y, "row": d, "export": c, "block128": bd, "tile_codes": tc, "dec_row": dr, "dec_tile": dt}
 
 
@@ -138,17 +142,19 @@ def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int 
         outputs = _oracle_pass(bits, threads)
         passes += 1
     dt, cpu = time.perf_counter() - t0, time.process_time() - c0
-    total = passes * sum(algorithmic_bytes(*bits.shape).values())
+    es = bits.dtype.itemsize
+    wname = "fp32" if es == 4 else "bf16"
+    total = passes * sum(algorithmic_bytes(*bits.shape, es).values())
     out = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
            "cpu_model": cpu_model(),
-           "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} bf16 weight, {passes} pass{'es' if passes > 1 else ''} of all six steps "
+           "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} {wname} weight, {passes} pass{'es' if passes > 1 else ''} of all six steps "
                      f"({dt:.1f} s wall, {cpu:.1f} s CPU on {threads} threads)"}
     # the same steps on one thread, over the first 2048 rows
     sub = bits[:2048]
     t0 = time.perf_counter()
     _oracle_pass(sub, 1)
     dt1 = time.perf_counter() - t0
-    out["one_thread"] = {"value": round(sum(algorithmic_bytes(*sub.shape).values()) / dt1 / 1e9, 3), "unit": "GB/s",
+    out["one_thread"] = {"value": round(sum(algorithmic_bytes(*sub.shape, es).values()) / dt1 / 1e9, 3), "unit": "GB/s",
                          "sample": f"rows 0..2047 of the same weight, one pass of all six steps ({dt1:.1f} s)"}
     return out, outputs
 
@@ -162,6 +168,8 @@ def parity(s, want: dict) -> dict:
         t = t.contiguous().cpu()
         if t.dtype == torch.bfloat16:
             return t.view(torch.int16).numpy().view("uint16")
+        if t.dtype == torch.float32:
+            return t.view(torch.int32).numpy().view("uint32")
         return t.numpy()
 
     got = {"proj": host(s["y"]), "row": host(s["data"]), "export": host(s["scale_c"]), "block128": host(s["bdata"]),
@@ -178,6 +186,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--weight", choices=["bf16", "fp32"], default="bf16",
+                    help="the weight's dtype: bf16 (the headline) or its fp32 master copy")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
@@ -195,10 +205,13 @@ def main():
 
     dev = torch.device("cuda:0")
     mxq.load()
-    bits = W.c4_headline()
+    fp32 = args.weight == "fp32"
+    es = 4 if fp32 else 2
+    bits = W.c4_master() if fp32 else W.c4_headline()
     rows, K = bits.shape
     nb = (K + 31) // 32
-    x0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    x0 = (torch.from_numpy(bits.view(np.int32)).to(dev).view(torch.float32) if fp32
+          else torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16))
     sets = []
     for i in range(NSETS):
         s = {
@@ -307,7 +320,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    nbytes = algorithmic_bytes(rows, K)
+    nbytes = algorithmic_bytes(rows, K, es)
     ms_per_step = wall * 1e3 / args.steps
     total = sum(nbytes.values())
     kernels = {}
@@ -326,7 +339,7 @@ def main():
         kernels[n] = {"us": round(us, 2), "us_median": round(med, 2), "us_min": round(lo, 2), "bytes": nbytes[n],
                       "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     extra = {}
-    extra_bytes = dict(packed_bytes(rows, K), fused=fused_bytes(rows, K), **col_bytes(rows, K))
+    extra_bytes = dict(packed_bytes(rows, K, es), fused=fused_bytes(rows, K, es), **col_bytes(rows, K, es))
     for n in extra_names:
         us, med, lo = burst_stats(n)
         gbs = extra_bytes[n] / (us * 1e-6) / 1e9
@@ -337,9 +350,11 @@ def main():
     extra["row_col"]["vs_separate_us"] = round(kernels["row"]["us"] + extra["col"]["us"], 2)
     dominant = max(names, key=lambda n: kernels[n]["us"])
     rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
-          "unit": "GB/s", "frac": kernels[dominant]["frac"], "traffic": read_traffic(dominant)}
+          "unit": "GB/s", "frac": kernels[dominant]["frac"],
+          # the committed counter summary is of the bf16 weight
+          "traffic": None if fp32 else read_traffic(dominant)}
     out = {
-        "metric": "GB/s and % HBM peak, MXFP4 proj + MXFP8-row/128x128 at 8192^2 bf16",
+        "metric": "GB/s and % HBM peak, MXFP4 proj + MXFP8-row/128x128 at 8192^2 " + args.weight,
         "value": round(total / (ms_per_step * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -349,12 +364,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # the path is integer work on the weight's 16-bit patterns (amax, exponent
+        # the path is integer work on the weight's bit patterns (amax, exponent
         # fields), with the E2M1 / E4M3 encodes done by the hardware conversions
-        "dtype": "u16",
+        "dtype": "u32" if fp32 else "u16",
         "data": "synthetic",
-        "config": {"workload": "8192x8192 bf16 weight, N(0,0.02) seed 1: proj + row (scale_ld 260) + export "
-                               "+ block128 + decode(row) + decode(tile)",
+        "config": {"workload": ("8192x8192 fp32 master weight (the bf16 headline weight before its cast)"
+                                if fp32 else "8192x8192 bf16 weight") +
+                               ", N(0,0.02) seed 1: proj + row (scale_ld 260) + export + block128 + decode(row) "
+                               "+ decode(tile), decodes to the weight's dtype",
                    "bytes_per_step": total, "buffer_sets": NSETS},
         "roofline": rl,
         "kernels": kernels,

@@ -29,3 +29,20 @@ def test_algorithmic_bytes_at_8192():
     assert b["proj"] == 268435456 and b["row"] == 203423744 and b["block128"] == 201330688
     assert bench.fused_bytes(8192, 8192) == 337641472
     assert bench.col_bytes(8192, 8192)["col"] == 203423744
+
+
+def test_algorithmic_bytes_fp32_weight():
+    """The fp32 master weight: 4-byte elements in, and the decodes write fp32."""
+    sys.path.insert(0, ROOT)
+    import bench
+    n, nb = 8192 * 8192, 8192 * 256
+    b = bench.algorithmic_bytes(8192, 8192, 4)
+    assert b["proj"] == 8 * n and b["row"] == 4 * n + n + nb and b["dec_row"] == n + nb + 4 * n
+    assert b["export"] == bench.algorithmic_bytes(8192, 8192)["export"]
+    assert bench.fused_bytes(8192, 8192, 4) == 9 * n + nb
+    assert bench.packed_bytes(8192, 8192, 4)["dequantize_mxfp4"] == n // 2 + nb + 4 * n
+
+
+def test_weight_choice_is_validated():
+    r = _run("--weight", "fp16")
+    assert r.returncode != 0 and "--weight" in r.stderr

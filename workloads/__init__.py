@@ -169,6 +169,12 @@ def c4_headline(seed: int = 1, shape=(8192, 8192)) -> np.ndarray:
     return _bf16_bits(torch.randn(*shape, generator=g) * 0.02)
 
 
+def c4_master(seed: int = 1, shape=(8192, 8192)) -> np.ndarray:
+    """fp32 bits of the headline weight before its bf16 cast (the master copy)."""
+    g = torch.Generator().manual_seed(seed)
+    return _fp32_bits(torch.randn(*shape, generator=g) * 0.02)
+
+
 def c5_mlp(which: str):
     """which: 'up' (28672 x 8192 bf16, seed 2), 'down' (8192 x 28672 bf16,
     seed 3) or 'up_master' (fp32 bits of the first before its bf16 cast)."""
