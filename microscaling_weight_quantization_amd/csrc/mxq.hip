@@ -92,9 +92,6 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_COL_ROWS
 #define MXQ_COL_ROWS 4            // columnwise: rows of the 32-row band per lane (a divisor of 32)
 #endif
-#ifndef MXQ_TILE_COLUMN_MAJOR
-#define MXQ_TILE_COLUMN_MAJOR 0   // 128x128 fold: consecutive workgroups walk down a tile column
-#endif
 // Cache policy of the streaming accesses.
 #ifndef MXQ_NT_LOADS
 #define MXQ_NT_LOADS 1            // streaming loads carry the non-temporal hint
@@ -681,12 +678,7 @@ __global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restr
   keep_denormals();
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-#if MXQ_TILE_COLUMN_MAJOR
-  const uint32_t band_count = gridDim.x / groups_per_row.d;
-  const uint32_t tg = blockIdx.x / band_count, tr = blockIdx.x - tg * band_count;
-#else
   const uint32_t tr = mxq_quot(blockIdx.x, groups_per_row), tg = blockIdx.x - tr * groups_per_row.d;
-#endif
   const uint32_t j = (tid % LPR) / CPT;                    // this lane's tile within the group
   const int64_t r0 = (int64_t)tr * 128 + tid / LPR;
   const int64_t col0 = (int64_t)tg * (128 * J) + (tid % LPR) * EPL;
