@@ -38,6 +38,7 @@ def draw(seed):
     pad = int(g.choice([0, 0, 1, 8, 13]))         # row stride K + pad
     off = int(g.choice([0, 0, 1, 3]))             # element offset of the view
     spad = int(g.choice([0, 0, 3, 8]))            # scale-storage pad
+    opad = int(g.choice([0, 0, 4, 5]))            # output row-stride pad (projection, decodes)
     nb = (K + 31) // 32
     e = g.integers(-134, 124, size=(rows, nb))
     v = g.standard_normal((rows, nb * 32)) * np.exp2(np.repeat(e, 32, axis=1).astype(np.float64))
@@ -51,7 +52,7 @@ def draw(seed):
         bits = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
     else:
         bits = v.view(np.uint32).copy()
-    return rows, K, dtype, pad, off, spad, bits
+    return rows, K, dtype, pad, off, spad, opad, bits
 
 
 def strided_view(bits, pad, off, dev):
@@ -65,16 +66,37 @@ def strided_view(bits, pad, off, dev):
     return view
 
 
+SENTINEL = {torch.bfloat16: 0x7E55, torch.float32: 0x7E55AA11}
+
+
+def out_view(rows, K, opad, tdt, dev):
+    """A [rows, K] output view with row stride K + opad whose pad columns hold a
+    sentinel pattern (checked afterwards: nothing may be written there)."""
+    idt = torch.int16 if tdt == torch.bfloat16 else torch.int32
+    full = torch.full((rows, K + opad), SENTINEL[tdt], dtype=idt, device=dev).view(tdt)
+    return full, full[:, :K]
+
+
+def check_pad(full, K, what):
+    if full.shape[1] > K:
+        pad = full[:, K:].view(torch.int16 if full.dtype == torch.bfloat16 else torch.int32)
+        assert bool((pad == SENTINEL[full.dtype]).all()), f"{what}: write into the row-stride pad"
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_case(dev, seed):
-    rows, K, dtype, pad, off, spad, bits = draw(seed)
-    print(f"case {seed}: rows={rows} K={K} {dtype} pad={pad} off={off} spad={spad}", flush=True)
+    rows, K, dtype, pad, off, spad, opad, bits = draw(seed)
+    print(f"case {seed}: rows={rows} K={K} {dtype} pad={pad} off={off} spad={spad} opad={opad}", flush=True)
     x = strided_view(bits, pad, off, dev)
     nb, bands = (K + 31) // 32, (rows + 31) // 32
     outs = ((torch.bfloat16, oracle.BF16), (torch.float32, oracle.FP32))
 
-    # projection
-    assert_bits(to_host(mxq.mxq_fake_quantize_mxfp4(x)), oracle.fake_quantize_mxfp4(bits, threads=THREADS), "projection")
+    # projection, into a padded output view
+    wy = oracle.fake_quantize_mxfp4(bits, threads=THREADS)
+    yfull, y = out_view(rows, K, opad, x.dtype, dev)
+    mxq.mxq_fake_quantize_mxfp4(x, y)
+    assert_bits(to_host(y), wy, "projection")
+    check_pad(yfull, K, "projection")
 
     # row lift, export, row decode
     scale = torch.full((rows, nb + spad), 0xA5, dtype=torch.uint8, device=dev)
@@ -85,13 +107,17 @@ def test_random_case(dev, seed):
     codes = mxq.mxq_export_mxfp8(data, scale, K)
     assert_bits(to_host(codes), oracle.export_mxfp8(ws, K), "export")
     for tdt, o in outs:
-        assert_bits(to_host(mxq.mxq_dequantize(data, codes, out_dtype=tdt)),
-                    oracle.dequantize(wd, ws[:, :nb], out_dtype=o, threads=THREADS), f"row decode {tdt}")
+        ofull, ov = out_view(rows, K, opad, tdt, dev)
+        mxq.mxq_dequantize(data, codes, out=ov)
+        assert_bits(to_host(ov), oracle.dequantize(wd, ws[:, :nb], out_dtype=o, threads=THREADS), f"row decode {tdt}")
+        check_pad(ofull, K, f"row decode {tdt}")
 
     # fused projection + row lift
     s2 = torch.full((rows, nb + spad), 0x5A, dtype=torch.uint8, device=dev)
-    y2, d2, s2 = mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x, scale=s2)
-    assert_bits(to_host(y2), oracle.fake_quantize_mxfp4(bits, threads=THREADS), "fused projection")
+    y2full, y2 = out_view(rows, K, opad, x.dtype, dev)
+    y2, d2, s2 = mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x, y=y2, scale=s2)
+    assert_bits(to_host(y2), wy, "fused projection")
+    check_pad(y2full, K, "fused projection")
     assert_bits(to_host(d2), wd, "fused payload")
     assert_bits(to_host(s2)[:, :nb], ws[:, :nb], "fused codes")
 
@@ -128,8 +154,10 @@ def test_random_case(dev, seed):
     assert_bits(to_host(packed), wp, "packed nibbles")
     assert_bits(to_host(ps), wps, "packed codes (padding untouched)")
     for tdt, o in outs:
-        assert_bits(to_host(mxq.mxq_dequantize_mxfp4(packed, ps, K, out_dtype=tdt)),
-                    oracle.dequantize_mxfp4(wp, wps, K, out_dtype=o, threads=THREADS), f"packed decode {tdt}")
+        ofull, ov = out_view(rows, K, opad, tdt, dev)
+        mxq.mxq_dequantize_mxfp4(packed, ps, K, out=ov)
+        assert_bits(to_host(ov), oracle.dequantize_mxfp4(wp, wps, K, out_dtype=o, threads=THREADS), f"packed decode {tdt}")
+        check_pad(ofull, K, f"packed decode {tdt}")
     pd, pc = mxq.mxq_mxfp4_packed_to_mxfp8_row(packed, ps, K)
     wpd, wpc = oracle.mxfp4_packed_to_mxfp8_row(wp, wps, K, threads=THREADS)
     assert_bits(to_host(pd), wpd, "row lift from packed")
