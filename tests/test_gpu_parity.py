@@ -479,3 +479,45 @@ def test_row_longer_than_2gb(dev):
         assert_bits(to_host(scale[:, c0 // 32:(c1 + 31) // 32]), ws, f"fused row codes [{c0}, {c1})")
     del x, y, data, scale
     torch.cuda.empty_cache()
+
+
+def test_concurrent_callers_on_their_own_streams(dev):
+    """The library holds no state: two host threads, each on its own stream and
+    its own weight, interleave the projection, row lift, fold and decode many
+    times; every output matches the oracle."""
+    import threading
+    weights = [W.c4_headline(seed=21, shape=(512, 1024)), W.fp32_fuzz(1 << 17).reshape(512, 256)]
+    want = []
+    for bits in weights:
+        wd, ws = oracle.mxfp4_to_mxfp8_row(bits, threads=THREADS)
+        wbd, wtc = oracle.mxfp4_to_fp8_block128(bits, threads=THREADS)
+        odt = oracle.FP32 if bits.dtype == np.uint32 else oracle.BF16
+        want.append((oracle.fake_quantize_mxfp4(bits, threads=THREADS), wd, ws, wbd, wtc,
+                     oracle.dequantize(wd, ws, out_dtype=odt, threads=THREADS)))
+    errors, results = [], [None, None]
+
+    def worker(i):
+        try:
+            x = to_dev(weights[i], dev)
+            stream = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(stream):
+                for _ in range(20):
+                    y = mxq.mxq_fake_quantize_mxfp4(x)
+                    d, s = mxq.mxq_mxfp4_to_mxfp8_row(x)
+                    bd, tc = mxq.mxq_mxfp4_to_fp8_block128(x)
+                    dec = mxq.mxq_dequantize(d, s, out_dtype=x.dtype)
+            stream.synchronize()
+            results[i] = (y, d, s, bd, tc, dec)
+        except Exception as e:      # reported from the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        for got, exp, what in zip(results[i], want[i], ("projection", "payload", "codes", "128x128 payload",
+                                                         "tile codes", "decode")):
+            assert_bits(to_host(got), exp, f"caller {i}: {what}")
