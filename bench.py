@@ -1,7 +1,7 @@
 """Throughput of the block-scaled weight-quantization path on one MI355X.
 
 One step = one pass of the whole path over the 8192 x 8192 bf16 weight
-(N(0, 0.02), seed 1):
+(N(0, 0.02), seed 1; --shape and --weight below name the other weights):
   proj      MXFP4 projection, bf16 -> bf16
   row       direct MXFP8 rowwise lift (E4M3 payload + E8M0 codes, scale storage
             padded to 260 columns so the export has to copy)
@@ -19,10 +19,16 @@ kernel's burst on the stream the kernels are launched on: "us" is the burst's
 mean per launch.  After the timed region a separate pass gives "us_median" /
 "us_min", the median / minimum over 5 sub-bursts of 5 launches.  Kernels
 outside the step (the fused passes, packed MXFP4, columnwise) are timed the
-same way after the step's timed region.
+same way after the step's timed region.  The default of 100 timed steps keeps
+the fixed cost of the synchronizations around the timed region (tens of us in
+all) below 1% of it.
 
-python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--calibrate] [--weight bf16|fp32]
-(--weight fp32 runs the same step on the fp32 master copy of the weight; bf16 is the headline)
+python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu] [--calibrate] [--weight bf16|fp32]
+                [--shape 8192x8192|28672x8192|8192x28672]
+(--weight fp32 runs the same step on the fp32 master copy of the weight; bf16 is the headline.
+--shape runs the same step on the MLP-shaped weights instead: 28672 x 8192 (N(0,0.02), seed 2; its
+fp32 master with --weight fp32) or 8192 x 28672 (seed 3, bf16 only).  The scale storage is always
+padded by 4 columns, so the export copies.)
 """
 from __future__ import annotations
 
@@ -38,8 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-ROWS = COLS = 8192
-SCALE_LD = 260                   # padded scale storage: ceil(K/32) = 256 plus 4 columns
+SCALE_PAD = 4                    # padded scale storage: ceil(K/32) plus 4 columns (8192: 260)
+SHAPES = ("8192x8192", "28672x8192", "8192x28672")
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_bf16.txt")
@@ -112,7 +118,7 @@ def _oracle_pass(bits, threads: int) -> dict:
     import oracle
     odt = oracle.FP32 if bits.dtype.itemsize == 4 else oracle.BF16
     y = oracle.fake_quantize_mxfp4(bits, threads=threads)
-    d, s = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=SCALE_LD, threads=threads)
+    d, s = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=(bits.shape[1] + 31) // 32 + SCALE_PAD, threads=threads)
     c = oracle.export_mxfp8(s, bits.shape[1])
     bd, tc = oracle.mxfp4_to_fp8_block128(bits, threads=threads)
     dr = oracle.dequantize(d, c, out_dtype=odt, threads=threads)
@@ -161,7 +167,7 @@ def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int 
 
 def parity(s, want: dict) -> dict:
     """The step's GPU outputs in one buffer set against the oracle's, bit for bit
-    (8192 x 8192, the timed launch configuration)."""
+    (the whole weight, in the timed launch configuration)."""
     import torch
 
     def host(t):
@@ -181,14 +187,18 @@ def parity(s, want: dict) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--weight", choices=["bf16", "fp32"], default="bf16",
                     help="the weight's dtype: bf16 (the headline) or its fp32 master copy")
+    ap.add_argument("--shape", choices=SHAPES, default=SHAPES[0],
+                    help="the weight's shape: 8192x8192 (the headline) or an MLP-shaped weight")
     args = ap.parse_args()
+    if args.shape == "8192x28672" and args.weight == "fp32":
+        ap.error("--shape 8192x28672 has no fp32 master weight (only the 28672x8192 weight has one)")
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -207,9 +217,14 @@ def main():
     mxq.load()
     fp32 = args.weight == "fp32"
     es = 4 if fp32 else 2
-    bits = W.c4_master() if fp32 else W.c4_headline()
+    headline = args.shape == SHAPES[0]
+    if headline:
+        bits = W.c4_master() if fp32 else W.c4_headline()
+    else:
+        bits = W.c5_mlp("down" if args.shape == "8192x28672" else "up_master" if fp32 else "up")
     rows, K = bits.shape
     nb = (K + 31) // 32
+    scale_ld = nb + SCALE_PAD
     x0 = (torch.from_numpy(bits.view(np.int32)).to(dev).view(torch.float32) if fp32
           else torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16))
     sets = []
@@ -218,7 +233,7 @@ def main():
             "x": x0.clone(),
             "y": torch.empty_like(x0),
             "data": torch.empty((rows, K), dtype=torch.uint8, device=dev),
-            "scale": torch.zeros((rows, SCALE_LD), dtype=torch.uint8, device=dev),
+            "scale": torch.zeros((rows, scale_ld), dtype=torch.uint8, device=dev),
             "scale_c": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
             "bdata": torch.empty((rows, K), dtype=torch.uint8, device=dev),
             "tc": torch.empty(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev),
@@ -231,7 +246,7 @@ def main():
             "packed": torch.empty((rows, K // 2), dtype=torch.uint8, device=dev),
             "pscale": torch.empty((rows, nb), dtype=torch.uint8, device=dev),
             "data2": torch.empty((rows, K), dtype=torch.uint8, device=dev),
-            "scale2": torch.zeros((rows, SCALE_LD), dtype=torch.uint8, device=dev),
+            "scale2": torch.zeros((rows, scale_ld), dtype=torch.uint8, device=dev),
             "cdata": torch.empty((rows, K), dtype=torch.uint8, device=dev),
             "cscale": torch.empty(((rows + 31) // 32, K), dtype=torch.uint8, device=dev),
         }
@@ -351,10 +366,11 @@ def main():
     dominant = max(names, key=lambda n: kernels[n]["us"])
     rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
           "unit": "GB/s", "frac": kernels[dominant]["frac"],
-          # the committed counter summary is of the bf16 weight
-          "traffic": None if fp32 else read_traffic(dominant)}
+          # the committed counter summary is of the 8192 x 8192 bf16 weight
+          "traffic": read_traffic(dominant) if headline and not fp32 else None}
     out = {
-        "metric": "GB/s and % HBM peak, MXFP4 proj + MXFP8-row/128x128 at 8192^2 " + args.weight,
+        "metric": "GB/s and % HBM peak, MXFP4 proj + MXFP8-row/128x128 at " +
+                  ("8192^2 " if headline else args.shape + " ") + args.weight,
         "value": round(total / (ms_per_step * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -368,9 +384,10 @@ def main():
         # fields), with the E2M1 / E4M3 encodes done by the hardware conversions
         "dtype": "u32" if fp32 else "u16",
         "data": "synthetic",
-        "config": {"workload": ("8192x8192 fp32 master weight (the bf16 headline weight before its cast)"
-                                if fp32 else "8192x8192 bf16 weight") +
-                               ", N(0,0.02) seed 1: proj + row (scale_ld 260) + export + block128 + decode(row) "
+        "config": {"workload": (f"{rows}x{K} fp32 master weight (the bf16 weight before its cast)"
+                                if fp32 else f"{rows}x{K} bf16 weight") +
+                               f", N(0,0.02) seed {1 if headline else 3 if args.shape == '8192x28672' else 2}: "
+                               f"proj + row (scale_ld {scale_ld}) + export + block128 + decode(row) "
                                "+ decode(tile), decodes to the weight's dtype",
                    "bytes_per_step": total, "buffer_sets": NSETS},
         "roofline": rl,

@@ -46,3 +46,24 @@ def test_algorithmic_bytes_fp32_weight():
 def test_weight_choice_is_validated():
     r = _run("--weight", "fp16")
     assert r.returncode != 0 and "--weight" in r.stderr
+
+
+def test_algorithmic_bytes_mlp_shapes():
+    """The MLP-shaped weights: 28672 x 8192 bf16 and its fp32 master (the byte
+    model at n = 28672 * 8192 elements and n / 32 blocks)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    b = bench.algorithmic_bytes(28672, 8192)
+    assert b["proj"] == 939524096 and b["row"] == 711983104
+    b = bench.algorithmic_bytes(28672, 8192, 4)
+    assert b["proj"] == 1879048192 and b["row"] == 1181745152
+    # the transposed weight moves the same bytes except where blocks and tiles are counted
+    assert bench.algorithmic_bytes(8192, 28672)["proj"] == 939524096
+    assert bench.algorithmic_bytes(8192, 28672)["export"] == 2 * 8192 * 896
+
+
+def test_shape_choice_is_validated():
+    r = _run("--shape", "100x48")
+    assert r.returncode != 0 and "--shape" in r.stderr
+    r = _run("--shape", "8192x28672", "--weight", "fp32")
+    assert r.returncode == 2 and "fp32 master" in r.stderr
