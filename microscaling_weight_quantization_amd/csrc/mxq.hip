@@ -1189,7 +1189,15 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
 //     the tile has none); tile code max(M - 6, 0), i.e. S = max(M - 6, -127).
 //  2. Lane t converts 16 elements (8 packed bytes -> 16 payload bytes) of R
 //     band rows, t / 32 + (128 / R) k, at the shift e - S of its block and
-//     tile; all R loads are issued first.  Poisoned blocks (code 255) get 0x7F.
+//     tile.  Poisoned blocks (code 255) get 0x7F.
+// A whole band (all 128 rows and 512 columns in range, aligned storage) runs
+// both parts as straight-line code: the code loads, then all R payload loads,
+// then the code pass, so the payload is in flight through the code pass and
+// the barrier (loads complete in order, and the code pass waits for the code
+// loads alone).  Its rows are addressed from the band's base pointers with
+// 32-bit lane offsets, so no load or store needs a guard.  An edge band (a
+// partial band or column group) converts one row at a time, so that this rare
+// path does not set the kernel's register count.
 // Workgroup order for the fold from packed.  The hardware deals workgroups
 // round-robin over the 8 XCDs (b runs on XCD b % 8), each with its own L2.
 // Neighbouring workgroups of a band read neighbouring 16-byte pieces of the
@@ -1202,36 +1210,20 @@ __device__ __forceinline__ uint32_t xcd_window_order(uint32_t b, uint32_t n) {
   return (b & ~63u) | ((b & 7u) << 3) | ((b >> 3) & 7u);
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_t* __restrict__ packed,
-                                                          const uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                          int64_t rows, int64_t K, uint8_t* __restrict__ data,
-                                                          uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                          MxqDivisor groups, bool codes_vec) {
-  __shared__ uint32_t s_codes[128][4];   // the band rows' 16 block codes
-  __shared__ uint32_t s_max[4][4];       // wave x tile
-  keep_denormals();
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t wb = xcd_window_order(blockIdx.x, gridDim.x);
-  const uint32_t tr = mxq_quot(wb, groups), tg = wb - tr * groups.d;
-  const int64_t r0 = (int64_t)tr * 128, nb = (K + 31) / 32, pw = (K + 1) / 2, ntc = (K + 127) / 128;
+constexpr int kPFoldRG = 128 / kPFoldRows;                  // row groups of the band
 
-  if (tid < 256u) {  // 1. block codes and tile codes (the first four waves)
-    const uint32_t rl = tid >> 1, h = tid & 1u;
-    const int64_t r = r0 + rl, j = (int64_t)tg * 16 + 8 * h;
-    uint32_t w[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};              // 255: no finite code
-    if (r < rows) {
-      const uint8_t* src = scale + r * scale_ld + j;
-      if (codes_vec && j + 8 <= nb) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-        w[0] = v[0], w[1] = v[1];
-      } else {
-        for (int k = 0; k < 8; k++)
-          if (j + k < nb) w[k / 4] = (w[k / 4] & ~(0xFFu << (8 * (k % 4)))) | ((uint32_t)src[k] << (8 * (k % 4)));
-      }
-    }
-    s_codes[rl][2 * h] = w[0];
-    s_codes[rl][2 * h + 1] = w[1];
+struct PFoldLds {
+  uint32_t codes[128][4];   // the band rows' 16 block codes
+  uint32_t max[4][4];       // wave x tile
+};
+
+// Part 1 from lane t's 8 codes w (band row t / 2, half t % 2): the codes go to
+// LDS and the four tile codes of the group come back (after a barrier).
+__device__ __forceinline__ void pfold_tile_codes(const uint32_t w[2], uint32_t tid, PFoldLds& L, uint32_t tcode[4]) {
+  const uint32_t lane = tid & 63u, wave = tid >> 6, rl = tid >> 1, h = tid & 1u;
+  if (tid < 256u) {  // the first four waves
+    L.codes[rl][2 * h] = w[0];
+    L.codes[rl][2 * h + 1] = w[1];
     uint32_t m[2] = {1u, 1u};
 #pragma unroll
     for (int t = 0; t < 2; t++)
@@ -1244,60 +1236,101 @@ __global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_
     for (int t = 0; t < 2; t++)
 #pragma unroll
       for (int off = 2; off < 64; off <<= 1) m[t] = max(m[t], (uint32_t)__shfl_xor((int)m[t], off));
-    if (lane < 2u) s_max[wave][2 * lane] = m[0], s_max[wave][2 * lane + 1] = m[1];
+    if (lane < 2u) L.max[wave][2 * lane] = m[0], L.max[wave][2 * lane + 1] = m[1];
   }
   __syncthreads();
-  uint32_t tcode[4];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    const uint32_t M = max(max(s_max[0][t], s_max[1][t]), max(s_max[2][t], s_max[3][t]));
+    const uint32_t M = max(max(L.max[0][t], L.max[1][t]), max(L.max[2][t], L.max[3][t]));
     tcode[t] = M > 6u ? M - 6u : 0u;
   }
-  if (tid < 4u && (int64_t)tg * 4 + tid < ntc)
-    tile_code[(int64_t)tr * tile_ld + tg * 4 + tid] =
-        (uint8_t)(tid == 0 ? tcode[0] : tid == 1 ? tcode[1] : tid == 2 ? tcode[2] : tcode[3]);
+}
 
-  // 2. payload
-  constexpr int RG = 128 / kPFoldRows;                       // row groups
-  const uint32_t cc = tid & 31u, rg = tid >> 5;             // 16-element column chunk, row group
+// 16 payload bytes of one lane's 8 packed bytes f, block code c, tile code ts.
+__device__ __forceinline__ u32x4 pfold_payload(u32x2 f, uint32_t c, uint32_t ts) {
+  const int ds = min((int)c - (int)ts, 6);                   // e - S <= 6 (code 255: not used)
+  const u32x2 lo = e4m3x8_of_fp4(f[0], ds), hi = e4m3x8_of_fp4(f[1], ds);
+  return c == 255u ? u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu} : u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_t* __restrict__ packed,
+                                                          const uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                          int64_t rows, int64_t K, uint8_t* __restrict__ data,
+                                                          uint8_t* __restrict__ tile_code, int64_t tile_ld,
+                                                          MxqDivisor groups, bool codes_vec) {
+  __shared__ PFoldLds L;
+  keep_denormals();
+  const uint32_t tid = threadIdx.x;
+  const uint32_t wb = xcd_window_order(blockIdx.x, gridDim.x);
+  const uint32_t tr = mxq_quot(wb, groups), tg = wb - tr * groups.d;
+  const int64_t r0 = (int64_t)tr * 128, nb = (K + 31) / 32, pw = (K + 1) / 2, ntc = (K + 127) / 128;
+  const uint32_t rl = tid >> 1, h = tid & 1u;                // part 1: band row and half
+  const uint32_t cc = tid & 31u, rg = tid >> 5;             // part 2: 16-element column chunk, row group
   const int64_t col0 = (int64_t)tg * 512 + cc * 16;
-  const uint32_t tt = cc >> 3;                               // tile within the group
-  const uint32_t ts = tt == 0 ? tcode[0] : tt == 1 ? tcode[1] : tt == 2 ? tcode[2] : tcode[3];
-  u32x2 f[kPFoldRows];
+  const int64_t j = (int64_t)tg * 16 + 8 * h;               // first of the lane's 8 block codes
+  uint32_t w[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};                // 255: no finite code
+  uint32_t tcode[4];
+
+  if (VEC && codes_vec && r0 + 128 <= rows && (int64_t)tg * 512 + 512 <= K && K <= ((int64_t)1 << 27)) {
+    // whole band (uniform branch)
+    if (tid < 256u) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(scale + (r0 + rl) * scale_ld + j);
+      w[0] = v[0], w[1] = v[1];
+    }
+    const uint8_t* pband = packed + r0 * pw;
+    const uint32_t lp = rg * (uint32_t)pw + (uint32_t)(col0 / 2);
+    u32x2 f[kPFoldRows];
 #pragma unroll
-  for (int k = 0; k < kPFoldRows; k++) {
-    f[k] = u32x2{0u, 0u};
-    const int64_t r = r0 + rg + RG * k;
-    if (r < rows && col0 < K) {
-      const uint8_t* prow = packed + r * pw;
-      if (VEC) {
-        f[k] = stream_load(reinterpret_cast<const u32x2*>(prow + col0 / 2));
-      } else {
-        for (int i = 0; i < 16; i += 2)
-          if (col0 + i < K) f[k][i / 8] |= (uint32_t)prow[(col0 + i) / 2] << (4 * (i % 8));
-      }
+    for (int k = 0; k < kPFoldRows; k++)
+      f[k] = stream_load(reinterpret_cast<const u32x2*>(pband + (int64_t)(kPFoldRG * k) * pw + lp));
+    pfold_tile_codes(w, tid, L, tcode);
+    if (tid < 4u) tile_code[(int64_t)tr * tile_ld + tg * 4 + tid] = (uint8_t)tcode[tid & 3u];
+    const uint32_t tt = cc >> 3, ts = tt == 0 ? tcode[0] : tt == 1 ? tcode[1] : tt == 2 ? tcode[2] : tcode[3];
+    uint8_t* dband = data + r0 * K;
+    const uint32_t ld = rg * (uint32_t)K + (uint32_t)col0;
+#pragma unroll
+    for (int k = 0; k < kPFoldRows; k++) {
+      const uint32_t c = (L.codes[rg + kPFoldRG * k][cc >> 3] >> (8 * ((cc >> 1) & 3u))) & 0xFFu;
+      stream_store(pfold_payload(f[k], c, ts), reinterpret_cast<u32x4*>(dband + (int64_t)(kPFoldRG * k) * K + ld));
+    }
+    return;
+  }
+
+  // edge band
+  if (tid < 256u && r0 + rl < rows) {
+    const uint8_t* src = scale + (r0 + rl) * scale_ld + j;
+    if (codes_vec && j + 8 <= nb) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      w[0] = v[0], w[1] = v[1];
+    } else {
+      for (int k = 0; k < 8; k++)
+        if (j + k < nb) w[k / 4] = (w[k / 4] & ~(0xFFu << (8 * (k % 4)))) | ((uint32_t)src[k] << (8 * (k % 4)));
     }
   }
-#pragma unroll
+  pfold_tile_codes(w, tid, L, tcode);
+  if (tid < 4u && (int64_t)tg * 4 + tid < ntc) tile_code[(int64_t)tr * tile_ld + tg * 4 + tid] = (uint8_t)tcode[tid & 3u];
+  const uint32_t tt = cc >> 3, ts = tt == 0 ? tcode[0] : tt == 1 ? tcode[1] : tt == 2 ? tcode[2] : tcode[3];
+#pragma unroll 1
   for (int k = 0; k < kPFoldRows; k++) {
-    const int64_t r = r0 + rg + RG * k;
-    if (r < rows && col0 < K) {
-      const uint32_t c = (s_codes[rg + RG * k][cc >> 3] >> (8 * ((cc >> 1) & 3u))) & 0xFFu;
-      u32x4 q;
-      if (c == 255u) {
-        q = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-      } else {
-        const int ds = (int)c - (int)ts;                       // e - S <= 6
-        const u32x2 lo = e4m3x8_of_fp4(f[k][0], ds), hi = e4m3x8_of_fp4(f[k][1], ds);
-        q = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-      uint8_t* drow = data + r * K;
-      if (VEC) {
-        stream_store(q, reinterpret_cast<u32x4*>(drow + col0));
-      } else {
-        for (int i = 0; i < 16; i++)
-          if (col0 + i < K) drow[col0 + i] = (uint8_t)(q[i / 4] >> (8 * (i % 4)));
-      }
+    const int64_t r = r0 + rg + kPFoldRG * k;
+    if (r >= rows || col0 >= K) continue;
+    const uint8_t* prow = packed + r * pw;
+    u32x2 f = {0u, 0u};
+    if (VEC) {
+      f = stream_load(reinterpret_cast<const u32x2*>(prow + col0 / 2));
+    } else {
+      for (int i = 0; i < 16; i += 2)
+        if (col0 + i < K) f[i / 8] |= (uint32_t)prow[(col0 + i) / 2] << (4 * (i % 8));
+    }
+    const uint32_t c = (L.codes[rg + kPFoldRG * k][cc >> 3] >> (8 * ((cc >> 1) & 3u))) & 0xFFu;
+    const u32x4 q = pfold_payload(f, c, ts);
+    uint8_t* drow = data + r * K;
+    if (VEC) {
+      stream_store(q, reinterpret_cast<u32x4*>(drow + col0));
+    } else {
+      for (int i = 0; i < 16; i++)
+        if (col0 + i < K) drow[col0 + i] = (uint8_t)(q[i / 4] >> (8 * (i % 4)));
     }
   }
 }
