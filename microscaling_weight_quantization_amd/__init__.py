@@ -17,6 +17,7 @@ block-scaling recipes" -- Description, Test results, Known limitations; and
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 from typing import NamedTuple, Optional
@@ -82,6 +83,25 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         return L
 
 
+def _device_operands(fn):
+    """Every tensor argument of an entry point must be a device tensor, all on one
+    device: the library takes raw device pointers, and a host pointer or one
+    from another GPU would reach a kernel as an invalid address."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        dev = None
+        for t in list(args) + list(kwargs.values()):
+            if isinstance(t, torch.Tensor):
+                if not t.is_cuda:
+                    raise ValueError(f"{fn.__name__}: operands must be device tensors, got one on {t.device}")
+                if dev is None:
+                    dev = t.device
+                elif t.device != dev:
+                    raise ValueError(f"{fn.__name__}: operands on {dev} and {t.device}; all must be on one device")
+        return fn(*args, **kwargs)
+    return wrapper
+
+
 def _check(L, rc: int):
     if rc != MXQ_OK:
         raise MxqError(rc, L.mxq_status_string(rc).decode())
@@ -126,6 +146,7 @@ def _stream(t: torch.Tensor):
 
 # ---- the C entry points, one to one ---------------------------------------------------
 
+@_device_operands
 def mxq_fake_quantize_mxfp4(x: torch.Tensor, y: Optional[torch.Tensor] = None, lib: str = "libmxq.so") -> torch.Tensor:
     """MXFP4 projection of x (bf16 / fp32) into y (same dtype; y may be x)."""
     L = load(lib)
@@ -140,6 +161,7 @@ def mxq_fake_quantize_mxfp4(x: torch.Tensor, y: Optional[torch.Tensor] = None, l
     return y
 
 
+@_device_operands
 def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
                            scale_ld: Optional[int] = None, lib: str = "libmxq.so",
                            noop: Optional[torch.Tensor] = None):
@@ -164,6 +186,7 @@ def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     return data, scale
 
 
+@_device_operands
 def mxq_mxfp4_to_fp8_block128(x: torch.Tensor, data: Optional[torch.Tensor] = None,
                               tile_code: Optional[torch.Tensor] = None, lib: str = "libmxq.so",
                               noop: Optional[torch.Tensor] = None):
@@ -196,6 +219,7 @@ def _payload_for(x: torch.Tensor, rows: int, K: int, data: Optional[torch.Tensor
     return data, pd
 
 
+@_device_operands
 def mxq_mxfp4_to_mxfp8_col(x: torch.Tensor, data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
                            scale_ld: Optional[int] = None, lib: str = "libmxq.so",
                            noop: Optional[torch.Tensor] = None):
@@ -216,6 +240,7 @@ def mxq_mxfp4_to_mxfp8_col(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     return data, scale
 
 
+@_device_operands
 def mxq_mxfp4_to_mxfp8_row_col(x: torch.Tensor, row_data: Optional[torch.Tensor] = None,
                                row_scale: Optional[torch.Tensor] = None, col_data: Optional[torch.Tensor] = None,
                                col_scale: Optional[torch.Tensor] = None, row_scale_ld: Optional[int] = None,
@@ -244,6 +269,7 @@ def mxq_mxfp4_to_mxfp8_row_col(x: torch.Tensor, row_data: Optional[torch.Tensor]
     return row_data, row_scale, col_data, col_scale
 
 
+@_device_operands
 def mxq_fake_quantize_mxfp4_with_mxfp8_row(x: torch.Tensor, y: Optional[torch.Tensor] = None,
                                            data: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
                                            scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
@@ -267,6 +293,7 @@ def mxq_fake_quantize_mxfp4_with_mxfp8_row(x: torch.Tensor, y: Optional[torch.Te
     return y, data, scale
 
 
+@_device_operands
 def mxq_export_mxfp8(data: Optional[torch.Tensor], scale_storage: Optional[torch.Tensor], K: int,
                      scale_out: Optional[torch.Tensor] = None, lib: str = "libmxq.so") -> torch.Tensor:
     """Compact [rows, ceil(K/32)] copy of padded E8M0 scale storage (rows, scale_ld)."""
@@ -283,6 +310,7 @@ def mxq_export_mxfp8(data: Optional[torch.Tensor], scale_storage: Optional[torch
     return scale_out
 
 
+@_device_operands
 def mxq_dequantize(data: torch.Tensor, scale: torch.Tensor, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3,
                    out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
                    lib: str = "libmxq.so") -> torch.Tensor:
@@ -300,6 +328,7 @@ def mxq_dequantize(data: torch.Tensor, scale: torch.Tensor, layout: int = MXQ_SC
     return out
 
 
+@_device_operands
 def mxq_quantize_mxfp4(x: torch.Tensor, packed: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
                        scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
     """Packed MXFP4 (deployment format) -> (nibble pairs uint8 [rows, ceil(K/2)], E8M0 codes)."""
@@ -327,6 +356,7 @@ def _packed_args(packed: torch.Tensor, scale: torch.Tensor, K: int):
     return pp, ps, ld_s, rows
 
 
+@_device_operands
 def mxq_dequantize_mxfp4(packed: torch.Tensor, scale: torch.Tensor, K: int, out: Optional[torch.Tensor] = None,
                          out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so") -> torch.Tensor:
     """Decode packed MXFP4 into bf16 / fp32 [rows, K]."""
@@ -339,6 +369,7 @@ def mxq_dequantize_mxfp4(packed: torch.Tensor, scale: torch.Tensor, K: int, out:
     return out
 
 
+@_device_operands
 def mxq_mxfp4_packed_to_mxfp8_row(packed: torch.Tensor, scale: torch.Tensor, K: int,
                                   data: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None,
                                   lib: str = "libmxq.so"):
@@ -355,6 +386,7 @@ def mxq_mxfp4_packed_to_mxfp8_row(packed: torch.Tensor, scale: torch.Tensor, K: 
     return data, scale_out
 
 
+@_device_operands
 def mxq_mxfp4_packed_to_fp8_block128(packed: torch.Tensor, scale: torch.Tensor, K: int,
                                      data: Optional[torch.Tensor] = None, tile_code: Optional[torch.Tensor] = None,
                                      lib: str = "libmxq.so"):

@@ -167,3 +167,27 @@ def test_binding_raises_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "library_path", lambda name="libmxq.so": str(tmp_path / name))
     with pytest.raises(FileNotFoundError):
         mxq.load("libmxq_missing.so")
+
+
+def test_binding_rejects_host_tensors():
+    """The binding passes raw pointers: a host tensor must be refused before any
+    launch (it would reach a kernel as an invalid device address)."""
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    calls = [
+        lambda: mxq.mxq_fake_quantize_mxfp4(x),
+        lambda: mxq.mxq_mxfp4_to_mxfp8_row(x),
+        lambda: mxq.mxq_mxfp4_to_fp8_block128(x),
+        lambda: mxq.mxq_mxfp4_to_mxfp8_col(x),
+        lambda: mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x),
+        lambda: mxq.mxq_quantize_mxfp4(x),
+        lambda: mxq.mxq_export_mxfp8(torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(4, 4, dtype=torch.uint8), 64),
+        lambda: mxq.mxq_dequantize(torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8)),
+        lambda: mxq.mxq_dequantize_mxfp4(torch.zeros(4, 32, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8), 64),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="device tensors"):
+            call()
+    # every entry function carries the check
+    names = [n for n in dir(mxq) if n.startswith("mxq_") and callable(getattr(mxq, n))]
+    assert names and all(hasattr(getattr(mxq, n), "__wrapped__") for n in names)

@@ -421,6 +421,11 @@ def test_errors(dev):
     assert e.value.status == mxq.MXQ_ERR_SHAPE
     with pytest.raises(ValueError):
         mxq.export_components(None, None, (4, 64))
+    # a host operand beside device ones is refused before any launch
+    with pytest.raises(ValueError, match="device tensors"):
+        mxq.mxq_fake_quantize_mxfp4(xb, torch.zeros((4, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="device tensors"):
+        mxq.mxq_mxfp4_to_mxfp8_row(xb, scale=torch.zeros((4, 2), dtype=torch.uint8))
 
 
 def test_decode_every_byte_and_code(dev):
