@@ -48,7 +48,8 @@ SCALE_PAD = 4                    # padded scale storage: ceil(K/32) plus 4 colum
 SHAPES = ("8192x8192", "28672x8192", "8192x28672")
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_bf16.txt")
+# committed rocprofv3 counter summaries of the 8192 x 8192 weight, per dtype
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_{}.txt")
 # The device code: the kernels and the divisor header they include.
 KERNEL_SOURCES = [os.path.join(ROOT, "microscaling_weight_quantization_amd", "csrc", n)
                   for n in ("mxq.hip", "fastdiv.h")]
@@ -98,11 +99,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
+def read_traffic(kernel: str, weight: str = "bf16"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if there is none or the kernels changed since."""
+    summary of the 8192 x 8192 weight of that dtype, or None if there is none
+    or the kernels changed since."""
     try:
-        lines = open(COUNTERS_FILE).read().splitlines()
+        lines = open(COUNTERS_FILE.format(weight)).read().splitlines()
     except OSError:
         return None
     meta = dict(l.split("=", 1) for l in lines if "=" in l and not l.startswith("#"))
@@ -366,8 +368,8 @@ def main():
     dominant = max(names, key=lambda n: kernels[n]["us"])
     rl = {"kernel": dominant, "bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
           "unit": "GB/s", "frac": kernels[dominant]["frac"],
-          # the committed counter summary is of the 8192 x 8192 bf16 weight
-          "traffic": read_traffic(dominant) if headline and not fp32 else None}
+          # the committed counter summaries are of the 8192 x 8192 weights
+          "traffic": read_traffic(dominant, args.weight) if headline else None}
     out = {
         "metric": "GB/s and % HBM peak, MXFP4 proj + MXFP8-row/128x128 at " +
                   ("8192^2 " if headline else args.shape + " ") + args.weight,
