@@ -19,9 +19,10 @@ kernel's burst on the stream the kernels are launched on: "us" is the burst's
 mean per launch.  After the timed region a separate pass gives "us_median" /
 "us_min", the median / minimum over 5 sub-bursts of 5 launches.  Kernels
 outside the step (the fused passes, packed MXFP4, columnwise) are timed the
-same way after the step's timed region.  The default of 100 timed steps keeps
-the fixed cost of the synchronizations around the timed region (tens of us in
-all) below 1% of it.
+same way after the step's timed region, and so is the runtime's own
+device-to-device copy of the weight ("copy_reference", the projection's bytes).
+The default of 100 timed steps keeps the fixed cost of the synchronizations
+around the timed region (tens of us in all) below 1% of it.
 
 python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu] [--calibrate] [--weight bf16|fp32]
                 [--shape 8192x8192|28672x8192|8192x28672]
@@ -330,6 +331,20 @@ def main():
     run(0, SUB * SPREAD_BURSTS, True, names + extra_names, sub=SUB, store=spread)
     torch.cuda.synchronize()
 
+    # For reference: the runtime's own device-to-device copy (hipMemcpyAsync) of
+    # the weight into a buffer of the same size -- the projection's traffic --
+    # over the same rotating buffer sets (the fused pass's output buffer, which
+    # no check reads).
+    for i in range(args.warmup):
+        sets[i % NSETS]["y2"].copy_(sets[i % NSETS]["x"])
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(args.steps):
+        sets[(i + 1) % NSETS]["y2"].copy_(sets[(i + 1) % NSETS]["x"])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_us = 1e3 * c0.elapsed_time(c1) / args.steps
+
     if args.calibrate:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -395,6 +410,10 @@ def main():
         "roofline": rl,
         "kernels": kernels,
         "outside_step": extra,
+        "copy_reference": {"what": "hipMemcpyAsync device to device of the weight (torch copy_)",
+                           "us": round(copy_us, 2), "bytes": 2 * es * rows * K,
+                           "GB/s": round(2 * es * rows * K / (copy_us * 1e-6) / 1e9, 1),
+                           "frac": round(2 * es * rows * K / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu:
         out["cpu_baseline"], want = cpu_baseline(bits, threads=min(16, os.cpu_count() or 1))
