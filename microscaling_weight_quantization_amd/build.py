@@ -1,10 +1,11 @@
 """Build the gfx950 library (hipcc, in-tree).
 
 ``python -m microscaling_weight_quantization_amd.build`` writes
-``libmxq.so`` next to this file, plus two variants of the same source used by
-the build-variant tests: ``libmxq_fastmath.so`` (fast-math, denormals flushed)
-and ``libmxq_o1.so`` (-O1).  Every step of the path is integer arithmetic, so
-all three must produce identical bits.
+``libmxq.so`` next to this file, plus three variants of the same source used by
+the build-variant tests: ``libmxq_fastmath.so`` (fast-math, denormals flushed),
+``libmxq_o1.so`` (-O1) and ``libmxq_o0.so`` (-O0, no optimisation).  Every
+step of the path is integer arithmetic, so all four builds must produce
+identical bits.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ VARIANTS = {
     "libmxq.so": ["-O3"],
     "libmxq_fastmath.so": ["-O3", "-ffast-math", "-fgpu-flush-denormals-to-zero"],
     "libmxq_o1.so": ["-O1"],
+    "libmxq_o0.so": ["-O0"],
 }
 
 

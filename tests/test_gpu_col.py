@@ -161,7 +161,7 @@ def test_col_empty_and_errors(dev):
     assert e.value.status == mxq.MXQ_ERR_ALIAS
 
 
-@pytest.mark.parametrize("variant", ["libmxq_fastmath.so", "libmxq_o1.so"])
+@pytest.mark.parametrize("variant", ["libmxq_fastmath.so", "libmxq_o1.so", "libmxq_o0.so"])
 def test_col_build_variants_identical_bits(dev, variant):
     for bits in (W.c2_exhaustive(natural=True), W.fp32_fuzz(1 << 16).reshape(-1, 128), W.c3_spread()[:256, :512]):
         check_col(np.ascontiguousarray(bits), dev, lib=variant)

@@ -447,10 +447,10 @@ def test_decode_every_byte_and_code(dev):
     assert_bits(got, oracle.dequantize(data, tcodes, layout=oracle.TILE_128X128, out_dtype=oracle.FP32), "tile decode")
 
 
-@pytest.mark.parametrize("variant", ["libmxq_fastmath.so", "libmxq_o1.so"])
+@pytest.mark.parametrize("variant", ["libmxq_fastmath.so", "libmxq_o1.so", "libmxq_o0.so"])
 def test_build_variants_identical_bits(dev, variant):
-    """Same source built with fast-math + flushed denormals, and at -O1: the
-    same bits (the pages rebuild with fast math and compare)."""
+    """Same source built with fast-math + flushed denormals, at -O1 and at -O0:
+    the same bits (the pages rebuild with fast math and compare)."""
     for bits in (W.c2_exhaustive(), W.c2_planted(), W.fp32_fuzz(1 << 16).reshape(-1, 128), W.c3_spread()[:256, :512]):
         check_all(np.ascontiguousarray(bits), dev, lib=variant)
 
