@@ -78,7 +78,10 @@ enum {
   MXQ_ERR_DTYPE = 3,            /* fp16 or an unknown dtype / format / layout */
   MXQ_ERR_NO_ROWWISE_DATA = 4,  /* export without payload or scale storage ([EXP]: ValueError) */
   MXQ_ERR_ALIAS = 5,            /* an output overlaps an input (other than the allowed exact in-place) */
-  MXQ_ERR_HIP = 6               /* the HIP runtime refused a launch */
+  MXQ_ERR_HIP = 6               /* the HIP runtime refused a launch: hipGetLastError() was not
+                                   hipSuccess right after it.  That includes an error left pending by
+                                   an earlier HIP call on the calling thread, which the call then
+                                   consumes, as hipGetLastError() does. */
 };
 
 /* Human-readable text of a status code (static storage; never NULL). */
