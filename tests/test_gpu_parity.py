@@ -248,6 +248,64 @@ def test_noop_flag_inside_a_replayed_graph(dev):
         assert_bits(to_host(tc), wtc, f"replay {step} tile codes")
 
 
+def test_whole_step_in_a_replayed_graph(dev):
+    """The whole path -- projection, row lift into padded scale storage, export,
+    128x128 fold and both decodes -- captured in one HIP graph and replayed with
+    a changing weight, eager work and synchronisation between replays; every
+    replay's outputs against the oracle, bit for bit."""
+    rows, K, sld = 384, 1536, 52                      # 3 tile bands x 12 tile columns; storage padded by 4
+    nb = K // 32
+    weights = [W.c4_headline(seed=21, shape=(rows, K)), W.c3_spread(seed=22, shape=(rows, K)).view(np.uint32)]
+    weights[1] = np.ascontiguousarray((weights[1] >> 16).astype(np.uint16))   # bf16 of the spread corpus, truncated
+    x = to_dev(weights[0], dev)
+    y = torch.empty_like(x)
+    data = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+    scale = torch.zeros((rows, sld), dtype=torch.uint8, device=dev)
+    comp = torch.empty((rows, nb), dtype=torch.uint8, device=dev)
+    bdata = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+    tc = torch.empty((rows // 128, K // 128), dtype=torch.uint8, device=dev)
+    dec_r = torch.empty_like(x)
+    dec_t = torch.empty_like(x)
+
+    def step():
+        mxq.mxq_fake_quantize_mxfp4(x, y)
+        mxq.mxq_mxfp4_to_mxfp8_row(x, data, scale)
+        mxq.mxq_export_mxfp8(data, scale, K, comp)
+        mxq.mxq_mxfp4_to_fp8_block128(x, bdata, tc)
+        mxq.mxq_dequantize(data, comp, out=dec_r)
+        mxq.mxq_dequantize(bdata, tc, layout=mxq.MXQ_SCALE_TILE_128X128, out=dec_t)
+
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm up outside the graph
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for replay, which in enumerate([0, 1, 1, 0, 1]):
+        bits = weights[which]
+        x.copy_(to_dev(bits, dev))                  # eager work between replays
+        for t in (y, data, scale[:, :nb], comp, bdata, tc, dec_r, dec_t):   # the storage's padding stays
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        wd, ws = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=sld)
+        wbd, wtc = oracle.mxfp4_to_fp8_block128(bits)
+        assert_bits(to_host(y), oracle.fake_quantize_mxfp4(bits), f"replay {replay} projection")
+        assert_bits(to_host(data), wd, f"replay {replay} row payload")
+        assert_bits(to_host(scale)[:, :nb], ws[:, :nb], f"replay {replay} row codes")
+        assert not to_host(scale)[:, nb:].any(), f"replay {replay}: scale padding written"
+        assert_bits(to_host(comp), oracle.export_mxfp8(ws, K), f"replay {replay} export")
+        assert_bits(to_host(bdata), wbd, f"replay {replay} 128x128 payload")
+        assert_bits(to_host(tc), wtc, f"replay {replay} tile codes")
+        assert_bits(to_host(dec_r), oracle.dequantize(wd, ws[:, :nb], out_dtype=oracle.BF16), f"replay {replay} row decode")
+        assert_bits(to_host(dec_t), oracle.dequantize(wbd, wtc, layout=oracle.TILE_128X128, out_dtype=oracle.BF16),
+                    f"replay {replay} tile decode")
+
+
 # ------------------------------------------------------------------ packed MXFP4 (deployment format)
 
 def check_packed(bits: np.ndarray, dev, scale_ld=None):
