@@ -1,0 +1,128 @@
+/*
+ * A plain C caller of the library: no PyTorch, only the HIP runtime's C API and
+ * include/mxq.h.  It runs the whole path on one bf16 weight read from a file --
+ * projection, row lift into padded scale storage, export, 128x128 fold and both
+ * decodes -- on a stream of its own, checks every status, and writes the outputs
+ * to a file for the test (tests/test_gpu_c_caller.py) to compare with the oracle.
+ * It also checks that argument errors come back as status codes before any
+ * launch.
+ *
+ * usage: c_caller ROWS K SCALE_LD IN.bin OUT.bin
+ *   IN.bin   ROWS*K bf16 bit patterns (uint16, little endian)
+ *   OUT.bin  y (bf16), data, exported codes, tile payload, tile codes,
+ *            row decode (bf16), tile decode (bf16), concatenated in that order
+ */
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "mxq.h"
+
+#define HIP_OK(call)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) {                                                             \
+      fprintf(stderr, "c_caller: %s failed: %s\n", #call, hipGetErrorString(e_));      \
+      exit(2);                                                                          \
+    }                                                                                   \
+  } while (0)
+
+#define MXQ_OK_OR_DIE(call)                                                             \
+  do {                                                                                  \
+    int s_ = (call);                                                                    \
+    if (s_ != MXQ_OK) {                                                                 \
+      fprintf(stderr, "c_caller: %s returned %d (%s)\n", #call, s_, mxq_status_string(s_)); \
+      exit(3);                                                                          \
+    }                                                                                   \
+  } while (0)
+
+int main(int argc, char** argv) {
+  if (argc != 6) {
+    fprintf(stderr, "usage: %s ROWS K SCALE_LD IN.bin OUT.bin\n", argv[0]);
+    return 1;
+  }
+  const int64_t rows = atoll(argv[1]), K = atoll(argv[2]), sld = atoll(argv[3]);
+  const int64_t nb = (K + 31) / 32, tr = (rows + 127) / 128, tcn = (K + 127) / 128, n = rows * K;
+  if (rows <= 0 || K <= 0 || sld < nb) {
+    fprintf(stderr, "c_caller: bad shape\n");
+    return 1;
+  }
+
+  uint16_t* hx = (uint16_t*)malloc((size_t)n * 2);
+  FILE* f = fopen(argv[4], "rb");
+  if (!hx || !f || fread(hx, 2, (size_t)n, f) != (size_t)n) {
+    fprintf(stderr, "c_caller: cannot read %s\n", argv[4]);
+    return 1;
+  }
+  fclose(f);
+
+  /* Argument errors: status codes, nothing enqueued. */
+  if (mxq_fake_quantize_mxfp4(NULL, K, NULL, K, rows, -1, MXQ_BF16, 0) != MXQ_ERR_SHAPE ||
+      mxq_fake_quantize_mxfp4(hx, K, hx, K, rows, K, MXQ_FP16, 0) != MXQ_ERR_DTYPE ||
+      mxq_export_mxfp8(NULL, NULL, rows, K, sld, NULL, 0) != MXQ_ERR_NO_ROWWISE_DATA ||
+      strlen(mxq_status_string(MXQ_ERR_ALIAS)) == 0) {
+    fprintf(stderr, "c_caller: argument checks did not return the documented codes\n");
+    return 4;
+  }
+
+  void *x, *y, *dec_r, *dec_t;
+  uint8_t *data, *scale, *comp, *bdata, *tc;
+  HIP_OK(hipMalloc(&x, (size_t)n * 2));
+  HIP_OK(hipMalloc(&y, (size_t)n * 2));
+  HIP_OK(hipMalloc(&dec_r, (size_t)n * 2));
+  HIP_OK(hipMalloc(&dec_t, (size_t)n * 2));
+  HIP_OK(hipMalloc((void**)&data, (size_t)n));
+  HIP_OK(hipMalloc((void**)&scale, (size_t)(rows * sld)));
+  HIP_OK(hipMalloc((void**)&comp, (size_t)(rows * nb)));
+  HIP_OK(hipMalloc((void**)&bdata, (size_t)n));
+  HIP_OK(hipMalloc((void**)&tc, (size_t)(tr * tcn)));
+  HIP_OK(hipMemcpy(x, hx, (size_t)n * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemset(scale, 0, (size_t)(rows * sld)));
+
+  hipStream_t s;
+  HIP_OK(hipStreamCreate(&s));
+  MXQ_OK_OR_DIE(mxq_fake_quantize_mxfp4(x, K, y, K, rows, K, MXQ_BF16, s));
+  MXQ_OK_OR_DIE(mxq_mxfp4_to_mxfp8_row(x, K, rows, K, MXQ_BF16, data, scale, sld, s));
+  MXQ_OK_OR_DIE(mxq_export_mxfp8(data, scale, rows, K, sld, comp, s));
+  MXQ_OK_OR_DIE(mxq_mxfp4_to_fp8_block128(x, K, rows, K, MXQ_BF16, bdata, tc, tcn, s));
+  MXQ_OK_OR_DIE(mxq_dequantize(data, comp, nb, rows, K, MXQ_E4M3, MXQ_SCALE_ROW_1X32, dec_r, K, MXQ_BF16, s));
+  MXQ_OK_OR_DIE(mxq_dequantize(bdata, tc, tcn, rows, K, MXQ_E4M3, MXQ_SCALE_TILE_128X128, dec_t, K, MXQ_BF16, s));
+  /* an overlap is refused: the payload written over the weight */
+  if (mxq_mxfp4_to_mxfp8_row(x, K, rows, K, MXQ_BF16, (uint8_t*)x, scale, sld, s) != MXQ_ERR_ALIAS) {
+    fprintf(stderr, "c_caller: an aliased output was not refused\n");
+    return 4;
+  }
+  HIP_OK(hipStreamSynchronize(s));
+
+  const size_t sizes[7] = {(size_t)n * 2, (size_t)n, (size_t)(rows * nb), (size_t)n, (size_t)(tr * tcn),
+                           (size_t)n * 2, (size_t)n * 2};
+  const void* bufs[7] = {y, data, comp, bdata, tc, dec_r, dec_t};
+  FILE* o = fopen(argv[5], "wb");
+  if (!o) {
+    fprintf(stderr, "c_caller: cannot write %s\n", argv[5]);
+    return 1;
+  }
+  for (int i = 0; i < 7; i++) {
+    void* h = malloc(sizes[i]);
+    HIP_OK(hipMemcpy(h, bufs[i], sizes[i], hipMemcpyDeviceToHost));
+    if (fwrite(h, 1, sizes[i], o) != sizes[i]) {
+      fprintf(stderr, "c_caller: short write\n");
+      return 1;
+    }
+    free(h);
+  }
+  fclose(o);
+  HIP_OK(hipStreamDestroy(s));
+  HIP_OK(hipFree(x));
+  HIP_OK(hipFree(y));
+  HIP_OK(hipFree(dec_r));
+  HIP_OK(hipFree(dec_t));
+  HIP_OK(hipFree(data));
+  HIP_OK(hipFree(scale));
+  HIP_OK(hipFree(comp));
+  HIP_OK(hipFree(bdata));
+  HIP_OK(hipFree(tc));
+  free(hx);
+  printf("c_caller: ok\n");
+  return 0;
+}
