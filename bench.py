@@ -369,7 +369,9 @@ def main():
         us, med, lo = burst_stats(n)
         gbs = nbytes[n] / (us * 1e-6) / 1e9
         kernels[n] = {"us": round(us, 2), "us_median": round(med, 2), "us_min": round(lo, 2), "bytes": nbytes[n],
-                      "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                      "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      # HBM bytes per launch from the committed counters (8192 x 8192 weights)
+                      "traffic": read_traffic(n, args.weight) if headline else None}
     extra = {}
     extra_bytes = dict(packed_bytes(rows, K, es), fused=fused_bytes(rows, K, es), **col_bytes(rows, K, es))
     for n in extra_names:
@@ -377,7 +379,8 @@ def main():
         gbs = extra_bytes[n] / (us * 1e-6) / 1e9
         extra["fused_proj_row" if n == "fused" else n] = {"us": round(us, 2), "us_median": round(med, 2),
                                                           "us_min": round(lo, 2), "bytes": extra_bytes[n],
-                                                          "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                                                          "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                                          "traffic": read_traffic(n, args.weight) if headline else None}
     extra["fused_proj_row"]["vs_separate_us"] = round(kernels["proj"]["us"] + kernels["row"]["us"], 2)
     extra["row_col"]["vs_separate_us"] = round(kernels["row"]["us"] + extra["col"]["us"], 2)
     dominant = max(names, key=lambda n: kernels[n]["us"])
