@@ -84,7 +84,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 // The banded kernels.
 #ifndef MXQ_PFOLD_ROWS
-#define MXQ_PFOLD_ROWS 16         // fold from packed MXFP4: band rows per lane (16, 8 or 4)
+#define MXQ_PFOLD_ROWS 8          // fold from packed MXFP4: band rows per lane (16, 8 or 4)
 #endif
 #ifndef MXQ_COL_THREADS
 #define MXQ_COL_THREADS 64        // columnwise: column lanes per workgroup, one 16-byte chunk each
