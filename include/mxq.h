@@ -7,10 +7,11 @@
  *   mxq_mxfp4_to_fp8_block128   direct 128x128 blockwise FP8 (E4M3 payload + tile codes)
  *   mxq_export_mxfp8            unpadded (*shape[:-1], ceil(K/32)) E8M0 scale export
  *   mxq_dequantize              FP8 payload + E8M0 codes -> bf16 / fp32
- * three variants of them:
+ * variants of them:
  *   mxq_fake_quantize_mxfp4_with_mxfp8_row    projection + row lift in one pass
  *   mxq_mxfp4_to_mxfp8_row_guarded,
  *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
+ *   mxq_mxfp4_to_mxfp8_row_grouped            the row lift of a list of weights in few launches
  * the packed MXFP4 deployment format:
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
  *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
@@ -171,6 +172,36 @@ int mxq_mxfp4_to_mxfp8_row_guarded(const void* x, int64_t ld_x, int64_t rows, in
 int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
                                       uint8_t* data, uint8_t* tile_code, int64_t tile_ld, const int32_t* noop,
                                       hipStream_t stream);
+
+/*
+ * One weight of a grouped row lift: the arguments of mxq_mxfp4_to_mxfp8_row for
+ * that weight (x, data and scale are device pointers).
+ */
+typedef struct {
+  const void* x;      /* [rows, K], row stride ld_x >= K */
+  int64_t ld_x;
+  int64_t rows;
+  int64_t K;
+  uint8_t* data;      /* [rows, K] E4M3 payload, contiguous */
+  uint8_t* scale;     /* [rows, scale_ld] E8M0 codes, scale_ld >= ceil(K/32); padding not written */
+  int64_t scale_ld;
+} mxq_row_group;
+
+/*
+ * The direct MXFP8 row lift of mxq_mxfp4_to_mxfp8_row applied to a list of
+ * weights of one dtype (the experts of a grouped linear layer, [QAT] Test
+ * results, end-to-end cases), in as few launches as possible: every launch
+ * carries a fixed cost of a few microseconds, which dominates for small weights.
+ * Results are bit-identical to one mxq_mxfp4_to_mxfp8_row call per weight.
+ *   groups    HOST array of n_groups descriptors, read during the call only
+ *   n_groups  >= 0; groups with rows == 0 or K == 0 are skipped
+ *   Every group is checked as mxq_mxfp4_to_mxfp8_row checks its arguments (the
+ *   first failing group's status is returned and nothing is enqueued).  In
+ *   addition no group's data or scale may overlap any group's x, data or scale
+ *   (MXQ_ERR_ALIAS); inputs may overlap each other.
+ */
+int mxq_mxfp4_to_mxfp8_row_grouped(const mxq_row_group* groups, int64_t n_groups, mxq_dtype dt,
+                                   hipStream_t stream);
 
 /*
  * MXFP8 columnwise from the MXFP4 decomposition ([QAT] Description, conversion

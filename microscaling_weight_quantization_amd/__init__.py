@@ -36,10 +36,17 @@ ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mx
                 "mxq_fake_quantize_mxfp4_with_mxfp8_row", "mxq_mxfp4_to_mxfp8_row_guarded",
                 "mxq_mxfp4_to_fp8_block128_guarded", "mxq_quantize_mxfp4", "mxq_dequantize_mxfp4",
                 "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
-                "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded")
+                "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded",
+                "mxq_mxfp4_to_mxfp8_row_grouped")
 
 _libs = {}
 _lock = threading.Lock()
+
+
+class _RowGroup(ctypes.Structure):
+    """mxq_row_group of include/mxq.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_ld", ctypes.c_int64)]
 
 
 class MxqError(RuntimeError):
@@ -77,6 +84,7 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_mxfp4_to_mxfp8_row_col.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp]
         L.mxq_mxfp4_to_mxfp8_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
         L.mxq_mxfp4_to_mxfp8_row_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp, vp]
+        L.mxq_mxfp4_to_mxfp8_row_grouped.argtypes = [ctypes.POINTER(_RowGroup), i64, i32, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -184,6 +192,48 @@ def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     else:
         _check(L, L.mxq_mxfp4_to_mxfp8_row_guarded(px, ldx, rows, K, dt, pd, ps, ld_s, _flag(noop), _stream(x)))
     return data, scale
+
+
+@_device_operands
+def mxq_mxfp4_to_mxfp8_row_grouped(xs, datas=None, scales=None, scale_ld: Optional[int] = None,
+                                   lib: str = "libmxq.so"):
+    """Direct MXFP8 rowwise lift of a list of weights of one dtype, in as few
+    launches as possible -> (list of payloads, list of E8M0 codes); the same
+    bytes as one mxq_mxfp4_to_mxfp8_row per weight.  `datas` / `scales`: lists
+    of outputs (None entries, or None for the whole list, are allocated)."""
+    L = load(lib)
+    xs = list(xs)
+    n = len(xs)
+    datas = [None] * n if datas is None else list(datas)
+    scales = [None] * n if scales is None else list(scales)
+    if len(datas) != n or len(scales) != n:
+        raise ValueError("datas and scales must have one entry per weight")
+    if n == 0:
+        return [], []
+    dev, dtype = xs[0].device, xs[0].dtype
+    for t in xs + datas + scales:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+            raise ValueError("mxq_mxfp4_to_mxfp8_row_grouped: operands must be device tensors on one device")
+    if any(x.dtype != dtype for x in xs):
+        raise ValueError("all weights of a group call must have one dtype")
+    dt = _dtype_code(xs[0])
+    table = (_RowGroup * n)()
+    for i, x in enumerate(xs):
+        px, rows, K, ldx = _matrix(x)
+        nb = (K + 31) // 32
+        if scales[i] is None:
+            scales[i] = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=dev)
+        if datas[i] is None:
+            datas[i] = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+        pd, _, _, ldd = _matrix(datas[i])
+        ps, _, _, ld_s = _matrix(scales[i])
+        if rows * K and (ldd != K or datas[i].numel() != rows * K):
+            raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+        table[i] = _RowGroup(px, ldx, rows, K, pd, ps, ld_s)
+    _check(L, L.mxq_mxfp4_to_mxfp8_row_grouped(table, n, dt, _stream(xs[0])))
+    return datas, scales
 
 
 @_device_operands

@@ -519,6 +519,72 @@ __device__ __forceinline__ uint32_t e4m3x4_each(uint32_t y01, uint32_t y23, floa
   return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, c), 0x07020100u);
 }
 
+// Grouped row lift: the row lift of up to kGroupMax weights in one launch.  Each
+// weight's steps are padded to whole workgroups, so a workgroup lies in one
+// weight; it finds that weight by a binary search of the table's first
+// workgroups (the table is a kernel argument, so the search is scalar), then
+// runs the row lift's steps on it.  Aligned (VEC) weights only; the host launches the
+// others one by one.
+constexpr int kGroupMax = 48;
+struct RowGroupDesc {
+  const void* x;
+  int64_t ld_x, K;
+  uint8_t* data;
+  uint8_t* scale;
+  int64_t scale_ld;
+  MxqDivisor steps_per_row;
+  uint32_t total_steps;
+};
+struct RowGroupTable {
+  uint32_t n;
+  uint32_t wg0[kGroupMax + 1];   // first workgroup of each weight; wg0[n] = the grid size
+  RowGroupDesc g[kGroupMax];
+};
+static_assert(sizeof(RowGroupTable) <= 3584, "the table must fit the kernel-argument segment");
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void row_grouped_kernel(const RowGroupTable tab) {
+  using G = StepGeom<T, kRowThreads>;
+  keep_denormals();
+  const uint32_t tid = threadIdx.x, b = blockIdx.x;
+  // the last weight whose first workgroup is <= b: wg0 increases strictly
+  // (no weight has zero workgroups), wg0[0] = 0 <= b < wg0[n]
+  uint32_t gi = 0, hi = tab.n;
+  while (hi - gi > 1u) {
+    const uint32_t mid = (gi + hi) >> 1;
+    if (tab.wg0[mid] <= b) gi = mid;
+    else hi = mid;
+  }
+  const RowGroupDesc& d = tab.g[gi];
+  const T* x = static_cast<const T*>(d.x);
+  const uint32_t lwg = b - tab.wg0[gi];
+  const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
+  u32x4 w[kRowSteps];
+#pragma unroll
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = lwg * kRowSteps + u;
+    w[u] = u32x4{0u, 0u, 0u, 0u};
+    if (step < d.total_steps) {
+      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
+      w[u] = load_chunk<T, true>(x + (int64_t)row * d.ld_x, seg * G::kElemsPerStep + lane_col, d.K);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowSteps; u++) {
+    const uint32_t step = lwg * kRowSteps + u;
+    if (step < d.total_steps) {
+      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
+      const int64_t col0 = seg * G::kElemsPerStep + lane_col;
+      const Block bl = chunk_block<T>(w[u]);
+      const float s = e8m0(bl.eb);
+      const uint32_t code = row_code(bl);
+      const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
+      store_payload<T, true>(d.data + (int64_t)row * d.K, col0, d.K, payload_chunk<T>(p, code, bl.poison));
+      if (tid % G::kLPB == 0 && col0 < d.K) d.scale[(int64_t)row * d.scale_ld + col0 / 32] = (uint8_t)code;
+    }
+  }
+}
+
 template <typename T, bool VEC, bool kRow>
 __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
     const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* __restrict__ cdata,
@@ -1555,6 +1621,46 @@ int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t
   return launch_status();
 }
 
+// Grouped row lift: aligned weights go into tables of up to kGroupMax, one
+// launch per table; the others take the single-weight launch.  The caller has
+// checked every group (shapes, spans, step counts, aliasing) beforehand.
+template <typename T>
+int launch_row_grouped(const mxq_row_group* gs, int64_t n, hipStream_t s) {
+  constexpr int EPL = Fmt<T>::kEPL;
+  RowGroupTable tab{};
+  int64_t wgs = 0;
+  auto flush = [&]() -> int {
+    if (tab.n == 0) return MXQ_OK;
+    tab.wg0[tab.n] = (uint32_t)wgs;
+    hipLaunchKernelGGL((row_grouped_kernel<T>), dim3((uint32_t)wgs), dim3(kRowThreads), 0, s, tab);
+    tab.n = 0;
+    wgs = 0;
+    return launch_status();
+  };
+  for (int64_t i = 0; i < n; i++) {
+    const mxq_row_group& g = gs[i];
+    if (g.rows == 0 || g.K == 0) continue;
+    if (!(aligned(g.x, 16) && g.ld_x % EPL == 0 && g.K % EPL == 0 && aligned(g.data, EPL))) {
+      const int st = launch_row<T>(g.x, g.ld_x, g.rows, g.K, g.data, g.scale, g.scale_ld, nullptr, 0, nullptr, s);
+      if (st != MXQ_OK) return st;
+      continue;
+    }
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t gw = grid_for(total, kRowSteps);
+    if (tab.n == (uint32_t)kGroupMax || wgs + gw >= kMaxSteps) {
+      const int st = flush();
+      if (st != MXQ_OK) return st;
+    }
+    tab.wg0[tab.n] = (uint32_t)wgs;
+    tab.g[tab.n] = RowGroupDesc{g.x, g.ld_x, g.K, g.data, g.scale, g.scale_ld, spr, total};
+    tab.n++;
+    wgs += gw;
+  }
+  return flush();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1588,12 +1694,19 @@ int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y, 
                         : launch_proj<uint32_t>(x, ld_x, y, ld_y, rows, K, stream);
 }
 
-static int row_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+// Argument checks of the row lift (and its fused and gated forms).  For a
+// non-empty matrix it returns MXQ_OK with *ranges = {x, data, scale}; for an
+// empty one MXQ_OK with *empty set.
+static int row_check(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
                      uint8_t* scale, int64_t scale_ld, void* y, int64_t ld_y, bool need_y, const int32_t* noop,
-                     bool need_noop, hipStream_t stream) {
+                     bool need_noop, Range* ranges, bool* empty) {
+  *empty = false;
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (rows == 0 || K == 0) return MXQ_OK;
+  if (rows == 0 || K == 0) {
+    *empty = true;
+    return MXQ_OK;
+  }
   if (!x || !data || !scale || (need_noop && !noop) || (need_y && !y)) return MXQ_ERR_NULL;
   const int64_t nb = (K + 31) / 32;
   if (ld_x < K || scale_ld < nb || (y && ld_y < K)) return MXQ_ERR_SHAPE;
@@ -1608,6 +1721,17 @@ static int row_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_d
     const bool in_place = (x == y) && (ld_x == ld_y);
     if ((!in_place && overlap(rx, ry)) || overlap(ry, rd) || overlap(ry, rs)) return MXQ_ERR_ALIAS;
   }
+  ranges[0] = rx, ranges[1] = rd, ranges[2] = rs;
+  return MXQ_OK;
+}
+
+static int row_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                     uint8_t* scale, int64_t scale_ld, void* y, int64_t ld_y, bool need_y, const int32_t* noop,
+                     bool need_noop, hipStream_t stream) {
+  Range r[3];
+  bool empty;
+  const int st = row_check(x, ld_x, rows, K, dt, data, scale, scale_ld, y, ld_y, need_y, noop, need_noop, r, &empty);
+  if (st != MXQ_OK || empty) return st;
   return dt == MXQ_BF16 ? launch_row<uint16_t>(x, ld_x, rows, K, data, scale, scale_ld, y, ld_y, noop, stream)
                         : launch_row<uint32_t>(x, ld_x, rows, K, data, scale, scale_ld, y, ld_y, noop, stream);
 }
@@ -1655,6 +1779,48 @@ int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows,
                                       uint8_t* data, uint8_t* tile_code, int64_t tile_ld, const int32_t* noop,
                                       hipStream_t stream) {
   return block128_entry(x, ld_x, rows, K, dt, data, tile_code, tile_ld, noop, true, stream);
+}
+
+int mxq_mxfp4_to_mxfp8_row_grouped(const mxq_row_group* groups, int64_t n_groups, mxq_dtype dt,
+                                   hipStream_t stream) {
+  if (check_dtype(dt)) return MXQ_ERR_DTYPE;
+  if (n_groups < 0) return MXQ_ERR_SHAPE;
+  if (n_groups == 0) return MXQ_OK;
+  if (!groups) return MXQ_ERR_NULL;
+  const int64_t eps = dt == MXQ_BF16 ? StepGeom<uint16_t, kRowThreads>::kElemsPerStep
+                                     : StepGeom<uint32_t, kRowThreads>::kElemsPerStep;
+  // every group on its own, then no output may overlap any other range
+  std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
+  iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 3);
+  for (int64_t i = 0; i < n_groups; i++) {
+    const mxq_row_group& g = groups[i];
+    Range r[3];
+    bool empty;
+    const int st = row_check(g.x, g.ld_x, g.rows, g.K, dt, g.data, g.scale, g.scale_ld, nullptr, 0, false, nullptr,
+                             false, r, &empty);
+    if (st != MXQ_OK) return st;
+    if (empty) continue;
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, eps, &spr, &total)) return MXQ_ERR_SHAPE;
+    iv.push_back({r[0], false});
+    iv.push_back({r[1], true});
+    iv.push_back({r[2], true});
+  }
+  // sweep in order of start address: a range overlaps an earlier one exactly
+  // when it starts before the largest end seen so far
+  std::sort(iv.begin(), iv.end(), [](const std::pair<Range, bool>& a, const std::pair<Range, bool>& b) {
+    return a.first.lo < b.first.lo;
+  });
+  uintptr_t end_out = 0, end_in = 0;
+  for (const auto& e : iv) {
+    const Range& r = e.first;
+    if (e.second ? r.lo < std::max(end_out, end_in) : r.lo < end_out) return MXQ_ERR_ALIAS;
+    uintptr_t& end = e.second ? end_out : end_in;
+    end = std::max(end, r.hi);
+  }
+  return dt == MXQ_BF16 ? launch_row_grouped<uint16_t>(groups, n_groups, stream)
+                        : launch_row_grouped<uint32_t>(groups, n_groups, stream);
 }
 
 static int col_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* row_data,

@@ -191,3 +191,38 @@ def test_binding_rejects_host_tensors():
     # every entry function carries the check
     names = [n for n in dir(mxq) if n.startswith("mxq_") and callable(getattr(mxq, n))]
     assert names and all(hasattr(getattr(mxq, n), "__wrapped__") for n in names)
+
+
+def test_grouped_row_lift_host_validation(lib):
+    """The grouped row lift checks every group as the single call does, and
+    refuses any output that overlaps another group's input or output -- all
+    before anything is enqueued (fake addresses; no GPU is touched)."""
+    G = mxq._RowGroup
+
+    def grp(x, data, scale, rows=4, K=64, ld=64, sld=2):
+        return G(x, ld, rows, K, data, scale, sld)
+
+    def call(*groups, dt=mxq.MXQ_BF16, n=None):
+        arr = (G * max(len(groups), 1))(*groups)
+        return lib.mxq_mxfp4_to_mxfp8_row_grouped(arr, len(groups) if n is None else n, dt, None)
+
+    # 4 x 64 bf16 weights take 512 bytes; payloads 256 bytes; codes 8 bytes
+    a = grp(0x100000, 0x200000, 0x300000)
+    b = grp(0x110000, 0x210000, 0x310000)
+    assert call(a, b, n=-1) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_mxfp8_row_grouped(None, 2, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_NULL
+    assert lib.mxq_mxfp4_to_mxfp8_row_grouped(None, 0, mxq.MXQ_BF16, None) == mxq.MXQ_OK
+    assert call(a, b, dt=mxq.MXQ_FP16) == mxq.MXQ_ERR_DTYPE
+    # a bad group anywhere in the list is reported
+    assert call(a, grp(0x110000, 0x210000, 0x310000, K=-1)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, grp(None, 0x210000, 0x310000)) == mxq.MXQ_ERR_NULL
+    assert call(a, grp(0x110000, 0x210000, 0x310000, sld=1)) == mxq.MXQ_ERR_SHAPE
+    assert call(grp(0x100000, 0x100100, 0x300000), b) == mxq.MXQ_ERR_ALIAS          # within one group
+    # across groups: an output over another group's input, over another output
+    assert call(a, grp(0x110000, 0x100100, 0x310000)) == mxq.MXQ_ERR_ALIAS          # b's payload in a's weight
+    assert call(a, grp(0x110000, 0x210000, 0x2000F0)) == mxq.MXQ_ERR_ALIAS          # b's codes in a's payload
+    assert call(a, grp(0x110000, 0x200080, 0x310000)) == mxq.MXQ_ERR_ALIAS          # two payloads overlap
+    assert call(a, grp(0x110000, 0x210000, 0x300004)) == mxq.MXQ_ERR_ALIAS          # two code arrays overlap
+    assert call(grp(0x110000, 0x210000, 0x310000), grp(0x2100F0, 0x220000, 0x320000)) == mxq.MXQ_ERR_ALIAS  # an input over an output
+    # empty groups only: nothing to do
+    assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK

@@ -1,0 +1,89 @@
+"""The grouped row lift (mxq_mxfp4_to_mxfp8_row_grouped) against the oracle:
+mixed ragged shapes in one call, padded scale storage left untouched, a
+misaligned weight (the per-weight path), empty weights, and more weights than
+one launch's table holds."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_weight_quantization_amd as mxq
+import oracle
+import workloads as W
+
+from .test_gpu_parity import THREADS, assert_bits, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return torch.device("cuda:0")
+
+
+def _weight(rows, K, dtype, seed):
+    if dtype == "bf16":
+        return W.c4_headline(seed=seed, shape=(rows, K)) if rows * K else np.zeros((rows, K), np.uint16)
+    flat = W.fp32_fuzz(((rows * K + 31) // 32) * 32 + 32, seed=seed).reshape(-1)
+    return np.ascontiguousarray(flat[: rows * K].reshape(rows, K))
+
+
+def _check_groups(dev, weights, xs, pads):
+    scales = [torch.full((b.shape[0], (b.shape[1] + 31) // 32 + p), 0xA5, dtype=torch.uint8, device=dev)
+              for b, p in zip(weights, pads)]
+    datas, scales = mxq.mxq_mxfp4_to_mxfp8_row_grouped(xs, scales=scales)
+    for i, (bits, d, s, p) in enumerate(zip(weights, datas, scales, pads)):
+        rows, K = bits.shape
+        if rows * K == 0:
+            continue
+        wd, ws = oracle.mxfp4_to_mxfp8_row(bits, scale_ld=(K + 31) // 32 + p, threads=THREADS, fill=0xA5)
+        assert_bits(to_host(d), wd, f"group {i} ({rows}x{K}) payload")
+        assert_bits(to_host(s), ws, f"group {i} ({rows}x{K}) codes, padding untouched")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_grouped_mixed_shapes(dev, dtype):
+    shapes = [(100, 48), (257, 1000), (64, 4096), (1, 33), (300, 2048), (0, 64), (128, 130), (33, 7), (513, 256)]
+    weights = [_weight(r, k, dtype, 40 + i) for i, (r, k) in enumerate(shapes)]
+    xs = [to_dev(b, dev) if b.size else torch.empty(b.shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                                   device=dev) for b in weights]
+    _check_groups(dev, weights, xs, pads=[i % 5 for i in range(len(shapes))])
+
+
+def test_grouped_with_a_misaligned_weight(dev):
+    """A weight that is a view one element into its storage cannot take the
+    16-byte path; the call converts it on its own and the rest grouped."""
+    weights = [_weight(96, 512, "bf16", 60), _weight(70, 300, "bf16", 61), _weight(128, 256, "bf16", 62)]
+    base = to_dev(np.concatenate([np.zeros((70, 1), np.uint16), weights[1]], axis=1), dev)
+    xs = [to_dev(weights[0], dev), base[:, 1:], to_dev(weights[2], dev)]
+    assert xs[1].data_ptr() % 16 != 0
+    _check_groups(dev, weights, xs, pads=[0, 3, 1])
+
+
+def test_grouped_more_weights_than_one_table(dev):
+    """130 weights: several launches' worth of tables; every output equals the
+    single-weight call and the oracle."""
+    rng = np.random.default_rng(70)
+    weights = []
+    for i in range(130):
+        rows, K = int(rng.integers(1, 200)), int(rng.choice([32, 64, 96, 200, 512, 1024, 1500]))
+        weights.append(_weight(rows, K, "bf16", 100 + i))
+    xs = [to_dev(b, dev) for b in weights]
+    _check_groups(dev, weights, xs, pads=[0] * len(weights))
+    for i in (0, 47, 48, 129):
+        d1, s1 = mxq.mxq_mxfp4_to_mxfp8_row(xs[i])
+        d2, s2 = mxq.mxq_mxfp4_to_mxfp8_row_grouped([xs[i]])
+        assert torch.equal(d1, d2[0]) and torch.equal(s1, s2[0])
+
+
+def test_grouped_overlapping_outputs_are_refused(dev):
+    a = to_dev(_weight(64, 256, "bf16", 80), dev)
+    b = to_dev(_weight(64, 256, "bf16", 81), dev)
+    data = torch.empty((64, 256), dtype=torch.uint8, device=dev)
+    with pytest.raises(mxq.MxqError) as e:
+        mxq.mxq_mxfp4_to_mxfp8_row_grouped([a, b], datas=[data, data])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
+    # the same input twice is fine (inputs may overlap)
+    d, s = mxq.mxq_mxfp4_to_mxfp8_row_grouped([a, a])
+    assert torch.equal(d[0], d[1]) and torch.equal(s[0], s[1])
