@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 SCALE_PAD = 4                    # padded scale storage: ceil(K/32) plus 4 columns (8192: 260)
+GROUPED = (48, 1024, 2048)       # outside the step: the grouped row lift of 48 weights of 1024 x 2048 (one launch)
 SHAPES = ("8192x8192", "28672x8192", "8192x28672")
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
@@ -230,6 +231,11 @@ def main():
     scale_ld = nb + SCALE_PAD
     x0 = (torch.from_numpy(bits.view(np.int32)).to(dev).view(torch.float32) if fp32
           else torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16))
+    gn, gr, gk = GROUPED
+    gen = torch.Generator().manual_seed(4)
+    g_host = (torch.randn(gn, gr, gk, generator=gen) * 0.02).to(torch.float32 if fp32 else torch.bfloat16)
+    g0 = g_host.to(dev)
+    del g_host
     sets = []
     for i in range(NSETS):
         s = {
@@ -252,6 +258,9 @@ def main():
             "scale2": torch.zeros((rows, scale_ld), dtype=torch.uint8, device=dev),
             "cdata": torch.empty((rows, K), dtype=torch.uint8, device=dev),
             "cscale": torch.empty(((rows + 31) // 32, K), dtype=torch.uint8, device=dev),
+            "gx": list(g0.clone().unbind(0)),
+            "gdata": [torch.empty((gr, gk), dtype=torch.uint8, device=dev) for _ in range(gn)],
+            "gscale": [torch.zeros((gr, gk // 32), dtype=torch.uint8, device=dev) for _ in range(gn)],
         }
         mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
         mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
@@ -259,7 +268,7 @@ def main():
         mxq.mxq_quantize_mxfp4(s["x"], s["packed"], s["pscale"])
         mxq.mxq_mxfp4_to_mxfp8_col(s["x"], s["cdata"], s["cscale"])
         sets.append(s)
-    del x0
+    del x0, g0
     torch.cuda.synchronize()
 
     names = ["proj", "row", "export", "block128", "dec_row", "dec_tile"]
@@ -287,12 +296,17 @@ def main():
                                                                      s["cscale"])
     launches["dec_col"] = lambda s: mxq.mxq_dequantize(s["cdata"], s["cscale"], layout=mxq.MXQ_SCALE_COL_32X1,
                                                        out=s["dec_c"])
+    # outside the step: the row lift of 48 weights of 1024 x 2048 in one grouped call
+    # (prepared once per buffer set, as for weights re-converted every step)
+    for s in sets:
+        s["grouped"] = mxq.GroupedRowLift(s["gx"], s["gdata"], s["gscale"])
+    launches["row_grouped"] = lambda s: s["grouped"]()
     extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128", "col",
-                   "row_col", "dec_col"]
+                   "row_col", "dec_col", "row_grouped"]
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
     offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1,
               "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0, "col": 2,
-              "row_col": 4, "dec_col": 1}
+              "row_col": 4, "dec_col": 1, "row_grouped": 0}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -373,7 +387,8 @@ def main():
                       # HBM bytes per launch from the committed counters (8192 x 8192 weights)
                       "traffic": read_traffic(n, args.weight) if headline else None}
     extra = {}
-    extra_bytes = dict(packed_bytes(rows, K, es), fused=fused_bytes(rows, K, es), **col_bytes(rows, K, es))
+    extra_bytes = dict(packed_bytes(rows, K, es), fused=fused_bytes(rows, K, es), **col_bytes(rows, K, es),
+                       row_grouped=gn * algorithmic_bytes(gr, gk, es)["row"])
     for n in extra_names:
         us, med, lo = burst_stats(n)
         gbs = extra_bytes[n] / (us * 1e-6) / 1e9

@@ -194,46 +194,65 @@ def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     return data, scale
 
 
+class GroupedRowLift:
+    """The grouped row lift prepared once for a fixed list of weights and
+    outputs: the descriptor table is built here, and each call enqueues the
+    conversion on torch's current stream with one call into the library (for
+    weights that are re-converted every training step).  The object keeps the
+    tensors alive; `datas` / `scales` are the outputs."""
+
+    def __init__(self, xs, datas=None, scales=None, scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+        self._L = load(lib)
+        xs = list(xs)
+        n = len(xs)
+        datas = [None] * n if datas is None else list(datas)
+        scales = [None] * n if scales is None else list(scales)
+        if len(datas) != n or len(scales) != n:
+            raise ValueError("datas and scales must have one entry per weight")
+        self.xs, self.n = xs, n
+        if n == 0:
+            self.datas, self.scales = [], []
+            return
+        dev, dtype = xs[0].device, xs[0].dtype
+        for t in xs + datas + scales:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+                raise ValueError("mxq_mxfp4_to_mxfp8_row_grouped: operands must be device tensors on one device")
+        if any(x.dtype != dtype for x in xs):
+            raise ValueError("all weights of a group call must have one dtype")
+        self._dt = _dtype_code(xs[0])
+        self._table = (_RowGroup * n)()
+        for i, x in enumerate(xs):
+            px, rows, K, ldx = _matrix(x)
+            nb = (K + 31) // 32
+            if scales[i] is None:
+                scales[i] = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=dev)
+            if datas[i] is None:
+                datas[i] = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+            pd, _, _, ldd = _matrix(datas[i])
+            ps, _, _, ld_s = _matrix(scales[i])
+            if rows * K and (ldd != K or datas[i].numel() != rows * K):
+                raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+            self._table[i] = _RowGroup(px, ldx, rows, K, pd, ps, ld_s)
+        self.datas, self.scales = datas, scales
+
+    def __call__(self):
+        if self.n:
+            _check(self._L, self._L.mxq_mxfp4_to_mxfp8_row_grouped(self._table, self.n, self._dt,
+                                                                    _stream(self.xs[0])))
+        return self.datas, self.scales
+
+
 @_device_operands
 def mxq_mxfp4_to_mxfp8_row_grouped(xs, datas=None, scales=None, scale_ld: Optional[int] = None,
                                    lib: str = "libmxq.so"):
     """Direct MXFP8 rowwise lift of a list of weights of one dtype, in as few
     launches as possible -> (list of payloads, list of E8M0 codes); the same
     bytes as one mxq_mxfp4_to_mxfp8_row per weight.  `datas` / `scales`: lists
-    of outputs (None entries, or None for the whole list, are allocated)."""
-    L = load(lib)
-    xs = list(xs)
-    n = len(xs)
-    datas = [None] * n if datas is None else list(datas)
-    scales = [None] * n if scales is None else list(scales)
-    if len(datas) != n or len(scales) != n:
-        raise ValueError("datas and scales must have one entry per weight")
-    if n == 0:
-        return [], []
-    dev, dtype = xs[0].device, xs[0].dtype
-    for t in xs + datas + scales:
-        if t is None:
-            continue
-        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
-            raise ValueError("mxq_mxfp4_to_mxfp8_row_grouped: operands must be device tensors on one device")
-    if any(x.dtype != dtype for x in xs):
-        raise ValueError("all weights of a group call must have one dtype")
-    dt = _dtype_code(xs[0])
-    table = (_RowGroup * n)()
-    for i, x in enumerate(xs):
-        px, rows, K, ldx = _matrix(x)
-        nb = (K + 31) // 32
-        if scales[i] is None:
-            scales[i] = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=dev)
-        if datas[i] is None:
-            datas[i] = torch.empty((rows, K), dtype=torch.uint8, device=dev)
-        pd, _, _, ldd = _matrix(datas[i])
-        ps, _, _, ld_s = _matrix(scales[i])
-        if rows * K and (ldd != K or datas[i].numel() != rows * K):
-            raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
-        table[i] = _RowGroup(px, ldx, rows, K, pd, ps, ld_s)
-    _check(L, L.mxq_mxfp4_to_mxfp8_row_grouped(table, n, dt, _stream(xs[0])))
-    return datas, scales
+    of outputs (None entries, or None for the whole list, are allocated).
+    GroupedRowLift prepares the call once for repeated use."""
+    return GroupedRowLift(xs, datas, scales, scale_ld, lib)()
 
 
 @_device_operands

@@ -519,12 +519,13 @@ __device__ __forceinline__ uint32_t e4m3x4_each(uint32_t y01, uint32_t y23, floa
   return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, c), 0x07020100u);
 }
 
-// Grouped row lift: the row lift of up to kGroupMax weights in one launch.  Each
-// weight's steps are padded to whole workgroups, so a workgroup lies in one
-// weight; it finds that weight by a binary search of the table's first
-// workgroups (the table is a kernel argument, so the search is scalar), then
-// runs the row lift's steps on it.  Aligned (VEC) weights only; the host launches the
-// others one by one.
+// Grouped row lift: the row lift of up to kGroupMax weights in one launch, on a
+// 2-D grid: blockIdx.y is the weight and blockIdx.x the workgroup within it, so
+// a workgroup reads its weight's descriptor from the kernel arguments (scalar
+// loads at a uniform offset) and needs no search.  The grid's x extent is the
+// largest weight's workgroup count; the workgroups past a smaller weight's own
+// count exit at once (the host keeps that padding small).  Aligned (VEC)
+// weights only; the host launches the others one by one.
 constexpr int kGroupMax = 48;
 struct RowGroupDesc {
   const void* x;
@@ -536,8 +537,6 @@ struct RowGroupDesc {
   uint32_t total_steps;
 };
 struct RowGroupTable {
-  uint32_t n;
-  uint32_t wg0[kGroupMax + 1];   // first workgroup of each weight; wg0[n] = the grid size
   RowGroupDesc g[kGroupMax];
 };
 static_assert(sizeof(RowGroupTable) <= 3584, "the table must fit the kernel-argument segment");
@@ -545,19 +544,12 @@ static_assert(sizeof(RowGroupTable) <= 3584, "the table must fit the kernel-argu
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void row_grouped_kernel(const RowGroupTable tab) {
   using G = StepGeom<T, kRowThreads>;
+  const RowGroupDesc d = tab.g[blockIdx.y];
+  const uint32_t lwg = blockIdx.x;
+  if (lwg * kRowSteps >= d.total_steps) return;              // uniform: past this weight's steps
   keep_denormals();
-  const uint32_t tid = threadIdx.x, b = blockIdx.x;
-  // the last weight whose first workgroup is <= b: wg0 increases strictly
-  // (no weight has zero workgroups), wg0[0] = 0 <= b < wg0[n]
-  uint32_t gi = 0, hi = tab.n;
-  while (hi - gi > 1u) {
-    const uint32_t mid = (gi + hi) >> 1;
-    if (tab.wg0[mid] <= b) gi = mid;
-    else hi = mid;
-  }
-  const RowGroupDesc& d = tab.g[gi];
+  const uint32_t tid = threadIdx.x;
   const T* x = static_cast<const T*>(d.x);
-  const uint32_t lwg = b - tab.wg0[gi];
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   u32x4 w[kRowSteps];
 #pragma unroll
@@ -1622,19 +1614,21 @@ int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t
 }
 
 // Grouped row lift: aligned weights go into tables of up to kGroupMax, one
-// launch per table; the others take the single-weight launch.  The caller has
-// checked every group (shapes, spans, step counts, aliasing) beforehand.
+// launch per table; the others take the single-weight launch.  A table is cut
+// early when a weight's size would pad its grid (weights x the largest
+// workgroup count) by more than a quarter of the real workgroups plus 4096
+// (workgroups that exit at once).  The caller has checked every group
+// (shapes, spans, step counts, aliasing) beforehand.
 template <typename T>
 int launch_row_grouped(const mxq_row_group* gs, int64_t n, hipStream_t s) {
   constexpr int EPL = Fmt<T>::kEPL;
   RowGroupTable tab{};
-  int64_t wgs = 0;
+  int64_t count = 0, max_w = 0, sum_w = 0;
   auto flush = [&]() -> int {
-    if (tab.n == 0) return MXQ_OK;
-    tab.wg0[tab.n] = (uint32_t)wgs;
-    hipLaunchKernelGGL((row_grouped_kernel<T>), dim3((uint32_t)wgs), dim3(kRowThreads), 0, s, tab);
-    tab.n = 0;
-    wgs = 0;
+    if (count == 0) return MXQ_OK;
+    hipLaunchKernelGGL((row_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(kRowThreads), 0, s,
+                       tab);
+    count = max_w = sum_w = 0;
     return launch_status();
   };
   for (int64_t i = 0; i < n; i++) {
@@ -1649,14 +1643,15 @@ int launch_row_grouped(const mxq_row_group* gs, int64_t n, hipStream_t s) {
     uint32_t total;
     if (steps_for(g.rows, g.K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
     const int64_t gw = grid_for(total, kRowSteps);
-    if (tab.n == (uint32_t)kGroupMax || wgs + gw >= kMaxSteps) {
+    const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
+    if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
       const int st = flush();
       if (st != MXQ_OK) return st;
     }
-    tab.wg0[tab.n] = (uint32_t)wgs;
-    tab.g[tab.n] = RowGroupDesc{g.x, g.ld_x, g.K, g.data, g.scale, g.scale_ld, spr, total};
-    tab.n++;
-    wgs += gw;
+    tab.g[count] = RowGroupDesc{g.x, g.ld_x, g.K, g.data, g.scale, g.scale_ld, spr, total};
+    count++;
+    max_w = std::max(max_w, gw);
+    sum_w += gw;
   }
   return flush();
 }

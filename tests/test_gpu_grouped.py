@@ -87,3 +87,20 @@ def test_grouped_overlapping_outputs_are_refused(dev):
     # the same input twice is fine (inputs may overlap)
     d, s = mxq.mxq_mxfp4_to_mxfp8_row_grouped([a, a])
     assert torch.equal(d[0], d[1]) and torch.equal(s[0], s[1])
+
+
+def test_prepared_grouped_call_follows_its_weights(dev):
+    """GroupedRowLift builds the table once; every call converts the weights'
+    current contents."""
+    a_bits = [_weight(64, 512, "bf16", 90 + i) for i in range(5)]
+    b_bits = [_weight(64, 512, "bf16", 95 + i) for i in range(5)]
+    xs = [to_dev(b, dev) for b in a_bits]
+    call = mxq.GroupedRowLift(xs, scale_ld=20)
+    for bits in (a_bits, b_bits, a_bits):
+        for x, b in zip(xs, bits):
+            x.copy_(to_dev(b, dev))
+        datas, scales = call()
+        for i, b in enumerate(bits):
+            wd, ws = oracle.mxfp4_to_mxfp8_row(b, scale_ld=20, threads=THREADS)
+            assert_bits(to_host(datas[i]), wd, f"weight {i} payload")
+            assert_bits(to_host(scales[i])[:, :16], ws[:, :16], f"weight {i} codes")
