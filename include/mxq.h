@@ -11,7 +11,8 @@
  *   mxq_fake_quantize_mxfp4_with_mxfp8_row    projection + row lift in one pass
  *   mxq_mxfp4_to_mxfp8_row_guarded,
  *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
- *   mxq_mxfp4_to_mxfp8_row_grouped            the row lift of a list of weights in few launches
+ *   mxq_mxfp4_to_mxfp8_row_grouped,
+ *   mxq_fake_quantize_mxfp4_grouped           the row lift / projection of a list of weights in few launches
  * the packed MXFP4 deployment format:
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
  *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
@@ -202,6 +203,34 @@ typedef struct {
  */
 int mxq_mxfp4_to_mxfp8_row_grouped(const mxq_row_group* groups, int64_t n_groups, mxq_dtype dt,
                                    hipStream_t stream);
+
+/*
+ * One weight of a grouped projection: the arguments of mxq_fake_quantize_mxfp4
+ * for that weight (x and y are device pointers).
+ */
+typedef struct {
+  const void* x;      /* [rows, K], row stride ld_x >= K */
+  int64_t ld_x;
+  void* y;            /* [rows, K] same dtype, row stride ld_y >= K; y == x with ld_y == ld_x is in place */
+  int64_t ld_y;
+  int64_t rows;
+  int64_t K;
+} mxq_proj_group;
+
+/*
+ * The MXFP4 projection of mxq_fake_quantize_mxfp4 ([QAT] Description, conversion
+ * mode 1, the default mode) applied to a list of weights of one dtype, in as
+ * few launches as possible.  Results are bit-identical to one
+ * mxq_fake_quantize_mxfp4 call per weight.
+ *   groups    HOST array of n_groups descriptors, read during the call only
+ *   n_groups  >= 0; groups with rows == 0 or K == 0 are skipped
+ *   Every group is checked as mxq_fake_quantize_mxfp4 checks its arguments
+ *   (the first failing group's status is returned and nothing is enqueued).
+ *   In addition no group's y may overlap any other group's x or y
+ *   (MXQ_ERR_ALIAS); inputs may overlap each other, and a group may be in place.
+ */
+int mxq_fake_quantize_mxfp4_grouped(const mxq_proj_group* groups, int64_t n_groups, mxq_dtype dt,
+                                    hipStream_t stream);
 
 /*
  * MXFP8 columnwise from the MXFP4 decomposition ([QAT] Description, conversion

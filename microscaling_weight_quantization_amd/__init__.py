@@ -37,7 +37,7 @@ ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mx
                 "mxq_mxfp4_to_fp8_block128_guarded", "mxq_quantize_mxfp4", "mxq_dequantize_mxfp4",
                 "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
                 "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded",
-                "mxq_mxfp4_to_mxfp8_row_grouped")
+                "mxq_mxfp4_to_mxfp8_row_grouped", "mxq_fake_quantize_mxfp4_grouped")
 
 _libs = {}
 _lock = threading.Lock()
@@ -47,6 +47,12 @@ class _RowGroup(ctypes.Structure):
     """mxq_row_group of include/mxq.h."""
     _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_ld", ctypes.c_int64)]
+
+
+class _ProjGroup(ctypes.Structure):
+    """mxq_proj_group of include/mxq.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("y", ctypes.c_void_p), ("ld_y", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class MxqError(RuntimeError):
@@ -85,6 +91,7 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_mxfp4_to_mxfp8_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, vp, vp]
         L.mxq_mxfp4_to_mxfp8_row_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp, vp]
         L.mxq_mxfp4_to_mxfp8_row_grouped.argtypes = [ctypes.POINTER(_RowGroup), i64, i32, vp]
+        L.mxq_fake_quantize_mxfp4_grouped.argtypes = [ctypes.POINTER(_ProjGroup), i64, i32, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -242,6 +249,59 @@ class GroupedRowLift:
             _check(self._L, self._L.mxq_mxfp4_to_mxfp8_row_grouped(self._table, self.n, self._dt,
                                                                     _stream(self.xs[0])))
         return self.datas, self.scales
+
+
+class GroupedProjection:
+    """The grouped MXFP4 projection prepared once for a fixed list of weights
+    and outputs (an output may be its weight itself, in place); each call
+    enqueues it on torch's current stream with one call into the library.  The
+    object keeps the tensors alive; `ys` are the outputs."""
+
+    def __init__(self, xs, ys=None, lib: str = "libmxq.so"):
+        self._L = load(lib)
+        xs = list(xs)
+        n = len(xs)
+        ys = [None] * n if ys is None else list(ys)
+        if len(ys) != n:
+            raise ValueError("ys must have one entry per weight")
+        self.xs, self.n = xs, n
+        if n == 0:
+            self.ys = []
+            return
+        dev, dtype = xs[0].device, xs[0].dtype
+        for t in xs + ys:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+                raise ValueError("mxq_fake_quantize_mxfp4_grouped: operands must be device tensors on one device")
+        if any(x.dtype != dtype for x in xs):
+            raise ValueError("all weights of a group call must have one dtype")
+        self._dt = _dtype_code(xs[0])
+        self._table = (_ProjGroup * n)()
+        for i, x in enumerate(xs):
+            if ys[i] is None:
+                ys[i] = torch.empty_like(x, memory_format=torch.contiguous_format)
+            if ys[i].dtype != x.dtype or ys[i].shape != x.shape:
+                raise ValueError("each output must have its weight's dtype and shape")
+            px, rows, K, ldx = _matrix(x)
+            py, _, _, ldy = _matrix(ys[i])
+            self._table[i] = _ProjGroup(px, ldx, py, ldy, rows, K)
+        self.ys = ys
+
+    def __call__(self):
+        if self.n:
+            _check(self._L, self._L.mxq_fake_quantize_mxfp4_grouped(self._table, self.n, self._dt, _stream(self.xs[0])))
+        return self.ys
+
+
+@_device_operands
+def mxq_fake_quantize_mxfp4_grouped(xs, ys=None, lib: str = "libmxq.so"):
+    """MXFP4 projection of a list of weights of one dtype, in as few launches as
+    possible -> list of outputs; the same bits as one mxq_fake_quantize_mxfp4 per
+    weight.  `ys`: list of outputs (None entries, or None for the whole list,
+    are allocated; an entry may be its weight, in place).  GroupedProjection
+    prepares the call once for repeated use."""
+    return GroupedProjection(xs, ys, lib)()
 
 
 @_device_operands

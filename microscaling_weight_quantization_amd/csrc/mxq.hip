@@ -577,6 +577,57 @@ __global__ __launch_bounds__(kRowThreads) void row_grouped_kernel(const RowGroup
   }
 }
 
+// Grouped projection, on the same pattern as the grouped row lift: blockIdx.y
+// is the weight, blockIdx.x the workgroup within it, with the projection's own
+// launch shape and stores.  A weight may be in place (y == x).
+struct ProjGroupDesc {
+  const void* x;
+  int64_t ld_x, K;
+  void* y;
+  int64_t ld_y;
+  MxqDivisor steps_per_row;
+  uint32_t total_steps;
+};
+struct ProjGroupTable {
+  ProjGroupDesc g[kGroupMax];
+};
+static_assert(sizeof(ProjGroupTable) <= 3584, "the table must fit the kernel-argument segment");
+
+template <typename T>
+__global__ __launch_bounds__(kProjThreads) void proj_grouped_kernel(const ProjGroupTable tab) {
+  using G = StepGeom<T, kProjThreads>;
+  const ProjGroupDesc d = tab.g[blockIdx.y];
+  const uint32_t lwg = blockIdx.x;
+  if (lwg * kProjSteps >= d.total_steps) return;             // uniform: past this weight's steps
+  keep_denormals();
+  const uint32_t tid = threadIdx.x;
+  const T* x = static_cast<const T*>(d.x);
+  T* y = static_cast<T*>(d.y);
+  const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
+  u32x4 w[kProjSteps];
+#pragma unroll
+  for (int u = 0; u < kProjSteps; u++) {
+    const uint32_t step = lwg * kProjSteps + u;
+    w[u] = u32x4{0u, 0u, 0u, 0u};
+    if (step < d.total_steps) {
+      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
+      w[u] = load_chunk<T, true>(x + (int64_t)row * d.ld_x, seg * G::kElemsPerStep + lane_col, d.K);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kProjSteps; u++) {
+    const uint32_t step = lwg * kProjSteps + u;
+    if (step < d.total_steps) {
+      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
+      const Block b = chunk_block<T>(w[u]);
+      const float s = e8m0(b.eb);
+      const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
+      store_chunk<T, true, true>(y + (int64_t)row * d.ld_y, seg * G::kElemsPerStep + lane_col, d.K,
+                                 proj_chunk<T>(p, b.poison));
+    }
+  }
+}
+
 template <typename T, bool VEC, bool kRow>
 __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
     const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* __restrict__ cdata,
@@ -1656,6 +1707,63 @@ int launch_row_grouped(const mxq_row_group* gs, int64_t n, hipStream_t s) {
   return flush();
 }
 
+// Grouped projection: the grouped row lift's batching, for the projection.
+template <typename T>
+int launch_proj_grouped(const mxq_proj_group* gs, int64_t n, hipStream_t s) {
+  constexpr int EPL = Fmt<T>::kEPL;
+  ProjGroupTable tab{};
+  int64_t count = 0, max_w = 0, sum_w = 0;
+  auto flush = [&]() -> int {
+    if (count == 0) return MXQ_OK;
+    hipLaunchKernelGGL((proj_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(kProjThreads), 0, s,
+                       tab);
+    count = max_w = sum_w = 0;
+    return launch_status();
+  };
+  for (int64_t i = 0; i < n; i++) {
+    const mxq_proj_group& g = gs[i];
+    if (g.rows == 0 || g.K == 0) continue;
+    if (!(aligned(g.x, 16) && aligned(g.y, 16) && g.ld_x % EPL == 0 && g.ld_y % EPL == 0 && g.K % EPL == 0 &&
+          fits32(g.K * (int64_t)sizeof(T)))) {
+      const int st = launch_proj<T>(g.x, g.ld_x, g.y, g.ld_y, g.rows, g.K, s);
+      if (st != MXQ_OK) return st;
+      continue;
+    }
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, StepGeom<T, kProjThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t gw = grid_for(total, kProjSteps);
+    const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
+    if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
+      const int st = flush();
+      if (st != MXQ_OK) return st;
+    }
+    tab.g[count] = ProjGroupDesc{g.x, g.ld_x, g.K, g.y, g.ld_y, spr, total};
+    count++;
+    max_w = std::max(max_w, gw);
+    sum_w += gw;
+  }
+  return flush();
+}
+
+// The ranges of a grouped call, each marked as an output or not: true when no
+// output overlaps any other range.  A sweep in order of start address: a range
+// overlaps an earlier one exactly when it starts before the largest end seen
+// so far (of outputs, for an input; of anything, for an output).
+bool grouped_ranges_disjoint(std::vector<std::pair<Range, bool>>& iv) {
+  std::sort(iv.begin(), iv.end(), [](const std::pair<Range, bool>& a, const std::pair<Range, bool>& b) {
+    return a.first.lo < b.first.lo;
+  });
+  uintptr_t end_out = 0, end_in = 0;
+  for (const auto& e : iv) {
+    const Range& r = e.first;
+    if (e.second ? r.lo < std::max(end_out, end_in) : r.lo < end_out) return false;
+    uintptr_t& end = e.second ? end_out : end_in;
+    end = std::max(end, r.hi);
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1673,20 +1781,65 @@ const char* mxq_status_string(int status) {
   }
 }
 
-int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows, int64_t K,
-                            mxq_dtype dt, hipStream_t stream) {
+// Argument checks of the projection.  For a non-empty matrix it returns MXQ_OK
+// with *rx / *ry and whether the call is in place; for an empty one MXQ_OK with
+// *empty set.
+static int proj_check(const void* x, int64_t ld_x, const void* y, int64_t ld_y, int64_t rows, int64_t K,
+                      mxq_dtype dt, Range* rx, Range* ry, bool* in_place, bool* empty) {
+  *empty = false;
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (rows == 0 || K == 0) return MXQ_OK;
+  if (rows == 0 || K == 0) {
+    *empty = true;
+    return MXQ_OK;
+  }
   if (!x || !y) return MXQ_ERR_NULL;
   if (ld_x < K || ld_y < K) return MXQ_ERR_SHAPE;
   const size_t es = dtype_size(dt);
-  const bool in_place = (x == y) && (ld_x == ld_y);
-  const Range rx = matrix_range(x, rows, K, ld_x, es), ry = matrix_range(y, rows, K, ld_y, es);
-  if (!spans_ok({rx, ry})) return MXQ_ERR_SHAPE;
-  if (!in_place && overlap(rx, ry)) return MXQ_ERR_ALIAS;
+  *in_place = (x == y) && (ld_x == ld_y);
+  *rx = matrix_range(x, rows, K, ld_x, es);
+  *ry = matrix_range(y, rows, K, ld_y, es);
+  if (!spans_ok({*rx, *ry})) return MXQ_ERR_SHAPE;
+  if (!*in_place && overlap(*rx, *ry)) return MXQ_ERR_ALIAS;
+  return MXQ_OK;
+}
+
+int mxq_fake_quantize_mxfp4(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows, int64_t K,
+                            mxq_dtype dt, hipStream_t stream) {
+  Range rx, ry;
+  bool in_place, empty;
+  const int st = proj_check(x, ld_x, y, ld_y, rows, K, dt, &rx, &ry, &in_place, &empty);
+  if (st != MXQ_OK || empty) return st;
   return dt == MXQ_BF16 ? launch_proj<uint16_t>(x, ld_x, y, ld_y, rows, K, stream)
                         : launch_proj<uint32_t>(x, ld_x, y, ld_y, rows, K, stream);
+}
+
+int mxq_fake_quantize_mxfp4_grouped(const mxq_proj_group* groups, int64_t n_groups, mxq_dtype dt,
+                                    hipStream_t stream) {
+  if (check_dtype(dt)) return MXQ_ERR_DTYPE;
+  if (n_groups < 0) return MXQ_ERR_SHAPE;
+  if (n_groups == 0) return MXQ_OK;
+  if (!groups) return MXQ_ERR_NULL;
+  const int64_t eps = dt == MXQ_BF16 ? StepGeom<uint16_t, kProjThreads>::kElemsPerStep
+                                     : StepGeom<uint32_t, kProjThreads>::kElemsPerStep;
+  std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
+  iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 2);
+  for (int64_t i = 0; i < n_groups; i++) {
+    const mxq_proj_group& g = groups[i];
+    Range rx, ry;
+    bool in_place, empty;
+    const int st = proj_check(g.x, g.ld_x, g.y, g.ld_y, g.rows, g.K, dt, &rx, &ry, &in_place, &empty);
+    if (st != MXQ_OK) return st;
+    if (empty) continue;
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, eps, &spr, &total)) return MXQ_ERR_SHAPE;
+    if (!in_place) iv.push_back({rx, false});               // in place: the range is an output only
+    iv.push_back({ry, true});
+  }
+  if (!grouped_ranges_disjoint(iv)) return MXQ_ERR_ALIAS;
+  return dt == MXQ_BF16 ? launch_proj_grouped<uint16_t>(groups, n_groups, stream)
+                        : launch_proj_grouped<uint32_t>(groups, n_groups, stream);
 }
 
 // Argument checks of the row lift (and its fused and gated forms).  For a
@@ -1802,18 +1955,7 @@ int mxq_mxfp4_to_mxfp8_row_grouped(const mxq_row_group* groups, int64_t n_groups
     iv.push_back({r[1], true});
     iv.push_back({r[2], true});
   }
-  // sweep in order of start address: a range overlaps an earlier one exactly
-  // when it starts before the largest end seen so far
-  std::sort(iv.begin(), iv.end(), [](const std::pair<Range, bool>& a, const std::pair<Range, bool>& b) {
-    return a.first.lo < b.first.lo;
-  });
-  uintptr_t end_out = 0, end_in = 0;
-  for (const auto& e : iv) {
-    const Range& r = e.first;
-    if (e.second ? r.lo < std::max(end_out, end_in) : r.lo < end_out) return MXQ_ERR_ALIAS;
-    uintptr_t& end = e.second ? end_out : end_in;
-    end = std::max(end, r.hi);
-  }
+  if (!grouped_ranges_disjoint(iv)) return MXQ_ERR_ALIAS;
   return dt == MXQ_BF16 ? launch_row_grouped<uint16_t>(groups, n_groups, stream)
                         : launch_row_grouped<uint32_t>(groups, n_groups, stream);
 }

@@ -226,3 +226,31 @@ def test_grouped_row_lift_host_validation(lib):
     assert call(grp(0x110000, 0x210000, 0x310000), grp(0x2100F0, 0x220000, 0x320000)) == mxq.MXQ_ERR_ALIAS  # an input over an output
     # empty groups only: nothing to do
     assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK
+
+
+def test_grouped_projection_host_validation(lib):
+    """The grouped projection checks every weight as the single call does (in
+    place allowed), and refuses an output over another weight's input or output,
+    before anything is enqueued (fake addresses; no GPU is touched)."""
+    G = mxq._ProjGroup
+
+    def grp(x, y, rows=4, K=64, ldx=64, ldy=64):
+        return G(x, ldx, y, ldy, rows, K)
+
+    def call(*groups, dt=mxq.MXQ_BF16, n=None):
+        arr = (G * max(len(groups), 1))(*groups)
+        return lib.mxq_fake_quantize_mxfp4_grouped(arr, len(groups) if n is None else n, dt, None)
+
+    a = grp(0x100000, 0x200000)                    # 4 x 64 bf16: 512 bytes each
+    b = grp(0x110000, 0x210000)
+    assert call(a, b, n=-1) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_fake_quantize_mxfp4_grouped(None, 1, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_NULL
+    assert call(a, b, dt=mxq.MXQ_FP16) == mxq.MXQ_ERR_DTYPE
+    assert call(a, grp(0x110000, None)) == mxq.MXQ_ERR_NULL
+    assert call(a, grp(0x110000, 0x210000, ldx=32)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, grp(0x110000, 0x110002)) == mxq.MXQ_ERR_ALIAS                 # partial overlap in one weight
+    assert call(a, grp(0x110000, 0x110000, ldx=64, ldy=128)) == mxq.MXQ_ERR_ALIAS  # in place needs equal strides
+    assert call(a, grp(0x110000, 0x100100)) == mxq.MXQ_ERR_ALIAS                 # b's output over a's weight
+    assert call(a, grp(0x110000, 0x200100)) == mxq.MXQ_ERR_ALIAS                 # two outputs overlap
+    assert call(grp(0x100000, 0x100000), grp(0x100100, 0x210000)) == mxq.MXQ_ERR_ALIAS  # a weight inside an in-place one
+    assert call(grp(None, None, rows=0), grp(None, None, K=0)) == mxq.MXQ_OK

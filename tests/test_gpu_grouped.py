@@ -104,3 +104,40 @@ def test_prepared_grouped_call_follows_its_weights(dev):
             wd, ws = oracle.mxfp4_to_mxfp8_row(b, scale_ld=20, threads=THREADS)
             assert_bits(to_host(datas[i]), wd, f"weight {i} payload")
             assert_bits(to_host(scales[i])[:, :16], ws[:, :16], f"weight {i} codes")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_grouped_projection_mixed_shapes(dev, dtype):
+    """Mixed ragged shapes, one weight converted in place, one misaligned (the
+    per-weight path), one empty, and more weights than one table holds."""
+    shapes = [(100, 48), (257, 1000), (64, 4096), (1, 33), (300, 2048), (0, 64), (128, 130), (33, 7), (513, 256)]
+    shapes += [(int(r), int(k)) for r, k in zip(np.random.default_rng(9).integers(1, 90, 50),
+                                                np.random.default_rng(10).choice([32, 64, 200, 512, 1024], 50))]
+    weights = [_weight(r, k, dtype, 200 + i) for i, (r, k) in enumerate(shapes)]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xs = [to_dev(b, dev) if b.size else torch.empty(b.shape, dtype=tdt, device=dev) for b in weights]
+    base = to_dev(np.concatenate([np.zeros((weights[4].shape[0], 1), weights[4].dtype), weights[4]], axis=1), dev)
+    xs[4] = base[:, 1:]                                         # misaligned view
+    ys = [None] * len(xs)
+    ys[2] = xs[2]                                               # in place
+    ys = mxq.mxq_fake_quantize_mxfp4_grouped(xs, ys)
+    assert ys[2].data_ptr() == xs[2].data_ptr()
+    for i, (bits, y) in enumerate(zip(weights, ys)):
+        if bits.size:
+            assert_bits(to_host(y), oracle.fake_quantize_mxfp4(bits, threads=THREADS), f"weight {i} {bits.shape}")
+
+
+def test_prepared_grouped_projection_and_overlaps(dev):
+    a_bits = [_weight(64, 512, "bf16", 300 + i) for i in range(4)]
+    b_bits = [_weight(64, 512, "bf16", 310 + i) for i in range(4)]
+    xs = [to_dev(b, dev) for b in a_bits]
+    call = mxq.GroupedProjection(xs)
+    for bits in (a_bits, b_bits):
+        for x, b in zip(xs, bits):
+            x.copy_(to_dev(b, dev))
+        for i, (b, y) in enumerate(zip(bits, call())):
+            assert_bits(to_host(y), oracle.fake_quantize_mxfp4(b, threads=THREADS), f"weight {i}")
+    y = torch.empty_like(xs[0])
+    with pytest.raises(mxq.MxqError) as e:
+        mxq.mxq_fake_quantize_mxfp4_grouped(xs[:2], [y, y])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
