@@ -11,8 +11,9 @@
  *   mxq_fake_quantize_mxfp4_with_mxfp8_row    projection + row lift in one pass
  *   mxq_mxfp4_to_mxfp8_row_guarded,
  *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
- *   mxq_mxfp4_to_mxfp8_row_grouped,
- *   mxq_fake_quantize_mxfp4_grouped           the row lift / projection of a list of weights in few launches
+ *   mxq_mxfp4_to_mxfp8_row_grouped, mxq_fake_quantize_mxfp4_grouped,
+ *   mxq_mxfp4_to_fp8_block128_grouped         the row lift / projection / fold of a list of weights
+ *                                             in few launches
  * the packed MXFP4 deployment format:
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
  *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
@@ -231,6 +232,36 @@ typedef struct {
  */
 int mxq_fake_quantize_mxfp4_grouped(const mxq_proj_group* groups, int64_t n_groups, mxq_dtype dt,
                                     hipStream_t stream);
+
+/*
+ * One weight of a grouped 128x128 fold: the arguments of
+ * mxq_mxfp4_to_fp8_block128 for that weight (x, data and tile_code are device
+ * pointers).
+ */
+typedef struct {
+  const void* x;      /* [rows, K], row stride ld_x >= K */
+  int64_t ld_x;
+  int64_t rows;
+  int64_t K;
+  uint8_t* data;      /* [rows, K] E4M3 payload, contiguous */
+  uint8_t* tile_code; /* [ceil(rows/128), tile_ld] E8M0 tile codes, tile_ld >= ceil(K/128) */
+  int64_t tile_ld;
+} mxq_block128_group;
+
+/*
+ * The direct 128x128 blockwise FP8 fold of mxq_mxfp4_to_fp8_block128 ([QAT]
+ * Description, conversion mode 2) applied to a list of weights of one dtype,
+ * in as few launches as possible.  Results are bit-identical to one
+ * mxq_mxfp4_to_fp8_block128 call per weight.
+ *   groups    HOST array of n_groups descriptors, read during the call only
+ *   n_groups  >= 0; groups with rows == 0 or K == 0 are skipped
+ *   Every group is checked as mxq_mxfp4_to_fp8_block128 checks its arguments
+ *   (the first failing group's status is returned and nothing is enqueued).
+ *   In addition no group's data or tile_code may overlap any group's x, data
+ *   or tile_code (MXQ_ERR_ALIAS); inputs may overlap each other.
+ */
+int mxq_mxfp4_to_fp8_block128_grouped(const mxq_block128_group* groups, int64_t n_groups, mxq_dtype dt,
+                                      hipStream_t stream);
 
 /*
  * MXFP8 columnwise from the MXFP4 decomposition ([QAT] Description, conversion

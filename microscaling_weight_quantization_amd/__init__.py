@@ -37,7 +37,8 @@ ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mx
                 "mxq_mxfp4_to_fp8_block128_guarded", "mxq_quantize_mxfp4", "mxq_dequantize_mxfp4",
                 "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
                 "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded",
-                "mxq_mxfp4_to_mxfp8_row_grouped", "mxq_fake_quantize_mxfp4_grouped")
+                "mxq_mxfp4_to_mxfp8_row_grouped", "mxq_fake_quantize_mxfp4_grouped",
+                "mxq_mxfp4_to_fp8_block128_grouped")
 
 _libs = {}
 _lock = threading.Lock()
@@ -53,6 +54,12 @@ class _ProjGroup(ctypes.Structure):
     """mxq_proj_group of include/mxq.h."""
     _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("y", ctypes.c_void_p), ("ld_y", ctypes.c_int64),
                 ("rows", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _Block128Group(ctypes.Structure):
+    """mxq_block128_group of include/mxq.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("data", ctypes.c_void_p), ("tile_code", ctypes.c_void_p), ("tile_ld", ctypes.c_int64)]
 
 
 class MxqError(RuntimeError):
@@ -92,6 +99,7 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_mxfp4_to_mxfp8_row_col_guarded.argtypes = [vp, i64, i64, i64, i32, u8p, u8p, i64, u8p, u8p, i64, vp, vp]
         L.mxq_mxfp4_to_mxfp8_row_grouped.argtypes = [ctypes.POINTER(_RowGroup), i64, i32, vp]
         L.mxq_fake_quantize_mxfp4_grouped.argtypes = [ctypes.POINTER(_ProjGroup), i64, i32, vp]
+        L.mxq_mxfp4_to_fp8_block128_grouped.argtypes = [ctypes.POINTER(_Block128Group), i64, i32, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -292,6 +300,63 @@ class GroupedProjection:
         if self.n:
             _check(self._L, self._L.mxq_fake_quantize_mxfp4_grouped(self._table, self.n, self._dt, _stream(self.xs[0])))
         return self.ys
+
+
+class GroupedBlock128:
+    """The grouped 128x128 fold prepared once for a fixed list of weights and
+    outputs; each call enqueues it on torch's current stream with one call into
+    the library.  The object keeps the tensors alive; `datas` / `tile_codes`
+    are the outputs."""
+
+    def __init__(self, xs, datas=None, tile_codes=None, lib: str = "libmxq.so"):
+        self._L = load(lib)
+        xs = list(xs)
+        n = len(xs)
+        datas = [None] * n if datas is None else list(datas)
+        tile_codes = [None] * n if tile_codes is None else list(tile_codes)
+        if len(datas) != n or len(tile_codes) != n:
+            raise ValueError("datas and tile_codes must have one entry per weight")
+        self.xs, self.n = xs, n
+        if n == 0:
+            self.datas, self.tile_codes = [], []
+            return
+        dev, dtype = xs[0].device, xs[0].dtype
+        for t in xs + datas + tile_codes:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+                raise ValueError("mxq_mxfp4_to_fp8_block128_grouped: operands must be device tensors on one device")
+        if any(x.dtype != dtype for x in xs):
+            raise ValueError("all weights of a group call must have one dtype")
+        self._dt = _dtype_code(xs[0])
+        self._table = (_Block128Group * n)()
+        for i, x in enumerate(xs):
+            px, rows, K, ldx = _matrix(x)
+            if datas[i] is None:
+                datas[i] = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+            if tile_codes[i] is None:
+                tile_codes[i] = torch.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev)
+            pd, _, _, ldd = _matrix(datas[i])
+            pt, _, _, ldt = _matrix(tile_codes[i])
+            if rows * K and (ldd != K or datas[i].numel() != rows * K):
+                raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+            self._table[i] = _Block128Group(px, ldx, rows, K, pd, pt, ldt)
+        self.datas, self.tile_codes = datas, tile_codes
+
+    def __call__(self):
+        if self.n:
+            _check(self._L, self._L.mxq_mxfp4_to_fp8_block128_grouped(self._table, self.n, self._dt,
+                                                                       _stream(self.xs[0])))
+        return self.datas, self.tile_codes
+
+
+@_device_operands
+def mxq_mxfp4_to_fp8_block128_grouped(xs, datas=None, tile_codes=None, lib: str = "libmxq.so"):
+    """Direct 128x128 blockwise FP8 of a list of weights of one dtype, in as few
+    launches as possible -> (list of payloads, list of tile codes); the same
+    bytes as one mxq_mxfp4_to_fp8_block128 per weight.  GroupedBlock128
+    prepares the call once for repeated use."""
+    return GroupedBlock128(xs, datas, tile_codes, lib)()
 
 
 @_device_operands

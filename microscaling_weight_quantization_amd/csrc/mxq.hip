@@ -775,19 +775,17 @@ struct FoldGeom {
   static_assert(kLPR <= 64, "a band row must fit in one wave");
 };
 
+// The fold of one group of J side-by-side tiles (tile row tr, group tg) by the
+// whole workgroup (a barrier inside); s_max: kFoldWaves * J words of LDS.  A
+// non-zero no-op flag leaves every output untouched.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
-                                                            int64_t K, uint8_t* __restrict__ data,
-                                                            uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                            uint32_t tiles_per_row, MxqDivisor groups_per_row,
-                                                            const int32_t* __restrict__ noop) {
+__device__ __forceinline__ void fold_tiles(const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K,
+                                           uint8_t* __restrict__ data, uint8_t* __restrict__ tile_code,
+                                           int64_t tile_ld, uint32_t tiles_per_row, uint32_t tr, uint32_t tg,
+                                           const int32_t* __restrict__ noop, uint32_t (*s_max)[FoldGeom<T>::kJ]) {
   using G = FoldGeom<T>;
   constexpr int EPL = G::kEPL, J = G::kJ, CPT = G::kCPT, LPR = G::kLPR, P = G::kPasses;
-  __shared__ uint32_t s_max[kFoldWaves][J];
-  keep_denormals();
-
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t tr = mxq_quot(blockIdx.x, groups_per_row), tg = blockIdx.x - tr * groups_per_row.d;
   const uint32_t j = (tid % LPR) / CPT;                    // this lane's tile within the group
   const int64_t r0 = (int64_t)tr * 128 + tid / LPR;
   const int64_t col0 = (int64_t)tg * (128 * J) + (tid % LPR) * EPL;
@@ -829,6 +827,45 @@ __global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restr
     const auto q = payload_chunk<T>(p, code, (poisoned >> i) & 1u);
     if (r < rows) store_payload<T, VEC>(data + r * K, col0, K, q);
   }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
+                                                            int64_t K, uint8_t* __restrict__ data,
+                                                            uint8_t* __restrict__ tile_code, int64_t tile_ld,
+                                                            uint32_t tiles_per_row, MxqDivisor groups_per_row,
+                                                            const int32_t* __restrict__ noop) {
+  __shared__ uint32_t s_max[kFoldWaves][FoldGeom<T>::kJ];
+  keep_denormals();
+  const uint32_t tr = mxq_quot(blockIdx.x, groups_per_row), tg = blockIdx.x - tr * groups_per_row.d;
+  fold_tiles<T, VEC>(x, ld_x, rows, K, data, tile_code, tile_ld, tiles_per_row, tr, tg, noop, s_max);
+}
+
+// Grouped fold: blockIdx.y is the weight and blockIdx.x the tile group within
+// it, with the single fold's workgroup and body (fold_tiles).
+struct FoldGroupDesc {
+  const void* x;
+  int64_t ld_x, rows, K;
+  uint8_t* data;
+  uint8_t* tile_code;
+  int64_t tile_ld;
+  MxqDivisor groups_per_row;
+  uint32_t tiles_per_row, n_groups;
+};
+struct FoldGroupTable {
+  FoldGroupDesc g[kGroupMax];
+};
+static_assert(sizeof(FoldGroupTable) <= 3840, "the table must fit the kernel-argument segment");
+
+template <typename T>
+__global__ __launch_bounds__(kFoldThreads) void block128_grouped_kernel(const FoldGroupTable tab) {
+  __shared__ uint32_t s_max[kFoldWaves][FoldGeom<T>::kJ];
+  const FoldGroupDesc d = tab.g[blockIdx.y];
+  if (blockIdx.x >= d.n_groups) return;                      // uniform: past this weight's tiles
+  keep_denormals();
+  const uint32_t tr = mxq_quot(blockIdx.x, d.groups_per_row), tg = blockIdx.x - tr * d.groups_per_row.d;
+  fold_tiles<T, true>(static_cast<const T*>(d.x), d.ld_x, d.rows, d.K, d.data, d.tile_code, d.tile_ld,
+                      d.tiles_per_row, tr, tg, nullptr, s_max);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1746,6 +1783,44 @@ int launch_proj_grouped(const mxq_proj_group* gs, int64_t n, hipStream_t s) {
   return flush();
 }
 
+// Grouped fold: the grouped row lift's batching, for the fold (one workgroup
+// per group of J tiles, as the single launch).
+template <typename T>
+int launch_block128_grouped(const mxq_block128_group* gs, int64_t n, hipStream_t s) {
+  constexpr int EPL = Fmt<T>::kEPL, J = FoldGeom<T>::kJ;
+  FoldGroupTable tab{};
+  int64_t count = 0, max_w = 0, sum_w = 0;
+  auto flush = [&]() -> int {
+    if (count == 0) return MXQ_OK;
+    hipLaunchKernelGGL((block128_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(kFoldThreads), 0,
+                       s, tab);
+    count = max_w = sum_w = 0;
+    return launch_status();
+  };
+  for (int64_t i = 0; i < n; i++) {
+    const mxq_block128_group& g = gs[i];
+    if (g.rows == 0 || g.K == 0) continue;
+    if (!(aligned(g.x, 16) && g.ld_x % EPL == 0 && g.K % EPL == 0 && aligned(g.data, EPL))) {
+      const int st = launch_block128<T>(g.x, g.ld_x, g.rows, g.K, g.data, g.tile_code, g.tile_ld, nullptr, s);
+      if (st != MXQ_OK) return st;
+      continue;
+    }
+    const int64_t tpr = (g.K + 127) / 128, gpr = (tpr + J - 1) / J, gw = gpr * ((g.rows + 127) / 128);
+    if (gw >= kMaxSteps) return MXQ_ERR_SHAPE;
+    const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
+    if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
+      const int st = flush();
+      if (st != MXQ_OK) return st;
+    }
+    tab.g[count] = FoldGroupDesc{g.x,         g.ld_x,     g.rows, g.K, g.data, g.tile_code, g.tile_ld,
+                                 mxq_divisor((uint32_t)gpr), (uint32_t)tpr, (uint32_t)gw};
+    count++;
+    max_w = std::max(max_w, gw);
+    sum_w += gw;
+  }
+  return flush();
+}
+
 // The ranges of a grouped call, each marked as an output or not: true when no
 // output overlaps any other range.  A sweep in order of start address: a range
 // overlaps an earlier one exactly when it starts before the largest end seen
@@ -1884,12 +1959,18 @@ static int row_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_d
                         : launch_row<uint32_t>(x, ld_x, rows, K, data, scale, scale_ld, y, ld_y, noop, stream);
 }
 
-static int block128_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
-                          uint8_t* tile_code, int64_t tile_ld, const int32_t* noop, bool need_noop,
-                          hipStream_t stream) {
+// Argument checks of the fold.  For a non-empty matrix it returns MXQ_OK with
+// *ranges = {x, data, tile_code}; for an empty one MXQ_OK with *empty set.
+static int block128_check(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                          uint8_t* tile_code, int64_t tile_ld, const int32_t* noop, bool need_noop, Range* ranges,
+                          bool* empty) {
+  *empty = false;
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (rows == 0 || K == 0) return MXQ_OK;
+  if (rows == 0 || K == 0) {
+    *empty = true;
+    return MXQ_OK;
+  }
   if (!x || !data || !tile_code || (need_noop && !noop)) return MXQ_ERR_NULL;
   const int64_t ntc = (K + 127) / 128, ntr = (rows + 127) / 128;
   if (ld_x < K || tile_ld < ntc) return MXQ_ERR_SHAPE;
@@ -1897,6 +1978,17 @@ static int block128_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, 
               rt = matrix_range(tile_code, ntr, ntc, tile_ld, 1);
   if (!spans_ok({rx, rd, rt})) return MXQ_ERR_SHAPE;
   if (overlap(rx, rd) || overlap(rx, rt) || overlap(rd, rt)) return MXQ_ERR_ALIAS;
+  ranges[0] = rx, ranges[1] = rd, ranges[2] = rt;
+  return MXQ_OK;
+}
+
+static int block128_entry(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* data,
+                          uint8_t* tile_code, int64_t tile_ld, const int32_t* noop, bool need_noop,
+                          hipStream_t stream) {
+  Range r[3];
+  bool empty;
+  const int st = block128_check(x, ld_x, rows, K, dt, data, tile_code, tile_ld, noop, need_noop, r, &empty);
+  if (st != MXQ_OK || empty) return st;
   return dt == MXQ_BF16 ? launch_block128<uint16_t>(x, ld_x, rows, K, data, tile_code, tile_ld, noop, stream)
                         : launch_block128<uint32_t>(x, ld_x, rows, K, data, tile_code, tile_ld, noop, stream);
 }
@@ -1927,6 +2019,34 @@ int mxq_mxfp4_to_fp8_block128_guarded(const void* x, int64_t ld_x, int64_t rows,
                                       uint8_t* data, uint8_t* tile_code, int64_t tile_ld, const int32_t* noop,
                                       hipStream_t stream) {
   return block128_entry(x, ld_x, rows, K, dt, data, tile_code, tile_ld, noop, true, stream);
+}
+
+int mxq_mxfp4_to_fp8_block128_grouped(const mxq_block128_group* groups, int64_t n_groups, mxq_dtype dt,
+                                      hipStream_t stream) {
+  if (check_dtype(dt)) return MXQ_ERR_DTYPE;
+  if (n_groups < 0) return MXQ_ERR_SHAPE;
+  if (n_groups == 0) return MXQ_OK;
+  if (!groups) return MXQ_ERR_NULL;
+  const int J = dt == MXQ_BF16 ? FoldGeom<uint16_t>::kJ : FoldGeom<uint32_t>::kJ;
+  std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
+  iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 3);
+  for (int64_t i = 0; i < n_groups; i++) {
+    const mxq_block128_group& g = groups[i];
+    Range r[3];
+    bool empty;
+    const int st = block128_check(g.x, g.ld_x, g.rows, g.K, dt, g.data, g.tile_code, g.tile_ld, nullptr, false, r,
+                                  &empty);
+    if (st != MXQ_OK) return st;
+    if (empty) continue;
+    const int64_t tpr = (g.K + 127) / 128, gpr = (tpr + J - 1) / J;
+    if (gpr * ((g.rows + 127) / 128) >= kMaxSteps) return MXQ_ERR_SHAPE;
+    iv.push_back({r[0], false});
+    iv.push_back({r[1], true});
+    iv.push_back({r[2], true});
+  }
+  if (!grouped_ranges_disjoint(iv)) return MXQ_ERR_ALIAS;
+  return dt == MXQ_BF16 ? launch_block128_grouped<uint16_t>(groups, n_groups, stream)
+                        : launch_block128_grouped<uint32_t>(groups, n_groups, stream);
 }
 
 int mxq_mxfp4_to_mxfp8_row_grouped(const mxq_row_group* groups, int64_t n_groups, mxq_dtype dt,

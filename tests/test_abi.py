@@ -254,3 +254,28 @@ def test_grouped_projection_host_validation(lib):
     assert call(a, grp(0x110000, 0x200100)) == mxq.MXQ_ERR_ALIAS                 # two outputs overlap
     assert call(grp(0x100000, 0x100000), grp(0x100100, 0x210000)) == mxq.MXQ_ERR_ALIAS  # a weight inside an in-place one
     assert call(grp(None, None, rows=0), grp(None, None, K=0)) == mxq.MXQ_OK
+
+
+def test_grouped_fold_host_validation(lib):
+    """The grouped fold checks every weight as the single call does and refuses
+    outputs over other weights' ranges, before anything is enqueued."""
+    G = mxq._Block128Group
+
+    def grp(x, data, tc, rows=4, K=256, ld=256, tld=2):
+        return G(x, ld, rows, K, data, tc, tld)
+
+    def call(*groups, dt=mxq.MXQ_BF16, n=None):
+        arr = (G * max(len(groups), 1))(*groups)
+        return lib.mxq_mxfp4_to_fp8_block128_grouped(arr, len(groups) if n is None else n, dt, None)
+
+    a = grp(0x100000, 0x200000, 0x300000)          # 4 x 256 bf16: 2 KiB; payload 1 KiB; 2 tile codes
+    b = grp(0x110000, 0x210000, 0x310000)
+    assert call(a, b, n=-1) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_mxfp4_to_fp8_block128_grouped(None, 1, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_NULL
+    assert call(a, b, dt=mxq.MXQ_FP16) == mxq.MXQ_ERR_DTYPE
+    assert call(a, grp(0x110000, 0x210000, None)) == mxq.MXQ_ERR_NULL
+    assert call(a, grp(0x110000, 0x210000, 0x310000, tld=1)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, grp(0x110000, 0x100400, 0x310000)) == mxq.MXQ_ERR_ALIAS      # b's payload in a's weight
+    assert call(a, grp(0x110000, 0x210000, 0x200010)) == mxq.MXQ_ERR_ALIAS      # b's codes in a's payload
+    assert call(a, grp(0x110000, 0x210000, 0x300001)) == mxq.MXQ_ERR_ALIAS      # code arrays overlap
+    assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK

@@ -141,3 +141,41 @@ def test_prepared_grouped_projection_and_overlaps(dev):
     with pytest.raises(mxq.MxqError) as e:
         mxq.mxq_fake_quantize_mxfp4_grouped(xs[:2], [y, y])
     assert e.value.status == mxq.MXQ_ERR_ALIAS
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_grouped_fold_mixed_shapes(dev, dtype):
+    """Mixed shapes with partial tiles, one misaligned weight (the per-weight
+    path), one empty, a spread-sweep weight, and more weights than one table
+    holds; each against the oracle."""
+    shapes = [(128, 128), (300, 520), (1, 33), (256, 4096), (0, 64), (129, 129), (64, 2048)]
+    shapes += [(int(r), int(k)) for r, k in zip(np.random.default_rng(11).integers(1, 300, 45),
+                                                np.random.default_rng(12).choice([32, 128, 200, 512, 640], 45))]
+    weights = [_weight(r, k, dtype, 400 + i) for i, (r, k) in enumerate(shapes)]
+    spread = W.c3_spread(seed=15, shape=(256, 512))
+    weights.append(spread if dtype == "fp32" else np.ascontiguousarray((spread >> 16).astype(np.uint16)))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xs = [to_dev(b, dev) if b.size else torch.empty(b.shape, dtype=tdt, device=dev) for b in weights]
+    base = to_dev(np.concatenate([np.zeros((weights[3].shape[0], 1), weights[3].dtype), weights[3]], axis=1), dev)
+    xs[3] = base[:, 1:]                                         # misaligned view
+    datas, codes = mxq.mxq_mxfp4_to_fp8_block128_grouped(xs)
+    for i, (bits, d, c) in enumerate(zip(weights, datas, codes)):
+        if bits.size:
+            wd, wc = oracle.mxfp4_to_fp8_block128(bits, threads=THREADS)
+            assert_bits(to_host(d), wd, f"weight {i} {bits.shape} payload")
+            assert_bits(to_host(c), wc, f"weight {i} {bits.shape} tile codes")
+
+
+def test_prepared_grouped_fold_follows_its_weights(dev):
+    a_bits = [_weight(256, 384, "bf16", 500 + i) for i in range(3)]
+    b_bits = [_weight(256, 384, "bf16", 510 + i) for i in range(3)]
+    xs = [to_dev(b, dev) for b in a_bits]
+    call = mxq.GroupedBlock128(xs)
+    for bits in (a_bits, b_bits):
+        for x, b in zip(xs, bits):
+            x.copy_(to_dev(b, dev))
+        datas, codes = call()
+        for i, b in enumerate(bits):
+            wd, wc = oracle.mxfp4_to_fp8_block128(b, threads=THREADS)
+            assert_bits(to_host(datas[i]), wd, f"weight {i} payload")
+            assert_bits(to_host(codes[i]), wc, f"weight {i} tile codes")
