@@ -401,18 +401,18 @@ struct StepGeom {
   static constexpr int64_t kElemsPerStep = (int64_t)kBlocksPerStep * 32;
 };
 
+// The projection's steps of workgroup wg: kProjSteps steps of kProjThreads
+// lanes, all loads issued before the first store.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict__ x, int64_t ld_x, T* __restrict__ y,
-                                                            int64_t ld_y, int64_t K, MxqDivisor steps_per_row,
-                                                            uint32_t total_steps) {
+__device__ __forceinline__ void proj_steps(const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y,
+                                           int64_t K, MxqDivisor steps_per_row, uint32_t total_steps, uint32_t wg) {
   using G = StepGeom<T, kProjThreads>;
-  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   u32x4 w[kProjSteps];
 #pragma unroll
   for (int u = 0; u < kProjSteps; u++) {
-    const uint32_t step = blockIdx.x * kProjSteps + u;
+    const uint32_t step = wg * kProjSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict_
   }
 #pragma unroll
   for (int u = 0; u < kProjSteps; u++) {
-    const uint32_t step = blockIdx.x * kProjSteps + u;
+    const uint32_t step = wg * kProjSteps + u;
     if (step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const Block b = chunk_block<T>(w[u]);
@@ -431,6 +431,14 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict_
                                 proj_chunk<T>(p, b.poison));
     }
   }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kProjThreads) void proj_kernel(const T* __restrict__ x, int64_t ld_x, T* __restrict__ y,
+                                                            int64_t ld_y, int64_t K, MxqDivisor steps_per_row,
+                                                            uint32_t total_steps) {
+  keep_denormals();
+  proj_steps<T, VEC>(x, ld_x, y, ld_y, K, steps_per_row, total_steps, blockIdx.x);
 }
 
 // A no-op flag (device memory): when it is non-zero the launch leaves every
@@ -448,22 +456,21 @@ struct RowShape {
   static constexpr int kTPB = kProj ? kFusedThreads : kRowThreads, kSteps = kProj ? kFusedSteps : kRowSteps;
 };
 
+// The row lift's steps of workgroup wg (with kProj, also the projection y);
+// all loads are issued before the no-op flag is read and before any store.
 template <typename T, bool VEC, bool kProj>
-__global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
-                                                                 uint8_t* __restrict__ data,
-                                                                 uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                                 T* __restrict__ y, int64_t ld_y,
-                                                                 MxqDivisor steps_per_row, uint32_t total_steps,
-                                                                 const int32_t* __restrict__ noop) {
+__device__ __forceinline__ void row_steps(const T* __restrict__ x, int64_t ld_x, int64_t K,
+                                          uint8_t* __restrict__ data, uint8_t* __restrict__ scale, int64_t scale_ld,
+                                          T* __restrict__ y, int64_t ld_y, MxqDivisor steps_per_row,
+                                          uint32_t total_steps, uint32_t wg, const int32_t* __restrict__ noop) {
   using G = StepGeom<T, RowShape<kProj>::kTPB>;
   constexpr int kRowSteps = RowShape<kProj>::kSteps;
-  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   u32x4 w[kRowSteps];
 #pragma unroll
   for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = blockIdx.x * kRowSteps + u;
+    const uint32_t step = wg * kRowSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
@@ -473,7 +480,7 @@ __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __r
   if (skipped(noop)) return;   // read once the input loads are in flight
 #pragma unroll
   for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = blockIdx.x * kRowSteps + u;
+    const uint32_t step = wg * kRowSteps + u;
     if (step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
@@ -487,6 +494,17 @@ __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __r
       if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)code;
     }
   }
+}
+
+template <typename T, bool VEC, bool kProj>
+__global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+                                                                 uint8_t* __restrict__ data,
+                                                                 uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                                 T* __restrict__ y, int64_t ld_y,
+                                                                 MxqDivisor steps_per_row, uint32_t total_steps,
+                                                                 const int32_t* __restrict__ noop) {
+  keep_denormals();
+  row_steps<T, VEC, kProj>(x, ld_x, K, data, scale, scale_ld, y, ld_y, steps_per_row, total_steps, blockIdx.x, noop);
 }
 
 // ------------------------------------------------------------------------------------
@@ -543,38 +561,11 @@ static_assert(sizeof(RowGroupTable) <= 3584, "the table must fit the kernel-argu
 
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void row_grouped_kernel(const RowGroupTable tab) {
-  using G = StepGeom<T, kRowThreads>;
   const RowGroupDesc d = tab.g[blockIdx.y];
-  const uint32_t lwg = blockIdx.x;
-  if (lwg * kRowSteps >= d.total_steps) return;              // uniform: past this weight's steps
+  if (blockIdx.x * kRowSteps >= d.total_steps) return;       // uniform: past this weight's steps
   keep_denormals();
-  const uint32_t tid = threadIdx.x;
-  const T* x = static_cast<const T*>(d.x);
-  const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
-  u32x4 w[kRowSteps];
-#pragma unroll
-  for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = lwg * kRowSteps + u;
-    w[u] = u32x4{0u, 0u, 0u, 0u};
-    if (step < d.total_steps) {
-      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
-      w[u] = load_chunk<T, true>(x + (int64_t)row * d.ld_x, seg * G::kElemsPerStep + lane_col, d.K);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = lwg * kRowSteps + u;
-    if (step < d.total_steps) {
-      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
-      const int64_t col0 = seg * G::kElemsPerStep + lane_col;
-      const Block bl = chunk_block<T>(w[u]);
-      const float s = e8m0(bl.eb);
-      const uint32_t code = row_code(bl);
-      const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
-      store_payload<T, true>(d.data + (int64_t)row * d.K, col0, d.K, payload_chunk<T>(p, code, bl.poison));
-      if (tid % G::kLPB == 0 && col0 < d.K) d.scale[(int64_t)row * d.scale_ld + col0 / 32] = (uint8_t)code;
-    }
-  }
+  row_steps<T, true, false>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld, nullptr, 0,
+                            d.steps_per_row, d.total_steps, blockIdx.x, nullptr);
 }
 
 // Grouped projection, on the same pattern as the grouped row lift: blockIdx.y
@@ -595,37 +586,11 @@ static_assert(sizeof(ProjGroupTable) <= 3584, "the table must fit the kernel-arg
 
 template <typename T>
 __global__ __launch_bounds__(kProjThreads) void proj_grouped_kernel(const ProjGroupTable tab) {
-  using G = StepGeom<T, kProjThreads>;
   const ProjGroupDesc d = tab.g[blockIdx.y];
-  const uint32_t lwg = blockIdx.x;
-  if (lwg * kProjSteps >= d.total_steps) return;             // uniform: past this weight's steps
+  if (blockIdx.x * kProjSteps >= d.total_steps) return;      // uniform: past this weight's steps
   keep_denormals();
-  const uint32_t tid = threadIdx.x;
-  const T* x = static_cast<const T*>(d.x);
-  T* y = static_cast<T*>(d.y);
-  const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
-  u32x4 w[kProjSteps];
-#pragma unroll
-  for (int u = 0; u < kProjSteps; u++) {
-    const uint32_t step = lwg * kProjSteps + u;
-    w[u] = u32x4{0u, 0u, 0u, 0u};
-    if (step < d.total_steps) {
-      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
-      w[u] = load_chunk<T, true>(x + (int64_t)row * d.ld_x, seg * G::kElemsPerStep + lane_col, d.K);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kProjSteps; u++) {
-    const uint32_t step = lwg * kProjSteps + u;
-    if (step < d.total_steps) {
-      const uint32_t row = mxq_quot(step, d.steps_per_row), seg = step - row * d.steps_per_row.d;
-      const Block b = chunk_block<T>(w[u]);
-      const float s = e8m0(b.eb);
-      const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
-      store_chunk<T, true, true>(y + (int64_t)row * d.ld_y, seg * G::kElemsPerStep + lane_col, d.K,
-                                 proj_chunk<T>(p, b.poison));
-    }
-  }
+  proj_steps<T, true>(static_cast<const T*>(d.x), d.ld_x, static_cast<T*>(d.y), d.ld_y, d.K, d.steps_per_row,
+                      d.total_steps, blockIdx.x);
 }
 
 template <typename T, bool VEC, bool kRow>
