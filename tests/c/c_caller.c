@@ -5,7 +5,8 @@
  * decodes -- on a stream of its own, checks every status, and writes the outputs
  * to a file for the test (tests/test_gpu_c_caller.py) to compare with the oracle.
  * It also checks that argument errors come back as status codes before any
- * launch.
+ * launch, and that the grouped row lift of two weights gives the single
+ * call's bytes.
  *
  * usage: c_caller ROWS K SCALE_LD IN.bin OUT.bin
  *   IN.bin   ROWS*K bf16 bit patterns (uint16, little endian)
@@ -87,12 +88,48 @@ int main(int argc, char** argv) {
   MXQ_OK_OR_DIE(mxq_mxfp4_to_fp8_block128(x, K, rows, K, MXQ_BF16, bdata, tc, tcn, s));
   MXQ_OK_OR_DIE(mxq_dequantize(data, comp, nb, rows, K, MXQ_E4M3, MXQ_SCALE_ROW_1X32, dec_r, K, MXQ_BF16, s));
   MXQ_OK_OR_DIE(mxq_dequantize(bdata, tc, tcn, rows, K, MXQ_E4M3, MXQ_SCALE_TILE_128X128, dec_t, K, MXQ_BF16, s));
+  /* The grouped row lift of two weights (the whole weight and its first half of
+   * rows, read-only overlap is allowed) gives the single call's bytes. */
+  const int64_t half = rows / 2 > 0 ? rows / 2 : 1;
+  uint8_t *gdata[2], *gscale[2];
+  for (int i = 0; i < 2; i++) {
+    HIP_OK(hipMalloc((void**)&gdata[i], (size_t)n));
+    HIP_OK(hipMalloc((void**)&gscale[i], (size_t)(rows * sld)));
+    HIP_OK(hipMemset(gscale[i], 0, (size_t)(rows * sld)));
+  }
+  const mxq_row_group groups[2] = {{x, K, rows, K, gdata[0], gscale[0], sld}, {x, K, half, K, gdata[1], gscale[1], sld}};
+  MXQ_OK_OR_DIE(mxq_mxfp4_to_mxfp8_row_grouped(groups, 2, MXQ_BF16, s));
   /* an overlap is refused: the payload written over the weight */
   if (mxq_mxfp4_to_mxfp8_row(x, K, rows, K, MXQ_BF16, (uint8_t*)x, scale, sld, s) != MXQ_ERR_ALIAS) {
     fprintf(stderr, "c_caller: an aliased output was not refused\n");
     return 4;
   }
   HIP_OK(hipStreamSynchronize(s));
+  {
+    uint8_t* a = (uint8_t*)malloc((size_t)n);
+    uint8_t* b = (uint8_t*)malloc((size_t)n);
+    const size_t sizes[2] = {(size_t)n, (size_t)(half * K)};
+    for (int i = 0; i < 2; i++) {
+      HIP_OK(hipMemcpy(a, data, sizes[i], hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(b, gdata[i], sizes[i], hipMemcpyDeviceToHost));
+      if (memcmp(a, b, sizes[i]) != 0) {
+        fprintf(stderr, "c_caller: grouped row lift differs from the single call (weight %d)\n", i);
+        return 5;
+      }
+      HIP_OK(hipMemcpy(a, scale, (size_t)((i ? half : rows) * sld), hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(b, gscale[i], (size_t)((i ? half : rows) * sld), hipMemcpyDeviceToHost));
+      if (memcmp(a, b, (size_t)((i ? half : rows) * sld)) != 0) {
+        fprintf(stderr, "c_caller: grouped codes differ from the single call (weight %d)\n", i);
+        return 5;
+      }
+    }
+    free(a);
+    free(b);
+    for (int i = 0; i < 2; i++) {
+      HIP_OK(hipFree(gdata[i]));
+      HIP_OK(hipFree(gscale[i]));
+    }
+  }
 
   const size_t sizes[7] = {(size_t)n * 2, (size_t)n, (size_t)(rows * nb), (size_t)n, (size_t)(tr * tcn),
                            (size_t)n * 2, (size_t)n * 2};
