@@ -46,7 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 SCALE_PAD = 4                    # padded scale storage: ceil(K/32) plus 4 columns (8192: 260)
-GROUPED = (48, 1024, 2048)       # outside the step: the grouped row lift of 48 weights of 1024 x 2048 (one launch)
+GROUPED = (48, 1024, 2048)       # outside the step: grouped calls over 48 weights of 1024 x 2048 (one launch each)
 SHAPES = ("8192x8192", "28672x8192", "8192x28672")
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
@@ -264,6 +264,7 @@ def main():
             "gy": [torch.empty((gr, gk), dtype=g0.dtype, device=dev) for _ in range(gn)],
             "gbdata": [torch.empty((gr, gk), dtype=torch.uint8, device=dev) for _ in range(gn)],
             "gtc": [torch.zeros((gr // 128, gk // 128), dtype=torch.uint8, device=dev) for _ in range(gn)],
+            "gdec": [torch.empty((gr, gk), dtype=g0.dtype, device=dev) for _ in range(gn)],
         }
         mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
         mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
@@ -299,22 +300,26 @@ def main():
                                                                      s["cscale"])
     launches["dec_col"] = lambda s: mxq.mxq_dequantize(s["cdata"], s["cscale"], layout=mxq.MXQ_SCALE_COL_32X1,
                                                        out=s["dec_c"])
-    # outside the step: the row lift, the projection and the fold of 48 weights of 1024 x 2048, each in one
-    # grouped call
+    # outside the step: the row lift, the projection, the fold and the row-layout decode of 48 weights of
+    # 1024 x 2048, each in one grouped call
     # (prepared once per buffer set, as for weights re-converted every step)
     for s in sets:
         s["grouped"] = mxq.GroupedRowLift(s["gx"], s["gdata"], s["gscale"])
         s["grouped_proj"] = mxq.GroupedProjection(s["gx"], s["gy"])
         s["grouped_fold"] = mxq.GroupedBlock128(s["gx"], s["gbdata"], s["gtc"])
+        s["grouped_dec"] = mxq.GroupedDequantize(s["gdata"], s["gscale"], outs=s["gdec"])
+        s["grouped"]()                                    # the payloads and codes the decode reads
     launches["row_grouped"] = lambda s: s["grouped"]()
     launches["proj_grouped"] = lambda s: s["grouped_proj"]()
     launches["block128_grouped"] = lambda s: s["grouped_fold"]()
+    launches["dec_row_grouped"] = lambda s: s["grouped_dec"]()
     extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128", "col",
-                   "row_col", "dec_col", "row_grouped", "proj_grouped", "block128_grouped"]
+                   "row_col", "dec_col", "row_grouped", "proj_grouped", "block128_grouped", "dec_row_grouped"]
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
     offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1,
               "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0, "col": 2,
-              "row_col": 4, "dec_col": 1, "row_grouped": 0, "proj_grouped": 2, "block128_grouped": 4}
+              "row_col": 4, "dec_col": 1, "row_grouped": 0, "proj_grouped": 2, "block128_grouped": 4,
+              "dec_row_grouped": 1}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -398,7 +403,8 @@ def main():
     extra_bytes = dict(packed_bytes(rows, K, es), fused=fused_bytes(rows, K, es), **col_bytes(rows, K, es),
                        row_grouped=gn * algorithmic_bytes(gr, gk, es)["row"],
                        proj_grouped=gn * algorithmic_bytes(gr, gk, es)["proj"],
-                       block128_grouped=gn * algorithmic_bytes(gr, gk, es)["block128"])
+                       block128_grouped=gn * algorithmic_bytes(gr, gk, es)["block128"],
+                       dec_row_grouped=gn * algorithmic_bytes(gr, gk, es)["dec_row"])
     for n in extra_names:
         us, med, lo = burst_stats(n)
         gbs = extra_bytes[n] / (us * 1e-6) / 1e9

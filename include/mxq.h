@@ -12,8 +12,9 @@
  *   mxq_mxfp4_to_mxfp8_row_guarded,
  *   mxq_mxfp4_to_fp8_block128_guarded         the direct conversions behind a device no-op flag
  *   mxq_mxfp4_to_mxfp8_row_grouped, mxq_fake_quantize_mxfp4_grouped,
- *   mxq_mxfp4_to_fp8_block128_grouped         the row lift / projection / fold of a list of weights
- *                                             in few launches
+ *   mxq_mxfp4_to_fp8_block128_grouped,
+ *   mxq_dequantize_grouped                    the row lift / projection / fold / decode of a list
+ *                                             of weights in few launches
  * the packed MXFP4 deployment format:
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
  *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
@@ -351,6 +352,37 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
 int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                    mxq_fp8 fmt, mxq_scale_layout layout, void* out, int64_t ld_out, mxq_dtype out_dt,
                    hipStream_t stream);
+
+/*
+ * One weight of a grouped decode: the arguments of mxq_dequantize for that
+ * weight (data, scale and out are device pointers).
+ */
+typedef struct {
+  const uint8_t* data;   /* [rows, K] uint8 payload, contiguous */
+  const uint8_t* scale;  /* E8M0 codes in the call's layout, row stride scale_ld */
+  int64_t scale_ld;
+  int64_t rows;
+  int64_t K;
+  void* out;             /* [rows, K] in the call's output dtype, row stride ld_out >= K */
+  int64_t ld_out;
+} mxq_dequant_group;
+
+/*
+ * The decode of mxq_dequantize (code 0 is 2^-127 and code 255 NaN, [QAT]
+ * Description; the same NaN and overflow rules) applied to a list of weights
+ * with one payload format, scale layout and output dtype (the experts of a
+ * grouped linear layer, [QAT] Test results, end-to-end cases), in as few
+ * launches as possible.  Results are bit-identical to one mxq_dequantize call
+ * per weight.
+ *   groups    HOST array of n_groups descriptors, read during the call only
+ *   n_groups  >= 0; groups with rows == 0 or K == 0 are skipped
+ *   Every group is checked as mxq_dequantize checks its arguments (the first
+ *   failing group's status is returned and nothing is enqueued).  In addition
+ *   no group's out may overlap any group's data, scale or out (MXQ_ERR_ALIAS);
+ *   inputs may overlap each other.
+ */
+int mxq_dequantize_grouped(const mxq_dequant_group* groups, int64_t n_groups, mxq_fp8 fmt,
+                           mxq_scale_layout layout, mxq_dtype out_dt, hipStream_t stream);
 
 /*
  * Packed MXFP4, the deployment format: E2M1 payloads with 1x32 power-of-two

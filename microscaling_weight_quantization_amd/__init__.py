@@ -38,7 +38,7 @@ ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mx
                 "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
                 "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded",
                 "mxq_mxfp4_to_mxfp8_row_grouped", "mxq_fake_quantize_mxfp4_grouped",
-                "mxq_mxfp4_to_fp8_block128_grouped")
+                "mxq_mxfp4_to_fp8_block128_grouped", "mxq_dequantize_grouped")
 
 _libs = {}
 _lock = threading.Lock()
@@ -60,6 +60,12 @@ class _Block128Group(ctypes.Structure):
     """mxq_block128_group of include/mxq.h."""
     _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("data", ctypes.c_void_p), ("tile_code", ctypes.c_void_p), ("tile_ld", ctypes.c_int64)]
+
+
+class _DequantGroup(ctypes.Structure):
+    """mxq_dequant_group of include/mxq.h."""
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_ld", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("K", ctypes.c_int64), ("out", ctypes.c_void_p), ("ld_out", ctypes.c_int64)]
 
 
 class MxqError(RuntimeError):
@@ -100,6 +106,7 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_mxfp4_to_mxfp8_row_grouped.argtypes = [ctypes.POINTER(_RowGroup), i64, i32, vp]
         L.mxq_fake_quantize_mxfp4_grouped.argtypes = [ctypes.POINTER(_ProjGroup), i64, i32, vp]
         L.mxq_mxfp4_to_fp8_block128_grouped.argtypes = [ctypes.POINTER(_Block128Group), i64, i32, vp]
+        L.mxq_dequantize_grouped.argtypes = [ctypes.POINTER(_DequantGroup), i64, i32, i32, i32, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -348,6 +355,65 @@ class GroupedBlock128:
             _check(self._L, self._L.mxq_mxfp4_to_fp8_block128_grouped(self._table, self.n, self._dt,
                                                                        _stream(self.xs[0])))
         return self.datas, self.tile_codes
+
+
+class GroupedDequantize:
+    """The grouped decode prepared once for a fixed list of payloads, codes and
+    outputs of one payload format, scale layout and output dtype; each call
+    enqueues it on torch's current stream with one call into the library.  The
+    object keeps the tensors alive; `outs` are the outputs."""
+
+    def __init__(self, datas, scales, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3, outs=None,
+                 out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so"):
+        self._L = load(lib)
+        datas, scales = list(datas), list(scales)
+        n = len(datas)
+        outs = [None] * n if outs is None else list(outs)
+        if len(scales) != n or len(outs) != n:
+            raise ValueError("scales and outs must have one entry per payload")
+        self.datas, self.n = datas, n
+        self._fmt, self._layout = fmt, layout
+        if n == 0:
+            self.outs = []
+            return
+        dev = datas[0].device
+        for t in datas + scales + outs:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+                raise ValueError("mxq_dequantize_grouped: operands must be device tensors on one device")
+        for i, d in enumerate(datas):
+            if outs[i] is None:
+                outs[i] = torch.empty(tuple(d.shape), dtype=out_dtype, device=dev)
+        if any(o.dtype != outs[0].dtype for o in outs):
+            raise ValueError("all outputs of a group call must have one dtype")
+        self._dt = _dtype_code(outs[0])
+        self._table = (_DequantGroup * n)()
+        for i in range(n):
+            pd, rows, K, ldd = _matrix(datas[i])
+            if rows * K and ldd != K:
+                raise ValueError("payload must be contiguous")
+            ps, _, _, lds = _matrix(scales[i])
+            po, _, _, ldo = _matrix(outs[i])
+            self._table[i] = _DequantGroup(pd, ps, lds, rows, K, po, ldo)
+        self.outs = outs
+
+    def __call__(self):
+        if self.n:
+            _check(self._L, self._L.mxq_dequantize_grouped(self._table, self.n, self._fmt, self._layout, self._dt,
+                                                            _stream(self.datas[0])))
+        return self.outs
+
+
+@_device_operands
+def mxq_dequantize_grouped(datas, scales, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3, outs=None,
+                           out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so"):
+    """Decode a list of FP8 payloads with their E8M0 codes (one format, scale
+    layout and output dtype), in as few launches as possible -> list of
+    outputs; the same bits as one mxq_dequantize per payload.  `outs`: list of
+    outputs (None entries, or None for the whole list, are allocated).
+    GroupedDequantize prepares the call once for repeated use."""
+    return GroupedDequantize(datas, scales, layout, fmt, outs, out_dtype, lib)()
 
 
 @_device_operands

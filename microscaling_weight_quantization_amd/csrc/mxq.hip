@@ -890,11 +890,12 @@ __device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8])
                bf16_pair_of_fp8_each<kE5M2, false>(q[1], s[4], s[5]), bf16_pair_of_fp8_each<kE5M2, true>(q[1], s[6], s[7])};
 }
 
+// The decode's body: workgroup wg's kDequantSteps steps of one weight.  The
+// single and grouped kernels both run it.
 template <typename TO, bool kE5M2, int kLay, bool VEC>
-__global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
-                                                           const uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                           int64_t K, TO* __restrict__ out, int64_t ld_out,
-                                                           MxqDivisor steps_per_row, uint32_t total_steps) {
+__device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, const uint8_t* __restrict__ scale,
+                                              int64_t scale_ld, int64_t K, TO* __restrict__ out, int64_t ld_out,
+                                              MxqDivisor steps_per_row, uint32_t total_steps, uint32_t wg) {
   // 8 payload bytes per lane per step; a step is kDequantThreads * 8 elements of one row.
   // Lane geometry: bf16 output takes 8 consecutive elements per lane (one 16-byte
   // store).  fp32 output (kSplit) takes two groups of 4, half a step apart, so
@@ -903,7 +904,6 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
   // only half lines per instruction and run far slower.
   constexpr bool kSplit = sizeof(TO) == 4;
   constexpr int64_t kHalf = (int64_t)kDequantThreads * 4;
-  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * (kSplit ? 4 : 8);
   // All of the workgroup's loads are issued before any decode or store.
@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
     cs[u] = 0u;
     if constexpr (kSplit) cs_b[u] = 0u;
     if constexpr (kLay == kLayCol) ccs[u] = u32x2{0u, 0u};
-    const uint32_t step = blockIdx.x * kDequantSteps + u;
+    const uint32_t step = wg * kDequantSteps + u;
     if (step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
@@ -972,7 +972,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
   }
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
-    const uint32_t step = blockIdx.x * kDequantSteps + u;
+    const uint32_t step = wg * kDequantSteps + u;
     if (step >= total_steps) break;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
@@ -1026,6 +1026,41 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
       }
     }
   }
+}
+
+template <typename TO, bool kE5M2, int kLay, bool VEC>
+__global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
+                                                           const uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                           int64_t K, TO* __restrict__ out, int64_t ld_out,
+                                                           MxqDivisor steps_per_row, uint32_t total_steps) {
+  keep_denormals();
+  dequant_steps<TO, kE5M2, kLay, VEC>(data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps, blockIdx.x);
+}
+
+// Grouped decode, on the grouped row lift's pattern: blockIdx.y is the weight,
+// blockIdx.x the workgroup within it; one payload format, scale layout and
+// output dtype per launch.  Aligned (VEC) weights only.
+struct DequantGroupDesc {
+  const uint8_t* data;
+  const uint8_t* scale;
+  int64_t scale_ld, K;
+  void* out;
+  int64_t ld_out;
+  MxqDivisor steps_per_row;
+  uint32_t total_steps;
+};
+struct DequantGroupTable {
+  DequantGroupDesc g[kGroupMax];
+};
+static_assert(sizeof(DequantGroupTable) <= 3584, "the table must fit the kernel-argument segment");
+
+template <typename TO, bool kE5M2, int kLay>
+__global__ __launch_bounds__(kDequantThreads) void dequant_grouped_kernel(const DequantGroupTable tab) {
+  const DequantGroupDesc d = tab.g[blockIdx.y];
+  if (blockIdx.x * kDequantSteps >= d.total_steps) return;   // uniform: past this weight's steps
+  keep_denormals();
+  dequant_steps<TO, kE5M2, kLay, true>(d.data, d.scale, d.scale_ld, d.K, static_cast<TO*>(d.out), d.ld_out,
+                                       d.steps_per_row, d.total_steps, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1786,6 +1821,60 @@ int launch_block128_grouped(const mxq_block128_group* gs, int64_t n, hipStream_t
   return flush();
 }
 
+// Grouped decode: the grouped row lift's batching, for the decode of one
+// payload format, scale layout and output dtype.
+template <typename TO, bool kE5M2, int kLay>
+int launch_dequant_grouped_t(const mxq_dequant_group* gs, int64_t n, hipStream_t s) {
+  constexpr int OPC = 16 / (int)sizeof(TO);
+  DequantGroupTable tab{};
+  int64_t count = 0, max_w = 0, sum_w = 0;
+  auto flush = [&]() -> int {
+    if (count == 0) return MXQ_OK;
+    hipLaunchKernelGGL((dequant_grouped_kernel<TO, kE5M2, kLay>), dim3((uint32_t)max_w, (uint32_t)count),
+                       dim3(kDequantThreads), 0, s, tab);
+    count = max_w = sum_w = 0;
+    return launch_status();
+  };
+  for (int64_t i = 0; i < n; i++) {
+    const mxq_dequant_group& g = gs[i];
+    if (g.rows == 0 || g.K == 0) continue;
+    if (!(aligned(g.data, 8) && g.K % 8 == 0 && aligned(g.out, 16) && g.ld_out % OPC == 0 &&
+          (kLay != kLayCol || (aligned(g.scale, 8) && g.scale_ld % 8 == 0)))) {
+      const int st = launch_dequant_t<TO, kE5M2, kLay>(g.data, g.scale, g.scale_ld, g.rows, g.K, g.out, g.ld_out, s);
+      if (st != MXQ_OK) return st;
+      continue;
+    }
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t gw = grid_for(total, kDequantSteps);
+    const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
+    if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
+      const int st = flush();
+      if (st != MXQ_OK) return st;
+    }
+    tab.g[count] = DequantGroupDesc{g.data, g.scale, g.scale_ld, g.K, g.out, g.ld_out, spr, total};
+    count++;
+    max_w = std::max(max_w, gw);
+    sum_w += gw;
+  }
+  return flush();
+}
+
+template <typename TO, bool kE5M2>
+int launch_dequant_grouped_f(const mxq_dequant_group* gs, int64_t n, mxq_scale_layout lay, hipStream_t s) {
+  if (lay == MXQ_SCALE_TILE_128X128) return launch_dequant_grouped_t<TO, kE5M2, kLayTile>(gs, n, s);
+  if (lay == MXQ_SCALE_COL_32X1) return launch_dequant_grouped_t<TO, kE5M2, kLayCol>(gs, n, s);
+  return launch_dequant_grouped_t<TO, kE5M2, kLayRow>(gs, n, s);
+}
+
+template <typename TO>
+int launch_dequant_grouped(const mxq_dequant_group* gs, int64_t n, mxq_fp8 fmt, mxq_scale_layout lay,
+                           hipStream_t s) {
+  return fmt == MXQ_E5M2 ? launch_dequant_grouped_f<TO, true>(gs, n, lay, s)
+                         : launch_dequant_grouped_f<TO, false>(gs, n, lay, s);
+}
+
 // The ranges of a grouped call, each marked as an output or not: true when no
 // output overlaps any other range.  A sweep in order of start address: a range
 // overlaps an earlier one exactly when it starts before the largest end seen
@@ -2129,6 +2218,31 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
   return launch_status();
 }
 
+// Argument checks of the decode, format and layout already checked.  For a
+// non-empty matrix it returns MXQ_OK with r = {data, scale, out}; for an empty
+// one MXQ_OK with *empty set.
+static int dequant_check(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
+                         mxq_scale_layout layout, const void* out, int64_t ld_out, mxq_dtype out_dt, Range* r,
+                         bool* empty) {
+  *empty = false;
+  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (rows == 0 || K == 0) {
+    *empty = true;
+    return MXQ_OK;
+  }
+  if (!data || !scale || !out) return MXQ_ERR_NULL;
+  const bool tile = layout == MXQ_SCALE_TILE_128X128, col = layout == MXQ_SCALE_COL_32X1;
+  const int64_t srows = tile ? (rows + 127) / 128 : col ? (rows + 31) / 32 : rows,
+                scols = tile ? (K + 127) / 128 : col ? K : (K + 31) / 32;
+  if (ld_out < K || scale_ld < scols) return MXQ_ERR_SHAPE;
+  r[0] = matrix_range(data, rows, K, K, 1);
+  r[1] = matrix_range(scale, srows, scols, scale_ld, 1);
+  r[2] = matrix_range(out, rows, K, ld_out, dtype_size(out_dt));
+  if (!spans_ok({r[0], r[1], r[2]})) return MXQ_ERR_SHAPE;
+  if (overlap(r[2], r[0]) || overlap(r[2], r[1])) return MXQ_ERR_ALIAS;
+  return MXQ_OK;
+}
+
 int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,
                    mxq_fp8 fmt, mxq_scale_layout layout, void* out, int64_t ld_out, mxq_dtype out_dt,
                    hipStream_t stream) {
@@ -2136,19 +2250,43 @@ int mxq_dequantize(const uint8_t* data, const uint8_t* scale, int64_t scale_ld, 
   if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_DTYPE;
   if (layout != MXQ_SCALE_ROW_1X32 && layout != MXQ_SCALE_TILE_128X128 && layout != MXQ_SCALE_COL_32X1)
     return MXQ_ERR_DTYPE;
-  if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (rows == 0 || K == 0) return MXQ_OK;
-  if (!data || !scale || !out) return MXQ_ERR_NULL;
-  const bool tile = layout == MXQ_SCALE_TILE_128X128, col = layout == MXQ_SCALE_COL_32X1;
-  const int64_t srows = tile ? (rows + 127) / 128 : col ? (rows + 31) / 32 : rows,
-                scols = tile ? (K + 127) / 128 : col ? K : (K + 31) / 32;
-  if (ld_out < K || scale_ld < scols) return MXQ_ERR_SHAPE;
-  const Range ro = matrix_range(out, rows, K, ld_out, dtype_size(out_dt)), rd = matrix_range(data, rows, K, K, 1),
-              rs = matrix_range(scale, srows, scols, scale_ld, 1);
-  if (!spans_ok({ro, rd, rs})) return MXQ_ERR_SHAPE;
-  if (overlap(ro, rd) || overlap(ro, rs)) return MXQ_ERR_ALIAS;
+  Range r[3];
+  bool empty;
+  const int st = dequant_check(data, scale, scale_ld, rows, K, layout, out, ld_out, out_dt, r, &empty);
+  if (st != MXQ_OK || empty) return st;
   return out_dt == MXQ_BF16 ? launch_dequant<uint16_t>(data, scale, scale_ld, rows, K, fmt, layout, out, ld_out, stream)
                             : launch_dequant<uint32_t>(data, scale, scale_ld, rows, K, fmt, layout, out, ld_out, stream);
+}
+
+int mxq_dequantize_grouped(const mxq_dequant_group* groups, int64_t n_groups, mxq_fp8 fmt, mxq_scale_layout layout,
+                           mxq_dtype out_dt, hipStream_t stream) {
+  if (check_dtype(out_dt)) return MXQ_ERR_DTYPE;
+  if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_DTYPE;
+  if (layout != MXQ_SCALE_ROW_1X32 && layout != MXQ_SCALE_TILE_128X128 && layout != MXQ_SCALE_COL_32X1)
+    return MXQ_ERR_DTYPE;
+  if (n_groups < 0) return MXQ_ERR_SHAPE;
+  if (n_groups == 0) return MXQ_OK;
+  if (!groups) return MXQ_ERR_NULL;
+  // every group on its own, then no output may overlap any other range
+  std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
+  iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 3);
+  for (int64_t i = 0; i < n_groups; i++) {
+    const mxq_dequant_group& g = groups[i];
+    Range r[3];
+    bool empty;
+    const int st = dequant_check(g.data, g.scale, g.scale_ld, g.rows, g.K, layout, g.out, g.ld_out, out_dt, r, &empty);
+    if (st != MXQ_OK) return st;
+    if (empty) continue;
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
+    iv.push_back({r[0], false});
+    iv.push_back({r[1], false});
+    iv.push_back({r[2], true});
+  }
+  if (!grouped_ranges_disjoint(iv)) return MXQ_ERR_ALIAS;
+  return out_dt == MXQ_BF16 ? launch_dequant_grouped<uint16_t>(groups, n_groups, fmt, layout, stream)
+                            : launch_dequant_grouped<uint32_t>(groups, n_groups, fmt, layout, stream);
 }
 
 int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* packed,

@@ -279,3 +279,35 @@ def test_grouped_fold_host_validation(lib):
     assert call(a, grp(0x110000, 0x210000, 0x200010)) == mxq.MXQ_ERR_ALIAS      # b's codes in a's payload
     assert call(a, grp(0x110000, 0x210000, 0x300001)) == mxq.MXQ_ERR_ALIAS      # code arrays overlap
     assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK
+
+
+def test_grouped_decode_host_validation(lib):
+    """The grouped decode checks the call's format, layout and output dtype,
+    every payload as the single call does, and refuses outputs over other
+    payloads' ranges, before anything is enqueued."""
+    G = mxq._DequantGroup
+
+    def grp(data, scale, out, rows=4, K=256, sld=8, ldo=256):
+        return G(data, scale, sld, rows, K, out, ldo)
+
+    def call(*groups, fmt=mxq.MXQ_E4M3, lay=mxq.MXQ_SCALE_ROW_1X32, dt=mxq.MXQ_BF16, n=None):
+        arr = (G * max(len(groups), 1))(*groups)
+        return lib.mxq_dequantize_grouped(arr, len(groups) if n is None else n, fmt, lay, dt, None)
+
+    a = grp(0x100000, 0x200000, 0x300000)          # 4 x 256 payload: 1 KiB; 4 x 8 codes; bf16 out 2 KiB
+    b = grp(0x110000, 0x210000, 0x310000)
+    assert call(a, b, n=-1) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_dequantize_grouped(None, 1, mxq.MXQ_E4M3, mxq.MXQ_SCALE_ROW_1X32, mxq.MXQ_BF16,
+                                      None) == mxq.MXQ_ERR_NULL
+    assert call(a, b, dt=mxq.MXQ_FP16) == mxq.MXQ_ERR_DTYPE
+    assert call(a, b, fmt=7) == mxq.MXQ_ERR_DTYPE
+    assert call(a, b, lay=9) == mxq.MXQ_ERR_DTYPE
+    assert call(a, grp(0x110000, None, 0x310000)) == mxq.MXQ_ERR_NULL
+    assert call(a, grp(0x110000, 0x210000, 0x310000, sld=7)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, grp(0x110000, 0x210000, 0x310000, ldo=255)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, b, lay=mxq.MXQ_SCALE_COL_32X1) == mxq.MXQ_ERR_SHAPE    # the column layout needs sld >= K
+    assert call(a, grp(0x110000, 0x210000, 0x100000)) == mxq.MXQ_ERR_ALIAS  # b's output over a's payload
+    assert call(a, grp(0x110000, 0x210000, 0x1FFF00)) == mxq.MXQ_ERR_ALIAS  # b's output over a's codes
+    assert call(a, grp(0x110000, 0x210000, 0x300010)) == mxq.MXQ_ERR_ALIAS  # outputs overlap
+    assert call(grp(0x100000, 0x200000, 0x100100)) == mxq.MXQ_ERR_ALIAS     # a single payload's own overlap
+    assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK

@@ -1,7 +1,7 @@
-"""The grouped row lift (mxq_mxfp4_to_mxfp8_row_grouped) against the oracle:
-mixed ragged shapes in one call, padded scale storage left untouched, a
-misaligned weight (the per-weight path), empty weights, and more weights than
-one launch's table holds."""
+"""The grouped entry points (row lift, projection, 128x128 fold and decode)
+against the oracle: mixed ragged shapes in one call, padded scale storage left
+untouched, misaligned operands (the per-weight path), empty weights, more
+weights than one launch's table holds, and overlaps across weights refused."""
 import numpy as np
 import pytest
 import torch
@@ -179,3 +179,101 @@ def test_prepared_grouped_fold_follows_its_weights(dev):
             wd, wc = oracle.mxfp4_to_fp8_block128(b, threads=THREADS)
             assert_bits(to_host(datas[i]), wd, f"weight {i} payload")
             assert_bits(to_host(codes[i]), wc, f"weight {i} tile codes")
+
+
+def _decode_inputs(shapes, layout, seed):
+    """Random payload bytes (every FP8 pattern, NaNs included) and random E8M0
+    codes (0 and 255 included) in the layout's scale shape, with padding
+    columns in every scale row (eight for the column layout, whose vector path
+    needs a row stride that is a multiple of 8)."""
+    rng = np.random.default_rng(seed)
+    datas, scales = [], []
+    for rows, K in shapes:
+        srows = {mxq.MXQ_SCALE_ROW_1X32: rows, mxq.MXQ_SCALE_TILE_128X128: (rows + 127) // 128,
+                 mxq.MXQ_SCALE_COL_32X1: (rows + 31) // 32}[layout]
+        scols = {mxq.MXQ_SCALE_ROW_1X32: (K + 31) // 32, mxq.MXQ_SCALE_TILE_128X128: (K + 127) // 128,
+                 mxq.MXQ_SCALE_COL_32X1: K}[layout]
+        datas.append(rng.integers(0, 256, (rows, K), dtype=np.uint8))
+        pad = 8 if layout == mxq.MXQ_SCALE_COL_32X1 else 2
+        scales.append(rng.integers(0, 256, (srows, scols + pad), dtype=np.uint8))
+    return datas, scales
+
+
+def _to_dev_u8(a, dev):
+    # an empty host array can arrive with a non-unit last stride: allocate it instead
+    return to_dev(a, dev) if a.size else torch.empty(a.shape, dtype=torch.uint8, device=dev)
+
+
+@pytest.mark.parametrize("layout", [mxq.MXQ_SCALE_ROW_1X32, mxq.MXQ_SCALE_TILE_128X128, mxq.MXQ_SCALE_COL_32X1])
+@pytest.mark.parametrize("fmt", [mxq.MXQ_E4M3, mxq.MXQ_E5M2])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_grouped_decode_mixed_shapes(dev, layout, fmt, out_dtype):
+    """Mixed ragged shapes in one call, one misaligned payload and one
+    misaligned output (the per-payload path), one empty, and more payloads than
+    one table holds; each against the oracle."""
+    shapes = [(128, 128), (300, 520), (1, 33), (256, 4096), (0, 64), (129, 136), (64, 2048), (40, 4104)]
+    shapes += [(int(r), int(k)) for r, k in zip(np.random.default_rng(21).integers(1, 300, 44),
+                                                np.random.default_rng(22).choice([8, 32, 128, 200, 512, 640], 44))]
+    datas_h, scales_h = _decode_inputs(shapes, layout, 600 + 10 * layout + fmt)
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    datas = [_to_dev_u8(d, dev) for d in datas_h]
+    scales = [_to_dev_u8(s, dev) for s in scales_h]
+    r, K = shapes[3]
+    base = torch.empty(r * K + 1, dtype=torch.uint8, device=dev)
+    base[1:].copy_(datas[3].reshape(-1))
+    datas[3] = base[1:].view(r, K)                              # payload not 8-byte aligned
+    outs = [torch.empty(d.shape, dtype=tdt, device=dev) for d in datas]
+    r, K = shapes[6]
+    outs[6] = torch.empty(r * K + 1, dtype=tdt, device=dev)[1:].view(r, K)   # output not 16-byte aligned
+    got = mxq.mxq_dequantize_grouped(datas, scales, layout=layout, fmt=fmt, outs=outs)
+    code = oracle.BF16 if out_dtype == "bf16" else oracle.FP32
+    for i, (d, s, o) in enumerate(zip(datas_h, scales_h, got)):
+        if d.size:
+            want = oracle.dequantize(d, s, layout=layout, fp8=fmt, out_dtype=code, threads=THREADS)
+            assert_bits(to_host(o), want, f"payload {i} {d.shape} layout {layout} fmt {fmt}")
+
+
+def test_grouped_decode_equals_single_calls_with_padded_outputs(dev):
+    """Outputs with a row stride above K: the grouped call writes the same
+    bytes as one mxq_dequantize per payload and leaves the padding alone.  The
+    last payload is the first one again (inputs may be shared)."""
+    shapes = [(200, 256), (64, 1024), (300, 96), (200, 256)]
+    datas_h, scales_h = _decode_inputs(shapes, mxq.MXQ_SCALE_ROW_1X32, 31)
+    datas = [to_dev(d, dev) for d in datas_h]
+    scales = [to_dev(s, dev) for s in scales_h]
+    datas[3], scales[3] = datas[0], scales[0]
+    big = [torch.full((r, K + 24), 7.0, dtype=torch.bfloat16, device=dev) for r, K in shapes]
+    one = [b.clone() for b in big]
+    mxq.mxq_dequantize_grouped(datas, scales, outs=[b[:, :K] for b, (_, K) in zip(big, shapes)])
+    for d, s, b, (_, K) in zip(datas, scales, one, shapes):
+        mxq.mxq_dequantize(d, s, out=b[:, :K])
+    for i in range(len(shapes)):
+        assert_bits(to_host(big[i]), to_host(one[i]), f"payload {i}")
+
+
+def test_prepared_grouped_decode_and_overlaps(dev):
+    shapes = [(256, 384)] * 3
+    a = _decode_inputs(shapes, mxq.MXQ_SCALE_TILE_128X128, 41)
+    b = _decode_inputs(shapes, mxq.MXQ_SCALE_TILE_128X128, 42)
+    datas = [to_dev(d, dev) for d in a[0]]
+    scales = [to_dev(s, dev) for s in a[1]]
+    call = mxq.GroupedDequantize(datas, scales, layout=mxq.MXQ_SCALE_TILE_128X128, out_dtype=torch.float32)
+    for dh, sh in (a, b):
+        for t, h in zip(datas + scales, dh + sh):
+            t.copy_(to_dev(h, dev))
+        outs = call()
+        for i in range(3):
+            want = oracle.dequantize(dh[i], sh[i], layout=mxq.MXQ_SCALE_TILE_128X128, out_dtype=oracle.FP32,
+                                     threads=THREADS)
+            assert_bits(to_host(outs[i]), want, f"payload {i}")
+    o = torch.empty((256, 384), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(mxq.MxqError) as e:                      # two payloads into one output
+        mxq.mxq_dequantize_grouped(datas[:2], scales[:2], layout=mxq.MXQ_SCALE_TILE_128X128, outs=[o, o])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
+    buf = torch.empty(2 * 256 * 384, dtype=torch.uint8, device=dev)
+    buf[: 256 * 384].copy_(datas[0].reshape(-1))
+    with pytest.raises(mxq.MxqError) as e:                      # payload 1's output over payload 0
+        mxq.mxq_dequantize_grouped([buf[: 256 * 384].view(256, 384), datas[1]], scales[:2],
+                                   layout=mxq.MXQ_SCALE_TILE_128X128,
+                                   outs=[o, buf.view(torch.bfloat16).view(256, 384)])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
