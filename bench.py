@@ -265,6 +265,8 @@ def main():
             "gbdata": [torch.empty((gr, gk), dtype=torch.uint8, device=dev) for _ in range(gn)],
             "gtc": [torch.zeros((gr // 128, gk // 128), dtype=torch.uint8, device=dev) for _ in range(gn)],
             "gdec": [torch.empty((gr, gk), dtype=g0.dtype, device=dev) for _ in range(gn)],
+            "gpk": [torch.empty((gr, gk // 2), dtype=torch.uint8, device=dev) for _ in range(gn)],
+            "gps": [torch.zeros((gr, gk // 32), dtype=torch.uint8, device=dev) for _ in range(gn)],
         }
         mxq.mxq_mxfp4_to_mxfp8_row(s["x"], s["data"], s["scale"])
         mxq.mxq_export_mxfp8(s["data"], s["scale"], K, s["scale_c"])
@@ -300,26 +302,29 @@ def main():
                                                                      s["cscale"])
     launches["dec_col"] = lambda s: mxq.mxq_dequantize(s["cdata"], s["cscale"], layout=mxq.MXQ_SCALE_COL_32X1,
                                                        out=s["dec_c"])
-    # outside the step: the row lift, the projection, the fold and the row-layout decode of 48 weights of
-    # 1024 x 2048, each in one grouped call
+    # outside the step: the row lift, the projection, the fold, the row-layout decode and the packed MXFP4
+    # encode of 48 weights of 1024 x 2048, each in one grouped call
     # (prepared once per buffer set, as for weights re-converted every step)
     for s in sets:
         s["grouped"] = mxq.GroupedRowLift(s["gx"], s["gdata"], s["gscale"])
         s["grouped_proj"] = mxq.GroupedProjection(s["gx"], s["gy"])
         s["grouped_fold"] = mxq.GroupedBlock128(s["gx"], s["gbdata"], s["gtc"])
         s["grouped_dec"] = mxq.GroupedDequantize(s["gdata"], s["gscale"], outs=s["gdec"])
+        s["grouped_q4"] = mxq.GroupedQuantizeMxfp4(s["gx"], s["gpk"], s["gps"])
         s["grouped"]()                                    # the payloads and codes the decode reads
     launches["row_grouped"] = lambda s: s["grouped"]()
     launches["proj_grouped"] = lambda s: s["grouped_proj"]()
     launches["block128_grouped"] = lambda s: s["grouped_fold"]()
     launches["dec_row_grouped"] = lambda s: s["grouped_dec"]()
+    launches["quantize_mxfp4_grouped"] = lambda s: s["grouped_q4"]()
     extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128", "col",
-                   "row_col", "dec_col", "row_grouped", "proj_grouped", "block128_grouped", "dec_row_grouped"]
+                   "row_col", "dec_col", "row_grouped", "proj_grouped", "block128_grouped", "dec_row_grouped",
+                   "quantize_mxfp4_grouped"]
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
     offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1,
               "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0, "col": 2,
               "row_col": 4, "dec_col": 1, "row_grouped": 0, "proj_grouped": 2, "block128_grouped": 4,
-              "dec_row_grouped": 1}
+              "dec_row_grouped": 1, "quantize_mxfp4_grouped": 3}
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -404,7 +409,8 @@ def main():
                        row_grouped=gn * algorithmic_bytes(gr, gk, es)["row"],
                        proj_grouped=gn * algorithmic_bytes(gr, gk, es)["proj"],
                        block128_grouped=gn * algorithmic_bytes(gr, gk, es)["block128"],
-                       dec_row_grouped=gn * algorithmic_bytes(gr, gk, es)["dec_row"])
+                       dec_row_grouped=gn * algorithmic_bytes(gr, gk, es)["dec_row"],
+                       quantize_mxfp4_grouped=gn * packed_bytes(gr, gk, es)["quantize_mxfp4"])
     for n in extra_names:
         us, med, lo = burst_stats(n)
         gbs = extra_bytes[n] / (us * 1e-6) / 1e9

@@ -17,7 +17,8 @@
  *                                             of weights in few launches
  * the packed MXFP4 deployment format:
  *   mxq_quantize_mxfp4, mxq_dequantize_mxfp4,
- *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128
+ *   mxq_mxfp4_packed_to_mxfp8_row, mxq_mxfp4_packed_to_fp8_block128,
+ *   mxq_quantize_mxfp4_grouped (the encode of a list of weights in few launches)
  * and MXFP8 columnwise (32x1) from the decomposition:
  *   mxq_mxfp4_to_mxfp8_col, mxq_mxfp4_to_mxfp8_row_col (row and column in one pass),
  *   and their no-op-flag-gated forms mxq_mxfp4_to_mxfp8_col_guarded,
@@ -401,6 +402,36 @@ int mxq_dequantize_grouped(const mxq_dequant_group* groups, int64_t n_groups, mx
  */
 int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* packed,
                        uint8_t* scale, int64_t scale_ld, hipStream_t stream);
+
+/*
+ * One weight of a grouped packed MXFP4 encode: the arguments of
+ * mxq_quantize_mxfp4 for that weight (x, packed and scale are device pointers).
+ */
+typedef struct {
+  const void* x;      /* [rows, K], row stride ld_x >= K */
+  int64_t ld_x;
+  int64_t rows;
+  int64_t K;
+  uint8_t* packed;    /* [rows, ceil(K/2)] nibble pairs, contiguous */
+  uint8_t* scale;     /* [rows, scale_ld] E8M0 codes, scale_ld >= ceil(K/32); padding not written */
+  int64_t scale_ld;
+} mxq_mxfp4_group;
+
+/*
+ * The packed MXFP4 encode of mxq_quantize_mxfp4 (the deployment format, [QAT]
+ * Description and Known limitations) applied to a list of weights of one
+ * dtype (the experts of a grouped linear layer), in as few launches as
+ * possible.  Results are bit-identical to one mxq_quantize_mxfp4 call per
+ * weight.
+ *   groups    HOST array of n_groups descriptors, read during the call only
+ *   n_groups  >= 0; groups with rows == 0 or K == 0 are skipped
+ *   Every group is checked as mxq_quantize_mxfp4 checks its arguments (the
+ *   first failing group's status is returned and nothing is enqueued).  In
+ *   addition no group's packed or scale may overlap any group's x, packed or
+ *   scale (MXQ_ERR_ALIAS); inputs may overlap each other.
+ */
+int mxq_quantize_mxfp4_grouped(const mxq_mxfp4_group* groups, int64_t n_groups, mxq_dtype dt,
+                               hipStream_t stream);
 
 /* Decode packed MXFP4: out = RNE_out(E2M1 * 2^(code-127)); code 255 -> canonical
  * NaN; values beyond the output range (codes 253, 254) -> Inf.  out [rows, K]

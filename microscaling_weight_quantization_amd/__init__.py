@@ -38,7 +38,7 @@ ENTRY_POINTS = ("mxq_status_string", "mxq_fake_quantize_mxfp4", "mxq_mxfp4_to_mx
                 "mxq_mxfp4_packed_to_mxfp8_row", "mxq_mxfp4_packed_to_fp8_block128", "mxq_mxfp4_to_mxfp8_col",
                 "mxq_mxfp4_to_mxfp8_row_col", "mxq_mxfp4_to_mxfp8_col_guarded", "mxq_mxfp4_to_mxfp8_row_col_guarded",
                 "mxq_mxfp4_to_mxfp8_row_grouped", "mxq_fake_quantize_mxfp4_grouped",
-                "mxq_mxfp4_to_fp8_block128_grouped", "mxq_dequantize_grouped")
+                "mxq_mxfp4_to_fp8_block128_grouped", "mxq_dequantize_grouped", "mxq_quantize_mxfp4_grouped")
 
 _libs = {}
 _lock = threading.Lock()
@@ -66,6 +66,12 @@ class _DequantGroup(ctypes.Structure):
     """mxq_dequant_group of include/mxq.h."""
     _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_ld", ctypes.c_int64),
                 ("rows", ctypes.c_int64), ("K", ctypes.c_int64), ("out", ctypes.c_void_p), ("ld_out", ctypes.c_int64)]
+
+
+class _Mxfp4Group(ctypes.Structure):
+    """mxq_mxfp4_group of include/mxq.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("ld_x", ctypes.c_int64), ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_ld", ctypes.c_int64)]
 
 
 class MxqError(RuntimeError):
@@ -107,6 +113,7 @@ def load(name: str = "libmxq.so") -> ctypes.CDLL:
         L.mxq_fake_quantize_mxfp4_grouped.argtypes = [ctypes.POINTER(_ProjGroup), i64, i32, vp]
         L.mxq_mxfp4_to_fp8_block128_grouped.argtypes = [ctypes.POINTER(_Block128Group), i64, i32, vp]
         L.mxq_dequantize_grouped.argtypes = [ctypes.POINTER(_DequantGroup), i64, i32, i32, i32, vp]
+        L.mxq_quantize_mxfp4_grouped.argtypes = [ctypes.POINTER(_Mxfp4Group), i64, i32, vp]
         for n in ENTRY_POINTS[1:]:
             getattr(L, n).restype = i32
         _libs[name] = L
@@ -403,6 +410,64 @@ class GroupedDequantize:
             _check(self._L, self._L.mxq_dequantize_grouped(self._table, self.n, self._fmt, self._layout, self._dt,
                                                             _stream(self.datas[0])))
         return self.outs
+
+
+class GroupedQuantizeMxfp4:
+    """The grouped packed MXFP4 encode prepared once for a fixed list of
+    weights and outputs; each call enqueues it on torch's current stream with
+    one call into the library.  The object keeps the tensors alive; `packeds` /
+    `scales` are the outputs."""
+
+    def __init__(self, xs, packeds=None, scales=None, scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+        self._L = load(lib)
+        xs = list(xs)
+        n = len(xs)
+        packeds = [None] * n if packeds is None else list(packeds)
+        scales = [None] * n if scales is None else list(scales)
+        if len(packeds) != n or len(scales) != n:
+            raise ValueError("packeds and scales must have one entry per weight")
+        self.xs, self.n = xs, n
+        if n == 0:
+            self.packeds, self.scales = [], []
+            return
+        dev, dtype = xs[0].device, xs[0].dtype
+        for t in xs + packeds + scales:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+                raise ValueError("mxq_quantize_mxfp4_grouped: operands must be device tensors on one device")
+        if any(x.dtype != dtype for x in xs):
+            raise ValueError("all weights of a group call must have one dtype")
+        self._dt = _dtype_code(xs[0])
+        self._table = (_Mxfp4Group * n)()
+        for i, x in enumerate(xs):
+            px, rows, K, ldx = _matrix(x)
+            nb, pw = (K + 31) // 32, (K + 1) // 2
+            if packeds[i] is None:
+                packeds[i] = torch.empty((rows, pw), dtype=torch.uint8, device=dev)
+            if scales[i] is None:
+                scales[i] = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=dev)
+            pp, _, _, ldp = _matrix(packeds[i])
+            ps, _, _, ld_s = _matrix(scales[i])
+            if rows * K and (ldp != pw or packeds[i].numel() != rows * pw):
+                raise ValueError("packed must be a contiguous [rows, ceil(K/2)] uint8 tensor")
+            self._table[i] = _Mxfp4Group(px, ldx, rows, K, pp, ps, ld_s)
+        self.packeds, self.scales = packeds, scales
+
+    def __call__(self):
+        if self.n:
+            _check(self._L, self._L.mxq_quantize_mxfp4_grouped(self._table, self.n, self._dt, _stream(self.xs[0])))
+        return self.packeds, self.scales
+
+
+@_device_operands
+def mxq_quantize_mxfp4_grouped(xs, packeds=None, scales=None, scale_ld: Optional[int] = None,
+                               lib: str = "libmxq.so"):
+    """Packed MXFP4 (deployment format) of a list of weights of one dtype, in as
+    few launches as possible -> (list of nibble pairs, list of E8M0 codes); the
+    same bytes as one mxq_quantize_mxfp4 per weight.  GroupedQuantizeMxfp4
+    prepares the call once for repeated use."""
+    return GroupedQuantizeMxfp4(xs, packeds, scales, scale_ld, lib)()
 
 
 @_device_operands

@@ -1078,21 +1078,22 @@ struct Nibbles<uint16_t> { typedef uint32_t type; };   // 8 nibbles per bf16 chu
 template <>
 struct Nibbles<uint32_t> { typedef uint16_t type; };   // 4 nibbles per fp32 chunk
 
+// The packed encode's body: workgroup wg's kRowSteps steps of one weight.  The
+// single and grouped kernels both run it.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
-                                                                  uint8_t* __restrict__ packed,
-                                                                  uint8_t* __restrict__ scale, int64_t scale_ld,
-                                                                  MxqDivisor steps_per_row, uint32_t total_steps) {
+__device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, int64_t ld_x, int64_t K,
+                                                     uint8_t* __restrict__ packed, uint8_t* __restrict__ scale,
+                                                     int64_t scale_ld, MxqDivisor steps_per_row, uint32_t total_steps,
+                                                     uint32_t wg) {
   using G = StepGeom<T, kRowThreads>;
   using N = typename Nibbles<T>::type;
-  keep_denormals();
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   const int64_t pw = (K + 1) / 2;
   u32x4 w[kRowSteps];
 #pragma unroll
   for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = blockIdx.x * kRowSteps + u;
+    const uint32_t step = wg * kRowSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
     if (step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
@@ -1101,7 +1102,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __
   }
 #pragma unroll
   for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = blockIdx.x * kRowSteps + u;
+    const uint32_t step = wg * kRowSteps + u;
     if (step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
@@ -1120,6 +1121,26 @@ __global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __
       }
     }
   }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+                                                                  uint8_t* __restrict__ packed,
+                                                                  uint8_t* __restrict__ scale, int64_t scale_ld,
+                                                                  MxqDivisor steps_per_row, uint32_t total_steps) {
+  keep_denormals();
+  quantize_mxfp4_steps<T, VEC>(x, ld_x, K, packed, scale, scale_ld, steps_per_row, total_steps, blockIdx.x);
+}
+
+// Grouped packed encode, on the grouped row lift's pattern and with its
+// descriptor (data = the packed nibble pairs).  Aligned (VEC) weights only.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_grouped_kernel(const RowGroupTable tab) {
+  const RowGroupDesc d = tab.g[blockIdx.y];
+  if (blockIdx.x * kRowSteps >= d.total_steps) return;       // uniform: past this weight's steps
+  keep_denormals();
+  quantize_mxfp4_steps<T, true>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld,
+                                d.steps_per_row, d.total_steps, blockIdx.x);
 }
 
 // Eight packed nibbles at E8M0 code c -> four bf16 pairs of p * 2^(c-127), with
@@ -1875,6 +1896,44 @@ int launch_dequant_grouped(const mxq_dequant_group* gs, int64_t n, mxq_fp8 fmt, 
                          : launch_dequant_grouped_f<TO, false>(gs, n, lay, s);
 }
 
+// Grouped packed encode: the grouped row lift's batching, for the encode.
+template <typename T>
+int launch_quantize_mxfp4_grouped(const mxq_mxfp4_group* gs, int64_t n, hipStream_t s) {
+  constexpr int EPL = Fmt<T>::kEPL;
+  RowGroupTable tab{};
+  int64_t count = 0, max_w = 0, sum_w = 0;
+  auto flush = [&]() -> int {
+    if (count == 0) return MXQ_OK;
+    hipLaunchKernelGGL((quantize_mxfp4_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count),
+                       dim3(kRowThreads), 0, s, tab);
+    count = max_w = sum_w = 0;
+    return launch_status();
+  };
+  for (int64_t i = 0; i < n; i++) {
+    const mxq_mxfp4_group& g = gs[i];
+    if (g.rows == 0 || g.K == 0) continue;
+    if (!(aligned(g.x, 16) && g.ld_x % EPL == 0 && g.K % EPL == 0 && aligned(g.packed, EPL / 2))) {
+      const int st = launch_quantize_mxfp4<T>(g.x, g.ld_x, g.rows, g.K, g.packed, g.scale, g.scale_ld, s);
+      if (st != MXQ_OK) return st;
+      continue;
+    }
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t gw = grid_for(total, kRowSteps);
+    const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
+    if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
+      const int st = flush();
+      if (st != MXQ_OK) return st;
+    }
+    tab.g[count] = RowGroupDesc{g.x, g.ld_x, g.K, g.packed, g.scale, g.scale_ld, spr, total};
+    count++;
+    max_w = std::max(max_w, gw);
+    sum_w += gw;
+  }
+  return flush();
+}
+
 // The ranges of a grouped call, each marked as an output or not: true when no
 // output overlaps any other range.  A sweep in order of start address: a range
 // overlaps an earlier one exactly when it starts before the largest end seen
@@ -2289,20 +2348,65 @@ int mxq_dequantize_grouped(const mxq_dequant_group* groups, int64_t n_groups, mx
                             : launch_dequant_grouped<uint32_t>(groups, n_groups, fmt, layout, stream);
 }
 
-int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* packed,
-                       uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
+// Argument checks of the packed encode.  For a non-empty matrix it returns
+// MXQ_OK with r = {x, packed, scale}; for an empty one MXQ_OK with *empty set.
+static int quantize_mxfp4_check(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt,
+                                const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, Range* r, bool* empty) {
+  *empty = false;
   if (check_dtype(dt)) return MXQ_ERR_DTYPE;
   if (rows < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (rows == 0 || K == 0) return MXQ_OK;
+  if (rows == 0 || K == 0) {
+    *empty = true;
+    return MXQ_OK;
+  }
   if (!x || !packed || !scale) return MXQ_ERR_NULL;
   const int64_t nb = (K + 31) / 32, pw = (K + 1) / 2;
   if (ld_x < K || scale_ld < nb) return MXQ_ERR_SHAPE;
-  const Range rx = matrix_range(x, rows, K, ld_x, dtype_size(dt)), rp = matrix_range(packed, rows, pw, pw, 1),
-              rs = matrix_range(scale, rows, nb, scale_ld, 1);
-  if (!spans_ok({rx, rp, rs})) return MXQ_ERR_SHAPE;
-  if (overlap(rx, rp) || overlap(rx, rs) || overlap(rp, rs)) return MXQ_ERR_ALIAS;
+  r[0] = matrix_range(x, rows, K, ld_x, dtype_size(dt));
+  r[1] = matrix_range(packed, rows, pw, pw, 1);
+  r[2] = matrix_range(scale, rows, nb, scale_ld, 1);
+  if (!spans_ok({r[0], r[1], r[2]})) return MXQ_ERR_SHAPE;
+  if (overlap(r[0], r[1]) || overlap(r[0], r[2]) || overlap(r[1], r[2])) return MXQ_ERR_ALIAS;
+  return MXQ_OK;
+}
+
+int mxq_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, mxq_dtype dt, uint8_t* packed,
+                       uint8_t* scale, int64_t scale_ld, hipStream_t stream) {
+  Range r[3];
+  bool empty;
+  const int st = quantize_mxfp4_check(x, ld_x, rows, K, dt, packed, scale, scale_ld, r, &empty);
+  if (st != MXQ_OK || empty) return st;
   return dt == MXQ_BF16 ? launch_quantize_mxfp4<uint16_t>(x, ld_x, rows, K, packed, scale, scale_ld, stream)
                         : launch_quantize_mxfp4<uint32_t>(x, ld_x, rows, K, packed, scale, scale_ld, stream);
+}
+
+int mxq_quantize_mxfp4_grouped(const mxq_mxfp4_group* groups, int64_t n_groups, mxq_dtype dt, hipStream_t stream) {
+  if (check_dtype(dt)) return MXQ_ERR_DTYPE;
+  if (n_groups < 0) return MXQ_ERR_SHAPE;
+  if (n_groups == 0) return MXQ_OK;
+  if (!groups) return MXQ_ERR_NULL;
+  const int64_t eps = dt == MXQ_BF16 ? StepGeom<uint16_t, kRowThreads>::kElemsPerStep
+                                     : StepGeom<uint32_t, kRowThreads>::kElemsPerStep;
+  // every group on its own, then no output may overlap any other range
+  std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
+  iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 3);
+  for (int64_t i = 0; i < n_groups; i++) {
+    const mxq_mxfp4_group& g = groups[i];
+    Range r[3];
+    bool empty;
+    const int st = quantize_mxfp4_check(g.x, g.ld_x, g.rows, g.K, dt, g.packed, g.scale, g.scale_ld, r, &empty);
+    if (st != MXQ_OK) return st;
+    if (empty) continue;
+    MxqDivisor spr;
+    uint32_t total;
+    if (steps_for(g.rows, g.K, eps, &spr, &total)) return MXQ_ERR_SHAPE;
+    iv.push_back({r[0], false});
+    iv.push_back({r[1], true});
+    iv.push_back({r[2], true});
+  }
+  if (!grouped_ranges_disjoint(iv)) return MXQ_ERR_ALIAS;
+  return dt == MXQ_BF16 ? launch_quantize_mxfp4_grouped<uint16_t>(groups, n_groups, stream)
+                        : launch_quantize_mxfp4_grouped<uint32_t>(groups, n_groups, stream);
 }
 
 int mxq_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t scale_ld, int64_t rows, int64_t K,

@@ -311,3 +311,31 @@ def test_grouped_decode_host_validation(lib):
     assert call(a, grp(0x110000, 0x210000, 0x300010)) == mxq.MXQ_ERR_ALIAS  # outputs overlap
     assert call(grp(0x100000, 0x200000, 0x100100)) == mxq.MXQ_ERR_ALIAS     # a single payload's own overlap
     assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK
+
+
+def test_grouped_mxfp4_encode_host_validation(lib):
+    """The grouped packed encode checks every weight as the single call does
+    and refuses outputs over other weights' ranges, before anything is
+    enqueued."""
+    G = mxq._Mxfp4Group
+
+    def grp(x, packed, scale, rows=4, K=256, ld=256, sld=8):
+        return G(x, ld, rows, K, packed, scale, sld)
+
+    def call(*groups, dt=mxq.MXQ_BF16, n=None):
+        arr = (G * max(len(groups), 1))(*groups)
+        return lib.mxq_quantize_mxfp4_grouped(arr, len(groups) if n is None else n, dt, None)
+
+    a = grp(0x100000, 0x200000, 0x300000)          # 4 x 256 bf16: 2 KiB; packed 512 B; 4 x 8 codes
+    b = grp(0x110000, 0x210000, 0x310000)
+    assert call(a, b, n=-1) == mxq.MXQ_ERR_SHAPE
+    assert lib.mxq_quantize_mxfp4_grouped(None, 1, mxq.MXQ_BF16, None) == mxq.MXQ_ERR_NULL
+    assert call(a, b, dt=mxq.MXQ_FP16) == mxq.MXQ_ERR_DTYPE
+    assert call(a, grp(0x110000, None, 0x310000)) == mxq.MXQ_ERR_NULL
+    assert call(a, grp(0x110000, 0x210000, 0x310000, sld=7)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, grp(0x110000, 0x210000, 0x310000, ld=255)) == mxq.MXQ_ERR_SHAPE
+    assert call(a, grp(0x110000, 0x1001F0, 0x310000)) == mxq.MXQ_ERR_ALIAS      # b's nibbles in a's weight
+    assert call(a, grp(0x110000, 0x210000, 0x2001F0)) == mxq.MXQ_ERR_ALIAS      # b's codes in a's nibbles
+    assert call(a, grp(0x110000, 0x210000, 0x300010)) == mxq.MXQ_ERR_ALIAS      # code arrays overlap
+    assert call(grp(0x100000, 0x100100, 0x300000)) == mxq.MXQ_ERR_ALIAS         # a single weight's own overlap
+    assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK

@@ -277,3 +277,50 @@ def test_prepared_grouped_decode_and_overlaps(dev):
                                    layout=mxq.MXQ_SCALE_TILE_128X128,
                                    outs=[o, buf.view(torch.bfloat16).view(256, 384)])
     assert e.value.status == mxq.MXQ_ERR_ALIAS
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_grouped_mxfp4_encode_mixed_shapes(dev, dtype):
+    """The packed MXFP4 encode of mixed shapes (odd K included) with padded
+    scale storage, one misaligned weight (the per-weight path), one empty, and
+    more weights than one table holds; each against the oracle."""
+    shapes = [(128, 128), (300, 520), (1, 33), (256, 4096), (0, 64), (129, 129), (64, 2048), (7, 31)]
+    shapes += [(int(r), int(k)) for r, k in zip(np.random.default_rng(31).integers(1, 300, 44),
+                                                np.random.default_rng(32).choice([32, 64, 200, 512, 641], 44))]
+    weights = [_weight(r, k, dtype, 700 + i) for i, (r, k) in enumerate(shapes)]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xs = [to_dev(b, dev) if b.size else torch.empty(b.shape, dtype=tdt, device=dev) for b in weights]
+    base = to_dev(np.concatenate([np.zeros((weights[3].shape[0], 1), weights[3].dtype), weights[3]], axis=1), dev)
+    xs[3] = base[:, 1:]                                         # misaligned view
+    pads = [i % 3 for i in range(len(shapes))]
+    scales = [torch.full((r, (k + 31) // 32 + p), 0xA5, dtype=torch.uint8, device=dev)
+              for (r, k), p in zip(shapes, pads)]
+    packeds, scales = mxq.mxq_quantize_mxfp4_grouped(xs, scales=scales)
+    for i, (bits, pk, sc, p) in enumerate(zip(weights, packeds, scales, pads)):
+        if bits.size:
+            wp, ws = oracle.quantize_mxfp4(bits, scale_ld=(bits.shape[1] + 31) // 32 + p, threads=THREADS,
+                                           fill=0xA5)
+            assert_bits(to_host(pk), wp, f"weight {i} {bits.shape} nibbles")
+            assert_bits(to_host(sc), ws, f"weight {i} {bits.shape} codes")
+
+
+def test_prepared_grouped_mxfp4_encode_and_overlaps(dev):
+    a_bits = [_weight(256, 384, "bf16", 800 + i) for i in range(3)]
+    b_bits = [_weight(256, 384, "bf16", 810 + i) for i in range(3)]
+    xs = [to_dev(b, dev) for b in a_bits]
+    call = mxq.GroupedQuantizeMxfp4(xs)
+    for bits in (a_bits, b_bits):
+        for x, b in zip(xs, bits):
+            x.copy_(to_dev(b, dev))
+        packeds, scales = call()
+        for i, b in enumerate(bits):
+            wp, ws = oracle.quantize_mxfp4(b, threads=THREADS)
+            assert_bits(to_host(packeds[i]), wp, f"weight {i} nibbles")
+            assert_bits(to_host(scales[i]), ws, f"weight {i} codes")
+    p = torch.empty((256, 192), dtype=torch.uint8, device=dev)
+    with pytest.raises(mxq.MxqError) as e:                      # two weights into one packed output
+        mxq.mxq_quantize_mxfp4_grouped(xs[:2], packeds=[p, p])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
+    with pytest.raises(mxq.MxqError) as e:                      # weight 1's codes inside weight 0
+        mxq.mxq_quantize_mxfp4_grouped(xs[:2], scales=[None, xs[0].view(torch.uint8)[:, :12]])
+    assert e.value.status == mxq.MXQ_ERR_ALIAS
