@@ -5,8 +5,8 @@
  * decodes -- on a stream of its own, checks every status, and writes the outputs
  * to a file for the test (tests/test_gpu_c_caller.py) to compare with the oracle.
  * It also checks that argument errors come back as status codes before any
- * launch, and that the grouped row lift of two weights gives the single
- * call's bytes.
+ * launch, and that the grouped row lift, decode and packed encode of two
+ * weights give the single calls' bytes.
  *
  * usage: c_caller ROWS K SCALE_LD IN.bin OUT.bin
  *   IN.bin   ROWS*K bf16 bit patterns (uint16, little endian)
@@ -122,6 +122,52 @@ int main(int argc, char** argv) {
         fprintf(stderr, "c_caller: grouped codes differ from the single call (weight %d)\n", i);
         return 5;
       }
+    }
+    /* grouped decode of the two row lifts, and grouped packed encode of the two weights */
+    void *gdec[2], *sdec;
+    uint8_t *gpk[2], *gps[2], *spk, *sps;
+    const int64_t pw = (K + 1) / 2;
+    HIP_OK(hipMalloc(&sdec, (size_t)n * 2));
+    HIP_OK(hipMalloc((void**)&spk, (size_t)(rows * pw)));
+    HIP_OK(hipMalloc((void**)&sps, (size_t)(rows * nb)));
+    for (int i = 0; i < 2; i++) {
+      HIP_OK(hipMalloc(&gdec[i], (size_t)n * 2));
+      HIP_OK(hipMalloc((void**)&gpk[i], (size_t)(rows * pw)));
+      HIP_OK(hipMalloc((void**)&gps[i], (size_t)(rows * nb)));
+    }
+    const mxq_dequant_group dg[2] = {{gdata[0], gscale[0], sld, rows, K, gdec[0], K},
+                                     {gdata[1], gscale[1], sld, half, K, gdec[1], K}};
+    const mxq_mxfp4_group qg[2] = {{x, K, rows, K, gpk[0], gps[0], nb}, {x, K, half, K, gpk[1], gps[1], nb}};
+    MXQ_OK_OR_DIE(mxq_dequantize(data, scale, sld, rows, K, MXQ_E4M3, MXQ_SCALE_ROW_1X32, sdec, K, MXQ_BF16, s));
+    MXQ_OK_OR_DIE(mxq_dequantize_grouped(dg, 2, MXQ_E4M3, MXQ_SCALE_ROW_1X32, MXQ_BF16, s));
+    MXQ_OK_OR_DIE(mxq_quantize_mxfp4(x, K, rows, K, MXQ_BF16, spk, sps, nb, s));
+    MXQ_OK_OR_DIE(mxq_quantize_mxfp4_grouped(qg, 2, MXQ_BF16, s));
+    HIP_OK(hipStreamSynchronize(s));
+    uint8_t* c = (uint8_t*)malloc((size_t)n * 2);
+    uint8_t* d = (uint8_t*)malloc((size_t)n * 2);
+    for (int i = 0; i < 2; i++) {
+      const int64_t r = i ? half : rows;
+      const void* pairs[3][2] = {{sdec, gdec[i]}, {spk, gpk[i]}, {sps, gps[i]}};
+      const size_t len[3] = {(size_t)(r * K * 2), (size_t)(r * pw), (size_t)(r * nb)};
+      for (int j = 0; j < 3; j++) {
+        HIP_OK(hipMemcpy(c, pairs[j][0], len[j], hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(d, pairs[j][1], len[j], hipMemcpyDeviceToHost));
+        if (memcmp(c, d, len[j]) != 0) {
+          fprintf(stderr, "c_caller: grouped %s differs from the single call (weight %d)\n",
+                  j == 0 ? "decode" : "packed encode", i);
+          return 5;
+        }
+      }
+    }
+    free(c);
+    free(d);
+    HIP_OK(hipFree(sdec));
+    HIP_OK(hipFree(spk));
+    HIP_OK(hipFree(sps));
+    for (int i = 0; i < 2; i++) {
+      HIP_OK(hipFree(gdec[i]));
+      HIP_OK(hipFree(gpk[i]));
+      HIP_OK(hipFree(gps[i]));
     }
     free(a);
     free(b);
