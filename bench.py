@@ -130,15 +130,29 @@ def _oracle_pass(bits, threads: int) -> dict:
     return {"proj": y, "row": d, "export": c, "block128": bd, "tile_codes": tc, "dec_row": dr, "dec_tile": dt}
 
 
-def cpu_model() -> str:
+def host_cpu() -> dict:
+    """The host's CPU as /proc/cpuinfo and the scheduler report it: the model
+    string, logical CPUs, physical cores (distinct (package, core) pairs) and
+    the CPUs this process may run on (its affinity set)."""
+    model, cores, cur = "unknown", set(), {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model == "unknown":
+                    model = v
+                elif k in ("physical id", "core id"):
+                    cur[k] = v
+                elif not k and cur:
+                    cores.add((cur.get("physical id"), cur.get("core id")))
+                    cur = {}
+        if cur:
+            cores.add((cur.get("physical id"), cur.get("core id")))
     except OSError:
         pass
-    return "unknown"
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return {"model": model, "logical": os.cpu_count(), "physical": len(cores) or None, "usable": usable}
 
 
 def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int = 8):
@@ -156,7 +170,7 @@ def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int 
     wname = "fp32" if es == 4 else "bf16"
     total = passes * sum(algorithmic_bytes(*bits.shape, es).values())
     out = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-           "cpu_model": cpu_model(),
+           "host_cpu": host_cpu(),
            "sample": f"the whole {bits.shape[0]}x{bits.shape[1]} {wname} weight, {passes} pass{'es' if passes > 1 else ''} of all six steps "
                      f"({dt:.1f} s wall, {cpu:.1f} s CPU on {threads} threads)"}
     # the same steps on one thread, over the first 2048 rows
@@ -437,9 +451,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # the path is integer work on the weight's bit patterns (amax, exponent
-        # fields), with the E2M1 / E4M3 encodes done by the hardware conversions
-        "dtype": "u32" if fp32 else "u16",
+        # the weight's own type; every step is integer work on its bit patterns
+        # (amax, exponent fields) plus the hardware E2M1 / E4M3 conversions
+        "dtype": "fp32" if fp32 else "bf16",
         "data": "synthetic",
         "config": {"workload": (f"{rows}x{K} fp32 master weight (the bf16 weight before its cast)"
                                 if fp32 else f"{rows}x{K} bf16 weight") +
@@ -456,7 +470,8 @@ def main():
                            "frac": round(2 * es * rows * K / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu:
-        out["cpu_baseline"], want = cpu_baseline(bits, threads=min(16, os.cpu_count() or 1))
+        # every CPU this process may run on (its affinity set), one oracle thread each
+        out["cpu_baseline"], want = cpu_baseline(bits, threads=host_cpu()["usable"])
         # the same oracle run gives the bytes for a full-size parity check of the step
         out["parity"] = parity(sets[0], want)
     print(json.dumps(out), flush=True)

@@ -171,6 +171,25 @@ def _matrix(t: torch.Tensor):
     return t.data_ptr(), rows, K, ld
 
 
+def _operand(t: torch.Tensor, rows: int, cols: int, what: str, contiguous: bool = False, byte: bool = False):
+    """(pointer, row stride) of an operand the call reads or writes as a
+    [rows, cols] matrix.  Raises ValueError, before anything is launched, when
+    the tensor is smaller than that region (the C entry points only see a
+    pointer and a stride, so a short buffer would be accessed out of bounds),
+    when `contiguous` is set and its rows are not packed (payloads have row
+    stride cols), or when `byte` is set and its elements are not bytes."""
+    if byte and t.element_size() != 1:
+        raise ValueError(f"{what} holds bytes (uint8), got {t.dtype}")
+    p, trows, tcols, ld = _matrix(t)
+    if rows * cols == 0:
+        return p, max(ld, cols)
+    if trows < rows or tcols < cols:
+        raise ValueError(f"{what} must cover [{rows}, {cols}], got [{trows}, {tcols}]")
+    if contiguous and ld != cols:
+        raise ValueError(f"{what} must be a contiguous [{rows}, {cols}] tensor (row stride {cols}), got row stride {ld}")
+    return p, ld
+
+
 def _flag(t: torch.Tensor) -> int:
     if t.dtype != torch.int32 or not t.is_cuda or t.numel() < 1:
         raise ValueError("the no-op flag is a device int32 tensor")
@@ -183,6 +202,22 @@ def _stream(t: torch.Tensor):
 
 # ---- the C entry points, one to one ---------------------------------------------------
 
+def _nb(K: int) -> int:
+    return (K + 31) // 32
+
+
+def _scale_for(x: torch.Tensor, rows: int, cols: int, ld: Optional[int]) -> torch.Tensor:
+    """A zeroed code array [rows, ld or cols] on x's device (padding stays 0)."""
+    return torch.zeros((rows, ld or cols), dtype=torch.uint8, device=x.device)
+
+
+def _payload_for(x: torch.Tensor, rows: int, K: int, data: Optional[torch.Tensor], what: str = "payload"):
+    if data is None:
+        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    pd, _ = _operand(data, rows, K, what, contiguous=True, byte=True)
+    return data, pd
+
+
 @_device_operands
 def mxq_fake_quantize_mxfp4(x: torch.Tensor, y: Optional[torch.Tensor] = None, lib: str = "libmxq.so") -> torch.Tensor:
     """MXFP4 projection of x (bf16 / fp32) into y (same dtype; y may be x)."""
@@ -193,7 +228,7 @@ def mxq_fake_quantize_mxfp4(x: torch.Tensor, y: Optional[torch.Tensor] = None, l
     if y.dtype != x.dtype or y.shape != x.shape:
         raise ValueError("y must have x's dtype and shape")
     px, rows, K, ldx = _matrix(x)
-    py, _, _, ldy = _matrix(y)
+    py, ldy = _operand(y, rows, K, "y")
     _check(L, L.mxq_fake_quantize_mxfp4(px, ldx, py, ldy, rows, K, dt, _stream(x)))
     return y
 
@@ -207,308 +242,14 @@ def mxq_mxfp4_to_mxfp8_row(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
-    nb = (K + 31) // 32
-    if scale is None:
-        scale = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=x.device)
-    if data is None:
-        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
-    pd, _, _, ldd = _matrix(data)
-    ps, _, sld, ld_s = _matrix(scale)
-    if rows * K and (ldd != K or data.numel() != rows * K):
-        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    scale = _scale_for(x, rows, _nb(K), scale_ld) if scale is None else scale
+    data, pd = _payload_for(x, rows, K, data)
+    ps, ld_s = _operand(scale, rows, _nb(K), "scale", byte=True)
     if noop is None:
         _check(L, L.mxq_mxfp4_to_mxfp8_row(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
     else:
         _check(L, L.mxq_mxfp4_to_mxfp8_row_guarded(px, ldx, rows, K, dt, pd, ps, ld_s, _flag(noop), _stream(x)))
     return data, scale
-
-
-class GroupedRowLift:
-    """The grouped row lift prepared once for a fixed list of weights and
-    outputs: the descriptor table is built here, and each call enqueues the
-    conversion on torch's current stream with one call into the library (for
-    weights that are re-converted every training step).  The object keeps the
-    tensors alive; `datas` / `scales` are the outputs."""
-
-    def __init__(self, xs, datas=None, scales=None, scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
-        self._L = load(lib)
-        xs = list(xs)
-        n = len(xs)
-        datas = [None] * n if datas is None else list(datas)
-        scales = [None] * n if scales is None else list(scales)
-        if len(datas) != n or len(scales) != n:
-            raise ValueError("datas and scales must have one entry per weight")
-        self.xs, self.n = xs, n
-        if n == 0:
-            self.datas, self.scales = [], []
-            return
-        dev, dtype = xs[0].device, xs[0].dtype
-        for t in xs + datas + scales:
-            if t is None:
-                continue
-            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
-                raise ValueError("mxq_mxfp4_to_mxfp8_row_grouped: operands must be device tensors on one device")
-        if any(x.dtype != dtype for x in xs):
-            raise ValueError("all weights of a group call must have one dtype")
-        self._dt = _dtype_code(xs[0])
-        self._table = (_RowGroup * n)()
-        for i, x in enumerate(xs):
-            px, rows, K, ldx = _matrix(x)
-            nb = (K + 31) // 32
-            if scales[i] is None:
-                scales[i] = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=dev)
-            if datas[i] is None:
-                datas[i] = torch.empty((rows, K), dtype=torch.uint8, device=dev)
-            pd, _, _, ldd = _matrix(datas[i])
-            ps, _, _, ld_s = _matrix(scales[i])
-            if rows * K and (ldd != K or datas[i].numel() != rows * K):
-                raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
-            self._table[i] = _RowGroup(px, ldx, rows, K, pd, ps, ld_s)
-        self.datas, self.scales = datas, scales
-
-    def __call__(self):
-        if self.n:
-            _check(self._L, self._L.mxq_mxfp4_to_mxfp8_row_grouped(self._table, self.n, self._dt,
-                                                                    _stream(self.xs[0])))
-        return self.datas, self.scales
-
-
-class GroupedProjection:
-    """The grouped MXFP4 projection prepared once for a fixed list of weights
-    and outputs (an output may be its weight itself, in place); each call
-    enqueues it on torch's current stream with one call into the library.  The
-    object keeps the tensors alive; `ys` are the outputs."""
-
-    def __init__(self, xs, ys=None, lib: str = "libmxq.so"):
-        self._L = load(lib)
-        xs = list(xs)
-        n = len(xs)
-        ys = [None] * n if ys is None else list(ys)
-        if len(ys) != n:
-            raise ValueError("ys must have one entry per weight")
-        self.xs, self.n = xs, n
-        if n == 0:
-            self.ys = []
-            return
-        dev, dtype = xs[0].device, xs[0].dtype
-        for t in xs + ys:
-            if t is None:
-                continue
-            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
-                raise ValueError("mxq_fake_quantize_mxfp4_grouped: operands must be device tensors on one device")
-        if any(x.dtype != dtype for x in xs):
-            raise ValueError("all weights of a group call must have one dtype")
-        self._dt = _dtype_code(xs[0])
-        self._table = (_ProjGroup * n)()
-        for i, x in enumerate(xs):
-            if ys[i] is None:
-                ys[i] = torch.empty_like(x, memory_format=torch.contiguous_format)
-            if ys[i].dtype != x.dtype or ys[i].shape != x.shape:
-                raise ValueError("each output must have its weight's dtype and shape")
-            px, rows, K, ldx = _matrix(x)
-            py, _, _, ldy = _matrix(ys[i])
-            self._table[i] = _ProjGroup(px, ldx, py, ldy, rows, K)
-        self.ys = ys
-
-    def __call__(self):
-        if self.n:
-            _check(self._L, self._L.mxq_fake_quantize_mxfp4_grouped(self._table, self.n, self._dt, _stream(self.xs[0])))
-        return self.ys
-
-
-class GroupedBlock128:
-    """The grouped 128x128 fold prepared once for a fixed list of weights and
-    outputs; each call enqueues it on torch's current stream with one call into
-    the library.  The object keeps the tensors alive; `datas` / `tile_codes`
-    are the outputs."""
-
-    def __init__(self, xs, datas=None, tile_codes=None, lib: str = "libmxq.so"):
-        self._L = load(lib)
-        xs = list(xs)
-        n = len(xs)
-        datas = [None] * n if datas is None else list(datas)
-        tile_codes = [None] * n if tile_codes is None else list(tile_codes)
-        if len(datas) != n or len(tile_codes) != n:
-            raise ValueError("datas and tile_codes must have one entry per weight")
-        self.xs, self.n = xs, n
-        if n == 0:
-            self.datas, self.tile_codes = [], []
-            return
-        dev, dtype = xs[0].device, xs[0].dtype
-        for t in xs + datas + tile_codes:
-            if t is None:
-                continue
-            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
-                raise ValueError("mxq_mxfp4_to_fp8_block128_grouped: operands must be device tensors on one device")
-        if any(x.dtype != dtype for x in xs):
-            raise ValueError("all weights of a group call must have one dtype")
-        self._dt = _dtype_code(xs[0])
-        self._table = (_Block128Group * n)()
-        for i, x in enumerate(xs):
-            px, rows, K, ldx = _matrix(x)
-            if datas[i] is None:
-                datas[i] = torch.empty((rows, K), dtype=torch.uint8, device=dev)
-            if tile_codes[i] is None:
-                tile_codes[i] = torch.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=dev)
-            pd, _, _, ldd = _matrix(datas[i])
-            pt, _, _, ldt = _matrix(tile_codes[i])
-            if rows * K and (ldd != K or datas[i].numel() != rows * K):
-                raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
-            self._table[i] = _Block128Group(px, ldx, rows, K, pd, pt, ldt)
-        self.datas, self.tile_codes = datas, tile_codes
-
-    def __call__(self):
-        if self.n:
-            _check(self._L, self._L.mxq_mxfp4_to_fp8_block128_grouped(self._table, self.n, self._dt,
-                                                                       _stream(self.xs[0])))
-        return self.datas, self.tile_codes
-
-
-class GroupedDequantize:
-    """The grouped decode prepared once for a fixed list of payloads, codes and
-    outputs of one payload format, scale layout and output dtype; each call
-    enqueues it on torch's current stream with one call into the library.  The
-    object keeps the tensors alive; `outs` are the outputs."""
-
-    def __init__(self, datas, scales, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3, outs=None,
-                 out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so"):
-        self._L = load(lib)
-        datas, scales = list(datas), list(scales)
-        n = len(datas)
-        outs = [None] * n if outs is None else list(outs)
-        if len(scales) != n or len(outs) != n:
-            raise ValueError("scales and outs must have one entry per payload")
-        self.datas, self.n = datas, n
-        self._fmt, self._layout = fmt, layout
-        if n == 0:
-            self.outs = []
-            return
-        dev = datas[0].device
-        for t in datas + scales + outs:
-            if t is None:
-                continue
-            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
-                raise ValueError("mxq_dequantize_grouped: operands must be device tensors on one device")
-        for i, d in enumerate(datas):
-            if outs[i] is None:
-                outs[i] = torch.empty(tuple(d.shape), dtype=out_dtype, device=dev)
-        if any(o.dtype != outs[0].dtype for o in outs):
-            raise ValueError("all outputs of a group call must have one dtype")
-        self._dt = _dtype_code(outs[0])
-        self._table = (_DequantGroup * n)()
-        for i in range(n):
-            pd, rows, K, ldd = _matrix(datas[i])
-            if rows * K and ldd != K:
-                raise ValueError("payload must be contiguous")
-            ps, _, _, lds = _matrix(scales[i])
-            po, _, _, ldo = _matrix(outs[i])
-            self._table[i] = _DequantGroup(pd, ps, lds, rows, K, po, ldo)
-        self.outs = outs
-
-    def __call__(self):
-        if self.n:
-            _check(self._L, self._L.mxq_dequantize_grouped(self._table, self.n, self._fmt, self._layout, self._dt,
-                                                            _stream(self.datas[0])))
-        return self.outs
-
-
-class GroupedQuantizeMxfp4:
-    """The grouped packed MXFP4 encode prepared once for a fixed list of
-    weights and outputs; each call enqueues it on torch's current stream with
-    one call into the library.  The object keeps the tensors alive; `packeds` /
-    `scales` are the outputs."""
-
-    def __init__(self, xs, packeds=None, scales=None, scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
-        self._L = load(lib)
-        xs = list(xs)
-        n = len(xs)
-        packeds = [None] * n if packeds is None else list(packeds)
-        scales = [None] * n if scales is None else list(scales)
-        if len(packeds) != n or len(scales) != n:
-            raise ValueError("packeds and scales must have one entry per weight")
-        self.xs, self.n = xs, n
-        if n == 0:
-            self.packeds, self.scales = [], []
-            return
-        dev, dtype = xs[0].device, xs[0].dtype
-        for t in xs + packeds + scales:
-            if t is None:
-                continue
-            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
-                raise ValueError("mxq_quantize_mxfp4_grouped: operands must be device tensors on one device")
-        if any(x.dtype != dtype for x in xs):
-            raise ValueError("all weights of a group call must have one dtype")
-        self._dt = _dtype_code(xs[0])
-        self._table = (_Mxfp4Group * n)()
-        for i, x in enumerate(xs):
-            px, rows, K, ldx = _matrix(x)
-            nb, pw = (K + 31) // 32, (K + 1) // 2
-            if packeds[i] is None:
-                packeds[i] = torch.empty((rows, pw), dtype=torch.uint8, device=dev)
-            if scales[i] is None:
-                scales[i] = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=dev)
-            pp, _, _, ldp = _matrix(packeds[i])
-            ps, _, _, ld_s = _matrix(scales[i])
-            if rows * K and (ldp != pw or packeds[i].numel() != rows * pw):
-                raise ValueError("packed must be a contiguous [rows, ceil(K/2)] uint8 tensor")
-            self._table[i] = _Mxfp4Group(px, ldx, rows, K, pp, ps, ld_s)
-        self.packeds, self.scales = packeds, scales
-
-    def __call__(self):
-        if self.n:
-            _check(self._L, self._L.mxq_quantize_mxfp4_grouped(self._table, self.n, self._dt, _stream(self.xs[0])))
-        return self.packeds, self.scales
-
-
-@_device_operands
-def mxq_quantize_mxfp4_grouped(xs, packeds=None, scales=None, scale_ld: Optional[int] = None,
-                               lib: str = "libmxq.so"):
-    """Packed MXFP4 (deployment format) of a list of weights of one dtype, in as
-    few launches as possible -> (list of nibble pairs, list of E8M0 codes); the
-    same bytes as one mxq_quantize_mxfp4 per weight.  GroupedQuantizeMxfp4
-    prepares the call once for repeated use."""
-    return GroupedQuantizeMxfp4(xs, packeds, scales, scale_ld, lib)()
-
-
-@_device_operands
-def mxq_dequantize_grouped(datas, scales, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3, outs=None,
-                           out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so"):
-    """Decode a list of FP8 payloads with their E8M0 codes (one format, scale
-    layout and output dtype), in as few launches as possible -> list of
-    outputs; the same bits as one mxq_dequantize per payload.  `outs`: list of
-    outputs (None entries, or None for the whole list, are allocated).
-    GroupedDequantize prepares the call once for repeated use."""
-    return GroupedDequantize(datas, scales, layout, fmt, outs, out_dtype, lib)()
-
-
-@_device_operands
-def mxq_mxfp4_to_fp8_block128_grouped(xs, datas=None, tile_codes=None, lib: str = "libmxq.so"):
-    """Direct 128x128 blockwise FP8 of a list of weights of one dtype, in as few
-    launches as possible -> (list of payloads, list of tile codes); the same
-    bytes as one mxq_mxfp4_to_fp8_block128 per weight.  GroupedBlock128
-    prepares the call once for repeated use."""
-    return GroupedBlock128(xs, datas, tile_codes, lib)()
-
-
-@_device_operands
-def mxq_fake_quantize_mxfp4_grouped(xs, ys=None, lib: str = "libmxq.so"):
-    """MXFP4 projection of a list of weights of one dtype, in as few launches as
-    possible -> list of outputs; the same bits as one mxq_fake_quantize_mxfp4 per
-    weight.  `ys`: list of outputs (None entries, or None for the whole list,
-    are allocated; an entry may be its weight, in place).  GroupedProjection
-    prepares the call once for repeated use."""
-    return GroupedProjection(xs, ys, lib)()
-
-
-@_device_operands
-def mxq_mxfp4_to_mxfp8_row_grouped(xs, datas=None, scales=None, scale_ld: Optional[int] = None,
-                                   lib: str = "libmxq.so"):
-    """Direct MXFP8 rowwise lift of a list of weights of one dtype, in as few
-    launches as possible -> (list of payloads, list of E8M0 codes); the same
-    bytes as one mxq_mxfp4_to_mxfp8_row per weight.  `datas` / `scales`: lists
-    of outputs (None entries, or None for the whole list, are allocated).
-    GroupedRowLift prepares the call once for repeated use."""
-    return GroupedRowLift(xs, datas, scales, scale_ld, lib)()
 
 
 @_device_operands
@@ -520,28 +261,15 @@ def mxq_mxfp4_to_fp8_block128(x: torch.Tensor, data: Optional[torch.Tensor] = No
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
-    if data is None:
-        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
-    if tile_code is None:
-        tile_code = torch.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=x.device)
-    pd, _, _, ldd = _matrix(data)
-    pt, trows, tcols, ldt = _matrix(tile_code)
-    if rows * K and (ldd != K or data.numel() != rows * K):
-        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    ntr, ntc = (rows + 127) // 128, (K + 127) // 128
+    tile_code = _scale_for(x, ntr, ntc, None) if tile_code is None else tile_code
+    data, pd = _payload_for(x, rows, K, data)
+    pt, ldt = _operand(tile_code, ntr, ntc, "tile_code", byte=True)
     if noop is None:
         _check(L, L.mxq_mxfp4_to_fp8_block128(px, ldx, rows, K, dt, pd, pt, ldt, _stream(x)))
     else:
         _check(L, L.mxq_mxfp4_to_fp8_block128_guarded(px, ldx, rows, K, dt, pd, pt, ldt, _flag(noop), _stream(x)))
     return data, tile_code
-
-
-def _payload_for(x: torch.Tensor, rows: int, K: int, data: Optional[torch.Tensor]):
-    if data is None:
-        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
-    pd, _, _, ldd = _matrix(data)
-    if rows * K and (ldd != K or data.numel() != rows * K):
-        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
-    return data, pd
 
 
 @_device_operands
@@ -554,10 +282,10 @@ def mxq_mxfp4_to_mxfp8_col(x: torch.Tensor, data: Optional[torch.Tensor] = None,
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
-    if scale is None:
-        scale = torch.zeros(((rows + 31) // 32, scale_ld or K), dtype=torch.uint8, device=x.device)
+    bands = (rows + 31) // 32
+    scale = _scale_for(x, bands, K, scale_ld) if scale is None else scale
     data, pd = _payload_for(x, rows, K, data)
-    ps, _, _, ld_s = _matrix(scale)
+    ps, ld_s = _operand(scale, bands, K, "scale", byte=True)
     if noop is None:
         _check(L, L.mxq_mxfp4_to_mxfp8_col(px, ldx, rows, K, dt, pd, ps, ld_s, _stream(x)))
     else:
@@ -577,15 +305,13 @@ def mxq_mxfp4_to_mxfp8_row_col(x: torch.Tensor, row_data: Optional[torch.Tensor]
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
-    nb = (K + 31) // 32
-    if row_scale is None:
-        row_scale = torch.zeros((rows, row_scale_ld or nb), dtype=torch.uint8, device=x.device)
-    if col_scale is None:
-        col_scale = torch.zeros(((rows + 31) // 32, col_scale_ld or K), dtype=torch.uint8, device=x.device)
-    row_data, prd = _payload_for(x, rows, K, row_data)
-    col_data, pcd = _payload_for(x, rows, K, col_data)
-    prs, _, _, ld_rs = _matrix(row_scale)
-    pcs, _, _, ld_cs = _matrix(col_scale)
+    bands = (rows + 31) // 32
+    row_scale = _scale_for(x, rows, _nb(K), row_scale_ld) if row_scale is None else row_scale
+    col_scale = _scale_for(x, bands, K, col_scale_ld) if col_scale is None else col_scale
+    row_data, prd = _payload_for(x, rows, K, row_data, "row payload")
+    col_data, pcd = _payload_for(x, rows, K, col_data, "column payload")
+    prs, ld_rs = _operand(row_scale, rows, _nb(K), "row_scale", byte=True)
+    pcs, ld_cs = _operand(col_scale, bands, K, "col_scale", byte=True)
     if noop is None:
         _check(L, L.mxq_mxfp4_to_mxfp8_row_col(px, ldx, rows, K, dt, prd, prs, ld_rs, pcd, pcs, ld_cs, _stream(x)))
     else:
@@ -602,18 +328,14 @@ def mxq_fake_quantize_mxfp4_with_mxfp8_row(x: torch.Tensor, y: Optional[torch.Te
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
-    nb = (K + 31) // 32
     if y is None:
         y = torch.empty_like(x, memory_format=torch.contiguous_format)
-    if scale is None:
-        scale = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=x.device)
-    if data is None:
-        data = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
-    py, _, _, ldy = _matrix(y)
-    pd, _, _, ldd = _matrix(data)
-    ps, _, _, ld_s = _matrix(scale)
-    if rows * K and (ldd != K or data.numel() != rows * K):
-        raise ValueError("payload must be a contiguous [rows, K] uint8 tensor")
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have x's dtype and shape")
+    scale = _scale_for(x, rows, _nb(K), scale_ld) if scale is None else scale
+    py, ldy = _operand(y, rows, K, "y")
+    data, pd = _payload_for(x, rows, K, data)
+    ps, ld_s = _operand(scale, rows, _nb(K), "scale", byte=True)
     _check(L, L.mxq_fake_quantize_mxfp4_with_mxfp8_row(px, ldx, py, ldy, rows, K, dt, pd, ps, ld_s, _stream(x)))
     return y, data, scale
 
@@ -626,13 +348,19 @@ def mxq_export_mxfp8(data: Optional[torch.Tensor], scale_storage: Optional[torch
     if data is None or scale_storage is None:
         rc = L.mxq_export_mxfp8(None, None, 0, K, 0, None, None)
         _check(L, rc)
-    ps, rows, sld, ld_s = _matrix(scale_storage)
-    nb = (K + 31) // 32
+    ps, rows, _, ld_s = _matrix(scale_storage)
+    nb = _nb(K)
     if scale_out is None:
         scale_out = torch.empty((rows, nb), dtype=torch.uint8, device=scale_storage.device)
-    po, _, _, _ = _matrix(scale_out)
+    _operand(scale_storage, rows, nb, "scale_storage", byte=True)
+    po, _ = _operand(scale_out, rows, nb, "scale_out", contiguous=True, byte=True)
     _check(L, L.mxq_export_mxfp8(data.data_ptr(), ps, rows, K, ld_s, po, _stream(scale_storage)))
     return scale_out
+
+
+_SCALE_GRID = {MXQ_SCALE_ROW_1X32: lambda rows, K: (rows, _nb(K)),
+               MXQ_SCALE_TILE_128X128: lambda rows, K: ((rows + 127) // 128, (K + 127) // 128),
+               MXQ_SCALE_COL_32X1: lambda rows, K: ((rows + 31) // 32, K)}
 
 
 @_device_operands
@@ -641,15 +369,14 @@ def mxq_dequantize(data: torch.Tensor, scale: torch.Tensor, layout: int = MXQ_SC
                    lib: str = "libmxq.so") -> torch.Tensor:
     """Decode FP8 payload bytes with E8M0 codes into bf16 / fp32."""
     L = load(lib)
-    pd, rows, K, ldd = _matrix(data)
-    if rows * K and ldd != K:
-        raise ValueError("payload must be contiguous")
-    ps, srows, scols, lds = _matrix(scale)
+    _, rows, K, _ = _matrix(data)
+    pd, _ = _operand(data, rows, K, "payload", contiguous=True, byte=True)
     if out is None:
         out = torch.empty((rows, K), dtype=out_dtype, device=data.device)
-    po, _, _, ldo = _matrix(out)
-    _check(L, L.mxq_dequantize(pd, ps, lds, rows, K, fmt, layout, po, ldo,
-                               _dtype_code(out), _stream(data)))
+    srows, scols = _SCALE_GRID[layout](rows, K) if layout in _SCALE_GRID else (0, 0)   # the C call rejects others
+    ps, lds = _operand(scale, srows, scols, "scale", byte=True)
+    po, ldo = _operand(out, rows, K, "out")
+    _check(L, L.mxq_dequantize(pd, ps, lds, rows, K, fmt, layout, po, ldo, _dtype_code(out), _stream(data)))
     return out
 
 
@@ -660,24 +387,20 @@ def mxq_quantize_mxfp4(x: torch.Tensor, packed: Optional[torch.Tensor] = None, s
     L = load(lib)
     dt = _dtype_code(x)
     px, rows, K, ldx = _matrix(x)
-    nb = (K + 31) // 32
+    pw = (K + 1) // 2
     if packed is None:
-        packed = torch.empty((rows, (K + 1) // 2), dtype=torch.uint8, device=x.device)
-    if scale is None:
-        scale = torch.zeros((rows, scale_ld or nb), dtype=torch.uint8, device=x.device)
-    pp, _, pw, ldp = _matrix(packed)
-    ps, _, _, ld_s = _matrix(scale)
-    if rows * K and (ldp != (K + 1) // 2 or pw != (K + 1) // 2):
-        raise ValueError("packed must be a contiguous [rows, ceil(K/2)] uint8 tensor")
+        packed = torch.empty((rows, pw), dtype=torch.uint8, device=x.device)
+    scale = _scale_for(x, rows, _nb(K), scale_ld) if scale is None else scale
+    pp, _ = _operand(packed, rows, pw, "packed", contiguous=True, byte=True)
+    ps, ld_s = _operand(scale, rows, _nb(K), "scale", byte=True)
     _check(L, L.mxq_quantize_mxfp4(px, ldx, rows, K, dt, pp, ps, ld_s, _stream(x)))
     return packed, scale
 
 
 def _packed_args(packed: torch.Tensor, scale: torch.Tensor, K: int):
-    pp, rows, pw, ldp = _matrix(packed)
-    if rows * K and (pw != (K + 1) // 2 or ldp != pw):
-        raise ValueError("packed must be a contiguous [rows, ceil(K/2)] uint8 tensor")
-    ps, _, _, ld_s = _matrix(scale)
+    _, rows, _, _ = _matrix(packed)
+    pp, _ = _operand(packed, rows, (K + 1) // 2, "packed", contiguous=True, byte=True)
+    ps, ld_s = _operand(scale, rows, _nb(K), "scale", byte=True)
     return pp, ps, ld_s, rows
 
 
@@ -689,7 +412,7 @@ def mxq_dequantize_mxfp4(packed: torch.Tensor, scale: torch.Tensor, K: int, out:
     pp, ps, ld_s, rows = _packed_args(packed, scale, K)
     if out is None:
         out = torch.empty((rows, K), dtype=out_dtype, device=packed.device)
-    po, _, _, ldo = _matrix(out)
+    po, ldo = _operand(out, rows, K, "out")
     _check(L, L.mxq_dequantize_mxfp4(pp, ps, ld_s, rows, K, po, ldo, _dtype_code(out), _stream(packed)))
     return out
 
@@ -701,12 +424,9 @@ def mxq_mxfp4_packed_to_mxfp8_row(packed: torch.Tensor, scale: torch.Tensor, K: 
     """Direct MXFP8 row lift from packed MXFP4 -> (payload uint8 [rows, K], codes)."""
     L = load(lib)
     pp, ps, ld_s, rows = _packed_args(packed, scale, K)
-    if data is None:
-        data = torch.empty((rows, K), dtype=torch.uint8, device=packed.device)
-    if scale_out is None:
-        scale_out = torch.zeros((rows, (K + 31) // 32), dtype=torch.uint8, device=packed.device)
-    pd, _, _, _ = _matrix(data)
-    po, _, _, ldo = _matrix(scale_out)
+    data, pd = _payload_for(packed, rows, K, data)
+    scale_out = _scale_for(packed, rows, _nb(K), None) if scale_out is None else scale_out
+    po, ldo = _operand(scale_out, rows, _nb(K), "scale_out", byte=True)
     _check(L, L.mxq_mxfp4_packed_to_mxfp8_row(pp, ps, ld_s, rows, K, pd, po, ldo, _stream(packed)))
     return data, scale_out
 
@@ -718,14 +438,244 @@ def mxq_mxfp4_packed_to_fp8_block128(packed: torch.Tensor, scale: torch.Tensor, 
     """Direct 128x128 blockwise FP8 from packed MXFP4 -> (payload uint8 [rows, K], tile codes)."""
     L = load(lib)
     pp, ps, ld_s, rows = _packed_args(packed, scale, K)
-    if data is None:
-        data = torch.empty((rows, K), dtype=torch.uint8, device=packed.device)
-    if tile_code is None:
-        tile_code = torch.zeros(((rows + 127) // 128, (K + 127) // 128), dtype=torch.uint8, device=packed.device)
-    pd, _, _, _ = _matrix(data)
-    pt, _, _, ldt = _matrix(tile_code)
+    ntr, ntc = (rows + 127) // 128, (K + 127) // 128
+    data, pd = _payload_for(packed, rows, K, data)
+    tile_code = _scale_for(packed, ntr, ntc, None) if tile_code is None else tile_code
+    pt, ldt = _operand(tile_code, ntr, ntc, "tile_code", byte=True)
     _check(L, L.mxq_mxfp4_packed_to_fp8_block128(pp, ps, ld_s, rows, K, pd, pt, ldt, _stream(packed)))
     return data, tile_code
+
+
+# ---- grouped calls ------------------------------------------------------------------------
+
+class _Grouped:
+    """A grouped entry point prepared once for a fixed list of weights and
+    outputs: the descriptor table is built (and every operand checked) here,
+    and each call enqueues the whole list on torch's current stream with one
+    call into the library, for weights re-converted every training step.  The
+    object keeps the tensors alive.
+
+    Subclasses name the C function and its descriptor struct, the list
+    arguments (the first is the per-weight input that sets rows and K),
+    `_describe`, which fills in missing outputs for weight i, checks its
+    operands and returns its descriptor, and `_extra_args`, the call's
+    arguments between the table and the stream."""
+    _fn: str
+    _struct: type
+    _lists: tuple
+
+    def __init__(self, lists, lib: str):
+        self._L = load(lib)
+        lists = [list(l) if l is not None else None for l in lists]
+        self.n = n = len(lists[0])
+        lists = [[None] * n if l is None else l for l in lists]
+        if any(len(l) != n for l in lists):
+            raise ValueError(f"{self._fn}: {', '.join(self._lists[1:])} must have one entry per weight")
+        self._tensors = lists
+        self._first = None
+        if n == 0:
+            return
+        for l in lists:
+            for t in l:
+                if t is not None and not (isinstance(t, torch.Tensor) and t.is_cuda):
+                    raise ValueError(f"{self._fn}: operands must be device tensors on one device")
+        dev = lists[0][0].device
+        if any(t is not None and t.device != dev for l in lists for t in l):
+            raise ValueError(f"{self._fn}: operands must be device tensors on one device")
+        self._first = lists[0][0]
+        self._table = (self._struct * n)(*[self._describe(i, dev) for i in range(n)])
+        self._extra = self._extra_args()
+
+    def _describe(self, i: int, dev):
+        raise NotImplementedError
+
+    def _extra_args(self):
+        return (self._same_dtype(self._tensors[0], "weights"),)
+
+    def _same_dtype(self, ts, what: str) -> int:
+        if any(t.dtype != ts[0].dtype for t in ts):
+            raise ValueError(f"all {what} of a group call must have one dtype")
+        return _dtype_code(ts[0])
+
+    def __call__(self):
+        if self.n:
+            _check(self._L, getattr(self._L, self._fn)(self._table, self.n, *self._extra, _stream(self._first)))
+        return self._outputs()
+
+
+class GroupedRowLift(_Grouped):
+    """The grouped row lift (mxq_mxfp4_to_mxfp8_row_grouped); `datas` / `scales` are the outputs."""
+    _fn, _struct, _lists = "mxq_mxfp4_to_mxfp8_row_grouped", _RowGroup, ("xs", "datas", "scales")
+
+    def __init__(self, xs, datas=None, scales=None, scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+        self._scale_ld = scale_ld
+        super().__init__((xs, datas, scales), lib)
+
+    def _describe(self, i, dev):
+        xs, datas, scales = self._tensors
+        px, rows, K, ldx = _matrix(xs[i])
+        if scales[i] is None:
+            scales[i] = _scale_for(xs[i], rows, _nb(K), self._scale_ld)
+        datas[i], pd = _payload_for(xs[i], rows, K, datas[i])
+        ps, ld_s = _operand(scales[i], rows, _nb(K), "scale", byte=True)
+        return _RowGroup(px, ldx, rows, K, pd, ps, ld_s)
+
+    def _outputs(self):
+        return self._tensors[1], self._tensors[2]
+
+    xs = property(lambda self: self._tensors[0])
+    datas = property(lambda self: self._tensors[1])
+    scales = property(lambda self: self._tensors[2])
+
+
+class GroupedProjection(_Grouped):
+    """The grouped MXFP4 projection (mxq_fake_quantize_mxfp4_grouped); an
+    output may be its weight itself (in place); `ys` are the outputs."""
+    _fn, _struct, _lists = "mxq_fake_quantize_mxfp4_grouped", _ProjGroup, ("xs", "ys")
+
+    def __init__(self, xs, ys=None, lib: str = "libmxq.so"):
+        super().__init__((xs, ys), lib)
+
+    def _describe(self, i, dev):
+        xs, ys = self._tensors
+        if ys[i] is None:
+            ys[i] = torch.empty_like(xs[i], memory_format=torch.contiguous_format)
+        if ys[i].dtype != xs[i].dtype or ys[i].shape != xs[i].shape:
+            raise ValueError("each output must have its weight's dtype and shape")
+        px, rows, K, ldx = _matrix(xs[i])
+        py, ldy = _operand(ys[i], rows, K, "y")
+        return _ProjGroup(px, ldx, py, ldy, rows, K)
+
+    def _outputs(self):
+        return self._tensors[1]
+
+    xs = property(lambda self: self._tensors[0])
+    ys = property(lambda self: self._tensors[1])
+
+
+class GroupedBlock128(_Grouped):
+    """The grouped 128x128 fold (mxq_mxfp4_to_fp8_block128_grouped); `datas` / `tile_codes` are the outputs."""
+    _fn, _struct, _lists = "mxq_mxfp4_to_fp8_block128_grouped", _Block128Group, ("xs", "datas", "tile_codes")
+
+    def __init__(self, xs, datas=None, tile_codes=None, lib: str = "libmxq.so"):
+        super().__init__((xs, datas, tile_codes), lib)
+
+    def _describe(self, i, dev):
+        xs, datas, tcs = self._tensors
+        px, rows, K, ldx = _matrix(xs[i])
+        ntr, ntc = (rows + 127) // 128, (K + 127) // 128
+        if tcs[i] is None:
+            tcs[i] = _scale_for(xs[i], ntr, ntc, None)
+        datas[i], pd = _payload_for(xs[i], rows, K, datas[i])
+        pt, ldt = _operand(tcs[i], ntr, ntc, "tile_code", byte=True)
+        return _Block128Group(px, ldx, rows, K, pd, pt, ldt)
+
+    def _outputs(self):
+        return self._tensors[1], self._tensors[2]
+
+    xs = property(lambda self: self._tensors[0])
+    datas = property(lambda self: self._tensors[1])
+    tile_codes = property(lambda self: self._tensors[2])
+
+
+class GroupedDequantize(_Grouped):
+    """The grouped decode (mxq_dequantize_grouped) of payloads with one format,
+    scale layout and output dtype; `outs` are the outputs."""
+    _fn, _struct, _lists = "mxq_dequantize_grouped", _DequantGroup, ("datas", "scales", "outs")
+
+    def __init__(self, datas, scales, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3, outs=None,
+                 out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so"):
+        self._layout, self._fmt, self._out_dtype = layout, fmt, out_dtype
+        super().__init__((datas, scales, outs), lib)
+
+    def _extra_args(self):
+        return (self._fmt, self._layout, self._same_dtype(self._tensors[2], "outputs"))
+
+    def _describe(self, i, dev):
+        datas, scales, outs = self._tensors
+        _, rows, K, _ = _matrix(datas[i])
+        if outs[i] is None:
+            outs[i] = torch.empty(tuple(datas[i].shape), dtype=self._out_dtype, device=dev)
+        pd, _ = _operand(datas[i], rows, K, "payload", contiguous=True, byte=True)
+        srows, scols = _SCALE_GRID[self._layout](rows, K) if self._layout in _SCALE_GRID else (0, 0)
+        ps, lds = _operand(scales[i], srows, scols, "scale", byte=True)
+        po, ldo = _operand(outs[i], rows, K, "out")
+        return _DequantGroup(pd, ps, lds, rows, K, po, ldo)
+
+    def _outputs(self):
+        return self._tensors[2]
+
+    datas = property(lambda self: self._tensors[0])
+    outs = property(lambda self: self._tensors[2])
+
+
+class GroupedQuantizeMxfp4(_Grouped):
+    """The grouped packed MXFP4 encode (mxq_quantize_mxfp4_grouped); `packeds` / `scales` are the outputs."""
+    _fn, _struct, _lists = "mxq_quantize_mxfp4_grouped", _Mxfp4Group, ("xs", "packeds", "scales")
+
+    def __init__(self, xs, packeds=None, scales=None, scale_ld: Optional[int] = None, lib: str = "libmxq.so"):
+        self._scale_ld = scale_ld
+        super().__init__((xs, packeds, scales), lib)
+
+    def _describe(self, i, dev):
+        xs, packeds, scales = self._tensors
+        px, rows, K, ldx = _matrix(xs[i])
+        pw = (K + 1) // 2
+        if packeds[i] is None:
+            packeds[i] = torch.empty((rows, pw), dtype=torch.uint8, device=dev)
+        if scales[i] is None:
+            scales[i] = _scale_for(xs[i], rows, _nb(K), self._scale_ld)
+        pp, _ = _operand(packeds[i], rows, pw, "packed", contiguous=True, byte=True)
+        ps, ld_s = _operand(scales[i], rows, _nb(K), "scale", byte=True)
+        return _Mxfp4Group(px, ldx, rows, K, pp, ps, ld_s)
+
+    def _outputs(self):
+        return self._tensors[1], self._tensors[2]
+
+    xs = property(lambda self: self._tensors[0])
+    packeds = property(lambda self: self._tensors[1])
+    scales = property(lambda self: self._tensors[2])
+
+
+@_device_operands
+def mxq_mxfp4_to_mxfp8_row_grouped(xs, datas=None, scales=None, scale_ld: Optional[int] = None,
+                                   lib: str = "libmxq.so"):
+    """Direct MXFP8 rowwise lift of a list of weights of one dtype, in as few
+    launches as possible -> (list of payloads, list of E8M0 codes); the same
+    bytes as one mxq_mxfp4_to_mxfp8_row per weight.  `datas` / `scales`: lists
+    of outputs (None entries, or None for the whole list, are allocated)."""
+    return GroupedRowLift(xs, datas, scales, scale_ld, lib)()
+
+
+@_device_operands
+def mxq_fake_quantize_mxfp4_grouped(xs, ys=None, lib: str = "libmxq.so"):
+    """MXFP4 projection of a list of weights of one dtype, in as few launches as
+    possible -> list of outputs; the same bits as one mxq_fake_quantize_mxfp4 per
+    weight (an entry of `ys` may be its weight, in place)."""
+    return GroupedProjection(xs, ys, lib)()
+
+
+@_device_operands
+def mxq_mxfp4_to_fp8_block128_grouped(xs, datas=None, tile_codes=None, lib: str = "libmxq.so"):
+    """Direct 128x128 blockwise FP8 of a list of weights of one dtype, in as few
+    launches as possible -> (list of payloads, list of tile codes)."""
+    return GroupedBlock128(xs, datas, tile_codes, lib)()
+
+
+@_device_operands
+def mxq_dequantize_grouped(datas, scales, layout: int = MXQ_SCALE_ROW_1X32, fmt: int = MXQ_E4M3, outs=None,
+                           out_dtype: torch.dtype = torch.bfloat16, lib: str = "libmxq.so"):
+    """Decode a list of FP8 payloads with their E8M0 codes (one format, scale
+    layout and output dtype), in as few launches as possible -> list of outputs."""
+    return GroupedDequantize(datas, scales, layout, fmt, outs, out_dtype, lib)()
+
+
+@_device_operands
+def mxq_quantize_mxfp4_grouped(xs, packeds=None, scales=None, scale_ld: Optional[int] = None,
+                               lib: str = "libmxq.so"):
+    """Packed MXFP4 (deployment format) of a list of weights of one dtype, in as
+    few launches as possible -> (list of nibble pairs, list of E8M0 codes)."""
+    return GroupedQuantizeMxfp4(xs, packeds, scales, scale_ld, lib)()
 
 
 # ---- convenience layer ------------------------------------------------------------------

@@ -62,10 +62,6 @@ def lib() -> ctypes.CDLL:
                 getattr(L, name).restype = ctypes.c_int
             L.orc_scale_exponent_bits.argtypes = [ctypes.c_uint32, i32]
             L.orc_e2m1_code_bits.argtypes = [ctypes.c_uint32, i32, i32]
-            L.orc_e2m1_codes.argtypes = [vp, i64, i32, i32, vp]
-            L.orc_fp8_encode_bulk.argtypes = [vp, i64, i32, i32, i32, vp]
-            L.orc_fp8_encode_bulk.restype = None
-            L.orc_e2m1_codes.restype = None
             L.orc_round_to_format.argtypes = [i32, ctypes.c_uint64, i32, i32, ctypes.POINTER(i32)]
             L.orc_round_to_format.restype = ctypes.c_uint32
             L.orc_unpack.argtypes = [ctypes.c_uint32, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_uint64),
@@ -278,24 +274,6 @@ def scale_exponent_bits(amax_bits: int, dtype: int = BF16) -> int:
 
 def e2m1_code_bits(x_bits: int, e: int, dtype: int = BF16) -> int:
     return lib().orc_e2m1_code_bits(x_bits, dtype, e)
-
-
-def e2m1_codes(x: np.ndarray, e: int) -> np.ndarray:
-    """4-bit E2M1 values (sign in bit 3) of RTNE(|x| / 2^e) for every element of a
-    bf16 (uint16) / fp32 (uint32) bit array; 0xFF where x is not finite."""
-    x = np.ascontiguousarray(x)
-    out = np.empty(x.shape, dtype=np.uint8)
-    lib().orc_e2m1_codes(_ptr(x), x.size, _dtype_of(x), e, _ptr(out))
-    return out
-
-
-def fp8_encode(x: np.ndarray, S: int, fmt: int = 2) -> np.ndarray:
-    """Nearest-even FP8 bytes (fmt 2 E4M3, 3 E5M2) of x * 2^-S for a bf16 / fp32
-    bit array; 0xFF on overflow or non-finite input."""
-    x = np.ascontiguousarray(x)
-    out = np.empty(x.shape, dtype=np.uint8)
-    lib().orc_fp8_encode_bulk(_ptr(x), x.size, _dtype_of(x), S, fmt, _ptr(out))
-    return out
 
 
 FMT_BF16, FMT_FP32, FMT_E4M3, FMT_E5M2 = 0, 1, 2, 3

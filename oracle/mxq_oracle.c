@@ -141,7 +141,7 @@ static const int E2M1_X2[8] = {0, 1, 2, 3, 4, 6, 8, 12};
  * i.e. the smallest integer e with 6 * 2^e >= amax, then clamped.
  * Reading: amax = 0 has log2 = -inf and clamps to -126. */
 static int scale_exponent_clamped(dyadic amax, int lo, int hi);
-int orc_scale_exponent(dyadic amax) { return scale_exponent_clamped(amax, -126, 125); }
+static int orc_scale_exponent(dyadic amax) { return scale_exponent_clamped(amax, -126, 125); }
 
 static int scale_exponent_clamped(dyadic amax, int lo, int hi) {
   int e;
@@ -165,7 +165,7 @@ static int scale_exponent_clamped(dyadic amax, int lo, int hi) {
 /* E2M1 code of |x| / 2^e rounded to the nearest grid point, ties to the even
  * code ([QAT] Description: round to nearest, ties to even, on E2M1).  Values above 6 have 6 as their
  * nearest grid point (the top scale saturates: [QAT] Known limitations). */
-int orc_e2m1_code(dyadic ax, int e) {
+static int orc_e2m1_code(dyadic ax, int e) {
   if (ax.M == 0) return 0;
   int j = ax.k - e;                                     /* t = M * 2^j */
   int l = bitlen(ax.M) + j;                             /* t in [2^(l-1), 2^l) */
@@ -650,29 +650,6 @@ int orc_e2m1_code_bits(uint32_t x_bits, int dtype, int e) {
   dyadic a = unpack(x_bits, dtype_fmt(dtype));
   if (a.cls != CLS_FINITE) return -1;
   return orc_e2m1_code(a, e);
-}
-
-/* E2M1 codes of RTNE(|x| / 2^e) for n elements (sign bit in bit 3, as a 4-bit
- * E2M1 value); 0xFF for a non-finite element. */
-void orc_e2m1_codes(const void* x, int64_t n, int dtype, int e, uint8_t* out) {
-  fmt_t f = dtype_fmt(dtype);
-  for (int64_t i = 0; i < n; i++) {
-    dyadic d = unpack(load_bits(x, dtype, (size_t)i), f);
-    out[i] = d.cls != CLS_FINITE ? 0xFF : (uint8_t)((d.neg << 3) | orc_e2m1_code(d, e));
-  }
-}
-
-/* Nearest-even FP8 encodings (fmt_id 2 E4M3, 3 E5M2) of x * 2^-S for n
- * elements; overflow or non-finite input gives 0xFF. */
-void orc_fp8_encode_bulk(const void* x, int64_t n, int dtype, int S, int fmt_id, uint8_t* out) {
-  fmt_t f = dtype_fmt(dtype), q = fmt_id == 2 ? FMT_E4M3 : FMT_E5M2;
-  for (int64_t i = 0; i < n; i++) {
-    dyadic d = unpack(load_bits(x, dtype, (size_t)i), f);
-    int inexact, ovf;
-    if (d.cls != CLS_FINITE) { out[i] = 0xFF; continue; }
-    uint32_t b = round_to_format(d.neg, d.M, d.k - S, q, &inexact, &ovf);
-    out[i] = ovf ? 0xFF : (uint8_t)b;
-  }
 }
 
 /* Nearest-even rounding of (-1)^neg * M * 2^k to fmt_id (0 bf16, 1 fp32, 2 E4M3, 3 E5M2).

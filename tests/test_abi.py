@@ -193,6 +193,30 @@ def test_binding_rejects_host_tensors():
     assert names and all(hasattr(getattr(mxq, n), "__wrapped__") for n in names)
 
 
+def test_binding_operand_extent_checks():
+    """Every operand whose extent the binding knows is checked against the
+    region the C call touches before anything is launched (the C entry points
+    see only a pointer and a stride): too few rows or columns, a single row
+    standing in for several, a payload that is not packed row by row, and a
+    payload or code array whose elements are not bytes all raise ValueError."""
+    import torch
+    op = mxq._operand
+    codes = torch.zeros(100, 4, dtype=torch.uint8)
+    assert op(codes, 100, 2, "scale")[1] == 4                        # padded storage: stride 4
+    assert op(codes[:, :2], 100, 2, "scale")[1] == 4                 # a strided view that covers the region
+    for bad, rows, cols in ((codes[:99], 100, 2), (codes[:, :1], 100, 2), (codes[:1], 100, 2),
+                            (torch.zeros(1, 400, dtype=torch.uint8), 100, 2)):
+        with pytest.raises(ValueError, match="must cover"):
+            op(bad, rows, cols, "scale")
+    data = torch.zeros(64, 128, dtype=torch.uint8)
+    assert op(data, 64, 128, "payload", contiguous=True, byte=True)[1] == 128
+    with pytest.raises(ValueError, match="contiguous"):
+        op(data[:, :96], 64, 96, "payload", contiguous=True, byte=True)
+    with pytest.raises(ValueError, match="bytes"):
+        op(torch.zeros(64, 128, dtype=torch.bfloat16), 64, 128, "payload", contiguous=True, byte=True)
+    assert op(torch.zeros(0, 4, dtype=torch.uint8), 0, 2, "scale")[1] == 4   # empty: nothing is touched
+
+
 def test_grouped_row_lift_host_validation(lib):
     """The grouped row lift checks every group as the single call does, and
     refuses any output that overlaps another group's input or output -- all

@@ -4,8 +4,8 @@ Tolerance is 0: every payload byte, scale code and output bit must match,
 NaNs included (both sides write the canonical quiet NaN).  Inputs are the
 seeded workloads of ``workloads`` -- the same host bits feed the oracle and the
 device copy.  Sizes: the small and exhaustive corpora, the 4096 x 4096 spread
-sweep and the 8192 x 8192 headline weight in full; the 28672 x 8192 /
-8192 x 28672 MLP weights are launched in full and compared on sampled rows.
+sweep, the 8192 x 8192 headline weight and the 28672 x 8192 / 8192 x 28672
+MLP weights (and the fp32 master of the first), all compared in full.
 """
 import numpy as np
 import pytest
@@ -118,42 +118,15 @@ def test_c4_headline(dev, scale_ld):
     check_all(W.c4_headline(), dev, scale_ld=scale_ld)
 
 
-def _sampled_rows(rows, n, seed):
-    g = np.random.default_rng(seed)
-    pick = np.unique(np.concatenate([[0, 1, rows - 1], g.choice(rows, n, replace=False)]))
-    return pick
-
-
 @pytest.mark.parametrize("which", ["up", "down", "up_master"])
-def test_c5_mlp_sampled(dev, which):
-    """Full-size launches; outputs compared on sampled rows (and whole 128-row
-    tile bands for the blockwise fold).  Scale storage padded by 4 columns so
-    the export takes the copy path."""
+def test_c5_mlp_full(dev, which):
+    """The MLP-shaped weights -- 28672 x 8192 and 8192 x 28672 bf16 and the fp32
+    master of the first -- compared in full, every output of every kernel
+    against the oracle: projection, row lift into scale storage padded by 4
+    columns (the padding checked untouched, so the export copies), the export,
+    the row decode, the 128x128 fold (every band) and its decode."""
     bits = W.c5_mlp(which)
-    rows, K = bits.shape
-    nb = (K + 31) // 32
-    x = to_dev(bits, dev)
-    tdt, odt = out_dtype_of(bits)
-    y = to_host(mxq.mxq_fake_quantize_mxfp4(x))
-    data, scale = mxq.mxq_mxfp4_to_mxfp8_row(x, scale_ld=nb + 4)
-    out = to_host(mxq.mxq_export_mxfp8(data, scale, K))
-    dec = to_host(mxq.mxq_dequantize(data, torch.from_numpy(out).to(dev), out_dtype=tdt))
-    data, scale = to_host(data), to_host(scale)
-    pick = _sampled_rows(rows, 384, 7)
-    sub = np.ascontiguousarray(bits[pick])
-    assert_bits(y[pick], oracle.fake_quantize_mxfp4(sub, threads=THREADS), "projection (sampled rows)")
-    wd, ws = oracle.mxfp4_to_mxfp8_row(sub, scale_ld=nb + 4, threads=THREADS)
-    assert_bits(data[pick], wd, "row payload (sampled rows)")
-    assert_bits(scale[pick][:, :nb], ws[:, :nb], "row codes (sampled rows)")
-    assert_bits(out[pick], ws[:, :nb], "export (sampled rows)")
-    assert_bits(dec, y, "decode of the row lift == projection (all rows)")
-    bd, tc = mxq.mxq_mxfp4_to_fp8_block128(x)
-    bd, tc = to_host(bd), to_host(tc)
-    for band in (0, rows // 128 // 2, rows // 128 - 1):
-        sl = slice(band * 128, band * 128 + 128)
-        wbd, wtc = oracle.mxfp4_to_fp8_block128(np.ascontiguousarray(bits[sl]), threads=THREADS)
-        assert_bits(bd[sl], wbd, f"128x128 payload (band {band})")
-        assert_bits(tc[band:band + 1], wtc, f"tile codes (band {band})")
+    check_all(bits, dev, scale_ld=(bits.shape[1] + 31) // 32 + 4)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -477,9 +450,8 @@ def test_errors(dev):
     with pytest.raises(mxq.MxqError) as e:      # partial overlap of x and y
         mxq.mxq_fake_quantize_mxfp4(buf[:, :64], buf[:, 1:65])
     assert e.value.status == mxq.MXQ_ERR_ALIAS
-    with pytest.raises(mxq.MxqError) as e:      # scale storage narrower than ceil(K/32)
+    with pytest.raises(ValueError, match="must cover"):   # scale storage narrower than ceil(K/32)
         mxq.mxq_mxfp4_to_mxfp8_row(xb, scale=torch.zeros((4, 1), dtype=torch.uint8, device=dev))
-    assert e.value.status == mxq.MXQ_ERR_SHAPE
     with pytest.raises(ValueError):
         mxq.export_components(None, None, (4, 64))
     # a host operand beside device ones is refused before any launch
@@ -487,6 +459,48 @@ def test_errors(dev):
         mxq.mxq_fake_quantize_mxfp4(xb, torch.zeros((4, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="device tensors"):
         mxq.mxq_mxfp4_to_mxfp8_row(xb, scale=torch.zeros((4, 2), dtype=torch.uint8))
+
+
+def test_undersized_operands_are_refused(dev):
+    """A caller-supplied output (or code input) smaller than the region the
+    call touches is refused with ValueError before any launch; the buffers are
+    left as they were."""
+    x = to_dev(W.c4_headline(shape=(256, 512)), dev)
+    u8 = lambda *shape: torch.full(shape, 0x3C, dtype=torch.uint8, device=dev)
+    data, scale, bdata, tc = u8(256, 512), u8(256, 16), u8(256, 512), u8(2, 4)
+    calls = {
+        "projection y": lambda: mxq.mxq_fake_quantize_mxfp4(x, torch.empty(256, 512, dtype=torch.bfloat16, device=dev)[:255]),
+        "row codes, too few rows": lambda: mxq.mxq_mxfp4_to_mxfp8_row(x, data, u8(255, 16)),
+        "row codes, one row": lambda: mxq.mxq_mxfp4_to_mxfp8_row(x, data, u8(1, 16 * 256)),
+        "row codes, too narrow": lambda: mxq.mxq_mxfp4_to_mxfp8_row(x, data, u8(256, 15)),
+        "row payload, short": lambda: mxq.mxq_mxfp4_to_mxfp8_row(x, u8(255, 512), scale),
+        "fold tile codes": lambda: mxq.mxq_mxfp4_to_fp8_block128(x, bdata, u8(1, 4)),
+        "column codes": lambda: mxq.mxq_mxfp4_to_mxfp8_col(x, data, u8(7, 512)),
+        "row + column codes": lambda: mxq.mxq_mxfp4_to_mxfp8_row_col(x, data, u8(256, 8), bdata, u8(8, 512)),
+        "fused codes": lambda: mxq.mxq_fake_quantize_mxfp4_with_mxfp8_row(x, None, data, u8(128, 16)),
+        "export out": lambda: mxq.mxq_export_mxfp8(data, scale, 512, u8(255, 16)),
+        "decode out": lambda: mxq.mxq_dequantize(data, scale, out=torch.empty(255, 512, dtype=torch.bfloat16, device=dev)),
+        "decode codes": lambda: mxq.mxq_dequantize(data, u8(256, 15)),
+        "decode tile codes": lambda: mxq.mxq_dequantize(data, u8(2, 3), layout=mxq.MXQ_SCALE_TILE_128X128),
+        "packed encode codes": lambda: mxq.mxq_quantize_mxfp4(x, u8(256, 256), u8(200, 16)),
+        "packed decode out": lambda: mxq.mxq_dequantize_mxfp4(u8(256, 256), scale, 512,
+                                                              out=torch.empty(1, 512, dtype=torch.float32, device=dev)),
+        "packed codes in": lambda: mxq.mxq_dequantize_mxfp4(u8(256, 256), u8(256, 8), 512),
+        "packed row lift payload": lambda: mxq.mxq_mxfp4_packed_to_mxfp8_row(u8(256, 256), scale, 512, u8(128, 512)),
+        "packed row lift codes": lambda: mxq.mxq_mxfp4_packed_to_mxfp8_row(u8(256, 256), scale, 512, data, u8(256, 1)),
+        "packed fold tile codes": lambda: mxq.mxq_mxfp4_packed_to_fp8_block128(u8(256, 256), scale, 512, bdata, u8(2, 1)),
+        "grouped row codes": lambda: mxq.mxq_mxfp4_to_mxfp8_row_grouped([x, x], [data, bdata], [scale, u8(64, 16)]),
+        "grouped fold tile codes": lambda: mxq.mxq_mxfp4_to_fp8_block128_grouped([x], [bdata], [u8(1, 1)]),
+        "grouped decode out": lambda: mxq.mxq_dequantize_grouped([data], [scale], outs=[torch.empty(3, 512, dtype=torch.bfloat16, device=dev)]),
+        "grouped packed codes": lambda: mxq.mxq_quantize_mxfp4_grouped([x], [u8(256, 256)], [u8(256, 2)]),
+    }
+    for what, call in calls.items():
+        with pytest.raises(ValueError):
+            call()
+            raise AssertionError(f"{what}: accepted")
+    torch.cuda.synchronize()
+    for t in (data, scale, bdata, tc):
+        assert (to_host(t) == 0x3C).all()
 
 
 def test_decode_every_byte_and_code(dev):

@@ -365,22 +365,25 @@ def test_export_shapes(facts):
     assert oracle.export_mxfp8(s16, 16).shape == (100, facts["export_scale_cols_K16"]["value"])
 
 
-def test_export_floor_mutation_fails_partial_block_cases(facts):
-    """The pages' mutation check: scale columns K // 32 break exactly the
-    partial-block cases (K = 48 and K = 16); full-block shapes are unaffected."""
-    failing = 0
-    for rows, K in ((100, 48), (100, 16), (7, 48), (7, 16), (3, 80), (2, 112), (100, 64), (4, 32)):
-        x = W.c1_small()[:rows, :min(K, 48)]
-        if K > 48:
-            x = np.tile(x, (1, 3))[:, :K]
-        x = np.ascontiguousarray(x)
-        _, scale = oracle.mxfp4_to_mxfp8_row(x, scale_ld=((K + 31) // 32 + 3) // 4 * 4)
-        good = oracle.export_mxfp8(scale, K)
-        bad = F.export(scale, K, mutation="floor_cols")
-        if good.shape != bad.shape:
-            failing += 1
-        assert np.array_equal(good, F.export(scale, K))
-    assert failing == facts["export_partial_block_cases_failing_with_floor"]["value"]
+@pytest.mark.parametrize("K,partial", [(48, True), (16, True), (80, True), (33, True), (32, False), (64, False),
+                                       (256, False)])
+def test_export_floor_mutation_breaks_exactly_the_partial_block_shapes(K, partial):
+    """[EXP] Testing: taking the scale width as K // 32 instead of ceil(K/32)
+    breaks the partial-block layouts -- the (100, 48) tensor and K = 16 -- and
+    leaves every K that is a multiple of 32 unchanged.  The exported scales of
+    each shape, built by the oracle, against the mutated export."""
+    rows = 100 if K == 48 else 7
+    x = np.ascontiguousarray(np.tile(W.c1_small()[:rows], (1, K // 48 + 1))[:, :K])
+    _, scale = oracle.mxfp4_to_mxfp8_row(x, scale_ld=((K + 31) // 32 + 3) // 4 * 4)
+    good = oracle.export_mxfp8(scale, K)
+    assert good.shape == (rows, (K + 31) // 32)
+    assert np.array_equal(good, F.export(scale, K))
+    bad = F.export(scale, K, mutation="floor_cols")
+    assert (bad.shape != good.shape) == partial
+    if partial:
+        assert bad.shape[1] == K // 32 < good.shape[1]    # the partial last block loses its scale
+    else:
+        assert np.array_equal(bad, good)
 
 
 # ---------------------------------------------------------------- oracle vs brute force
@@ -396,6 +399,45 @@ def test_oracle_matches_brute_force_bf16(name):
 
 def test_oracle_matches_brute_force_fp32():
     x = W.fp32_fuzz(1 << 13)
+    assert np.array_equal(oracle.fake_quantize_mxfp4(x), F.fake_quantize(x, "fp32"))
+    d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+    d1, s1 = F.row_lift(x, "fp32")
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+
+
+def test_oracle_matches_brute_force_fp32_edges():
+    """fp32 at its edges -- the ladder 2^-127 .. 2^-149 with the 2^-128 tie,
+    midpoints one ulp either side, 1.5*2^k +- 1 ulp as a block's amax down into
+    the subnormals, 6*2^125 up to the largest fp32, NaN payloads -- through the
+    projection, row lift, fold, columnwise conversion and packed encode,
+    against exact rationals ([QAT] Test results (B200), projection kernel row)."""
+    x = W.c2_planted_fp32()
+    assert np.array_equal(oracle.fake_quantize_mxfp4(x), F.fake_quantize(x, "fp32"))
+    d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
+    d1, s1 = F.row_lift(x, "fp32")
+    assert np.array_equal(d0, d1) and np.array_equal(s0, s1)
+    d0, c0 = oracle.mxfp4_to_fp8_block128(x)
+    d1, c1 = F.block128(x, "fp32")
+    assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
+    d0, c0 = oracle.mxfp4_to_mxfp8_col(x)
+    d1, c1 = F.col_lift(x, "fp32")
+    assert np.array_equal(d0, d1) and np.array_equal(c0, c1)
+    p0, s0 = oracle.quantize_mxfp4(x)
+    p1, s1 = F.quantize_mxfp4(x, "fp32")
+    assert np.array_equal(p0, p1) and np.array_equal(s0, s1)
+
+
+def test_oracle_matches_brute_force_on_every_fp32_tie():
+    """Every block of the fp32 value x exponent corpus that holds an exact E2M1
+    tie (each midpoint at each block exponent, both signs), through the
+    projection and the row lift, against exact rationals."""
+    b = W.value_exponent_pairs("fp32").reshape(-1, 32)
+    v = b.view(np.float32).astype(np.float64)
+    scale = v[:, 0] / 6.0
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = np.abs(v) / np.where(scale > 0, scale, np.nan)[:, None]
+    x = np.ascontiguousarray(b[np.isin(t, W.MIDPOINTS).any(axis=1)])
+    assert 1000 < len(x) <= 3528
     assert np.array_equal(oracle.fake_quantize_mxfp4(x), F.fake_quantize(x, "fp32"))
     d0, s0 = oracle.mxfp4_to_mxfp8_row(x)
     d1, s1 = F.row_lift(x, "fp32")
@@ -725,3 +767,20 @@ def test_oracle_matches_brute_force_at_every_block_exponent():
     dc0, sc0 = oracle.mxfp4_to_mxfp8_col(x)
     dc1, sc1 = F.col_lift(x, "bf16")
     assert np.array_equal(dc0, dc1) and np.array_equal(sc0, sc1)
+
+
+def test_every_oracle_function_is_pinned():
+    """Every public function of the oracle package is exercised by this file,
+    and the C library exports exactly the entry points the package binds."""
+    import inspect
+    import re
+    import subprocess
+    src = open(__file__).read()
+    public = [n for n, f in inspect.getmembers(oracle, inspect.isfunction)
+              if not n.startswith("_") and f.__module__ == oracle.__name__ and n not in ("build", "lib")]
+    unpinned = [n for n in public if not re.search(r"oracle\." + n + r"\(", src)]
+    assert not unpinned, unpinned
+    nm = subprocess.run(["nm", "-D", "--defined-only", oracle.build()], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
+    bound = set(re.findall(r"L\.(orc_\w+)\.", inspect.getsource(oracle.lib)))
+    assert exported == bound, (exported ^ bound)

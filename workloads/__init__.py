@@ -114,6 +114,64 @@ def c2_planted(seed: int = 0) -> np.ndarray:
     return np.stack(rows[:64]).astype(np.uint16)
 
 
+def fp32_bits_of(values) -> np.ndarray:
+    """Exact fp32 bits of float64 values that fp32 represents exactly (checked)."""
+    v = np.asarray(values, dtype=np.float64)
+    f32 = v.astype(np.float32)
+    if not np.array_equal(f32.astype(np.float64), v, equal_nan=True):
+        raise ValueError("value not representable in fp32")
+    return f32.view(np.uint32).copy()
+
+
+def c2_planted_fp32(seed: int = 0) -> np.ndarray:
+    """160 x 32 fp32 edge rows (one 1x32 block per row): the 64 rows of
+    c2_planted widened exactly, then the fp32-only edges -- the ladder
+    2^-127 .. 2^-149 with the 2^-128 tie in a block of scale 2^-126, every E2M1
+    midpoint one fp32 ulp either side at low, middle and top exponents,
+    1.5*2^k and its fp32 neighbours as a block's amax (down into the fp32
+    subnormals), values from 6*2^125 up to the largest fp32, and non-finite
+    poisoning with several NaN payloads."""
+    rows = [r.astype(np.uint32) << 16 for r in c2_planted(seed)]
+    r = lambda vals: rows.append(np.asarray(vals, dtype=np.uint32))
+    two = lambda k: int(fp32_bits_of(np.ldexp(1.0, k)))
+    NEG = 0x80000000
+    ladder = [two(-127 - i) for i in range(23)]                    # 2^-127 .. 2^-149 (fp32 subnormals)
+    r(ladder + [v | NEG for v in ladder[1:10]])
+    r([v | NEG for v in ladder] + ladder[1:10])
+    r([two(-127), two(-128)] * 16)                                 # the 2^-128 tie beside 2^-127
+    r([two(-128)] * 32)                                            # amax 2^-128 alone: e = -126, all ties to 0
+    r([two(-128) | NEG, two(-149)] * 16)
+    for e in (-126, -125, -122, -121, -100, -1, 0, 1, 100, 124, 125):
+        for sign in (0, NEG):                                      # midpoints exactly and one ulp either side
+            vals = [int(fp32_bits_of(np.ldexp(6.0, e)))]
+            for m in MIDPOINTS:
+                b = int(fp32_bits_of(np.ldexp(m, e)))
+                vals += [b - 1, b, b + 1]
+            vals += [int(fp32_bits_of(np.ldexp(6.0, e))) - 1, int(fp32_bits_of(np.ldexp(0.5, e))) - 1,
+                     int(fp32_bits_of(np.ldexp(0.5, e))) + 1]
+            vals += [vals[0]] * (32 - len(vals))
+            r([v | sign for v in vals])
+    for k in (-148, -140, -130, -128, -127, -126, -125, -124, -123, -60, -1, 0, 1, 60, 126, 127):
+        b = int(fp32_bits_of(np.ldexp(1.5, k)))                   # 1.5*2^k - 1 ulp, exactly, + 1 ulp as amax
+        for d in (-1, 0, 1):
+            r([b + d, (b + d) | NEG] * 8 + [two(k - 3), two(k - 4) | NEG] * 8 if k > -146 else [b + d, (b + d) | NEG] * 16)
+    sat = np.linspace(0x7F400000, 0x7F7FFFFF, 32).astype(np.int64)
+    r(sat)                                                         # 6*2^125 up to FLT_MAX
+    r([0x7F7FFFFF, 0xFF7FFFFF] * 8 + [0x7F400001, 0xFF400001] * 8)
+    r([0x7F3FFFFF] * 16 + [0x7F400000, 0x7F400001] * 8)            # just below, at and above the cap
+    r([0x3F800000] * 31 + [0x7F800000])                            # +Inf poisons
+    r([0x3F800000] * 31 + [0xFF800000])                            # -Inf poisons
+    r([0x7F800001] + [two(-127)] * 31)                             # signalling NaN in a 2^-127 block
+    r([0x3F800000, 0xFFC00000] + [0xBF800000] * 30)                # negative quiet NaN
+    r([0x7FFFFFFF] + [0x00000001] * 31)                            # NaN with a full payload beside 2^-149
+    g = torch.Generator().manual_seed(seed + 1)
+    while len(rows) < 160:                                         # random rows at scattered scales
+        i = len(rows)
+        rows.append(_fp32_bits(torch.randn(32, generator=g) * float(2.0 ** (((i * 41) % 270) - 145))))
+    assert all(len(x) == 32 for x in rows) and len(rows) == 160, len(rows)
+    return np.stack(rows).astype(np.uint32)
+
+
 def c3_spread(seed: int = 2, shape=(4096, 4096)) -> np.ndarray:
     """fp32 bits.  Tile t (row-major) has spread d = t mod 17 and base exponent
     b uniform in [-110, 100], or b = -126 for tiles with floor(t/17) mod 4 == 0.
@@ -190,12 +248,21 @@ def c5_mlp(which: str):
     raise ValueError(which)
 
 
+# Low halves that widen a bf16 pattern into the fp32 corpus: 0x0000 is the
+# bf16 value itself (every E2M1 grid point and midpoint, exactly), 0x0001 its
+# neighbour one fp32 ulp up, 0xFFFF the neighbour one fp32 ulp below the next
+# bf16 pattern; None draws one random low half per pattern.
+FP32_LOW_HALVES = (0x0000, 0x0001, 0xFFFF, None)
+
+
 def value_exponent_pairs(dtype: str = "bf16", width: int = 256, seed: int = 7) -> np.ndarray:
     """Every (element value, block exponent e) pair, e in [-126, 125]: for each
     e, every finite value with |x| <= 6 * 2^e (every finite value at e = 125,
     where larger ones saturate) is placed in 1x32 blocks whose first element is
     6 * 2^e, so that is the block's amax and e its scale exponent.  bf16: all
-    65536 patterns; fp32: every bf16 pattern widened with two random low halves.
+    65536 patterns; fp32: every bf16 pattern widened with each low half of
+    FP32_LOW_HALVES, so every E2M1 midpoint and its neighbours one fp32 ulp
+    either side meet every e (and the fp32 subnormals 2^-149 .. occur).
     Returned as a [rows, width] bit array (zeros pad the last row)."""
     g = np.random.default_rng(seed)
     if dtype == "bf16":
@@ -204,8 +271,8 @@ def value_exponent_pairs(dtype: str = "bf16", width: int = 256, seed: int = 7) -
         out_t, anchor_of = np.uint16, lambda e: int(bf16_bits_of(np.ldexp(6.0, e)))
     else:
         hi = np.arange(65536, dtype=np.uint32) << 16
-        pool = np.concatenate([hi | g.integers(0, 65536, 65536).astype(np.uint32),
-                               hi | g.integers(0, 65536, 65536).astype(np.uint32)])
+        pool = np.concatenate([hi | (g.integers(0, 65536, 65536).astype(np.uint32) if low is None else np.uint32(low))
+                               for low in FP32_LOW_HALVES])
         vals = pool
         out_t = np.uint32
         anchor_of = lambda e: int(np.array(np.ldexp(6.0, e), dtype=np.float32).view(np.uint32))
