@@ -52,7 +52,10 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_PROJ_THREADS 64       // projection (one wave)
 #endif
 #ifndef MXQ_ROW_THREADS
-#define MXQ_ROW_THREADS 256       // row lift, MXFP4 encode
+#define MXQ_ROW_THREADS 64        // row lift (one wave)
+#endif
+#ifndef MXQ_Q4_THREADS
+#define MXQ_Q4_THREADS 256        // MXFP4 encode
 #endif
 #ifndef MXQ_FUSED_THREADS
 #define MXQ_FUSED_THREADS 64      // fused projection + row lift
@@ -71,13 +74,19 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_PROJ_STEPS 1
 #endif
 #ifndef MXQ_ROW_STEPS
-#define MXQ_ROW_STEPS 2
+#define MXQ_ROW_STEPS 1
+#endif
+#ifndef MXQ_Q4_STEPS
+#define MXQ_Q4_STEPS 2
 #endif
 #ifndef MXQ_FUSED_STEPS
 #define MXQ_FUSED_STEPS 1
 #endif
 #ifndef MXQ_DEQUANT_STEPS
-#define MXQ_DEQUANT_STEPS 2
+#define MXQ_DEQUANT_STEPS 1
+#endif
+#ifndef MXQ_DQ4_STEPS
+#define MXQ_DQ4_STEPS 2           // packed MXFP4 decode
 #endif
 #ifndef MXQ_PACKED_STEPS
 #define MXQ_PACKED_STEPS 1
@@ -109,6 +118,7 @@ constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS, kD
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
               kPackedSteps = MXQ_PACKED_STEPS;
 constexpr int kFusedThreads = MXQ_FUSED_THREADS, kFusedSteps = MXQ_FUSED_STEPS;
+constexpr int kQ4Threads = MXQ_Q4_THREADS, kQ4Steps = MXQ_Q4_STEPS, kDq4Steps = MXQ_DQ4_STEPS;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
 static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
@@ -145,6 +155,19 @@ __device__ __forceinline__ void stream_store_row_sc1(u32x4 v, void* base, uint32
   (void)nbytes;
   stream_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off));
 #endif
+}
+
+// 2-, 4-, 8- or 16-byte streaming store at byte offset `off` of a row whose base
+// address is the same for the whole wave: a buffer store carrying the nt bit.
+// (The compiler can drop the non-temporal hint of a plain store when it merges
+// code paths; the buffer form keeps the cache policy in the instruction.)
+template <typename V>
+__device__ __forceinline__ void stream_store_at(V v, void* base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  if constexpr (sizeof(V) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 2);
+  else if constexpr (sizeof(V) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 2);
+  else if constexpr (sizeof(V) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 2);
+  else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 2);
 }
 
 // ------------------------------------------------------------------------------------
@@ -449,6 +472,18 @@ __device__ __forceinline__ bool skipped(const int32_t* __restrict__ noop) {
   return noop != nullptr && *reinterpret_cast<const volatile int32_t*>(noop) != 0;
 }
 
+// E8M0 code of a block, stored by the lane that holds the block's first chunk.
+// One step's codes are a short run (16 bytes for bf16 at 64 lanes) of a 128-byte
+// line whose other runs come from the neighbouring workgroups, which the
+// dispatcher deals to other XCDs and so other L2s.  The store carries the sc1
+// cache-policy bit: for such partial-line stores it measured faster than a
+// plain store, and far faster than a non-temporal one.  base: the step's first
+// code, the same address for the whole wave; off: this lane's code from it.
+__device__ __forceinline__ void store_code(uint8_t* base, uint32_t off, uint32_t code) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, r, off, 0, 16);   // sc1
+}
+
 // Row lift; with kProj it also writes the projection y (the fused one-pass form).
 // Launch shape of the row kernel: the row lift's, or (kProj) the fused pass's.
 template <bool kProj>
@@ -458,11 +493,15 @@ struct RowShape {
 
 // The row lift's steps of workgroup wg (with kProj, also the projection y);
 // all loads are issued before the no-op flag is read and before any store.
-template <typename T, bool VEC, bool kProj>
+// FULL: every step of every workgroup is whole and inside the matrix (16-byte
+// path, K a multiple of a step's width, the grid an exact number of steps), so
+// there is no bounds check and nothing to branch around before the first load.
+template <typename T, bool VEC, bool kProj, bool FULL = false>
 __device__ __forceinline__ void row_steps(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                           uint8_t* __restrict__ data, uint8_t* __restrict__ scale, int64_t scale_ld,
                                           T* __restrict__ y, int64_t ld_y, MxqDivisor steps_per_row,
                                           uint32_t total_steps, uint32_t wg, const int32_t* __restrict__ noop) {
+  static_assert(VEC || !FULL, "the full-step form takes the 16-byte path");
   using G = StepGeom<T, RowShape<kProj>::kTPB>;
   constexpr int kRowSteps = RowShape<kProj>::kSteps;
   const uint32_t tid = threadIdx.x;
@@ -472,31 +511,42 @@ __device__ __forceinline__ void row_steps(const T* __restrict__ x, int64_t ld_x,
   for (int u = 0; u < kRowSteps; u++) {
     const uint32_t step = wg * kRowSteps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
-    if (step < total_steps) {
+    if (FULL || step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
-      w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
+      if constexpr (FULL)
+        w[u] = stream_load(reinterpret_cast<const u32x4*>(x + (int64_t)row * ld_x + seg * G::kElemsPerStep + lane_col));
+      else
+        w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
     }
   }
   if (skipped(noop)) return;   // read once the input loads are in flight
 #pragma unroll
   for (int u = 0; u < kRowSteps; u++) {
     const uint32_t step = wg * kRowSteps + u;
-    if (step < total_steps) {
+    if (FULL || step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
       const Block b = chunk_block<T>(w[u]);
       const float s = e8m0(b.eb);
       const uint32_t code = row_code(b);
       const Proj16<T> p = project<T>(fp4_of(w[u], s, T{}), s);
-      // the projection output goes out like the projection kernel's (nt sc1 buffer stores)
-      if constexpr (kProj) store_chunk<T, VEC, true>(y + (int64_t)row * ld_y, col0, K, proj_chunk<T>(p, b.poison));
-      store_payload<T, VEC>(data + (int64_t)row * K, col0, K, payload_chunk<T>(p, code, b.poison));
-      if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)code;
+      if constexpr (FULL) {
+        if constexpr (kProj)
+          stream_store_row_sc1(proj_chunk<T>(p, b.poison), y + (int64_t)row * ld_y, (uint32_t)(K * sizeof(T)),
+                               (uint32_t)(col0 * sizeof(T)));
+        stream_store_at(payload_chunk<T>(p, code, b.poison), data + (int64_t)row * K, (uint32_t)col0);
+        if (tid % G::kLPB == 0) store_code(scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep, tid / G::kLPB, code);
+      } else {
+        // the projection output goes out like the projection kernel's (nt sc1 buffer stores)
+        if constexpr (kProj) store_chunk<T, VEC, true>(y + (int64_t)row * ld_y, col0, K, proj_chunk<T>(p, b.poison));
+        store_payload<T, VEC>(data + (int64_t)row * K, col0, K, payload_chunk<T>(p, code, b.poison));
+        if (tid % G::kLPB == 0 && col0 < K) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)code;
+      }
     }
   }
 }
 
-template <typename T, bool VEC, bool kProj>
+template <typename T, bool VEC, bool kProj, bool FULL>
 __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                                  uint8_t* __restrict__ data,
                                                                  uint8_t* __restrict__ scale, int64_t scale_ld,
@@ -504,7 +554,8 @@ __global__ __launch_bounds__(RowShape<kProj>::kTPB) void row_kernel(const T* __r
                                                                  MxqDivisor steps_per_row, uint32_t total_steps,
                                                                  const int32_t* __restrict__ noop) {
   keep_denormals();
-  row_steps<T, VEC, kProj>(x, ld_x, K, data, scale, scale_ld, y, ld_y, steps_per_row, total_steps, blockIdx.x, noop);
+  row_steps<T, VEC, kProj, FULL>(x, ld_x, K, data, scale, scale_ld, y, ld_y, steps_per_row, total_steps, blockIdx.x,
+                                 noop);
 }
 
 // ------------------------------------------------------------------------------------
@@ -891,8 +942,10 @@ __device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8])
 }
 
 // The decode's body: workgroup wg's kDequantSteps steps of one weight.  The
-// single and grouped kernels both run it.
-template <typename TO, bool kE5M2, int kLay, bool VEC>
+// single and grouped kernels both run it.  FULL: every step whole and inside
+// the matrix (aligned rows, K a multiple of a step, an exact grid), so no
+// bounds checks; its stores are buffer stores with the nt bit.
+template <typename TO, bool kE5M2, int kLay, bool VEC, bool FULL = false>
 __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, const uint8_t* __restrict__ scale,
                                               int64_t scale_ld, int64_t K, TO* __restrict__ out, int64_t ld_out,
                                               MxqDivisor steps_per_row, uint32_t total_steps, uint32_t wg) {
@@ -918,16 +971,16 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
     if constexpr (kSplit) cs_b[u] = 0u;
     if constexpr (kLay == kLayCol) ccs[u] = u32x2{0u, 0u};
     const uint32_t step = wg * kDequantSteps + u;
-    if (step >= total_steps) continue;
+    if (!FULL && step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
-    if (col0 >= K) continue;
+    if (!FULL && col0 >= K) continue;
     const uint8_t* drow = data + (int64_t)row * K;
     if constexpr (kSplit) {
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         const int64_t c = col0 + h * kHalf;
-        if (c >= K) continue;
+        if (!FULL && c >= K) continue;
         if (VEC) {
           qs[u][h] = stream_load(reinterpret_cast<const uint32_t*>(drow + c));
         } else {
@@ -973,10 +1026,10 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     const uint32_t step = wg * kDequantSteps + u;
-    if (step >= total_steps) break;
+    if (!FULL && step >= total_steps) break;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
-    if (col0 >= K) continue;
+    if (!FULL && col0 >= K) continue;
     const u32x2 q = qs[u];
     float s8[8];
 #pragma unroll
@@ -998,7 +1051,9 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
           if ((h & 0x7FFFu) > 0x7F80u) o[i / 2] = (o[i / 2] & ~(0xFFFFu << (16 * (i % 2)))) | (0x7FC0u << (16 * (i % 2)));
         }
       }
-      if (VEC) {
+      if constexpr (FULL) {
+        stream_store_at(o, orow, (uint32_t)(col0 * sizeof(TO)));
+      } else if (VEC) {
         stream_store(o, reinterpret_cast<u32x4*>(orow + col0));
       } else {
         for (int i = 0; i < 8; i++)
@@ -1015,7 +1070,10 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
           if ((f[i] & 0x7FFFFFFFu) > 0x7F800000u) f[i] = 0x7FC00000u;
       }
       // the two groups: elements col0 .. col0+3 and col0+kHalf .. col0+kHalf+3
-      if (VEC) {
+      if constexpr (FULL) {
+        stream_store_at(u32x4{f[0], f[1], f[2], f[3]}, orow, (uint32_t)(col0 * sizeof(TO)));
+        stream_store_at(u32x4{f[4], f[5], f[6], f[7]}, orow, (uint32_t)((col0 + kHalf) * sizeof(TO)));
+      } else if (VEC) {
         stream_store(u32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<u32x4*>(orow + col0));
         if (col0 + kHalf < K) stream_store(u32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<u32x4*>(orow + col0 + kHalf));
       } else {
@@ -1028,13 +1086,14 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
   }
 }
 
-template <typename TO, bool kE5M2, int kLay, bool VEC>
+template <typename TO, bool kE5M2, int kLay, bool VEC, bool FULL>
 __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
                                                            MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
-  dequant_steps<TO, kE5M2, kLay, VEC>(data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps, blockIdx.x);
+  dequant_steps<TO, kE5M2, kLay, VEC, FULL>(data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps,
+                                            blockIdx.x);
 }
 
 // Grouped decode, on the grouped row lift's pattern: blockIdx.y is the weight,
@@ -1078,36 +1137,45 @@ struct Nibbles<uint16_t> { typedef uint32_t type; };   // 8 nibbles per bf16 chu
 template <>
 struct Nibbles<uint32_t> { typedef uint16_t type; };   // 4 nibbles per fp32 chunk
 
-// The packed encode's body: workgroup wg's kRowSteps steps of one weight.  The
+// The packed encode's body: workgroup wg's kQ4Steps steps of one weight.  The
 // single and grouped kernels both run it.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool FULL = false>
 __device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                      uint8_t* __restrict__ packed, uint8_t* __restrict__ scale,
                                                      int64_t scale_ld, MxqDivisor steps_per_row, uint32_t total_steps,
                                                      uint32_t wg) {
-  using G = StepGeom<T, kRowThreads>;
+  using G = StepGeom<T, kQ4Threads>;
   using N = typename Nibbles<T>::type;
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   const int64_t pw = (K + 1) / 2;
-  u32x4 w[kRowSteps];
+  u32x4 w[kQ4Steps];
 #pragma unroll
-  for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = wg * kRowSteps + u;
+  for (int u = 0; u < kQ4Steps; u++) {
+    const uint32_t step = wg * kQ4Steps + u;
     w[u] = u32x4{0u, 0u, 0u, 0u};
-    if (step < total_steps) {
+    if (FULL || step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
-      w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
+      if constexpr (FULL)
+        w[u] = stream_load(reinterpret_cast<const u32x4*>(x + (int64_t)row * ld_x + seg * G::kElemsPerStep + lane_col));
+      else
+        w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kRowSteps; u++) {
-    const uint32_t step = wg * kRowSteps + u;
-    if (step < total_steps) {
+  for (int u = 0; u < kQ4Steps; u++) {
+    const uint32_t step = wg * kQ4Steps + u;
+    if (FULL || step < total_steps) {
       const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
       const int64_t col0 = seg * G::kElemsPerStep + lane_col;
       const Block b = chunk_block<T, 253>(w[u]);
       const uint32_t f = b.poison ? 0u : fp4_of(w[u], e8m0(b.eb), T{});
+      if constexpr (FULL) {
+        stream_store_at((N)f, packed + (int64_t)row * pw, (uint32_t)(col0 / 2));
+        if (tid % G::kLPB == 0)
+          store_code(scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep, tid / G::kLPB, b.poison ? 255u : b.eb);
+        continue;
+      }
       if (col0 < K) {
         uint8_t* prow = packed + (int64_t)row * pw;
         if constexpr (VEC) {
@@ -1123,21 +1191,21 @@ __device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, in
   }
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
+template <typename T, bool VEC, bool FULL>
+__global__ __launch_bounds__(kQ4Threads) void quantize_mxfp4_kernel(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                                                   uint8_t* __restrict__ packed,
                                                                   uint8_t* __restrict__ scale, int64_t scale_ld,
                                                                   MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
-  quantize_mxfp4_steps<T, VEC>(x, ld_x, K, packed, scale, scale_ld, steps_per_row, total_steps, blockIdx.x);
+  quantize_mxfp4_steps<T, VEC, FULL>(x, ld_x, K, packed, scale, scale_ld, steps_per_row, total_steps, blockIdx.x);
 }
 
 // Grouped packed encode, on the grouped row lift's pattern and with its
 // descriptor (data = the packed nibble pairs).  Aligned (VEC) weights only.
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void quantize_mxfp4_grouped_kernel(const RowGroupTable tab) {
+__global__ __launch_bounds__(kQ4Threads) void quantize_mxfp4_grouped_kernel(const RowGroupTable tab) {
   const RowGroupDesc d = tab.g[blockIdx.y];
-  if (blockIdx.x * kRowSteps >= d.total_steps) return;       // uniform: past this weight's steps
+  if (blockIdx.x * kQ4Steps >= d.total_steps) return;       // uniform: past this weight's steps
   keep_denormals();
   quantize_mxfp4_steps<T, true>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld,
                                 d.steps_per_row, d.total_steps, blockIdx.x);
@@ -1183,14 +1251,14 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)tid * (kSplit ? 4 : 8), pw = (K + 1) / 2;
   // All of the workgroup's loads are issued before any decode or store.
-  uint32_t fs[kDequantSteps], cs[kDequantSteps];
-  uint32_t fs_b[kSplit ? kDequantSteps : 1], cs_b[kSplit ? kDequantSteps : 1];   // kSplit: the second group
+  uint32_t fs[kDq4Steps], cs[kDq4Steps];
+  uint32_t fs_b[kSplit ? kDq4Steps : 1], cs_b[kSplit ? kDq4Steps : 1];   // kSplit: the second group
 #pragma unroll
-  for (int u = 0; u < kDequantSteps; u++) {
+  for (int u = 0; u < kDq4Steps; u++) {
     fs[u] = 0u;
     cs[u] = 0u;
     if constexpr (kSplit) fs_b[u] = 0u, cs_b[u] = 0u;
-    const uint32_t step = blockIdx.x * kDequantSteps + u;
+    const uint32_t step = blockIdx.x * kDq4Steps + u;
     if (step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
@@ -1223,8 +1291,8 @@ __global__ __launch_bounds__(kDq4Threads) void dequantize_mxfp4_kernel(const uin
     cs[u] = scale[(int64_t)row * scale_ld + col0 / 32];
   }
 #pragma unroll
-  for (int u = 0; u < kDequantSteps; u++) {
-    const uint32_t step = blockIdx.x * kDequantSteps + u;
+  for (int u = 0; u < kDq4Steps; u++) {
+    const uint32_t step = blockIdx.x * kDq4Steps + u;
     if (step >= total_steps) break;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDq4Threads * 8) + lane_col;
@@ -1287,7 +1355,7 @@ __device__ __forceinline__ u32x2 e4m3x8_of_fp4(uint32_t f, int ds) {
 // MXFP8 row lift from packed MXFP4: each lane takes 16 elements (8 packed bytes
 // in, 16 payload bytes out), so a block of 32 spans two lanes; even lanes write
 // the block's code.  A step is kPackedThreads * 16 elements of one row.
-template <bool VEC>
+template <bool VEC, bool FULL>
 __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const uint8_t* __restrict__ packed,
                                                                   const uint8_t* __restrict__ scale,
                                                                   int64_t scale_ld, int64_t K,
@@ -1305,10 +1373,10 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
     f[u] = u32x2{0u, 0u};
     c[u] = 0u;
     const uint32_t step = blockIdx.x * kPackedSteps + u;
-    if (step >= total_steps) continue;
+    if (!FULL && step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
-    if (col0 >= K) continue;
+    if (!FULL && col0 >= K) continue;
     const uint8_t* prow = packed + (int64_t)row * pw;
     if (VEC) {
       f[u] = stream_load(reinterpret_cast<const u32x2*>(prow + col0 / 2));
@@ -1321,22 +1389,23 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
 #pragma unroll
   for (int u = 0; u < kPackedSteps; u++) {
     const uint32_t step = blockIdx.x * kPackedSteps + u;
-    if (step >= total_steps) break;
+    if (!FULL && step >= total_steps) break;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
-    if (col0 >= K) continue;
-    u32x4 q;
-    uint32_t code = 0u;
-    if (c[u] == 255u) {
-      q = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-      code = 255u;
-    } else {
-      code = c[u] > 6u ? c[u] - 6u : 0u;                       // S = max(e - 6, -127)
-      const int ds = (int)min(c[u], 6u);
-      const u32x2 lo = e4m3x8_of_fp4(f[u][0], ds), hi = e4m3x8_of_fp4(f[u][1], ds);
-      q = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
+    if (!FULL && col0 >= K) continue;
+    // branch-free (convert, then select the poisoned form), so that no load
+    // is sunk below a test of the other
+    const bool poison = c[u] == 255u;
+    const int ds = (int)min(c[u], 6u);
+    const u32x2 lo = e4m3x8_of_fp4(f[u][0], ds), hi = e4m3x8_of_fp4(f[u][1], ds);
+    const u32x4 q = poison ? u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu} : u32x4{lo[0], lo[1], hi[0], hi[1]};
+    const uint32_t code = poison ? 255u : (c[u] > 6u ? c[u] - 6u : 0u);   // S = max(e - 6, -127)
     uint8_t* drow = data + (int64_t)row * K;
+    if constexpr (FULL) {
+      stream_store_at(q, drow, (uint32_t)col0);
+      if (tid % 2 == 0) store_code(code_out + (int64_t)row * code_ld + seg * (kPackedThreads / 2), tid / 2, code);
+      continue;
+    }
     if (VEC) {
       stream_store(q, reinterpret_cast<u32x4*>(drow + col0));
     } else {
@@ -1596,14 +1665,19 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
                    (!fused || (aligned(y, 16) && ld_y % EPL == 0 && fits32(K * (int64_t)sizeof(T))));
+  // every step whole and every workgroup's steps inside the grid: no bounds checks
+  const bool full = vec && spr.d * (int64_t)((tpb / Fmt<T>::kLPB) * 32) == K && total % steps == 0 &&
+                    fits32(K * (int64_t)sizeof(T));
   const dim3 grid(grid_for(total, steps)), block(tpb);
-#define MXQ_ROW_LAUNCH(V, P)                                                                                  \
-  hipLaunchKernelGGL((row_kernel<T, V, P>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \
+#define MXQ_ROW_LAUNCH(V, P, F)                                                                                  \
+  hipLaunchKernelGGL((row_kernel<T, V, P, F>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \
                      (T*)y, ld_y, spr, total, noop)
   if (fused) {
-    if (vec) MXQ_ROW_LAUNCH(true, true); else MXQ_ROW_LAUNCH(false, true);
+    if (full) MXQ_ROW_LAUNCH(true, true, true); else if (vec) MXQ_ROW_LAUNCH(true, true, false);
+    else MXQ_ROW_LAUNCH(false, true, false);
   } else {
-    if (vec) MXQ_ROW_LAUNCH(true, false); else MXQ_ROW_LAUNCH(false, false);
+    if (full) MXQ_ROW_LAUNCH(true, false, true); else if (vec) MXQ_ROW_LAUNCH(true, false, false);
+    else MXQ_ROW_LAUNCH(false, false, false);
   }
 #undef MXQ_ROW_LAUNCH
   return launch_status();
@@ -1659,12 +1733,18 @@ int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
   const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0 &&
                    (kLay != kLayCol || (aligned(scale, 8) && scale_ld % 8 == 0));
+  // every step whole and every workgroup's steps inside the grid: no bounds checks
+  const bool full = vec && spr.d * (int64_t)(kDequantThreads * 8) == K && total % kDequantSteps == 0 &&
+                    fits32(K * (int64_t)sizeof(TO));
   const dim3 grid(grid_for(total, kDequantSteps)), block(kDequantThreads);
-  if (vec)
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true>), grid, block, 0, s, data, scale, scale_ld, K,
+  if (full)
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true, true>), grid, block, 0, s, data, scale, scale_ld, K,
+                       (TO*)out, ld_out, spr, total);
+  else if (vec)
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true, false>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
   else
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, false>), grid, block, 0, s, data, scale, scale_ld, K,
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, false, false>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
   return launch_status();
 }
@@ -1691,15 +1771,21 @@ int launch_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, 
                           int64_t scale_ld, hipStream_t s) {
   MxqDivisor spr;
   uint32_t total;
-  if (steps_for(rows, K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, StepGeom<T, kQ4Threads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(packed, EPL / 2);
-  const dim3 grid(grid_for(total, kRowSteps)), block(kRowThreads);
-  if (vec)
-    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, true>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
+  // every step whole and every workgroup's steps inside the grid: no bounds checks
+  const bool full = vec && spr.d * (int64_t)StepGeom<T, kQ4Threads>::kElemsPerStep == K && total % kQ4Steps == 0 &&
+                    fits32(K * (int64_t)sizeof(T));
+  const dim3 grid(grid_for(total, kQ4Steps)), block(kQ4Threads);
+  if (full)
+    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, true, true>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
+                       scale_ld, spr, total);
+  else if (vec)
+    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, true, false>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
                        scale_ld, spr, total);
   else
-    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, false>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
+    hipLaunchKernelGGL((quantize_mxfp4_kernel<T, false, false>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
                        scale_ld, spr, total);
   return launch_status();
 }
@@ -1712,7 +1798,7 @@ int launch_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scale, int64_t
   if (steps_for(rows, K, kDq4Threads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);
   const bool vec = aligned(packed, 4) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0;
-  const dim3 grid(grid_for(total, kDequantSteps)), block(kDq4Threads);
+  const dim3 grid(grid_for(total, kDq4Steps)), block(kDq4Threads);
   if (vec)
     hipLaunchKernelGGL((dequantize_mxfp4_kernel<TO, true>), grid, block, 0, s, packed, scale, scale_ld, K, (TO*)out,
                        ld_out, spr, total);
@@ -1905,7 +1991,7 @@ int launch_quantize_mxfp4_grouped(const mxq_mxfp4_group* gs, int64_t n, hipStrea
   auto flush = [&]() -> int {
     if (count == 0) return MXQ_OK;
     hipLaunchKernelGGL((quantize_mxfp4_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count),
-                       dim3(kRowThreads), 0, s, tab);
+                       dim3(kQ4Threads), 0, s, tab);
     count = max_w = sum_w = 0;
     return launch_status();
   };
@@ -1919,8 +2005,8 @@ int launch_quantize_mxfp4_grouped(const mxq_mxfp4_group* gs, int64_t n, hipStrea
     }
     MxqDivisor spr;
     uint32_t total;
-    if (steps_for(g.rows, g.K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
-    const int64_t gw = grid_for(total, kRowSteps);
+    if (steps_for(g.rows, g.K, StepGeom<T, kQ4Threads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t gw = grid_for(total, kQ4Steps);
     const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
     if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
       const int st = flush();
@@ -2385,8 +2471,8 @@ int mxq_quantize_mxfp4_grouped(const mxq_mxfp4_group* groups, int64_t n_groups, 
   if (n_groups < 0) return MXQ_ERR_SHAPE;
   if (n_groups == 0) return MXQ_OK;
   if (!groups) return MXQ_ERR_NULL;
-  const int64_t eps = dt == MXQ_BF16 ? StepGeom<uint16_t, kRowThreads>::kElemsPerStep
-                                     : StepGeom<uint32_t, kRowThreads>::kElemsPerStep;
+  const int64_t eps = dt == MXQ_BF16 ? StepGeom<uint16_t, kQ4Threads>::kElemsPerStep
+                                     : StepGeom<uint32_t, kQ4Threads>::kElemsPerStep;
   // every group on its own, then no output may overlap any other range
   std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
   iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 3);
@@ -2441,12 +2527,17 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
   uint32_t total;
   if (steps_for(rows, K, kPackedThreads * 16, &spr, &total)) return MXQ_ERR_SHAPE;
   const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
+  // every step whole and every workgroup's steps inside the grid: no bounds checks
+  const bool full = vec && spr.d * (int64_t)(kPackedThreads * 16) == K && total % kPackedSteps == 0 && fits32(K);
   const dim3 grid(grid_for(total, kPackedSteps)), block(kPackedThreads);
-  if (vec)
-    hipLaunchKernelGGL((packed_convert_kernel<true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+  if (full)
+    hipLaunchKernelGGL((packed_convert_kernel<true, true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+                       scale_out, scale_out_ld, spr, total);
+  else if (vec)
+    hipLaunchKernelGGL((packed_convert_kernel<true, false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
                        scale_out, scale_out_ld, spr, total);
   else
-    hipLaunchKernelGGL((packed_convert_kernel<false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
+    hipLaunchKernelGGL((packed_convert_kernel<false, false>), grid, block, 0, stream, packed, scale, scale_ld, K, data,
                        scale_out, scale_out_ld, spr, total);
   return launch_status();
 }
