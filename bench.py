@@ -19,8 +19,12 @@ kernel's burst on the stream the kernels are launched on: "us" is the burst's
 mean per launch.  After the timed region a separate pass gives "us_median" /
 "us_min", the median / minimum over 5 sub-bursts of 5 launches.  Kernels
 outside the step (the fused passes, packed MXFP4, columnwise) are timed the
-same way after the step's timed region, and so is the runtime's own
-device-to-device copy of the weight ("copy_reference", the projection's bytes).
+same way after the step's timed region, and so are the access-shape reference
+kernels of libmxq_shapes.so ("access_shapes": each moves one kernel's bytes in
+that kernel's access pattern with no quantization arithmetic, and each kernel
+with a shape reports "of_shape", the shape's time over its own), and the
+runtime's own device-to-device copy of the weight ("copy_reference", the
+projection's bytes).
 The default of 100 timed steps keeps the fixed cost of the synchronizations
 around the timed region (tens of us in all) below 1% of it.
 
@@ -34,6 +38,7 @@ padded by 4 columns, so the export copies.)
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -50,6 +55,16 @@ GROUPED = (48, 1024, 2048)       # outside the step: grouped calls over 48 weigh
 SHAPES = ("8192x8192", "28672x8192", "8192x28672")
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
+# The access-shape reference kernels (libmxq_shapes.so, shape codes of include/mxq_shapes.h) timed
+# after the step: name -> (shape code, input buffer, code buffer).  Each moves the bytes of the
+# kernel named in SHAPE_KERNEL in that kernel's access pattern, with no quantization arithmetic;
+# the tile and linear variants split the fold's pattern into its parts (tile-shaped addressing,
+# the workgroup-wide barrier, the 1024-lane two-chunk workgroup).
+SHAPES_OF = {"shape_copy16": (0, "x", "scale2"), "shape_row": (1, "x", "scale2"), "shape_row_codes": (2, "x", "scale2"),
+             "shape_decode": (3, "data", "scale_c"), "shape_tile": (4, "x", "scale2"),
+             "shape_tile_no_barrier": (5, "x", "scale2"), "shape_linear1024": (6, "x", "scale2"),
+             "shape_linear1024_no_barrier": (7, "x", "scale2")}
+SHAPE_KERNEL = {"shape_copy16": "proj", "shape_row_codes": "row", "shape_decode": "dec_row", "shape_tile": "block128"}
 # committed rocprofv3 counter summaries of the 8192 x 8192 weight, per dtype
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_{}.txt")
 # The device code: the kernels and the divisor header they include.
@@ -334,11 +349,30 @@ def main():
     extra_names = ["fused", "quantize_mxfp4", "dequantize_mxfp4", "packed_to_row", "packed_to_block128", "col",
                    "row_col", "dec_col", "row_grouped", "proj_grouped", "block128_grouped", "dec_row_grouped",
                    "quantize_mxfp4_grouped"]
+    # outside the step: the access-shape reference kernels (libmxq_shapes.so), each moving its
+    # kernel's bytes in that kernel's access pattern with no quantization arithmetic
+    shapes_lib = ctypes.CDLL(mxq.build.library_path("libmxq_shapes.so"))
+    shapes_lib.mxq_shape_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    shape_stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def shape_launch(code, src, dst, codes):
+        def go(s):
+            rc = shapes_lib.mxq_shape_run(code, es, s[src].data_ptr(), s[dst].data_ptr(), s[codes].data_ptr(), rows, K,
+                                          shape_stream)
+            if rc:
+                raise RuntimeError(f"access shape {code} did not launch (status {rc})")
+        return go
+
+    for n, (code, src, codes) in SHAPES_OF.items():
+        launches[n] = shape_launch(code, src, "y2", codes)
+    shape_names = list(SHAPES_OF)
     # kernel -> buffer-set offset; consecutive launches of one kernel walk the six sets
     offset = {"proj": 0, "row": 2, "export": 2, "block128": 4, "dec_row": 3, "dec_tile": 5, "fused": 1,
               "quantize_mxfp4": 1, "dequantize_mxfp4": 3, "packed_to_row": 5, "packed_to_block128": 0, "col": 2,
               "row_col": 4, "dec_col": 1, "row_grouped": 0, "proj_grouped": 2, "block128_grouped": 4,
               "dec_row_grouped": 1, "quantize_mxfp4_grouped": 3}
+    offset.update({n: i % NSETS for i, n in enumerate(SHAPES_OF)})
 
     # The timed region runs K whole passes kernel-major: each kernel is launched K
     # times back to back (rotating buffer sets) between two HIP events on the
@@ -369,12 +403,12 @@ def main():
     run(args.warmup, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    run(0, args.warmup, False, extra_names)
-    run(args.warmup, args.steps, True, extra_names)
+    run(0, args.warmup, False, extra_names + shape_names)
+    run(args.warmup, args.steps, True, extra_names + shape_names)
     torch.cuda.synchronize()
     # spread of the per-launch time: SPREAD_BURSTS sub-bursts of SUB launches each
     spread = {}
-    run(0, SUB * SPREAD_BURSTS, True, names + extra_names, sub=SUB, store=spread)
+    run(0, SUB * SPREAD_BURSTS, True, names + extra_names + shape_names, sub=SUB, store=spread)
     torch.cuda.synchronize()
 
     # For reference: the runtime's own device-to-device copy (hipMemcpyAsync) of
@@ -432,6 +466,23 @@ def main():
                                                           "us_min": round(lo, 2), "bytes": extra_bytes[n],
                                                           "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                                                           "traffic": read_traffic(n, args.weight) if headline else None}
+    # the access shapes, each with its kernel's algorithmic bytes (the barrier-free and linear variants of
+    # the fold's pattern with the fold's, the payload-only row shape without the codes)
+    n_el, tiles = rows * K, ((rows + 127) // 128) * ((K + 127) // 128)
+    shape_bytes = {"shape_copy16": nbytes["proj"], "shape_row": es * n_el + n_el, "shape_row_codes": nbytes["row"],
+                   "shape_decode": nbytes["dec_row"], "shape_tile": nbytes["block128"],
+                   "shape_tile_no_barrier": nbytes["block128"], "shape_linear1024": es * n_el + n_el,
+                   "shape_linear1024_no_barrier": es * n_el + n_el}
+    shapes_out = {}
+    for n in shape_names:
+        us, med, lo = burst_stats(n)
+        gbs = shape_bytes[n] / (us * 1e-6) / 1e9
+        shapes_out[n[len("shape_"):]] = {"us": round(us, 2), "us_median": round(med, 2), "us_min": round(lo, 2),
+                                         "bytes": shape_bytes[n], "GB/s": round(gbs, 1),
+                                         "frac": round(gbs / HBM_PEAK_GBS, 4), "of_kernel": SHAPE_KERNEL.get(n)}
+    for n, k in SHAPE_KERNEL.items():
+        # the kernel's speed as a fraction of its access shape's (1.0: the pattern alone sets its time)
+        kernels[k]["of_shape"] = round(shapes_out[n[len("shape_"):]]["us"] / kernels[k]["us"], 4)
     extra["fused_proj_row"]["vs_separate_us"] = round(kernels["proj"]["us"] + kernels["row"]["us"], 2)
     extra["row_col"]["vs_separate_us"] = round(kernels["row"]["us"] + extra["col"]["us"], 2)
     dominant = max(names, key=lambda n: kernels[n]["us"])
@@ -464,6 +515,7 @@ def main():
         "roofline": rl,
         "kernels": kernels,
         "outside_step": extra,
+        "access_shapes": shapes_out,
         "copy_reference": {"what": "hipMemcpyAsync device to device of the weight (torch copy_)",
                            "us": round(copy_us, 2), "bytes": 2 * es * rows * K,
                            "GB/s": round(2 * es * rows * K / (copy_us * 1e-6) / 1e9, 1),

@@ -5,7 +5,8 @@
 the build-variant tests: ``libmxq_fastmath.so`` (fast-math, denormals flushed),
 ``libmxq_o1.so`` (-O1) and ``libmxq_o0.so`` (-O0, no optimisation).  Every
 step of the path is integer arithmetic, so all four builds must produce
-identical bits.
+identical bits.  ``libmxq_shapes.so`` holds the access-shape reference kernels
+(``csrc/shapes.hip``) that bench.py times beside the library's kernels.
 """
 from __future__ import annotations
 
@@ -29,7 +30,9 @@ VARIANTS = {
     "libmxq_fastmath.so": ["-O3", "-ffast-math", "-fgpu-flush-denormals-to-zero"],
     "libmxq_o1.so": ["-O1"],
     "libmxq_o0.so": ["-O0"],
+    "libmxq_shapes.so": ["-O3"],
 }
+SOURCES = {"libmxq_shapes.so": os.path.join(HERE, "csrc", "shapes.hip")}   # the others: SRC
 
 
 def hipcc() -> str:
@@ -42,7 +45,7 @@ def hipcc() -> str:
 def build_one(name: str, flags, verbose: bool = False) -> str:
     out = os.path.join(HERE, name)
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc()] + COMMON + flags + [SRC, "-o", tmp]
+    cmd = [hipcc()] + COMMON + flags + [SOURCES.get(name, SRC), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
@@ -65,7 +68,8 @@ def stale(name: str = "libmxq.so") -> bool:
     if not os.path.exists(lib):
         return True
     t = os.path.getmtime(lib)
-    return any(os.path.getmtime(p) > t for p in (SRC, os.path.join(INCLUDE, "mxq.h")))
+    srcs = (SOURCES[name], os.path.join(INCLUDE, "mxq_shapes.h")) if name in SOURCES else (SRC, os.path.join(INCLUDE, "mxq.h"))
+    return any(os.path.getmtime(p) > t for p in srcs)
 
 
 if __name__ == "__main__":

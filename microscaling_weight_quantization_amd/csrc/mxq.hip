@@ -45,14 +45,26 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------------------
 // Launch-shape tunables (compile-time).  The defaults are the best of sweeps at
-// 8192 x 8192 bf16 on one MI355X.
+// 8192 x 8192 bf16 on one MI355X, each burst timed after other kernels, after an
+// idle gap and after itself: a one-wave, one-step row lift is the fastest right
+// after another streaming kernel but up to 10% slower after idle or after
+// itself, where 256 lanes of two steps hold steady within 2%.
 // ------------------------------------------------------------------------------------
 // Lanes per workgroup of the streaming kernels.
 #ifndef MXQ_PROJ_THREADS
 #define MXQ_PROJ_THREADS 64       // projection (one wave)
 #endif
 #ifndef MXQ_ROW_THREADS
-#define MXQ_ROW_THREADS 64        // row lift (one wave)
+#define MXQ_ROW_THREADS 256       // row lift
+#endif
+#ifndef MXQ_ROW_GROUPED_THREADS
+#define MXQ_ROW_GROUPED_THREADS 256   // grouped row lift
+#endif
+#ifndef MXQ_ROW_GROUPED_STEPS
+#define MXQ_ROW_GROUPED_STEPS 2
+#endif
+#ifndef MXQ_DEQUANT_GROUPED_STEPS
+#define MXQ_DEQUANT_GROUPED_STEPS 2   // grouped FP8 decode (64 lanes)
 #endif
 #ifndef MXQ_Q4_THREADS
 #define MXQ_Q4_THREADS 256        // MXFP4 encode
@@ -74,7 +86,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_PROJ_STEPS 1
 #endif
 #ifndef MXQ_ROW_STEPS
-#define MXQ_ROW_STEPS 1
+#define MXQ_ROW_STEPS 2
 #endif
 #ifndef MXQ_Q4_STEPS
 #define MXQ_Q4_STEPS 2
@@ -119,6 +131,8 @@ constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSt
               kPackedSteps = MXQ_PACKED_STEPS;
 constexpr int kFusedThreads = MXQ_FUSED_THREADS, kFusedSteps = MXQ_FUSED_STEPS;
 constexpr int kQ4Threads = MXQ_Q4_THREADS, kQ4Steps = MXQ_Q4_STEPS, kDq4Steps = MXQ_DQ4_STEPS;
+constexpr int kRowGroupedThreads = MXQ_ROW_GROUPED_THREADS, kRowGroupedSteps = MXQ_ROW_GROUPED_STEPS,
+              kDequantGroupedSteps = MXQ_DEQUANT_GROUPED_STEPS;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
 static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
@@ -486,9 +500,10 @@ __device__ __forceinline__ void store_code(uint8_t* base, uint32_t off, uint32_t
 
 // Row lift; with kProj it also writes the projection y (the fused one-pass form).
 // Launch shape of the row kernel: the row lift's, or (kProj) the fused pass's.
-template <bool kProj>
+template <bool kProj, bool kGrouped = false>
 struct RowShape {
-  static constexpr int kTPB = kProj ? kFusedThreads : kRowThreads, kSteps = kProj ? kFusedSteps : kRowSteps;
+  static constexpr int kTPB = kGrouped ? kRowGroupedThreads : kProj ? kFusedThreads : kRowThreads;
+  static constexpr int kSteps = kGrouped ? kRowGroupedSteps : kProj ? kFusedSteps : kRowSteps;
 };
 
 // The row lift's steps of workgroup wg (with kProj, also the projection y);
@@ -496,14 +511,14 @@ struct RowShape {
 // FULL: every step of every workgroup is whole and inside the matrix (16-byte
 // path, K a multiple of a step's width, the grid an exact number of steps), so
 // there is no bounds check and nothing to branch around before the first load.
-template <typename T, bool VEC, bool kProj, bool FULL = false>
+template <typename T, bool VEC, bool kProj, bool FULL = false, bool kGrouped = false>
 __device__ __forceinline__ void row_steps(const T* __restrict__ x, int64_t ld_x, int64_t K,
                                           uint8_t* __restrict__ data, uint8_t* __restrict__ scale, int64_t scale_ld,
                                           T* __restrict__ y, int64_t ld_y, MxqDivisor steps_per_row,
                                           uint32_t total_steps, uint32_t wg, const int32_t* __restrict__ noop) {
   static_assert(VEC || !FULL, "the full-step form takes the 16-byte path");
-  using G = StepGeom<T, RowShape<kProj>::kTPB>;
-  constexpr int kRowSteps = RowShape<kProj>::kSteps;
+  using G = StepGeom<T, RowShape<kProj, kGrouped>::kTPB>;
+  constexpr int kRowSteps = RowShape<kProj, kGrouped>::kSteps;
   const uint32_t tid = threadIdx.x;
   const int64_t lane_col = (int64_t)(tid / G::kLPB) * 32 + (tid % G::kLPB) * G::kEPL;
   u32x4 w[kRowSteps];
@@ -611,12 +626,12 @@ struct RowGroupTable {
 static_assert(sizeof(RowGroupTable) <= 3584, "the table must fit the kernel-argument segment");
 
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void row_grouped_kernel(const RowGroupTable tab) {
+__global__ __launch_bounds__(kRowGroupedThreads) void row_grouped_kernel(const RowGroupTable tab) {
   const RowGroupDesc d = tab.g[blockIdx.y];
-  if (blockIdx.x * kRowSteps >= d.total_steps) return;       // uniform: past this weight's steps
+  if (blockIdx.x * kRowGroupedSteps >= d.total_steps) return;   // uniform: past this weight's steps
   keep_denormals();
-  row_steps<T, true, false>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld, nullptr, 0,
-                            d.steps_per_row, d.total_steps, blockIdx.x, nullptr);
+  row_steps<T, true, false, false, true>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld,
+                                         nullptr, 0, d.steps_per_row, d.total_steps, blockIdx.x, nullptr);
 }
 
 // Grouped projection, on the same pattern as the grouped row lift: blockIdx.y
@@ -945,7 +960,7 @@ __device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8])
 // single and grouped kernels both run it.  FULL: every step whole and inside
 // the matrix (aligned rows, K a multiple of a step, an exact grid), so no
 // bounds checks; its stores are buffer stores with the nt bit.
-template <typename TO, bool kE5M2, int kLay, bool VEC, bool FULL = false>
+template <typename TO, bool kE5M2, int kLay, bool VEC, bool FULL = false, int kDequantSteps = ::kDequantSteps>
 __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, const uint8_t* __restrict__ scale,
                                               int64_t scale_ld, int64_t K, TO* __restrict__ out, int64_t ld_out,
                                               MxqDivisor steps_per_row, uint32_t total_steps, uint32_t wg) {
@@ -1116,10 +1131,11 @@ static_assert(sizeof(DequantGroupTable) <= 3584, "the table must fit the kernel-
 template <typename TO, bool kE5M2, int kLay>
 __global__ __launch_bounds__(kDequantThreads) void dequant_grouped_kernel(const DequantGroupTable tab) {
   const DequantGroupDesc d = tab.g[blockIdx.y];
-  if (blockIdx.x * kDequantSteps >= d.total_steps) return;   // uniform: past this weight's steps
+  if (blockIdx.x * kDequantGroupedSteps >= d.total_steps) return;   // uniform: past this weight's steps
   keep_denormals();
-  dequant_steps<TO, kE5M2, kLay, true>(d.data, d.scale, d.scale_ld, d.K, static_cast<TO*>(d.out), d.ld_out,
-                                       d.steps_per_row, d.total_steps, blockIdx.x);
+  dequant_steps<TO, kE5M2, kLay, true, false, kDequantGroupedSteps>(d.data, d.scale, d.scale_ld, d.K,
+                                                                    static_cast<TO*>(d.out), d.ld_out,
+                                                                    d.steps_per_row, d.total_steps, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1207,8 +1223,8 @@ __global__ __launch_bounds__(kQ4Threads) void quantize_mxfp4_grouped_kernel(cons
   const RowGroupDesc d = tab.g[blockIdx.y];
   if (blockIdx.x * kQ4Steps >= d.total_steps) return;       // uniform: past this weight's steps
   keep_denormals();
-  quantize_mxfp4_steps<T, true>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld,
-                                d.steps_per_row, d.total_steps, blockIdx.x);
+  quantize_mxfp4_steps<T, true, false>(static_cast<const T*>(d.x), d.ld_x, d.K, d.data, d.scale, d.scale_ld,
+                                       d.steps_per_row, d.total_steps, blockIdx.x);
 }
 
 // Eight packed nibbles at E8M0 code c -> four bf16 pairs of p * 2^(c-127), with
@@ -1573,14 +1589,22 @@ __global__ __launch_bounds__(kPFoldThreads) void packed_fold_kernel(const uint8_
 
 // ------------------------------------------------------------------------------------
 // Export: strided copy of the first ncols columns of each row, in units of V
-// (16, 4 or 1 bytes, whichever the pointers, strides and width allow).
+// (16, 4 or 1 bytes, whichever the pointers, strides and width allow).  Rows
+// are flattened (one unit per lane), so short rows still fill whole waves.
+// Workgroup order: the dispatcher deals workgroup b to XCD b % 8, each XCD
+// with its own L2, and a padded storage row is not a whole number of 128-byte
+// lines, so neighbouring workgroups share the lines at their boundary.  Chunk c
+// of the grid (rounded up to a multiple of 8) goes to workgroup
+// (c % per) * 8 + c / per with per = grid / 8: XCD x copies the contiguous
+// chunks x * per .. x * per + per - 1, and only the 7 lines between those runs
+// are fetched by two L2s.
 // ------------------------------------------------------------------------------------
 template <typename V>
 __global__ __launch_bounds__(kThreads) void export_kernel(const uint8_t* __restrict__ src, int64_t src_ld,
                                                           uint8_t* __restrict__ dst, MxqDivisor units_per_row,
                                                           uint32_t total_units) {
-  // one V-sized unit per lane, rows flattened, so short rows still fill whole waves
-  const uint64_t i64 = (uint64_t)blockIdx.x * kThreads + threadIdx.x;   // the last group may pass 2^32
+  const uint32_t per = gridDim.x / 8, chunk = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const uint64_t i64 = (uint64_t)chunk * kThreads + threadIdx.x;   // the last chunk may pass 2^32
   if (i64 >= total_units) return;
   const uint32_t i = (uint32_t)i64;
   const uint32_t r = mxq_quot(i, units_per_row), j = i - r * units_per_row.d;
@@ -1821,7 +1845,7 @@ int launch_row_grouped(const mxq_row_group* gs, int64_t n, hipStream_t s) {
   int64_t count = 0, max_w = 0, sum_w = 0;
   auto flush = [&]() -> int {
     if (count == 0) return MXQ_OK;
-    hipLaunchKernelGGL((row_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(kRowThreads), 0, s,
+    hipLaunchKernelGGL((row_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(kRowGroupedThreads), 0, s,
                        tab);
     count = max_w = sum_w = 0;
     return launch_status();
@@ -1836,8 +1860,8 @@ int launch_row_grouped(const mxq_row_group* gs, int64_t n, hipStream_t s) {
     }
     MxqDivisor spr;
     uint32_t total;
-    if (steps_for(g.rows, g.K, StepGeom<T, kRowThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
-    const int64_t gw = grid_for(total, kRowSteps);
+    if (steps_for(g.rows, g.K, StepGeom<T, kRowGroupedThreads>::kElemsPerStep, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t gw = grid_for(total, kRowGroupedSteps);
     const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
     if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
       const int st = flush();
@@ -1954,7 +1978,7 @@ int launch_dequant_grouped_t(const mxq_dequant_group* gs, int64_t n, hipStream_t
     MxqDivisor spr;
     uint32_t total;
     if (steps_for(g.rows, g.K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
-    const int64_t gw = grid_for(total, kDequantSteps);
+    const int64_t gw = grid_for(total, kDequantGroupedSteps);
     const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
     if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
       const int st = flush();
@@ -2254,8 +2278,11 @@ int mxq_mxfp4_to_mxfp8_row_grouped(const mxq_row_group* groups, int64_t n_groups
   if (n_groups < 0) return MXQ_ERR_SHAPE;
   if (n_groups == 0) return MXQ_OK;
   if (!groups) return MXQ_ERR_NULL;
-  const int64_t eps = dt == MXQ_BF16 ? StepGeom<uint16_t, kRowThreads>::kElemsPerStep
-                                     : StepGeom<uint32_t, kRowThreads>::kElemsPerStep;
+  // the smaller step of the grouped kernel and of the single launch an unaligned weight takes: the most steps
+  const int64_t eps = dt == MXQ_BF16 ? std::min(StepGeom<uint16_t, kRowThreads>::kElemsPerStep,
+                                                StepGeom<uint16_t, kRowGroupedThreads>::kElemsPerStep)
+                                     : std::min(StepGeom<uint32_t, kRowThreads>::kElemsPerStep,
+                                                StepGeom<uint32_t, kRowGroupedThreads>::kElemsPerStep);
   // every group on its own, then no output may overlap any other range
   std::vector<std::pair<Range, bool>> iv;                   // (range, is an output)
   iv.reserve((size_t)std::min<int64_t>(n_groups, 1 << 20) * 3);
@@ -2351,7 +2378,8 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
                         : (a % 4 == 0 && scale_ld % 4 == 0 && nb % 4 == 0) ? 4 : 1;
   const int64_t units = rows * (nb / width);
   if (units >= kMaxSteps * 2) return MXQ_ERR_SHAPE;
-  const dim3 grid((uint32_t)((units + kThreads - 1) / kThreads)), block(kThreads);
+  // a multiple of 8 workgroups (the kernel gives each XCD a contiguous run of chunks)
+  const dim3 grid((uint32_t)(((units + kThreads - 1) / kThreads + 7) / 8 * 8)), block(kThreads);
   const MxqDivisor upr = mxq_divisor((uint32_t)(nb / width));
   const uint32_t total = (uint32_t)units;
   if (width == 16)

@@ -1,0 +1,221 @@
+// shapes.hip -- access-shape reference kernels (measurement only; see include/mxq_shapes.h).
+//
+// Each kernel moves the bytes of one of libmxq's kernels over a [rows, K] matrix
+// in the same access pattern -- the same lanes per workgroup, chunks per lane,
+// load and store widths and cache-policy bits, the same barrier -- with a few
+// bit operations in place of the quantization (every output byte depends on the
+// loaded bytes, so no load can be dropped).  Timing a kernel beside its shape
+// separates what the kernel's own instructions cost from what its memory
+// pattern costs on the machine.  Nothing here is on the quantization path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq_shapes.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// A 16-byte chunk folded to 16 / ES bytes (ES = 2: 8 bytes, ES = 4: 4 bytes).
+template <int ES>
+struct Narrow;
+template <>
+struct Narrow<2> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type of(u32x4 w, uint32_t m) { return u32x2{(w[0] ^ (w[1] << 1)) + m, w[2] ^ (w[3] << 1)}; }
+};
+template <>
+struct Narrow<4> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ type of(u32x4 w, uint32_t m) { return (w[0] ^ (w[1] << 1) ^ (w[2] << 2) ^ (w[3] << 3)) + m; }
+};
+
+template <int AUX = 2, typename V>
+__device__ __forceinline__ void store_nt(V v, void* base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  if constexpr (sizeof(V) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, AUX);
+  else if constexpr (sizeof(V) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, AUX);
+  else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, AUX);
+}
+
+// The projection's pattern: 64-lane workgroups, one 16-byte chunk per lane in,
+// one out (nt sc1 stores).  Workgroup b covers bytes [1024 b, 1024 b + 1024).
+__global__ __launch_bounds__(64) void copy16_kernel(const u32x4* __restrict__ in, uint8_t* __restrict__ out) {
+  const u32x4 w = __builtin_nontemporal_load(in + (uint64_t)blockIdx.x * 64 + threadIdx.x);
+  store_nt<2 | 16>(w ^ 0x01010101u, out + (uint64_t)blockIdx.x * 1024, threadIdx.x * 16);
+}
+
+// The row lift's pattern: 256-lane workgroups, two 16-byte chunks per lane
+// (chunks l and 256 + l of the workgroup's 8 KB, both loaded before any store),
+// 16 / ES bytes out per chunk (nt); with CODES also one byte per 32 elements
+// (the lane that holds a block's first chunk), stored with the sc1 bit.
+template <int ES, bool CODES>
+__global__ __launch_bounds__(256) void row_kernel(const u32x4* __restrict__ in, uint8_t* __restrict__ out,
+                                                  uint8_t* __restrict__ codes) {
+  constexpr int kLanesPerBlock = 32 / (16 / ES);   // lanes holding one 32-element block: 4 (2-byte) or 8 (4-byte)
+  const uint32_t t = threadIdx.x;
+  u32x4 w[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) w[u] = __builtin_nontemporal_load(in + (uint64_t)blockIdx.x * 512 + u * 256 + t);
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    uint32_t m = max(max(w[u][0], w[u][1]), max(w[u][2], w[u][3])) >> 24;
+    m = max(m, dpp<0xB1>(m));
+    m = max(m, dpp<0x4E>(m));
+    const uint32_t c = u * 256 + t;                 // the chunk within the workgroup
+    store_nt(Narrow<ES>::of(w[u], m), out + (uint64_t)blockIdx.x * (8192 / ES), c * (16 / ES));
+    if (CODES && t % kLanesPerBlock == 0) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          codes + (uint64_t)blockIdx.x * (512 / kLanesPerBlock), 0, 0x7FFFFFFF, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)m, r, c / kLanesPerBlock, 0, 16);
+    }
+  }
+}
+
+// The row decode's pattern: 64-lane workgroups, 16 / ES payload bytes and one
+// code byte per lane in, 16 bytes out (nt).
+template <int ES>
+__global__ __launch_bounds__(64) void decode_kernel(const uint8_t* __restrict__ in, const uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ out) {
+  constexpr int kIn = 16 / ES;
+  const uint32_t t = threadIdx.x;
+  const uint64_t e0 = ((uint64_t)blockIdx.x * 64 + t) * (16 / ES);     // first element of the lane
+  uint32_t a = 0, b = 0;
+  if constexpr (kIn == 8) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(in + e0));
+    a = v[0], b = v[1];
+  } else {
+    a = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(in + e0));
+  }
+  const uint32_t c = codes[e0 / 32];
+  store_nt(u32x4{a + c, a >> 1, b ^ c, b >> 1}, out + (uint64_t)blockIdx.x * 1024, t * 16);
+}
+
+// The 128x128 fold's pattern: one 1024-lane workgroup per tile, 16-byte chunks,
+// 128 * ES / 16 lanes across a tile row (16 for ES 2, 32 for ES 4), every chunk
+// loaded first, a tile-wide maximum through LDS and a barrier (BARRIER), then
+// 16 / ES bytes out per chunk and one byte per tile.
+template <int ES, bool BARRIER>
+__global__ __launch_bounds__(1024) void tile_kernel(const uint8_t* __restrict__ in, int64_t K, uint8_t* __restrict__ out,
+                                                    uint8_t* __restrict__ codes, uint32_t tiles_per_row) {
+  constexpr int CPT = 128 * ES / 16;         // lanes across one tile row
+  constexpr int RPP = 1024 / CPT;            // tile rows per pass
+  constexpr int P = 128 / RPP;               // chunks per lane
+  __shared__ uint32_t s_max[16];
+  const uint32_t t = threadIdx.x, tr = blockIdx.x / tiles_per_row, tc = blockIdx.x % tiles_per_row;
+  const uint64_t r0 = (uint64_t)tr * 128 + t / CPT, c0 = (uint64_t)tc * 128 + (t % CPT) * (16 / ES);
+  u32x4 w[P];
+#pragma unroll
+  for (int i = 0; i < P; i++)
+    w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in + ((r0 + i * RPP) * K + c0) * ES));
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < P; i++) m = max(m, max(max(w[i][0], w[i][1]), max(w[i][2], w[i][3])) >> 24);
+  m = max(m, dpp<0xB1>(m));
+  m = max(m, dpp<0x4E>(m));
+  m = max(m, dpp<0x141>(m));
+  m = max(m, dpp<0x140>(m));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+  if constexpr (BARRIER) {
+    if ((t & 63u) == 0) s_max[t >> 6] = m;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; v++) m = max(m, s_max[v]);
+  }
+#pragma unroll
+  for (int i = 0; i < P; i++) store_nt(Narrow<ES>::of(w[i], m), out + (r0 + i * RPP) * K, (uint32_t)c0);
+  if (t == 0) codes[blockIdx.x] = (uint8_t)m;
+}
+
+// The fold's workgroup (1024 lanes, two 16-byte chunks per lane: chunks l and
+// 1024 + l of the workgroup's 32 KB) over a plain contiguous stream, with or
+// without the barrier.
+template <int ES, bool BARRIER>
+__global__ __launch_bounds__(1024) void linear_kernel(const u32x4* __restrict__ in, uint8_t* __restrict__ out) {
+  __shared__ uint32_t s_max[16];
+  const uint32_t t = threadIdx.x;
+  const uint64_t c = (uint64_t)blockIdx.x * 2048 + t;
+  const u32x4 a = __builtin_nontemporal_load(in + c), b = __builtin_nontemporal_load(in + c + 1024);
+  uint32_t m = max(max(a[0], a[3]), max(b[1], b[2])) >> 24;
+  m = max(m, dpp<0xB1>(m));
+  m = max(m, dpp<0x4E>(m));
+  if constexpr (BARRIER) {
+    if ((t & 63u) == 0) s_max[t >> 6] = m;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; v++) m = max(m, s_max[v]);
+  }
+  uint8_t* o = out + (uint64_t)blockIdx.x * 2048 * (16 / ES);
+  store_nt(Narrow<ES>::of(a, m), o, t * (16 / ES));
+  store_nt(Narrow<ES>::of(b, m), o, (1024 + t) * (16 / ES));
+}
+
+int status() { return hipGetLastError() == hipSuccess ? 0 : 2; }
+
+template <int ES>
+int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t K, hipStream_t s) {
+  const int64_t bytes = rows * K * ES;                       // input bytes
+  const uint32_t chunks = (uint32_t)(bytes / 16);
+  switch (shape) {
+    case MXQ_SHAPE_COPY16:
+      if (bytes % 1024) return 1;
+      hipLaunchKernelGGL(copy16_kernel, dim3(chunks / 64), dim3(64), 0, s, (const u32x4*)in, (uint8_t*)out);
+      return status();
+    case MXQ_SHAPE_ROW:
+    case MXQ_SHAPE_ROW_CODES:
+      if (bytes % 8192) return 1;
+      if (shape == MXQ_SHAPE_ROW)
+        hipLaunchKernelGGL((row_kernel<ES, false>), dim3(chunks / 512), dim3(256), 0, s, (const u32x4*)in,
+                           (uint8_t*)out, (uint8_t*)codes);
+      else
+        hipLaunchKernelGGL((row_kernel<ES, true>), dim3(chunks / 512), dim3(256), 0, s, (const u32x4*)in,
+                           (uint8_t*)out, (uint8_t*)codes);
+      return status();
+    case MXQ_SHAPE_DECODE:
+      if ((rows * K) % (64 * (16 / ES))) return 1;
+      hipLaunchKernelGGL((decode_kernel<ES>), dim3((uint32_t)(rows * K / (64 * (16 / ES)))), dim3(64), 0, s,
+                         (const uint8_t*)in, (const uint8_t*)codes, (uint8_t*)out);
+      return status();
+    case MXQ_SHAPE_TILE:
+    case MXQ_SHAPE_TILE_NO_BARRIER: {
+      if (rows % 128 || K % 128) return 1;
+      const uint32_t tpr = (uint32_t)(K / 128), tiles = (uint32_t)(rows / 128) * tpr;
+      if (shape == MXQ_SHAPE_TILE)
+        hipLaunchKernelGGL((tile_kernel<ES, true>), dim3(tiles), dim3(1024), 0, s, (const uint8_t*)in, K, (uint8_t*)out,
+                           (uint8_t*)codes, tpr);
+      else
+        hipLaunchKernelGGL((tile_kernel<ES, false>), dim3(tiles), dim3(1024), 0, s, (const uint8_t*)in, K,
+                           (uint8_t*)out, (uint8_t*)codes, tpr);
+      return status();
+    }
+    case MXQ_SHAPE_LINEAR1024:
+    case MXQ_SHAPE_LINEAR1024_NO_BARRIER:
+      if (bytes % 32768) return 1;
+      if (shape == MXQ_SHAPE_LINEAR1024)
+        hipLaunchKernelGGL((linear_kernel<ES, true>), dim3(chunks / 2048), dim3(1024), 0, s, (const u32x4*)in,
+                           (uint8_t*)out);
+      else
+        hipLaunchKernelGGL((linear_kernel<ES, false>), dim3(chunks / 2048), dim3(1024), 0, s, (const u32x4*)in,
+                           (uint8_t*)out);
+      return status();
+    default:
+      return 1;
+  }
+}
+
+}  // namespace
+
+extern "C" int mxq_shape_run(int shape, int element_size, const void* in, void* out, void* codes, int64_t rows,
+                             int64_t K, hipStream_t stream) {
+  if (!in || !out || !codes || rows <= 0 || K <= 0 || rows * K >= ((int64_t)1 << 34)) return 1;
+  if (element_size == 2) return run<2>(shape, in, out, codes, rows, K, stream);
+  if (element_size == 4) return run<4>(shape, in, out, codes, rows, K, stream);
+  return 1;
+}

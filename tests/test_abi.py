@@ -363,3 +363,30 @@ def test_grouped_mxfp4_encode_host_validation(lib):
     assert call(a, grp(0x110000, 0x210000, 0x300010)) == mxq.MXQ_ERR_ALIAS      # code arrays overlap
     assert call(grp(0x100000, 0x100100, 0x300000)) == mxq.MXQ_ERR_ALIAS         # a single weight's own overlap
     assert call(grp(None, None, None, rows=0), grp(None, None, None, K=0)) == mxq.MXQ_OK
+
+
+def test_access_shape_library_loads_and_refuses_bad_arguments():
+    """libmxq_shapes.so (measurement only) exports the one entry point
+    include/mxq_shapes.h declares, the header compiles as C, and the call
+    turns down what does not fit before anything is launched."""
+    name = "libmxq_shapes.so"
+    if B.stale(name):
+        B.build([name])
+    path = B.library_path(name)
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    assert set(re.findall(r"\sT\s+(mxq_\w+)$", out, flags=re.M)) == {"mxq_shape_run"}
+    header = os.path.join(B.ROOT, "include", "mxq_shapes.h")
+    src = '#include "mxq_shapes.h"\nint main(void) { return MXQ_SHAPE_LINEAR1024_NO_BARRIER == 7 ? 0 : 1; }\n'
+    r = subprocess.run(["gcc", "-fsyntax-only", "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(header),
+                        "-I", "/opt/rocm/include", "-x", "c", "-"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    L = ctypes.CDLL(path)
+    L.mxq_shape_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    fake = ctypes.c_void_p(0x100000)
+    assert L.mxq_shape_run(0, 2, None, fake, fake, 8, 512, None) == 1          # null input
+    assert L.mxq_shape_run(0, 3, fake, fake, fake, 8, 512, None) == 1          # element size
+    assert L.mxq_shape_run(99, 2, fake, fake, fake, 8, 512, None) == 1         # no such shape
+    assert L.mxq_shape_run(1, 2, fake, fake, fake, 1, 64, None) == 1           # not whole workgroups
+    assert L.mxq_shape_run(4, 2, fake, fake, fake, 100, 128, None) == 1        # rows not tiles
+    assert L.mxq_shape_run(0, 2, fake, fake, fake, 0, 512, None) == 1          # empty
