@@ -147,8 +147,9 @@ def _oracle_pass(bits, threads: int) -> dict:
 
 def host_cpu() -> dict:
     """The host's CPU as /proc/cpuinfo and the scheduler report it: the model
-    string, logical CPUs, physical cores (distinct (package, core) pairs) and
-    the CPUs this process may run on (its affinity set)."""
+    string, logical CPUs, physical cores (distinct (package, core) pairs), the
+    CPUs this process may run on (its affinity set) and the cgroup's CPU
+    quota, which caps the time all its threads together may use."""
     model, cores, cur = "unknown", set(), {}
     try:
         with open("/proc/cpuinfo") as f:
@@ -167,7 +168,14 @@ def host_cpu() -> dict:
     except OSError:
         pass
     usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    return {"model": model, "logical": os.cpu_count(), "physical": len(cores) or None, "usable": usable}
+    quota = None                                   # the cgroup's CPU quota in CPUs (cgroup v2 cpu.max), if any
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        quota = None if q == "max" else round(int(q) / int(period), 2)
+    except (OSError, ValueError):
+        pass
+    return {"model": model, "logical": os.cpu_count(), "physical": len(cores) or None, "usable": usable,
+            "cgroup_cpu_quota": quota}
 
 
 def cpu_baseline(bits, threads: int, cpu_seconds: float = 12.0, max_passes: int = 8):

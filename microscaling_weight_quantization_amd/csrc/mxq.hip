@@ -69,6 +69,32 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_Q4_THREADS
 #define MXQ_Q4_THREADS 256        // MXFP4 encode
 #endif
+// Consecutive workgroups per XCD run (see xcd_run): the row-layout FP8 decode
+// and the row lift from packed MXFP4, whose neighbouring workgroups read (and,
+// for the latter, write) parts of one line of block codes.  Runs remove the
+// duplicate code-line fetches (L2 fetch bytes 1.21x -> 1.00x of the decode's
+// reads at 8 per run, 1.20x -> 1.03x for the packed lift at 4) but cost time
+// (decode 32.4 -> 34.9 us, packed lift 18.6 -> 20.9 us at 8192 x 8192), so the
+// plain order (1) is the default.
+// Code stores of the full-step row lift: 1 = the first lane of each 16-lane
+// row gathers that row's 16 / lanes-per-block codes and stores them with one
+// 4-byte (bf16) or 2-byte (fp32) store; 0 = one byte store per block (sc1).
+// AUX is the gathered stores' cache-policy field.  At 8192 x 8192 bf16 the
+// gathered plain stores took the row lift from 33.7-34.0 us to 33.1-33.5 us
+// (sc1: unchanged, nt: 34.1-34.6); the fused projection + row lift was 0.3 us
+// slower with them and keeps the byte stores.
+#ifndef MXQ_ROW_CODE_WORDS
+#define MXQ_ROW_CODE_WORDS 1
+#endif
+#ifndef MXQ_ROW_CODE_AUX
+#define MXQ_ROW_CODE_AUX 0
+#endif
+#ifndef MXQ_DEQUANT_XCD_RUN
+#define MXQ_DEQUANT_XCD_RUN 1
+#endif
+#ifndef MXQ_PACKED_XCD_RUN
+#define MXQ_PACKED_XCD_RUN 1
+#endif
 #ifndef MXQ_FUSED_THREADS
 #define MXQ_FUSED_THREADS 64      // fused projection + row lift
 #endif
@@ -133,6 +159,7 @@ constexpr int kFusedThreads = MXQ_FUSED_THREADS, kFusedSteps = MXQ_FUSED_STEPS;
 constexpr int kQ4Threads = MXQ_Q4_THREADS, kQ4Steps = MXQ_Q4_STEPS, kDq4Steps = MXQ_DQ4_STEPS;
 constexpr int kRowGroupedThreads = MXQ_ROW_GROUPED_THREADS, kRowGroupedSteps = MXQ_ROW_GROUPED_STEPS,
               kDequantGroupedSteps = MXQ_DEQUANT_GROUPED_STEPS;
+constexpr int kDequantXcdRun = MXQ_DEQUANT_XCD_RUN, kPackedXcdRun = MXQ_PACKED_XCD_RUN;
 constexpr int kPFoldRows = MXQ_PFOLD_ROWS, kPFoldThreads = 4096 / kPFoldRows;   // 128 rows x 32 chunks
 static_assert(kPFoldRows * kPFoldThreads == 4096 && kPFoldThreads >= 256, "packed fold geometry");
 constexpr int kColThreads = MXQ_COL_THREADS, kColRows = MXQ_COL_ROWS, kColGroups = 32 / kColRows;
@@ -498,6 +525,31 @@ __device__ __forceinline__ void store_code(uint8_t* base, uint32_t off, uint32_t
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, r, off, 0, 16);   // sc1
 }
 
+// The block codes of a 16-lane row, gathered into its first lane: with kLPB
+// lanes per block the row holds 16 / kLPB blocks, whose codes sit in lanes 0,
+// kLPB, 2 kLPB, ...; row_shl:n moves lane i + n's value to lane i.  Lane 0's
+// result packs them lowest block first (little-endian: the code bytes in
+// storage order).  Only the row's first lane's value is meaningful.
+template <int kLPB>
+__device__ __forceinline__ uint32_t row_codes(uint32_t code) {
+  static_assert(kLPB == 4 || kLPB == 8, "4 (bf16) or 8 (fp32) lanes per block");
+  if constexpr (kLPB == 4)
+    return code | (dpp<0x104>(code) << 8) | (dpp<0x108>(code) << 16) | (dpp<0x10C>(code) << 24);
+  else
+    return code | (dpp<0x108>(code) << 8);
+}
+
+// Store of a 16-lane row's gathered codes (4 bytes for kLPB 4, 2 bytes for 8)
+// at byte offset off of base; off and base aligned to the store's width.
+template <int kLPB>
+__device__ __forceinline__ void store_row_codes(uint8_t* base, uint32_t off, uint32_t codes) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+  if constexpr (kLPB == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(codes, r, off, 0, MXQ_ROW_CODE_AUX);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)codes, r, off, 0, MXQ_ROW_CODE_AUX);
+}
+
 // Row lift; with kProj it also writes the projection y (the fused one-pass form).
 // Launch shape of the row kernel: the row lift's, or (kProj) the fused pass's.
 template <bool kProj, bool kGrouped = false>
@@ -550,7 +602,13 @@ __device__ __forceinline__ void row_steps(const T* __restrict__ x, int64_t ld_x,
           stream_store_row_sc1(proj_chunk<T>(p, b.poison), y + (int64_t)row * ld_y, (uint32_t)(K * sizeof(T)),
                                (uint32_t)(col0 * sizeof(T)));
         stream_store_at(payload_chunk<T>(p, code, b.poison), data + (int64_t)row * K, (uint32_t)col0);
-        if (tid % G::kLPB == 0) store_code(scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep, tid / G::kLPB, code);
+        uint8_t* const crow = scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep;
+        if constexpr (MXQ_ROW_CODE_WORDS && !kProj) {
+          const uint32_t codes = row_codes<G::kLPB>(code);
+          if (tid % 16 == 0) store_row_codes<G::kLPB>(crow, tid / G::kLPB, codes);
+        } else {
+          if (tid % G::kLPB == 0) store_code(crow, tid / G::kLPB, code);
+        }
       } else {
         // the projection output goes out like the projection kernel's (nt sc1 buffer stores)
         if constexpr (kProj) store_chunk<T, VEC, true>(y + (int64_t)row * ld_y, col0, K, proj_chunk<T>(p, b.poison));
@@ -956,6 +1014,25 @@ __device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8])
                bf16_pair_of_fp8_each<kE5M2, false>(q[1], s[4], s[5]), bf16_pair_of_fp8_each<kE5M2, true>(q[1], s[6], s[7])};
 }
 
+// Workgroup order for kernels whose neighbouring workgroups share lines of
+// block codes.  The dispatcher deals workgroup b to XCD b % 8, and each XCD has
+// its own L2, so in the plain order a code line that M neighbouring workgroups
+// read is fetched by M L2s.  With M > 1, each run of 8 M workgroups is
+// reordered so that XCD x takes the M consecutive logical workgroups
+// 8 M g + M x .. 8 M g + M x + M - 1; the last, partial run keeps the plain
+// order.  A permutation of 0 .. n - 1.
+template <int M>
+__device__ __forceinline__ uint32_t xcd_run(uint32_t b, uint32_t n) {
+  if constexpr (M == 1) {
+    return b;
+  } else {
+    constexpr uint32_t G = 8u * M;
+    if (b >= n - n % G) return b;
+    const uint32_t r = b % G;
+    return b - r + (r % 8u) * M + r / 8u;
+  }
+}
+
 // The decode's body: workgroup wg's kDequantSteps steps of one weight.  The
 // single and grouped kernels both run it.  FULL: every step whole and inside
 // the matrix (aligned rows, K a multiple of a step, an exact grid), so no
@@ -1108,7 +1185,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t*
                                                            MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
   dequant_steps<TO, kE5M2, kLay, VEC, FULL>(data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps,
-                                            blockIdx.x);
+                                            xcd_run<kLay == kLayRow ? kDequantXcdRun : 1>(blockIdx.x, gridDim.x));
 }
 
 // Grouped decode, on the grouped row lift's pattern: blockIdx.y is the weight,
@@ -1379,7 +1456,7 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
                                                                   uint8_t* __restrict__ code_out, int64_t code_ld,
                                                                   MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
-  const uint32_t tid = threadIdx.x;
+  const uint32_t tid = threadIdx.x, wg = xcd_run<kPackedXcdRun>(blockIdx.x, gridDim.x);
   const int64_t lane_col = (int64_t)tid * 16, pw = (K + 1) / 2;
   // All of the workgroup's loads are issued before any conversion or store.
   u32x2 f[kPackedSteps];
@@ -1388,7 +1465,7 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
   for (int u = 0; u < kPackedSteps; u++) {
     f[u] = u32x2{0u, 0u};
     c[u] = 0u;
-    const uint32_t step = blockIdx.x * kPackedSteps + u;
+    const uint32_t step = wg * kPackedSteps + u;
     if (!FULL && step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
@@ -1404,7 +1481,7 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
   }
 #pragma unroll
   for (int u = 0; u < kPackedSteps; u++) {
-    const uint32_t step = blockIdx.x * kPackedSteps + u;
+    const uint32_t step = wg * kPackedSteps + u;
     if (!FULL && step >= total_steps) break;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kPackedThreads * 16) + lane_col;
@@ -1690,8 +1767,10 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL) &&
                    (!fused || (aligned(y, 16) && ld_y % EPL == 0 && fits32(K * (int64_t)sizeof(T))));
   // every step whole and every workgroup's steps inside the grid: no bounds checks
+  // (and, for the gathered code stores, scale rows aligned to their width: 16 / kLPB bytes)
+  const int code_width = MXQ_ROW_CODE_WORDS && !fused ? 16 / Fmt<T>::kLPB : 1;
   const bool full = vec && spr.d * (int64_t)((tpb / Fmt<T>::kLPB) * 32) == K && total % steps == 0 &&
-                    fits32(K * (int64_t)sizeof(T));
+                    fits32(K * (int64_t)sizeof(T)) && aligned(scale, code_width) && scale_ld % code_width == 0;
   const dim3 grid(grid_for(total, steps)), block(tpb);
 #define MXQ_ROW_LAUNCH(V, P, F)                                                                                  \
   hipLaunchKernelGGL((row_kernel<T, V, P, F>), grid, block, 0, s, (const T*)x, ld_x, K, data, scale, scale_ld, \

@@ -421,6 +421,30 @@ def test_strided_and_misaligned_views(dev, dtype):
         assert_bits(to_host(y), oracle.fake_quantize_mxfp4(bits), f"proj into strided y off={off}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_row_code_storage_alignment(dev, dtype):
+    """Whole-step rows (K = two steps of the row lift) with the code storage at
+    every alignment: a base pointer 0-3 bytes off and row strides nb .. nb + 4.
+    The full-step row lift gathers a 16-lane row's codes into one 4-byte (bf16)
+    or 2-byte (fp32) store where the storage is aligned to that width, and
+    stores bytes otherwise; each against the oracle, padding untouched."""
+    src = W.c2_planted() if dtype == "bf16" else W.c2_planted_fp32()
+    rows, K = 64, 4096
+    bits = np.ascontiguousarray(np.resize(src.reshape(-1), rows * K).reshape(rows, K))
+    x = to_dev(bits, dev)
+    nb = K // 32
+    wd, ws = oracle.mxfp4_to_mxfp8_row(bits, threads=THREADS)
+    for off in (0, 1, 2, 3):
+        for ld in (nb, nb + 1, nb + 2, nb + 4):
+            buf = torch.full((rows * ld + 8,), 0x5A, dtype=torch.uint8, device=dev)
+            scale = buf[off:off + rows * ld].view(rows, ld)[:, :nb]
+            data, _ = mxq.mxq_mxfp4_to_mxfp8_row(x, scale=scale)
+            want = np.full(rows * ld + 8, 0x5A, np.uint8)
+            want[off:off + rows * ld].reshape(rows, ld)[:, :nb] = ws
+            assert_bits(to_host(data), wd, f"payload off={off} ld={ld}")
+            assert_bits(to_host(buf), want, f"codes off={off} ld={ld}")
+
+
 def test_in_place_projection(dev):
     bits = W.c1_small()
     x = to_dev(bits, dev)
