@@ -126,8 +126,16 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_FUSED_STEPS
 #define MXQ_FUSED_STEPS 1
 #endif
-#ifndef MXQ_DEQUANT_STEPS
-#define MXQ_DEQUANT_STEPS 1
+// FP8 decodes: to bf16, two steps (row layout 32.7-33.0 us at 8192 x 8192 in
+// every order; one step ran 32.2 after the fold but 36.0 after itself); to
+// fp32, one step (tile layout at 28672 x 8192: 186 us against 196 with two).
+// A check-free form with buffer stores was tried for both and was slower or
+// less steady (fp32 tile layout at 28672 x 8192: 200 us).
+#ifndef MXQ_DEQUANT_STEPS_BF16
+#define MXQ_DEQUANT_STEPS_BF16 2
+#endif
+#ifndef MXQ_DEQUANT_STEPS_FP32
+#define MXQ_DEQUANT_STEPS_FP32 1
 #endif
 #ifndef MXQ_DQ4_STEPS
 #define MXQ_DQ4_STEPS 2           // packed MXFP4 decode
@@ -159,8 +167,12 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;     // 4 waves: workgroup size of the remaining streaming kernels
 constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS, kDequantThreads = MXQ_DEQUANT_THREADS,
               kDq4Threads = MXQ_DQ4_THREADS, kPackedThreads = MXQ_PACKED_THREADS;
-constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kDequantSteps = MXQ_DEQUANT_STEPS,
-              kPackedSteps = MXQ_PACKED_STEPS;
+constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kPackedSteps = MXQ_PACKED_STEPS;
+// Steps per workgroup of the single FP8 decode, by output type.
+template <typename TO>
+struct DequantSteps {
+  static constexpr int value = sizeof(TO) == 2 ? MXQ_DEQUANT_STEPS_BF16 : MXQ_DEQUANT_STEPS_FP32;
+};
 constexpr int kFusedThreads = MXQ_FUSED_THREADS, kFusedSteps = MXQ_FUSED_STEPS;
 constexpr int kQ4Threads = MXQ_Q4_THREADS, kQ4Steps = MXQ_Q4_STEPS, kDq4Steps = MXQ_DQ4_STEPS;
 constexpr int kRowGroupedThreads = MXQ_ROW_GROUPED_THREADS, kRowGroupedSteps = MXQ_ROW_GROUPED_STEPS,
@@ -1049,10 +1061,8 @@ __device__ __forceinline__ uint32_t xcd_run(uint32_t b, uint32_t n) {
 }
 
 // The decode's body: workgroup wg's kDequantSteps steps of one weight.  The
-// single and grouped kernels both run it.  FULL: every step whole and inside
-// the matrix (aligned rows, K a multiple of a step, an exact grid), so no
-// bounds checks; its stores are buffer stores with the nt bit.
-template <typename TO, bool kE5M2, int kLay, bool VEC, bool FULL = false, int kDequantSteps = ::kDequantSteps>
+// single and grouped kernels both run it.
+template <typename TO, bool kE5M2, int kLay, bool VEC, int kDequantSteps>
 __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, const uint8_t* __restrict__ scale,
                                               int64_t scale_ld, int64_t K, TO* __restrict__ out, int64_t ld_out,
                                               MxqDivisor steps_per_row, uint32_t total_steps, uint32_t wg) {
@@ -1078,16 +1088,16 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
     if constexpr (kSplit) cs_b[u] = 0u;
     if constexpr (kLay == kLayCol) ccs[u] = u32x2{0u, 0u};
     const uint32_t step = wg * kDequantSteps + u;
-    if (!FULL && step >= total_steps) continue;
+    if (step >= total_steps) continue;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
-    if (!FULL && col0 >= K) continue;
+    if (col0 >= K) continue;
     const uint8_t* drow = data + (int64_t)row * K;
     if constexpr (kSplit) {
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         const int64_t c = col0 + h * kHalf;
-        if (!FULL && c >= K) continue;
+        if (c >= K) continue;
         if (VEC) {
           qs[u][h] = stream_load(reinterpret_cast<const uint32_t*>(drow + c));
         } else {
@@ -1133,10 +1143,10 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
 #pragma unroll
   for (int u = 0; u < kDequantSteps; u++) {
     const uint32_t step = wg * kDequantSteps + u;
-    if (!FULL && step >= total_steps) break;
+    if (step >= total_steps) break;
     const uint32_t row = mxq_quot(step, steps_per_row), seg = step - row * steps_per_row.d;
     const int64_t col0 = (int64_t)seg * (kDequantThreads * 8) + lane_col;
-    if (!FULL && col0 >= K) continue;
+    if (col0 >= K) continue;
     const u32x2 q = qs[u];
     float s8[8];
 #pragma unroll
@@ -1158,9 +1168,7 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
           if ((h & 0x7FFFu) > 0x7F80u) o[i / 2] = (o[i / 2] & ~(0xFFFFu << (16 * (i % 2)))) | (0x7FC0u << (16 * (i % 2)));
         }
       }
-      if constexpr (FULL) {
-        stream_store_at(o, orow, (uint32_t)(col0 * sizeof(TO)));
-      } else if (VEC) {
+      if (VEC) {
         stream_store(o, reinterpret_cast<u32x4*>(orow + col0));
       } else {
         for (int i = 0; i < 8; i++)
@@ -1177,10 +1185,7 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
           if ((f[i] & 0x7FFFFFFFu) > 0x7F800000u) f[i] = 0x7FC00000u;
       }
       // the two groups: elements col0 .. col0+3 and col0+kHalf .. col0+kHalf+3
-      if constexpr (FULL) {
-        stream_store_at(u32x4{f[0], f[1], f[2], f[3]}, orow, (uint32_t)(col0 * sizeof(TO)));
-        stream_store_at(u32x4{f[4], f[5], f[6], f[7]}, orow, (uint32_t)((col0 + kHalf) * sizeof(TO)));
-      } else if (VEC) {
+      if (VEC) {
         stream_store(u32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<u32x4*>(orow + col0));
         if (col0 + kHalf < K) stream_store(u32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<u32x4*>(orow + col0 + kHalf));
       } else {
@@ -1193,14 +1198,15 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
   }
 }
 
-template <typename TO, bool kE5M2, int kLay, bool VEC, bool FULL>
+template <typename TO, bool kE5M2, int kLay, bool VEC>
 __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
                                                            MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
-  dequant_steps<TO, kE5M2, kLay, VEC, FULL>(data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps,
-                                            xcd_run<kLay == kLayRow ? kDequantXcdRun : 1>(blockIdx.x, gridDim.x));
+  dequant_steps<TO, kE5M2, kLay, VEC, DequantSteps<TO>::value>(
+      data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps,
+      xcd_run<kLay == kLayRow ? kDequantXcdRun : 1>(blockIdx.x, gridDim.x));
 }
 
 // Grouped decode, on the grouped row lift's pattern: blockIdx.y is the weight,
@@ -1225,7 +1231,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_grouped_kernel(const 
   const DequantGroupDesc d = tab.g[blockIdx.y];
   if (blockIdx.x * kDequantGroupedSteps >= d.total_steps) return;   // uniform: past this weight's steps
   keep_denormals();
-  dequant_steps<TO, kE5M2, kLay, true, false, kDequantGroupedSteps>(d.data, d.scale, d.scale_ld, d.K,
+  dequant_steps<TO, kE5M2, kLay, true, kDequantGroupedSteps>(d.data, d.scale, d.scale_ld, d.K,
                                                                     static_cast<TO*>(d.out), d.ld_out,
                                                                     d.steps_per_row, d.total_steps, blockIdx.x);
 }
@@ -1858,18 +1864,12 @@ int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
   const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0 &&
                    (kLay != kLayCol || (aligned(scale, 8) && scale_ld % 8 == 0));
-  // every step whole and every workgroup's steps inside the grid: no bounds checks
-  const bool full = vec && spr.d * (int64_t)(kDequantThreads * 8) == K && total % kDequantSteps == 0 &&
-                    fits32(K * (int64_t)sizeof(TO));
-  const dim3 grid(grid_for(total, kDequantSteps)), block(kDequantThreads);
-  if (full)
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true, true>), grid, block, 0, s, data, scale, scale_ld, K,
-                       (TO*)out, ld_out, spr, total);
-  else if (vec)
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true, false>), grid, block, 0, s, data, scale, scale_ld, K,
+  const dim3 grid(grid_for(total, DequantSteps<TO>::value)), block(kDequantThreads);
+  if (vec)
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
   else
-    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, false, false>), grid, block, 0, s, data, scale, scale_ld, K,
+    hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, false>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
   return launch_status();
 }
