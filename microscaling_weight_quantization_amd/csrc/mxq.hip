@@ -86,8 +86,14 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_ROW_CODE_WORDS
 #define MXQ_ROW_CODE_WORDS 1
 #endif
-#ifndef MXQ_ROW_CODE_AUX
-#define MXQ_ROW_CODE_AUX 0
+#ifndef MXQ_CODE_AUX
+#define MXQ_CODE_AUX 0
+#endif
+#ifndef MXQ_Q4_CODE_WORDS
+#define MXQ_Q4_CODE_WORDS 1       // the same for the full-step MXFP4 encode
+#endif
+#ifndef MXQ_PACKED_CODE_WORDS
+#define MXQ_PACKED_CODE_WORDS 1   // and the full-step row lift from packed MXFP4 (4 codes per 8 lanes)
 #endif
 // The fold's check-free form for whole tile groups, for fp32 weights: 52.1 us
 // against 52.5 at 8192 x 8192.  For bf16 it was slower (35.2-35.4 us against
@@ -543,30 +549,33 @@ __device__ __forceinline__ void store_code(uint8_t* base, uint32_t off, uint32_t
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, r, off, 0, 16);   // sc1
 }
 
-// The block codes of a 16-lane row, gathered into its first lane: with kLPB
-// lanes per block the row holds 16 / kLPB blocks, whose codes sit in lanes 0,
-// kLPB, 2 kLPB, ...; row_shl:n moves lane i + n's value to lane i.  Lane 0's
-// result packs them lowest block first (little-endian: the code bytes in
-// storage order).  Only the row's first lane's value is meaningful.
+// Gathered code stores.  With kLPB lanes per block (2, 4 or 8), the codes of
+// kCodes consecutive blocks sit in lanes l, l + kLPB, ... of a group of kLanes
+// lanes inside one 16-lane DPP row (row_shl:n moves lane i + n's value to
+// lane i).  gather() packs them into the group's first lane, lowest block
+// first (little-endian: the code bytes in storage order); every lane must run
+// it, and only the first lane's value is meaningful.  store() is that lane's
+// one kCodes-byte store at byte offset off of base (both aligned to kCodes).
 template <int kLPB>
-__device__ __forceinline__ uint32_t row_codes(uint32_t code) {
-  static_assert(kLPB == 4 || kLPB == 8, "4 (bf16) or 8 (fp32) lanes per block");
-  if constexpr (kLPB == 4)
-    return code | (dpp<0x104>(code) << 8) | (dpp<0x108>(code) << 16) | (dpp<0x10C>(code) << 24);
-  else
-    return code | (dpp<0x108>(code) << 8);
-}
-
-// Store of a 16-lane row's gathered codes (4 bytes for kLPB 4, 2 bytes for 8)
-// at byte offset off of base; off and base aligned to the store's width.
-template <int kLPB>
-__device__ __forceinline__ void store_row_codes(uint8_t* base, uint32_t off, uint32_t codes) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
-  if constexpr (kLPB == 4)
-    __builtin_amdgcn_raw_buffer_store_b32(codes, r, off, 0, MXQ_ROW_CODE_AUX);
-  else
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)codes, r, off, 0, MXQ_ROW_CODE_AUX);
-}
+struct CodeGather {
+  static_assert(kLPB == 2 || kLPB == 4 || kLPB == 8, "2, 4 or 8 lanes per block");
+  static constexpr int kCodes = kLPB == 8 ? 2 : 4, kLanes = kCodes * kLPB;
+  static __device__ __forceinline__ uint32_t gather(uint32_t code) {
+    if constexpr (kLPB == 2)
+      return code | (dpp<0x102>(code) << 8) | (dpp<0x104>(code) << 16) | (dpp<0x106>(code) << 24);
+    else if constexpr (kLPB == 4)
+      return code | (dpp<0x104>(code) << 8) | (dpp<0x108>(code) << 16) | (dpp<0x10C>(code) << 24);
+    else
+      return code | (dpp<0x108>(code) << 8);
+  }
+  static __device__ __forceinline__ void store(uint8_t* base, uint32_t off, uint32_t codes) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
+    if constexpr (kCodes == 4)
+      __builtin_amdgcn_raw_buffer_store_b32(codes, r, off, 0, MXQ_CODE_AUX);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)codes, r, off, 0, MXQ_CODE_AUX);
+  }
+};
 
 // Row lift; with kProj it also writes the projection y (the fused one-pass form).
 // Launch shape of the row kernel: the row lift's, or (kProj) the fused pass's.
@@ -622,8 +631,9 @@ __device__ __forceinline__ void row_steps(const T* __restrict__ x, int64_t ld_x,
         stream_store_at(payload_chunk<T>(p, code, b.poison), data + (int64_t)row * K, (uint32_t)col0);
         uint8_t* const crow = scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep;
         if constexpr (MXQ_ROW_CODE_WORDS && !kProj) {
-          const uint32_t codes = row_codes<G::kLPB>(code);
-          if (tid % 16 == 0) store_row_codes<G::kLPB>(crow, tid / G::kLPB, codes);
+          using CG = CodeGather<G::kLPB>;
+          const uint32_t codes = CG::gather(code);
+          if (tid % CG::kLanes == 0) CG::store(crow, tid / G::kLPB, codes);
         } else {
           if (tid % G::kLPB == 0) store_code(crow, tid / G::kLPB, code);
         }
@@ -1286,8 +1296,15 @@ __device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, in
       const uint32_t f = b.poison ? 0u : fp4_of(w[u], e8m0(b.eb), T{});
       if constexpr (FULL) {
         stream_store_at((N)f, packed + (int64_t)row * pw, (uint32_t)(col0 / 2));
-        if (tid % G::kLPB == 0)
-          store_code(scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep, tid / G::kLPB, b.poison ? 255u : b.eb);
+        uint8_t* const crow = scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep;
+        const uint32_t code = b.poison ? 255u : b.eb;
+        if constexpr (MXQ_Q4_CODE_WORDS) {
+          using CG = CodeGather<G::kLPB>;
+          const uint32_t codes = CG::gather(code);
+          if (tid % CG::kLanes == 0) CG::store(crow, tid / G::kLPB, codes);
+        } else {
+          if (tid % G::kLPB == 0) store_code(crow, tid / G::kLPB, code);
+        }
         continue;
       }
       if (col0 < K) {
@@ -1517,7 +1534,14 @@ __global__ __launch_bounds__(kPackedThreads) void packed_convert_kernel(const ui
     uint8_t* drow = data + (int64_t)row * K;
     if constexpr (FULL) {
       stream_store_at(q, drow, (uint32_t)col0);
-      if (tid % 2 == 0) store_code(code_out + (int64_t)row * code_ld + seg * (kPackedThreads / 2), tid / 2, code);
+      uint8_t* const crow = code_out + (int64_t)row * code_ld + seg * (kPackedThreads / 2);
+      if constexpr (MXQ_PACKED_CODE_WORDS) {
+        using CG = CodeGather<2>;
+        const uint32_t codes = CG::gather(code);
+        if (tid % CG::kLanes == 0) CG::store(crow, tid / 2, codes);
+      } else {
+        if (tid % 2 == 0) store_code(crow, tid / 2, code);
+      }
       continue;
     }
     if (VEC) {
@@ -1789,7 +1813,7 @@ int launch_row(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* da
                    (!fused || (aligned(y, 16) && ld_y % EPL == 0 && fits32(K * (int64_t)sizeof(T))));
   // every step whole and every workgroup's steps inside the grid: no bounds checks
   // (and, for the gathered code stores, scale rows aligned to their width: 16 / kLPB bytes)
-  const int code_width = MXQ_ROW_CODE_WORDS && !fused ? 16 / Fmt<T>::kLPB : 1;
+  const int code_width = MXQ_ROW_CODE_WORDS && !fused ? CodeGather<Fmt<T>::kLPB>::kCodes : 1;
   const bool full = vec && spr.d * (int64_t)((tpb / Fmt<T>::kLPB) * 32) == K && total % steps == 0 &&
                     fits32(K * (int64_t)sizeof(T)) && aligned(scale, code_width) && scale_ld % code_width == 0;
   const dim3 grid(grid_for(total, steps)), block(tpb);
@@ -1900,8 +1924,10 @@ int launch_quantize_mxfp4(const void* x, int64_t ld_x, int64_t rows, int64_t K, 
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(packed, EPL / 2);
   // every step whole and every workgroup's steps inside the grid: no bounds checks
+  // (and, for the gathered code stores, code rows aligned to their width)
+  const int code_width = MXQ_Q4_CODE_WORDS ? CodeGather<Fmt<T>::kLPB>::kCodes : 1;
   const bool full = vec && spr.d * (int64_t)StepGeom<T, kQ4Threads>::kElemsPerStep == K && total % kQ4Steps == 0 &&
-                    fits32(K * (int64_t)sizeof(T));
+                    fits32(K * (int64_t)sizeof(T)) && aligned(scale, code_width) && scale_ld % code_width == 0;
   const dim3 grid(grid_for(total, kQ4Steps)), block(kQ4Threads);
   if (full)
     hipLaunchKernelGGL((quantize_mxfp4_kernel<T, true, true>), grid, block, 0, s, (const T*)x, ld_x, K, packed, scale,
@@ -2657,7 +2683,10 @@ int mxq_mxfp4_packed_to_mxfp8_row(const uint8_t* packed, const uint8_t* scale, i
   if (steps_for(rows, K, kPackedThreads * 16, &spr, &total)) return MXQ_ERR_SHAPE;
   const bool vec = aligned(packed, 8) && aligned(data, 16) && K % 16 == 0;
   // every step whole and every workgroup's steps inside the grid: no bounds checks
-  const bool full = vec && spr.d * (int64_t)(kPackedThreads * 16) == K && total % kPackedSteps == 0 && fits32(K);
+  // (and, for the gathered code stores, code rows aligned to their width: 4 bytes)
+  const int code_width = MXQ_PACKED_CODE_WORDS ? CodeGather<2>::kCodes : 1;
+  const bool full = vec && spr.d * (int64_t)(kPackedThreads * 16) == K && total % kPackedSteps == 0 && fits32(K) &&
+                    aligned(scale_out, code_width) && scale_out_ld % code_width == 0;
   const dim3 grid(grid_for(total, kPackedSteps)), block(kPackedThreads);
   if (full)
     hipLaunchKernelGGL((packed_convert_kernel<true, true>), grid, block, 0, stream, packed, scale, scale_ld, K, data,

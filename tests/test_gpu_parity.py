@@ -422,27 +422,47 @@ def test_strided_and_misaligned_views(dev, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_row_code_storage_alignment(dev, dtype):
-    """Whole-step rows (K = two steps of the row lift) with the code storage at
-    every alignment: a base pointer 0-3 bytes off and row strides nb .. nb + 4.
-    The full-step row lift gathers a 16-lane row's codes into one 4-byte (bf16)
-    or 2-byte (fp32) store where the storage is aligned to that width, and
-    stores bytes otherwise; each against the oracle, padding untouched."""
+def test_code_storage_alignment(dev, dtype):
+    """Whole-step rows (K = 4096: whole steps of the row lift, the MXFP4 encode
+    and the row lift from packed MXFP4) with the code storage at every
+    alignment: a base pointer 0-3 bytes off and row strides nb .. nb + 4.  The
+    full-step kernels gather a group of lanes' codes into one 4-byte (2-byte
+    for the fp32 row lift and encode) store where the storage is aligned to
+    that width, and store bytes otherwise; each against the oracle, with the
+    storage around the codes untouched."""
     src = W.c2_planted() if dtype == "bf16" else W.c2_planted_fp32()
     rows, K = 64, 4096
     bits = np.ascontiguousarray(np.resize(src.reshape(-1), rows * K).reshape(rows, K))
     x = to_dev(bits, dev)
     nb = K // 32
     wd, ws = oracle.mxfp4_to_mxfp8_row(bits, threads=THREADS)
+    wp, wps = oracle.quantize_mxfp4(bits, threads=THREADS)
+    wpd, wpc = oracle.mxfp4_packed_to_mxfp8_row(wp, wps, K, threads=THREADS)
+    pk, pks = to_dev(wp, dev), to_dev(wps, dev)
     for off in (0, 1, 2, 3):
         for ld in (nb, nb + 1, nb + 2, nb + 4):
-            buf = torch.full((rows * ld + 8,), 0x5A, dtype=torch.uint8, device=dev)
-            scale = buf[off:off + rows * ld].view(rows, ld)[:, :nb]
+            def storage():
+                buf = torch.full((rows * ld + 8,), 0x5A, dtype=torch.uint8, device=dev)
+                return buf, buf[off:off + rows * ld].view(rows, ld)[:, :nb]
+
+            def expect(codes):
+                want = np.full(rows * ld + 8, 0x5A, np.uint8)
+                want[off:off + rows * ld].reshape(rows, ld)[:, :nb] = codes
+                return want
+
+            what = f"off={off} ld={ld}"
+            buf, scale = storage()
             data, _ = mxq.mxq_mxfp4_to_mxfp8_row(x, scale=scale)
-            want = np.full(rows * ld + 8, 0x5A, np.uint8)
-            want[off:off + rows * ld].reshape(rows, ld)[:, :nb] = ws
-            assert_bits(to_host(data), wd, f"payload off={off} ld={ld}")
-            assert_bits(to_host(buf), want, f"codes off={off} ld={ld}")
+            assert_bits(to_host(data), wd, f"row payload {what}")
+            assert_bits(to_host(buf), expect(ws), f"row codes {what}")
+            buf, scale = storage()
+            packed, _ = mxq.mxq_quantize_mxfp4(x, scale=scale)
+            assert_bits(to_host(packed), wp, f"packed nibbles {what}")
+            assert_bits(to_host(buf), expect(wps), f"packed codes {what}")
+            buf, scale = storage()
+            data, _ = mxq.mxq_mxfp4_packed_to_mxfp8_row(pk, pks, K, scale_out=scale)
+            assert_bits(to_host(data), wpd, f"row-from-packed payload {what}")
+            assert_bits(to_host(buf), expect(wpc), f"row-from-packed codes {what}")
 
 
 def test_in_place_projection(dev):
