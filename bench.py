@@ -29,11 +29,12 @@ The default of 100 timed steps keeps the fixed cost of the synchronizations
 around the timed region (tens of us in all) below 1% of it.
 
 python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu] [--calibrate] [--weight bf16|fp32]
-                [--shape 8192x8192|28672x8192|8192x28672]
+                [--shape 8192x8192|28672x8192|8192x28672] [--orders]
 (--weight fp32 runs the same step on the fp32 master copy of the weight; bf16 is the headline.
 --shape runs the same step on the MLP-shaped weights instead: 28672 x 8192 (N(0,0.02), seed 2; its
 fp32 master with --weight fp32) or 8192 x 28672 (seed 3, bf16 only).  The scale storage is always
-padded by 4 columns, so the export copies.)
+padded by 4 columns, so the export copies.  --orders adds "orders": every kernel's burst mean per
+launch right after a burst of the fold, after a 30 ms idle gap and after a burst of itself.)
 """
 from __future__ import annotations
 
@@ -55,6 +56,7 @@ GROUPED = (48, 1024, 2048)       # outside the step: grouped calls over 48 weigh
 SHAPES = ("8192x8192", "28672x8192", "8192x28672")
 NSETS = 6
 SUB, SPREAD_BURSTS = 5, 5   # median / min: 5 sub-bursts of 5 launches, after the timed region
+ORDER_REPS, ORDER_LAUNCHES = 4, 60   # --orders: bursts of 60 launches, median of 4 repetitions
 # The access-shape reference kernels (libmxq_shapes.so, shape codes of include/mxq_shapes.h) timed
 # after the step: name -> (shape code, input buffer, code buffer).  Each moves the bytes of the
 # kernel named in SHAPE_KERNEL in that kernel's access pattern, with no quantization arithmetic;
@@ -237,6 +239,9 @@ def main():
                     help="the weight's dtype: bf16 (the headline) or its fp32 master copy")
     ap.add_argument("--shape", choices=SHAPES, default=SHAPES[0],
                     help="the weight's shape: 8192x8192 (the headline) or an MLP-shaped weight")
+    ap.add_argument("--orders", action="store_true",
+                    help="also time every kernel's burst after a burst of the fold, after an idle gap and after "
+                         "a burst of itself (field 'orders')")
     args = ap.parse_args()
     if args.shape == "8192x28672" and args.weight == "fp32":
         ap.error("--shape 8192x28672 has no fp32 master weight (only the 28672x8192 weight has one)")
@@ -433,6 +438,34 @@ def main():
     torch.cuda.synchronize()
     copy_us = 1e3 * c0.elapsed_time(c1) / args.steps
 
+    orders = None
+    if args.orders:
+        # Each kernel's burst mean in three orders, outside the timed region: right
+        # after a burst of the fold, after a 30 ms idle gap, after a burst of
+        # itself (the median of ORDER_REPS repetitions).  A kernel whose speed
+        # depends on the state the one before it leaves the GPU in shows it here.
+        def burst(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(ORDER_LAUNCHES):
+                launches[n](sets[(i + offset[n]) % NSETS])
+            b.record(stream)
+            return a, b
+
+        res = {}
+        for _ in range(ORDER_REPS):
+            for n in names + extra_names:
+                for pre in ("after_fold", "after_idle", "after_itself"):
+                    torch.cuda.synchronize()
+                    if pre == "after_idle":
+                        time.sleep(0.03)
+                    else:
+                        burst("block128" if pre == "after_fold" else n)
+                    a, b = burst(n)
+                    torch.cuda.synchronize()
+                    res.setdefault(n, {}).setdefault(pre, []).append(1e3 * a.elapsed_time(b) / ORDER_LAUNCHES)
+        orders = {n: {pre: round(statistics.median(v), 2) for pre, v in d.items()} for n, d in res.items()}
+
     if args.calibrate:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -529,6 +562,8 @@ def main():
                            "GB/s": round(2 * es * rows * K / (copy_us * 1e-6) / 1e9, 1),
                            "frac": round(2 * es * rows * K / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    if orders is not None:
+        out["orders"] = orders
     if not args.no_cpu:
         # every CPU this process may run on (its affinity set), one oracle thread each
         out["cpu_baseline"], want = cpu_baseline(bits, threads=host_cpu()["usable"])
