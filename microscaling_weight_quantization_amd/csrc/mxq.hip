@@ -101,6 +101,9 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_FOLD_FULL
 #define MXQ_FOLD_FULL 1
 #endif
+#ifndef MXQ_FOLD_READLANE
+#define MXQ_FOLD_READLANE 1       // the fold's wave maximum from four readlanes (one tile per workgroup)
+#endif
 #ifndef MXQ_DEQUANT_XCD_RUN
 #define MXQ_DEQUANT_XCD_RUN 1
 #endif
@@ -931,10 +934,18 @@ __device__ __forceinline__ void fold_tiles(const T* __restrict__ x, int64_t ld_x
     poisoned |= (uint64_t)b.poison << i;
     if (!b.poison) m = max(m, b.eb);
   }
-  m = max16(m);
-  if constexpr (CPT == 32) m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+  m = max16(m);                                            // every lane: its 16-lane row's maximum
+  if constexpr (J == 1 && MXQ_FOLD_READLANE) {
+    // One tile per workgroup: the whole wave is one tile, so its maximum is the
+    // largest of the four rows' maxima, read as scalars (no shuffle through the
+    // LDS crossbar, and no wait on one, between the loads and the barrier).
+    m = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+            max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+  } else {
+    if constexpr (CPT == 32) m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
 #pragma unroll
-  for (int off = LPR; off < 64; off *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    for (int off = LPR; off < 64; off *= 2) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  }
   if (lane < (uint32_t)LPR && lane % CPT == 0) s_max[wave][j] = m;
   __syncthreads();
 #pragma unroll
