@@ -22,6 +22,17 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
+// The fold's wave-wide maximum: DPP within each 16-lane row (pair swap, quad
+// swap, half-row mirror, row mirror), then the four rows' maxima as scalars.
+__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
+  m = max(m, dpp<0xB1>(m));
+  m = max(m, dpp<0x4E>(m));
+  m = max(m, dpp<0x141>(m));
+  m = max(m, dpp<0x140>(m));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+}
+
 // A 16-byte chunk folded to 16 / ES bytes (ES = 2: 8 bytes, ES = 4: 4 bytes).
 template <int ES>
 struct Narrow;
@@ -99,8 +110,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const uint8_t* __restrict__ 
 
 // The 128x128 fold's pattern: one 1024-lane workgroup per tile, 16-byte chunks,
 // 128 * ES / 16 lanes across a tile row (16 for ES 2, 32 for ES 4), every chunk
-// loaded first, a tile-wide maximum through LDS and a barrier (BARRIER), then
-// 16 / ES bytes out per chunk and one byte per tile.
+// loaded first, the fold's wave maximum, a tile-wide maximum through LDS and a
+// barrier (BARRIER), then 16 / ES bytes out per chunk and one byte per tile.
 template <int ES, bool BARRIER>
 __global__ __launch_bounds__(1024) void tile_kernel(const uint8_t* __restrict__ in, int64_t K, uint8_t* __restrict__ out,
                                                     uint8_t* __restrict__ codes, uint32_t tiles_per_row) {
@@ -117,12 +128,7 @@ __global__ __launch_bounds__(1024) void tile_kernel(const uint8_t* __restrict__ 
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < P; i++) m = max(m, max(max(w[i][0], w[i][1]), max(w[i][2], w[i][3])) >> 24);
-  m = max(m, dpp<0xB1>(m));
-  m = max(m, dpp<0x4E>(m));
-  m = max(m, dpp<0x141>(m));
-  m = max(m, dpp<0x140>(m));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+  m = wave_max(m);
   if constexpr (BARRIER) {
     if ((t & 63u) == 0) s_max[t >> 6] = m;
     __syncthreads();
@@ -130,22 +136,23 @@ __global__ __launch_bounds__(1024) void tile_kernel(const uint8_t* __restrict__ 
     for (int v = 0; v < 16; v++) m = max(m, s_max[v]);
   }
 #pragma unroll
-  for (int i = 0; i < P; i++) store_nt(Narrow<ES>::of(w[i], m), out + (r0 + i * RPP) * K, (uint32_t)c0);
+  for (int i = 0; i < P; i++)   // stores off the band's first row (a base the whole workgroup shares)
+    store_nt(Narrow<ES>::of(w[i], m), out + (uint64_t)tr * 128 * K, (uint32_t)((r0 - (uint64_t)tr * 128 + i * RPP) * K + c0));
   if (t == 0) codes[blockIdx.x] = (uint8_t)m;
 }
 
 // The fold's workgroup (1024 lanes, two 16-byte chunks per lane: chunks l and
-// 1024 + l of the workgroup's 32 KB) over a plain contiguous stream, with or
-// without the barrier.
+// 1024 + l of the workgroup's 32 KB) over a plain contiguous stream, with the
+// same wave maximum, with or without the barrier: the tile shape's arithmetic
+// and synchronization on linear addresses.
 template <int ES, bool BARRIER>
 __global__ __launch_bounds__(1024) void linear_kernel(const u32x4* __restrict__ in, uint8_t* __restrict__ out) {
   __shared__ uint32_t s_max[16];
   const uint32_t t = threadIdx.x;
   const uint64_t c = (uint64_t)blockIdx.x * 2048 + t;
   const u32x4 a = __builtin_nontemporal_load(in + c), b = __builtin_nontemporal_load(in + c + 1024);
-  uint32_t m = max(max(a[0], a[3]), max(b[1], b[2])) >> 24;
-  m = max(m, dpp<0xB1>(m));
-  m = max(m, dpp<0x4E>(m));
+  uint32_t m = max(max(max(a[0], a[1]), max(a[2], a[3])), max(max(b[0], b[1]), max(b[2], b[3]))) >> 24;
+  m = wave_max(m);
   if constexpr (BARRIER) {
     if ((t & 63u) == 0) s_max[t >> 6] = m;
     __syncthreads();
@@ -185,7 +192,7 @@ int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t
       return status();
     case MXQ_SHAPE_TILE:
     case MXQ_SHAPE_TILE_NO_BARRIER: {
-      if (rows % 128 || K % 128) return 1;
+      if (rows % 128 || K % 128 || 128 * K >= ((int64_t)1 << 31)) return 1;   // a band's payload: 32-bit offsets
       const uint32_t tpr = (uint32_t)(K / 128), tiles = (uint32_t)(rows / 128) * tpr;
       if (shape == MXQ_SHAPE_TILE)
         hipLaunchKernelGGL((tile_kernel<ES, true>), dim3(tiles), dim3(1024), 0, s, (const uint8_t*)in, K, (uint8_t*)out,
