@@ -65,8 +65,9 @@ ORDER_REPS, ORDER_LAUNCHES = 4, 60   # --orders: bursts of 60 launches, median o
 SHAPES_OF = {"shape_copy16": (0, "x", "scale2"), "shape_row": (1, "x", "scale2"), "shape_row_codes": (2, "x", "scale2"),
              "shape_decode": (3, "data", "scale_c"), "shape_tile": (4, "x", "scale2"),
              "shape_tile_no_barrier": (5, "x", "scale2"), "shape_linear1024": (6, "x", "scale2"),
-             "shape_linear1024_no_barrier": (7, "x", "scale2")}
-SHAPE_KERNEL = {"shape_copy16": "proj", "shape_row_codes": "row", "shape_decode": "dec_row", "shape_tile": "block128"}
+             "shape_linear1024_no_barrier": (7, "x", "scale2"), "shape_packed_row": (8, "packed", "pscale")}
+SHAPE_KERNEL = {"shape_copy16": "proj", "shape_row_codes": "row", "shape_decode": "dec_row", "shape_tile": "block128",
+                "shape_packed_row": "packed_to_row"}
 # committed rocprofv3 counter summaries of the 8192 x 8192 weight, per dtype
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_8192x8192_{}.txt")
 # The device code: the kernels and the divisor header they include.
@@ -513,7 +514,8 @@ def main():
     shape_bytes = {"shape_copy16": nbytes["proj"], "shape_row": es * n_el + n_el, "shape_row_codes": nbytes["row"],
                    "shape_decode": nbytes["dec_row"], "shape_tile": nbytes["block128"],
                    "shape_tile_no_barrier": nbytes["block128"], "shape_linear1024": es * n_el + n_el,
-                   "shape_linear1024_no_barrier": es * n_el + n_el}
+                   "shape_linear1024_no_barrier": es * n_el + n_el,
+                   "shape_packed_row": packed_bytes(rows, K, es)["packed_to_row"]}
     shapes_out = {}
     for n in shape_names:
         us, med, lo = burst_stats(n)
@@ -523,7 +525,8 @@ def main():
                                          "frac": round(gbs / HBM_PEAK_GBS, 4), "of_kernel": SHAPE_KERNEL.get(n)}
     for n, k in SHAPE_KERNEL.items():
         # the kernel's speed as a fraction of its access shape's (1.0: the pattern alone sets its time)
-        kernels[k]["of_shape"] = round(shapes_out[n[len("shape_"):]]["us"] / kernels[k]["us"], 4)
+        entry = kernels[k] if k in kernels else extra[k]
+        entry["of_shape"] = round(shapes_out[n[len("shape_"):]]["us"] / entry["us"], 4)
     extra["fused_proj_row"]["vs_separate_us"] = round(kernels["proj"]["us"] + kernels["row"]["us"], 2)
     extra["row_col"]["vs_separate_us"] = round(kernels["row"]["us"] + extra["col"]["us"], 2)
     dominant = max(names, key=lambda n: kernels[n]["us"])

@@ -11,14 +11,15 @@
  * kernel timings, re-done on MI355X).
  *
  * int mxq_shape_run(shape, element_size, in, out, codes, rows, K, stream)
- *   in     [rows, K] input elements, contiguous (MXQ_SHAPE_DECODE: [rows, K] payload bytes)
+ *   in     [rows, K] input elements, contiguous (MXQ_SHAPE_DECODE: [rows, K] payload bytes;
+ *          MXQ_SHAPE_PACKED_ROW: [rows, K / 2] packed bytes, element_size ignored)
  *   out    at least rows * K * element_size bytes
  *   codes  at least max(rows * K / 32, rows * K / 16384) bytes (code bytes the shape writes or reads)
  *   Returns 0 when launched, 1 when the shape does not fit (sizes, pointers), 2 when the runtime
  *   refused the launch.  Each shape needs whole workgroups of work: COPY16: rows * K *
  *   element_size a multiple of 1024; ROW, ROW_CODES: a multiple of 8192; DECODE: rows * K a
  *   multiple of 64 * 16 / element_size; TILE*: rows and K multiples of 128; LINEAR1024*:
- *   rows * K * element_size a multiple of 32768.
+ *   rows * K * element_size a multiple of 32768; PACKED_ROW: rows * K a multiple of 1024.
  */
 #ifndef MXQ_SHAPES_H
 #define MXQ_SHAPES_H
@@ -38,7 +39,9 @@ enum {
   MXQ_SHAPE_TILE = 4,                   /* 128x128 fold: 1024 lanes per tile, all loads, LDS max, barrier, stores */
   MXQ_SHAPE_TILE_NO_BARRIER = 5,        /* TILE without the workgroup-wide maximum (wave-wide only) */
   MXQ_SHAPE_LINEAR1024 = 6,             /* the fold's 1024-lane, 2-chunk workgroup over a contiguous stream */
-  MXQ_SHAPE_LINEAR1024_NO_BARRIER = 7   /* LINEAR1024 without the barrier */
+  MXQ_SHAPE_LINEAR1024_NO_BARRIER = 7,  /* LINEAR1024 without the barrier */
+  MXQ_SHAPE_PACKED_ROW = 8              /* row lift from packed MXFP4: 64 lanes, 8 B + a code byte in, 16 B out (nt),
+                                           gathered 4-byte code stores back over the codes read */
 };
 
 int mxq_shape_run(int shape, int element_size, const void* in, void* out, void* codes, int64_t rows, int64_t K,

@@ -164,6 +164,22 @@ __global__ __launch_bounds__(1024) void linear_kernel(const u32x4* __restrict__ 
   store_nt(Narrow<ES>::of(b, m), o, (1024 + t) * (16 / ES));
 }
 
+// The row lift from packed MXFP4's pattern: 64-lane workgroups, 8 packed bytes
+// and one code byte (two lanes per code) in per lane, 16 payload bytes out
+// (nt), and the codes of each 8 lanes gathered into one 4-byte store.  The
+// gathered word is written back over the codes it was read from (the same
+// bytes), so the shape needs no second code buffer.
+__global__ __launch_bounds__(64) void packed_row_kernel(const u32x2* __restrict__ in, uint8_t* __restrict__ out,
+                                                        uint8_t* __restrict__ codes) {
+  const uint32_t t = threadIdx.x;
+  const u32x2 f = __builtin_nontemporal_load(in + (uint64_t)blockIdx.x * 64 + t);
+  uint8_t* const wcodes = codes + (uint64_t)blockIdx.x * 32;     // the workgroup's 32 codes
+  const uint32_t c = wcodes[t / 2];
+  store_nt(u32x4{f[0] ^ c, f[0] >> 4, f[1] + c, f[1] >> 4}, out + (uint64_t)blockIdx.x * 1024, t * 16);
+  const uint32_t w = c | (dpp<0x102>(c) << 8) | (dpp<0x104>(c) << 16) | (dpp<0x106>(c) << 24);
+  if (t % 8 == 0) store_nt<0>(w, wcodes, t / 2);
+}
+
 int status() { return hipGetLastError() == hipSuccess ? 0 : 2; }
 
 template <int ES>
@@ -211,6 +227,11 @@ int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t
       else
         hipLaunchKernelGGL((linear_kernel<ES, false>), dim3(chunks / 2048), dim3(1024), 0, s, (const u32x4*)in,
                            (uint8_t*)out);
+      return status();
+    case MXQ_SHAPE_PACKED_ROW:
+      if ((rows * K) % 1024) return 1;
+      hipLaunchKernelGGL(packed_row_kernel, dim3((uint32_t)(rows * K / 1024)), dim3(64), 0, s, (const u32x2*)in,
+                         (uint8_t*)out, (uint8_t*)codes);
       return status();
     default:
       return 1;
