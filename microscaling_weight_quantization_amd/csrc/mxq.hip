@@ -113,8 +113,11 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_FUSED_THREADS
 #define MXQ_FUSED_THREADS 64      // fused projection + row lift
 #endif
-#ifndef MXQ_DEQUANT_THREADS
-#define MXQ_DEQUANT_THREADS 64    // FP8 decodes (8 elements per lane)
+#ifndef MXQ_DEQUANT_THREADS_BF16
+#define MXQ_DEQUANT_THREADS_BF16 64   // FP8 decodes to bf16 (8 elements per lane)
+#endif
+#ifndef MXQ_DEQUANT_THREADS_FP32
+#define MXQ_DEQUANT_THREADS_FP32 128  // FP8 decodes to fp32
 #endif
 #ifndef MXQ_DQ4_THREADS
 #define MXQ_DQ4_THREADS 256       // packed MXFP4 decode (8 elements per lane)
@@ -135,11 +138,12 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_FUSED_STEPS
 #define MXQ_FUSED_STEPS 1
 #endif
-// FP8 decodes: to bf16, two steps (row layout 32.7-33.0 us at 8192 x 8192 in
-// every order; one step ran 32.2 after the fold but 36.0 after itself); to
-// fp32, one step (tile layout at 28672 x 8192: 186 us against 196 with two).
-// A check-free form with buffer stores was tried for both and was slower or
-// less steady (fp32 tile layout at 28672 x 8192: 200 us).
+// FP8 decodes: to bf16, 64 lanes and two steps (row layout 32.7-33.0 us at
+// 8192 x 8192 in every order; one step ran 32.2 after the fold but 36.0 after
+// itself; 128 or 256 lanes 33.7-34.7); to fp32, 128 lanes and one step (row /
+// tile layout at 28672 x 8192: 181 / 179 us, against 191 / 187 with 64 lanes
+// and 196 in the tile layout with two steps).  A check-free form with buffer
+// stores was tried for both and was slower or less steady.
 #ifndef MXQ_DEQUANT_STEPS_BF16
 #define MXQ_DEQUANT_STEPS_BF16 2
 #endif
@@ -174,13 +178,15 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kThreads = 256;     // 4 waves: workgroup size of the remaining streaming kernels
-constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS, kDequantThreads = MXQ_DEQUANT_THREADS,
+constexpr int kProjThreads = MXQ_PROJ_THREADS, kRowThreads = MXQ_ROW_THREADS,
               kDq4Threads = MXQ_DQ4_THREADS, kPackedThreads = MXQ_PACKED_THREADS;
 constexpr int kProjSteps = MXQ_PROJ_STEPS, kRowSteps = MXQ_ROW_STEPS, kPackedSteps = MXQ_PACKED_STEPS;
-// Steps per workgroup of the single FP8 decode, by output type.
+// Launch shape of the FP8 decodes by output type: lanes per workgroup (single
+// and grouped kernels) and steps per workgroup (single kernel).
 template <typename TO>
-struct DequantSteps {
-  static constexpr int value = sizeof(TO) == 2 ? MXQ_DEQUANT_STEPS_BF16 : MXQ_DEQUANT_STEPS_FP32;
+struct DequantShape {
+  static constexpr int kThreads = sizeof(TO) == 2 ? MXQ_DEQUANT_THREADS_BF16 : MXQ_DEQUANT_THREADS_FP32;
+  static constexpr int kSteps = sizeof(TO) == 2 ? MXQ_DEQUANT_STEPS_BF16 : MXQ_DEQUANT_STEPS_FP32;
 };
 constexpr int kFusedThreads = MXQ_FUSED_THREADS, kFusedSteps = MXQ_FUSED_STEPS;
 constexpr int kQ4Threads = MXQ_Q4_THREADS, kQ4Steps = MXQ_Q4_STEPS, kDq4Steps = MXQ_DQ4_STEPS;
@@ -1088,6 +1094,7 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
                                               int64_t scale_ld, int64_t K, TO* __restrict__ out, int64_t ld_out,
                                               MxqDivisor steps_per_row, uint32_t total_steps, uint32_t wg) {
   // 8 payload bytes per lane per step; a step is kDequantThreads * 8 elements of one row.
+  constexpr int kDequantThreads = DequantShape<TO>::kThreads;
   // Lane geometry: bf16 output takes 8 consecutive elements per lane (one 16-byte
   // store).  fp32 output (kSplit) takes two groups of 4, half a step apart, so
   // that each of the lane's two 16-byte stores is part of one contiguous
@@ -1220,12 +1227,12 @@ __device__ __forceinline__ void dequant_steps(const uint8_t* __restrict__ data, 
 }
 
 template <typename TO, bool kE5M2, int kLay, bool VEC>
-__global__ __launch_bounds__(kDequantThreads) void dequant_kernel(const uint8_t* __restrict__ data,
+__global__ __launch_bounds__(DequantShape<TO>::kThreads) void dequant_kernel(const uint8_t* __restrict__ data,
                                                            const uint8_t* __restrict__ scale, int64_t scale_ld,
                                                            int64_t K, TO* __restrict__ out, int64_t ld_out,
                                                            MxqDivisor steps_per_row, uint32_t total_steps) {
   keep_denormals();
-  dequant_steps<TO, kE5M2, kLay, VEC, DequantSteps<TO>::value>(
+  dequant_steps<TO, kE5M2, kLay, VEC, DequantShape<TO>::kSteps>(
       data, scale, scale_ld, K, out, ld_out, steps_per_row, total_steps,
       xcd_run<kLay == kLayRow ? kDequantXcdRun : 1>(blockIdx.x, gridDim.x));
 }
@@ -1248,7 +1255,7 @@ struct DequantGroupTable {
 static_assert(sizeof(DequantGroupTable) <= 3584, "the table must fit the kernel-argument segment");
 
 template <typename TO, bool kE5M2, int kLay>
-__global__ __launch_bounds__(kDequantThreads) void dequant_grouped_kernel(const DequantGroupTable tab) {
+__global__ __launch_bounds__(DequantShape<TO>::kThreads) void dequant_grouped_kernel(const DequantGroupTable tab) {
   const DequantGroupDesc d = tab.g[blockIdx.y];
   if (blockIdx.x * kDequantGroupedSteps >= d.total_steps) return;   // uniform: past this weight's steps
   keep_denormals();
@@ -1895,11 +1902,11 @@ int launch_dequant_t(const uint8_t* data, const uint8_t* scale, int64_t scale_ld
                      int64_t ld_out, hipStream_t s) {
   MxqDivisor spr;
   uint32_t total;
-  if (steps_for(rows, K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
+  if (steps_for(rows, K, DequantShape<TO>::kThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
   constexpr int OPC = 16 / (int)sizeof(TO);   // output elements per 16-byte store
   const bool vec = aligned(data, 8) && K % 8 == 0 && aligned(out, 16) && ld_out % OPC == 0 &&
                    (kLay != kLayCol || (aligned(scale, 8) && scale_ld % 8 == 0));
-  const dim3 grid(grid_for(total, DequantSteps<TO>::value)), block(kDequantThreads);
+  const dim3 grid(grid_for(total, DequantShape<TO>::kSteps)), block(DequantShape<TO>::kThreads);
   if (vec)
     hipLaunchKernelGGL((dequant_kernel<TO, kE5M2, kLay, true>), grid, block, 0, s, data, scale, scale_ld, K,
                        (TO*)out, ld_out, spr, total);
@@ -2100,7 +2107,7 @@ int launch_dequant_grouped_t(const mxq_dequant_group* gs, int64_t n, hipStream_t
   auto flush = [&]() -> int {
     if (count == 0) return MXQ_OK;
     hipLaunchKernelGGL((dequant_grouped_kernel<TO, kE5M2, kLay>), dim3((uint32_t)max_w, (uint32_t)count),
-                       dim3(kDequantThreads), 0, s, tab);
+                       dim3(DequantShape<TO>::kThreads), 0, s, tab);
     count = max_w = sum_w = 0;
     return launch_status();
   };
@@ -2115,7 +2122,7 @@ int launch_dequant_grouped_t(const mxq_dequant_group* gs, int64_t n, hipStream_t
     }
     MxqDivisor spr;
     uint32_t total;
-    if (steps_for(g.rows, g.K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
+    if (steps_for(g.rows, g.K, DequantShape<TO>::kThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
     const int64_t gw = grid_for(total, kDequantGroupedSteps);
     const int64_t padded = (count + 1) * std::max(max_w, gw), real = sum_w + gw;
     if (count == kGroupMax || (count > 0 && padded > real + real / 4 + 4096)) {
@@ -2590,7 +2597,8 @@ int mxq_dequantize_grouped(const mxq_dequant_group* groups, int64_t n_groups, mx
     if (empty) continue;
     MxqDivisor spr;
     uint32_t total;
-    if (steps_for(g.rows, g.K, kDequantThreads * 8, &spr, &total)) return MXQ_ERR_SHAPE;
+    const int64_t eps = 8 * (out_dt == MXQ_BF16 ? DequantShape<uint16_t>::kThreads : DequantShape<uint32_t>::kThreads);
+    if (steps_for(g.rows, g.K, eps, &spr, &total)) return MXQ_ERR_SHAPE;
     iv.push_back({r[0], false});
     iv.push_back({r[1], false});
     iv.push_back({r[2], true});
