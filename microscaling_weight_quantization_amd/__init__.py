@@ -126,15 +126,16 @@ def _device_operands(fn):
     from another GPU would reach a kernel as an invalid address."""
     @functools.wraps(fn)
     def wrapper(*args, **kwargs):
-        dev = None
-        for t in list(args) + list(kwargs.values()):
+        dev = -2                                            # get_device(): -1 for a host tensor
+        for t in (*args, *kwargs.values()):
             if isinstance(t, torch.Tensor):
-                if not t.is_cuda:
+                d = t.get_device()
+                if d < 0 or not t.is_cuda:
                     raise ValueError(f"{fn.__name__}: operands must be device tensors, got one on {t.device}")
-                if dev is None:
-                    dev = t.device
-                elif t.device != dev:
-                    raise ValueError(f"{fn.__name__}: operands on {dev} and {t.device}; all must be on one device")
+                if dev == -2:
+                    dev = d
+                elif d != dev:
+                    raise ValueError(f"{fn.__name__}: operands on cuda:{dev} and cuda:{d}; all must be on one device")
         return fn(*args, **kwargs)
     return wrapper
 
@@ -196,7 +197,15 @@ def _flag(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
+# torch's current stream as a raw handle.  The internal accessor returns the
+# handle directly (a tenth of the time of building a Stream object); the public
+# call is the fallback where a torch build lacks it.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor):
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(t.get_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
