@@ -98,6 +98,9 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 // The fold's check-free form for whole tile groups, for fp32 weights: 52.1 us
 // against 52.5 at 8192 x 8192.  For bf16 it was slower (35.2-35.4 us against
 // 34.5, with buffer or global stores alike), so bf16 keeps the checked form.
+#ifndef MXQ_EXPORT4
+#define MXQ_EXPORT4 1             // the export from 4-byte-aligned padded rows: 16-byte stores
+#endif
 #ifndef MXQ_FOLD_FULL
 #define MXQ_FOLD_FULL 1
 #endif
@@ -1751,6 +1754,22 @@ __global__ __launch_bounds__(kThreads) void export_kernel(const uint8_t* __restr
   reinterpret_cast<V*>(dst)[i] = reinterpret_cast<const V*>(src + (int64_t)r * src_ld)[j];
 }
 
+// The export of 4-byte-aligned source rows into 16-byte-aligned destination
+// rows (a padded stride such as ceil(K/32) + 4): each lane loads four
+// consecutive 4-byte units of one row and stores them as one 16-byte unit.
+// units_per_row and total_units count 16-byte destination units.
+__global__ __launch_bounds__(kThreads) void export4_kernel(const uint8_t* __restrict__ src, int64_t src_ld,
+                                                           uint8_t* __restrict__ dst, MxqDivisor units_per_row,
+                                                           uint32_t total_units) {
+  const uint32_t per = gridDim.x / 8, chunk = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const uint64_t i64 = (uint64_t)chunk * kThreads + threadIdx.x;
+  if (i64 >= total_units) return;
+  const uint32_t i = (uint32_t)i64;
+  const uint32_t r = mxq_quot(i, units_per_row), j = i - r * units_per_row.d;
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src + (int64_t)r * src_ld) + 4 * j;
+  reinterpret_cast<u32x4*>(dst)[i] = u32x4{s[0], s[1], s[2], s[3]};
+}
+
 // ------------------------------------------------------------------------------------
 // Host side: validation and launch
 // ------------------------------------------------------------------------------------
@@ -2527,7 +2546,13 @@ int mxq_export_mxfp8(const uint8_t* data, const uint8_t* scale_storage, int64_t 
   const dim3 grid((uint32_t)(((units + kThreads - 1) / kThreads + 7) / 8 * 8)), block(kThreads);
   const MxqDivisor upr = mxq_divisor((uint32_t)(nb / width));
   const uint32_t total = (uint32_t)units;
-  if (width == 16)
+  if (MXQ_EXPORT4 && width == 4 && aligned(scale_out, 16) && nb % 16 == 0) {
+    // four 4-byte units per lane, one 16-byte store
+    const int64_t units16 = rows * (nb / 16);
+    const dim3 grid16((uint32_t)(((units16 + kThreads - 1) / kThreads + 7) / 8 * 8));
+    hipLaunchKernelGGL(export4_kernel, grid16, block, 0, stream, scale_storage, scale_ld, scale_out,
+                       mxq_divisor((uint32_t)(nb / 16)), (uint32_t)units16);
+  } else if (width == 16)
     hipLaunchKernelGGL(export_kernel<u32x4>, grid, block, 0, stream, scale_storage, scale_ld, scale_out, upr, total);
   else if (width == 4)
     hipLaunchKernelGGL(export_kernel<uint32_t>, grid, block, 0, stream, scale_storage, scale_ld, scale_out, upr, total);
