@@ -465,6 +465,32 @@ def test_code_storage_alignment(dev, dtype):
             assert_bits(to_host(buf), expect(wpc), f"row-from-packed codes {what}")
 
 
+@pytest.mark.parametrize("K", [512, 640, 4096, 4128])   # ceil(K/32) = 16, 20, 128, 129
+def test_export_every_unit_width(dev, K):
+    """The unpadded export against the oracle for code rows of 16, 20, 128 and
+    129 bytes, padded strides ceil(K/32) + 0, 1, 4 and 16, and storage and
+    output bases 0, 1 or 4 bytes off: 16-byte units, 4-byte units, the
+    four-4-byte-units-to-one-16-byte-store form and single bytes all run, and
+    the bytes around the output stay untouched."""
+    rows = 37
+    nb = (K + 31) // 32
+    rng = np.random.default_rng(K)
+    data = torch.zeros((rows, K), dtype=torch.uint8, device=dev)
+    for pad in (0, 1, 4, 16):
+        ld = nb + pad
+        codes = rng.integers(0, 256, size=(rows, ld), dtype=np.uint8)
+        for soff in (0, 1, 4):
+            sbuf = torch.from_numpy(np.concatenate([np.zeros(soff, np.uint8), codes.reshape(-1)])).to(dev)
+            storage = sbuf[soff:].view(rows, ld)
+            for ooff in (0, 1, 4):
+                obuf = torch.full((rows * nb + 8,), 0xA5, dtype=torch.uint8, device=dev)
+                out = obuf[ooff:ooff + rows * nb].view(rows, nb)
+                mxq.mxq_export_mxfp8(data, storage, K, scale_out=out)
+                want = np.full(rows * nb + 8, 0xA5, np.uint8)
+                want[ooff:ooff + rows * nb] = oracle.export_mxfp8(codes, K).reshape(-1)
+                assert_bits(to_host(obuf), want, f"export K={K} ld={ld} soff={soff} ooff={ooff}")
+
+
 def test_in_place_projection(dev):
     bits = W.c1_small()
     x = to_dev(bits, dev)
