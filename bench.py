@@ -249,8 +249,8 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
-              "(whole rows shard with no communication, so each GPU would run this kernel on its share).",
+        print("bench.py measures one GPU: the library runs on a single MI355X and has no multi-GPU path "
+              "(whole rows shard with no communication, so each GPU would run these kernels on its share).",
               file=sys.stderr)
         sys.exit(2)
 
