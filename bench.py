@@ -64,8 +64,8 @@ ORDER_REPS, ORDER_LAUNCHES = 4, 60   # --orders: bursts of 60 launches, median o
 # the workgroup-wide barrier, the 1024-lane two-chunk workgroup).
 SHAPES_OF = {"shape_copy16": (0, "x", "scale2"), "shape_row": (1, "x", "scale2"), "shape_row_codes": (2, "x", "scale2"),
              "shape_decode": (3, "data", "scale_c"), "shape_tile": (4, "x", "scale2"),
-             "shape_tile_no_barrier": (5, "x", "scale2"), "shape_linear1024": (6, "x", "scale2"),
-             "shape_linear1024_no_barrier": (7, "x", "scale2"), "shape_packed_row": (8, "packed", "pscale")}
+             "shape_tile_no_barrier": (5, "x", "scale2"), "shape_linear_fold": (6, "x", "scale2"),
+             "shape_linear_fold_no_barrier": (7, "x", "scale2"), "shape_packed_row": (8, "packed", "pscale")}
 SHAPE_KERNEL = {"shape_copy16": "proj", "shape_row_codes": "row", "shape_decode": "dec_row", "shape_tile": "block128",
                 "shape_packed_row": "packed_to_row"}
 # committed rocprofv3 counter summaries of the 8192 x 8192 weight, per dtype
@@ -513,8 +513,8 @@ def main():
     n_el, tiles = rows * K, ((rows + 127) // 128) * ((K + 127) // 128)
     shape_bytes = {"shape_copy16": nbytes["proj"], "shape_row": es * n_el + n_el, "shape_row_codes": nbytes["row"],
                    "shape_decode": nbytes["dec_row"], "shape_tile": nbytes["block128"],
-                   "shape_tile_no_barrier": nbytes["block128"], "shape_linear1024": es * n_el + n_el,
-                   "shape_linear1024_no_barrier": es * n_el + n_el,
+                   "shape_tile_no_barrier": nbytes["block128"], "shape_linear_fold": es * n_el + n_el,
+                   "shape_linear_fold_no_barrier": es * n_el + n_el,
                    "shape_packed_row": packed_bytes(rows, K, es)["packed_to_row"]}
     shapes_out = {}
     for n in shape_names:

@@ -18,8 +18,10 @@
  *   Returns 0 when launched, 1 when the shape does not fit (sizes, pointers), 2 when the runtime
  *   refused the launch.  Each shape needs whole workgroups of work: COPY16: rows * K *
  *   element_size a multiple of 1024; ROW, ROW_CODES: a multiple of 8192; DECODE: rows * K a
- *   multiple of 64 * 16 / element_size; TILE*: rows and K multiples of 128; LINEAR1024*:
- *   rows * K * element_size a multiple of 32768; PACKED_ROW: rows * K a multiple of 1024.
+ *   multiple of 64 * 16 / element_size; TILE*: rows and K multiples of 128; LINEAR_FOLD*:
+ *   rows * K a multiple of 16384 (a tile's elements); PACKED_ROW: rows * K a multiple of 1024.
+ *   The fold's workgroup (TILE*, LINEAR_FOLD*) is 512 lanes for element_size 2 and 1024 for 4,
+ *   as in libmxq's fold.
  */
 #ifndef MXQ_SHAPES_H
 #define MXQ_SHAPES_H
@@ -36,10 +38,11 @@ enum {
   MXQ_SHAPE_ROW = 1,                    /* row lift payload: 256 lanes, two 16 B chunks in, 16/es B out (nt) each */
   MXQ_SHAPE_ROW_CODES = 2,              /* ROW plus one code byte per 32 elements (sc1) */
   MXQ_SHAPE_DECODE = 3,                 /* row decode: 64 lanes, 16/es B + a code byte in, 16 B out (nt) */
-  MXQ_SHAPE_TILE = 4,                   /* 128x128 fold: 1024 lanes per tile, all loads, LDS max, barrier, stores */
+  MXQ_SHAPE_TILE = 4,                   /* 128x128 fold: its workgroup per tile in its tile order, all loads,
+                                           LDS max, barrier, stores */
   MXQ_SHAPE_TILE_NO_BARRIER = 5,        /* TILE without the workgroup-wide maximum (wave-wide only) */
-  MXQ_SHAPE_LINEAR1024 = 6,             /* the fold's 1024-lane, 2-chunk workgroup over a contiguous stream */
-  MXQ_SHAPE_LINEAR1024_NO_BARRIER = 7,  /* LINEAR1024 without the barrier */
+  MXQ_SHAPE_LINEAR_FOLD = 6,            /* the fold's workgroup (lanes, chunks per lane) over a contiguous stream */
+  MXQ_SHAPE_LINEAR_FOLD_NO_BARRIER = 7, /* LINEAR_FOLD without the barrier */
   MXQ_SHAPE_PACKED_ROW = 8              /* row lift from packed MXFP4: 64 lanes, 8 B + a code byte in, 16 B out (nt),
                                            gathered 4-byte code stores back over the codes read */
 };

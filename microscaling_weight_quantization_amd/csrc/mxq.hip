@@ -104,6 +104,38 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_FOLD_FULL
 #define MXQ_FOLD_FULL 1
 #endif
+// The fold's workgroup by input type: lanes per tile, and runs of side-by-side
+// tiles of a band per XCD (see xcd_run).  Burst means over four orders (after
+// the projection, after the row lift, after idle, after itself), from 1024
+// lanes in the plain order:
+//   bf16, 512 lanes in runs of 8: 8192 x 8192 34.7 -> 34.0 us, 28672 x 8192
+//   116.0 -> 109.8 us (1024 lanes in runs of 4: 34.2 / 112.8; 512 in runs of 2
+//   or 16: 34.3 / 111.9 and 36.7 / 117.0; 256 lanes: 36.5-39.3 / 115.9-124.4);
+//   fp32, 1024 lanes in runs of 4: 8192 x 8192 52.5 -> 52.0 us (512 lanes
+//   55.8-56.0); runs of 16-64 were 1-19% slower for both.
+#ifndef MXQ_FOLD_THREADS_BF16
+#define MXQ_FOLD_THREADS_BF16 512
+#endif
+#ifndef MXQ_FOLD_THREADS_FP32
+#define MXQ_FOLD_THREADS_FP32 1024
+#endif
+#ifndef MXQ_FOLD_XCD_RUN_BF16
+#define MXQ_FOLD_XCD_RUN_BF16 8
+#endif
+#ifndef MXQ_FOLD_XCD_RUN_FP32
+#define MXQ_FOLD_XCD_RUN_FP32 4
+#endif
+// The columnwise kernel's order of 32-row band groups (see xcd_run), by input
+// type.  fp32 in runs of 8 per XCD (burst means over four orders, col / row +
+// col: 8192 x 8192 54.8 -> 52.8 us / 68.2 -> 66.3 us, 28672 x 8192 188.3 ->
+// 179.7 us / 225.6 -> 219.8 us); bf16 in the plain order (runs of 2-8 were
+// within +-1%, faster at one size and slower at the other).
+#ifndef MXQ_COL_XCD_RUN_BF16
+#define MXQ_COL_XCD_RUN_BF16 1
+#endif
+#ifndef MXQ_COL_XCD_RUN_FP32
+#define MXQ_COL_XCD_RUN_FP32 8
+#endif
 #ifndef MXQ_FOLD_READLANE
 #define MXQ_FOLD_READLANE 1       // the fold's wave maximum from four readlanes (one tile per workgroup)
 #endif
@@ -289,6 +321,24 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+// Workgroup order in runs per XCD.  The dispatcher deals workgroup b to XCD
+// b % 8, and each XCD has its own L2, so in the plain order M neighbouring
+// workgroups run on M XCDs (a code line they share is fetched by M L2s).  With
+// M > 1, each run of 8 M workgroups is reordered so that XCD x takes the M
+// consecutive logical workgroups 8 M g + M x .. 8 M g + M x + M - 1; the last,
+// partial run keeps the plain order.  A permutation of 0 .. n - 1.
+template <int M>
+__device__ __forceinline__ uint32_t xcd_run(uint32_t b, uint32_t n) {
+  if constexpr (M == 1) {
+    return b;
+  } else {
+    constexpr uint32_t G = 8u * M;
+    if (b >= n - n % G) return b;
+    const uint32_t r = b % G;
+    return b - r + (r % 8u) * M + r / 8u;
+  }
+}
+
 constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within each group of 8
@@ -768,7 +818,8 @@ __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
   __shared__ uint32_t s_cmax[kColGroups > 1 ? kColGroups : 1][NW][kColThreads];
   keep_denormals();
   const uint32_t lane = threadIdx.x % kColThreads, rg = threadIdx.x / kColThreads;   // rg: uniform per wave
-  const uint32_t band = mxq_quot(blockIdx.x, groups), grp = blockIdx.x - band * groups.d;
+  const uint32_t bid = xcd_run<sizeof(T) == 2 ? MXQ_COL_XCD_RUN_BF16 : MXQ_COL_XCD_RUN_FP32>(blockIdx.x, gridDim.x);
+  const uint32_t band = mxq_quot(bid, groups), grp = bid - band * groups.d;
   const int64_t col0 = (int64_t)grp * (kColThreads * EPL) + (int64_t)lane * EPL;
   const int64_t rb = (int64_t)band * 32 + (int64_t)rg * R;   // this lane group's first row
   const bool in = col0 < K;
@@ -877,11 +928,6 @@ __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
 #ifndef MXQ_TILES_PER_WG
 #define MXQ_TILES_PER_WG 1
 #endif
-#ifndef MXQ_FOLD_THREADS
-#define MXQ_FOLD_THREADS 1024
-#endif
-constexpr int kFoldThreads = MXQ_FOLD_THREADS;
-constexpr int kFoldWaves = kFoldThreads / 64;
 
 constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within each row of 16
 
@@ -899,13 +945,17 @@ struct FoldGeom {
   static constexpr int kJ = sizeof(T) == 2 ? MXQ_TILES_PER_WG : (MXQ_TILES_PER_WG > 2 ? 2 : MXQ_TILES_PER_WG);
   static constexpr int kCPT = 128 / kEPL;                  // lanes across one tile row (16 / 32)
   static constexpr int kLPR = kCPT * kJ;                   // lanes across the band row (<= 64)
-  static constexpr int kRowsPerPass = kFoldThreads / kLPR;
+  static constexpr int kThreads = sizeof(T) == 2 ? MXQ_FOLD_THREADS_BF16 : MXQ_FOLD_THREADS_FP32;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kRun = sizeof(T) == 2 ? MXQ_FOLD_XCD_RUN_BF16 : MXQ_FOLD_XCD_RUN_FP32;
+  static constexpr int kRowsPerPass = kThreads / kLPR;
   static constexpr int kPasses = 128 / kRowsPerPass;
   static_assert(kLPR <= 64, "a band row must fit in one wave");
+  static_assert(kThreads % 64 == 0 && kThreads <= 1024 && kRowsPerPass * kPasses == 128, "fold geometry");
 };
 
 // The fold of one group of J side-by-side tiles (tile row tr, group tg) by the
-// whole workgroup (a barrier inside); s_max: kFoldWaves * J words of LDS.  A
+// whole workgroup (a barrier inside); s_max: G::kWaves * J words of LDS.  A
 // non-zero no-op flag leaves every output untouched.  FULL: whole tile groups
 // (rows a multiple of 128, K of 128 J, a band's payload under 2 GiB), so no
 // bounds checks; payload stores are buffer stores (nt) off the band's start.
@@ -958,7 +1008,7 @@ __device__ __forceinline__ void fold_tiles(const T* __restrict__ x, int64_t ld_x
   if (lane < (uint32_t)LPR && lane % CPT == 0) s_max[wave][j] = m;
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < kFoldWaves; v++) m = max(m, s_max[v][j]);
+  for (int v = 0; v < G::kWaves; v++) m = max(m, s_max[v][j]);
   const uint32_t code = m > 6u ? m - 6u : 0u;              // S + 127 = max(M - 6, -127) + 127
   const uint32_t tc = tg * J + j;
   if (tid < (uint32_t)LPR && tid % CPT == 0 && tc < tiles_per_row) tile_code[(int64_t)tr * tile_ld + tc] = (uint8_t)code;
@@ -976,14 +1026,15 @@ __device__ __forceinline__ void fold_tiles(const T* __restrict__ x, int64_t ld_x
 }
 
 template <typename T, bool VEC, bool FULL>
-__global__ __launch_bounds__(kFoldThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
+__global__ __launch_bounds__(FoldGeom<T>::kThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
                                                             int64_t K, uint8_t* __restrict__ data,
                                                             uint8_t* __restrict__ tile_code, int64_t tile_ld,
                                                             uint32_t tiles_per_row, MxqDivisor groups_per_row,
                                                             const int32_t* __restrict__ noop) {
-  __shared__ uint32_t s_max[kFoldWaves][FoldGeom<T>::kJ];
+  __shared__ uint32_t s_max[FoldGeom<T>::kWaves][FoldGeom<T>::kJ];
   keep_denormals();
-  const uint32_t tr = mxq_quot(blockIdx.x, groups_per_row), tg = blockIdx.x - tr * groups_per_row.d;
+  const uint32_t bid = xcd_run<FoldGeom<T>::kRun>(blockIdx.x, gridDim.x);
+  const uint32_t tr = mxq_quot(bid, groups_per_row), tg = bid - tr * groups_per_row.d;
   fold_tiles<T, VEC, FULL>(x, ld_x, rows, K, data, tile_code, tile_ld, tiles_per_row, tr, tg, noop, s_max);
 }
 
@@ -1004,8 +1055,8 @@ struct FoldGroupTable {
 static_assert(sizeof(FoldGroupTable) <= 3840, "the table must fit the kernel-argument segment");
 
 template <typename T>
-__global__ __launch_bounds__(kFoldThreads) void block128_grouped_kernel(const FoldGroupTable tab) {
-  __shared__ uint32_t s_max[kFoldWaves][FoldGeom<T>::kJ];
+__global__ __launch_bounds__(FoldGeom<T>::kThreads) void block128_grouped_kernel(const FoldGroupTable tab) {
+  __shared__ uint32_t s_max[FoldGeom<T>::kWaves][FoldGeom<T>::kJ];
   const FoldGroupDesc d = tab.g[blockIdx.y];
   if (blockIdx.x >= d.n_groups) return;                      // uniform: past this weight's tiles
   keep_denormals();
@@ -1071,24 +1122,6 @@ __device__ __forceinline__ u32x4 decode8_bf16_each(u32x2 q, const float (&s)[8])
                bf16_pair_of_fp8_each<kE5M2, false>(q[1], s[4], s[5]), bf16_pair_of_fp8_each<kE5M2, true>(q[1], s[6], s[7])};
 }
 
-// Workgroup order for kernels whose neighbouring workgroups share lines of
-// block codes.  The dispatcher deals workgroup b to XCD b % 8, and each XCD has
-// its own L2, so in the plain order a code line that M neighbouring workgroups
-// read is fetched by M L2s.  With M > 1, each run of 8 M workgroups is
-// reordered so that XCD x takes the M consecutive logical workgroups
-// 8 M g + M x .. 8 M g + M x + M - 1; the last, partial run keeps the plain
-// order.  A permutation of 0 .. n - 1.
-template <int M>
-__device__ __forceinline__ uint32_t xcd_run(uint32_t b, uint32_t n) {
-  if constexpr (M == 1) {
-    return b;
-  } else {
-    constexpr uint32_t G = 8u * M;
-    if (b >= n - n % G) return b;
-    const uint32_t r = b % G;
-    return b - r + (r % 8u) * M + r / 8u;
-  }
-}
 
 // The decode's body: workgroup wg's kDequantSteps steps of one weight.  The
 // single and grouped kernels both run it.
@@ -1899,7 +1932,7 @@ int launch_block128(const void* x, int64_t ld_x, int64_t rows, int64_t K, uint8_
   if (groups >= kMaxSteps) return MXQ_ERR_SHAPE;
   constexpr int EPL = Fmt<T>::kEPL;
   const bool vec = aligned(x, 16) && ld_x % EPL == 0 && K % EPL == 0 && aligned(data, EPL);
-  const dim3 grid((uint32_t)groups), block(kFoldThreads);
+  const dim3 grid((uint32_t)groups), block(FoldGeom<T>::kThreads);
   if constexpr (sizeof(T) == 4 && MXQ_FOLD_FULL) {
     if (vec && rows % 128 == 0 && K % (128 * J) == 0 && fits32(128 * K)) {
       hipLaunchKernelGGL((block128_kernel<T, true, true>), grid, block, 0, s, (const T*)x, ld_x, rows, K, data,
@@ -2087,7 +2120,7 @@ int launch_block128_grouped(const mxq_block128_group* gs, int64_t n, hipStream_t
   int64_t count = 0, max_w = 0, sum_w = 0;
   auto flush = [&]() -> int {
     if (count == 0) return MXQ_OK;
-    hipLaunchKernelGGL((block128_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(kFoldThreads), 0,
+    hipLaunchKernelGGL((block128_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(FoldGeom<T>::kThreads), 0,
                        s, tab);
     count = max_w = sum_w = 0;
     return launch_status();

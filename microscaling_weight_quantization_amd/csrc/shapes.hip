@@ -108,18 +108,42 @@ __global__ __launch_bounds__(64) void decode_kernel(const uint8_t* __restrict__ 
   store_nt(u32x4{a + c, a >> 1, b ^ c, b >> 1}, out + (uint64_t)blockIdx.x * 1024, t * 16);
 }
 
-// The 128x128 fold's pattern: one 1024-lane workgroup per tile, 16-byte chunks,
-// 128 * ES / 16 lanes across a tile row (16 for ES 2, 32 for ES 4), every chunk
-// loaded first, the fold's wave maximum, a tile-wide maximum through LDS and a
-// barrier (BARRIER), then 16 / ES bytes out per chunk and one byte per tile.
+// The 128x128 fold's workgroup by element size: lanes per tile (512 for ES 2,
+// 1024 for ES 4; 128 * ES / 16 lanes across a tile row, 16-byte chunks), and
+// the tile order: the workgroups are dealt to the 8 XCDs in turn, and each run
+// of 8 M workgroups is reordered so that XCD x takes M side-by-side tiles
+// (M = 8 for ES 2, 4 for ES 4; the last, partial run keeps the plain order).
+template <int ES>
+struct FoldShape {
+  static constexpr int kThreads = ES == 2 ? 512 : 1024;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kRun = ES == 2 ? 8 : 4;
+  static constexpr int kCPT = 128 * ES / 16;              // lanes across one tile row
+  static constexpr int kRPP = kThreads / kCPT;            // tile rows per pass
+  static constexpr int kP = 128 / kRPP;                   // chunks per lane
+};
+template <int M>
+__device__ __forceinline__ uint32_t in_runs(uint32_t b, uint32_t n) {
+  constexpr uint32_t G = 8u * M;
+  if (b >= n - n % G) return b;
+  const uint32_t r = b % G;
+  return b - r + (r % 8u) * M + r / 8u;
+}
+
+// The 128x128 fold's pattern: one FoldShape workgroup per tile, in the fold's
+// tile order, every chunk loaded first, the fold's wave maximum, a tile-wide
+// maximum through LDS and a barrier (BARRIER), then 16 / ES bytes out per chunk
+// and one byte per tile.
 template <int ES, bool BARRIER>
-__global__ __launch_bounds__(1024) void tile_kernel(const uint8_t* __restrict__ in, int64_t K, uint8_t* __restrict__ out,
-                                                    uint8_t* __restrict__ codes, uint32_t tiles_per_row) {
-  constexpr int CPT = 128 * ES / 16;         // lanes across one tile row
-  constexpr int RPP = 1024 / CPT;            // tile rows per pass
-  constexpr int P = 128 / RPP;               // chunks per lane
-  __shared__ uint32_t s_max[16];
-  const uint32_t t = threadIdx.x, tr = blockIdx.x / tiles_per_row, tc = blockIdx.x % tiles_per_row;
+__global__ __launch_bounds__(FoldShape<ES>::kThreads) void tile_kernel(const uint8_t* __restrict__ in, int64_t K,
+                                                                    uint8_t* __restrict__ out,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    uint32_t tiles_per_row) {
+  using S = FoldShape<ES>;
+  constexpr int CPT = S::kCPT, RPP = S::kRPP, P = S::kP;
+  __shared__ uint32_t s_max[S::kWaves];
+  const uint32_t t = threadIdx.x, bid = in_runs<S::kRun>(blockIdx.x, gridDim.x);
+  const uint32_t tr = bid / tiles_per_row, tc = bid % tiles_per_row;
   const uint64_t r0 = (uint64_t)tr * 128 + t / CPT, c0 = (uint64_t)tc * 128 + (t % CPT) * (16 / ES);
   u32x4 w[P];
 #pragma unroll
@@ -133,35 +157,42 @@ __global__ __launch_bounds__(1024) void tile_kernel(const uint8_t* __restrict__ 
     if ((t & 63u) == 0) s_max[t >> 6] = m;
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 16; v++) m = max(m, s_max[v]);
+    for (int v = 0; v < S::kWaves; v++) m = max(m, s_max[v]);
   }
 #pragma unroll
   for (int i = 0; i < P; i++)   // stores off the band's first row (a base the whole workgroup shares)
     store_nt(Narrow<ES>::of(w[i], m), out + (uint64_t)tr * 128 * K, (uint32_t)((r0 - (uint64_t)tr * 128 + i * RPP) * K + c0));
-  if (t == 0) codes[blockIdx.x] = (uint8_t)m;
+  if (t == 0) codes[bid] = (uint8_t)m;
 }
 
-// The fold's workgroup (1024 lanes, two 16-byte chunks per lane: chunks l and
-// 1024 + l of the workgroup's 32 KB) over a plain contiguous stream, with the
-// same wave maximum, with or without the barrier: the tile shape's arithmetic
-// and synchronization on linear addresses.
+// The fold's workgroup (FoldShape: its lanes and chunks per lane, chunk l + i *
+// lanes of the workgroup's 128 * 128 * ES bytes) over a plain contiguous stream
+// in the plain order, with the same wave maximum, with or without the barrier:
+// the tile shape's arithmetic and synchronization on linear addresses.
 template <int ES, bool BARRIER>
-__global__ __launch_bounds__(1024) void linear_kernel(const u32x4* __restrict__ in, uint8_t* __restrict__ out) {
-  __shared__ uint32_t s_max[16];
+__global__ __launch_bounds__(FoldShape<ES>::kThreads) void linear_kernel(const u32x4* __restrict__ in,
+                                                                      uint8_t* __restrict__ out) {
+  using S = FoldShape<ES>;
+  constexpr int N = S::kThreads, P = S::kP;
+  __shared__ uint32_t s_max[S::kWaves];
   const uint32_t t = threadIdx.x;
-  const uint64_t c = (uint64_t)blockIdx.x * 2048 + t;
-  const u32x4 a = __builtin_nontemporal_load(in + c), b = __builtin_nontemporal_load(in + c + 1024);
-  uint32_t m = max(max(max(a[0], a[1]), max(a[2], a[3])), max(max(b[0], b[1]), max(b[2], b[3]))) >> 24;
+  const uint64_t c = (uint64_t)blockIdx.x * (N * P) + t;
+  u32x4 w[P];
+#pragma unroll
+  for (int i = 0; i < P; i++) w[i] = __builtin_nontemporal_load(in + c + i * N);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < P; i++) m = max(m, max(max(w[i][0], w[i][1]), max(w[i][2], w[i][3])) >> 24);
   m = wave_max(m);
   if constexpr (BARRIER) {
     if ((t & 63u) == 0) s_max[t >> 6] = m;
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 16; v++) m = max(m, s_max[v]);
+    for (int v = 0; v < S::kWaves; v++) m = max(m, s_max[v]);
   }
-  uint8_t* o = out + (uint64_t)blockIdx.x * 2048 * (16 / ES);
-  store_nt(Narrow<ES>::of(a, m), o, t * (16 / ES));
-  store_nt(Narrow<ES>::of(b, m), o, (1024 + t) * (16 / ES));
+  uint8_t* o = out + (uint64_t)blockIdx.x * (N * P) * (16 / ES);
+#pragma unroll
+  for (int i = 0; i < P; i++) store_nt(Narrow<ES>::of(w[i], m), o, (i * N + t) * (16 / ES));
 }
 
 // The row lift from packed MXFP4's pattern: 64-lane workgroups, 8 packed bytes
@@ -210,24 +241,27 @@ int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t
     case MXQ_SHAPE_TILE_NO_BARRIER: {
       if (rows % 128 || K % 128 || 128 * K >= ((int64_t)1 << 31)) return 1;   // a band's payload: 32-bit offsets
       const uint32_t tpr = (uint32_t)(K / 128), tiles = (uint32_t)(rows / 128) * tpr;
+      constexpr int N = FoldShape<ES>::kThreads;
       if (shape == MXQ_SHAPE_TILE)
-        hipLaunchKernelGGL((tile_kernel<ES, true>), dim3(tiles), dim3(1024), 0, s, (const uint8_t*)in, K, (uint8_t*)out,
+        hipLaunchKernelGGL((tile_kernel<ES, true>), dim3(tiles), dim3(N), 0, s, (const uint8_t*)in, K, (uint8_t*)out,
                            (uint8_t*)codes, tpr);
       else
-        hipLaunchKernelGGL((tile_kernel<ES, false>), dim3(tiles), dim3(1024), 0, s, (const uint8_t*)in, K,
+        hipLaunchKernelGGL((tile_kernel<ES, false>), dim3(tiles), dim3(N), 0, s, (const uint8_t*)in, K,
                            (uint8_t*)out, (uint8_t*)codes, tpr);
       return status();
     }
-    case MXQ_SHAPE_LINEAR1024:
-    case MXQ_SHAPE_LINEAR1024_NO_BARRIER:
-      if (bytes % 32768) return 1;
-      if (shape == MXQ_SHAPE_LINEAR1024)
-        hipLaunchKernelGGL((linear_kernel<ES, true>), dim3(chunks / 2048), dim3(1024), 0, s, (const u32x4*)in,
+    case MXQ_SHAPE_LINEAR_FOLD:
+    case MXQ_SHAPE_LINEAR_FOLD_NO_BARRIER: {
+      constexpr int N = FoldShape<ES>::kThreads, PER = N * FoldShape<ES>::kP;   // chunks per workgroup
+      if (chunks % PER) return 1;
+      if (shape == MXQ_SHAPE_LINEAR_FOLD)
+        hipLaunchKernelGGL((linear_kernel<ES, true>), dim3(chunks / PER), dim3(N), 0, s, (const u32x4*)in,
                            (uint8_t*)out);
       else
-        hipLaunchKernelGGL((linear_kernel<ES, false>), dim3(chunks / 2048), dim3(1024), 0, s, (const u32x4*)in,
+        hipLaunchKernelGGL((linear_kernel<ES, false>), dim3(chunks / PER), dim3(N), 0, s, (const u32x4*)in,
                            (uint8_t*)out);
       return status();
+    }
     case MXQ_SHAPE_PACKED_ROW:
       if ((rows * K) % 1024) return 1;
       hipLaunchKernelGGL(packed_row_kernel, dim3((uint32_t)(rows * K / 1024)), dim3(64), 0, s, (const u32x2*)in,

@@ -376,7 +376,7 @@ def test_access_shape_library_loads_and_refuses_bad_arguments():
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     assert set(re.findall(r"\sT\s+(mxq_\w+)$", out, flags=re.M)) == {"mxq_shape_run"}
     header = os.path.join(B.ROOT, "include", "mxq_shapes.h")
-    src = '#include "mxq_shapes.h"\nint main(void) { return MXQ_SHAPE_LINEAR1024_NO_BARRIER == 7 ? 0 : 1; }\n'
+    src = '#include "mxq_shapes.h"\nint main(void) { return MXQ_SHAPE_LINEAR_FOLD_NO_BARRIER == 7 ? 0 : 1; }\n'
     r = subprocess.run(["gcc", "-fsyntax-only", "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(header),
                         "-I", "/opt/rocm/include", "-x", "c", "-"], input=src, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
@@ -389,4 +389,5 @@ def test_access_shape_library_loads_and_refuses_bad_arguments():
     assert L.mxq_shape_run(99, 2, fake, fake, fake, 8, 512, None) == 1         # no such shape
     assert L.mxq_shape_run(1, 2, fake, fake, fake, 1, 64, None) == 1           # not whole workgroups
     assert L.mxq_shape_run(4, 2, fake, fake, fake, 100, 128, None) == 1        # rows not tiles
+    assert L.mxq_shape_run(6, 2, fake, fake, fake, 8, 512, None) == 1          # not whole tiles of elements
     assert L.mxq_shape_run(0, 2, fake, fake, fake, 0, 512, None) == 1          # empty
