@@ -89,6 +89,17 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_CODE_AUX
 #define MXQ_CODE_AUX 0
 #endif
+// The full-step MXFP4 encode's gathered code stores, by input type: 1 = after
+// every packed-payload store of the workgroup, 0 = each step's right after its
+// payload.  After: fp32 8192 x 8192 51.3 -> 47.9 us, 28672 x 8192 168.6 ->
+// 163.3 us; bf16 8192 x 8192 28.7 -> 28.0 us but 16384 x 16384 104.3 -> 107.9
+// and 28672 x 8192 91.8 -> 94.4 us (burst means over four orders).
+#ifndef MXQ_Q4_CODES_LAST_BF16
+#define MXQ_Q4_CODES_LAST_BF16 0
+#endif
+#ifndef MXQ_Q4_CODES_LAST_FP32
+#define MXQ_Q4_CODES_LAST_FP32 1
+#endif
 #ifndef MXQ_Q4_CODE_WORDS
 #define MXQ_Q4_CODE_WORDS 1       // the same for the full-step MXFP4 encode
 #endif
@@ -1340,6 +1351,11 @@ __device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, in
         w[u] = load_chunk<T, VEC>(x + (int64_t)row * ld_x, seg * G::kElemsPerStep + lane_col, K);
     }
   }
+  using CG = CodeGather<G::kLPB>;
+  constexpr bool kLast =
+      FULL && MXQ_Q4_CODE_WORDS && (sizeof(T) == 2 ? MXQ_Q4_CODES_LAST_BF16 : MXQ_Q4_CODES_LAST_FP32);
+  uint32_t cw[kQ4Steps];                                   // kLast: each step's gathered codes and row
+  uint8_t* cr[kQ4Steps];
 #pragma unroll
   for (int u = 0; u < kQ4Steps; u++) {
     const uint32_t step = wg * kQ4Steps + u;
@@ -1352,8 +1368,10 @@ __device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, in
         stream_store_at((N)f, packed + (int64_t)row * pw, (uint32_t)(col0 / 2));
         uint8_t* const crow = scale + (int64_t)row * scale_ld + seg * G::kBlocksPerStep;
         const uint32_t code = b.poison ? 255u : b.eb;
-        if constexpr (MXQ_Q4_CODE_WORDS) {
-          using CG = CodeGather<G::kLPB>;
+        if constexpr (kLast) {
+          cw[u] = CG::gather(code);
+          cr[u] = crow;
+        } else if constexpr (MXQ_Q4_CODE_WORDS) {
           const uint32_t codes = CG::gather(code);
           if (tid % CG::kLanes == 0) CG::store(crow, tid / G::kLPB, codes);
         } else {
@@ -1373,6 +1391,12 @@ __device__ __forceinline__ void quantize_mxfp4_steps(const T* __restrict__ x, in
         if (tid % G::kLPB == 0) scale[(int64_t)row * scale_ld + col0 / 32] = (uint8_t)(b.poison ? 255u : b.eb);
       }
     }
+  }
+  if constexpr (kLast) {
+    // the block codes go out after every packed-payload store of the workgroup
+#pragma unroll
+    for (int u = 0; u < kQ4Steps; u++)
+      if (tid % CG::kLanes == 0) CG::store(cr[u], tid / G::kLPB, cw[u]);
   }
 }
 
