@@ -265,8 +265,8 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 // the same for the whole wave (nbytes: the row's length, below 2^31).  With
 // MXQ_PROJ_STORE_SC1 it is a buffer store carrying the nt and sc1 bits, which
 // measured about 3% faster than nt alone for the projection's read-one /
-// write-one stream (and slower for the other kernels, the fused projection +
-// row lift included, which keep stream_store).
+// write-one stream.  The FP8 decodes keep non-temporal global stores: buffer
+// stores, with nt, sc1 or both, made their bf16 output 2-4% slower.
 __device__ __forceinline__ void stream_store_row_sc1(u32x4 v, void* base, uint32_t nbytes, uint32_t off) {
 #if MXQ_PROJ_STORE_SC1
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
@@ -278,16 +278,27 @@ __device__ __forceinline__ void stream_store_row_sc1(u32x4 v, void* base, uint32
 }
 
 // 2-, 4-, 8- or 16-byte streaming store at byte offset `off` of a row whose base
-// address is the same for the whole wave: a buffer store carrying the nt bit.
-// (The compiler can drop the non-temporal hint of a plain store when it merges
-// code paths; the buffer form keeps the cache policy in the instruction.)
+// address is the same for the whole wave: a buffer store carrying its
+// cache-policy bits (the compiler can drop the non-temporal hint of a plain
+// store when it merges code paths; the buffer form keeps it in the
+// instruction).  The bits are nt and sc1.  Against nt alone,
+// burst means over four orders: row lift bf16 8192 x 8192 33.2 -> 33.0 us,
+// 28672 x 8192 109.3 -> 106.8 us, fp32 55.4 -> 53.3 us and 180.7 -> 176.4 us;
+// fused projection + row lift bf16 53.8 -> 52.4 us and 184.9 -> 181.3 us; fp32
+// MXFP4 encode 48.0 -> 47.5 us and 163.8 -> 160.9 us; the fp32 fold and the row
+// lift from packed MXFP4 within 0.5%.  (sc1 alone was 4-5% faster at 8192 x
+// 8192 but 4-5% slower at 28672 x 8192.)
+#ifndef MXQ_PAYLOAD_AUX
+#define MXQ_PAYLOAD_AUX 18
+#endif
 template <typename V>
 __device__ __forceinline__ void stream_store_at(V v, void* base, uint32_t off) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
-  if constexpr (sizeof(V) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 2);
-  else if constexpr (sizeof(V) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 2);
-  else if constexpr (sizeof(V) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 2);
-  else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 2);
+  constexpr int A = MXQ_PAYLOAD_AUX;
+  if constexpr (sizeof(V) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, A);
+  else if constexpr (sizeof(V) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, A);
+  else if constexpr (sizeof(V) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, A);
+  else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, A);
 }
 
 // ------------------------------------------------------------------------------------
