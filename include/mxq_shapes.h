@@ -35,7 +35,7 @@ extern "C" {
 
 enum {
   MXQ_SHAPE_COPY16 = 0,                 /* projection: 64 lanes, 16 B in, 16 B out (nt sc1) per lane */
-  MXQ_SHAPE_ROW = 1,                    /* row lift payload: 256 lanes, two 16 B chunks in, 16/es B out (nt) each */
+  MXQ_SHAPE_ROW = 1,                    /* row lift payload: 256 lanes, two 16 B chunks in, 16/es B out (nt sc1) each */
   MXQ_SHAPE_ROW_CODES = 2,              /* ROW plus one code byte per 32 elements (sc1) */
   MXQ_SHAPE_DECODE = 3,                 /* row decode: 64 lanes, 16/es B + a code byte in, 16 B out (nt) */
   MXQ_SHAPE_TILE = 4,                   /* 128x128 fold: its workgroup per tile in its tile order, all loads,
@@ -43,7 +43,7 @@ enum {
   MXQ_SHAPE_TILE_NO_BARRIER = 5,        /* TILE without the workgroup-wide maximum (wave-wide only) */
   MXQ_SHAPE_LINEAR_FOLD = 6,            /* the fold's workgroup (lanes, chunks per lane) over a contiguous stream */
   MXQ_SHAPE_LINEAR_FOLD_NO_BARRIER = 7, /* LINEAR_FOLD without the barrier */
-  MXQ_SHAPE_PACKED_ROW = 8              /* row lift from packed MXFP4: 64 lanes, 8 B + a code byte in, 16 B out (nt),
+  MXQ_SHAPE_PACKED_ROW = 8              /* row lift from packed MXFP4: 64 lanes, 8 B + a code byte in, 16 B out (nt sc1),
                                            gathered 4-byte code stores back over the codes read */
 };
 

@@ -64,8 +64,8 @@ __global__ __launch_bounds__(64) void copy16_kernel(const u32x4* __restrict__ in
 
 // The row lift's pattern: 256-lane workgroups, two 16-byte chunks per lane
 // (chunks l and 256 + l of the workgroup's 8 KB, both loaded before any store),
-// 16 / ES bytes out per chunk (nt); with CODES also one byte per 32 elements
-// (the lane that holds a block's first chunk), stored with the sc1 bit.
+// 16 / ES bytes out per chunk (nt sc1); with CODES also one byte per 32
+// elements (the lane that holds a block's first chunk), stored with the sc1 bit.
 template <int ES, bool CODES>
 __global__ __launch_bounds__(256) void row_kernel(const u32x4* __restrict__ in, uint8_t* __restrict__ out,
                                                   uint8_t* __restrict__ codes) {
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void row_kernel(const u32x4* __restrict__ in, 
     m = max(m, dpp<0xB1>(m));
     m = max(m, dpp<0x4E>(m));
     const uint32_t c = u * 256 + t;                 // the chunk within the workgroup
-    store_nt(Narrow<ES>::of(w[u], m), out + (uint64_t)blockIdx.x * (8192 / ES), c * (16 / ES));
+    store_nt<2 | 16>(Narrow<ES>::of(w[u], m), out + (uint64_t)blockIdx.x * (8192 / ES), c * (16 / ES));
     if (CODES && t % kLanesPerBlock == 0) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           codes + (uint64_t)blockIdx.x * (512 / kLanesPerBlock), 0, 0x7FFFFFFF, 0x00020000);
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(FoldShape<ES>::kThreads) void linear_kernel(const u
 
 // The row lift from packed MXFP4's pattern: 64-lane workgroups, 8 packed bytes
 // and one code byte (two lanes per code) in per lane, 16 payload bytes out
-// (nt), and the codes of each 8 lanes gathered into one 4-byte store.  The
+// (nt sc1), and the codes of each 8 lanes gathered into one 4-byte store.  The
 // gathered word is written back over the codes it was read from (the same
 // bytes), so the shape needs no second code buffer.
 __global__ __launch_bounds__(64) void packed_row_kernel(const u32x2* __restrict__ in, uint8_t* __restrict__ out,
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64) void packed_row_kernel(const u32x2* __restrict_
   const u32x2 f = __builtin_nontemporal_load(in + (uint64_t)blockIdx.x * 64 + t);
   uint8_t* const wcodes = codes + (uint64_t)blockIdx.x * 32;     // the workgroup's 32 codes
   const uint32_t c = wcodes[t / 2];
-  store_nt(u32x4{f[0] ^ c, f[0] >> 4, f[1] + c, f[1] >> 4}, out + (uint64_t)blockIdx.x * 1024, t * 16);
+  store_nt<2 | 16>(u32x4{f[0] ^ c, f[0] >> 4, f[1] + c, f[1] >> 4}, out + (uint64_t)blockIdx.x * 1024, t * 16);
   const uint32_t w = c | (dpp<0x102>(c) << 8) | (dpp<0x104>(c) << 16) | (dpp<0x106>(c) << 24);
   if (t % 8 == 0) store_nt<0>(w, wcodes, t / 2);
 }
