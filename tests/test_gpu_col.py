@@ -97,6 +97,18 @@ def test_col_ragged_shapes(dev, rows, K, dtype):
     check_col(np.ascontiguousarray(flat[: rows * K].reshape(rows, K)), dev, pad=rows % 3)
 
 
+@pytest.mark.parametrize("rows,K", [(1024, 8320), (2016, 2304), (100, 300), (2048, 2048)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_col_band_order_tails(dev, rows, K, dtype):
+    """For fp32 the columnwise kernel deals its workgroups (32-row band x 256
+    columns) to the XCDs in runs of 8, in groups of 64, and the last, partial
+    group keeps the plain order: 1056, 567, 8 and 512 workgroups leave tails
+    of 32, 55, 8 and 0.  bf16 (plain order) on the same shapes."""
+    src = W.c2_planted() if dtype == "bf16" else W.c2_planted_fp32()
+    bits = np.ascontiguousarray(np.resize(src.reshape(-1), rows * K).reshape(rows, K))
+    check_col(bits, dev, pad=3)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_col_strided_and_misaligned_views(dev, dtype):
     base = W.c2_planted() if dtype == "bf16" else W.fp32_fuzz(64 * 200).reshape(64, 200)

@@ -481,6 +481,19 @@ def test_step_boundary_shapes(dev, dtype, rows, K):
     check_packed(bits, dev)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("rows,K", [(1024, 8320), (640, 16256), (1000, 4100), (256, 8192)])
+def test_fold_tile_order_tails(dev, dtype, rows, K):
+    """The 128x128 fold deals its tiles to the XCDs in runs (8 side-by-side
+    tiles per XCD for bf16, 4 for fp32, so groups of 64 or 32 tiles), and the
+    last, partial group keeps the plain order.  Tile counts 520, 635, 264 and
+    128 leave tails of 8, 59, 8 and 0 tiles (bf16) and 8, 27, 8 and 0 (fp32);
+    every tile against the oracle."""
+    src = W.c2_planted() if dtype == "bf16" else W.c2_planted_fp32()
+    bits = np.ascontiguousarray(np.resize(src.reshape(-1), rows * K).reshape(rows, K))
+    check_all(bits, dev, scale_ld=(K + 31) // 32 + 4)
+
+
 @pytest.mark.parametrize("K", [512, 640, 4096, 4128])   # ceil(K/32) = 16, 20, 128, 129
 def test_export_every_unit_width(dev, K):
     """The unpadded export against the oracle for code rows of 16, 20, 128 and
