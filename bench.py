@@ -61,11 +61,13 @@ ORDER_REPS, ORDER_LAUNCHES = 4, 60   # --orders: bursts of 60 launches, median o
 # after the step: name -> (shape code, input buffer, code buffer).  Each moves the bytes of the
 # kernel named in SHAPE_KERNEL in that kernel's access pattern, with no quantization arithmetic;
 # the tile and linear variants split the fold's pattern into its parts (tile-shaped addressing,
-# the workgroup-wide barrier, the 1024-lane two-chunk workgroup).
+# the workgroup-wide barrier, the fold's workgroup), and the read and write streams give the
+# machine's read-only and write-only rates.
 SHAPES_OF = {"shape_copy16": (0, "x", "scale2"), "shape_row": (1, "x", "scale2"), "shape_row_codes": (2, "x", "scale2"),
              "shape_decode": (3, "data", "scale_c"), "shape_tile": (4, "x", "scale2"),
              "shape_tile_no_barrier": (5, "x", "scale2"), "shape_linear_fold": (6, "x", "scale2"),
-             "shape_linear_fold_no_barrier": (7, "x", "scale2"), "shape_packed_row": (8, "packed", "pscale")}
+             "shape_linear_fold_no_barrier": (7, "x", "scale2"), "shape_packed_row": (8, "packed", "pscale"),
+             "shape_read": (9, "x", "scale2"), "shape_write": (10, "x", "scale2")}
 SHAPE_KERNEL = {"shape_copy16": "proj", "shape_row_codes": "row", "shape_decode": "dec_row", "shape_tile": "block128",
                 "shape_packed_row": "packed_to_row"}
 # committed rocprofv3 counter summaries of the 8192 x 8192 weight, per dtype
@@ -515,7 +517,8 @@ def main():
                    "shape_decode": nbytes["dec_row"], "shape_tile": nbytes["block128"],
                    "shape_tile_no_barrier": nbytes["block128"], "shape_linear_fold": es * n_el + n_el,
                    "shape_linear_fold_no_barrier": es * n_el + n_el,
-                   "shape_packed_row": packed_bytes(rows, K, es)["packed_to_row"]}
+                   "shape_packed_row": packed_bytes(rows, K, es)["packed_to_row"],
+                   "shape_read": es * n_el, "shape_write": es * n_el}
     shapes_out = {}
     for n in shape_names:
         us, med, lo = burst_stats(n)

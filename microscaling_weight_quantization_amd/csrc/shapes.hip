@@ -213,6 +213,26 @@ __global__ __launch_bounds__(64) void packed_row_kernel(const u32x2* __restrict_
 
 int status() { return hipGetLastError() == hipSuccess ? 0 : 2; }
 
+// The machine's plain streams, for scale: a read-only stream (64-lane
+// workgroups, 8 chunks of 16 B per lane, nt; the loads feed a test that
+// practically never stores) and a write-only one (4 chunks per lane, nt sc1).
+// With one chunk per lane either is bound by how fast one-wave workgroups are
+// dispatched, so they take several.
+__global__ __launch_bounds__(64) void read_kernel(const u32x4* __restrict__ in, uint32_t* __restrict__ sink) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const u32x4 w = __builtin_nontemporal_load(in + ((uint64_t)blockIdx.x * 8 + u) * 64 + threadIdx.x);
+    x ^= w[0] ^ (w[1] << 1) ^ (w[2] << 2) ^ (w[3] << 3);
+  }
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+__global__ __launch_bounds__(64) void write_kernel(uint8_t* __restrict__ out) {
+  const u32x4 v = u32x4{blockIdx.x, threadIdx.x, 0x01010101u, 0x02020202u};
+#pragma unroll
+  for (int u = 0; u < 4; u++) store_nt<2 | 16>(v, out + ((uint64_t)blockIdx.x * 4 + u) * 1024, threadIdx.x * 16);
+}
+
 template <int ES>
 int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t K, hipStream_t s) {
   const int64_t bytes = rows * K * ES;                       // input bytes
@@ -266,6 +286,14 @@ int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t
       if ((rows * K) % 1024) return 1;
       hipLaunchKernelGGL(packed_row_kernel, dim3((uint32_t)(rows * K / 1024)), dim3(64), 0, s, (const u32x2*)in,
                          (uint8_t*)out, (uint8_t*)codes);
+      return status();
+    case MXQ_SHAPE_READ:
+      if (bytes % 8192) return 1;
+      hipLaunchKernelGGL(read_kernel, dim3(chunks / 512), dim3(64), 0, s, (const u32x4*)in, (uint32_t*)out);
+      return status();
+    case MXQ_SHAPE_WRITE:
+      if (bytes % 4096) return 1;
+      hipLaunchKernelGGL(write_kernel, dim3(chunks / 256), dim3(64), 0, s, (uint8_t*)out);
       return status();
     default:
       return 1;
