@@ -295,10 +295,14 @@ template <typename V>
 __device__ __forceinline__ void stream_store_at(V v, void* base, uint32_t off) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, 0x00020000);
   constexpr int A = MXQ_PAYLOAD_AUX;
-  if constexpr (sizeof(V) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, A);
-  else if constexpr (sizeof(V) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, A);
-  else if constexpr (sizeof(V) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, A);
-  else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, A);
+  if constexpr (sizeof(V) == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, A);
+  else if constexpr (sizeof(V) == 8)
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, A);
+  else if constexpr (sizeof(V) == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, A);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, A);
 }
 
 // ------------------------------------------------------------------------------------
@@ -944,8 +948,9 @@ __global__ __launch_bounds__(kColThreads * kColGroups) void col_kernel(
 // run of J * 256 bytes (bf16) per load.  Each lane keeps only the E2M1 nibbles,
 // block exponents and poison bits of its chunks (all in one tile); the largest
 // finite block exponent of every tile is reduced with DPP inside each 16-lane
-// row, shuffles across rows of the wave, and LDS across the workgroup's waves;
-// then every lane folds and writes its payload.
+// row, readlanes (one tile per workgroup) or shuffles across the rows of the
+// wave, and LDS across the workgroup's waves; then every lane folds and writes
+// its payload.
 // ------------------------------------------------------------------------------------
 #ifndef MXQ_TILES_PER_WG
 #define MXQ_TILES_PER_WG 1
@@ -980,7 +985,7 @@ struct FoldGeom {
 // whole workgroup (a barrier inside); s_max: G::kWaves * J words of LDS.  A
 // non-zero no-op flag leaves every output untouched.  FULL: whole tile groups
 // (rows a multiple of 128, K of 128 J, a band's payload under 2 GiB), so no
-// bounds checks; payload stores are buffer stores (nt) off the band's start.
+// bounds checks; payload stores are buffer stores (nt sc1) off the band's start.
 template <typename T, bool VEC, bool FULL = false>
 __device__ __forceinline__ void fold_tiles(const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K,
                                            uint8_t* __restrict__ data, uint8_t* __restrict__ tile_code,
@@ -1048,11 +1053,10 @@ __device__ __forceinline__ void fold_tiles(const T* __restrict__ x, int64_t ld_x
 }
 
 template <typename T, bool VEC, bool FULL>
-__global__ __launch_bounds__(FoldGeom<T>::kThreads) void block128_kernel(const T* __restrict__ x, int64_t ld_x, int64_t rows,
-                                                            int64_t K, uint8_t* __restrict__ data,
-                                                            uint8_t* __restrict__ tile_code, int64_t tile_ld,
-                                                            uint32_t tiles_per_row, MxqDivisor groups_per_row,
-                                                            const int32_t* __restrict__ noop) {
+__global__ __launch_bounds__(FoldGeom<T>::kThreads) void block128_kernel(
+    const T* __restrict__ x, int64_t ld_x, int64_t rows, int64_t K, uint8_t* __restrict__ data,
+    uint8_t* __restrict__ tile_code, int64_t tile_ld, uint32_t tiles_per_row, MxqDivisor groups_per_row,
+    const int32_t* __restrict__ noop) {
   __shared__ uint32_t s_max[FoldGeom<T>::kWaves][FoldGeom<T>::kJ];
   keep_denormals();
   const uint32_t bid = xcd_run<FoldGeom<T>::kRun>(blockIdx.x, gridDim.x);
@@ -2155,8 +2159,8 @@ int launch_block128_grouped(const mxq_block128_group* gs, int64_t n, hipStream_t
   int64_t count = 0, max_w = 0, sum_w = 0;
   auto flush = [&]() -> int {
     if (count == 0) return MXQ_OK;
-    hipLaunchKernelGGL((block128_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count), dim3(FoldGeom<T>::kThreads), 0,
-                       s, tab);
+    hipLaunchKernelGGL((block128_grouped_kernel<T>), dim3((uint32_t)max_w, (uint32_t)count),
+                       dim3(FoldGeom<T>::kThreads), 0, s, tab);
     count = max_w = sum_w = 0;
     return launch_status();
   };
