@@ -19,7 +19,7 @@
  *   refused the launch.  Each shape needs whole workgroups of work: COPY16: rows * K *
  *   element_size a multiple of 1024; ROW, ROW_CODES: a multiple of 8192; DECODE: rows * K a
  *   multiple of 64 * 16 / element_size; TILE*: rows and K multiples of 128; LINEAR_FOLD*:
- *   rows * K a multiple of 16384 (a tile's elements); PACKED_ROW: rows * K a multiple of 1024;
+ *   rows * K a multiple of 16384 (a tile's elements); PACKED_ROW: rows * K a multiple of 4096;
  *   READ: rows * K * element_size a multiple of 8192; WRITE: a multiple of 4096.
  *   The fold's workgroup (TILE*, LINEAR_FOLD*) is 512 lanes for element_size 2 and 1024 for 4,
  *   as in libmxq's fold.
@@ -44,8 +44,8 @@ enum {
   MXQ_SHAPE_TILE_NO_BARRIER = 5,        /* TILE without the workgroup-wide maximum (wave-wide only) */
   MXQ_SHAPE_LINEAR_FOLD = 6,            /* the fold's workgroup (lanes, chunks per lane) over a contiguous stream */
   MXQ_SHAPE_LINEAR_FOLD_NO_BARRIER = 7, /* LINEAR_FOLD without the barrier */
-  MXQ_SHAPE_PACKED_ROW = 8,             /* row lift from packed MXFP4: 64 lanes, 8 B + a code byte in, 16 B out (nt sc1),
-                                           gathered 4-byte code stores back over the codes read */
+  MXQ_SHAPE_PACKED_ROW = 8,             /* row lift from packed MXFP4: 64 lanes x 4 steps, 8 B + a code byte in, 16 B
+                                           out (nt sc1), gathered 4-byte code stores back over the codes read */
   MXQ_SHAPE_READ = 9,                   /* the machine's read-only stream: 64 lanes x 8 chunks of 16 B in (nt), none out */
   MXQ_SHAPE_WRITE = 10                  /* the machine's write-only stream: 64 lanes x 4 chunks of 16 B out (nt sc1) */
 };

@@ -70,12 +70,14 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #define MXQ_Q4_THREADS 256        // MXFP4 encode
 #endif
 // Consecutive workgroups per XCD run (see xcd_run): the row-layout FP8 decode
-// and the row lift from packed MXFP4, whose neighbouring workgroups read (and,
-// for the latter, write) parts of one line of block codes.  Runs remove the
-// duplicate code-line fetches (L2 fetch bytes 1.21x -> 1.00x of the decode's
-// reads at 8 per run, 1.20x -> 1.03x for the packed lift at 4) but cost time
-// (decode 32.4 -> 34.9 us, packed lift 18.6 -> 20.9 us at 8192 x 8192), so the
-// plain order (1) is the default.
+// and the row lift from packed MXFP4, whose neighbouring workgroups can read
+// (and, for the latter, write) parts of one line of block codes.  Runs remove
+// the duplicate code-line fetches (L2 fetch bytes 1.21x -> 1.00x of the
+// decode's reads at 8 per run; 1.20x -> 1.03x for the packed lift at one step
+// per workgroup and 4 per run) but cost time (decode 32.4 -> 34.9 us, packed
+// lift 18.6 -> 20.9 us at 8192 x 8192), so the plain order (1) is the default.
+// At its four steps per workgroup the packed lift's workgroups each take one
+// whole line of codes.
 // Code stores of the full-step row lift: 1 = the first lane of each 16-lane
 // row gathers that row's 16 / lanes-per-block codes and stores them with one
 // 4-byte (bf16) or 2-byte (fp32) store; 0 = one byte store per block (sc1).
@@ -199,8 +201,13 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXQ_DQ4_STEPS
 #define MXQ_DQ4_STEPS 2           // packed MXFP4 decode
 #endif
+// Row lift from packed MXFP4: 64 lanes x 4 steps, so a workgroup takes 4096
+// elements of a row, whose 128 block codes fill one 128-byte line.  Burst
+// means over four orders, against one step: 8192 x 8192 19.8 -> 18.9 us,
+// 28672 x 8192 62.5 -> 57.8 us, and after itself 21.0 -> 19.2 us and 69.0 ->
+// 58.6 us (2 or 8 steps, or 128 or 256 lanes, 0.5-5% slower).
 #ifndef MXQ_PACKED_STEPS
-#define MXQ_PACKED_STEPS 1
+#define MXQ_PACKED_STEPS 4
 #endif
 // The banded kernels.
 #ifndef MXQ_PFOLD_ROWS

@@ -195,20 +195,30 @@ __global__ __launch_bounds__(FoldShape<ES>::kThreads) void linear_kernel(const u
   for (int i = 0; i < P; i++) store_nt(Narrow<ES>::of(w[i], m), o, (i * N + t) * (16 / ES));
 }
 
-// The row lift from packed MXFP4's pattern: 64-lane workgroups, 8 packed bytes
-// and one code byte (two lanes per code) in per lane, 16 payload bytes out
-// (nt sc1), and the codes of each 8 lanes gathered into one 4-byte store.  The
-// gathered word is written back over the codes it was read from (the same
-// bytes), so the shape needs no second code buffer.
+// The row lift from packed MXFP4's pattern: 64-lane workgroups of 4 steps
+// (4096 elements of a row, one 128-byte line of codes), 8 packed bytes and one
+// code byte (two lanes per code) in per lane per step, all loaded first; then
+// per step 16 payload bytes out (nt sc1) and the codes of each 8 lanes gathered
+// into one 4-byte store.  The gathered word is written back over the codes it
+// was read from (the same bytes), so the shape needs no second code buffer.
 __global__ __launch_bounds__(64) void packed_row_kernel(const u32x2* __restrict__ in, uint8_t* __restrict__ out,
                                                         uint8_t* __restrict__ codes) {
   const uint32_t t = threadIdx.x;
-  const u32x2 f = __builtin_nontemporal_load(in + (uint64_t)blockIdx.x * 64 + t);
-  uint8_t* const wcodes = codes + (uint64_t)blockIdx.x * 32;     // the workgroup's 32 codes
-  const uint32_t c = wcodes[t / 2];
-  store_nt<2 | 16>(u32x4{f[0] ^ c, f[0] >> 4, f[1] + c, f[1] >> 4}, out + (uint64_t)blockIdx.x * 1024, t * 16);
-  const uint32_t w = c | (dpp<0x102>(c) << 8) | (dpp<0x104>(c) << 16) | (dpp<0x106>(c) << 24);
-  if (t % 8 == 0) store_nt<0>(w, wcodes, t / 2);
+  uint8_t* const wcodes = codes + (uint64_t)blockIdx.x * 128;    // the workgroup's 128 codes
+  u32x2 f[4];
+  uint32_t c[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    f[u] = __builtin_nontemporal_load(in + ((uint64_t)blockIdx.x * 4 + u) * 64 + t);
+    c[u] = wcodes[u * 32 + t / 2];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    store_nt<2 | 16>(u32x4{f[u][0] ^ c[u], f[u][0] >> 4, f[u][1] + c[u], f[u][1] >> 4},
+                     out + ((uint64_t)blockIdx.x * 4 + u) * 1024, t * 16);
+    const uint32_t w = c[u] | (dpp<0x102>(c[u]) << 8) | (dpp<0x104>(c[u]) << 16) | (dpp<0x106>(c[u]) << 24);
+    if (t % 8 == 0) store_nt<0>(w, wcodes, u * 32 + t / 2);
+  }
 }
 
 int status() { return hipGetLastError() == hipSuccess ? 0 : 2; }
@@ -283,8 +293,8 @@ int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t
       return status();
     }
     case MXQ_SHAPE_PACKED_ROW:
-      if ((rows * K) % 1024) return 1;
-      hipLaunchKernelGGL(packed_row_kernel, dim3((uint32_t)(rows * K / 1024)), dim3(64), 0, s, (const u32x2*)in,
+      if ((rows * K) % 4096) return 1;
+      hipLaunchKernelGGL(packed_row_kernel, dim3((uint32_t)(rows * K / 4096)), dim3(64), 0, s, (const u32x2*)in,
                          (uint8_t*)out, (uint8_t*)codes);
       return status();
     case MXQ_SHAPE_READ:

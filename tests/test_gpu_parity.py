@@ -466,15 +466,16 @@ def test_code_storage_alignment(dev, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("rows,K", [(1, 2048), (2, 2048), (33, 2048), (33, 4096), (129, 1024), (127, 6144),
-                                    (128, 128), (256, 3072)])
+@pytest.mark.parametrize("rows,K", [(1, 2048), (2, 2048), (3, 2048), (4, 2048), (33, 2048), (33, 4096), (129, 1024),
+                                    (127, 6144), (128, 128), (256, 3072)])
 def test_step_boundary_shapes(dev, dtype, rows, K):
     """Shapes at the edges of the kernels' whole-step forms: the row lift, the
     MXFP4 encode and the packed row lift take their check-free forms only for
-    whole steps (2048 bf16 / 1024 fp32 elements, 1024 packed) and an even
-    step count, the fp32 fold only for whole 128-row bands.  Odd step
-    totals, single rows and partial bands take the checked forms; both
-    against the oracle."""
+    whole steps (2048 bf16 / 1024 fp32 elements, 1024 packed) and a step
+    count that is a multiple of the steps per workgroup (2, 2 and 4), the
+    fp32 fold only for whole 128-row bands.  The other step totals, single
+    rows and partial bands take the checked forms; both against the
+    oracle."""
     src = W.c2_planted() if dtype == "bf16" else W.c2_planted_fp32()
     bits = np.ascontiguousarray(np.resize(src.reshape(-1), rows * K).reshape(rows, K))
     check_all(bits, dev, scale_ld=(K + 31) // 32 + 4)
