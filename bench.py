@@ -22,9 +22,10 @@ outside the step (the fused passes, packed MXFP4, columnwise) are timed the
 same way after the step's timed region, and so are the access-shape reference
 kernels of libmxq_shapes.so ("access_shapes": each moves one kernel's bytes in
 that kernel's access pattern with no quantization arithmetic, and each kernel
-with a shape reports "of_shape", the shape's time over its own), and the
-runtime's own device-to-device copy of the weight ("copy_reference", the
-projection's bytes).
+with a shape reports "of_shape", the shape's time over its own; "read" and
+"write" are the machine's plain read-only and write-only streams over the
+weight's bytes), and the runtime's own device-to-device copy of the weight
+("copy_reference", the projection's bytes).
 The default of 100 timed steps keeps the fixed cost of the synchronizations
 around the timed region (tens of us in all) below 1% of it.
 
