@@ -68,7 +68,9 @@ SHAPES_OF = {"shape_copy16": (0, "x", "scale2"), "shape_row": (1, "x", "scale2")
              "shape_decode": (3, "data", "scale_c"), "shape_tile": (4, "x", "scale2"),
              "shape_tile_no_barrier": (5, "x", "scale2"), "shape_linear_fold": (6, "x", "scale2"),
              "shape_linear_fold_no_barrier": (7, "x", "scale2"), "shape_packed_row": (8, "packed", "pscale"),
-             "shape_read": (9, "x", "scale2"), "shape_write": (10, "x", "scale2")}
+             "shape_read": (9, "x", "scale2"), "shape_write": (10, "x", "scale2"),
+             "shape_tile_loads": (11, "x", "scale2"), "shape_linear_loads": (12, "x", "scale2"),
+             "shape_tile_stores": (13, "x", "scale2"), "shape_linear_stores": (14, "x", "scale2")}
 SHAPE_KERNEL = {"shape_copy16": "proj", "shape_row_codes": "row", "shape_decode": "dec_row", "shape_tile": "block128",
                 "shape_packed_row": "packed_to_row"}
 # committed rocprofv3 counter summaries of the 8192 x 8192 weight, per dtype
@@ -519,7 +521,8 @@ def main():
                    "shape_tile_no_barrier": nbytes["block128"], "shape_linear_fold": es * n_el + n_el,
                    "shape_linear_fold_no_barrier": es * n_el + n_el,
                    "shape_packed_row": packed_bytes(rows, K, es)["packed_to_row"],
-                   "shape_read": es * n_el, "shape_write": es * n_el}
+                   "shape_read": es * n_el, "shape_write": es * n_el, "shape_tile_loads": es * n_el,
+                   "shape_linear_loads": es * n_el, "shape_tile_stores": n_el, "shape_linear_stores": n_el}
     shapes_out = {}
     for n in shape_names:
         us, med, lo = burst_stats(n)

@@ -20,7 +20,8 @@
  *   element_size a multiple of 1024; ROW, ROW_CODES: a multiple of 8192; DECODE: rows * K a
  *   multiple of 64 * 16 / element_size; TILE*: rows and K multiples of 128; LINEAR_FOLD*:
  *   rows * K a multiple of 16384 (a tile's elements); PACKED_ROW: rows * K a multiple of 4096;
- *   READ: rows * K * element_size a multiple of 8192; WRITE: a multiple of 4096.
+ *   READ: rows * K * element_size a multiple of 8192; WRITE: a multiple of 4096;
+ *   TILE_LOADS, LINEAR_LOADS, TILE_STORES, LINEAR_STORES: as TILE*.
  *   The fold's workgroup (TILE*, LINEAR_FOLD*) is 512 lanes for element_size 2 and 1024 for 4,
  *   as in libmxq's fold.
  */
@@ -47,7 +48,11 @@ enum {
   MXQ_SHAPE_PACKED_ROW = 8,             /* row lift from packed MXFP4: 64 lanes x 4 steps, 8 B + a code byte in, 16 B
                                            out (nt sc1), gathered 4-byte code stores back over the codes read */
   MXQ_SHAPE_READ = 9,                   /* the machine's read-only stream: 64 lanes x 8 chunks of 16 B in (nt), none out */
-  MXQ_SHAPE_WRITE = 10                  /* the machine's write-only stream: 64 lanes x 4 chunks of 16 B out (nt sc1) */
+  MXQ_SHAPE_WRITE = 10,                 /* the machine's write-only stream: 64 lanes x 4 chunks of 16 B out (nt sc1) */
+  MXQ_SHAPE_TILE_LOADS = 11,            /* TILE's loads alone (its workgroup and tile order) */
+  MXQ_SHAPE_LINEAR_LOADS = 12,          /* LINEAR_FOLD's loads alone */
+  MXQ_SHAPE_TILE_STORES = 13,           /* TILE's stores alone */
+  MXQ_SHAPE_LINEAR_STORES = 14          /* LINEAR_FOLD's stores alone */
 };
 
 int mxq_shape_run(int shape, int element_size, const void* in, void* out, void* codes, int64_t rows, int64_t K,

@@ -195,6 +195,41 @@ __global__ __launch_bounds__(FoldShape<ES>::kThreads) void linear_kernel(const u
   for (int i = 0; i < P; i++) store_nt(Narrow<ES>::of(w[i], m), o, (i * N + t) * (16 / ES));
 }
 
+// The fold's pattern split into its reads and its writes: the fold's workgroup
+// and tile order (TILE) or the same workgroup over a contiguous stream, either
+// only loading its chunks (their bits feed a test that practically never
+// stores) or only storing 16 / ES bytes per chunk.  No reduction, no barrier.
+template <int ES, bool TILE, bool LOAD>
+__global__ __launch_bounds__(FoldShape<ES>::kThreads) void fold_io_kernel(const uint8_t* __restrict__ in, int64_t K,
+                                                                       uint8_t* __restrict__ out,
+                                                                       uint32_t tiles_per_row) {
+  using S = FoldShape<ES>;
+  constexpr int CPT = S::kCPT, RPP = S::kRPP, P = S::kP, N = S::kThreads;
+  const uint32_t t = threadIdx.x, bid = TILE ? in_runs<S::kRun>(blockIdx.x, gridDim.x) : blockIdx.x;
+  const uint32_t tr = bid / tiles_per_row, tc = bid % tiles_per_row;
+  if constexpr (LOAD) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      const uint64_t row = (uint64_t)tr * 128 + t / CPT + i * RPP, col = (uint64_t)tc * 128 + (t % CPT) * (16 / ES);
+      const uint64_t off = TILE ? (row * K + col) * ES : ((uint64_t)bid * (N * P) + i * N + t) * 16;
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in + off));
+      x ^= w[0] ^ (w[1] << 1) ^ (w[2] << 2) ^ (w[3] << 3);
+    }
+    if (x == 0x9E3779B9u) reinterpret_cast<uint32_t*>(out)[bid] = x;
+  } else {
+    const u32x4 w = u32x4{t, bid, 0x01010101u, 0x02020202u};
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      if constexpr (TILE)
+        store_nt(Narrow<ES>::of(w, (uint32_t)i), out + (uint64_t)tr * 128 * K,
+                 (uint32_t)((t / CPT + i * RPP) * K + (uint64_t)tc * 128 + (t % CPT) * (16 / ES)));
+      else
+        store_nt(Narrow<ES>::of(w, (uint32_t)i), out + (uint64_t)bid * (N * P) * (16 / ES), (i * N + t) * (16 / ES));
+    }
+  }
+}
+
 // The row lift from packed MXFP4's pattern: 64-lane workgroups of 4 steps
 // (4096 elements of a row, one 128-byte line of codes), 8 packed bytes and one
 // code byte (two lanes per code) in per lane per step, all loaded first; then
@@ -297,6 +332,25 @@ int run(int shape, const void* in, void* out, void* codes, int64_t rows, int64_t
       hipLaunchKernelGGL(packed_row_kernel, dim3((uint32_t)(rows * K / 4096)), dim3(64), 0, s, (const u32x2*)in,
                          (uint8_t*)out, (uint8_t*)codes);
       return status();
+    case MXQ_SHAPE_TILE_LOADS:
+    case MXQ_SHAPE_LINEAR_LOADS:
+    case MXQ_SHAPE_TILE_STORES:
+    case MXQ_SHAPE_LINEAR_STORES: {
+      if (rows % 128 || K % 128 || 128 * K >= ((int64_t)1 << 31)) return 1;
+      const uint32_t tpr = (uint32_t)(K / 128), tiles = (uint32_t)(rows / 128) * tpr;
+      constexpr int N = FoldShape<ES>::kThreads;
+      const uint8_t* i8 = (const uint8_t*)in;
+      uint8_t* o8 = (uint8_t*)out;
+      if (shape == MXQ_SHAPE_TILE_LOADS)
+        hipLaunchKernelGGL((fold_io_kernel<ES, true, true>), dim3(tiles), dim3(N), 0, s, i8, K, o8, tpr);
+      else if (shape == MXQ_SHAPE_LINEAR_LOADS)
+        hipLaunchKernelGGL((fold_io_kernel<ES, false, true>), dim3(tiles), dim3(N), 0, s, i8, K, o8, tpr);
+      else if (shape == MXQ_SHAPE_TILE_STORES)
+        hipLaunchKernelGGL((fold_io_kernel<ES, true, false>), dim3(tiles), dim3(N), 0, s, i8, K, o8, tpr);
+      else
+        hipLaunchKernelGGL((fold_io_kernel<ES, false, false>), dim3(tiles), dim3(N), 0, s, i8, K, o8, tpr);
+      return status();
+    }
     case MXQ_SHAPE_READ:
       if (bytes % 8192) return 1;
       hipLaunchKernelGGL(read_kernel, dim3(chunks / 512), dim3(64), 0, s, (const u32x4*)in, (uint32_t*)out);

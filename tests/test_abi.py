@@ -391,4 +391,5 @@ def test_access_shape_library_loads_and_refuses_bad_arguments():
     assert L.mxq_shape_run(4, 2, fake, fake, fake, 100, 128, None) == 1        # rows not tiles
     assert L.mxq_shape_run(6, 2, fake, fake, fake, 8, 512, None) == 1          # not whole tiles of elements
     assert L.mxq_shape_run(9, 2, fake, fake, fake, 1, 2048, None) == 1         # not whole read workgroups
+    assert L.mxq_shape_run(13, 2, fake, fake, fake, 100, 128, None) == 1       # rows not tiles
     assert L.mxq_shape_run(0, 2, fake, fake, fake, 0, 512, None) == 1          # empty
