@@ -1093,7 +1093,12 @@ __global__ __launch_bounds__(FoldGeom<T>::kThreads) void block128_grouped_kernel
   const FoldGroupDesc d = tab.g[blockIdx.y];
   if (blockIdx.x >= d.n_groups) return;                      // uniform: past this weight's tiles
   keep_denormals();
-  const uint32_t tr = mxq_quot(blockIdx.x, d.groups_per_row), tg = blockIdx.x - tr * d.groups_per_row.d;
+  // bf16: the single fold's tile runs per XCD, within the weight (the XCD of a
+  // workgroup follows blockIdx.x when the grid's x extent is a multiple of 8):
+  // 48 weights of 1024 x 2048 in 51.0 -> 48.7 us; fp32 keeps the plain order
+  // (80.2 -> 81.5 us with its runs of 4)
+  const uint32_t bid = xcd_run<sizeof(T) == 2 ? FoldGeom<T>::kRun : 1>(blockIdx.x, d.n_groups);
+  const uint32_t tr = mxq_quot(bid, d.groups_per_row), tg = bid - tr * d.groups_per_row.d;
   fold_tiles<T, true>(static_cast<const T*>(d.x), d.ld_x, d.rows, d.K, d.data, d.tile_code, d.tile_ld,
                       d.tiles_per_row, tr, tg, nullptr, s_max);
 }
